@@ -1,0 +1,260 @@
+/*
+ * pagedattn.h - C ABI of a paged-attention library for AMD Instinct MI355X
+ * (gfx950): paged attention over a block-table KV cache.
+ *
+ * The KV cache is a pool of fixed-size blocks.  Each sequence owns an
+ * ordered list of block ids (its block table), and blocks may be shared
+ * between sequences with a common prefix.  New tokens are scattered into
+ * the pool through a slot mapping.  Decode and chunked-prefill attention
+ * read the pool in place, block by block, through the tables.
+ *
+ * Sources, by page and passage:
+ *   [TS]  TensorSharp, "Mistral 3" model page.  Section 3 "Forward graph"
+ *         scales Q by 1/sqrt(headDim), appends K/V to the cache, then runs
+ *         standard causal GQA attention.  Section 11 "Batched / paged
+ *         forward" gives the per-layer paged buffer
+ *         [numBlocks * blockSize * numKvHeads * headDim], the slotMapping
+ *         scatter to blockId * blockSize + offset, and the online-softmax
+ *         paged attention loop parallel over (sequence, head).
+ *   [MR]  "Pure-Rust engines as a comparison" (mistral.rs), section on
+ *         paged attention: blocks of 8, 16 or 32 tokens, default 32, and
+ *         an explicit unsupported setting is an error rather than a silent
+ *         fallback.  The scheduling section gives chunked prefill of up to
+ *         512 tokens under a 4096-token budget.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every pointer named *device* is HIP device memory.  The caller
+ *    allocates and owns every buffer.  The library never allocates, never
+ *    frees and never synchronises.  It keeps no per-call state, so calls
+ *    are reentrant and may run on any number of streams at once.
+ *  - `stream` is a hipStream_t passed as void*; NULL is the null stream.
+ *    Every call only enqueues work on it.  Results are visible after the
+ *    caller synchronises with that stream.
+ *  - Layouts are row-major and contiguous:
+ *      k_cache, v_cache : [num_blocks, block_size, num_kv_heads, head_dim]
+ *      block_tables     : [num_seqs, max_blocks_per_seq] int32
+ *      context_lens     : [num_seqs] int32 (tokens already in the cache,
+ *                         including the tokens this step wrote)
+ *    A token at logical position p of sequence i sits in physical block
+ *    block_tables[i][p / block_size] at offset p % block_size.  Its slot is
+ *    block_id * block_size + offset.
+ *  - Query head h reads kv head h / (num_heads / num_kv_heads).
+ *  - `scale` multiplies every q.k dot product.  It is normally
+ *    1/sqrt(head_dim).
+ *  - Element types: q, k_cache, v_cache and out share one dtype (fp32 or
+ *    bf16).  Arithmetic is fp32 in either case.  bf16 outputs are rounded
+ *    to nearest even.
+ *  - Supported shapes: block_size in {8, 16, 32}, head_dim in {64, 128},
+ *    num_heads / num_kv_heads in {1, 2, 4, 8}.
+ *
+ * Errors
+ * ------
+ *  Every entry point checks its arguments on the host before it enqueues
+ *  anything.  On failure it returns a negative pa_status and records a
+ *  message naming what was expected and what it got; read the message
+ *  with pa_last_error_message() (thread-local).  Nothing aborts.  A
+ *  launch failure reported by the HIP runtime returns PA_ERR_HIP.  Faults
+ *  during execution surface at the caller's next synchronisation.
+ *
+ *  Contracts on the *contents* of device buffers are the caller's, and the
+ *  host cannot check them without reading device memory:
+ *    - block ids lie in [0, num_blocks);
+ *    - context_lens[i] <= max_context_len and
+ *      context_lens[i] <= max_blocks_per_seq * block_size;
+ *    - slots are distinct.
+ *  The kernels still never touch memory outside the buffers the sizes
+ *  describe.  A block id outside [0, num_blocks) drops that block's tokens
+ *  from the softmax.  A context length above either bound is cut to the
+ *  bound.  A slot outside [0, num_blocks * block_size) is skipped.  A
+ *  result computed under a broken contract is unspecified.
+ */
+#ifndef PAGEDATTN_H
+#define PAGEDATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pa_dtype {
+  PA_DTYPE_F32 = 0,
+  PA_DTYPE_BF16 = 1
+} pa_dtype;
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_NULL = -1,        /* a required pointer is NULL                     */
+  PA_ERR_DTYPE = -2,       /* dtype is not a pa_dtype value                  */
+  PA_ERR_SHAPE = -3,       /* a size is out of range, or sizes disagree      */
+  PA_ERR_BLOCK_SIZE = -4,  /* block_size not in {8, 16, 32}                  */
+  PA_ERR_HEAD_DIM = -5,    /* head_dim not in {64, 128}                      */
+  PA_ERR_GQA = -6,         /* num_heads / num_kv_heads not in {1, 2, 4, 8}   */
+  PA_ERR_WORKSPACE = -7,   /* split-K workspace missing or too small         */
+  PA_ERR_UNSUPPORTED = -8, /* a valid request this build does not implement  */
+  PA_ERR_HIP = -9,         /* the HIP runtime reported an error              */
+  PA_ERR_PARTITION = -10   /* partition_size not 0 or a positive multiple
+                              of block_size                                  */
+} pa_status;
+
+/* One layer's paged KV pool.  The pointers are device memory owned by the
+ * caller, laid out [num_blocks, block_size, num_kv_heads, head_dim] and
+ * contiguous.  [TS] section 11. */
+typedef struct pa_kv_cache {
+  void *k_cache;
+  void *v_cache;
+  int32_t num_blocks;
+  int32_t block_size;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t dtype; /* pa_dtype */
+} pa_kv_cache;
+
+/* ---------------------------------------------------------------------
+ * pa_kv_cache_write - scatter new tokens' K and V into the paged pool.
+ * [TS] section 11: the slotMapping scatter.  [TS] section 3: K/V are
+ * appended before attention, so the tokens a step writes are attended by
+ * that same step.
+ *
+ *   key, value   : device, [num_tokens, num_kv_heads, head_dim], cache dtype.
+ *   slot_mapping : device, [num_tokens] int64.  Token t is copied to slot
+ *                  slot_mapping[t], i.e. to block slot/block_size at offset
+ *                  slot%block_size, for every kv head.  A negative slot
+ *                  skips its token (padding).  A slot at or past
+ *                  num_blocks*block_size is skipped as well.
+ *   num_tokens   : >= 0.  0 enqueues nothing.
+ *
+ * The copy is bit-exact.  Slots must be distinct: if two tokens name the
+ * same slot, which one lands there is unspecified.  Only num_kv_heads *
+ * head_dim * element_size % 16 == 0 is required of the shape; block_size
+ * and head_dim need not be in the attention-supported sets.
+ * --------------------------------------------------------------------- */
+int pa_kv_cache_write(const pa_kv_cache *cache, const void *key, const void *value,
+                      const int64_t *slot_mapping, int32_t num_tokens, void *stream);
+
+/* ---------------------------------------------------------------------
+ * pa_decode_workspace_bytes - bytes of fp32 workspace that split-K decode
+ * needs: the per-partition running max m, sum l and unnormalised output
+ * o[head_dim] for every (sequence, query head, partition), where there are
+ * ceil(max_context_len / partition_size) partitions.  Returns 0 when
+ * partition_size <= 0 (single pass) or when there is at most one
+ * partition.  Negative sizes also give 0.
+ * --------------------------------------------------------------------- */
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                 int32_t max_context_len, int32_t partition_size);
+
+/* ---------------------------------------------------------------------
+ * pa_decode - attention of one new query token per sequence over its whole
+ * context in the paged cache.  [TS] section 3 (scaled causal GQA over the
+ * cache, the new token included once written), section 11 (paged buffers
+ * and the online-softmax loop over (sequence, head)).
+ *
+ *   out            : device, [num_seqs, num_heads, head_dim], cache dtype.
+ *   q              : device, [num_seqs, num_heads, head_dim], cache dtype.
+ *   block_tables   : device, [num_seqs, max_blocks_per_seq] int32.  Entries
+ *                    past a sequence's last block are never read.
+ *   context_lens   : device, [num_seqs] int32.  The query token is the
+ *                    last of its sequence's context_lens[i] tokens and sees
+ *                    all of them.  A context of 0 gives a zero output.
+ *   max_context_len: host int, an upper bound of context_lens.  It sizes
+ *                    the grid and the workspace, so no device read is
+ *                    needed.
+ *   scale          : multiplies q.k.
+ *   partition_size : 0 for a single pass, with one work-group per
+ *                    (sequence, kv head) walking the whole context.
+ *                    Otherwise it is split-K flash-decoding: a positive
+ *                    multiple of block_size that sets the tokens per
+ *                    partition.  Each partition yields (m, l, o), and a
+ *                    reduce kernel merges them with the same rescaling rule
+ *                    the online softmax applies between tiles.  A sequence
+ *                    that fits in one partition is written directly.
+ *   workspace      : device, >= pa_decode_workspace_bytes(...) bytes when
+ *                    partition_size > 0 and max_context_len > partition_size;
+ *                    otherwise it may be NULL.  It is only scratch:
+ *                    contents before and after the call carry no meaning.
+ *
+ * pa_decode enqueues pa_decode_partition and then pa_decode_reduce.
+ * --------------------------------------------------------------------- */
+int pa_decode(const pa_kv_cache *cache, void *out, const void *q, int32_t num_seqs,
+              int32_t num_heads, const int32_t *block_tables, int32_t max_blocks_per_seq,
+              const int32_t *context_lens, int32_t max_context_len, float scale,
+              int32_t partition_size, void *workspace, size_t workspace_bytes, void *stream);
+
+/* ---------------------------------------------------------------------
+ * pa_decode_partition - first stage of pa_decode, same arguments.  It
+ * writes the final output of every sequence with at most one partition.
+ * For every other sequence it writes (m, l, o) per partition into the
+ * workspace.  Call pa_decode_reduce afterwards on the same stream.  A
+ * caller may run other work between the two stages.
+ * --------------------------------------------------------------------- */
+int pa_decode_partition(const pa_kv_cache *cache, void *out, const void *q, int32_t num_seqs,
+                        int32_t num_heads, const int32_t *block_tables, int32_t max_blocks_per_seq,
+                        const int32_t *context_lens, int32_t max_context_len, float scale,
+                        int32_t partition_size, void *workspace, size_t workspace_bytes,
+                        void *stream);
+
+/* ---------------------------------------------------------------------
+ * pa_decode_reduce - second stage of pa_decode.  For every sequence with
+ * more than one partition, it merges the partitions' (m, l, o) into
+ *   out = sum_p o_p * 2^(m_p - M) / sum_p l_p * 2^(m_p - M),  M = max_p m_p,
+ * where m is kept in base-2 units of the scaled scores.  Sequences with
+ * at most one partition are left untouched.  dtype, num_seqs, num_heads,
+ * head_dim, context_lens, max_context_len, partition_size and the
+ * workspace must match the pa_decode_partition call that filled it.
+ * --------------------------------------------------------------------- */
+int pa_decode_reduce(void *out, int32_t dtype, int32_t num_seqs, int32_t num_heads,
+                     int32_t head_dim, const int32_t *context_lens, int32_t max_context_len,
+                     int32_t partition_size, const void *workspace, size_t workspace_bytes,
+                     void *stream);
+
+/* ---------------------------------------------------------------------
+ * pa_prefill_chunk - causal attention of a packed chunk of new tokens per
+ * sequence over that sequence's cached prefix plus the chunk itself.
+ * [TS] section 3: scaled causal GQA; the chunk's K/V are written with
+ * pa_kv_cache_write first.  [MR] scheduling section: prefill proceeds in
+ * chunks of up to 512 tokens under a 4096-token step budget.
+ *
+ *   out, q          : device, [num_query_tokens, num_heads, head_dim], cache
+ *                     dtype.  Sequence i owns rows
+ *                     query_start_loc[i] .. query_start_loc[i+1]-1.
+ *   query_start_loc : device, [num_seqs + 1] int32, non-decreasing, with
+ *                     last entry <= num_query_tokens.  Rows at or past
+ *                     num_query_tokens are never touched.
+ *   max_query_len   : host int, an upper bound of each sequence's row
+ *                     count.  It sizes the grid.
+ *   context_lens    : device, [num_seqs] int32: cached prefix plus chunk.
+ *                     Chunk row t of sequence i has absolute position
+ *                     context_lens[i] - q_len_i + t and sees keys at
+ *                     positions 0 .. that position (causal mask aligned to
+ *                     the end of the context).
+ *   block_tables, max_blocks_per_seq, max_context_len, scale : as for
+ *                     pa_decode.
+ *
+ * This build implements bf16 only, on bf16 MFMA tiles with fp32
+ * accumulation.  The softmax weights are rounded to bf16 before they
+ * multiply V.  fp32 caches return PA_ERR_UNSUPPORTED.
+ * --------------------------------------------------------------------- */
+int pa_prefill_chunk(const pa_kv_cache *cache, void *out, const void *q,
+                     const int32_t *query_start_loc, int32_t num_seqs, int32_t num_heads,
+                     int32_t num_query_tokens, int32_t max_query_len,
+                     const int32_t *block_tables, int32_t max_blocks_per_seq,
+                     const int32_t *context_lens, int32_t max_context_len, float scale,
+                     void *stream);
+
+/* Short static name of a status code, e.g. "PA_ERR_BLOCK_SIZE". */
+const char *pa_status_string(int status);
+
+/* Message of the last failed call on this thread, e.g.
+ * "block_size 24 not in {8, 16, 32}".  Empty after a successful call. */
+const char *pa_last_error_message(void);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int pa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDATTN_H */

@@ -1,0 +1,34 @@
+"""Paged attention over a block-table KV cache for AMD Instinct MI355X (gfx950).
+
+The work is done by hand-written HIP kernels behind the C ABI in
+``include/pagedattn.h`` (``libpagedattn.so``, built in-tree by
+``paged_attention_kv_cache_amd.build``).  This package is only the binding:
+
+* ``pa_kv_cache_write``  - slot-mapping scatter of new K/V into the pool
+* ``pa_decode``          - one query per sequence over its context; split-K
+  partitions plus reduce (``pa_decode_partition`` / ``pa_decode_reduce``
+  run the two stages separately)
+* ``pa_prefill_chunk``   - causal attention of packed chunks over their
+  cached prefixes (bf16 MFMA)
+"""
+
+from ._binding import (  # noqa: F401
+    LIB_PATH,
+    PA_DTYPE_BF16,
+    PA_DTYPE_F32,
+    STATUS,
+    PagedAttnError,
+    PaKvCache,
+    load_library,
+    make_cache,
+    pa_decode,
+    pa_decode_partition,
+    pa_decode_reduce,
+    pa_decode_workspace_bytes,
+    pa_kv_cache_write,
+    pa_last_error_message,
+    pa_prefill_chunk,
+    pa_status_string,
+    pa_version,
+)
+from .contracts import check_decode_contracts, check_prefill_contracts, check_slot_mapping  # noqa: F401

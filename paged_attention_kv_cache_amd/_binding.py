@@ -1,0 +1,291 @@
+"""ctypes binding of ``libpagedattn.so`` (the C ABI in ``include/pagedattn.h``).
+
+Argument marshalling only: tensors in, device pointers and sizes out, the
+status code checked.  Every step of the computation runs in the library's
+HIP kernels.  torch supplies device memory and the current stream.  If the
+library has not been built, the first call raises: there is no fallback
+path.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Optional
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libpagedattn.so")
+
+PA_DTYPE_F32 = 0
+PA_DTYPE_BF16 = 1
+
+STATUS = {
+    0: "PA_OK",
+    -1: "PA_ERR_NULL",
+    -2: "PA_ERR_DTYPE",
+    -3: "PA_ERR_SHAPE",
+    -4: "PA_ERR_BLOCK_SIZE",
+    -5: "PA_ERR_HEAD_DIM",
+    -6: "PA_ERR_GQA",
+    -7: "PA_ERR_WORKSPACE",
+    -8: "PA_ERR_UNSUPPORTED",
+    -9: "PA_ERR_HIP",
+    -10: "PA_ERR_PARTITION",
+}
+
+# every function the header declares, with its ctypes signature
+_i32 = ctypes.c_int32
+_vp = ctypes.c_void_p
+_f32 = ctypes.c_float
+_sz = ctypes.c_size_t
+
+
+class PaKvCache(ctypes.Structure):
+    _fields_ = [
+        ("k_cache", _vp),
+        ("v_cache", _vp),
+        ("num_blocks", _i32),
+        ("block_size", _i32),
+        ("num_kv_heads", _i32),
+        ("head_dim", _i32),
+        ("dtype", _i32),
+    ]
+
+
+_PCACHE = ctypes.POINTER(PaKvCache)
+
+SIGNATURES = {
+    "pa_kv_cache_write": (ctypes.c_int, [_PCACHE, _vp, _vp, _vp, _i32, _vp]),
+    "pa_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
+    "pa_decode": (ctypes.c_int, [_PCACHE, _vp, _vp, _i32, _i32, _vp, _i32, _vp, _i32, _f32, _i32,
+                                 _vp, _sz, _vp]),
+    "pa_decode_partition": (ctypes.c_int, [_PCACHE, _vp, _vp, _i32, _i32, _vp, _i32, _vp, _i32, _f32,
+                                           _i32, _vp, _sz, _vp]),
+    "pa_decode_reduce": (ctypes.c_int, [_vp, _i32, _i32, _i32, _i32, _vp, _i32, _i32, _vp, _sz, _vp]),
+    "pa_prefill_chunk": (ctypes.c_int, [_PCACHE, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _i32, _vp,
+                                        _i32, _f32, _vp]),
+    "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "pa_last_error_message": (ctypes.c_char_p, []),
+    "pa_version": (ctypes.c_int, []),
+}
+
+_lib = None
+_lock = threading.Lock()
+
+
+class PagedAttnError(RuntimeError):
+    """A negative status from the library, with its message."""
+
+    def __init__(self, func: str, code: int, message: str):
+        self.func = func
+        self.code = code
+        self.status = STATUS.get(code, f"status {code}")
+        self.message = message
+        super().__init__(f"{func}: {self.status}: {message}")
+
+
+def load_library(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load the shared library once and attach the ctypes signatures."""
+    global _lib
+    with _lock:
+        if _lib is not None and path is None:
+            return _lib
+        p = path or LIB_PATH
+        if not os.path.exists(p):
+            raise RuntimeError(
+                f"{p} is not built; build it with `python -c \"import __graft_entry__ as g; g.build()\"` "
+                "or `python paged_attention_kv_cache_amd/build.py` (there is no fallback path)")
+        lib = ctypes.CDLL(p)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        if path is None:
+            _lib = lib
+        return lib
+
+
+def _check(func: str, code: int) -> None:
+    if code != 0:
+        msg = load_library().pa_last_error_message()
+        raise PagedAttnError(func, code, msg.decode() if msg else "")
+
+
+# ---------------------------------------------------------------- tensors
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return PA_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return PA_DTYPE_F32
+    raise TypeError(f"unsupported dtype {t.dtype}; expected torch.float32 or torch.bfloat16")
+
+
+def _dev(t, name: str, dtype=None, ndim: Optional[int] = None):
+    """Device pointer of a contiguous GPU tensor (checks only)."""
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor, got device {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    return ctypes.c_void_p(handle)
+
+
+def make_cache(k_cache, v_cache) -> PaKvCache:
+    """Descriptor for one layer's pool ``[num_blocks, block_size, num_kv_heads, head_dim]``."""
+    if k_cache.shape != v_cache.shape or k_cache.dim() != 4:
+        raise ValueError(f"k_cache {tuple(k_cache.shape)} and v_cache {tuple(v_cache.shape)} must be equal 4-d shapes")
+    if k_cache.dtype != v_cache.dtype:
+        raise TypeError("k_cache and v_cache dtypes differ")
+    nb, bs, hkv, d = (int(x) for x in k_cache.shape)
+    return PaKvCache(_dev(k_cache, "k_cache").value, _dev(v_cache, "v_cache").value, nb, bs, hkv, d,
+                     _dtype_code(k_cache))
+
+
+# ------------------------------------------------------------ entry points
+
+def pa_version() -> int:
+    return int(load_library().pa_version())
+
+
+def pa_status_string(code: int) -> str:
+    return load_library().pa_status_string(code).decode()
+
+
+def pa_last_error_message() -> str:
+    return load_library().pa_last_error_message().decode()
+
+
+def pa_decode_workspace_bytes(num_seqs: int, num_heads: int, head_dim: int, max_context_len: int,
+                              partition_size: int) -> int:
+    return int(load_library().pa_decode_workspace_bytes(num_seqs, num_heads, head_dim, max_context_len,
+                                                        partition_size))
+
+
+def pa_kv_cache_write(key, value, k_cache, v_cache, slot_mapping, stream=None) -> None:
+    """Scatter ``key``/``value`` ``[T, Hkv, D]`` into the pool at ``slot_mapping`` (int64 [T])."""
+    torch = _torch()
+    cache = make_cache(k_cache, v_cache)
+    if key.shape != value.shape or key.dim() != 3 or tuple(key.shape[1:]) != tuple(k_cache.shape[2:]):
+        raise ValueError(f"key/value {tuple(key.shape)}/{tuple(value.shape)} must be [T, "
+                         f"{k_cache.shape[2]}, {k_cache.shape[3]}]")
+    if slot_mapping.shape != (key.shape[0],):
+        raise ValueError(f"slot_mapping {tuple(slot_mapping.shape)} must be [{key.shape[0]}]")
+    code = load_library().pa_kv_cache_write(
+        ctypes.byref(cache), _dev(key, "key", k_cache.dtype), _dev(value, "value", k_cache.dtype),
+        _dev(slot_mapping, "slot_mapping", torch.int64), int(key.shape[0]), _stream(stream))
+    _check("pa_kv_cache_write", code)
+
+
+def _decode_args(q, k_cache, v_cache, block_tables, context_lens, out):
+    torch = _torch()
+    cache = make_cache(k_cache, v_cache)
+    S, H, D = (int(x) for x in q.shape)
+    if D != int(k_cache.shape[3]):
+        raise ValueError(f"q head_dim {D} != cache head_dim {k_cache.shape[3]}")
+    if block_tables.dim() != 2 or int(block_tables.shape[0]) != S:
+        raise ValueError(f"block_tables {tuple(block_tables.shape)} must be [{S}, max_blocks_per_seq]")
+    if tuple(context_lens.shape) != (S,):
+        raise ValueError(f"context_lens {tuple(context_lens.shape)} must be [{S}]")
+    if out is None:
+        out = torch.empty_like(q)
+    elif tuple(out.shape) != tuple(q.shape) or out.dtype != q.dtype:
+        raise ValueError("out must match q in shape and dtype")
+    ptrs = (_dev(out, "out", k_cache.dtype, 3), _dev(q, "q", k_cache.dtype, 3),
+            _dev(block_tables, "block_tables", torch.int32), _dev(context_lens, "context_lens", torch.int32))
+    return cache, S, H, D, out, ptrs
+
+
+def _workspace(workspace, need: int, device):
+    torch = _torch()
+    if need == 0:
+        return ctypes.c_void_p(0), 0
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    nbytes = workspace.numel() * workspace.element_size()
+    return ctypes.c_void_p(workspace.data_ptr()), nbytes
+
+
+def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, max_context_len: int,
+              partition_size: int = 512, out=None, workspace=None, stream=None, _stage: str = "both"):
+    """Paged decode: ``q [S, H, D]`` -> ``out [S, H, D]``.
+
+    ``partition_size`` 0 runs one pass per (sequence, kv head); otherwise
+    split-K partitions of that many tokens plus the reduce kernel.
+    ``workspace`` (uint8 GPU tensor) is allocated here when not given.
+    """
+    cache, S, H, D, out, (p_out, p_q, p_bt, p_cl) = _decode_args(q, k_cache, v_cache, block_tables,
+                                                                 context_lens, out)
+    lib = load_library()
+    need = int(lib.pa_decode_workspace_bytes(S, H, D, int(max_context_len), int(partition_size)))
+    p_ws, ws_bytes = _workspace(workspace, need, q.device)
+    st = _stream(stream)
+    mbps = int(block_tables.shape[1])
+    if _stage in ("both", "partition"):
+        fn = lib.pa_decode if _stage == "both" else lib.pa_decode_partition
+        code = fn(ctypes.byref(cache), p_out, p_q, S, H, p_bt, mbps, p_cl, int(max_context_len),
+                  float(scale), int(partition_size), p_ws, ws_bytes, st)
+        _check("pa_decode" if _stage == "both" else "pa_decode_partition", code)
+    if _stage == "reduce":
+        code = lib.pa_decode_reduce(p_out, cache.dtype, S, H, D, p_cl, int(max_context_len),
+                                    int(partition_size), p_ws, ws_bytes, st)
+        _check("pa_decode_reduce", code)
+    return out
+
+
+def pa_decode_partition(q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len,
+                        partition_size, out, workspace, stream=None):
+    """First stage of :func:`pa_decode` (same arguments; ``out`` and
+    ``workspace`` must be given)."""
+    return pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len,
+                     partition_size, out=out, workspace=workspace, stream=stream, _stage="partition")
+
+
+def pa_decode_reduce(q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len,
+                     partition_size, out, workspace, stream=None):
+    """Second stage of :func:`pa_decode` (same arguments as the first)."""
+    return pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len,
+                     partition_size, out=out, workspace=workspace, stream=stream, _stage="reduce")
+
+
+def pa_prefill_chunk(q, query_start_loc, k_cache, v_cache, block_tables, context_lens, scale: float,
+                     max_query_len: int, max_context_len: int, out=None, stream=None):
+    """Chunked prefill: packed ``q [Tq, H, D]`` -> ``out [Tq, H, D]``."""
+    torch = _torch()
+    cache = make_cache(k_cache, v_cache)
+    Tq, H, D = (int(x) for x in q.shape)
+    S = int(context_lens.shape[0])
+    if tuple(query_start_loc.shape) != (S + 1,):
+        raise ValueError(f"query_start_loc {tuple(query_start_loc.shape)} must be [{S + 1}]")
+    if block_tables.dim() != 2 or int(block_tables.shape[0]) != S:
+        raise ValueError(f"block_tables {tuple(block_tables.shape)} must be [{S}, max_blocks_per_seq]")
+    if out is None:
+        out = torch.empty_like(q)
+    code = load_library().pa_prefill_chunk(
+        ctypes.byref(cache), _dev(out, "out", k_cache.dtype, 3), _dev(q, "q", k_cache.dtype, 3),
+        _dev(query_start_loc, "query_start_loc", torch.int32), S, H, Tq, int(max_query_len),
+        _dev(block_tables, "block_tables", torch.int32), int(block_tables.shape[1]),
+        _dev(context_lens, "context_lens", torch.int32), int(max_context_len), float(scale),
+        _stream(stream))
+    _check("pa_prefill_chunk", code)
+    return out

@@ -1,0 +1,324 @@
+// C ABI of the paged-attention library: argument validation, error
+// reporting and dispatch to the HIP launchers.  Everything here runs on the
+// host before any work is enqueued.  It never reads device memory, never
+// allocates and never synchronises.
+//
+// The validation follows the error convention of the mistral.rs page
+// ("Pure-Rust engines as a comparison", paged-attention section): an
+// unsupported explicit setting, such as a block size outside {8, 16, 32},
+// is an error, not a silent fallback.  Each message names the expected
+// values and the value received.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <hip/hip_runtime_api.h>
+
+#include "pa_common.h"
+#include "pagedattn.h"
+
+namespace {
+
+thread_local char g_msg[512] = "";
+
+int fail(int status, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_msg, sizeof(g_msg), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  g_msg[0] = '\0';
+  return PA_OK;
+}
+
+int hip_fail(hipError_t e, const char *what) {
+  return fail(PA_ERR_HIP, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
+}
+
+int elem_bytes(int dtype) { return dtype == PA_DTYPE_BF16 ? 2 : 4; }
+
+constexpr int kMaxGridYZ = 65535;
+
+// Cache descriptor checks shared by all entry points.  `attention` adds
+// the shape limits of the attention kernels.
+int check_cache(const pa_kv_cache *c, bool attention) {
+  if (!c) return fail(PA_ERR_NULL, "cache descriptor is NULL");
+  if (!c->k_cache || !c->v_cache)
+    return fail(PA_ERR_NULL, "cache k_cache=%p v_cache=%p: both must be device pointers", c->k_cache,
+                c->v_cache);
+  if (c->dtype != PA_DTYPE_F32 && c->dtype != PA_DTYPE_BF16)
+    return fail(PA_ERR_DTYPE, "dtype %d not in {0 (f32), 1 (bf16)}", c->dtype);
+  if (c->num_blocks <= 0) return fail(PA_ERR_SHAPE, "num_blocks %d must be > 0", c->num_blocks);
+  if (c->num_kv_heads <= 0) return fail(PA_ERR_SHAPE, "num_kv_heads %d must be > 0", c->num_kv_heads);
+  if (c->head_dim <= 0) return fail(PA_ERR_HEAD_DIM, "head_dim %d must be > 0", c->head_dim);
+  if (c->block_size <= 0) return fail(PA_ERR_BLOCK_SIZE, "block_size %d must be > 0", c->block_size);
+  if (attention) {
+    if (c->block_size != 8 && c->block_size != 16 && c->block_size != 32)
+      return fail(PA_ERR_BLOCK_SIZE, "block_size %d not in {8, 16, 32}", c->block_size);
+    if (c->head_dim != 64 && c->head_dim != 128)
+      return fail(PA_ERR_HEAD_DIM, "head_dim %d not in {64, 128}", c->head_dim);
+    if (c->num_kv_heads > kMaxGridYZ)
+      return fail(PA_ERR_SHAPE, "num_kv_heads %d above %d", c->num_kv_heads, kMaxGridYZ);
+  }
+  return PA_OK;
+}
+
+int check_heads(const pa_kv_cache *c, int num_heads) {
+  if (num_heads <= 0) return fail(PA_ERR_SHAPE, "num_heads %d must be > 0", num_heads);
+  if (num_heads % c->num_kv_heads)
+    return fail(PA_ERR_GQA, "num_heads %d is not a multiple of num_kv_heads %d", num_heads,
+                c->num_kv_heads);
+  const int g = num_heads / c->num_kv_heads;
+  if (g != 1 && g != 2 && g != 4 && g != 8)
+    return fail(PA_ERR_GQA, "num_heads / num_kv_heads = %d not in {1, 2, 4, 8}", g);
+  if (num_heads > kMaxGridYZ) return fail(PA_ERR_SHAPE, "num_heads %d above %d", num_heads, kMaxGridYZ);
+  return PA_OK;
+}
+
+int num_partitions(int max_context_len, int partition_size) {
+  if (partition_size <= 0 || max_context_len <= partition_size) return 1;
+  return (int)(((int64_t)max_context_len + partition_size - 1) / partition_size);
+}
+
+// Workspace carve-up: m [S][H][P], l [S][H][P], o [S][H][P][D], each region
+// 256-byte aligned.
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t workspace_bytes(int num_seqs, int num_heads, int head_dim, int max_context_len,
+                       int partition_size) {
+  if (num_seqs <= 0 || num_heads <= 0 || head_dim <= 0 || max_context_len <= 0 ||
+      partition_size <= 0)
+    return 0;
+  const int P = num_partitions(max_context_len, partition_size);
+  if (P <= 1) return 0;
+  const size_t n = (size_t)num_seqs * num_heads * P;
+  return 2 * align256(n * sizeof(float)) + align256(n * head_dim * sizeof(float));
+}
+
+int prepare_decode(const pa_kv_cache *cache, void *out, const void *q, int32_t num_seqs,
+                   int32_t num_heads, const int32_t *block_tables, int32_t max_blocks_per_seq,
+                   const int32_t *context_lens, int32_t max_context_len, float scale,
+                   int32_t partition_size, void *workspace, size_t ws_bytes, pa::DecodeArgs *a) {
+  int st = check_cache(cache, true);
+  if (st) return st;
+  if ((st = check_heads(cache, num_heads))) return st;
+  if (num_seqs < 0) return fail(PA_ERR_SHAPE, "num_seqs %d must be >= 0", num_seqs);
+  if (num_seqs > kMaxGridYZ) return fail(PA_ERR_SHAPE, "num_seqs %d above %d", num_seqs, kMaxGridYZ);
+  if (max_blocks_per_seq <= 0)
+    return fail(PA_ERR_SHAPE, "max_blocks_per_seq %d must be > 0", max_blocks_per_seq);
+  if (max_context_len < 0) return fail(PA_ERR_SHAPE, "max_context_len %d must be >= 0", max_context_len);
+  if (!isfinite(scale)) return fail(PA_ERR_SHAPE, "scale %g is not finite", (double)scale);
+  if (partition_size < 0 || (partition_size > 0 && partition_size % cache->block_size))
+    return fail(PA_ERR_PARTITION, "partition_size %d is neither 0 nor a positive multiple of block_size %d",
+                partition_size, cache->block_size);
+  if (num_seqs > 0 && (!out || !q || !block_tables || !context_lens))
+    return fail(PA_ERR_NULL, "out=%p q=%p block_tables=%p context_lens=%p: all must be device pointers",
+                out, q, (const void *)block_tables, (const void *)context_lens);
+  const int P = num_partitions(max_context_len, partition_size);
+  const size_t need = workspace_bytes(num_seqs, num_heads, cache->head_dim, max_context_len, partition_size);
+  if (need > 0) {
+    if (!workspace) return fail(PA_ERR_WORKSPACE, "workspace is NULL; %zu bytes needed", need);
+    if (ws_bytes < need)
+      return fail(PA_ERR_WORKSPACE, "workspace_bytes %zu < %zu needed", ws_bytes, need);
+  }
+  a->cache = {cache->k_cache, cache->v_cache, cache->num_blocks, cache->block_size,
+              cache->num_kv_heads, cache->head_dim, cache->dtype};
+  a->out = out;
+  a->q = q;
+  a->num_seqs = num_seqs;
+  a->num_heads = num_heads;
+  a->block_tables = block_tables;
+  a->max_blocks_per_seq = max_blocks_per_seq;
+  a->context_lens = context_lens;
+  a->max_context_len = max_context_len;
+  a->scale = scale;
+  a->partition_size = (P > 1) ? partition_size : 0;
+  a->max_partitions = P;
+  a->ws_m = a->ws_l = a->ws_o = nullptr;
+  if (need > 0) {
+    const size_t n = (size_t)num_seqs * num_heads * P;
+    char *w = static_cast<char *>(workspace);
+    a->ws_m = reinterpret_cast<float *>(w);
+    a->ws_l = reinterpret_cast<float *>(w + align256(n * sizeof(float)));
+    a->ws_o = reinterpret_cast<float *>(w + 2 * align256(n * sizeof(float)));
+  }
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_version(void) { return 10000; }  // 1.0.0
+
+const char *pa_last_error_message(void) { return g_msg; }
+
+const char *pa_status_string(int status) {
+  switch (status) {
+    case PA_OK: return "PA_OK";
+    case PA_ERR_NULL: return "PA_ERR_NULL";
+    case PA_ERR_DTYPE: return "PA_ERR_DTYPE";
+    case PA_ERR_SHAPE: return "PA_ERR_SHAPE";
+    case PA_ERR_BLOCK_SIZE: return "PA_ERR_BLOCK_SIZE";
+    case PA_ERR_HEAD_DIM: return "PA_ERR_HEAD_DIM";
+    case PA_ERR_GQA: return "PA_ERR_GQA";
+    case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE";
+    case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED";
+    case PA_ERR_HIP: return "PA_ERR_HIP";
+    case PA_ERR_PARTITION: return "PA_ERR_PARTITION";
+  }
+  return "PA_UNKNOWN_STATUS";
+}
+
+int pa_kv_cache_write(const pa_kv_cache *cache, const void *key, const void *value,
+                      const int64_t *slot_mapping, int32_t num_tokens, void *stream) {
+  int st = check_cache(cache, false);
+  if (st) return st;
+  if (num_tokens < 0) return fail(PA_ERR_SHAPE, "num_tokens %d must be >= 0", num_tokens);
+  const int64_t row_bytes = (int64_t)cache->num_kv_heads * cache->head_dim * elem_bytes(cache->dtype);
+  if (row_bytes % 16)
+    return fail(PA_ERR_SHAPE, "num_kv_heads * head_dim * element size = %lld bytes is not a multiple of 16",
+                (long long)row_bytes);
+  if (row_bytes > (1 << 30)) return fail(PA_ERR_SHAPE, "row of %lld bytes too large", (long long)row_bytes);
+  if (num_tokens == 0) return ok();
+  if (!key || !value || !slot_mapping)
+    return fail(PA_ERR_NULL, "key=%p value=%p slot_mapping=%p: all must be device pointers", key, value,
+                (const void *)slot_mapping);
+  const int64_t num_slots = (int64_t)cache->num_blocks * cache->block_size;
+  hipError_t e = pa::launch_kv_cache_write(cache->k_cache, cache->v_cache, num_slots, (int)row_bytes, key,
+                                           value, slot_mapping, num_tokens, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "kv_cache_write launch");
+  return ok();
+}
+
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                 int32_t max_context_len, int32_t partition_size) {
+  return workspace_bytes(num_seqs, num_heads, head_dim, max_context_len, partition_size);
+}
+
+int pa_decode_partition(const pa_kv_cache *cache, void *out, const void *q, int32_t num_seqs,
+                        int32_t num_heads, const int32_t *block_tables, int32_t max_blocks_per_seq,
+                        const int32_t *context_lens, int32_t max_context_len, float scale,
+                        int32_t partition_size, void *workspace, size_t workspace_bytes,
+                        void *stream) {
+  pa::DecodeArgs a;
+  int st = prepare_decode(cache, out, q, num_seqs, num_heads, block_tables, max_blocks_per_seq,
+                          context_lens, max_context_len, scale, partition_size, workspace,
+                          workspace_bytes, &a);
+  if (st) return st;
+  if (num_seqs == 0) return ok();
+  hipError_t e = pa::launch_decode_partition(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "decode partition launch");
+  return ok();
+}
+
+int pa_decode_reduce(void *out, int32_t dtype, int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                     const int32_t *context_lens, int32_t max_context_len, int32_t partition_size,
+                     const void *workspace, size_t ws_bytes, void *stream) {
+  if (dtype != PA_DTYPE_F32 && dtype != PA_DTYPE_BF16)
+    return fail(PA_ERR_DTYPE, "dtype %d not in {0 (f32), 1 (bf16)}", dtype);
+  if (head_dim != 64 && head_dim != 128) return fail(PA_ERR_HEAD_DIM, "head_dim %d not in {64, 128}", head_dim);
+  if (num_seqs < 0 || num_seqs > kMaxGridYZ)
+    return fail(PA_ERR_SHAPE, "num_seqs %d not in [0, %d]", num_seqs, kMaxGridYZ);
+  if (num_heads <= 0 || num_heads > kMaxGridYZ)
+    return fail(PA_ERR_SHAPE, "num_heads %d not in [1, %d]", num_heads, kMaxGridYZ);
+  if (max_context_len < 0) return fail(PA_ERR_SHAPE, "max_context_len %d must be >= 0", max_context_len);
+  if (partition_size < 0) return fail(PA_ERR_PARTITION, "partition_size %d must be >= 0", partition_size);
+  const int P = num_partitions(max_context_len, partition_size);
+  if (num_seqs == 0 || P <= 1) return ok();
+  if (!out || !context_lens)
+    return fail(PA_ERR_NULL, "out=%p context_lens=%p: both must be device pointers", out,
+                (const void *)context_lens);
+  const size_t need = workspace_bytes(num_seqs, num_heads, head_dim, max_context_len, partition_size);
+  if (!workspace) return fail(PA_ERR_WORKSPACE, "workspace is NULL; %zu bytes needed", need);
+  if (ws_bytes < need) return fail(PA_ERR_WORKSPACE, "workspace_bytes %zu < %zu needed", ws_bytes, need);
+  pa::DecodeArgs a{};
+  a.cache.dtype = dtype;
+  a.cache.head_dim = head_dim;
+  a.cache.block_size = 1;  // unused by the reduce
+  a.cache.num_kv_heads = 1;
+  a.out = out;
+  a.num_seqs = num_seqs;
+  a.num_heads = num_heads;
+  a.context_lens = context_lens;
+  a.max_context_len = max_context_len;
+  a.max_blocks_per_seq = max_context_len;  // with block_size 1: no extra cap
+  a.partition_size = partition_size;
+  a.max_partitions = P;
+  const size_t n = (size_t)num_seqs * num_heads * P;
+  char *w = static_cast<char *>(const_cast<void *>(workspace));
+  a.ws_m = reinterpret_cast<float *>(w);
+  a.ws_l = reinterpret_cast<float *>(w + align256(n * sizeof(float)));
+  a.ws_o = reinterpret_cast<float *>(w + 2 * align256(n * sizeof(float)));
+  hipError_t e = pa::launch_decode_reduce(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "decode reduce launch");
+  return ok();
+}
+
+int pa_decode(const pa_kv_cache *cache, void *out, const void *q, int32_t num_seqs, int32_t num_heads,
+              const int32_t *block_tables, int32_t max_blocks_per_seq, const int32_t *context_lens,
+              int32_t max_context_len, float scale, int32_t partition_size, void *workspace,
+              size_t workspace_bytes, void *stream) {
+  pa::DecodeArgs a;
+  int st = prepare_decode(cache, out, q, num_seqs, num_heads, block_tables, max_blocks_per_seq,
+                          context_lens, max_context_len, scale, partition_size, workspace,
+                          workspace_bytes, &a);
+  if (st) return st;
+  if (num_seqs == 0) return ok();
+  hipError_t e = pa::launch_decode_partition(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "decode partition launch");
+  e = pa::launch_decode_reduce(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "decode reduce launch");
+  return ok();
+}
+
+int pa_prefill_chunk(const pa_kv_cache *cache, void *out, const void *q, const int32_t *query_start_loc,
+                     int32_t num_seqs, int32_t num_heads, int32_t num_query_tokens, int32_t max_query_len,
+                     const int32_t *block_tables, int32_t max_blocks_per_seq, const int32_t *context_lens,
+                     int32_t max_context_len, float scale, void *stream) {
+  int st = check_cache(cache, true);
+  if (st) return st;
+  if ((st = check_heads(cache, num_heads))) return st;
+  if (cache->dtype != PA_DTYPE_BF16)
+    return fail(PA_ERR_UNSUPPORTED, "prefill_chunk supports dtype 1 (bf16) only; got %d", cache->dtype);
+  if (num_seqs < 0 || num_seqs > kMaxGridYZ)
+    return fail(PA_ERR_SHAPE, "num_seqs %d not in [0, %d]", num_seqs, kMaxGridYZ);
+  if (num_query_tokens < 0) return fail(PA_ERR_SHAPE, "num_query_tokens %d must be >= 0", num_query_tokens);
+  if (max_query_len < 0) return fail(PA_ERR_SHAPE, "max_query_len %d must be >= 0", max_query_len);
+  if (max_blocks_per_seq <= 0)
+    return fail(PA_ERR_SHAPE, "max_blocks_per_seq %d must be > 0", max_blocks_per_seq);
+  if (max_context_len < 0) return fail(PA_ERR_SHAPE, "max_context_len %d must be >= 0", max_context_len);
+  if (!isfinite(scale)) return fail(PA_ERR_SHAPE, "scale %g is not finite", (double)scale);
+  if (num_seqs == 0 || num_query_tokens == 0 || max_query_len == 0) return ok();
+  if (!out || !q || !query_start_loc || !block_tables || !context_lens)
+    return fail(PA_ERR_NULL,
+                "out=%p q=%p query_start_loc=%p block_tables=%p context_lens=%p: all must be device pointers",
+                out, q, (const void *)query_start_loc, (const void *)block_tables, (const void *)context_lens);
+  pa::PrefillArgs a;
+  a.cache = {cache->k_cache, cache->v_cache, cache->num_blocks, cache->block_size,
+             cache->num_kv_heads, cache->head_dim, cache->dtype};
+  a.out = out;
+  a.q = q;
+  a.query_start_loc = query_start_loc;
+  a.num_seqs = num_seqs;
+  a.num_heads = num_heads;
+  a.num_query_tokens = num_query_tokens;
+  a.max_query_len = max_query_len;
+  a.block_tables = block_tables;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.context_lens = context_lens;
+  a.max_context_len = max_context_len;
+  a.scale = scale;
+  hipError_t e = pa::launch_prefill_chunk(a, (hipStream_t)stream);
+  if (e == hipErrorNotSupported)
+    return fail(PA_ERR_UNSUPPORTED, "prefill_chunk: head_dim %d with num_heads/num_kv_heads %d not built",
+                cache->head_dim, num_heads / cache->num_kv_heads);
+  if (e != hipSuccess) return hip_fail(e, "prefill_chunk launch");
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,174 @@
+// Internal helpers shared by the HIP kernels of the paged-attention library
+// (gfx950 / CDNA4, wave64).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+// ---------------------------------------------------------------- types
+struct bf16_t {
+  uint16_t bits;
+};
+
+template <typename T>
+struct ElemTraits;
+template <>
+struct ElemTraits<float> {
+  static constexpr int kBytes = 4;
+};
+template <>
+struct ElemTraits<bf16_t> {
+  static constexpr int kBytes = 2;
+};
+
+// bf16 <-> fp32.  Widening is exact (the bf16 bits are the high half of
+// the fp32 bits); narrowing rounds to nearest, ties to even, and keeps NaN
+// quiet.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;  // NaN
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// Widen a 16-byte chunk into floats.
+template <typename T>
+struct Chunk;
+template <>
+struct Chunk<float> {
+  static constexpr int kElems = 4;
+  __device__ __forceinline__ static void widen(const uint4 &c, float *f) {
+    f[0] = __uint_as_float(c.x);
+    f[1] = __uint_as_float(c.y);
+    f[2] = __uint_as_float(c.z);
+    f[3] = __uint_as_float(c.w);
+  }
+};
+template <>
+struct Chunk<bf16_t> {
+  static constexpr int kElems = 8;
+  __device__ __forceinline__ static void widen(const uint4 &c, float *f) {
+    f[0] = bf16_lo(c.x);
+    f[1] = bf16_hi(c.x);
+    f[2] = bf16_lo(c.y);
+    f[3] = bf16_hi(c.y);
+    f[4] = bf16_lo(c.z);
+    f[5] = bf16_hi(c.z);
+    f[6] = bf16_lo(c.w);
+    f[7] = bf16_hi(c.w);
+  }
+};
+
+// ------------------------------------------------------- lane exchanges
+// DPP controls (GCN/CDNA encoding).
+enum : int {
+  kDppQuadXor1 = 0xB1,     // quad_perm [1,0,3,2]
+  kDppQuadXor2 = 0x4E,     // quad_perm [2,3,0,1]
+  kDppRowRor4 = 0x124,     // row_ror:4  (lane i reads lane (i+4) mod 16 of its row)
+  kDppRowRor8 = 0x128,     // row_ror:8
+  kDppRowHalfMirror = 0x141,
+  kDppRowMirror = 0x140,
+};
+
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl, 0xF, 0xF, false));
+}
+
+// Sum over aligned groups of kLanes consecutive lanes (kLanes in
+// {1,2,4,8,16,32,64}); every lane of the group receives the group sum.
+template <int kLanes>
+__device__ __forceinline__ float group_sum(float x) {
+  if constexpr (kLanes >= 2) x += dpp_f32<kDppQuadXor1>(x);
+  if constexpr (kLanes >= 4) x += dpp_f32<kDppQuadXor2>(x);
+  if constexpr (kLanes == 8) x += dpp_f32<kDppRowHalfMirror>(x);
+  if constexpr (kLanes >= 16) {
+    x += dpp_f32<kDppRowRor4>(x);
+    x += dpp_f32<kDppRowRor8>(x);
+  }
+  if constexpr (kLanes >= 32) x += __shfl_xor(x, 16);
+  if constexpr (kLanes >= 64) x += __shfl_xor(x, 32);
+  return x;
+}
+
+// Combine a value across the lanes that share (lane % kLanes), i.e. across
+// the 64/kLanes groups of a wave.
+template <int kLanes>
+__device__ __forceinline__ float across_groups_max(float x) {
+  if constexpr (kLanes <= 8) x = fmaxf(x, __shfl_xor(x, 8));
+  if constexpr (kLanes <= 16) x = fmaxf(x, __shfl_xor(x, 16));
+  if constexpr (kLanes <= 32) x = fmaxf(x, __shfl_xor(x, 32));
+  return x;
+}
+template <int kLanes>
+__device__ __forceinline__ float across_groups_sum(float x) {
+  if constexpr (kLanes <= 8) x += __shfl_xor(x, 8);
+  if constexpr (kLanes <= 16) x += __shfl_xor(x, 16);
+  if constexpr (kLanes <= 32) x += __shfl_xor(x, 32);
+  return x;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+}  // namespace pa
+
+// ------------------------------------------------------------ launchers
+// Host-side launchers implemented next to their kernels.  Arguments are
+// already validated by the ABI layer.
+namespace pa {
+
+struct CacheView {
+  const void *k;
+  const void *v;
+  int num_blocks, block_size, num_kv_heads, head_dim, dtype;
+};
+
+hipError_t launch_kv_cache_write(void *k_cache, void *v_cache, int64_t num_slots, int row_bytes,
+                                 const void *key, const void *value, const int64_t *slots,
+                                 int num_tokens, hipStream_t stream);
+
+struct DecodeArgs {
+  CacheView cache;
+  void *out;
+  const void *q;
+  int num_seqs, num_heads;
+  const int32_t *block_tables;
+  int max_blocks_per_seq;
+  const int32_t *context_lens;
+  int max_context_len;
+  float scale;
+  int partition_size;      // > 0: tokens per partition (split-K); 0: single pass
+  int max_partitions;      // ceil(max_context_len / partition_size), >= 1
+  float *ws_m, *ws_l, *ws_o;
+};
+
+hipError_t launch_decode_partition(const DecodeArgs &a, hipStream_t stream);
+hipError_t launch_decode_reduce(const DecodeArgs &a, hipStream_t stream);
+
+struct PrefillArgs {
+  CacheView cache;
+  void *out;
+  const void *q;
+  const int32_t *query_start_loc;
+  int num_seqs, num_heads, num_query_tokens, max_query_len;
+  const int32_t *block_tables;
+  int max_blocks_per_seq;
+  const int32_t *context_lens;
+  int max_context_len;
+  float scale;
+};
+
+hipError_t launch_prefill_chunk(const PrefillArgs &a, hipStream_t stream);
+
+}  // namespace pa

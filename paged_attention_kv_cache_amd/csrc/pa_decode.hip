@@ -1,0 +1,414 @@
+// Paged decode attention: one query token per sequence against its whole
+// context in the block-table KV cache, with optional split-K
+// (flash-decoding) partitions and a reduce kernel.
+//
+// What is computed: TensorSharp, Mistral 3 page, section 3 "Forward graph".
+// The newest token's K/V are already in the cache; scores
+// s_p = scale * q.k_p for every context position p; softmax over p; the
+// weighted sum of V.  Query head h reads kv head h / G (GQA, section 4.1).
+// The paged layout and the online-softmax loop parallel over (sequence,
+// head) are from section 11 "Batched / paged forward".
+//
+// How it maps to gfx950:
+//  * One work-group (4 waves) per (partition, kv head, sequence).  It owns
+//    the G = num_heads / num_kv_heads query heads of that kv head, so each
+//    K/V byte of the partition is read from HBM exactly once for all G
+//    heads.
+//  * One token's K row for one kv head is head_dim contiguous elements
+//    (256 B for bf16 x 128), read by L = row_bytes / 16 lanes with one
+//    128-bit load each.  A wave covers 64 / L tokens per load instruction
+//    and keeps kUnroll loads of K and kUnroll loads of V in flight per
+//    lane.
+//  * The q.k partial sums are reduced across the L lanes of a row with DPP
+//    (quad permutes and row rotates), so no LDS traffic is needed.
+//  * Each wave runs its own online softmax over its chunks (running max m,
+//    running sum l, accumulator rescaled by 2^(m_old - m_new)).  Scores are
+//    kept in base-2 units: q is pre-multiplied by scale * log2(e), so that
+//    one v_exp_f32 gives each weight.  A token outside the context or in an
+//    invalid block is *selected out*: its score is -inf, its weight is
+//    exactly 0, and its V is never loaded, so stale or NaN pool contents
+//    cannot leak in.
+//  * The four waves merge (m, l, o) through LDS with the same rescaling
+//    rule.  A sequence that fits in one partition is normalised and stored
+//    directly.  Otherwise the partition's (m, l, o) go to the workspace and
+//    the reduce kernel merges the partitions.
+//  * The block id of each load is the same for the whole wave (a load
+//    covers 64 / L consecutive tokens inside one block), so block-table
+//    reads are scalar loads.
+#include "pa_common.h"
+
+namespace pa {
+
+template <typename T, int D>
+struct DecodeShape {
+  static constexpr int kElems = Chunk<T>::kElems;         // elements per 16-byte chunk
+  static constexpr int kLanesPerRow = D / kElems;         // lanes sharing one token row
+  static constexpr int kRowsPerWave = 64 / kLanesPerRow;  // tokens per load instruction
+  static constexpr int kUnroll = 8;                       // K (and V) loads in flight per lane
+  static constexpr int kChunk = kRowsPerWave * kUnroll;   // tokens per wave step
+  static constexpr int kWaves = 4;
+  static constexpr int kThreads = 64 * kWaves;
+  static_assert(kThreads == 256, "launch bounds assume 256 threads");
+  static_assert(kLanesPerRow >= 8 && kLanesPerRow <= 32, "unsupported row width");
+};
+
+struct DecodeKernelArgs {
+  void *out;
+  const void *q;
+  const void *k_cache;
+  const void *v_cache;
+  const int32_t *block_tables;
+  const int32_t *context_lens;
+  float *ws_m;
+  float *ws_l;
+  float *ws_o;
+  int num_heads;
+  int num_kv_heads;
+  int num_blocks;
+  int block_shift;       // log2(block_size)
+  int max_blocks_per_seq;
+  int ctx_cap;           // min(max_context_len, max_blocks_per_seq * block_size)
+  int partition_size;    // tokens per partition; 0 = whole context
+  int max_partitions;
+  float scale_log2;      // scale * log2(e)
+};
+
+__device__ __forceinline__ int decode_context(const DecodeKernelArgs &a, int seq) {
+  int ctx = a.context_lens[seq];
+  ctx = ctx < a.ctx_cap ? ctx : a.ctx_cap;
+  return ctx > 0 ? ctx : 0;
+}
+
+__device__ __forceinline__ int decode_num_partitions(const DecodeKernelArgs &a, int ctx) {
+  if (a.partition_size <= 0 || ctx <= 0) return 1;
+  return (ctx + a.partition_size - 1) / a.partition_size;
+}
+
+template <typename T>
+__device__ __forceinline__ void store_one(void *base, size_t idx, float v);
+template <>
+__device__ __forceinline__ void store_one<float>(void *base, size_t idx, float v) {
+  static_cast<float *>(base)[idx] = v;
+}
+template <>
+__device__ __forceinline__ void store_one<bf16_t>(void *base, size_t idx, float v) {
+  static_cast<uint16_t *>(base)[idx] = (uint16_t)f32_to_bf16_bits(v);
+}
+
+template <typename T, int D, int G>
+__global__ void __launch_bounds__(256)
+decode_partition_kernel(const DecodeKernelArgs a) {
+  using S = DecodeShape<T, D>;
+  constexpr int E = S::kElems;
+  constexpr int L = S::kLanesPerRow;
+  constexpr int R = S::kRowsPerWave;
+  constexpr int U = S::kUnroll;
+  constexpr int CH = S::kChunk;
+  constexpr int W = S::kWaves;
+
+  const int part = blockIdx.x;
+  const int kvh = blockIdx.y;
+  const int seq = blockIdx.z;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int row = lane / L;
+  const int col = lane % L;
+
+  const int ctx = decode_context(a, seq);
+  const int nparts = decode_num_partitions(a, ctx);
+  if (part >= nparts) return;
+  const int ps = a.partition_size > 0 ? a.partition_size : ctx;
+  const int p0 = part * ps;
+  const int p1 = min(ctx, p0 + ps);
+
+  // q of the G heads of this kv head, this lane's 16-byte slice of D,
+  // pre-multiplied by scale * log2(e).
+  float qf[G][E];
+  {
+    const uint4 *qv = reinterpret_cast<const uint4 *>(
+        static_cast<const T *>(a.q) + ((size_t)seq * a.num_heads + (size_t)kvh * G) * D);
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const uint4 c = qv[h * L + col];
+      Chunk<T>::widen(c, qf[h]);
+#pragma unroll
+      for (int e = 0; e < E; ++e) qf[h][e] *= a.scale_log2;
+    }
+  }
+
+  const size_t slot_stride = (size_t)a.num_kv_heads * D;  // elements between slots
+  const T *kbase = static_cast<const T *>(a.k_cache) + (size_t)kvh * D + col * E;
+  const T *vbase = static_cast<const T *>(a.v_cache) + (size_t)kvh * D + col * E;
+  const int32_t *bt = a.block_tables + (size_t)seq * a.max_blocks_per_seq;
+  const int bs_mask = (1 << a.block_shift) - 1;
+
+  float m_run[G], l_run[G], acc[G][E];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    m_run[h] = -INFINITY;
+    l_run[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[h][e] = 0.f;
+  }
+
+  const int ntok = p1 - p0;
+  const int nchunks = ntok > 0 ? (ntok + CH - 1) / CH : 0;
+  for (int c = wave; c < nchunks; c += W) {
+    const int cbase = p0 + c * CH;
+    uint4 kr[U], vr[U];
+    bool valid[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int tok0 = cbase + u * R;  // first token of this load, same for the wave
+      const int tok = tok0 + row;
+      int blk = -1;
+      if (tok0 < p1) blk = bt[tok0 >> a.block_shift];
+      valid[u] = (tok < p1) && ((unsigned)blk < (unsigned)a.num_blocks);
+      kr[u] = make_uint4(0, 0, 0, 0);
+      vr[u] = make_uint4(0, 0, 0, 0);
+      if (valid[u]) {
+        const size_t slot = ((size_t)blk << a.block_shift) + (tok & bs_mask);
+        kr[u] = *reinterpret_cast<const uint4 *>(kbase + slot * slot_stride);
+        vr[u] = *reinterpret_cast<const uint4 *>(vbase + slot * slot_stride);
+      }
+    }
+
+    // scores (base-2 units) for this lane's row token of every load
+    float s[U][G];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float kf[E];
+      Chunk<T>::widen(kr[u], kf);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float dot = 0.f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) dot = fmaf(qf[h][e], kf[e], dot);
+        dot = group_sum<L>(dot);
+        s[u][h] = valid[u] ? dot : -INFINITY;
+      }
+    }
+
+    // online softmax update over the chunk
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float cm = s[0][h];
+#pragma unroll
+      for (int u = 1; u < U; ++u) cm = fmaxf(cm, s[u][h]);
+      cm = across_groups_max<L>(cm);
+      const float m_new = fmaxf(m_run[h], cm);
+      const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run[h] - m_new);
+      m_run[h] = m_new;
+      l_run[h] *= alpha;
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[h][e] *= alpha;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float vf[E];
+      Chunk<T>::widen(vr[u], vf);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float p = valid[u] ? fast_exp2(s[u][h] - m_run[h]) : 0.f;
+        l_run[h] += p;
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[h][e] = fmaf(p, vf[e], acc[h][e]);
+      }
+    }
+  }
+
+  // sum the rows of the wave (m is already uniform over the wave)
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    l_run[h] = across_groups_sum<L>(l_run[h]);
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[h][e] = across_groups_sum<L>(acc[h][e]);
+  }
+
+  __shared__ float sm_m[W][G];
+  __shared__ float sm_l[W][G];
+  __shared__ float sm_o[W][G][D];
+  if (lane < L) {
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < E; ++e) sm_o[wave][h][col * E + e] = acc[h][e];
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      sm_m[wave][h] = m_run[h];
+      sm_l[wave][h] = l_run[h];
+    }
+  }
+  __syncthreads();
+
+  const bool direct = (nparts == 1);
+  for (int i = threadIdx.x; i < G * D; i += S::kThreads) {
+    const int h = i / D;
+    const int d = i - h * D;
+    float M = sm_m[0][h];
+#pragma unroll
+    for (int w = 1; w < W; ++w) M = fmaxf(M, sm_m[w][h]);
+    float o = 0.f, l = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < W; ++w) {
+        const float mw = sm_m[w][h];
+        const float f = (mw == -INFINITY) ? 0.f : fast_exp2(mw - M);
+        o = fmaf(sm_o[w][h][d], f, o);
+        l = fmaf(sm_l[w][h], f, l);
+      }
+    }
+    const int head = kvh * G + h;
+    if (direct) {
+      const float r = (l > 0.f) ? o / l : 0.f;
+      store_one<T>(a.out, ((size_t)seq * a.num_heads + head) * D + d, r);
+    } else {
+      const size_t idx = ((size_t)seq * a.num_heads + head) * a.max_partitions + part;
+      a.ws_o[idx * D + d] = o;
+      if (d == 0) {
+        a.ws_m[idx] = M;
+        a.ws_l[idx] = l;
+      }
+    }
+  }
+}
+
+// Merge the partitions of every multi-partition sequence:
+//   M = max_p m_p,  out = sum_p o_p 2^(m_p - M) / sum_p l_p 2^(m_p - M).
+// One work-group of 256 threads per (query head, sequence); thread t owns
+// dimension t % D of partitions t / D, t / D + 256 / D, ...
+template <typename T, int D>
+__global__ void __launch_bounds__(256)
+decode_reduce_kernel(const DecodeKernelArgs a) {
+  constexpr int kThreads = 256;
+  constexpr int kGroups = kThreads / D;
+  const int head = blockIdx.x;
+  const int seq = blockIdx.y;
+  const int ctx = decode_context(a, seq);
+  const int nparts = decode_num_partitions(a, ctx);
+  if (nparts <= 1) return;
+
+  const size_t base = ((size_t)seq * a.num_heads + head) * a.max_partitions;
+  __shared__ float sm_red[kThreads];
+  __shared__ float sm_o[kGroups][D];
+  __shared__ float sm_l[kGroups];
+
+  float mx = -INFINITY;
+  for (int p = threadIdx.x; p < nparts; p += kThreads) mx = fmaxf(mx, a.ws_m[base + p]);
+  sm_red[threadIdx.x] = mx;
+  __syncthreads();
+  for (int s = kThreads / 2; s > 0; s >>= 1) {
+    if ((int)threadIdx.x < s) sm_red[threadIdx.x] = fmaxf(sm_red[threadIdx.x], sm_red[threadIdx.x + s]);
+    __syncthreads();
+  }
+  const float M = sm_red[0];
+
+  const int d = threadIdx.x % D;
+  const int g = threadIdx.x / D;
+  float o = 0.f, l = 0.f;
+  if (M != -INFINITY) {
+    for (int p = g; p < nparts; p += kGroups) {
+      const float mp = a.ws_m[base + p];
+      const float f = (mp == -INFINITY) ? 0.f : fast_exp2(mp - M);
+      o = fmaf(a.ws_o[(base + p) * D + d], f, o);
+      l = fmaf(a.ws_l[base + p], f, l);
+    }
+  }
+  sm_o[g][d] = o;
+  if (d == 0) sm_l[g] = l;
+  __syncthreads();
+  if (g == 0) {
+    float ot = 0.f, lt = 0.f;
+#pragma unroll
+    for (int i = 0; i < kGroups; ++i) {
+      ot += sm_o[i][d];
+      lt += sm_l[i];
+    }
+    const float r = (lt > 0.f) ? ot / lt : 0.f;
+    store_one<T>(a.out, ((size_t)seq * a.num_heads + head) * D + d, r);
+  }
+}
+
+// ---------------------------------------------------------------- host
+static DecodeKernelArgs make_kernel_args(const DecodeArgs &a) {
+  DecodeKernelArgs k;
+  k.out = a.out;
+  k.q = a.q;
+  k.k_cache = a.cache.k;
+  k.v_cache = a.cache.v;
+  k.block_tables = a.block_tables;
+  k.context_lens = a.context_lens;
+  k.ws_m = a.ws_m;
+  k.ws_l = a.ws_l;
+  k.ws_o = a.ws_o;
+  k.num_heads = a.num_heads;
+  k.num_kv_heads = a.cache.num_kv_heads;
+  k.num_blocks = a.cache.num_blocks;
+  int shift = 0;
+  while ((1 << shift) < a.cache.block_size) ++shift;
+  k.block_shift = shift;
+  k.max_blocks_per_seq = a.max_blocks_per_seq;
+  const int64_t table_cap = (int64_t)a.max_blocks_per_seq * a.cache.block_size;
+  k.ctx_cap = (int)(table_cap < a.max_context_len ? table_cap : a.max_context_len);
+  k.partition_size = a.partition_size;
+  k.max_partitions = a.max_partitions;
+  k.scale_log2 = a.scale * kLog2e;
+  return k;
+}
+
+template <typename T, int D, int G>
+static hipError_t launch_partition_t(const DecodeArgs &a, hipStream_t stream) {
+  const DecodeKernelArgs k = make_kernel_args(a);
+  dim3 grid(a.max_partitions, a.cache.num_kv_heads, a.num_seqs);
+  hipLaunchKernelGGL((decode_partition_kernel<T, D, G>), grid, dim3(DecodeShape<T, D>::kThreads), 0,
+                     stream, k);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+static hipError_t launch_partition_g(const DecodeArgs &a, hipStream_t stream) {
+  switch (a.num_heads / a.cache.num_kv_heads) {
+    case 1: return launch_partition_t<T, D, 1>(a, stream);
+    case 2: return launch_partition_t<T, D, 2>(a, stream);
+    case 4: return launch_partition_t<T, D, 4>(a, stream);
+    case 8: return launch_partition_t<T, D, 8>(a, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename T>
+static hipError_t launch_partition_d(const DecodeArgs &a, hipStream_t stream) {
+  switch (a.cache.head_dim) {
+    case 64: return launch_partition_g<T, 64>(a, stream);
+    case 128: return launch_partition_g<T, 128>(a, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode_partition(const DecodeArgs &a, hipStream_t stream) {
+  if (a.num_seqs == 0) return hipSuccess;
+  if (a.cache.dtype == 1) return launch_partition_d<bf16_t>(a, stream);
+  return launch_partition_d<float>(a, stream);
+}
+
+template <typename T, int D>
+static hipError_t launch_reduce_t(const DecodeArgs &a, hipStream_t stream) {
+  const DecodeKernelArgs k = make_kernel_args(a);
+  dim3 grid(a.num_heads, a.num_seqs);
+  hipLaunchKernelGGL((decode_reduce_kernel<T, D>), grid, dim3(256), 0, stream, k);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_reduce(const DecodeArgs &a, hipStream_t stream) {
+  if (a.num_seqs == 0 || a.partition_size <= 0 || a.max_partitions <= 1) return hipSuccess;
+  const bool bf = (a.cache.dtype == 1);
+  switch (a.cache.head_dim) {
+    case 64: return bf ? launch_reduce_t<bf16_t, 64>(a, stream) : launch_reduce_t<float, 64>(a, stream);
+    case 128: return bf ? launch_reduce_t<bf16_t, 128>(a, stream) : launch_reduce_t<float, 128>(a, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pa

@@ -1,0 +1,224 @@
+"""pa_decode on the GPU against the CPU oracle: the five workloads at full
+size (sampled where the oracle would be slow), a sweep of shapes, the
+bit-exact index and leak probes, and edge cases."""
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from gpu_util import (DeviceCase, assert_close, log, oracle_decode, to_host_bits, to_host_f32,
+                      torch)
+
+pytestmark = pytest.mark.gpu
+
+BENCH_PARTITION = 256     # the split-K partition the benchmark times for the bs32 batch
+
+
+def _run(case, partition_size, max_context_len=None):
+    dev = DeviceCase(case)
+    dev.write()
+    out = dev.decode(partition_size, max_context_len=max_context_len)
+    torch().cuda.synchronize()
+    return dev, to_host_f32(out, case.dtype)
+
+
+def test_tiny_fp32_decode():
+    case = W.make_config("tiny_fp32_decode")
+    ref = oracle_decode(case)
+    for ps in (0, 16, 32, 48, 64, 512):
+        log(f"tiny fp32 decode partition={ps}")
+        _, got = _run(case, ps)
+        assert_close(got, ref, W.F32, f"partition {ps}")
+
+
+CTX_MIX = [1, 2, 7, 8, 9, 15, 16, 17, 31, 32, 33, 63, 64, 65, 100, 257, 700]
+
+
+@pytest.mark.parametrize("dtype,head_dim", [(W.BF16, 128), (W.BF16, 64), (W.F32, 64), (W.F32, 128)])
+@pytest.mark.parametrize("group", [1, 2, 4, 8])
+def test_decode_shapes(dtype, head_dim, group):
+    hkv = 2
+    for bs in (8, 16, 32):
+        case = W.random_decode(1000 * group + bs + head_dim, CTX_MIX, num_heads=hkv * group,
+                               num_kv_heads=hkv, head_dim=head_dim, block_size=bs, dtype=dtype,
+                               extra_table_cols=2)
+        ref = oracle_decode(case)
+        for ps in (0, bs, 4 * bs, 256):
+            log(f"decode {dtype} D={head_dim} G={group} bs={bs} partition={ps}")
+            _, got = _run(case, ps)
+            assert_close(got, ref, dtype, f"{dtype} D{head_dim} G{group} bs{bs} ps{ps}")
+
+
+@pytest.mark.parametrize("ps", [0, 512, BENCH_PARTITION])
+def test_decode_batch_bs32_full(ps):
+    case = W.make_config("decode_batch_bs32")
+    ref = oracle_decode(case)
+    log(f"decode batch 32 x U[512,4096] partition={ps}")
+    _, got = _run(case, ps)
+    mx, mean = assert_close(got, ref, W.BF16, f"bs32 batch ps{ps}")
+    print(f"bs32 batch ps={ps}: max-abs {mx:.2e} mean-abs {mean:.2e}")
+
+
+@pytest.mark.timeout(900)
+def test_long_context_split_k_full():
+    case = W.make_config("long_context_decode")
+    log(f"long-context decode ctx={case.context_lens.tolist()} partition=512")
+    _, got = _run(case, 512)
+    ref = oracle_decode(case)
+    mx, mean = assert_close(got, ref, W.BF16, "long context")
+    print(f"long context: max-abs {mx:.2e} mean-abs {mean:.2e} |o| mean {np.abs(ref).mean():.3f}")
+
+
+@pytest.mark.parametrize("name", ["prefix_shared_decode_bs8", "prefix_shared_decode_bs16"])
+def test_prefix_shared_full(name):
+    case = W.make_config(name)
+    ref = oracle_decode(case)
+    for ps in (0, 256):
+        log(f"{name} partition={ps}")
+        _, got = _run(case, ps)
+        assert_close(got, ref, W.BF16, f"{name} ps{ps}")
+
+
+def test_stages_equal_fused_call():
+    import paged_attention_kv_cache_amd as P
+    case = W.random_decode(77, [5, 300, 1000, 2049], num_heads=32, num_kv_heads=8, head_dim=128,
+                           block_size=32, dtype=W.BF16)
+    dev = DeviceCase(case)
+    dev.write()
+    t = torch()
+    ps = 128
+    need = P.pa_decode_workspace_bytes(4, 32, 128, case.max_context_len, ps)
+    ws = t.empty(need, dtype=t.uint8, device="cuda")
+    log("decode stages vs fused")
+    fused = dev.decode(ps, workspace=ws).clone()
+    out = t.empty_like(dev.q)
+    args = (dev.q, dev.k_cache, dev.v_cache, dev.block_tables, dev.context_lens, case.scale,
+            case.max_context_len, ps)
+    P.pa_decode_partition(*args, out=out, workspace=ws)
+    P.pa_decode_reduce(*args, out=out, workspace=ws)
+    t.cuda.synchronize()
+    assert np.array_equal(to_host_bits(out), to_host_bits(fused))
+
+
+def test_no_cross_sequence_leakage():
+    """Each sequence's output in a batch equals the same sequence run alone,
+    bit for bit (same kernel configuration)."""
+    t = torch()
+    case = W.random_decode(31, [40, 1, 513, 2000, 77], num_heads=32, num_kv_heads=8, head_dim=128,
+                           block_size=16, dtype=W.BF16)
+    dev = DeviceCase(case)
+    dev.write()
+    ps = 256
+    log("decode batch for leakage check")
+    full = to_host_bits(dev.decode(ps))
+    import paged_attention_kv_cache_amd as P
+    for i in range(case.num_seqs):
+        log(f"decode sequence {i} alone")
+        one = P.pa_decode(dev.q[i:i + 1].contiguous(), dev.k_cache, dev.v_cache,
+                          dev.block_tables[i:i + 1].contiguous(), dev.context_lens[i:i + 1].contiguous(),
+                          case.scale, case.max_context_len, ps)
+        t.cuda.synchronize()
+        assert np.array_equal(to_host_bits(one)[0], full[i]), f"sequence {i}"
+
+
+def _bf16(x):
+    return W.f32_to_bf16_bits(np.float32(x).reshape(1))[0]
+
+
+def _probe_case(seed, ctx, bs, num_seqs, targets, leak=False):
+    """Index probe: q = 40 e0 for every head; in sequence i every key has a
+    zero first component except the one at position targets[i], which is
+    40 e0.  Every score is exactly 0 but the target's (40^2 / sqrt(128) =
+    141 nats above), so every other weight underflows to exactly 0 and the
+    output is V[target] bit for bit.  With ``leak`` the slot just past the
+    context and every padding block hold keys 80 e0, four times the
+    target's score: any read of them shows up."""
+    case = W.random_decode(seed, [ctx] * num_seqs, num_heads=32, num_kv_heads=8, head_dim=128,
+                           block_size=bs, dtype=W.BF16, poison=not leak, extra_table_cols=1)
+    c40, c80, zero = _bf16(40.0), _bf16(80.0), np.uint16(0)
+    nb = case.num_blocks
+    kflat = case.k_cache.reshape(nb * bs, 8, 128)
+    kflat[case.slot_mapping] = case.new_key        # edit the real values of the new tokens too
+    for i in range(num_seqs):
+        row = case.block_tables[i]
+        for p in range(ctx):
+            s = int(row[p // bs]) * bs + p % bs
+            if p == targets[i]:
+                kflat[s] = zero
+                kflat[s, :, 0] = c40
+            else:
+                kflat[s, :, 0] = zero
+        if leak:
+            past = ctx  # first position outside the context
+            blk = int(row[past // bs])
+            s = blk * bs + past % bs
+            kflat[s] = zero
+            kflat[s, :, 0] = c80
+    if leak:
+        pad = case.pad_block
+        case.k_cache[pad] = zero
+        case.k_cache[pad, :, :, 0] = c80
+    # the new tokens carry the edited values; their slots stay poisoned
+    # until the write
+    case.new_key = kflat[case.slot_mapping].copy()
+    if not leak:
+        kflat[case.slot_mapping] = np.uint16(0x7FC0)
+    case.q[:] = zero
+    case.q[:, :, 0] = c40
+    return case
+
+
+@pytest.mark.parametrize("bs", [8, 16, 32])
+def test_index_probe_every_position(bs):
+    ctx = 3 * 64 + 5           # several partitions of 64 and a ragged tail
+    targets = list(range(ctx))
+    case = _probe_case(5 + bs, ctx, bs, ctx, targets)
+    vflat = W.storage_to_f32(case.v_cache, W.BF16).reshape(-1, 8, 128)
+    vnew = W.storage_to_f32(case.new_value, W.BF16)
+    for ps in (0, 64, 2 * bs):
+        log(f"index probe bs={bs} partition={ps}")
+        _, got = _run(case, ps)
+        for i, p in enumerate(targets):
+            s = int(case.block_tables[i, p // bs]) * bs + p % bs
+            v = vnew[i] if p == ctx - 1 else vflat[s]
+            exp = np.repeat(v, 4, axis=0)                  # head h reads kv head h // 4
+            assert np.array_equal(got[i], exp), f"bs{bs} ps{ps} target {p}"
+
+
+@pytest.mark.parametrize("bs", [8, 16, 32])
+def test_leak_probe_past_context(bs):
+    ctx = 2 * 32 + 3           # partial last block at every block size
+    targets = [(7 * i) % ctx for i in range(6)]
+    case = _probe_case(50 + bs, ctx, bs, 6, targets, leak=True)
+    vflat = W.storage_to_f32(case.v_cache, W.BF16).reshape(-1, 8, 128)
+    vnew = W.storage_to_f32(case.new_value, W.BF16)
+    for ps in (0, bs, 32):
+        log(f"leak probe bs={bs} partition={ps}")
+        _, got = _run(case, ps)
+        for i, p in enumerate(targets):
+            s = int(case.block_tables[i, p // bs]) * bs + p % bs
+            v = vnew[i] if p == ctx - 1 else vflat[s]
+            assert np.array_equal(got[i], np.repeat(v, 4, axis=0)), f"bs{bs} ps{ps} seq {i} leaked"
+
+
+def test_context_zero_and_one():
+    case = W.random_decode(9, [0, 1, 5], num_heads=8, num_kv_heads=2, head_dim=64, block_size=16,
+                           dtype=W.F32)
+    ref = oracle_decode(case)
+    for ps in (0, 16):
+        log(f"ctx 0/1 partition={ps}")
+        _, got = _run(case, ps)
+        assert np.array_equal(got[0], np.zeros_like(got[0]))
+        assert np.array_equal(got[1], np.repeat(W.storage_to_f32(case.new_value, W.F32)[1], 4, axis=0))
+        assert_close(got, ref, W.F32, f"ps{ps}")
+
+
+def test_loose_max_context_len():
+    """A host bound above the real maximum only adds empty partitions."""
+    case = W.random_decode(12, [100, 37], num_heads=16, num_kv_heads=4, head_dim=128, block_size=32,
+                           dtype=W.BF16, extra_table_cols=10)
+    ref = oracle_decode(case)
+    log("loose max_context_len")
+    _, got = _run(case, 32, max_context_len=400)
+    assert_close(got, ref, W.BF16, "loose bound")

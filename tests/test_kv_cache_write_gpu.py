@@ -1,0 +1,60 @@
+"""kv_cache_write on the GPU against the oracle's scatter: bit-exact, and every
+slot not named by the slot mapping left untouched (pools poisoned with NaN)."""
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from gpu_util import DeviceCase, log, to_host_bits, torch
+
+pytestmark = pytest.mark.gpu
+
+
+def _check_write(case, what):
+    log(f"kv_cache_write {what}: T={case.slot_mapping.size} pool={case.k_cache.shape} {case.dtype}")
+    dev = DeviceCase(case)
+    dev.write()
+    torch().cuda.synchronize()
+    k_ref, v_ref = oracle.kv_cache_write(case.k_cache, case.v_cache, case.new_key, case.new_value,
+                                         case.slot_mapping)
+    k_got, v_got = to_host_bits(dev.k_cache), to_host_bits(dev.v_cache)
+    bits = np.uint16 if case.dtype == W.BF16 else np.uint32
+    assert np.array_equal(k_got.view(bits), k_ref.view(bits)), f"{what}: K pool differs"
+    assert np.array_equal(v_got.view(bits), v_ref.view(bits)), f"{what}: V pool differs"
+
+
+def test_write_tiny_fp32_one_token():
+    _check_write(W.make_config("tiny_fp32_decode"), "tiny fp32, 1 token")
+
+
+@pytest.mark.parametrize("bs", [8, 16, 32])
+@pytest.mark.parametrize("dtype", [W.BF16, W.F32])
+def test_write_prefill_chunks(bs, dtype):
+    case = W.random_prefill(100 + bs, [0, 7, 33, 100], [5, 64, 31, 1], num_heads=8, num_kv_heads=2,
+                            head_dim=64, block_size=bs, dtype=dtype)
+    _check_write(case, f"prefill chunks bs{bs}")
+
+
+def test_write_skips_negative_and_out_of_pool_slots():
+    case = W.random_prefill(7, [3, 10], [9, 4], num_heads=4, num_kv_heads=4, head_dim=128,
+                            block_size=16, dtype=W.BF16)
+    sm = case.slot_mapping.copy()
+    sm[2] = -1
+    sm[5] = case.num_blocks * case.block_size          # one past the pool
+    sm[7] = case.num_blocks * case.block_size + 12345
+    case.slot_mapping = sm
+    log("kv_cache_write with skipped slots")
+    dev = DeviceCase(case)
+    dev.write()
+    torch().cuda.synchronize()
+    sm_oracle = sm.copy()
+    sm_oracle[sm_oracle >= case.num_blocks * case.block_size] = -1   # documented: skipped
+    k_ref, v_ref = oracle.kv_cache_write(case.k_cache, case.v_cache, case.new_key, case.new_value, sm_oracle)
+    assert np.array_equal(to_host_bits(dev.k_cache), k_ref)
+    assert np.array_equal(to_host_bits(dev.v_cache), v_ref)
+
+
+def test_write_chunked_prefill_full_size():
+    case = W.make_config("chunked_prefill")
+    _check_write(case, "chunked prefill 8 x 512")
