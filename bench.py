@@ -1,0 +1,342 @@
+"""Benchmark of the paged-attention hot path on one MI355X.
+
+A step is one decode step of the bs32 batch: ``pa_kv_cache_write`` of the
+32 new tokens, then ``pa_decode_partition`` and ``pa_decode_reduce`` over
+32 sequences with contexts uniform in [512, 4096] (32 q / 8 kv heads,
+head_dim 128, block_size 32, bf16).  Inputs are resident in HBM before
+timing starts.  Each step uses the next of R copies of the KV pool (about
+2 GB in total), so the 256 MB Infinity Cache cannot serve the KV from an
+earlier step.
+
+Prints one JSON line: throughput in tokens/s, the roofline of the decode
+partition kernel (its algorithmic bytes over its event-timed duration,
+against 8 TB/s), a secondary prefill-chunk measurement (MFMA fraction),
+and the CPU oracle timed on the host as a baseline.
+
+    python bench.py [--steps K] [--warmup W] [--partition P] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "paged decode tokens/s + achieved KV GB/s (% HBM peak), bs32 ctx4K GQA 32/8 bf16"
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
+BF16_DENSE_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--partition", type=int, default=256, help="split-K partition (tokens)")
+    ap.add_argument("--rotate-gb", type=float, default=2.0, help="total size of rotated KV pools")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    return ap.parse_args()
+
+
+def source_hash(*names) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "paged_attention_kv_cache_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(kernel_key: str, src_hash: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel source; else None."""
+    path = os.path.join(PROFILE_DIR, "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        data = json.load(open(path))
+        rec = data.get(kernel_key)
+        if rec and rec.get("source_hash") == src_hash:
+            return rec.get("hbm_bytes_per_launch")
+    except (OSError, ValueError):
+        return None
+    return None
+
+
+def to_dev(arr, dtype):
+    import torch
+    import workloads as W
+    if dtype == W.BF16:
+        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(arr)).cuda()
+
+
+def bench_decode(args):
+    import torch
+    import paged_attention_kv_cache_amd as P
+    import workloads as W
+
+    log("building the bs32 decode workload")
+    case = W.make_config("decode_batch_bs32", poison=False)
+    S, H, D = case.q.shape
+    kv_bytes = case.kv_bytes_logical()
+    pool_bytes = 2 * case.k_cache.nbytes
+    R = max(2, int(math.ceil(args.rotate_gb * 1e9 / pool_bytes)))
+    log(f"S={S} ctx sum={int(case.context_lens.sum())} KV={kv_bytes / 1e6:.1f} MB, "
+        f"pool={pool_bytes / 1e6:.1f} MB x {R} rotations")
+
+    k0 = to_dev(case.k_cache, case.dtype)
+    v0 = to_dev(case.v_cache, case.dtype)
+    pools = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(R - 1)]
+    q = to_dev(case.q, case.dtype)
+    new_k = to_dev(case.new_key, case.dtype)
+    new_v = to_dev(case.new_value, case.dtype)
+    slots = torch.from_numpy(case.slot_mapping).cuda()
+    bt = torch.from_numpy(case.block_tables).cuda()
+    cl = torch.from_numpy(case.context_lens).cuda()
+    out = torch.empty_like(q)
+    ps = args.partition
+    mcl = case.max_context_len
+    need = P.pa_decode_workspace_bytes(S, H, D, mcl, ps)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+
+    def step(r, ev=None):
+        k, v = pools[r]
+        if ev is not None:
+            ev[0].record()
+        P.pa_kv_cache_write(new_k, new_v, k, v, slots)
+        if ev is not None:
+            ev[1].record()
+        P.pa_decode_partition(q, k, v, bt, cl, case.scale, mcl, ps, out=out, workspace=ws)
+        if ev is not None:
+            ev[2].record()
+        P.pa_decode_reduce(q, k, v, bt, cl, case.scale, mcl, ps, out=out, workspace=ws)
+        if ev is not None:
+            ev[3].record()
+
+    log(f"warmup {args.warmup} steps")
+    for i in range(args.warmup):
+        step(i % R)
+    torch.cuda.synchronize()
+
+    # per-kernel durations: events around each launch, on the launch stream
+    log(f"timing {args.steps} steps")
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for i in range(args.steps):
+        step(i % R, evs[i])
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = start.elapsed_time(end)
+    ms_step = total_ms / args.steps
+    t_write = np.mean([e[0].elapsed_time(e[1]) for e in evs])
+    t_part = np.mean([e[1].elapsed_time(e[2]) for e in evs])
+    t_red = np.mean([e[2].elapsed_time(e[3]) for e in evs])
+
+    # the same steps without the interleaved events, for the headline
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        step(i % R)
+    end.record()
+    torch.cuda.synchronize()
+    ms_step_plain = start.elapsed_time(end) / args.steps
+
+    # algorithmic bytes of one decode partition launch: every context
+    # token's K and V row for all kv heads, q read once, the output (for
+    # single-partition sequences) or nothing else counted
+    q_bytes = case.q.nbytes
+    part_bytes = kv_bytes + q_bytes + case.context_lens.nbytes + int(
+        sum(-(-int(n) // case.block_size) for n in case.context_lens)) * 4
+    achieved = part_bytes / (t_part * 1e-3) / 1e9
+    src = source_hash("pa_decode.hip", "pa_common.h")
+    res = dict(
+        case=case, S=S, R=R, ms_step=ms_step_plain, ms_step_with_events=ms_step, wall=wall,
+        t_write=t_write, t_part=t_part, t_red=t_red, kv_bytes=kv_bytes, part_bytes=part_bytes,
+        achieved=achieved, src=src, ps=ps,
+    )
+    log(f"step {ms_step_plain * 1e3:.1f} us (events {ms_step * 1e3:.1f}); write {t_write * 1e3:.1f} us, "
+        f"partition {t_part * 1e3:.1f} us, reduce {t_red * 1e3:.1f} us; partition {achieved:.0f} GB/s")
+    del pools
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_prefill(args):
+    import torch
+    import paged_attention_kv_cache_amd as P
+    import workloads as W
+
+    case = W.make_config("chunked_prefill", poison=False)
+    k = to_dev(case.k_cache, case.dtype)
+    v = to_dev(case.v_cache, case.dtype)
+    q = to_dev(case.q, case.dtype)
+    qsl = torch.from_numpy(case.query_start_loc).cuda()
+    bt = torch.from_numpy(case.block_tables).cuda()
+    cl = torch.from_numpy(case.context_lens).cuda()
+    nk = to_dev(case.new_key, case.dtype)
+    nv = to_dev(case.new_value, case.dtype)
+    sm = torch.from_numpy(case.slot_mapping).cuda()
+    out = torch.empty_like(q)
+    P.pa_kv_cache_write(nk, nv, k, v, sm)
+
+    def run():
+        P.pa_prefill_chunk(q, qsl, k, v, bt, cl, case.scale, case.max_query_len, case.max_context_len,
+                           out=out)
+
+    try:
+        run()
+    except P.PagedAttnError as e:
+        if e.status == "PA_ERR_UNSUPPORTED":
+            return None
+        raise
+    for _ in range(5):
+        run()
+    torch.cuda.synchronize()
+    n = 50
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n)]
+    for i in range(n):
+        evs[i][0].record()
+        run()
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    t_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    # algorithmic FLOPs: 4 * D per visible (query, key) pair per query head
+    H, D = case.num_heads, case.head_dim
+    pairs = 0
+    for i, n_ctx in enumerate(case.context_lens.tolist()):
+        ql = int(case.query_lens[i])
+        prefix = n_ctx - ql
+        pairs += ql * prefix + ql * (ql + 1) // 2
+    flops = 4.0 * D * pairs * H
+    tflops = flops / (t_ms * 1e-3) / 1e12
+    return dict(us=t_ms * 1e3, tflops=tflops, frac=tflops / BF16_DENSE_PEAK_TFLOPS, flops=flops,
+                tokens_per_s=int(case.query_start_loc[-1]) / (t_ms * 1e-3),
+                src=source_hash("pa_prefill.hip", "pa_common.h"))
+
+
+def cpu_baseline(case, seconds):
+    """The oracle as it stands, on the host cores: write + decode steps of the
+    whole bs32 batch, repeated for about ``seconds``."""
+    import oracle
+    import workloads as W
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    q = W.storage_to_f32(case.q, case.dtype)
+    kf = W.storage_to_f32(case.k_cache, case.dtype)
+    vf = W.storage_to_f32(case.v_cache, case.dtype)
+    nk = W.storage_to_f32(case.new_key, case.dtype)
+    nv = W.storage_to_f32(case.new_value, case.dtype)
+    ctx_mgr = threadpool_limits(1) if threadpool_limits else None
+    steps, t0 = 0, time.perf_counter()
+    try:
+        while True:
+            k2, v2 = oracle.kv_cache_write(kf, vf, nk, nv, case.slot_mapping)
+            oracle.paged_decode(q, k2, v2, case.block_tables, case.context_lens, case.scale)
+            steps += 1
+            if time.perf_counter() - t0 >= seconds:
+                break
+    finally:
+        if ctx_mgr is not None:
+            ctx_mgr.__exit__(None, None, None)
+    dt = time.perf_counter() - t0
+    return dict(value=case.num_seqs * steps / dt, unit="tokens/s", cores=1, kind="oracle",
+                sample=f"{steps} whole write+decode steps of the bs32 batch ({case.num_seqs} sequences, "
+                       f"float64 oracle, 1 BLAS thread) in {dt:.1f} s")
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only; the decode and prefill kernels "
+                                   "are measured on a single MI355X (--gpus 1)"}))
+        sys.exit(2)
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    import paged_attention_kv_cache_amd as P
+    P.load_library()
+
+    dec = bench_decode(args)
+    pre = None if args.no_prefill else bench_prefill(args)
+    case = dec["case"]
+    tokens_per_s = dec["S"] / (dec["ms_step"] * 1e-3)
+    traffic = traffic_from_profiles("decode_partition", dec["src"])
+    line = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(dec["ms_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "bf16 paged decode batch: 32 sequences, context U[512,4096], 32 q / 8 kv heads, "
+                        "head_dim 128, block_size 32, pool 1.25x; step = kv_cache_write + decode "
+                        "partition + reduce",
+            "num_seqs": dec["S"],
+            "context_tokens": int(case.context_lens.sum()),
+            "block_size": case.block_size,
+            "partition_size": dec["ps"],
+            "kv_pool_rotations": dec["R"],
+        },
+        "kv_gbps": round(dec["achieved"], 1),
+        "kv_hbm_frac": round(dec["achieved"] / HBM_PEAK_GBPS, 4),
+        "roofline": {
+            "kernel": "decode_partition_kernel<bf16,128,4>",
+            "bound": "hbm",
+            "achieved": round(dec["achieved"], 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(dec["achieved"] / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": dec["part_bytes"],
+            "avg_launch_us": round(dec["t_part"] * 1e3, 2),
+        },
+        "kernel_us": {"kv_cache_write": round(dec["t_write"] * 1e3, 2),
+                      "decode_partition": round(dec["t_part"] * 1e3, 2),
+                      "decode_reduce": round(dec["t_red"] * 1e3, 2)},
+    }
+    if pre is not None:
+        line["prefill_chunk"] = {
+            "workload": "8 sequences x 512-token chunk over prefix U[0,3584], 32q/8kv, D128, BS32, bf16",
+            "us": round(pre["us"], 2), "tokens_per_s": round(pre["tokens_per_s"], 1),
+            "roofline": {"bound": "mfma", "achieved": round(pre["tflops"], 1), "peak": BF16_DENSE_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(pre["frac"], 4),
+                         "algorithmic_flops_per_launch": pre["flops"]},
+        }
+    if not args.no_cpu_baseline:
+        log(f"timing the CPU oracle for ~{args.cpu_seconds:.0f} s")
+        line["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -40,8 +40,8 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (set HIPCC or install ROCm)")
 
 
-def _compile(src: str, extra: list[str]) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+def _compile(src: str, extra: list[str], build_dir: str = BUILD) -> str:
+    obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
     cmd = [hipcc(), *COMMON_FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
@@ -51,20 +51,25 @@ def _compile(src: str, extra: list[str]) -> str:
     return obj
 
 
-def build(verbose: bool = False, extra_flags: list[str] | None = None) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = False, extra_flags: list[str] | None = None, out_path: str | None = None,
+          build_dir: str | None = None) -> str:
+    """Compile every source and link the library (default: in-tree next to
+    this file).  ``extra_flags`` go to every compile, e.g. ``-DNAME=value``."""
+    bdir = build_dir or BUILD
+    out = out_path or LIB_PATH
+    os.makedirs(bdir, exist_ok=True)
     extra = list(extra_flags or [])
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, extra), SOURCES))
-    tmp = LIB_PATH + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, extra, bdir), SOURCES))
+    tmp = out + ".tmp"
     cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"linking failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, out)
     if verbose:
-        print(f"built {LIB_PATH}", file=sys.stderr)
-    return LIB_PATH
+        print(f"built {out}", file=sys.stderr)
+    return out
 
 
 if __name__ == "__main__":

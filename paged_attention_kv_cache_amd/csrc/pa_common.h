@@ -117,6 +117,54 @@ __device__ __forceinline__ float across_groups_sum(float x) {
   return x;
 }
 
+// gfx950 lane swaps: permlane16_swap(x, x) yields the even and the odd
+// 16-lane row of each row pair, permlane32_swap(x, x) the two wave halves,
+// so one VALU op plus an add combines lanes l and l^16 (or l^32).
+__device__ __forceinline__ float xor16_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor16_max(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+// lane l reads lane l^4 (within 32-lane halves), through the LDS crossbar
+__device__ __forceinline__ float swizzle_xor4(float x) {
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x101F));
+}
+// every lane of a quad reads quad lane H
+template <int H>
+__device__ __forceinline__ float quad_bcast(float x) {
+  return dpp_f32<H * 0x55>(x);
+}
+
+// bf16 pair helpers: fp32 dot product of two bf16 pairs plus an fp32
+// addend (v_dot2_f32_bf16), and round-to-nearest-even packing of two floats
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c,
+                                         false);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2_rne(float lo, float hi) {
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+// (lo half of a, lo half of b) and (hi half of a, hi half of b)
+__device__ __forceinline__ uint32_t interleave_lo(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x05040100u);
+}
+__device__ __forceinline__ uint32_t interleave_hi(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x07060302u);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 constexpr float kLog2e = 1.4426950408889634f;

@@ -35,6 +35,8 @@
 //  * The block id of each load is the same for the whole wave (a load
 //    covers 64 / L consecutive tokens inside one block), so block-table
 //    reads are scalar loads.
+#include <type_traits>
+
 #include "pa_common.h"
 
 namespace pa {
@@ -275,15 +277,355 @@ decode_partition_kernel(const DecodeKernelArgs a) {
   }
 }
 
+// ------------------------------------------------------------------------
+// bf16 fast path (G in {1, 2, 4}).  Same decomposition and numerics as the
+// generic kernel above, with the per-token work cut down for the VALU:
+//  * q.k in bf16 pairs with v_dot2_f32_bf16 (products exact, fp32 sums), no
+//    widening of K;
+//  * a reduce-scatter across the row instead of an all-reduce: after it,
+//    lane c of a row holds the full score of head c % G only, so each lane
+//    computes one exponential per token;
+//  * P.V in bf16 pairs over two tokens: the weights of tokens t and t+1 are
+//    rounded to bf16 (nearest even) and paired, V elements of the two
+//    tokens are interleaved with v_perm_b32, and v_dot2_f32_bf16 adds both
+//    products to the fp32 accumulator.  The running sum l uses the fp32
+//    weights;
+//  * the K and V loads of a wave's next chunk are issued as soon as the
+//    registers of the current chunk are consumed, so they overlap the
+//    softmax and P.V work of the current chunk.
+#ifndef PA_DECODE_UNROLL
+#define PA_DECODE_UNROLL 8
+#endif
+
+// Reduce-scatter of G per-lane partial sums over a row of L lanes: lane c
+// returns the row total of head c % G (all lanes of the row with the same
+// c % G get the same value).
+template <int L, int G>
+__device__ __forceinline__ float row_scatter_sum(const float (&v)[G], int col) {
+  float r;
+  if constexpr (G == 4) {
+    const bool b0 = col & 1;
+    const bool b1 = (col >> 1) & 1;
+    float a = b0 ? v[1] : v[0];
+    float b = b0 ? v[3] : v[2];
+    const float sa = b0 ? v[0] : v[1];
+    const float sb = b0 ? v[2] : v[3];
+    a += dpp_f32<kDppQuadXor1>(sa);
+    b += dpp_f32<kDppQuadXor1>(sb);
+    const float keep = b1 ? b : a;
+    const float send = b1 ? a : b;
+    r = keep + dpp_f32<kDppQuadXor2>(send);
+  } else if constexpr (G == 2) {
+    const bool b0 = col & 1;
+    const float keep = b0 ? v[1] : v[0];
+    const float send = b0 ? v[0] : v[1];
+    r = keep + dpp_f32<kDppQuadXor1>(send);
+    r += dpp_f32<kDppQuadXor2>(r);
+  } else {
+    r = v[0];
+    r += dpp_f32<kDppQuadXor1>(r);
+    r += dpp_f32<kDppQuadXor2>(r);
+  }
+  if constexpr (L == 16) {
+    r += dpp_f32<kDppRowRor4>(r);
+    r += dpp_f32<kDppRowRor8>(r);
+  } else {
+    static_assert(L == 8, "rows of 8 or 16 lanes");
+    r += swizzle_xor4(r);
+  }
+  return r;
+}
+
+// max / sum of a value over the rows of a wave (lanes c, c+L, c+2L, ...)
+template <int L>
+__device__ __forceinline__ float rows_max(float x) {
+  if constexpr (L == 8) x = fmaxf(x, dpp_f32<kDppRowRor8>(x));
+  x = xor16_max(x);
+  return xor32_max(x);
+}
+template <int L>
+__device__ __forceinline__ float rows_sum(float x) {
+  if constexpr (L == 8) x += dpp_f32<kDppRowRor8>(x);
+  x = xor16_sum(x);
+  return xor32_sum(x);
+}
+
+// value of head H from the quad lane that owns it
+template <int G, int H>
+__device__ __forceinline__ float from_head(float x) {
+  if constexpr (G == 1) return x;
+  else return quad_bcast<H>(x);
+}
+
+// Addressing of one wave step.  Load u of chunk c covers the R tokens
+// tok0 .. tok0+R-1 (tok0 = chunk start + u*R), all in one block, so the
+// block id and the element offset of that token group are the same for the
+// whole wave and live in scalar registers.  A lane adds its own fixed byte
+// offset (its row times the slot stride plus its 16-byte column).
+template <int U, int R>
+__device__ __forceinline__ void chunk_rows(size_t (&off)[U], bool (&ok)[U], const int32_t *bt, int cbase,
+                                           int p1, int shift, int bs_mask, int num_blocks,
+                                           size_t slot_stride, int max_blocks) {
+  // table reads are unconditional (index clamped into the row) so that all
+  // of them are in flight together
+  int blk[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) blk[u] = bt[min((cbase + u * R) >> shift, max_blocks - 1)];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int tok0 = cbase + u * R;
+    ok[u] = (tok0 < p1) && ((unsigned)blk[u] < (unsigned)num_blocks);
+    off[u] = ok[u] ? (((size_t)blk[u] << shift) + (size_t)(tok0 & bs_mask)) * slot_stride : 0;  // 0: pool start
+  }
+}
+
+// Unconditional loads: a lane past the context still reads inside the
+// pool (its own row of the same block, or the first row of the pool when
+// the block id is invalid), and its values are discarded by selects.
+#ifndef PA_DECODE_PRIO
+#define PA_DECODE_PRIO 0
+#endif
+#ifndef PA_DECODE_NT
+#define PA_DECODE_NT 1
+#endif
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+
+template <int U>
+__device__ __forceinline__ void chunk_load(uint4 (&buf)[U], const size_t (&off)[U], const uint16_t *base,
+                                           uint32_t lane_bytes) {
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const char *ptr = reinterpret_cast<const char *>(base + off[u]) + lane_bytes;
+#if PA_DECODE_NT
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(ptr));
+    buf[u] = make_uint4(v.x, v.y, v.z, v.w);
+#else
+    buf[u] = *reinterpret_cast<const uint4 *>(ptr);
+#endif
+  }
+}
+
+template <int D, int G>
+__global__ void __launch_bounds__(256)
+decode_partition_bf16_kernel(const DecodeKernelArgs a) {
+  constexpr int L = D / 8;         // lanes per token row (8 bf16 per lane)
+  constexpr int R = 64 / L;        // token rows per load instruction
+  constexpr int U = PA_DECODE_UNROLL;
+  constexpr int CH = R * U;        // tokens per wave step
+  constexpr int W = 4;
+  static_assert(U % 2 == 0, "tokens are paired for the P.V dot products");
+
+  const int part = blockIdx.x;
+  const int kvh = blockIdx.y;
+  const int seq = blockIdx.z;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
+  const int row = lane / L;
+  const int col = lane % L;
+
+  const int ctx = decode_context(a, seq);
+  const int nparts = decode_num_partitions(a, ctx);
+  if (part >= nparts) return;
+  const int ps = a.partition_size > 0 ? a.partition_size : ctx;
+  const int p0 = part * ps;
+  const int p1 = min(ctx, p0 + ps);
+
+  uint32_t qp[G][4];
+  {
+    const uint4 *qv = reinterpret_cast<const uint4 *>(
+        static_cast<const uint16_t *>(a.q) + ((size_t)seq * a.num_heads + (size_t)kvh * G) * D);
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const uint4 c = qv[h * L + col];
+      qp[h][0] = c.x;
+      qp[h][1] = c.y;
+      qp[h][2] = c.z;
+      qp[h][3] = c.w;
+    }
+  }
+  const float sl = a.scale_log2;
+  const size_t slot_stride = (size_t)a.num_kv_heads * D;
+  const uint16_t *kbase = static_cast<const uint16_t *>(a.k_cache) + (size_t)kvh * D;
+  const uint16_t *vbase = static_cast<const uint16_t *>(a.v_cache) + (size_t)kvh * D;
+  const uint32_t lane_bytes = (uint32_t)(((size_t)row * slot_stride + (size_t)col * 8) * 2);
+  const int32_t *bt = a.block_tables + (size_t)seq * a.max_blocks_per_seq;
+  const int shift = a.block_shift;
+  const int bs_mask = (1 << shift) - 1;
+
+  float m = -INFINITY;  // running max of head col % G (base-2 units)
+  float l = 0.f;        // running sum of head col % G
+  float acc[G][8];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+
+  const int ntok = p1 - p0;
+  const int nchunks = ntok > 0 ? (ntok + CH - 1) / CH : 0;
+  for (int c = wave; c < nchunks; c += W) {
+    const int cbase = p0 + c * CH;
+    size_t off[U];
+    bool ok[U];
+    chunk_rows<U, R>(off, ok, bt, cbase, p1, shift, bs_mask, a.num_blocks, slot_stride,
+                     a.max_blocks_per_seq);
+    uint4 kr[U], vr[U];
+#if PA_DECODE_PRIO
+    __builtin_amdgcn_s_setprio(3);
+#endif
+    chunk_load<U>(kr, off, kbase, lane_bytes);
+    chunk_load<U>(vr, off, vbase, lane_bytes);
+#if PA_DECODE_PRIO
+    __builtin_amdgcn_s_setprio(0);
+#endif
+    bool valid[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) valid[u] = ok[u] && (cbase + u * R + row < p1);
+
+    float s[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float d[G];
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float t = dot2_bf16(qp[h][0], kr[u].x, 0.f);
+        t = dot2_bf16(qp[h][1], kr[u].y, t);
+        t = dot2_bf16(qp[h][2], kr[u].z, t);
+        d[h] = dot2_bf16(qp[h][3], kr[u].w, t);
+      }
+      const float r = row_scatter_sum<L, G>(d, col);
+      s[u] = valid[u] ? r * sl : -INFINITY;
+    }
+    float cm = s[0];
+#pragma unroll
+    for (int u = 1; u < U; ++u) cm = fmaxf(cm, s[u]);
+    cm = rows_max<L>(cm);
+    const float m_new = fmaxf(m, cm);
+    const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m - m_new);
+    m = m_new;
+    float p[U];
+    float psum = 0.f;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      p[u] = valid[u] ? fast_exp2(s[u] - m) : 0.f;
+      psum += p[u];
+    }
+    l = l * alpha + psum;
+
+    float ah[G];
+    if constexpr (G >= 1) ah[0] = from_head<G, 0>(alpha);
+    if constexpr (G >= 2) ah[1] = from_head<G, 1>(alpha);
+    if constexpr (G >= 4) {
+      ah[2] = from_head<G, 2>(alpha);
+      ah[3] = from_head<G, 3>(alpha);
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[h][e] *= ah[h];
+
+    // rows outside the context (or in an invalid block) may hold anything,
+    // NaN included: select them to zero so that weight 0 gives exactly 0
+    bool full = cbase + CH <= p1;
+#pragma unroll
+    for (int u = 0; u < U; ++u) full = full && ok[u];
+    if (!full) {
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (!valid[u]) vr[u] = make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < U; u += 2) {
+      uint32_t vp[8];
+      vp[0] = interleave_lo(vr[u].x, vr[u + 1].x);
+      vp[1] = interleave_hi(vr[u].x, vr[u + 1].x);
+      vp[2] = interleave_lo(vr[u].y, vr[u + 1].y);
+      vp[3] = interleave_hi(vr[u].y, vr[u + 1].y);
+      vp[4] = interleave_lo(vr[u].z, vr[u + 1].z);
+      vp[5] = interleave_hi(vr[u].z, vr[u + 1].z);
+      vp[6] = interleave_lo(vr[u].w, vr[u + 1].w);
+      vp[7] = interleave_hi(vr[u].w, vr[u + 1].w);
+      uint32_t pk[G];
+      if constexpr (G >= 1) pk[0] = pack_bf16x2_rne(from_head<G, 0>(p[u]), from_head<G, 0>(p[u + 1]));
+      if constexpr (G >= 2) pk[1] = pack_bf16x2_rne(from_head<G, 1>(p[u]), from_head<G, 1>(p[u + 1]));
+      if constexpr (G >= 4) {
+        pk[2] = pack_bf16x2_rne(from_head<G, 2>(p[u]), from_head<G, 2>(p[u + 1]));
+        pk[3] = pack_bf16x2_rne(from_head<G, 3>(p[u]), from_head<G, 3>(p[u + 1]));
+      }
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[h][e] = dot2_bf16(pk[h], vp[e], acc[h][e]);
+    }
+
+  }
+
+  // wave totals: sum the rows
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[h][e] = rows_sum<L>(acc[h][e]);
+  l = rows_sum<L>(l);
+
+  __shared__ float sm_m[W][G];
+  __shared__ float sm_l[W][G];
+  __shared__ float sm_o[W][G][D];
+  if (lane < L) {
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sm_o[wave][h][col * 8 + e] = acc[h][e];
+  }
+  if (lane < G) {  // lane c of row 0 owns head c
+    sm_m[wave][lane] = m;
+    sm_l[wave][lane] = l;
+  }
+  __syncthreads();
+
+  const bool direct = (nparts == 1);
+  for (int i = threadIdx.x; i < G * D; i += 256) {
+    const int h = i / D;
+    const int d = i - h * D;
+    float M = sm_m[0][h];
+#pragma unroll
+    for (int w = 1; w < W; ++w) M = fmaxf(M, sm_m[w][h]);
+    float o = 0.f, lt = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < W; ++w) {
+        const float mw = sm_m[w][h];
+        const float f = (mw == -INFINITY) ? 0.f : fast_exp2(mw - M);
+        o = fmaf(sm_o[w][h][d], f, o);
+        lt = fmaf(sm_l[w][h], f, lt);
+      }
+    }
+    const int head = kvh * G + h;
+    if (direct) {
+      const float r = (lt > 0.f) ? o / lt : 0.f;
+      store_one<bf16_t>(a.out, ((size_t)seq * a.num_heads + head) * D + d, r);
+    } else {
+      const size_t idx = ((size_t)seq * a.num_heads + head) * a.max_partitions + part;
+      a.ws_o[idx * D + d] = o;
+      if (d == 0) {
+        a.ws_m[idx] = M;
+        a.ws_l[idx] = lt;
+      }
+    }
+  }
+}
+
 // Merge the partitions of every multi-partition sequence:
 //   M = max_p m_p,  out = sum_p o_p 2^(m_p - M) / sum_p l_p 2^(m_p - M).
-// One work-group of 256 threads per (query head, sequence); thread t owns
-// dimension t % D of partitions t / D, t / D + 256 / D, ...
+// One work-group of 256 threads per (query head, sequence).  Thread t owns
+// four consecutive dimensions (one 16-byte load) of every partition
+// p = t / (D/4) (mod 256 / (D/4)); each thread keeps four partitions' loads
+// in flight.
 template <typename T, int D>
 __global__ void __launch_bounds__(256)
 decode_reduce_kernel(const DecodeKernelArgs a) {
   constexpr int kThreads = 256;
-  constexpr int kGroups = kThreads / D;
+  constexpr int kLanesPerPart = D / 4;               // float4 per lane
+  constexpr int kGroups = kThreads / kLanesPerPart;  // partitions per pass
+  constexpr int kUnroll = 4;
   const int head = blockIdx.x;
   const int seq = blockIdx.y;
   const int ctx = decode_context(a, seq);
@@ -292,7 +634,7 @@ decode_reduce_kernel(const DecodeKernelArgs a) {
 
   const size_t base = ((size_t)seq * a.num_heads + head) * a.max_partitions;
   __shared__ float sm_red[kThreads];
-  __shared__ float sm_o[kGroups][D];
+  __shared__ float4 sm_o[kGroups][kLanesPerPart];
   __shared__ float sm_l[kGroups];
 
   float mx = -INFINITY;
@@ -305,29 +647,55 @@ decode_reduce_kernel(const DecodeKernelArgs a) {
   }
   const float M = sm_red[0];
 
-  const int d = threadIdx.x % D;
-  const int g = threadIdx.x / D;
-  float o = 0.f, l = 0.f;
+  const int d4 = threadIdx.x % kLanesPerPart;
+  const int g = threadIdx.x / kLanesPerPart;
+  const float4 *o4 = reinterpret_cast<const float4 *>(a.ws_o);
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+  float l = 0.f;
   if (M != -INFINITY) {
-    for (int p = g; p < nparts; p += kGroups) {
-      const float mp = a.ws_m[base + p];
-      const float f = (mp == -INFINITY) ? 0.f : fast_exp2(mp - M);
-      o = fmaf(a.ws_o[(base + p) * D + d], f, o);
-      l = fmaf(a.ws_l[base + p], f, l);
+    for (int p0 = g; p0 < nparts; p0 += kGroups * kUnroll) {
+      float mp[kUnroll], lp[kUnroll];
+      float4 op[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int p = p0 + u * kGroups;
+        const bool in = p < nparts;
+        const size_t idx = base + (in ? p : 0);
+        mp[u] = in ? a.ws_m[idx] : -INFINITY;
+        lp[u] = in ? a.ws_l[idx] : 0.f;
+        op[u] = in ? o4[idx * (D / 4) + d4] : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const float f = (mp[u] == -INFINITY) ? 0.f : fast_exp2(mp[u] - M);
+        o.x = fmaf(op[u].x, f, o.x);
+        o.y = fmaf(op[u].y, f, o.y);
+        o.z = fmaf(op[u].z, f, o.z);
+        o.w = fmaf(op[u].w, f, o.w);
+        l = fmaf(lp[u], f, l);
+      }
     }
   }
-  sm_o[g][d] = o;
-  if (d == 0) sm_l[g] = l;
+  sm_o[g][d4] = o;
+  if (d4 == 0) sm_l[g] = l;
   __syncthreads();
   if (g == 0) {
-    float ot = 0.f, lt = 0.f;
+    float4 ot = make_float4(0.f, 0.f, 0.f, 0.f);
+    float lt = 0.f;
 #pragma unroll
     for (int i = 0; i < kGroups; ++i) {
-      ot += sm_o[i][d];
+      const float4 v = sm_o[i][d4];
+      ot.x += v.x;
+      ot.y += v.y;
+      ot.z += v.z;
+      ot.w += v.w;
       lt += sm_l[i];
     }
-    const float r = (lt > 0.f) ? ot / lt : 0.f;
-    store_one<T>(a.out, ((size_t)seq * a.num_heads + head) * D + d, r);
+    const size_t ob = ((size_t)seq * a.num_heads + head) * D + d4 * 4;
+    store_one<T>(a.out, ob + 0, lt > 0.f ? ot.x / lt : 0.f);
+    store_one<T>(a.out, ob + 1, lt > 0.f ? ot.y / lt : 0.f);
+    store_one<T>(a.out, ob + 2, lt > 0.f ? ot.z / lt : 0.f);
+    store_one<T>(a.out, ob + 3, lt > 0.f ? ot.w / lt : 0.f);
   }
 }
 
@@ -362,8 +730,12 @@ template <typename T, int D, int G>
 static hipError_t launch_partition_t(const DecodeArgs &a, hipStream_t stream) {
   const DecodeKernelArgs k = make_kernel_args(a);
   dim3 grid(a.max_partitions, a.cache.num_kv_heads, a.num_seqs);
-  hipLaunchKernelGGL((decode_partition_kernel<T, D, G>), grid, dim3(DecodeShape<T, D>::kThreads), 0,
-                     stream, k);
+  if constexpr (std::is_same<T, bf16_t>::value && G <= 4) {
+    hipLaunchKernelGGL((decode_partition_bf16_kernel<D, G>), grid, dim3(256), 0, stream, k);
+  } else {
+    hipLaunchKernelGGL((decode_partition_kernel<T, D, G>), grid, dim3(DecodeShape<T, D>::kThreads), 0,
+                       stream, k);
+  }
   return hipGetLastError();
 }
 

@@ -210,7 +210,7 @@ def test_context_zero_and_one():
         log(f"ctx 0/1 partition={ps}")
         _, got = _run(case, ps)
         assert np.array_equal(got[0], np.zeros_like(got[0]))
-        assert np.array_equal(got[1], np.repeat(W.storage_to_f32(case.new_value, W.F32)[1], 4, axis=0))
+        assert np.array_equal(got[1], np.repeat(W.storage_to_f32(case.new_value, W.F32)[0], 4, axis=0))
         assert_close(got, ref, W.F32, f"ps{ps}")
 
 

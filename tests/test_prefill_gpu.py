@@ -1,0 +1,144 @@
+"""pa_prefill_chunk on the GPU against the CPU oracle: the 8 x 512-token
+chunked-prefill workload at full size, a sweep of shapes and ragged
+chunks, bit-exact causal-boundary probes, and consistency with decode."""
+
+import numpy as np
+import pytest
+
+import workloads as W
+from gpu_util import DeviceCase, assert_close, log, oracle_decode, oracle_prefill, to_host_bits, to_host_f32, torch
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(case, max_context_len=None):
+    dev = DeviceCase(case)
+    dev.write()
+    out = dev.prefill(max_context_len=max_context_len)
+    torch().cuda.synchronize()
+    return dev, to_host_f32(out, case.dtype)
+
+
+def test_chunked_prefill_full():
+    case = W.make_config("chunked_prefill")
+    log(f"chunked prefill 8 x 512 over prefixes {(case.context_lens - 512).tolist()}")
+    _, got = _run(case)
+    ref = oracle_prefill(case)
+    mx, mean = assert_close(got, ref, W.BF16, "chunked prefill")
+    print(f"chunked prefill: max-abs {mx:.2e} mean-abs {mean:.2e}")
+
+
+PREFIXES = [0, 0, 5, 31, 32, 64, 100, 257]
+QLENS = [1, 64, 33, 1, 32, 95, 128, 200]
+
+
+@pytest.mark.parametrize("head_dim", [128, 64])
+@pytest.mark.parametrize("group", [1, 2, 4, 8])
+def test_prefill_shapes(head_dim, group):
+    hkv = 2
+    for bs in (8, 16, 32):
+        case = W.random_prefill(300 + 10 * group + bs + head_dim, PREFIXES, QLENS, num_heads=hkv * group,
+                                num_kv_heads=hkv, head_dim=head_dim, block_size=bs, dtype=W.BF16,
+                                extra_table_cols=2)
+        log(f"prefill D={head_dim} G={group} bs={bs}")
+        _, got = _run(case)
+        ref = oracle_prefill(case)
+        assert_close(got, ref, W.BF16, f"D{head_dim} G{group} bs{bs}")
+
+
+def test_prefill_empty_and_single_token_chunks():
+    case = W.random_prefill(7, [10, 0, 40, 3], [0, 1, 0, 5], num_heads=8, num_kv_heads=2, head_dim=128,
+                            block_size=16, dtype=W.BF16)
+    log("prefill with empty chunks")
+    _, got = _run(case)
+    ref = oracle_prefill(case)
+    assert_close(got, ref, W.BF16, "empty chunks")
+
+
+def test_prefill_chunk_of_one_matches_decode():
+    """A chunk of one token per sequence is a decode step."""
+    case = W.random_prefill(17, [0, 40, 511, 1000], [1, 1, 1, 1], num_heads=32, num_kv_heads=8,
+                            head_dim=128, block_size=32, dtype=W.BF16)
+    log("prefill q_len=1 vs decode")
+    dev, got = _run(case)
+    import paged_attention_kv_cache_amd as P
+    dec = P.pa_decode(dev.q, dev.k_cache, dev.v_cache, dev.block_tables, dev.context_lens, case.scale,
+                      case.max_context_len, 0)
+    torch().cuda.synchronize()
+    got_dec = to_host_f32(dec, W.BF16)
+    assert_close(got, got_dec, W.BF16, "prefill vs decode")
+    ref = oracle_prefill(case)
+    assert_close(got, ref, W.BF16, "prefill q_len=1")
+
+
+def test_prefill_no_cross_sequence_leakage():
+    import paged_attention_kv_cache_amd as P
+    t = torch()
+    case = W.random_prefill(23, [0, 300, 77], [100, 64, 130], num_heads=32, num_kv_heads=8, head_dim=128,
+                            block_size=16, dtype=W.BF16)
+    dev = DeviceCase(case)
+    dev.write()
+    log("prefill batch for leakage check")
+    full = to_host_bits(dev.prefill())
+    qsl = case.query_start_loc
+    for i in range(case.num_seqs):
+        r0, r1 = int(qsl[i]), int(qsl[i + 1])
+        log(f"prefill sequence {i} alone")
+        one = P.pa_prefill_chunk(dev.q[r0:r1].contiguous(), t.tensor([0, r1 - r0], dtype=t.int32, device="cuda"),
+                                 dev.k_cache, dev.v_cache, dev.block_tables[i:i + 1].contiguous(),
+                                 dev.context_lens[i:i + 1].contiguous(), case.scale, r1 - r0,
+                                 case.max_context_len)
+        t.cuda.synchronize()
+        assert np.array_equal(to_host_bits(one), full[r0:r1]), f"sequence {i}"
+
+
+def _bf16(x):
+    return W.f32_to_bf16_bits(np.float32(x).reshape(1))[0]
+
+
+@pytest.mark.parametrize("bs", [8, 16, 32])
+def test_prefill_causal_boundary_probe(bs):
+    """Every query is 40 e0; every key has a zero first component except a
+    target key at position 3 (visible to every chunk row: score gap 141
+    nats) and, in sequence i, a key 80 e0 at position prefix + t_i + 1 (four
+    times the target's score).  Rows t <= t_i must return V[3] bit for bit
+    (the big key is above their diagonal), rows t > t_i must return the big
+    key's V bit for bit (it is visible to them and dominates)."""
+    prefix, q_len = 40, 200
+    probe_rows = [0, 30, 31, 32, 63, 64, 100, 127, 128, q_len - 2]
+    S = len(probe_rows)
+    case = W.random_prefill(60 + bs, [prefix] * S, [q_len] * S, num_heads=32, num_kv_heads=8, head_dim=128,
+                            block_size=bs, dtype=W.BF16, poison=False)
+    c40, c80, zero = _bf16(40.0), _bf16(80.0), np.uint16(0)
+    nb = case.num_blocks
+    kflat = case.k_cache.reshape(nb * bs, 8, 128)
+    kflat[case.slot_mapping] = case.new_key
+    ctx = prefix + q_len
+    for i, ti in enumerate(probe_rows):
+        row = case.block_tables[i]
+        for p in range(ctx):
+            s = int(row[p // bs]) * bs + p % bs
+            kflat[s, :, 0] = zero
+            if p == 3:
+                kflat[s] = zero
+                kflat[s, :, 0] = c40
+            if p == prefix + ti + 1:
+                kflat[s] = zero
+                kflat[s, :, 0] = c80
+    case.new_key = kflat[case.slot_mapping].copy()
+    case.q[:] = zero
+    case.q[:, :, 0] = c40
+    log(f"prefill causal probe bs={bs}")
+    _, got = _run(case)
+    vflat = W.storage_to_f32(case.v_cache, W.BF16).reshape(-1, 8, 128)
+    vnew = W.storage_to_f32(case.new_value, W.BF16)
+    qsl = case.query_start_loc
+    for i, ti in enumerate(probe_rows):
+        row = case.block_tables[i]
+        s3 = int(row[3 // bs]) * bs + 3 % bs
+        v_target = vflat[s3]
+        big = prefix + ti + 1
+        v_big = vnew[int(qsl[i]) + (big - prefix)]       # the big key is one of the chunk's tokens
+        for t in range(q_len):
+            exp = np.repeat(v_target if t <= ti else v_big, 4, axis=0)
+            assert np.array_equal(got[int(qsl[i]) + t], exp), f"bs{bs} seq {i} (t_i={ti}) row {t}"
