@@ -51,6 +51,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first copy 1 GiB device-to-device (a kernel of known traffic for counter runs)")
     return ap.parse_args()
 
 
@@ -279,6 +281,12 @@ def main():
     import paged_attention_kv_cache_amd as P
     P.load_library()
 
+    if args.copy_calibration:
+        src = torch.ones(1 << 29, dtype=torch.bfloat16, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)          # 1 GiB read + 1 GiB written
+        torch.cuda.synchronize()
+        del src, dst
     dec = bench_decode(args)
     pre = None if args.no_prefill else bench_prefill(args)
     case = dec["case"]

@@ -296,6 +296,15 @@ decode_partition_kernel(const DecodeKernelArgs a) {
 #ifndef PA_DECODE_UNROLL
 #define PA_DECODE_UNROLL 8
 #endif
+#ifndef PA_DECODE_WAVES
+#define PA_DECODE_WAVES 4
+#endif
+// grid order of the partition kernel: 1 = kv head fastest, then sequence,
+// then partition, so that the partitions that exist for every sequence are
+// dispatched first and the empty ones (past short contexts) come last
+#ifndef PA_DECODE_ORDER
+#define PA_DECODE_ORDER 1
+#endif
 
 // Reduce-scatter of G per-lane partial sums over a row of L lanes: lane c
 // returns the row total of head c % G (all lanes of the row with the same
@@ -406,18 +415,24 @@ __device__ __forceinline__ void chunk_load(uint4 (&buf)[U], const size_t (&off)[
 }
 
 template <int D, int G>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(64 * PA_DECODE_WAVES)
 decode_partition_bf16_kernel(const DecodeKernelArgs a) {
   constexpr int L = D / 8;         // lanes per token row (8 bf16 per lane)
   constexpr int R = 64 / L;        // token rows per load instruction
   constexpr int U = PA_DECODE_UNROLL;
   constexpr int CH = R * U;        // tokens per wave step
-  constexpr int W = 4;
+  constexpr int W = PA_DECODE_WAVES;
   static_assert(U % 2 == 0, "tokens are paired for the P.V dot products");
 
+#if PA_DECODE_ORDER == 1
+  const int kvh = blockIdx.x;
+  const int seq = blockIdx.y;
+  const int part = blockIdx.z;
+#else
   const int part = blockIdx.x;
   const int kvh = blockIdx.y;
   const int seq = blockIdx.z;
+#endif
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
   const int row = lane / L;
@@ -582,7 +597,7 @@ decode_partition_bf16_kernel(const DecodeKernelArgs a) {
   __syncthreads();
 
   const bool direct = (nparts == 1);
-  for (int i = threadIdx.x; i < G * D; i += 256) {
+  for (int i = threadIdx.x; i < G * D; i += 64 * W) {
     const int h = i / D;
     const int d = i - h * D;
     float M = sm_m[0][h];
@@ -633,19 +648,19 @@ decode_reduce_kernel(const DecodeKernelArgs a) {
   if (nparts <= 1) return;
 
   const size_t base = ((size_t)seq * a.num_heads + head) * a.max_partitions;
-  __shared__ float sm_red[kThreads];
+  __shared__ float sm_max;
   __shared__ float4 sm_o[kGroups][kLanesPerPart];
   __shared__ float sm_l[kGroups];
 
-  float mx = -INFINITY;
-  for (int p = threadIdx.x; p < nparts; p += kThreads) mx = fmaxf(mx, a.ws_m[base + p]);
-  sm_red[threadIdx.x] = mx;
-  __syncthreads();
-  for (int s = kThreads / 2; s > 0; s >>= 1) {
-    if ((int)threadIdx.x < s) sm_red[threadIdx.x] = fmaxf(sm_red[threadIdx.x], sm_red[threadIdx.x + s]);
-    __syncthreads();
+  if (threadIdx.x < 64) {  // one wave finds M
+    float mx = -INFINITY;
+    for (int p = threadIdx.x; p < nparts; p += 64) mx = fmaxf(mx, a.ws_m[base + p]);
+#pragma unroll
+    for (int k = 1; k < 64; k <<= 1) mx = fmaxf(mx, __shfl_xor(mx, k));
+    if (threadIdx.x == 0) sm_max = mx;
   }
-  const float M = sm_red[0];
+  __syncthreads();
+  const float M = sm_max;
 
   const int d4 = threadIdx.x % kLanesPerPart;
   const int g = threadIdx.x / kLanesPerPart;
@@ -731,7 +746,10 @@ static hipError_t launch_partition_t(const DecodeArgs &a, hipStream_t stream) {
   const DecodeKernelArgs k = make_kernel_args(a);
   dim3 grid(a.max_partitions, a.cache.num_kv_heads, a.num_seqs);
   if constexpr (std::is_same<T, bf16_t>::value && G <= 4) {
-    hipLaunchKernelGGL((decode_partition_bf16_kernel<D, G>), grid, dim3(256), 0, stream, k);
+#if PA_DECODE_ORDER == 1
+    grid = dim3(a.cache.num_kv_heads, a.num_seqs, a.max_partitions);
+#endif
+    hipLaunchKernelGGL((decode_partition_bf16_kernel<D, G>), grid, dim3(64 * PA_DECODE_WAVES), 0, stream, k);
   } else {
     hipLaunchKernelGGL((decode_partition_kernel<T, D, G>), grid, dim3(DecodeShape<T, D>::kThreads), 0,
                        stream, k);

@@ -9,8 +9,9 @@
 // shapes of the scheduling section of the mistral.rs comparison page.
 //
 // How it maps to gfx950:
-//  * A work-group (4 waves) serves one kv head: its G query heads (4 at
-//    most per work-group) x 32-token query groups of one sequence's chunk.
+//  * A work-group (8 waves) serves one kv head: its G query heads (8 at
+//    most) x 32-token query groups of one sequence's chunk (64 tokens for
+//    G = 4).
 //    Every K/V tile is gathered once per work-group and shared by all of
 //    its query heads through LDS.
 //  * K/V tiles of 64 keys are gathered through the block table (one 16-byte
@@ -27,6 +28,11 @@
 //    O^T += V^T P^T (A = V^T from LDS), so P never goes through LDS.
 //  * The causal mask (bottom-right aligned) is applied only on tiles that
 //    cross the diagonal of the wave's 32 queries, by selecting -inf.
+//  * LDS holds two K/V tiles: the next tile's global loads are in flight
+//    while the current tile is multiplied, and are stored to the other
+//    buffer afterwards, so each tile costs one barrier.
+//  * The output is rescaled only when a query's max grows by more than 2^8
+//    (the final division by the running sum makes any reference max exact).
 //  * Work ids are remapped so that the query tiles of one (sequence, kv
 //    head), which read the same K/V, land on the same XCD and share its L2.
 //    Tiles with more keys (later in the chunk) are dispatched first.
@@ -67,22 +73,128 @@ __device__ __forceinline__ bf16x8_t pack8(const f32x16_t &s, int base) {
   return r;
 }
 
+// Gather of one K/V tile (keys k0 .. k0+63) from the pool into registers.
+// The tile's block ids come from a small LDS array filled ahead of time, so
+// no load waits on a block-table read.  Each lane's loads have fixed
+// (key, column) slots:
+//   K: chunk i = tid + 512 j is key i / C16, 16-byte column i % C16 (whole
+//      rows coalesced);
+//   V: a lane takes keys 2p, 2p+1 (same block) of one column chunk so that
+//      it can write (V[2p][d], V[2p+1][d]) dword pairs of the transposed tile.
+// Loads are unconditional: a key at or past kend, or in an invalid block,
+// reads the first row of the pool instead and is zeroed when stored.
+constexpr int kPrefillThreads = 512;  // 8 waves
+
+template <int D>
+struct TileRegs {
+  static constexpr int C16 = D / 8;
+  static constexpr int NK = (64 * C16 + kPrefillThreads - 1) / kPrefillThreads;  // K chunks per thread
+  static constexpr int NV = (32 * C16 + kPrefillThreads - 1) / kPrefillThreads;  // V key pairs per thread
+  uint4 k[NK];
+  uint4 va[NV], vb[NV];
+  bool kok[NK], vaok[NV], vbok[NV];
+};
+
+constexpr int kMaxTileBlocks = 8;  // 64 keys / smallest block size
+
+// block ids of the tile starting at key k0 (64 / block_size entries); the
+// work-group keeps them in a tiny LDS array, filled two tiles ahead
+__device__ __forceinline__ int tile_block_id(const int32_t *bt, int k0, int j, int shift, int max_blocks) {
+  return bt[min((k0 >> shift) + j, max_blocks - 1)];
+}
+
+template <int D>
+__device__ __forceinline__ void tile_load(TileRegs<D> &r, const int *ids, const uint16_t *kbase,
+                                          const uint16_t *vbase, int k0, int kend, int shift, int bs_mask,
+                                          int num_blocks, size_t slot_stride, int tid) {
+  constexpr int C16 = D / 8;
+#pragma unroll
+  for (int j = 0; j < TileRegs<D>::NK; ++j) {
+    const int i = tid + kPrefillThreads * j;
+    const int key = (i / C16) & 63;
+    const int blk = ids[key >> shift];
+    const bool ok = (i < 64 * C16) && (k0 + key < kend) && ((unsigned)blk < (unsigned)num_blocks);
+    const size_t slot = ok ? ((size_t)blk << shift) + (size_t)((k0 + key) & bs_mask) : 0;
+    r.k[j] = *reinterpret_cast<const uint4 *>(kbase + slot * slot_stride + (i % C16) * 8);
+    r.kok[j] = ok;
+  }
+#pragma unroll
+  for (int j = 0; j < TileRegs<D>::NV; ++j) {
+    const int i = tid + kPrefillThreads * j;
+    const int key = 2 * (i % 32);
+    const int c = (i / 32) % C16;
+    const int blk = ids[key >> shift];  // keys 2p and 2p+1 share a block
+    const bool inb = (i < 32 * C16) && ((unsigned)blk < (unsigned)num_blocks);
+    const bool oka = inb && (k0 + key < kend);
+    const bool okb = inb && (k0 + key + 1 < kend);
+    const size_t slot = oka ? ((size_t)blk << shift) + (size_t)((k0 + key) & bs_mask) : 0;
+    const uint16_t *src = vbase + slot * slot_stride + c * 8;
+    r.va[j] = *reinterpret_cast<const uint4 *>(src);
+    r.vb[j] = *reinterpret_cast<const uint4 *>(src + (oka ? slot_stride : 0));
+    r.vaok[j] = oka;
+    r.vbok[j] = okb;
+  }
+}
+
+// component-wise (a ?: 0); a select on the vector objects themselves would
+// pick between their addresses and force both into scratch memory
+__device__ __forceinline__ uint4 keep_if(bool ok, const uint4 &v) {
+  return make_uint4(ok ? v.x : 0u, ok ? v.y : 0u, ok ? v.z : 0u, ok ? v.w : 0u);
+}
+
+template <int D, int KSTR, int VSTR>
+__device__ __forceinline__ void tile_store(const TileRegs<D> &r, uint16_t *sk, uint16_t *svt, int tid) {
+  constexpr int C16 = D / 8;
+#pragma unroll
+  for (int j = 0; j < TileRegs<D>::NK; ++j) {
+    const int i = tid + kPrefillThreads * j;
+    if (i < 64 * C16)
+      *reinterpret_cast<uint4 *>(sk + (i / C16) * KSTR + (i % C16) * 8) = keep_if(r.kok[j], r.k[j]);
+  }
+#pragma unroll
+  for (int j = 0; j < TileRegs<D>::NV; ++j) {
+    const int i = tid + kPrefillThreads * j;
+    if (i < 32 * C16) {
+      const int p = i % 32;
+      const int c = i / 32;
+      uint32_t *dst = reinterpret_cast<uint32_t *>(svt + (c * 8) * VSTR + 2 * p);
+      constexpr int W = VSTR / 2;  // dwords per V^T row
+      const uint4 a = keep_if(r.vaok[j], r.va[j]);
+      const uint4 b = keep_if(r.vbok[j], r.vb[j]);
+      dst[0 * W] = interleave_lo(a.x, b.x);
+      dst[1 * W] = interleave_hi(a.x, b.x);
+      dst[2 * W] = interleave_lo(a.y, b.y);
+      dst[3 * W] = interleave_hi(a.y, b.y);
+      dst[4 * W] = interleave_lo(a.z, b.z);
+      dst[5 * W] = interleave_hi(a.z, b.z);
+      dst[6 * W] = interleave_lo(a.w, b.w);
+      dst[7 * W] = interleave_hi(a.w, b.w);
+    }
+  }
+}
+
+// a rescale of O is done only when a query's running max grows by more than
+// this many base-2 units; until then the weights may exceed 1 by up to 2^8,
+// which the fp32 accumulators and the bf16 weights carry exactly as well
+constexpr float kRescaleSlack = 8.f;
+
 template <int D, int G>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(kPrefillThreads)
 prefill_chunk_kernel(const PrefillKernelArgs a) {
-  constexpr int GW = G < 4 ? G : 4;  // query heads per work-group
-  constexpr int HALVES = G / GW;     // work-groups per kv head along heads
-  constexpr int TG = 4 / GW;         // 32-token query groups per work-group
+  constexpr int NW = kPrefillThreads / 64;
+  constexpr int GW = G < NW ? G : NW;  // query heads per work-group
+  constexpr int HALVES = G / GW;       // work-groups per kv head along heads
+  constexpr int TG = NW / GW;          // 32-token query groups per work-group
   constexpr int QT = 32 * TG;        // query tokens per work-group
   constexpr int KT = 64;             // keys per tile
   constexpr int KSTR = D + 8;        // LDS row stride of K, bf16 elements
   constexpr int VSTR = KT + 8;       // LDS row stride of V^T, bf16 elements
   constexpr int NDS = D / 16;        // k-steps of Q K^T
   constexpr int NDT = D / 32;        // 32-row tiles of O^T
-  constexpr int C16 = D / 8;         // 16-byte chunks per K/V row
 
-  __shared__ __attribute__((aligned(16))) uint16_t sk[KT * KSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t svt[D * VSTR];
+  // two buffers: the next tile is stored while the current one is used
+  __shared__ __attribute__((aligned(16))) uint16_t sk[2][KT * KSTR];
+  __shared__ __attribute__((aligned(16))) uint16_t svt[2][D * VSTR];
 
   // work id: consecutive ids share a (sequence, kv head) and sit on one XCD
   const int nwg = gridDim.x;  // a multiple of 8
@@ -142,7 +254,7 @@ prefill_chunk_kernel(const PrefillKernelArgs a) {
   const int bs_mask = (1 << shift) - 1;
   const float sl = a.scale_log2;
 
-  float m = -INFINITY;  // running max of this lane's query (base-2 units)
+  float m = -INFINITY;  // reference max of this lane's query (base-2 units)
   float l = 0.f;        // running sum over this lane's keys
   f32x16_t o[NDT];
 #pragma unroll
@@ -150,58 +262,32 @@ prefill_chunk_kernel(const PrefillKernelArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
 
+  // tile 0 goes straight to LDS.  Block ids: sid[b] holds the ids of the
+  // tile whose loads are issued next from it; threads 0..7 fetch the ids of
+  // the tile after that while the current tile is multiplied.
+  __shared__ int sid[2][kMaxTileBlocks];
+  if (tid < kMaxTileBlocks) {
+    sid[0][tid] = tile_block_id(bt, 0, tid, shift, a.max_blocks_per_seq);
+    sid[1][tid] = tile_block_id(bt, KT, tid, shift, a.max_blocks_per_seq);
+  }
+  __syncthreads();
+  TileRegs<D> tr;
+  tile_load<D>(tr, sid[0], kbase, vbase, 0, kend, shift, bs_mask, a.num_blocks, slot_stride, tid);
+  tile_store<D, KSTR, VSTR>(tr, sk[0], svt[0], tid);
+  __syncthreads();
+
   for (int kt = 0; kt < ntiles; ++kt) {
     const int k0 = kt * KT;
-    // K tile, row-major: C16 lanes per key row, whole rows coalesced
-#pragma unroll
-    for (int j = 0; j < KT * C16 / 256; ++j) {
-      const int i = tid + 256 * j;
-      const int key = i / C16;
-      const int c = i % C16;
-      const int kpos = k0 + key;
-      uint4 val = make_uint4(0, 0, 0, 0);
-      if (kpos < kend) {
-        const int blk = bt[kpos >> shift];
-        if ((unsigned)blk < (unsigned)a.num_blocks)
-          val = *reinterpret_cast<const uint4 *>(
-              kbase + ((size_t)(blk << shift) + (size_t)(kpos & bs_mask)) * slot_stride + c * 8);
-      }
-      *reinterpret_cast<uint4 *>(sk + key * KSTR + c * 8) = val;
-    }
-    // V tile, transposed: a lane takes keys 2p and 2p+1 of one 16-byte
-    // column chunk and writes (V[2p][d], V[2p+1][d]) pairs as dwords
-#pragma unroll
-    for (int j = 0; j < 32 * C16 / 256; ++j) {
-      const int i = tid + 256 * j;
-      const int p = i % 32;
-      const int c = i / 32;
-      const int ka = k0 + 2 * p;
-      uint4 va = make_uint4(0, 0, 0, 0), vb = make_uint4(0, 0, 0, 0);
-      if (ka < kend) {
-        const int blk = bt[ka >> shift];
-        if ((unsigned)blk < (unsigned)a.num_blocks)
-          va = *reinterpret_cast<const uint4 *>(
-              vbase + ((size_t)(blk << shift) + (size_t)(ka & bs_mask)) * slot_stride + c * 8);
-      }
-      if (ka + 1 < kend) {
-        const int blk = bt[(ka + 1) >> shift];
-        if ((unsigned)blk < (unsigned)a.num_blocks)
-          vb = *reinterpret_cast<const uint4 *>(
-              vbase + ((size_t)(blk << shift) + (size_t)((ka + 1) & bs_mask)) * slot_stride + c * 8);
-      }
-      uint32_t *dst = reinterpret_cast<uint32_t *>(svt + (c * 8) * VSTR + 2 * p);
-      constexpr int kRowWords = VSTR / 2;
-      dst[0 * kRowWords] = interleave_lo(va.x, vb.x);
-      dst[1 * kRowWords] = interleave_hi(va.x, vb.x);
-      dst[2 * kRowWords] = interleave_lo(va.y, vb.y);
-      dst[3 * kRowWords] = interleave_hi(va.y, vb.y);
-      dst[4 * kRowWords] = interleave_lo(va.z, vb.z);
-      dst[5 * kRowWords] = interleave_hi(va.z, vb.z);
-      dst[6 * kRowWords] = interleave_lo(va.w, vb.w);
-      dst[7 * kRowWords] = interleave_hi(va.w, vb.w);
-    }
-    __syncthreads();
+    const int buf = kt & 1;
+    // next tile's loads are in flight during this tile's products (past the
+    // last tile they read only in-pool rows that are zeroed)
+    tile_load<D>(tr, sid[(kt + 1) & 1], kbase, vbase, k0 + KT, kend, shift, bs_mask, a.num_blocks, slot_stride,
+                 tid);
+    int next_id = 0;
+    if (tid < kMaxTileBlocks) next_id = tile_block_id(bt, k0 + 2 * KT, tid, shift, a.max_blocks_per_seq);
 
+    const uint16_t *skb = sk[buf];
+    const uint16_t *svb = svt[buf];
     // S^T = K Q^T for keys k0 .. k0+31 (s0) and k0+32 .. k0+63 (s1)
     f32x16_t s0, s1;
 #pragma unroll
@@ -211,47 +297,48 @@ prefill_chunk_kernel(const PrefillKernelArgs a) {
     }
 #pragma unroll
     for (int ds = 0; ds < NDS; ++ds) {
-      const bf16x8_t a0 = *reinterpret_cast<const bf16x8_t *>(sk + col * KSTR + ds * 16 + hh * 8);
-      const bf16x8_t a1 = *reinterpret_cast<const bf16x8_t *>(sk + (32 + col) * KSTR + ds * 16 + hh * 8);
+      const bf16x8_t a0 = *reinterpret_cast<const bf16x8_t *>(skb + col * KSTR + ds * 16 + hh * 8);
+      const bf16x8_t a1 = *reinterpret_cast<const bf16x8_t *>(skb + (32 + col) * KSTR + ds * 16 + hh * 8);
       s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qb[ds], s0, 0, 0, 0);
       s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qb[ds], s1, 0, 0, 0);
     }
 
-    // scale; causal mask on tiles that cross this wave's diagonal.
-    // Accumulator register r of this lane holds key 8*(r/4) + 4*hh + r%4.
-    const bool diag = k0 + KT - 1 > prefix + tw0;
-    float tmax = -INFINITY;
+    // causal mask on tiles that cross this wave's diagonal (raw scores;
+    // register r of this lane holds key 8*(r/4) + 4*hh + r%4)
+    if (k0 + KT - 1 > prefix + tw0) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int kr = 8 * (r >> 2) + 4 * hh + (r & 3);
-      float v0 = s0[r] * sl;
-      float v1 = s1[r] * sl;
-      if (diag) {
-        v0 = (k0 + kr <= qpos) ? v0 : -INFINITY;
-        v1 = (k0 + 32 + kr <= qpos) ? v1 : -INFINITY;
+      for (int r = 0; r < 16; ++r) {
+        const int kr = 8 * (r >> 2) + 4 * hh + (r & 3);
+        s0[r] = (k0 + kr <= qpos) ? s0[r] : -INFINITY;
+        s1[r] = (k0 + 32 + kr <= qpos) ? s1[r] : -INFINITY;
       }
-      s0[r] = v0;
-      s1[r] = v1;
-      tmax = fmaxf(tmax, fmaxf(v0, v1));
     }
-    tmax = xor32_max(tmax);
-    const float m_new = fmaxf(m, tmax);
-    const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m - m_new);
-    m = m_new;
+    float rmax = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) rmax = fmaxf(rmax, fmaxf(s0[r], s1[r]));
+    const float tmax = xor32_max(rmax) * sl;  // scale > 0 keeps the order
+    const bool grow = tmax > m + kRescaleSlack;
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+      const float m_new = grow ? tmax : m;
+      const float alpha = (m == -INFINITY) ? 0.f : fast_exp2(m - m_new);
+      m = m_new;
+      l *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+    }
+    const float nm = (m == -INFINITY) ? 0.f : -m;  // rows with no key yet: every score is -inf
     float psum = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const float p0 = (m == -INFINITY) ? 0.f : fast_exp2(s0[r] - m);
-      const float p1 = (m == -INFINITY) ? 0.f : fast_exp2(s1[r] - m);
+      const float p0 = fast_exp2(fmaf(s0[r], sl, nm));
+      const float p1 = fast_exp2(fmaf(s1[r], sl, nm));
       s0[r] = p0;
       s1[r] = p1;
       psum += p0 + p1;
     }
-    l = l * alpha + psum;
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+    l += psum;
 
     // P^T in the B layout: k-step (sub-tile st, half u) = registers 8u..8u+7
     // of s_st, i.e. keys st*32 + 16u + 8*(e/4) + 4*hh + e%4 for slot e
@@ -264,7 +351,7 @@ prefill_chunk_kernel(const PrefillKernelArgs a) {
     // O^T += V^T P^T; the A operand takes the same keys from row d of V^T
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
-      const uint16_t *vrow = svt + (dt * 32 + col) * VSTR;
+      const uint16_t *vrow = svb + (dt * 32 + col) * VSTR;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         const int kb0 = (ks >> 1) * 32 + (ks & 1) * 16 + 4 * hh;
@@ -274,6 +361,9 @@ prefill_chunk_kernel(const PrefillKernelArgs a) {
         o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[ks], o[dt], 0, 0, 0);
       }
     }
+
+    tile_store<D, KSTR, VSTR>(tr, sk[buf ^ 1], svt[buf ^ 1], tid);
+    if (tid < kMaxTileBlocks) sid[kt & 1][tid] = next_id;  // ids of tile kt+2
     __syncthreads();
   }
 
@@ -295,9 +385,10 @@ prefill_chunk_kernel(const PrefillKernelArgs a) {
 
 template <int D, int G>
 static hipError_t launch_t(const PrefillArgs &a, hipStream_t stream) {
-  constexpr int GW = G < 4 ? G : 4;
+  constexpr int NW = kPrefillThreads / 64;
+  constexpr int GW = G < NW ? G : NW;
   constexpr int HALVES = G / GW;
-  constexpr int QT = 32 * (4 / GW);
+  constexpr int QT = 32 * (NW / GW);
   PrefillKernelArgs k;
   k.out = a.out;
   k.q = a.q;
@@ -324,7 +415,7 @@ static hipError_t launch_t(const PrefillArgs &a, hipStream_t stream) {
   k.n_work = (int)n_work;
   k.scale_log2 = a.scale * kLog2e;
   const unsigned grid = (unsigned)((n_work + 7) / 8 * 8);
-  hipLaunchKernelGGL((prefill_chunk_kernel<D, G>), dim3(grid), dim3(256), 0, stream, k);
+  hipLaunchKernelGGL((prefill_chunk_kernel<D, G>), dim3(grid), dim3(kPrefillThreads), 0, stream, k);
   return hipGetLastError();
 }
 

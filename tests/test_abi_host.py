@@ -1,0 +1,220 @@
+"""The C ABI on the host (no GPU): the shared library loads, exports every
+function the header declares, and rejects bad arguments with the documented
+status codes and messages before anything is enqueued.  Every call here
+fails validation, so no HIP work is ever issued."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import paged_attention_kv_cache_amd as P
+from paged_attention_kv_cache_amd import _binding
+from paged_attention_kv_cache_amd.contracts import (ContractError, check_decode_contracts,
+                                                    check_prefill_contracts, check_slot_mapping)
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pagedattn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(P.LIB_PATH):
+        from paged_attention_kv_cache_amd import build
+        build.build()
+    return P.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_expected_entry_points():
+    names = declared_functions()
+    for n in ("pa_kv_cache_write", "pa_decode", "pa_decode_partition", "pa_decode_reduce",
+              "pa_decode_workspace_bytes", "pa_prefill_chunk", "pa_status_string",
+              "pa_last_error_message", "pa_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", P.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT\s+(pa_[a-z0-9_]+)\b", out))
+    for name in declared_functions():
+        assert name in exported, f"{name} declared in pagedattn.h but not exported"
+        assert hasattr(lib, name)
+    # the binding knows every declared function and no other
+    assert set(_binding.SIGNATURES) == set(declared_functions())
+
+
+def test_version_and_status_strings(lib):
+    assert P.pa_version() == 10000
+    for code, name in _binding.STATUS.items():
+        assert P.pa_status_string(code) == name
+    assert P.pa_status_string(-99) == "PA_UNKNOWN_STATUS"
+
+
+FAKE = 0x1000  # never dereferenced: every call below fails validation first
+
+
+def cache(nb=10, bs=32, hkv=8, d=128, dtype=1, k=FAKE, v=FAKE):
+    return _binding.PaKvCache(k, v, nb, bs, hkv, d, dtype)
+
+
+def decode(lib, c, S=4, H=32, mbps=8, mcl=100, scale=0.1, ps=0, ws=None, ws_bytes=0, out=FAKE, q=FAKE,
+           bt=FAKE, cl=FAKE):
+    return lib.pa_decode(ctypes.byref(c), out, q, S, H, bt, mbps, cl, mcl, scale, ps, ws, ws_bytes, None)
+
+
+def msg():
+    return P.pa_last_error_message()
+
+
+@pytest.mark.parametrize("bs", [0, 4, 24, 64, 12])
+def test_decode_rejects_block_size(lib, bs):
+    assert decode(lib, cache(bs=bs)) == -4
+    assert f"block_size {bs}" in msg()
+
+
+@pytest.mark.parametrize("d", [32, 96, 256])
+def test_decode_rejects_head_dim(lib, d):
+    assert decode(lib, cache(d=d)) == -5
+    assert f"head_dim {d} not in {{64, 128}}" in msg()
+
+
+def test_decode_rejects_gqa(lib):
+    assert decode(lib, cache(hkv=8), H=30) == -6
+    assert "not a multiple" in msg()
+    assert decode(lib, cache(hkv=2), H=32) == -6          # group of 16
+    assert "not in {1, 2, 4, 8}" in msg()
+
+
+def test_decode_rejects_dtype_and_nulls(lib):
+    assert decode(lib, cache(dtype=7)) == -2
+    assert "dtype 7" in msg()
+    assert decode(lib, cache(k=0)) == -1
+    assert lib.pa_decode(None, FAKE, FAKE, 1, 32, FAKE, 8, FAKE, 100, 0.1, 0, None, 0, None) == -1
+    assert decode(lib, cache(), q=0) == -1
+    assert "all must be device pointers" in msg()
+
+
+def test_decode_rejects_partition_and_workspace(lib):
+    assert decode(lib, cache(), ps=48) == -10
+    assert "partition_size 48" in msg()
+    assert decode(lib, cache(), ps=-32) == -10
+    need = P.pa_decode_workspace_bytes(4, 32, 128, 1000, 256)
+    assert decode(lib, cache(), mcl=1000, ps=256) == -7
+    assert f"{need} bytes needed" in msg()
+    assert decode(lib, cache(), mcl=1000, ps=256, ws=FAKE, ws_bytes=need - 1) == -7
+    assert f"< {need} needed" in msg()
+
+
+def test_decode_rejects_shapes(lib):
+    assert decode(lib, cache(), S=-1) == -3
+    assert decode(lib, cache(), S=70000) == -3
+    assert decode(lib, cache(), mbps=0) == -3
+    assert decode(lib, cache(), mcl=-5) == -3
+    assert decode(lib, cache(), scale=float("nan")) == -3
+    assert decode(lib, cache(nb=0)) == -3
+
+
+def test_workspace_formula(lib):
+    def expect(S, H, D, mcl, ps):
+        if ps <= 0 or mcl <= ps:
+            return 0
+        Pn = -(-mcl // ps)
+        n = S * H * Pn
+        a = lambda x: (x + 255) // 256 * 256
+        return 2 * a(4 * n) + a(4 * n * D)
+    for args in [(32, 32, 128, 4096, 256), (4, 32, 128, 131072, 512), (1, 8, 64, 100, 16),
+                 (3, 8, 64, 100, 0), (3, 8, 64, 100, 100), (3, 8, 64, 101, 100)]:
+        assert P.pa_decode_workspace_bytes(*args) == expect(*args), args
+    assert P.pa_decode_workspace_bytes(-1, 32, 128, 4096, 256) == 0
+
+
+def test_reduce_validation(lib):
+    assert lib.pa_decode_reduce(FAKE, 3, 4, 32, 128, FAKE, 1000, 256, FAKE, 10 ** 9, None) == -2
+    assert lib.pa_decode_reduce(FAKE, 1, 4, 32, 96, FAKE, 1000, 256, FAKE, 10 ** 9, None) == -5
+    assert lib.pa_decode_reduce(FAKE, 1, 4, 32, 128, FAKE, 1000, 256, None, 0, None) == -7
+    assert lib.pa_decode_reduce(FAKE, 1, 4, 32, 128, FAKE, 1000, 256, FAKE, 16, None) == -7
+    # nothing to merge: a single partition, or no sequences
+    assert lib.pa_decode_reduce(FAKE, 1, 4, 32, 128, FAKE, 100, 256, None, 0, None) == 0
+    assert lib.pa_decode_reduce(None, 1, 0, 32, 128, None, 1000, 256, None, 0, None) == 0
+
+
+def test_kv_cache_write_validation(lib):
+    c = cache()
+    assert lib.pa_kv_cache_write(ctypes.byref(c), FAKE, FAKE, FAKE, -1, None) == -3
+    assert lib.pa_kv_cache_write(ctypes.byref(c), None, FAKE, FAKE, 5, None) == -1
+    assert lib.pa_kv_cache_write(ctypes.byref(c), FAKE, FAKE, FAKE, 0, None) == 0   # nothing to do
+    odd = cache(hkv=1, d=6)                                                            # 12-byte rows
+    assert lib.pa_kv_cache_write(ctypes.byref(odd), FAKE, FAKE, FAKE, 5, None) == -3
+    assert "multiple of 16" in msg()
+    # write takes any block size (only attention restricts it)
+    assert lib.pa_kv_cache_write(ctypes.byref(cache(bs=24)), FAKE, FAKE, FAKE, 0, None) == 0
+
+
+def test_prefill_validation(lib):
+    c = cache()
+    args = lambda cc, **kw: (ctypes.byref(cc), kw.get("out", FAKE), FAKE, FAKE, kw.get("S", 2), kw.get("H", 32),
+                             kw.get("T", 64), kw.get("mql", 32), FAKE, 8, FAKE, 100, kw.get("scale", 0.1), None)
+    assert lib.pa_prefill_chunk(*args(cache(dtype=0))) == -8
+    assert "bf16" in msg()
+    assert lib.pa_prefill_chunk(*args(cache(bs=24))) == -4
+    assert lib.pa_prefill_chunk(*args(c, H=33)) == -6
+    assert lib.pa_prefill_chunk(*args(c, T=-1)) == -3
+    assert lib.pa_prefill_chunk(*args(c, out=0)) == -1
+    assert lib.pa_prefill_chunk(*args(c, scale=float("inf"))) == -3
+    assert lib.pa_prefill_chunk(*args(c, T=0)) == 0
+    assert lib.pa_prefill_chunk(*args(c, S=0)) == 0
+
+
+def test_error_message_clears_on_success(lib):
+    decode(lib, cache(bs=24))
+    assert msg()
+    assert lib.pa_kv_cache_write(ctypes.byref(cache()), FAKE, FAKE, FAKE, 0, None) == 0
+    assert msg() == ""
+
+
+def test_python_errors_carry_status(lib):
+    err = _binding.PagedAttnError("pa_decode", -4, "block_size 24 not in {8, 16, 32}")
+    assert err.status == "PA_ERR_BLOCK_SIZE" and "pa_decode" in str(err)
+
+
+# ---------------------------------------------------------------- contracts
+
+def test_contract_checks():
+    check_slot_mapping([0, 5, -1, 7], 2, 4)
+    with pytest.raises(ContractError, match="outside a pool"):
+        check_slot_mapping([8], 2, 4)
+    with pytest.raises(ContractError, match="written twice"):
+        check_slot_mapping([3, 3], 2, 4)
+    bt = np.array([[1, 0, 9], [2, 3, 9]])
+    check_decode_contracts(bt, [5, 8], num_blocks=4, block_size=4, max_context_len=8)
+    with pytest.raises(ContractError, match="block id"):
+        check_decode_contracts(bt, [9, 8], num_blocks=4, block_size=4, max_context_len=12)
+    with pytest.raises(ContractError, match="above max_context_len"):
+        check_decode_contracts(bt, [5, 8], num_blocks=4, block_size=4, max_context_len=7)
+    with pytest.raises(ContractError, match="needs more than"):
+        check_decode_contracts(bt, [13, 8], num_blocks=10, block_size=4, max_context_len=20)
+    check_prefill_contracts([0, 3, 5], bt, [5, 8], 4, 4, max_query_len=3, max_context_len=8, num_query_tokens=5)
+    with pytest.raises(ContractError, match="longer than its context"):
+        check_prefill_contracts([0, 6, 8], bt, [5, 8], 4, 4, max_query_len=6, max_context_len=8,
+                                num_query_tokens=8)
+    with pytest.raises(ContractError, match="max_query_len"):
+        check_prefill_contracts([0, 3, 5], bt, [5, 8], 4, 4, max_query_len=2, max_context_len=8,
+                                num_query_tokens=5)
+
+
+def test_workloads_satisfy_contracts():
+    import workloads as W
+    for c in (W.make_config("tiny_fp32_decode"),
+              W.random_decode(3, [1, 50, 300], block_size=8, dtype=W.BF16),
+              W.random_prefill(4, [0, 33], [17, 64], block_size=16)):
+        check_slot_mapping(c.slot_mapping, c.num_blocks, c.block_size)
+        check_decode_contracts(c.block_tables, c.context_lens, c.num_blocks, c.block_size, c.max_context_len)
