@@ -28,13 +28,16 @@
 //    O^T += V^T P^T (A = V^T from LDS), so P never goes through LDS.
 //  * The causal mask (bottom-right aligned) is applied only on tiles that
 //    cross the diagonal of the wave's 32 queries, by selecting -inf.
-//  * LDS holds two K/V tiles: the next tile's global loads are in flight
-//    while the current tile is multiplied, and are stored to the other
-//    buffer afterwards, so each tile costs one barrier.
+//  * LDS holds three K and three V tiles.  In step t a wave computes the
+//    scores of tile t+1 while it runs the softmax of tile t (independent
+//    work for the matrix and vector units), then multiplies V of tile t;
+//    the global loads of tile t+2 are in flight meanwhile and are stored
+//    before the step's single barrier.
 //  * The output is rescaled only when a query's max grows by more than 2^8
 //    (the final division by the running sum makes any reference max exact).
-//  * Work ids are remapped so that the query tiles of one (sequence, kv
-//    head), which read the same K/V, land on the same XCD and share its L2.
+//  * Work ids are remapped so that each XCD serves whole kv heads of every
+//    sequence: the XCDs get equal work, and the query tiles of one
+//    (sequence, kv head), which read the same K/V, share that XCD's L2.
 //    Tiles with more keys (later in the chunk) are dispatched first.
 #include "pa_common.h"
 
@@ -83,7 +86,15 @@ __device__ __forceinline__ bf16x8_t pack8(const f32x16_t &s, int base) {
 //      it can write (V[2p][d], V[2p+1][d]) dword pairs of the transposed tile.
 // Loads are unconditional: a key at or past kend, or in an invalid block,
 // reads the first row of the pool instead and is zeroed when stored.
-constexpr int kPrefillThreads = 512;  // 8 waves
+// waves per work-group (8: one work-group per CU shares each tile among
+// 8 waves; 4: two work-groups per CU, whose phases drift apart)
+#ifndef PA_PREFILL_INTERLEAVE
+#define PA_PREFILL_INTERLEAVE 0
+#endif
+#ifndef PA_PREFILL_WAVES
+#define PA_PREFILL_WAVES 8
+#endif
+constexpr int kPrefillThreads = 64 * PA_PREFILL_WAVES;
 
 template <int D>
 struct TileRegs {
@@ -179,7 +190,7 @@ __device__ __forceinline__ void tile_store(const TileRegs<D> &r, uint16_t *sk, u
 constexpr float kRescaleSlack = 8.f;
 
 template <int D, int G>
-__global__ void __launch_bounds__(kPrefillThreads)
+__global__ void __launch_bounds__(kPrefillThreads, 8 / PA_PREFILL_WAVES)
 prefill_chunk_kernel(const PrefillKernelArgs a) {
   constexpr int NW = kPrefillThreads / 64;
   constexpr int GW = G < NW ? G : NW;  // query heads per work-group
@@ -192,22 +203,29 @@ prefill_chunk_kernel(const PrefillKernelArgs a) {
   constexpr int NDS = D / 16;        // k-steps of Q K^T
   constexpr int NDT = D / 32;        // 32-row tiles of O^T
 
-  // two buffers: the next tile is stored while the current one is used
-  __shared__ __attribute__((aligned(16))) uint16_t sk[2][KT * KSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t svt[2][D * VSTR];
+  // three buffers each for K and V: at step t the waves read K of tile t+1
+  // and V of tile t while tile t+2 is stored
+  __shared__ __attribute__((aligned(16))) uint16_t sk[3][KT * KSTR];
+  __shared__ __attribute__((aligned(16))) uint16_t svt[3][D * VSTR];
+  __shared__ int sid[3][kMaxTileBlocks];
 
-  // work id: consecutive ids share a (sequence, kv head) and sit on one XCD
+  // Work id.  Work-groups are dispatched round-robin over the 8 XCDs; the
+  // remap gives each XCD a contiguous range of work ids.  Ids are ordered
+  // (kv head, head half, query tile from the last, sequence), so an XCD
+  // serves whole kv heads of every sequence (equal work per XCD when the
+  // head groups are a multiple of 8), all query tiles of a (sequence, kv
+  // head) share one L2, and the tiles with the most keys start first.
   const int nwg = gridDim.x;  // a multiple of 8
   const int bid = blockIdx.x;
   const int wid = (bid & 7) * (nwg >> 3) + (bid >> 3);
   if (wid >= a.n_work) return;
   int rest = wid;
+  const int seq = rest % a.num_seqs;
+  rest /= a.num_seqs;
   const int qt_rev = rest % a.n_qtiles;
   rest /= a.n_qtiles;
   const int half = rest % HALVES;
-  rest /= HALVES;
-  const int kvh = rest % a.num_kv_heads;
-  const int seq = rest / a.num_kv_heads;
+  const int kvh = rest / HALVES;
   const int qtile = a.n_qtiles - 1 - qt_rev;
 
   int r1 = min(a.query_start_loc[seq + 1], a.num_query_tokens);
@@ -262,34 +280,8 @@ prefill_chunk_kernel(const PrefillKernelArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
 
-  // tile 0 goes straight to LDS.  Block ids: sid[b] holds the ids of the
-  // tile whose loads are issued next from it; threads 0..7 fetch the ids of
-  // the tile after that while the current tile is multiplied.
-  __shared__ int sid[2][kMaxTileBlocks];
-  if (tid < kMaxTileBlocks) {
-    sid[0][tid] = tile_block_id(bt, 0, tid, shift, a.max_blocks_per_seq);
-    sid[1][tid] = tile_block_id(bt, KT, tid, shift, a.max_blocks_per_seq);
-  }
-  __syncthreads();
-  TileRegs<D> tr;
-  tile_load<D>(tr, sid[0], kbase, vbase, 0, kend, shift, bs_mask, a.num_blocks, slot_stride, tid);
-  tile_store<D, KSTR, VSTR>(tr, sk[0], svt[0], tid);
-  __syncthreads();
-
-  for (int kt = 0; kt < ntiles; ++kt) {
-    const int k0 = kt * KT;
-    const int buf = kt & 1;
-    // next tile's loads are in flight during this tile's products (past the
-    // last tile they read only in-pool rows that are zeroed)
-    tile_load<D>(tr, sid[(kt + 1) & 1], kbase, vbase, k0 + KT, kend, shift, bs_mask, a.num_blocks, slot_stride,
-                 tid);
-    int next_id = 0;
-    if (tid < kMaxTileBlocks) next_id = tile_block_id(bt, k0 + 2 * KT, tid, shift, a.max_blocks_per_seq);
-
-    const uint16_t *skb = sk[buf];
-    const uint16_t *svb = svt[buf];
-    // S^T = K Q^T for keys k0 .. k0+31 (s0) and k0+32 .. k0+63 (s1)
-    f32x16_t s0, s1;
+  // S^T tile of keys k0 .. k0+63 (s0: first 32 keys, s1: last 32)
+  auto qk = [&](const uint16_t *skb, f32x16_t &s0, f32x16_t &s1) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       s0[r] = 0.f;
@@ -302,6 +294,36 @@ prefill_chunk_kernel(const PrefillKernelArgs a) {
       s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qb[ds], s0, 0, 0, 0);
       s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qb[ds], s1, 0, 0, 0);
     }
+  };
+
+  // Pipeline, one barrier per step t:
+  //   loads of tile t+2 -> registers;  S(t+1) = K(t+1) Q^T;  softmax of S(t);
+  //   O += V(t) P(t);  registers -> LDS buffers of tile t+2.
+  // Block ids: sid[j % 3] holds the ids of tile j, filled three tiles ahead.
+  if (tid < kMaxTileBlocks) {
+#pragma unroll
+    for (int j = 0; j < 3; ++j) sid[j][tid] = tile_block_id(bt, j * KT, tid, shift, a.max_blocks_per_seq);
+  }
+  __syncthreads();
+  TileRegs<D> tr;
+  tile_load<D>(tr, sid[0], kbase, vbase, 0, kend, shift, bs_mask, a.num_blocks, slot_stride, tid);
+  tile_store<D, KSTR, VSTR>(tr, sk[0], svt[0], tid);
+  tile_load<D>(tr, sid[1], kbase, vbase, KT, kend, shift, bs_mask, a.num_blocks, slot_stride, tid);
+  tile_store<D, KSTR, VSTR>(tr, sk[1], svt[1], tid);
+  __syncthreads();
+
+  f32x16_t c0, c1;  // S of the current tile
+  qk(sk[0], c0, c1);
+
+  for (int kt = 0; kt < ntiles; ++kt) {
+    const int k0 = kt * KT;
+    const int b0 = kt % 3;
+    const int b1 = (kt + 1) % 3;
+    const int b2 = (kt + 2) % 3;
+    // tile t+2 from the pool (past the last tile: in-pool rows, zeroed)
+    tile_load<D>(tr, sid[b2], kbase, vbase, k0 + 2 * KT, kend, shift, bs_mask, a.num_blocks, slot_stride, tid);
+    int next_id = 0;
+    if (tid < kMaxTileBlocks) next_id = tile_block_id(bt, k0 + 3 * KT, tid, shift, a.max_blocks_per_seq);
 
     // causal mask on tiles that cross this wave's diagonal (raw scores;
     // register r of this lane holds key 8*(r/4) + 4*hh + r%4)
@@ -309,13 +331,13 @@ prefill_chunk_kernel(const PrefillKernelArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int kr = 8 * (r >> 2) + 4 * hh + (r & 3);
-        s0[r] = (k0 + kr <= qpos) ? s0[r] : -INFINITY;
-        s1[r] = (k0 + 32 + kr <= qpos) ? s1[r] : -INFINITY;
+        c0[r] = (k0 + kr <= qpos) ? c0[r] : -INFINITY;
+        c1[r] = (k0 + 32 + kr <= qpos) ? c1[r] : -INFINITY;
       }
     }
     float rmax = -INFINITY;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) rmax = fmaxf(rmax, fmaxf(s0[r], s1[r]));
+    for (int r = 0; r < 16; ++r) rmax = fmaxf(rmax, fmaxf(c0[r], c1[r]));
     const float tmax = xor32_max(rmax) * sl;  // scale > 0 keeps the order
     const bool grow = tmax > m + kRescaleSlack;
     if (__builtin_amdgcn_ballot_w64(grow)) {
@@ -328,27 +350,43 @@ prefill_chunk_kernel(const PrefillKernelArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
     }
+    // From here to the P.V products the code is one basic block: the
+    // scores of the next tile (independent of this tile's softmax; on the
+    // last step the buffer holds the zero-filled tile past the end and the
+    // result is not used) are interleaved with the exponentials below, so
+    // the matrix and vector units work at the same time.
+    f32x16_t n0, n1;
+    qk(sk[b1], n0, n1);
     const float nm = (m == -INFINITY) ? 0.f : -m;  // rows with no key yet: every score is -inf
     float psum = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const float p0 = fast_exp2(fmaf(s0[r], sl, nm));
-      const float p1 = fast_exp2(fmaf(s1[r], sl, nm));
-      s0[r] = p0;
-      s1[r] = p1;
+      const float p0 = fast_exp2(fmaf(c0[r], sl, nm));
+      const float p1 = fast_exp2(fmaf(c1[r], sl, nm));
+      c0[r] = p0;
+      c1[r] = p1;
       psum += p0 + p1;
     }
     l += psum;
+#if PA_PREFILL_INTERLEAVE
+#pragma unroll
+    for (int i = 0; i < 2 * NDS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, PA_PREFILL_INTERLEAVE, 0);  // some VALU
+    }
+#endif
 
     // P^T in the B layout: k-step (sub-tile st, half u) = registers 8u..8u+7
-    // of s_st, i.e. keys st*32 + 16u + 8*(e/4) + 4*hh + e%4 for slot e
+    // of c_st, i.e. keys st*32 + 16u + 8*(e/4) + 4*hh + e%4 for slot e
     bf16x8_t pb[4];
-    pb[0] = pack8(s0, 0);
-    pb[1] = pack8(s0, 8);
-    pb[2] = pack8(s1, 0);
-    pb[3] = pack8(s1, 8);
+    pb[0] = pack8(c0, 0);
+    pb[1] = pack8(c0, 8);
+    pb[2] = pack8(c1, 0);
+    pb[3] = pack8(c1, 8);
 
     // O^T += V^T P^T; the A operand takes the same keys from row d of V^T
+    const uint16_t *svb = svt[b0];
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
       const uint16_t *vrow = svb + (dt * 32 + col) * VSTR;
@@ -362,9 +400,11 @@ prefill_chunk_kernel(const PrefillKernelArgs a) {
       }
     }
 
-    tile_store<D, KSTR, VSTR>(tr, sk[buf ^ 1], svt[buf ^ 1], tid);
-    if (tid < kMaxTileBlocks) sid[kt & 1][tid] = next_id;  // ids of tile kt+2
+    tile_store<D, KSTR, VSTR>(tr, sk[b2], svt[b2], tid);
+    if (tid < kMaxTileBlocks) sid[b0][tid] = next_id;  // ids of tile t+3
     __syncthreads();
+    c0 = n0;
+    c1 = n1;
   }
 
   const float lt = xor32_sum(l);
