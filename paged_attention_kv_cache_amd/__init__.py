@@ -10,6 +10,10 @@ The work is done by hand-written HIP kernels behind the C ABI in
   run the two stages separately)
 * ``pa_prefill_chunk``   - causal attention of packed chunks over their
   cached prefixes (bf16 MFMA)
+
+Host side (``include/pagedattn_kvm.h``): ``KvManager`` (block pool, LRU free
+list, block-hash prefix cache) and ``StepScheduler`` (alternating prompt /
+decode steps) produce the block tables and slot mappings those kernels take.
 """
 
 from ._binding import (  # noqa: F401
@@ -31,4 +35,5 @@ from ._binding import (  # noqa: F401
     pa_status_string,
     pa_version,
 )
+from .kv_manager import KIND_DECODE, KIND_IDLE, KIND_PROMPT, KvManager, Step, StepScheduler  # noqa: F401
 from .contracts import check_decode_contracts, check_prefill_contracts, check_slot_mapping  # noqa: F401

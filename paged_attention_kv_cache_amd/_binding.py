@@ -1,4 +1,5 @@
-"""ctypes binding of ``libpagedattn.so`` (the C ABI in ``include/pagedattn.h``).
+"""ctypes binding of ``libpagedattn.so`` (the C ABI in ``include/pagedattn.h``
+and ``include/pagedattn_kvm.h``).
 
 Argument marshalling only: tensors in, device pointers and sizes out, the
 status code checked.  Every step of the computation runs in the library's
@@ -32,6 +33,8 @@ STATUS = {
     -8: "PA_ERR_UNSUPPORTED",
     -9: "PA_ERR_HIP",
     -10: "PA_ERR_PARTITION",
+    -11: "PA_ERR_NO_BLOCKS",
+    -12: "PA_ERR_REQUEST",
 }
 
 # every function the header declares, with its ctypes signature
@@ -54,6 +57,30 @@ class PaKvCache(ctypes.Structure):
 
 
 _PCACHE = ctypes.POINTER(PaKvCache)
+_i64 = ctypes.c_int64
+_pi32 = ctypes.POINTER(_i32)
+_pi64 = ctypes.POINTER(_i64)
+
+
+class PaKvmStats(ctypes.Structure):
+    _fields_ = [(n, _i64) for n in (
+        "num_blocks", "block_size", "free_blocks", "cached_blocks", "active_requests",
+        "prefix_queries", "prefix_hit_blocks", "prefix_hit_tokens", "evictions")]
+
+
+class PaSchedConfig(ctypes.Structure):
+    _fields_ = [(n, _i32) for n in (
+        "max_batched_tokens", "max_chunk_tokens", "max_decode_steps", "min_decode_steps", "max_seqs")]
+
+
+class PaStep(ctypes.Structure):
+    _fields_ = [
+        ("kind", _i32), ("num_seqs", _i32), ("num_tokens", _i32), ("max_query_len", _i32),
+        ("max_context_len", _i32), ("max_blocks_per_seq", _i32),
+        ("request_ids", _pi64), ("query_start_loc", _pi32), ("context_lens", _pi32),
+        ("block_tables", _pi32), ("slot_mapping", _pi64),
+        ("cap_seqs", _i32), ("cap_tokens", _i32), ("cap_blocks", _i32),
+    ]
 
 SIGNATURES = {
     "pa_kv_cache_write": (ctypes.c_int, [_PCACHE, _vp, _vp, _vp, _i32, _vp]),
@@ -68,6 +95,25 @@ SIGNATURES = {
     "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "pa_last_error_message": (ctypes.c_char_p, []),
     "pa_version": (ctypes.c_int, []),
+    # host KV manager and step scheduler
+    "pa_kvm_create": (_vp, [_i32, _i32, _i32]),
+    "pa_kvm_destroy": (None, [_vp]),
+    "pa_kvm_add_request": (ctypes.c_int, [_vp, _i64, _pi32, _i32]),
+    "pa_kvm_append_tokens": (ctypes.c_int, [_vp, _i64, _pi32, _i32]),
+    "pa_kvm_get_computed_blocks": (ctypes.c_int, [_vp, _i64, _pi32]),
+    "pa_kvm_allocate_slots": (ctypes.c_int, [_vp, _i64, _i32]),
+    "pa_kvm_commit": (ctypes.c_int, [_vp, _i64, _i32]),
+    "pa_kvm_free": (ctypes.c_int, [_vp, _i64]),
+    "pa_kvm_block_table": (ctypes.c_int, [_vp, _i64, _pi32, _i32, _pi32]),
+    "pa_kvm_slot_mapping": (ctypes.c_int, [_vp, _i64, _i32, _i32, _pi64]),
+    "pa_kvm_request_info": (ctypes.c_int, [_vp, _i64, _pi32, _pi32, _pi32]),
+    "pa_kvm_get_stats": (ctypes.c_int, [_vp, ctypes.POINTER(PaKvmStats)]),
+    "pa_sched_create": (_vp, [_vp, ctypes.POINTER(PaSchedConfig)]),
+    "pa_sched_destroy": (None, [_vp]),
+    "pa_sched_add_request": (ctypes.c_int, [_vp, _i64, _pi32, _i32, _i32]),
+    "pa_sched_next_step": (ctypes.c_int, [_vp, ctypes.POINTER(PaStep)]),
+    "pa_sched_complete_step": (ctypes.c_int, [_vp, ctypes.POINTER(PaStep), _pi32, _pi32]),
+    "pa_sched_counts": (ctypes.c_int, [_vp, _pi32, _pi32, _pi32]),
 }
 
 _lib = None

@@ -22,7 +22,10 @@ LIB_NAME = "libpagedattn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 ARCH = "gfx950"
 
-SOURCES = ["abi.cpp", "kv_cache_write.hip", "pa_decode.hip", "pa_prefill.hip"]
+SOURCES = ["abi.cpp", "kv_cache_write.hip", "pa_decode.hip", "pa_prefill.hip", "kv_manager.cpp"]
+# plain host C++ (no device code): built by the host compiler
+HOST_SOURCES = {"kv_manager.cpp"}
+HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-I", INCLUDE, "-I", CSRC]
 
 COMMON_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
@@ -42,9 +45,12 @@ def hipcc() -> str:
 
 def _compile(src: str, extra: list[str], build_dir: str = BUILD) -> str:
     obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *COMMON_FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
-    if src.endswith(".cpp"):
-        cmd[1:1] = ["-x", "hip"]
+    if src in HOST_SOURCES:
+        cmd = [os.environ.get("CXX", "g++"), *HOST_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    else:
+        cmd = [hipcc(), *COMMON_FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
+        if src.endswith(".cpp"):
+            cmd[1:1] = ["-x", "hip"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compiling {src} failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

@@ -16,13 +16,17 @@
 #include <hip/hip_runtime_api.h>
 
 #include "pa_common.h"
+#include "pa_error.h"
 #include "pagedattn.h"
+#include "pagedattn_kvm.h"
+
+namespace pa {
 
 namespace {
-
 thread_local char g_msg[512] = "";
+}
 
-int fail(int status, const char *fmt, ...) {
+int set_error(int status, const char *fmt, ...) {
   va_list ap;
   va_start(ap, fmt);
   vsnprintf(g_msg, sizeof(g_msg), fmt, ap);
@@ -30,10 +34,23 @@ int fail(int status, const char *fmt, ...) {
   return status;
 }
 
-int ok() {
+int clear_error() {
   g_msg[0] = '\0';
   return PA_OK;
 }
+
+const char *last_error() { return g_msg; }
+
+}  // namespace pa
+
+namespace {
+
+template <typename... A>
+int fail(int status, const char *fmt, A... a) {
+  return pa::set_error(status, fmt, a...);
+}
+
+int ok() { return pa::clear_error(); }
 
 int hip_fail(hipError_t e, const char *what) {
   return fail(PA_ERR_HIP, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
@@ -155,7 +172,7 @@ extern "C" {
 
 int pa_version(void) { return 10000; }  // 1.0.0
 
-const char *pa_last_error_message(void) { return g_msg; }
+const char *pa_last_error_message(void) { return pa::last_error(); }
 
 const char *pa_status_string(int status) {
   switch (status) {
@@ -170,6 +187,8 @@ const char *pa_status_string(int status) {
     case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED";
     case PA_ERR_HIP: return "PA_ERR_HIP";
     case PA_ERR_PARTITION: return "PA_ERR_PARTITION";
+    case PA_ERR_NO_BLOCKS: return "PA_ERR_NO_BLOCKS";
+    case PA_ERR_REQUEST: return "PA_ERR_REQUEST";
   }
   return "PA_UNKNOWN_STATUS";
 }

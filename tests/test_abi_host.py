@@ -17,7 +17,8 @@ from paged_attention_kv_cache_amd.contracts import (ContractError, check_decode_
                                                     check_prefill_contracts, check_slot_mapping)
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "pagedattn.h")
+INCLUDE = os.path.join(ROOT, "include")
+HEADERS = sorted(os.path.join(INCLUDE, f) for f in os.listdir(INCLUDE) if f.endswith(".h"))
 
 
 @pytest.fixture(scope="module")
@@ -29,16 +30,19 @@ def lib():
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(pa_[a-z0-9_]+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(pa_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_header_declares_the_expected_entry_points():
     names = declared_functions()
     for n in ("pa_kv_cache_write", "pa_decode", "pa_decode_partition", "pa_decode_reduce",
               "pa_decode_workspace_bytes", "pa_prefill_chunk", "pa_status_string",
-              "pa_last_error_message", "pa_version"):
+              "pa_last_error_message", "pa_version", "pa_kvm_create", "pa_kvm_get_computed_blocks",
+              "pa_kvm_allocate_slots", "pa_kvm_free", "pa_sched_next_step", "pa_sched_complete_step"):
         assert n in names
 
 
@@ -46,7 +50,7 @@ def test_library_exports_every_declared_symbol(lib):
     out = subprocess.run(["nm", "-D", "--defined-only", P.LIB_PATH], capture_output=True, text=True).stdout
     exported = set(re.findall(r"\bT\s+(pa_[a-z0-9_]+)\b", out))
     for name in declared_functions():
-        assert name in exported, f"{name} declared in pagedattn.h but not exported"
+        assert name in exported, f"{name} declared in include/ but not exported"
         assert hasattr(lib, name)
     # the binding knows every declared function and no other
     assert set(_binding.SIGNATURES) == set(declared_functions())

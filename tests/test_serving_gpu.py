@@ -1,0 +1,27 @@
+"""The serving loop on the GPU (see serving_util): scheduler-built block
+tables and slot mappings drive the library's write, prefill and decode
+kernels, and every output row matches the oracle's attention over the
+request's dense K/V.  The pool is small enough that requests are
+preempted and recomputed, and half of them share a system prompt
+(prefix-cache hits)."""
+
+import pytest
+
+import workloads as W
+
+from gpu_util import BF16_MAX_ABS, log
+from serving_util import LibraryBackend, serve_and_check
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("partition_size", [0, 64])
+def test_scheduled_serving_matches_dense_oracle(partition_size):
+    tr = W.serving_trace(seed=6000, num_requests=12, num_blocks=64)
+    r = serve_and_check(tr, LibraryBackend(tr), partition_size=partition_size)
+    assert r["stats"]["prefix_hit_tokens"] > 0, r["stats"]
+    assert r["recomputed"] > 0, "the pool was expected to force preemption"
+    assert 1 in r["kinds"] and 2 in r["kinds"]
+    assert r["worst"] <= BF16_MAX_ABS
+    log(f"serving ps={partition_size}: {r['steps']} steps, worst max-abs {r['worst']:.2e}, "
+        f"{r['recomputed']} recomputed, hits {r['stats']['prefix_hit_tokens']} tokens")

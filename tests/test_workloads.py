@@ -110,3 +110,22 @@ def test_boost_scales_by_eight():
     boosted = np.any(kc != kd, axis=-1)
     frac = boosted.sum() / (500 * 2)
     assert 0.02 < frac < 0.09
+
+
+def test_serving_trace_kv_depends_only_on_the_token_prefix():
+    tr = W.serving_trace(seed=11, num_requests=4)
+    a = tr.prompts[0]
+    b = a[:30] + [a[30] + 1] + a[31:]
+    ka, va, _ = tr.kv(a)
+    kb, vb, _ = tr.kv(b)
+    assert np.array_equal(ka[:30], kb[:30]) and np.array_equal(va[:30], vb[:30])
+    assert not np.array_equal(ka[30:], kb[30:])  # every later position changes
+    assert all(not np.array_equal(ka[i], kb[i]) for i in range(30, len(a)))
+    # incremental extension equals the draw from scratch
+    k1, v1, st = tr.kv(a[:17])
+    k2, v2, _ = tr.kv(a, start=17, state=st)
+    assert np.array_equal(np.concatenate([k1, k2]), ka) and np.array_equal(np.concatenate([v1, v2]), va)
+    # even requests share the system prompt; queries differ by request
+    assert tr.prompts[0][:64] == tr.prompts[2][:64]
+    assert not np.array_equal(tr.q(0, 0, 1), tr.q(2, 0, 1))
+    assert ka.dtype == np.uint16 and tr.q(1, 5, 3).shape == (3, tr.num_heads, tr.head_dim)

@@ -24,3 +24,4 @@ from .generate import (  # noqa: F401
     CONFIG_NAMES,
     make_config,
 )
+from .serving import ServingTrace, serving_trace  # noqa: F401
