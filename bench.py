@@ -50,6 +50,7 @@ def parse():
     ap.add_argument("--rotate-gb", type=float, default=2.0, help="total size of rotated KV pools")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--quick", action="store_true", help="skip the long-context and prefix-shared decode lines")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first copy 1 GiB device-to-device (a kernel of known traffic for counter runs)")
@@ -193,6 +194,83 @@ def bench_decode(args):
     log(f"step {ms_step_plain * 1e3:.1f} us (events {ms_step * 1e3:.1f}); write {t_write * 1e3:.1f} us, "
         f"partition {t_part * 1e3:.1f} us (back to back {t_part_b2b * 1e3:.1f}), reduce {t_red * 1e3:.1f} us; "
         f"partition {achieved:.0f} GB/s")
+    del pools
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_decode_secondary(name, ps, steps=30):
+    """Decode partition + reduce on another workload: time per launch pair
+    (back to back over rotated pools), logical KV GB/s (every context token
+    of every sequence) and unique KV GB/s (each shared physical block once)."""
+    import torch
+    import paged_attention_kv_cache_amd as P
+    import workloads as W
+
+    log(f"building {name}")
+    case = W.make_config(name, poison=False)
+    S, H, D = case.q.shape
+    pool_bytes = 2 * case.k_cache.nbytes
+    R = max(2, int(math.ceil(2.0e9 / pool_bytes)))
+    k0 = to_dev(case.k_cache, case.dtype)
+    v0 = to_dev(case.v_cache, case.dtype)
+    pools = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(R - 1)]
+    q = to_dev(case.q, case.dtype)
+    bt = torch.from_numpy(case.block_tables).cuda()
+    cl = torch.from_numpy(case.context_lens).cuda()
+    out = torch.empty_like(q)
+    mcl = case.max_context_len
+    ws = torch.empty(max(P.pa_decode_workspace_bytes(S, H, D, mcl, ps), 1), dtype=torch.uint8, device="cuda")
+
+    def part(i):
+        k, v = pools[i % R]
+        P.pa_decode_partition(q, k, v, bt, cl, case.scale, mcl, ps, out=out, workspace=ws)
+
+    def red(i):
+        k, v = pools[i % R]
+        P.pa_decode_reduce(q, k, v, bt, cl, case.scale, mcl, ps, out=out, workspace=ws)
+
+    for i in range(4):
+        part(i)
+        red(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        part(i)
+    e1.record()
+    torch.cuda.synchronize()
+    t_part = e0.elapsed_time(e1) / steps
+    e0.record()
+    for i in range(steps):
+        part(i)
+        red(i)
+    e1.record()
+    torch.cuda.synchronize()
+    t_both = e0.elapsed_time(e1) / steps
+    logical = case.kv_bytes_logical()
+    row_bytes = case.num_kv_heads * case.head_dim * 2 * 2          # K+V of one token, all kv heads
+    unique_tokens = 0
+    seen = set()
+    for i, n in enumerate(case.context_lens.tolist()):
+        for j in range(-(-n // case.block_size)):
+            b = int(case.block_tables[i, j])
+            if b in seen:
+                continue
+            seen.add(b)
+            unique_tokens += min(case.block_size, n - j * case.block_size)
+    unique = unique_tokens * row_bytes
+    res = {
+        "workload": name, "num_seqs": S, "context_tokens": int(case.context_lens.sum()), "partition_size": ps,
+        "partition_us": round(t_part * 1e3, 2), "partition_plus_reduce_us": round(t_both * 1e3, 2),
+        "tokens_per_s": round(S / (t_both * 1e-3), 1),
+        "logical_kv_gbps": round(logical / (t_part * 1e-3) / 1e9, 1),
+        "unique_kv_gbps": round(unique / (t_part * 1e-3) / 1e9, 1),
+        "unique_kv_hbm_frac": round(unique / (t_part * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "logical_kv_bytes": logical, "unique_kv_bytes": unique,
+    }
+    log(f"{name}: partition {t_part * 1e3:.1f} us, +reduce {t_both * 1e3:.1f} us, "
+        f"logical {res['logical_kv_gbps']:.0f} GB/s, unique {res['unique_kv_gbps']:.0f} GB/s")
     del pools
     torch.cuda.empty_cache()
     return res
@@ -355,6 +433,12 @@ def main():
                          "traffic": traffic_from_profiles("prefill_chunk", pre["src"]),
                          "algorithmic_flops_per_launch": pre["flops"]},
         }
+    if not args.quick:
+        line["decode_other_workloads"] = [
+            bench_decode_secondary("long_context_decode", 512),
+            bench_decode_secondary("prefix_shared_decode_bs16", 512),
+            bench_decode_secondary("prefix_shared_decode_bs8", 512),
+        ]
     if not args.no_cpu_baseline:
         log(f"timing the CPU oracle for ~{args.cpu_seconds:.0f} s")
         line["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
