@@ -137,33 +137,34 @@ def bench_decode(args):
         step(i % R)
     torch.cuda.synchronize()
 
-    # per-kernel durations: events around each launch, on the launch stream
-    log(f"timing {args.steps} steps")
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    # the headline: exactly K steps between one pair of events, right after
+    # the warmup
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
+    log(f"timing {args.steps} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    start.record()
-    for i in range(args.steps):
-        step(i % R, evs[i])
-    end.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    total_ms = start.elapsed_time(end)
-    ms_step = total_ms / args.steps
-    t_write = np.mean([e[0].elapsed_time(e[1]) for e in evs])
-    t_part = np.mean([e[1].elapsed_time(e[2]) for e in evs])
-    t_red = np.mean([e[2].elapsed_time(e[3]) for e in evs])
-
-    # the same steps without the interleaved events, for the headline
-    torch.cuda.synchronize()
     start.record()
     for i in range(args.steps):
         step(i % R)
     end.record()
     torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
     ms_step_plain = start.elapsed_time(end) / args.steps
+
+    # diagnostics: per-kernel durations from events around each launch (on
+    # the launch stream), which add gaps of their own
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        step(i % R, evs[i])
+    end.record()
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(end) / args.steps
+    t_write = np.mean([e[0].elapsed_time(e[1]) for e in evs])
+    t_part = np.mean([e[1].elapsed_time(e[2]) for e in evs])
+    t_red = np.mean([e[2].elapsed_time(e[3]) for e in evs])
 
     # the partition kernel alone, launched back to back on the rotated pools
     # between one pair of events: its average launch duration, without the

@@ -371,15 +371,23 @@ __device__ __forceinline__ float from_head(float x) {
 // block id and the element offset of that token group are the same for the
 // whole wave and live in scalar registers.  A lane adds its own fixed byte
 // offset (its row times the slot stride plus its 16-byte column).
+// Read-only view for inputs that no work-group writes during a launch
+// (block tables, context lengths): loads through the constant address
+// space stay scalar for wave-uniform indices even after the kernel's own
+// stores and fences.
+typedef const __attribute__((address_space(4))) int32_t *ro_i32_ptr;
+__device__ __forceinline__ ro_i32_ptr read_only(const int32_t *p) { return (ro_i32_ptr)(p); }
+
 template <int U, int R>
 __device__ __forceinline__ void chunk_rows(size_t (&off)[U], bool (&ok)[U], const int32_t *bt, int cbase,
                                            int p1, int shift, int bs_mask, int num_blocks,
                                            size_t slot_stride, int max_blocks) {
   // table reads are unconditional (index clamped into the row) so that all
   // of them are in flight together
+  const ro_i32_ptr tab = read_only(bt);
   int blk[U];
 #pragma unroll
-  for (int u = 0; u < U; ++u) blk[u] = bt[min((cbase + u * R) >> shift, max_blocks - 1)];
+  for (int u = 0; u < U; ++u) blk[u] = tab[min((cbase + u * R) >> shift, max_blocks - 1)];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int tok0 = cbase + u * R;
@@ -414,16 +422,208 @@ __device__ __forceinline__ void chunk_load(uint4 (&buf)[U], const size_t (&off)[
   }
 }
 
+// Per-wave online softmax of the G query heads of kv head `kvh` over the
+// tokens p0 .. p1-1 of sequence `seq`.  The wave takes chunks of CH tokens
+// c = wave, wave + W, ...; on return m (base-2 units) and l hold the wave's
+// running max and sum of head col % G, acc the wave's P.V sums (rows already
+// summed, valid in every lane).
+template <int D, int G>
+struct Bf16Decode {
+  static constexpr int L = D / 8;   // lanes per token row (8 bf16 per lane)
+  static constexpr int R = 64 / L;  // token rows per load instruction
+  static constexpr int U = PA_DECODE_UNROLL;
+  static constexpr int CH = R * U;  // tokens per wave step
+  static constexpr int W = PA_DECODE_WAVES;
+  static_assert(U % 2 == 0, "tokens are paired for the P.V dot products");
+
+  __device__ static __forceinline__ void attend(const DecodeKernelArgs &a, int seq, int kvh, int p0, int p1,
+                                                int wave, int lane, float &m, float &l, float (&acc)[G][8]) {
+    const int row = lane / L;
+    const int col = lane % L;
+    uint32_t qp[G][4];
+    {
+      const uint4 *qv = reinterpret_cast<const uint4 *>(
+          static_cast<const uint16_t *>(a.q) + ((size_t)seq * a.num_heads + (size_t)kvh * G) * D);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const uint4 c = qv[h * L + col];
+        qp[h][0] = c.x;
+        qp[h][1] = c.y;
+        qp[h][2] = c.z;
+        qp[h][3] = c.w;
+      }
+    }
+    const float sl = a.scale_log2;
+    const size_t slot_stride = (size_t)a.num_kv_heads * D;
+    const uint16_t *kbase = static_cast<const uint16_t *>(a.k_cache) + (size_t)kvh * D;
+    const uint16_t *vbase = static_cast<const uint16_t *>(a.v_cache) + (size_t)kvh * D;
+    const uint32_t lane_bytes = (uint32_t)(((size_t)row * slot_stride + (size_t)col * 8) * 2);
+    const int32_t *bt = a.block_tables + (size_t)seq * a.max_blocks_per_seq;
+    const int shift = a.block_shift;
+    const int bs_mask = (1 << shift) - 1;
+
+    m = -INFINITY;
+    l = 0.f;
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+
+    const int ntok = p1 - p0;
+    const int nchunks = ntok > 0 ? (ntok + CH - 1) / CH : 0;
+    for (int c = wave; c < nchunks; c += W) {
+      const int cbase = p0 + c * CH;
+      size_t off[U];
+      bool ok[U];
+      chunk_rows<U, R>(off, ok, bt, cbase, p1, shift, bs_mask, a.num_blocks, slot_stride,
+                       a.max_blocks_per_seq);
+      uint4 kr[U], vr[U];
+#if PA_DECODE_PRIO
+      __builtin_amdgcn_s_setprio(3);
+#endif
+      chunk_load<U>(kr, off, kbase, lane_bytes);
+      chunk_load<U>(vr, off, vbase, lane_bytes);
+#if PA_DECODE_PRIO
+      __builtin_amdgcn_s_setprio(0);
+#endif
+      bool valid[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) valid[u] = ok[u] && (cbase + u * R + row < p1);
+
+      float s[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        float d[G];
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          float t = dot2_bf16(qp[h][0], kr[u].x, 0.f);
+          t = dot2_bf16(qp[h][1], kr[u].y, t);
+          t = dot2_bf16(qp[h][2], kr[u].z, t);
+          d[h] = dot2_bf16(qp[h][3], kr[u].w, t);
+        }
+        const float r = row_scatter_sum<L, G>(d, col);
+        s[u] = valid[u] ? r * sl : -INFINITY;
+      }
+      float cm = s[0];
+#pragma unroll
+      for (int u = 1; u < U; ++u) cm = fmaxf(cm, s[u]);
+      cm = rows_max<L>(cm);
+      const float m_new = fmaxf(m, cm);
+      const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m - m_new);
+      m = m_new;
+      float p[U];
+      float psum = 0.f;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        p[u] = valid[u] ? fast_exp2(s[u] - m) : 0.f;
+        psum += p[u];
+      }
+      l = l * alpha + psum;
+
+      float ah[G];
+      if constexpr (G >= 1) ah[0] = from_head<G, 0>(alpha);
+      if constexpr (G >= 2) ah[1] = from_head<G, 1>(alpha);
+      if constexpr (G >= 4) {
+        ah[2] = from_head<G, 2>(alpha);
+        ah[3] = from_head<G, 3>(alpha);
+      }
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[h][e] *= ah[h];
+
+      // rows outside the context (or in an invalid block) may hold anything,
+      // NaN included: select them to zero so that weight 0 gives exactly 0
+      bool full = cbase + CH <= p1;
+#pragma unroll
+      for (int u = 0; u < U; ++u) full = full && ok[u];
+      if (!full) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+          if (!valid[u]) vr[u] = make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < U; u += 2) {
+        uint32_t vp[8];
+        vp[0] = interleave_lo(vr[u].x, vr[u + 1].x);
+        vp[1] = interleave_hi(vr[u].x, vr[u + 1].x);
+        vp[2] = interleave_lo(vr[u].y, vr[u + 1].y);
+        vp[3] = interleave_hi(vr[u].y, vr[u + 1].y);
+        vp[4] = interleave_lo(vr[u].z, vr[u + 1].z);
+        vp[5] = interleave_hi(vr[u].z, vr[u + 1].z);
+        vp[6] = interleave_lo(vr[u].w, vr[u + 1].w);
+        vp[7] = interleave_hi(vr[u].w, vr[u + 1].w);
+        uint32_t pk[G];
+        if constexpr (G >= 1) pk[0] = pack_bf16x2_rne(from_head<G, 0>(p[u]), from_head<G, 0>(p[u + 1]));
+        if constexpr (G >= 2) pk[1] = pack_bf16x2_rne(from_head<G, 1>(p[u]), from_head<G, 1>(p[u + 1]));
+        if constexpr (G >= 4) {
+          pk[2] = pack_bf16x2_rne(from_head<G, 2>(p[u]), from_head<G, 2>(p[u + 1]));
+          pk[3] = pack_bf16x2_rne(from_head<G, 3>(p[u]), from_head<G, 3>(p[u + 1]));
+        }
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[h][e] = dot2_bf16(pk[h], vp[e], acc[h][e]);
+      }
+    }
+
+    // wave totals: sum the rows
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[h][e] = rows_sum<L>(acc[h][e]);
+    l = rows_sum<L>(l);
+  }
+
+  // LDS staging of the W waves' (m, l, acc) for the combine
+  struct Stage {
+    float m[W][G];
+    float l[W][G];
+    float o[W][G][D];
+  };
+
+  __device__ static __forceinline__ void stage(Stage &sm, int wave, int lane, float m, float l,
+                                               const float (&acc)[G][8]) {
+    const int col = lane % L;
+    if (lane < L) {
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sm.o[wave][h][col * 8 + e] = acc[h][e];
+    }
+    if (lane < G) {  // lane c of row 0 owns head c
+      sm.m[wave][lane] = m;
+      sm.l[wave][lane] = l;
+    }
+  }
+
+  // combine of output i = h * D + d over the staged waves: M = max, o and
+  // the sum scaled to M (both 0 when every wave is empty)
+  __device__ static __forceinline__ void combine(const Stage &sm, int i, float &M, float &o, float &lt) {
+    const int h = i / D;
+    const int d = i - h * D;
+    M = sm.m[0][h];
+#pragma unroll
+    for (int w = 1; w < W; ++w) M = fmaxf(M, sm.m[w][h]);
+    o = 0.f;
+    lt = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < W; ++w) {
+        const float mw = sm.m[w][h];
+        const float f = (mw == -INFINITY) ? 0.f : fast_exp2(mw - M);
+        o = fmaf(sm.o[w][h][d], f, o);
+        lt = fmaf(sm.l[w][h], f, lt);
+      }
+    }
+  }
+};
+
 template <int D, int G>
 __global__ void __launch_bounds__(64 * PA_DECODE_WAVES)
 decode_partition_bf16_kernel(const DecodeKernelArgs a) {
-  constexpr int L = D / 8;         // lanes per token row (8 bf16 per lane)
-  constexpr int R = 64 / L;        // token rows per load instruction
-  constexpr int U = PA_DECODE_UNROLL;
-  constexpr int CH = R * U;        // tokens per wave step
-  constexpr int W = PA_DECODE_WAVES;
-  static_assert(U % 2 == 0, "tokens are paired for the P.V dot products");
-
+  using K = Bf16Decode<D, G>;
+  constexpr int W = K::W;
 #if PA_DECODE_ORDER == 1
   const int kvh = blockIdx.x;
   const int seq = blockIdx.y;
@@ -435,8 +635,6 @@ decode_partition_bf16_kernel(const DecodeKernelArgs a) {
 #endif
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
-  const int row = lane / L;
-  const int col = lane % L;
 
   const int ctx = decode_context(a, seq);
   const int nparts = decode_num_partitions(a, ctx);
@@ -445,175 +643,19 @@ decode_partition_bf16_kernel(const DecodeKernelArgs a) {
   const int p0 = part * ps;
   const int p1 = min(ctx, p0 + ps);
 
-  uint32_t qp[G][4];
-  {
-    const uint4 *qv = reinterpret_cast<const uint4 *>(
-        static_cast<const uint16_t *>(a.q) + ((size_t)seq * a.num_heads + (size_t)kvh * G) * D);
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const uint4 c = qv[h * L + col];
-      qp[h][0] = c.x;
-      qp[h][1] = c.y;
-      qp[h][2] = c.z;
-      qp[h][3] = c.w;
-    }
-  }
-  const float sl = a.scale_log2;
-  const size_t slot_stride = (size_t)a.num_kv_heads * D;
-  const uint16_t *kbase = static_cast<const uint16_t *>(a.k_cache) + (size_t)kvh * D;
-  const uint16_t *vbase = static_cast<const uint16_t *>(a.v_cache) + (size_t)kvh * D;
-  const uint32_t lane_bytes = (uint32_t)(((size_t)row * slot_stride + (size_t)col * 8) * 2);
-  const int32_t *bt = a.block_tables + (size_t)seq * a.max_blocks_per_seq;
-  const int shift = a.block_shift;
-  const int bs_mask = (1 << shift) - 1;
+  float m, l, acc[G][8];
+  K::attend(a, seq, kvh, p0, p1, wave, lane, m, l, acc);
 
-  float m = -INFINITY;  // running max of head col % G (base-2 units)
-  float l = 0.f;        // running sum of head col % G
-  float acc[G][8];
-#pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
-
-  const int ntok = p1 - p0;
-  const int nchunks = ntok > 0 ? (ntok + CH - 1) / CH : 0;
-  for (int c = wave; c < nchunks; c += W) {
-    const int cbase = p0 + c * CH;
-    size_t off[U];
-    bool ok[U];
-    chunk_rows<U, R>(off, ok, bt, cbase, p1, shift, bs_mask, a.num_blocks, slot_stride,
-                     a.max_blocks_per_seq);
-    uint4 kr[U], vr[U];
-#if PA_DECODE_PRIO
-    __builtin_amdgcn_s_setprio(3);
-#endif
-    chunk_load<U>(kr, off, kbase, lane_bytes);
-    chunk_load<U>(vr, off, vbase, lane_bytes);
-#if PA_DECODE_PRIO
-    __builtin_amdgcn_s_setprio(0);
-#endif
-    bool valid[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) valid[u] = ok[u] && (cbase + u * R + row < p1);
-
-    float s[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      float d[G];
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        float t = dot2_bf16(qp[h][0], kr[u].x, 0.f);
-        t = dot2_bf16(qp[h][1], kr[u].y, t);
-        t = dot2_bf16(qp[h][2], kr[u].z, t);
-        d[h] = dot2_bf16(qp[h][3], kr[u].w, t);
-      }
-      const float r = row_scatter_sum<L, G>(d, col);
-      s[u] = valid[u] ? r * sl : -INFINITY;
-    }
-    float cm = s[0];
-#pragma unroll
-    for (int u = 1; u < U; ++u) cm = fmaxf(cm, s[u]);
-    cm = rows_max<L>(cm);
-    const float m_new = fmaxf(m, cm);
-    const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m - m_new);
-    m = m_new;
-    float p[U];
-    float psum = 0.f;
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      p[u] = valid[u] ? fast_exp2(s[u] - m) : 0.f;
-      psum += p[u];
-    }
-    l = l * alpha + psum;
-
-    float ah[G];
-    if constexpr (G >= 1) ah[0] = from_head<G, 0>(alpha);
-    if constexpr (G >= 2) ah[1] = from_head<G, 1>(alpha);
-    if constexpr (G >= 4) {
-      ah[2] = from_head<G, 2>(alpha);
-      ah[3] = from_head<G, 3>(alpha);
-    }
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[h][e] *= ah[h];
-
-    // rows outside the context (or in an invalid block) may hold anything,
-    // NaN included: select them to zero so that weight 0 gives exactly 0
-    bool full = cbase + CH <= p1;
-#pragma unroll
-    for (int u = 0; u < U; ++u) full = full && ok[u];
-    if (!full) {
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-        if (!valid[u]) vr[u] = make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int u = 0; u < U; u += 2) {
-      uint32_t vp[8];
-      vp[0] = interleave_lo(vr[u].x, vr[u + 1].x);
-      vp[1] = interleave_hi(vr[u].x, vr[u + 1].x);
-      vp[2] = interleave_lo(vr[u].y, vr[u + 1].y);
-      vp[3] = interleave_hi(vr[u].y, vr[u + 1].y);
-      vp[4] = interleave_lo(vr[u].z, vr[u + 1].z);
-      vp[5] = interleave_hi(vr[u].z, vr[u + 1].z);
-      vp[6] = interleave_lo(vr[u].w, vr[u + 1].w);
-      vp[7] = interleave_hi(vr[u].w, vr[u + 1].w);
-      uint32_t pk[G];
-      if constexpr (G >= 1) pk[0] = pack_bf16x2_rne(from_head<G, 0>(p[u]), from_head<G, 0>(p[u + 1]));
-      if constexpr (G >= 2) pk[1] = pack_bf16x2_rne(from_head<G, 1>(p[u]), from_head<G, 1>(p[u + 1]));
-      if constexpr (G >= 4) {
-        pk[2] = pack_bf16x2_rne(from_head<G, 2>(p[u]), from_head<G, 2>(p[u + 1]));
-        pk[3] = pack_bf16x2_rne(from_head<G, 3>(p[u]), from_head<G, 3>(p[u + 1]));
-      }
-#pragma unroll
-      for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[h][e] = dot2_bf16(pk[h], vp[e], acc[h][e]);
-    }
-
-  }
-
-  // wave totals: sum the rows
-#pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[h][e] = rows_sum<L>(acc[h][e]);
-  l = rows_sum<L>(l);
-
-  __shared__ float sm_m[W][G];
-  __shared__ float sm_l[W][G];
-  __shared__ float sm_o[W][G][D];
-  if (lane < L) {
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) sm_o[wave][h][col * 8 + e] = acc[h][e];
-  }
-  if (lane < G) {  // lane c of row 0 owns head c
-    sm_m[wave][lane] = m;
-    sm_l[wave][lane] = l;
-  }
+  __shared__ typename K::Stage sm;
+  K::stage(sm, wave, lane, m, l, acc);
   __syncthreads();
 
   const bool direct = (nparts == 1);
   for (int i = threadIdx.x; i < G * D; i += 64 * W) {
-    const int h = i / D;
-    const int d = i - h * D;
-    float M = sm_m[0][h];
-#pragma unroll
-    for (int w = 1; w < W; ++w) M = fmaxf(M, sm_m[w][h]);
-    float o = 0.f, lt = 0.f;
-    if (M != -INFINITY) {
-#pragma unroll
-      for (int w = 0; w < W; ++w) {
-        const float mw = sm_m[w][h];
-        const float f = (mw == -INFINITY) ? 0.f : fast_exp2(mw - M);
-        o = fmaf(sm_o[w][h][d], f, o);
-        lt = fmaf(sm_l[w][h], f, lt);
-      }
-    }
-    const int head = kvh * G + h;
+    float M, o, lt;
+    K::combine(sm, i, M, o, lt);
+    const int head = kvh * G + i / D;
+    const int d = i % D;
     if (direct) {
       const float r = (lt > 0.f) ? o / lt : 0.f;
       store_one<bf16_t>(a.out, ((size_t)seq * a.num_heads + head) * D + d, r);

@@ -222,3 +222,15 @@ def test_loose_max_context_len():
     log("loose max_context_len")
     _, got = _run(case, 32, max_context_len=400)
     assert_close(got, ref, W.BF16, "loose bound")
+
+
+
+def test_many_partitions():
+    """Hundreds of partitions of one sequence merged by the reduce kernel."""
+    case = W.random_decode(67, [300 * 32 + 5, 40], num_heads=32, num_kv_heads=8, head_dim=128, block_size=32,
+                           dtype=W.BF16)
+    ref = oracle_decode(case)
+    for ps in (32, 64):
+        log(f"{-(-case.max_context_len // ps)} partitions")
+        _, got = _run(case, ps)
+        assert_close(got, ref, W.BF16, f"ps{ps}")
