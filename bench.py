@@ -277,6 +277,98 @@ def bench_decode_secondary(name, ps, steps=30):
     return res
 
 
+def bench_serving(seed=7000, num_requests=96, num_blocks=12000):
+    """The scheduler driving the kernels over a request trace: every step the
+    host plans (pa_sched_next_step), copies the step's tables through pinned
+    buffers, and launches kv_cache_write plus prefill or decode; the step is
+    then committed with 'sampled' tokens.  K/V/Q values are random device
+    data (they do not change the work).  Reports prompt + generated tokens
+    per second of wall time, and the share of it the GPU was busy."""
+    import torch
+    import paged_attention_kv_cache_amd as P
+    import workloads as W
+
+    Hq, Hkv, D, bs = 32, 8, 128, 32
+    rng = np.random.default_rng(seed)
+    system = rng.integers(1, 32000, 512).tolist()
+    prompts, max_new = {}, {}
+    for r in range(num_requests):
+        body = rng.integers(1, 32000, int(rng.integers(128, 2049))).tolist()
+        prompts[r] = (system + body) if r % 3 == 0 else body
+        max_new[r] = int(rng.integers(32, 257))
+    kvm = P.KvManager(num_blocks, bs)
+    cap_seqs, cap_tokens, cap_blocks = 64, 4096, 128
+    sched = P.StepScheduler(kvm, max_batched_tokens=cap_tokens, max_chunk_tokens=512, max_decode_steps=8,
+                            min_decode_steps=1, max_seqs=cap_seqs, max_blocks_per_seq=cap_blocks)
+    for r in range(num_requests):
+        sched.add_request(r, prompts[r], max_new[r])
+    kc = torch.randn((num_blocks, bs, Hkv, D), device="cuda").to(torch.bfloat16)
+    vc = torch.randn_like(kc)
+    src_k = torch.randn((cap_tokens, Hkv, D), device="cuda").to(torch.bfloat16)
+    src_v = torch.randn_like(src_k)
+    src_q = torch.randn((cap_tokens, Hq, D), device="cuda").to(torch.bfloat16)
+    out = torch.empty_like(src_q)
+    pin = dict(qsl=torch.zeros(cap_seqs + 1, dtype=torch.int32).pin_memory(),
+               ctx=torch.zeros(cap_seqs, dtype=torch.int32).pin_memory(),
+               tab=torch.zeros((cap_seqs, cap_blocks), dtype=torch.int32).pin_memory(),
+               slots=torch.zeros(cap_tokens, dtype=torch.int64).pin_memory())
+    dev = {k: torch.empty_like(v, device="cuda") for k, v in pin.items()}
+    ws = torch.zeros(P.pa_decode_workspace_bytes(cap_seqs, Hq, D, cap_blocks * bs, 256), dtype=torch.uint8,
+                     device="cuda")
+    scale = 1.0 / math.sqrt(D)
+    busy = []
+    prompt_tokens = decode_tokens = steps = 0
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while True:
+        w, a, _ = sched.counts()
+        if w == 0 and a == 0:
+            break
+        st = sched.next_step()
+        n, T = st.num_seqs, st.num_tokens
+        pin["qsl"][: n + 1].numpy()[:] = st.query_start_loc
+        pin["ctx"][:n].numpy()[:] = st.context_lens
+        pin["tab"][:n].numpy()[:] = st.block_tables
+        pin["slots"][:T].numpy()[:] = st.slot_mapping
+        for k in pin:
+            dev[k].copy_(pin[k], non_blocking=True)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        P.pa_kv_cache_write(src_k[:T], src_v[:T], kc, vc, dev["slots"][:T])
+        if st.kind == P.KIND_PROMPT:
+            P.pa_prefill_chunk(src_q[:T], dev["qsl"][: n + 1], kc, vc, dev["tab"][:n], dev["ctx"][:n], scale,
+                               st.max_query_len, st.max_context_len, out=out[:T])
+            prompt_tokens += T
+        else:
+            P.pa_decode(src_q[:n], kc, vc, dev["tab"][:n], dev["ctx"][:n], scale, st.max_context_len, 256,
+                        out=out[:n], workspace=ws)
+            decode_tokens += T
+        e1.record()
+        busy.append((e0, e1))
+        sched.complete_step(rng.integers(1, 32000, n).tolist())
+        steps += 1
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = sum(a.elapsed_time(b) for a, b in busy)
+    st = kvm.stats()
+    res = {
+        "workload": f"{num_requests} requests, prompts U[128,2048] (+512-token shared system prompt on a third), "
+                    f"generation U[32,256]; 32q/8kv, D128, BS32, bf16; budget 4096 tokens, 512-token chunks, "
+                    f"<= 8 decode steps in a row, pool {num_blocks} blocks",
+        "steps": steps, "prompt_tokens": prompt_tokens, "generated_tokens": decode_tokens,
+        "wall_s": round(wall, 3), "tokens_per_s": round((prompt_tokens + decode_tokens) / wall, 1),
+        "gpu_busy_frac": round(gpu_ms * 1e-3 / wall, 3),
+        "prefix_hit_tokens": st["prefix_hit_tokens"],
+    }
+    log(f"serving: {steps} steps, {prompt_tokens} prompt + {decode_tokens} generated tokens in {wall:.2f} s "
+        f"({res['tokens_per_s']:.0f} tokens/s, GPU busy {res['gpu_busy_frac']:.0%})")
+    sched.close()
+    kvm.close()
+    del kc, vc
+    torch.cuda.empty_cache()
+    return res
+
+
 def bench_prefill(args):
     import torch
     import paged_attention_kv_cache_amd as P
@@ -440,6 +532,7 @@ def main():
             bench_decode_secondary("prefix_shared_decode_bs16", 512),
             bench_decode_secondary("prefix_shared_decode_bs8", 512),
         ]
+        line["serving_loop"] = bench_serving()
     if not args.no_cpu_baseline:
         log(f"timing the CPU oracle for ~{args.cpu_seconds:.0f} s")
         line["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
