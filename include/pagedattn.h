@@ -135,6 +135,28 @@ int pa_kv_cache_write(const pa_kv_cache *cache, const void *key, const void *val
                       const int64_t *slot_mapping, int32_t num_tokens, void *stream);
 
 /* ---------------------------------------------------------------------
+ * pa_kv_cache_copy_blocks - copy whole blocks (K and V, every kv head)
+ * from one pool to another, or inside one pool.  [TS] section 11: a pool
+ * grown into a larger allocation keeps the K/V already written; with an id
+ * map the same call copies a shared block into a sequence's own block.
+ *
+ *   src, dst         : pools with the same dtype, block_size, num_kv_heads
+ *                      and head_dim (num_blocks may differ; they may be the
+ *                      same pool).
+ *   src_ids, dst_ids : device, [num_copies] int32, copy i moves block
+ *                      src_ids[i] of src to block dst_ids[i] of dst; or both
+ *                      NULL to copy blocks 0 .. num_copies-1 to the same ids
+ *                      (then num_copies must fit both pools).  A copy whose
+ *                      id is outside its pool is skipped.  Destination ids
+ *                      must be distinct, and no destination block may also
+ *                      be a source block of the same call.
+ *   num_copies       : >= 0.  0 enqueues nothing.
+ * The copy is bit-exact.
+ * --------------------------------------------------------------------- */
+int pa_kv_cache_copy_blocks(const pa_kv_cache *src, const pa_kv_cache *dst, const int32_t *src_ids,
+                            const int32_t *dst_ids, int32_t num_copies, void *stream);
+
+/* ---------------------------------------------------------------------
  * pa_decode_workspace_bytes - bytes of fp32 workspace that split-K decode
  * needs: the per-partition running max m, sum l and unnormalised output
  * o[head_dim] for every (sequence, query head, partition), where there are

@@ -100,6 +100,14 @@ int pa_kvm_request_info(const pa_kvm *m, int64_t request_id, int32_t *num_tokens
 
 int pa_kvm_get_stats(const pa_kvm *m, pa_kvm_stats *stats);
 
+/* Grow the pool to new_num_blocks (>= the current count), after the caller
+ * has moved the device pool into an allocation of that size (e.g. with
+ * pa_kv_cache_copy_blocks; [TS] section 11, the grow path of the paged
+ * buffers).  Block ids already handed out keep their meaning; the new ids
+ * go to the front of the free list, so they are used before any cached
+ * block is recycled. */
+int pa_kvm_grow(pa_kvm *m, int32_t new_num_blocks);
+
 /* ------------------------------------------------------------------------
  * Step scheduler: alternates all-prompt and all-completion steps ([MR]
  * scheduling section).

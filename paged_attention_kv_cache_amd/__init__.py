@@ -5,6 +5,8 @@ The work is done by hand-written HIP kernels behind the C ABI in
 ``paged_attention_kv_cache_amd.build``).  This package is only the binding:
 
 * ``pa_kv_cache_write``  - slot-mapping scatter of new K/V into the pool
+* ``pa_kv_cache_copy_blocks`` - whole-block copies (pool growth, copy of a
+  shared block)
 * ``pa_decode``          - one query per sequence over its context; split-K
   partitions plus reduce (``pa_decode_partition`` / ``pa_decode_reduce``
   run the two stages separately)
@@ -29,11 +31,13 @@ from ._binding import (  # noqa: F401
     pa_decode_partition,
     pa_decode_reduce,
     pa_decode_workspace_bytes,
+    pa_kv_cache_copy_blocks,
     pa_kv_cache_write,
     pa_last_error_message,
     pa_prefill_chunk,
     pa_status_string,
     pa_version,
 )
-from .kv_manager import KIND_DECODE, KIND_IDLE, KIND_PROMPT, KvManager, Step, StepScheduler  # noqa: F401
+from .kv_manager import (KIND_DECODE, KIND_IDLE, KIND_PROMPT, KvManager, Step, StepScheduler,  # noqa: F401
+                         grow_pool)
 from .contracts import check_decode_contracts, check_prefill_contracts, check_slot_mapping  # noqa: F401

@@ -92,6 +92,7 @@ SIGNATURES = {
     "pa_decode_reduce": (ctypes.c_int, [_vp, _i32, _i32, _i32, _i32, _vp, _i32, _i32, _vp, _sz, _vp]),
     "pa_prefill_chunk": (ctypes.c_int, [_PCACHE, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _i32, _vp,
                                         _i32, _f32, _vp]),
+    "pa_kv_cache_copy_blocks": (ctypes.c_int, [_PCACHE, _PCACHE, _vp, _vp, _i32, _vp]),
     "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "pa_last_error_message": (ctypes.c_char_p, []),
     "pa_version": (ctypes.c_int, []),
@@ -108,6 +109,7 @@ SIGNATURES = {
     "pa_kvm_slot_mapping": (ctypes.c_int, [_vp, _i64, _i32, _i32, _pi64]),
     "pa_kvm_request_info": (ctypes.c_int, [_vp, _i64, _pi32, _pi32, _pi32]),
     "pa_kvm_get_stats": (ctypes.c_int, [_vp, ctypes.POINTER(PaKvmStats)]),
+    "pa_kvm_grow": (ctypes.c_int, [_vp, _i32]),
     "pa_sched_create": (_vp, [_vp, ctypes.POINTER(PaSchedConfig)]),
     "pa_sched_destroy": (None, [_vp]),
     "pa_sched_add_request": (ctypes.c_int, [_vp, _i64, _pi32, _i32, _i32]),
@@ -239,6 +241,29 @@ def pa_kv_cache_write(key, value, k_cache, v_cache, slot_mapping, stream=None) -
         ctypes.byref(cache), _dev(key, "key", k_cache.dtype), _dev(value, "value", k_cache.dtype),
         _dev(slot_mapping, "slot_mapping", torch.int64), int(key.shape[0]), _stream(stream))
     _check("pa_kv_cache_write", code)
+
+
+def pa_kv_cache_copy_blocks(src_k, src_v, dst_k, dst_v, src_ids=None, dst_ids=None, num_copies=None,
+                            stream=None) -> None:
+    """Copy whole blocks between pools (or inside one).  With no ids, blocks
+    0 .. num_copies-1 (default: all of the source) go to the same ids."""
+    torch = _torch()
+    src = make_cache(src_k, src_v)
+    dst = make_cache(dst_k, dst_v)
+    if (src_ids is None) != (dst_ids is None):
+        raise ValueError("give both src_ids and dst_ids, or neither")
+    if src_ids is None:
+        n = int(src_k.shape[0]) if num_copies is None else int(num_copies)
+        ps = pd = ctypes.c_void_p(0)
+    else:
+        n = int(src_ids.numel())
+        if int(dst_ids.numel()) != n:
+            raise ValueError("src_ids and dst_ids differ in length")
+        ps = _dev(src_ids, "src_ids", torch.int32)
+        pd = _dev(dst_ids, "dst_ids", torch.int32)
+    code = load_library().pa_kv_cache_copy_blocks(ctypes.byref(src), ctypes.byref(dst), ps, pd, n,
+                                                  _stream(stream))
+    _check("pa_kv_cache_copy_blocks", code)
 
 
 def _decode_args(q, k_cache, v_cache, block_tables, context_lens, out):

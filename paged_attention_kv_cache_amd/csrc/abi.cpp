@@ -214,6 +214,37 @@ int pa_kv_cache_write(const pa_kv_cache *cache, const void *key, const void *val
   return ok();
 }
 
+int pa_kv_cache_copy_blocks(const pa_kv_cache *src, const pa_kv_cache *dst, const int32_t *src_ids,
+                            const int32_t *dst_ids, int32_t num_copies, void *stream) {
+  int st = check_cache(src, false);
+  if (st) return st;
+  if ((st = check_cache(dst, false))) return st;
+  if (src->dtype != dst->dtype)
+    return fail(PA_ERR_DTYPE, "source dtype %d differs from destination dtype %d", src->dtype, dst->dtype);
+  if (src->block_size != dst->block_size || src->num_kv_heads != dst->num_kv_heads ||
+      src->head_dim != dst->head_dim)
+    return fail(PA_ERR_SHAPE, "block shapes differ: source (%d, %d, %d), destination (%d, %d, %d) as "
+                "(block_size, num_kv_heads, head_dim)", src->block_size, src->num_kv_heads, src->head_dim,
+                dst->block_size, dst->num_kv_heads, dst->head_dim);
+  if (num_copies < 0) return fail(PA_ERR_SHAPE, "num_copies %d must be >= 0", num_copies);
+  if ((src_ids == nullptr) != (dst_ids == nullptr))
+    return fail(PA_ERR_NULL, "src_ids=%p dst_ids=%p: give both or neither", (const void *)src_ids,
+                (const void *)dst_ids);
+  if (!src_ids && (num_copies > src->num_blocks || num_copies > dst->num_blocks))
+    return fail(PA_ERR_SHAPE, "identity copy of %d blocks: source has %d, destination %d", num_copies,
+                src->num_blocks, dst->num_blocks);
+  const int64_t block_bytes =
+      (int64_t)src->block_size * src->num_kv_heads * src->head_dim * elem_bytes(src->dtype);
+  if (block_bytes % 16)
+    return fail(PA_ERR_SHAPE, "a block is %lld bytes, not a multiple of 16", (long long)block_bytes);
+  if (num_copies == 0) return ok();
+  hipError_t e = pa::launch_kv_cache_copy_blocks(src->k_cache, src->v_cache, dst->k_cache, dst->v_cache,
+                                                 src->num_blocks, dst->num_blocks, block_bytes, src_ids,
+                                                 dst_ids, num_copies, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "kv_cache_copy_blocks launch");
+  return ok();
+}
+
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
                                  int32_t max_context_len, int32_t partition_size) {
   return workspace_bytes(num_seqs, num_heads, head_dim, max_context_len, partition_size);

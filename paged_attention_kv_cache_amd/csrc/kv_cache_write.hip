@@ -49,4 +49,49 @@ hipError_t launch_kv_cache_write(void *k_cache, void *v_cache, int64_t num_slots
   return hipGetLastError();
 }
 
+// Whole-block copy between pools of the same block shape (or inside one
+// pool): growing a pool into a larger allocation keeps the K/V of the
+// sequences already placed (TensorSharp, Mistral 3 page, section 11, the
+// grow path of the paged buffers), and a block-id map copies shared blocks
+// for a sequence that must write into its own copy.  A block of K (or V) is
+// block_size * num_kv_heads * head_dim contiguous elements; the grid walks
+// 16-byte chunks of every (copy, K|V, block) with 128-bit loads and stores.
+// Copies whose ids fall outside either pool are skipped.
+__global__ void __launch_bounds__(256)
+kv_cache_copy_blocks_kernel(const uint4 *__restrict__ src_k, const uint4 *__restrict__ src_v,
+                            uint4 *__restrict__ dst_k, uint4 *__restrict__ dst_v, int src_blocks,
+                            int dst_blocks, int64_t chunks_per_block, const int32_t *__restrict__ src_ids,
+                            const int32_t *__restrict__ dst_ids, int num_copies) {
+  const int64_t per_copy = 2 * chunks_per_block;  // K then V
+  const int64_t total = (int64_t)num_copies * per_copy;
+  for (int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; g < total;
+       g += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t c = g / per_copy;
+    int64_t r = g - c * per_copy;
+    const bool is_v = r >= chunks_per_block;
+    if (is_v) r -= chunks_per_block;
+    const int sb = src_ids ? src_ids[c] : (int)c;
+    const int db = dst_ids ? dst_ids[c] : (int)c;
+    if ((unsigned)sb >= (unsigned)src_blocks || (unsigned)db >= (unsigned)dst_blocks) continue;
+    const uint4 x = (is_v ? src_v : src_k)[(int64_t)sb * chunks_per_block + r];
+    (is_v ? dst_v : dst_k)[(int64_t)db * chunks_per_block + r] = x;
+  }
+}
+
+hipError_t launch_kv_cache_copy_blocks(const void *src_k, const void *src_v, void *dst_k, void *dst_v,
+                                       int src_blocks, int dst_blocks, int64_t block_bytes,
+                                       const int32_t *src_ids, const int32_t *dst_ids, int num_copies,
+                                       hipStream_t stream) {
+  const int64_t chunks = block_bytes / 16;
+  const int64_t total = (int64_t)num_copies * 2 * chunks;
+  const int threads = 256;
+  int64_t blocks = (total + threads - 1) / threads;
+  if (blocks > 65536) blocks = 65536;  // grid-stride beyond this
+  hipLaunchKernelGGL(kv_cache_copy_blocks_kernel, dim3((unsigned)blocks), dim3(threads), 0, stream,
+                     static_cast<const uint4 *>(src_k), static_cast<const uint4 *>(src_v),
+                     static_cast<uint4 *>(dst_k), static_cast<uint4 *>(dst_v), src_blocks, dst_blocks, chunks,
+                     src_ids, dst_ids, num_copies);
+  return hipGetLastError();
+}
+
 }  // namespace pa

@@ -68,6 +68,16 @@ struct pa_kvm {
   std::unordered_map<int64_t, Request> requests;
   pa_kvm_stats stats{};
 
+  void push_head(int32_t b) {
+    Block &x = blocks[b];
+    x.prev = -1;
+    x.next = head;
+    if (head >= 0) blocks[head].prev = b;
+    else tail = b;
+    head = b;
+    x.in_free = true;
+    ++free_count;
+  }
   void push_tail(int32_t b) {
     Block &x = blocks[b];
     x.prev = tail;
@@ -317,6 +327,21 @@ int pa_kvm_get_stats(const pa_kvm *m, pa_kvm_stats *s) {
   *s = m->stats;
   s->free_blocks = m->free_count;
   s->cached_blocks = (int64_t)m->cache.size();
+  pa::clear_error();
+  return PA_OK;
+}
+
+int pa_kvm_grow(pa_kvm *m, int32_t new_num_blocks) {
+  if (!m) return pa::set_error(PA_ERR_NULL, "manager is NULL");
+  if (new_num_blocks < m->num_blocks)
+    return pa::set_error(PA_ERR_SHAPE, "new_num_blocks %d below the current %d (a pool only grows)", new_num_blocks,
+                         m->num_blocks);
+  const int32_t old = m->num_blocks;
+  m->blocks.resize(new_num_blocks);
+  // fresh blocks in front, lowest id first
+  for (int32_t b = new_num_blocks - 1; b >= old; --b) m->push_head(b);
+  m->num_blocks = new_num_blocks;
+  m->stats.num_blocks = new_num_blocks;
   pa::clear_error();
   return PA_OK;
 }

@@ -185,6 +185,10 @@ struct CacheView {
 hipError_t launch_kv_cache_write(void *k_cache, void *v_cache, int64_t num_slots, int row_bytes,
                                  const void *key, const void *value, const int64_t *slots,
                                  int num_tokens, hipStream_t stream);
+hipError_t launch_kv_cache_copy_blocks(const void *src_k, const void *src_v, void *dst_k, void *dst_v,
+                                       int src_blocks, int dst_blocks, int64_t block_bytes,
+                                       const int32_t *src_ids, const int32_t *dst_ids, int num_copies,
+                                       hipStream_t stream);
 
 struct DecodeArgs {
   CacheView cache;

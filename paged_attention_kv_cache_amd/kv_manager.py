@@ -102,6 +102,11 @@ class KvManager:
             self._h, request_id, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)))
         return a.value, b.value, c.value
 
+    def grow(self, new_num_blocks: int) -> None:
+        """Extend the pool to new_num_blocks (after the device pool moved)."""
+        _check("pa_kvm_grow", self._lib.pa_kvm_grow(self._h, new_num_blocks))
+        self.num_blocks = new_num_blocks
+
     def stats(self) -> dict:
         s = PaKvmStats()
         _check("pa_kvm_get_stats", self._lib.pa_kvm_get_stats(self._h, ctypes.byref(s)))
@@ -191,3 +196,21 @@ class StepScheduler:
         _check("pa_sched_counts", self._lib.pa_sched_counts(self._h, ctypes.byref(a), ctypes.byref(b),
                                                              ctypes.byref(c)))
         return a.value, b.value, c.value
+
+
+def grow_pool(kvm: KvManager, k_cache, v_cache, new_num_blocks: int):
+    """Move a device pool (``[num_blocks, block_size, num_kv_heads,
+    head_dim]`` K and V tensors) into an allocation of ``new_num_blocks``
+    blocks with the library's block copy, and extend the manager to match.
+    Returns the new (K, V) tensors."""
+    import torch
+    from ._binding import pa_kv_cache_copy_blocks
+    old = int(k_cache.shape[0])
+    if new_num_blocks < old:
+        raise ValueError(f"a pool only grows ({old} -> {new_num_blocks})")
+    shape = (new_num_blocks,) + tuple(k_cache.shape[1:])
+    nk = torch.empty(shape, dtype=k_cache.dtype, device=k_cache.device)
+    nv = torch.empty(shape, dtype=v_cache.dtype, device=v_cache.device)
+    pa_kv_cache_copy_blocks(k_cache, v_cache, nk, nv, num_copies=old)
+    kvm.grow(new_num_blocks)
+    return nk, nv

@@ -38,6 +38,11 @@ class OracleBackend:
         self.kc = np.zeros(shape, np.float64)
         self.vc = np.zeros(shape, np.float64)
 
+    def grow(self, kvm, new_num_blocks):
+        pad = lambda c: np.concatenate([c, np.zeros((new_num_blocks - c.shape[0],) + c.shape[1:], c.dtype)])
+        self.kc, self.vc = pad(self.kc), pad(self.vc)
+        kvm.grow(new_num_blocks)
+
     def step(self, st, keys, vals, qs, scale, partition_size):
         f = lambda x: W.storage_to_f32(x, W.BF16).astype(np.float64)
         self.kc, self.vc = oracle.kv_cache_write(self.kc, self.vc, f(keys), f(vals), st.slot_mapping)
@@ -57,6 +62,10 @@ class LibraryBackend:
         shape = (trace.num_blocks, trace.block_size, trace.num_kv_heads, trace.head_dim)
         self.kc = t.zeros(shape, dtype=t.bfloat16, device="cuda")
         self.vc = t.zeros_like(self.kc)
+
+    def grow(self, kvm, new_num_blocks):
+        import paged_attention_kv_cache_amd as P
+        self.kc, self.vc = P.grow_pool(kvm, self.kc, self.vc, new_num_blocks)
 
     def step(self, st, keys, vals, qs, scale, partition_size):
         import paged_attention_kv_cache_amd as P
@@ -78,8 +87,10 @@ class LibraryBackend:
 
 
 def serve_and_check(trace, backend, partition_size=0, max_batched_tokens=256, max_chunk_tokens=128,
-                    max_seqs=8, max_blocks_per_seq=32, tag=""):
-    """Runs the trace to completion; returns a summary dict."""
+                    max_seqs=8, max_blocks_per_seq=32, tag="", grow_at=None):
+    """Runs the trace to completion; returns a summary dict.  ``grow_at``
+    maps a step index to a larger pool size: before that step the backend's
+    pool is moved into the larger allocation and the manager extended."""
     import paged_attention_kv_cache_amd as P
 
     m = P.KvManager(trace.num_blocks, trace.block_size)
@@ -97,6 +108,9 @@ def serve_and_check(trace, backend, partition_size=0, max_batched_tokens=256, ma
         w, a, _ = s.counts()
         if w == 0 and a == 0:
             break
+        if grow_at and step in grow_at:
+            log(f"serving{tag}: pool grows to {grow_at[step]} blocks before step {step}")
+            backend.grow(m, grow_at[step])
         st = s.next_step()
         assert st.kind in (P.KIND_PROMPT, P.KIND_DECODE)
         kinds.append(st.kind)

@@ -222,3 +222,18 @@ def test_workloads_satisfy_contracts():
               W.random_prefill(4, [0, 33], [17, 64], block_size=16)):
         check_slot_mapping(c.slot_mapping, c.num_blocks, c.block_size)
         check_decode_contracts(c.block_tables, c.context_lens, c.num_blocks, c.block_size, c.max_context_len)
+
+
+def test_copy_blocks_validation(lib):
+    a, b = cache(nb=10), cache(nb=20)
+    cp = lambda s, d, si=None, di=None, n=5: lib.pa_kv_cache_copy_blocks(ctypes.byref(s), ctypes.byref(d), si,
+                                                                         di, n, None)
+    assert cp(a, b, n=0) == 0                                    # nothing to do
+    assert cp(a, cache(nb=20, dtype=0)) == -2
+    assert cp(a, cache(nb=20, bs=16)) == -3 and "block shapes differ" in msg()
+    assert cp(a, cache(nb=20, d=64)) == -3
+    assert cp(a, b, si=FAKE) == -1 and "both or neither" in msg()
+    assert cp(a, b, n=-1) == -3
+    assert cp(a, b, n=11) == -3 and "identity copy of 11 blocks" in msg()
+    assert cp(b, a, n=11) == -3
+    assert cp(a, cache(k=0)) == -1

@@ -6,7 +6,7 @@ import pytest
 
 import oracle
 import workloads as W
-from gpu_util import DeviceCase, log, to_host_bits, torch
+from gpu_util import DeviceCase, log, to_dev, to_host_bits, torch
 
 pytestmark = pytest.mark.gpu
 
@@ -58,3 +58,37 @@ def test_write_skips_negative_and_out_of_pool_slots():
 def test_write_chunked_prefill_full_size():
     case = W.make_config("chunked_prefill")
     _check_write(case, "chunked prefill 8 x 512")
+
+
+def test_copy_blocks_grow_and_remap():
+    """Identity copy of a pool into a larger one, and an id-mapped copy inside
+    one pool, are bit-exact; untouched and out-of-range targets stay as they
+    were."""
+    import paged_attention_kv_cache_amd as P
+    t = torch()
+    rng = np.random.default_rng(5)
+    for dtype, shape in ((W.BF16, (37, 16, 8, 128)), (W.F32, (11, 8, 2, 64))):
+        n = shape[0]
+        k = rng.standard_normal(shape).astype(np.float32)
+        v = rng.standard_normal(shape).astype(np.float32)
+        if dtype == W.BF16:
+            k, v = W.f32_to_bf16_bits(k), W.f32_to_bf16_bits(v)
+        dk, dv = to_dev(k, dtype), to_dev(v, dtype)
+        log(f"copy blocks grow {dtype} {shape}")
+        big_k = t.full((n + 9,) + shape[1:], float("nan"), dtype=dk.dtype, device="cuda")
+        big_v = t.full_like(big_k, float("nan"))
+        P.pa_kv_cache_copy_blocks(dk, dv, big_k, big_v)
+        t.cuda.synchronize()
+        gk, gv = to_host_bits(big_k), to_host_bits(big_v)
+        assert np.array_equal(gk[:n], k) and np.array_equal(gv[:n], v)
+        assert np.isnan(W.storage_to_f32(gk[n:], dtype)).all()
+        # id map inside one pool, with one out-of-range pair skipped
+        src = np.array([0, 3, 5, n + 100], dtype=np.int32)
+        dst = np.array([7, 1, 2, 4], dtype=np.int32)
+        log(f"copy blocks remap {dtype}")
+        P.pa_kv_cache_copy_blocks(dk, dv, dk, dv, t.from_numpy(src).cuda(), t.from_numpy(dst).cuda())
+        t.cuda.synchronize()
+        ek, ev = k.copy(), v.copy()
+        for a, b in zip(src[:3], dst[:3]):
+            ek[b], ev[b] = k[a], v[a]
+        assert np.array_equal(to_host_bits(dk), ek) and np.array_equal(to_host_bits(dv), ev)

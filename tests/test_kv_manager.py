@@ -381,3 +381,27 @@ def test_scheduler_errors():
     assert e.value.status == "PA_ERR_REQUEST"
     with pytest.raises(PagedAttnError):
         s2.add_request(2, [], 1)
+
+
+def test_grow_puts_fresh_blocks_first_and_keeps_the_cache():
+    m = KvManager(4, 8)
+    a = toks(32)
+    serve_prompt(m, 1, a)
+    blocks = m.block_table(1).tolist()
+    m.free(1)
+    m.grow(10)
+    st = m.stats()
+    assert st["num_blocks"] == 10 and st["free_blocks"] == 10 and st["cached_blocks"] == 4
+    m.add_request(2, toks(24, base=300))
+    m.get_computed_blocks(2)
+    m.allocate_slots(2, 24)
+    assert m.block_table(2).tolist() == [4, 5, 6]       # fresh ids before recycling cached ones
+    assert m.stats()["evictions"] == 0
+    m.add_request(3, a + [9])
+    assert m.get_computed_blocks(3) == 32                # the old blocks still hit
+    assert m.block_table(3).tolist() == blocks
+    with pytest.raises(PagedAttnError) as e:
+        m.grow(8)
+    assert e.value.status == "PA_ERR_SHAPE"
+    m.grow(10)                                           # same size: nothing changes
+    assert m.stats()["num_blocks"] == 10

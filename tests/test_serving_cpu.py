@@ -18,3 +18,14 @@ def test_scheduled_serving_with_oracle_backend():
     assert r["recomputed"] > 0
     assert 1 in r["kinds"] and 2 in r["kinds"]
     assert r["worst"] < 1e-5  # oracle against oracle: float64 with bf16-valued inputs (rounding only)
+
+
+def test_serving_with_pool_growth_oracle_backend():
+    """The pool grows mid-trace (K/V of placed sequences carried over); every
+    step still reads back exactly the dense attention."""
+    tr = W.serving_trace(seed=6002, num_requests=8, num_blocks=16, prompt_range=(10, 150), new_range=(2, 10),
+                         shared_prefix=32, num_heads=4, num_kv_heads=2, head_dim=64)
+    r = serve_and_check(tr, OracleBackend(tr), max_batched_tokens=128, max_chunk_tokens=64, max_seqs=6,
+                        max_blocks_per_seq=16, tag="-cpu-grow", grow_at={4: 24, 9: 64})
+    assert r["stats"]["num_blocks"] == 64
+    assert r["worst"] < 1e-5

@@ -25,3 +25,12 @@ def test_scheduled_serving_matches_dense_oracle(partition_size):
     assert r["worst"] <= BF16_MAX_ABS
     log(f"serving ps={partition_size}: {r['steps']} steps, worst max-abs {r['worst']:.2e}, "
         f"{r['recomputed']} recomputed, hits {r['stats']['prefix_hit_tokens']} tokens")
+
+
+def test_serving_with_pool_growth():
+    """The device pool grows twice mid-trace through pa_kv_cache_copy_blocks;
+    outputs keep matching the oracle's dense attention."""
+    tr = W.serving_trace(seed=6003, num_requests=12, num_blocks=40)
+    r = serve_and_check(tr, LibraryBackend(tr), partition_size=64, grow_at={6: 56, 14: 160}, tag="-grow")
+    assert r["stats"]["num_blocks"] == 160
+    assert r["worst"] <= BF16_MAX_ABS
