@@ -25,6 +25,11 @@ ARCH = "gfx950"
 SOURCES = ["abi.cpp", "kv_cache_write.hip", "pa_decode.hip", "pa_prefill.hip", "kv_manager.cpp"]
 # plain host C++ (no device code): built by the host compiler
 HOST_SOURCES = {"kv_manager.cpp"}
+# per-source device flags.  The prefill kernel never relies on NaN semantics
+# (masked and poisoned keys are removed by selects on integer conditions and
+# zeroed V rows), so it runs without the IEEE-mode NaN quieting, which would
+# otherwise add a canonicalising move before every max of an MFMA result.
+SOURCE_FLAGS = {"pa_prefill.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans"]}
 HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-I", INCLUDE, "-I", CSRC]
 
 COMMON_FLAGS = [
@@ -48,7 +53,7 @@ def _compile(src: str, extra: list[str], build_dir: str = BUILD) -> str:
     if src in HOST_SOURCES:
         cmd = [os.environ.get("CXX", "g++"), *HOST_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
     else:
-        cmd = [hipcc(), *COMMON_FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [hipcc(), *COMMON_FLAGS, *SOURCE_FLAGS.get(src, []), *extra, "-c", os.path.join(CSRC, src), "-o", obj]
         if src.endswith(".cpp"):
             cmd[1:1] = ["-x", "hip"]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -95,6 +95,12 @@ __device__ __forceinline__ bf16x8_t pack8(const f32x16_t &s, int base) {
 #define PA_PREFILL_WAVES 8
 #endif
 constexpr int kPrefillThreads = 64 * PA_PREFILL_WAVES;
+#ifndef PA_PREFILL_VPAD
+#define PA_PREFILL_VPAD 4
+#endif
+#ifndef PA_PREFILL_ORDER
+#define PA_PREFILL_ORDER 1
+#endif
 
 template <int D>
 struct TileRegs {
@@ -106,44 +112,74 @@ struct TileRegs {
   bool kok[NK], vaok[NV], vbok[NV];
 };
 
+// Per-thread constants of the tile gather.  A tile starts at a multiple of
+// 64 keys and the block size divides 64, so a thread's key, its block's
+// index inside the tile, its row inside that block and its 16-byte column
+// are the same for every tile; only the block ids change.
+template <int D>
+struct TileLanes {
+  static constexpr int C16 = D / 8;
+  int kkey[TileRegs<D>::NK];   // key of K chunk j (or 64: no chunk)
+  int kblk[TileRegs<D>::NK];   // its block's index inside the tile
+  uint32_t koff[TileRegs<D>::NK];  // element offset inside the block
+  int vkey[TileRegs<D>::NV];   // first key of V pair j (or 64)
+  int vblk[TileRegs<D>::NV];
+  uint32_t voff[TileRegs<D>::NV];
+};
+
 constexpr int kMaxTileBlocks = 8;  // 64 keys / smallest block size
 
-// block ids of the tile starting at key k0 (64 / block_size entries); the
-// work-group keeps them in a tiny LDS array, filled two tiles ahead
-__device__ __forceinline__ int tile_block_id(const int32_t *bt, int k0, int j, int shift, int max_blocks) {
-  return bt[min((k0 >> shift) + j, max_blocks - 1)];
-}
-
 template <int D>
-__device__ __forceinline__ void tile_load(TileRegs<D> &r, const int *ids, const uint16_t *kbase,
-                                          const uint16_t *vbase, int k0, int kend, int shift, int bs_mask,
-                                          int num_blocks, size_t slot_stride, int tid) {
+__device__ __forceinline__ void tile_lanes(TileLanes<D> &t, int tid, int shift, int bs_mask, uint32_t slot_stride) {
   constexpr int C16 = D / 8;
 #pragma unroll
   for (int j = 0; j < TileRegs<D>::NK; ++j) {
     const int i = tid + kPrefillThreads * j;
-    const int key = (i / C16) & 63;
-    const int blk = ids[key >> shift];
-    const bool ok = (i < 64 * C16) && (k0 + key < kend) && ((unsigned)blk < (unsigned)num_blocks);
-    const size_t slot = ok ? ((size_t)blk << shift) + (size_t)((k0 + key) & bs_mask) : 0;
-    r.k[j] = *reinterpret_cast<const uint4 *>(kbase + slot * slot_stride + (i % C16) * 8);
-    r.kok[j] = ok;
+    const int key = (i < 64 * C16) ? (i / C16) : 64;
+    t.kkey[j] = key;
+    t.kblk[j] = (key & 63) >> shift;
+    t.koff[j] = (uint32_t)(key & bs_mask) * slot_stride + (uint32_t)(i % C16) * 8;
   }
 #pragma unroll
   for (int j = 0; j < TileRegs<D>::NV; ++j) {
     const int i = tid + kPrefillThreads * j;
-    const int key = 2 * (i % 32);
-    const int c = (i / 32) % C16;
-    const int blk = ids[key >> shift];  // keys 2p and 2p+1 share a block
-    const bool inb = (i < 32 * C16) && ((unsigned)blk < (unsigned)num_blocks);
-    const bool oka = inb && (k0 + key < kend);
-    const bool okb = inb && (k0 + key + 1 < kend);
-    const size_t slot = oka ? ((size_t)blk << shift) + (size_t)((k0 + key) & bs_mask) : 0;
-    const uint16_t *src = vbase + slot * slot_stride + c * 8;
-    r.va[j] = *reinterpret_cast<const uint4 *>(src);
-    r.vb[j] = *reinterpret_cast<const uint4 *>(src + (oka ? slot_stride : 0));
-    r.vaok[j] = oka;
-    r.vbok[j] = okb;
+    const int key = (i < 32 * C16) ? 2 * (i % 32) : 64;
+    t.vkey[j] = key;
+    t.vblk[j] = (key & 63) >> shift;
+    t.voff[j] = (uint32_t)(key & bs_mask) * slot_stride + (uint32_t)((i / 32) % C16) * 8;
+  }
+}
+
+// block ids of the tile starting at key k0 (64 / block_size entries); the
+// work-group keeps them in a tiny LDS array, filled ahead of time
+__device__ __forceinline__ int tile_block_id(const int32_t *bt, int k0, int j, int shift, int max_blocks) {
+  return bt[min((k0 >> shift) + j, max_blocks - 1)];
+}
+
+// Gather of one K/V tile (keys k0 .. k0+63) into registers.  Loads are
+// unconditional: a key at or past kend, or in an invalid block, reads a row
+// of block 0 instead (inside the pool) and is fixed when stored.
+template <int D>
+__device__ __forceinline__ void tile_load(TileRegs<D> &r, const TileLanes<D> &t, const int *ids,
+                                          const uint16_t *kbase, const uint16_t *vbase, int k0, int kend,
+                                          int num_blocks, size_t block_stride, uint32_t slot_stride) {
+#pragma unroll
+  for (int j = 0; j < TileRegs<D>::NK; ++j) {
+    const int blk = ids[t.kblk[j]];
+    const bool ok = (t.kkey[j] < 64) && ((unsigned)blk < (unsigned)num_blocks);
+    const size_t base = (size_t)(ok ? blk : 0) * block_stride + t.koff[j];
+    r.k[j] = *reinterpret_cast<const uint4 *>(kbase + base);
+    r.kok[j] = ok || t.kkey[j] >= 64;  // K of a masked key needs no fix: its score is replaced
+  }
+#pragma unroll
+  for (int j = 0; j < TileRegs<D>::NV; ++j) {
+    const int blk = ids[t.vblk[j]];  // keys 2p and 2p+1 share a block
+    const bool inb = (t.vkey[j] < 64) && ((unsigned)blk < (unsigned)num_blocks);
+    const size_t base = (size_t)(inb ? blk : 0) * block_stride + t.voff[j];
+    r.va[j] = *reinterpret_cast<const uint4 *>(vbase + base);
+    r.vb[j] = *reinterpret_cast<const uint4 *>(vbase + base + slot_stride);
+    r.vaok[j] = inb && (k0 + t.vkey[j] < kend);
+    r.vbok[j] = inb && (k0 + t.vkey[j] + 1 < kend);
   }
 }
 
@@ -154,13 +190,28 @@ __device__ __forceinline__ uint4 keep_if(bool ok, const uint4 &v) {
 }
 
 template <int D, int KSTR, int VSTR>
-__device__ __forceinline__ void tile_store(const TileRegs<D> &r, uint16_t *sk, uint16_t *svt, int tid) {
+__device__ __forceinline__ void tile_store(TileRegs<D> &r, uint16_t *sk, uint16_t *svt, int tid) {
   constexpr int C16 = D / 8;
+  // zero what must not enter the products (rare: the last tile, or a block
+  // id outside the pool); the common full tile skips the selects
+  bool all_ok = true;
+#pragma unroll
+  for (int j = 0; j < TileRegs<D>::NK; ++j) all_ok = all_ok && r.kok[j];
+#pragma unroll
+  for (int j = 0; j < TileRegs<D>::NV; ++j) all_ok = all_ok && r.vaok[j] && r.vbok[j];
+  if (!all_ok) {
+#pragma unroll
+    for (int j = 0; j < TileRegs<D>::NK; ++j) r.k[j] = keep_if(r.kok[j], r.k[j]);
+#pragma unroll
+    for (int j = 0; j < TileRegs<D>::NV; ++j) {
+      r.va[j] = keep_if(r.vaok[j], r.va[j]);
+      r.vb[j] = keep_if(r.vbok[j], r.vb[j]);
+    }
+  }
 #pragma unroll
   for (int j = 0; j < TileRegs<D>::NK; ++j) {
     const int i = tid + kPrefillThreads * j;
-    if (i < 64 * C16)
-      *reinterpret_cast<uint4 *>(sk + (i / C16) * KSTR + (i % C16) * 8) = keep_if(r.kok[j], r.k[j]);
+    if (i < 64 * C16) *reinterpret_cast<uint4 *>(sk + (i / C16) * KSTR + (i % C16) * 8) = r.k[j];
   }
 #pragma unroll
   for (int j = 0; j < TileRegs<D>::NV; ++j) {
@@ -170,8 +221,8 @@ __device__ __forceinline__ void tile_store(const TileRegs<D> &r, uint16_t *sk, u
       const int c = i / 32;
       uint32_t *dst = reinterpret_cast<uint32_t *>(svt + (c * 8) * VSTR + 2 * p);
       constexpr int W = VSTR / 2;  // dwords per V^T row
-      const uint4 a = keep_if(r.vaok[j], r.va[j]);
-      const uint4 b = keep_if(r.vbok[j], r.vb[j]);
+      const uint4 a = r.va[j];
+      const uint4 b = r.vb[j];
       dst[0 * W] = interleave_lo(a.x, b.x);
       dst[1 * W] = interleave_hi(a.x, b.x);
       dst[2 * W] = interleave_lo(a.y, b.y);
@@ -189,6 +240,8 @@ __device__ __forceinline__ void tile_store(const TileRegs<D> &r, uint16_t *sk, u
 // which the fp32 accumulators and the bf16 weights carry exactly as well
 constexpr float kRescaleSlack = 8.f;
 
+constexpr uint32_t kBf16PairOnes = 0x3F803F80u;  // two bf16 1.0
+
 template <int D, int G>
 __global__ void __launch_bounds__(kPrefillThreads, 8 / PA_PREFILL_WAVES)
 prefill_chunk_kernel(const PrefillKernelArgs a) {
@@ -199,7 +252,7 @@ prefill_chunk_kernel(const PrefillKernelArgs a) {
   constexpr int QT = 32 * TG;        // query tokens per work-group
   constexpr int KT = 64;             // keys per tile
   constexpr int KSTR = D + 8;        // LDS row stride of K, bf16 elements
-  constexpr int VSTR = KT + 8;       // LDS row stride of V^T, bf16 elements
+  constexpr int VSTR = KT + PA_PREFILL_VPAD;  // LDS row stride of V^T, bf16 elements
   constexpr int NDS = D / 16;        // k-steps of Q K^T
   constexpr int NDT = D / 32;        // 32-row tiles of O^T
 
@@ -220,10 +273,17 @@ prefill_chunk_kernel(const PrefillKernelArgs a) {
   const int wid = (bid & 7) * (nwg >> 3) + (bid >> 3);
   if (wid >= a.n_work) return;
   int rest = wid;
+#if PA_PREFILL_ORDER == 1
+  const int qt_rev = rest % a.n_qtiles;
+  rest /= a.n_qtiles;
+  const int seq = rest % a.num_seqs;
+  rest /= a.num_seqs;
+#else
   const int seq = rest % a.num_seqs;
   rest /= a.num_seqs;
   const int qt_rev = rest % a.n_qtiles;
   rest /= a.n_qtiles;
+#endif
   const int half = rest % HALVES;
   const int kvh = rest / HALVES;
   const int qtile = a.n_qtiles - 1 - qt_rev;
@@ -264,13 +324,16 @@ prefill_chunk_kernel(const PrefillKernelArgs a) {
   const int kend = max(0, min(ctx, prefix + t_last + 1));
   const int ntiles = (kend + KT - 1) / KT;
 
-  const size_t slot_stride = (size_t)a.num_kv_heads * D;
+  const uint32_t slot_stride = (uint32_t)a.num_kv_heads * D;
+  const size_t block_stride = (size_t)slot_stride << a.block_shift;
   const uint16_t *kbase = static_cast<const uint16_t *>(a.k_cache) + (size_t)kvh * D;
   const uint16_t *vbase = static_cast<const uint16_t *>(a.v_cache) + (size_t)kvh * D;
   const int32_t *bt = a.block_tables + (size_t)seq * a.max_blocks_per_seq;
   const int shift = a.block_shift;
   const int bs_mask = (1 << shift) - 1;
   const float sl = a.scale_log2;
+  TileLanes<D> lanes;
+  tile_lanes<D>(lanes, tid, shift, bs_mask, slot_stride);
 
   float m = -INFINITY;  // reference max of this lane's query (base-2 units)
   float l = 0.f;        // running sum over this lane's keys
@@ -306,9 +369,9 @@ prefill_chunk_kernel(const PrefillKernelArgs a) {
   }
   __syncthreads();
   TileRegs<D> tr;
-  tile_load<D>(tr, sid[0], kbase, vbase, 0, kend, shift, bs_mask, a.num_blocks, slot_stride, tid);
+  tile_load<D>(tr, lanes, sid[0], kbase, vbase, 0, kend, a.num_blocks, block_stride, slot_stride);
   tile_store<D, KSTR, VSTR>(tr, sk[0], svt[0], tid);
-  tile_load<D>(tr, sid[1], kbase, vbase, KT, kend, shift, bs_mask, a.num_blocks, slot_stride, tid);
+  tile_load<D>(tr, lanes, sid[1], kbase, vbase, KT, kend, a.num_blocks, block_stride, slot_stride);
   tile_store<D, KSTR, VSTR>(tr, sk[1], svt[1], tid);
   __syncthreads();
 
@@ -321,7 +384,7 @@ prefill_chunk_kernel(const PrefillKernelArgs a) {
     const int b1 = (kt + 1) % 3;
     const int b2 = (kt + 2) % 3;
     // tile t+2 from the pool (past the last tile: in-pool rows, zeroed)
-    tile_load<D>(tr, sid[b2], kbase, vbase, k0 + 2 * KT, kend, shift, bs_mask, a.num_blocks, slot_stride, tid);
+    tile_load<D>(tr, lanes, sid[b2], kbase, vbase, k0 + 2 * KT, kend, a.num_blocks, block_stride, slot_stride);
     int next_id = 0;
     if (tid < kMaxTileBlocks) next_id = tile_block_id(bt, k0 + 3 * KT, tid, shift, a.max_blocks_per_seq);
 
@@ -337,7 +400,7 @@ prefill_chunk_kernel(const PrefillKernelArgs a) {
     }
     float rmax = -INFINITY;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) rmax = fmaxf(rmax, fmaxf(c0[r], c1[r]));
+    for (int r = 0; r < 16; ++r) rmax = fmaxf(fmaxf(rmax, c0[r]), c1[r]);
     const float tmax = xor32_max(rmax) * sl;  // scale > 0 keeps the order
     const bool grow = tmax > m + kRescaleSlack;
     if (__builtin_amdgcn_ballot_w64(grow)) {
@@ -358,16 +421,11 @@ prefill_chunk_kernel(const PrefillKernelArgs a) {
     f32x16_t n0, n1;
     qk(sk[b1], n0, n1);
     const float nm = (m == -INFINITY) ? 0.f : -m;  // rows with no key yet: every score is -inf
-    float psum = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const float p0 = fast_exp2(fmaf(c0[r], sl, nm));
-      const float p1 = fast_exp2(fmaf(c1[r], sl, nm));
-      c0[r] = p0;
-      c1[r] = p1;
-      psum += p0 + p1;
+      c0[r] = fast_exp2(fmaf(c0[r], sl, nm));
+      c1[r] = fast_exp2(fmaf(c1[r], sl, nm));
     }
-    l += psum;
 #if PA_PREFILL_INTERLEAVE
 #pragma unroll
     for (int i = 0; i < 2 * NDS; ++i) {
@@ -384,6 +442,20 @@ prefill_chunk_kernel(const PrefillKernelArgs a) {
     pb[1] = pack8(c0, 8);
     pb[2] = pack8(c1, 0);
     pb[3] = pack8(c1, 8);
+    // the running sum takes the same bf16 weights that multiply V, two at a
+    // time (v_dot2_f32_bf16 against ones), so numerator and denominator agree
+    {
+      float ps = 0.f;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint4 w = __builtin_bit_cast(uint4, pb[u]);
+        ps = dot2_bf16(w.x, kBf16PairOnes, ps);
+        ps = dot2_bf16(w.y, kBf16PairOnes, ps);
+        ps = dot2_bf16(w.z, kBf16PairOnes, ps);
+        ps = dot2_bf16(w.w, kBf16PairOnes, ps);
+      }
+      l += ps;
+    }
 
     // O^T += V^T P^T; the A operand takes the same keys from row d of V^T
     const uint16_t *svb = svt[b0];
