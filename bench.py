@@ -200,7 +200,7 @@ def bench_decode(args):
     return res
 
 
-def bench_decode_secondary(name, ps, steps=30):
+def bench_decode_secondary(name, ps, steps=30, groups=None):
     """Decode partition + reduce on another workload: time per launch pair
     (back to back over rotated pools), logical KV GB/s (every context token
     of every sequence) and unique KV GB/s (each shared physical block once)."""
@@ -270,6 +270,33 @@ def bench_decode_secondary(name, ps, steps=30):
         "unique_kv_hbm_frac": round(unique / (t_part * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "logical_kv_bytes": logical, "unique_kv_bytes": unique,
     }
+    if groups:
+        # cascade decode: the shared blocks read once per group
+        gs = torch.tensor(groups[0], dtype=torch.int32, device="cuda")
+        sl = torch.tensor(groups[1], dtype=torch.int32, device="cuda")
+        mg = max(b - a for a, b in zip(groups[0][:-1], groups[0][1:]))
+        wsc = torch.empty(max(P.pa_decode_cascade_workspace_bytes(S, H, D, mcl, ps), 1), dtype=torch.uint8,
+                          device="cuda")
+
+        def casc(i):
+            k, v = pools[i % R]
+            P.pa_decode_cascade(q, k, v, bt, cl, case.scale, mcl, gs, sl, mg, ps, out=out, workspace=wsc,
+                                max_shared_len=max(groups[1]))
+
+        for i in range(4):
+            casc(i)
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(steps):
+            casc(i)
+        e1.record()
+        torch.cuda.synchronize()
+        t_c = e0.elapsed_time(e1) / steps
+        res["cascade_us"] = round(t_c * 1e3, 2)
+        res["cascade_tokens_per_s"] = round(S / (t_c * 1e-3), 1)
+        res["cascade_unique_kv_gbps"] = round(unique / (t_c * 1e-3) / 1e9, 1)
+        res["cascade_unique_kv_hbm_frac"] = round(unique / (t_c * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)
+        log(f"{name}: cascade {t_c * 1e3:.1f} us, unique {res['cascade_unique_kv_gbps']:.0f} GB/s")
     log(f"{name}: partition {t_part * 1e3:.1f} us, +reduce {t_both * 1e3:.1f} us, "
         f"logical {res['logical_kv_gbps']:.0f} GB/s, unique {res['unique_kv_gbps']:.0f} GB/s")
     del pools
@@ -369,12 +396,12 @@ def bench_serving(seed=7000, num_requests=96, num_blocks=12000):
     return res
 
 
-def bench_prefill(args):
+def bench_prefill(args, block_size=32):
     import torch
     import paged_attention_kv_cache_amd as P
     import workloads as W
 
-    case = W.make_config("chunked_prefill", poison=False)
+    case = W.chunked_prefill(poison=False, block_size=block_size)
     k = to_dev(case.k_cache, case.dtype)
     v = to_dev(case.v_cache, case.dtype)
     q = to_dev(case.q, case.dtype)
@@ -526,11 +553,18 @@ def main():
                          "traffic": traffic_from_profiles("prefill_chunk", pre["src"]),
                          "algorithmic_flops_per_launch": pre["flops"]},
         }
+    if not args.quick and pre is not None:
+        line["prefill_other_block_sizes"] = []
+        for bs in (16, 8):
+            p2 = bench_prefill(args, block_size=bs)
+            line["prefill_other_block_sizes"].append({
+                "block_size": bs, "us": round(p2["us"], 2), "tokens_per_s": round(p2["tokens_per_s"], 1),
+                "tflops": round(p2["tflops"], 1), "mfma_frac": round(p2["frac"], 4)})
     if not args.quick:
         line["decode_other_workloads"] = [
             bench_decode_secondary("long_context_decode", 512),
-            bench_decode_secondary("prefix_shared_decode_bs16", 512),
-            bench_decode_secondary("prefix_shared_decode_bs8", 512),
+            bench_decode_secondary("prefix_shared_decode_bs16", 512, groups=([0, 16, 32, 48, 64], [64 * 16] * 4)),
+            bench_decode_secondary("prefix_shared_decode_bs8", 512, groups=([0, 16, 32, 48, 64], [64 * 8] * 4)),
         ]
         line["serving_loop"] = bench_serving()
     if not args.no_cpu_baseline:

@@ -232,6 +232,51 @@ int pa_decode_reduce(void *out, int32_t dtype, int32_t num_seqs, int32_t num_hea
                      void *stream);
 
 /* ---------------------------------------------------------------------
+ * pa_decode_cascade - pa_decode for a batch whose sequences come in groups
+ * that share a prefix of whole blocks (the same physical blocks lead their
+ * block tables, as the block-hash prefix cache of [MR] produces; [TS]
+ * section 11 reuses blocks across sequences the same way).  The shared
+ * tokens are read once per group: an MFMA pass computes every member's
+ * attention over them (one split-K partial per 128-token chunk), the
+ * members' own tokens run as split-K partitions after those, and the
+ * reduce merges all of them.  The workspace holds
+ * ceil(max_context_len / 128) + ceil(max_context_len / partition_size)
+ * partials per (row, head).  The result
+ * is pa_decode's up to rounding.
+ *
+ *   cache ... partition_size : as pa_decode (partition_size > 0 required).
+ *   num_groups     : >= 1 when num_seqs > 0.
+ *   group_start    : device, [num_groups + 1] int32, ascending, from 0 to
+ *                    num_seqs: group g is rows group_start[g] ..
+ *                    group_start[g+1]-1 (a sequence sharing nothing is a
+ *                    group of one with shared_len 0).
+ *   shared_len     : device, [num_groups] int32, tokens the group shares (a
+ *                    multiple of block_size): every row of the group that
+ *                    has a token at position p < shared_len keeps it in the
+ *                    same block.  The shared blocks are read through the
+ *                    table of the group's longest row; a row whose context
+ *                    ends inside the shared part sees only its own tokens.
+ *   max_group_size : host int, >= every group's size (sizes the grid).
+ *   max_shared_len : host int, >= 0, an upper bound of shared_len that sizes
+ *                    the shared pass's grid (ceil(max_shared_len / 128)
+ *                    chunks per group).  A shared_len above it is clamped
+ *                    to 128 * that many chunks; the tokens past the clamp
+ *                    run in the members' own partitions, so the result
+ *                    stays correct and only the sharing is lost.
+ *   workspace      : device, >= pa_decode_cascade_workspace_bytes(...)
+ *                    bytes; scratch.
+ * bf16 only, num_heads / num_kv_heads in {1, 2, 4} (PA_ERR_UNSUPPORTED
+ * otherwise).
+ * --------------------------------------------------------------------- */
+size_t pa_decode_cascade_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                         int32_t max_context_len, int32_t partition_size);
+int pa_decode_cascade(const pa_kv_cache *cache, void *out, const void *q, int32_t num_seqs, int32_t num_heads,
+                      const int32_t *block_tables, int32_t max_blocks_per_seq, const int32_t *context_lens,
+                      int32_t max_context_len, float scale, int32_t partition_size, int32_t num_groups,
+                      const int32_t *group_start, const int32_t *shared_len, int32_t max_group_size,
+                      int32_t max_shared_len, void *workspace, size_t workspace_bytes, void *stream);
+
+/* ---------------------------------------------------------------------
  * pa_prefill_chunk - causal attention of a packed chunk of new tokens per
  * sequence over that sequence's cached prefix plus the chunk itself.
  * [TS] section 3: scaled causal GQA; the chunk's K/V are written with

@@ -10,6 +10,9 @@ The work is done by hand-written HIP kernels behind the C ABI in
 * ``pa_decode``          - one query per sequence over its context; split-K
   partitions plus reduce (``pa_decode_partition`` / ``pa_decode_reduce``
   run the two stages separately)
+* ``pa_decode_cascade``  - decode of groups sharing a prefix of whole blocks,
+  the shared tokens read once per group (an MFMA pass) and merged with each
+  sequence's own split-K partitions
 * ``pa_prefill_chunk``   - causal attention of packed chunks over their
   cached prefixes (bf16 MFMA)
 
@@ -28,6 +31,8 @@ from ._binding import (  # noqa: F401
     load_library,
     make_cache,
     pa_decode,
+    pa_decode_cascade,
+    pa_decode_cascade_workspace_bytes,
     pa_decode_partition,
     pa_decode_reduce,
     pa_decode_workspace_bytes,

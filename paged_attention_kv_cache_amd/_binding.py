@@ -93,6 +93,9 @@ SIGNATURES = {
     "pa_prefill_chunk": (ctypes.c_int, [_PCACHE, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _i32, _vp,
                                         _i32, _f32, _vp]),
     "pa_kv_cache_copy_blocks": (ctypes.c_int, [_PCACHE, _PCACHE, _vp, _vp, _i32, _vp]),
+    "pa_decode_cascade_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
+    "pa_decode_cascade": (ctypes.c_int, [_PCACHE, _vp, _vp, _i32, _i32, _vp, _i32, _vp, _i32, _f32, _i32, _i32,
+                                         _vp, _vp, _i32, _i32, _vp, _sz, _vp]),
     "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "pa_last_error_message": (ctypes.c_char_p, []),
     "pa_version": (ctypes.c_int, []),
@@ -337,6 +340,38 @@ def pa_decode_reduce(q, k_cache, v_cache, block_tables, context_lens, scale, max
     """Second stage of :func:`pa_decode` (same arguments as the first)."""
     return pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len,
                      partition_size, out=out, workspace=workspace, stream=stream, _stage="reduce")
+
+
+def pa_decode_cascade_workspace_bytes(num_seqs: int, num_heads: int, head_dim: int, max_context_len: int,
+                                      partition_size: int) -> int:
+    return int(load_library().pa_decode_cascade_workspace_bytes(num_seqs, num_heads, head_dim, max_context_len,
+                                                                partition_size))
+
+
+def pa_decode_cascade(q, k_cache, v_cache, block_tables, context_lens, scale: float, max_context_len: int,
+                      group_start, shared_len, max_group_size: int, partition_size: int = 256, out=None,
+                      workspace=None, stream=None, max_shared_len: Optional[int] = None):
+    """Decode of groups that share a prefix of whole blocks: the shared
+    tokens are read once per group (``group_start [G+1]``, ``shared_len
+    [G]`` int32 GPU tensors; ``max_group_size`` and ``max_shared_len`` host
+    ints, the latter defaulting to ``max_context_len``)."""
+    torch = _torch()
+    cache, S, H, D, out, (p_out, p_q, p_bt, p_cl) = _decode_args(q, k_cache, v_cache, block_tables,
+                                                                 context_lens, out)
+    G = int(shared_len.numel())
+    if tuple(group_start.shape) != (G + 1,):
+        raise ValueError(f"group_start {tuple(group_start.shape)} must be [{G + 1}]")
+    lib = load_library()
+    need = int(lib.pa_decode_cascade_workspace_bytes(S, H, D, int(max_context_len), int(partition_size)))
+    p_ws, ws_bytes = _workspace(workspace, need, q.device)
+    code = lib.pa_decode_cascade(ctypes.byref(cache), p_out, p_q, S, H, p_bt, int(block_tables.shape[1]), p_cl,
+                                 int(max_context_len), float(scale), int(partition_size), G,
+                                 _dev(group_start, "group_start", torch.int32),
+                                 _dev(shared_len, "shared_len", torch.int32), int(max_group_size),
+                                 int(max_context_len if max_shared_len is None else max_shared_len), p_ws,
+                                 ws_bytes, _stream(stream))
+    _check("pa_decode_cascade", code)
+    return out
 
 
 def pa_prefill_chunk(q, query_start_loc, k_cache, v_cache, block_tables, context_lens, scale: float,

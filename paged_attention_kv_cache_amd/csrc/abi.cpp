@@ -9,6 +9,8 @@
 // is an error, not a silent fallback.  Each message names the expected
 // values and the value received.
 #include <math.h>
+
+#include <algorithm>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -119,7 +121,8 @@ size_t workspace_bytes(int num_seqs, int num_heads, int head_dim, int max_contex
 int prepare_decode(const pa_kv_cache *cache, void *out, const void *q, int32_t num_seqs,
                    int32_t num_heads, const int32_t *block_tables, int32_t max_blocks_per_seq,
                    const int32_t *context_lens, int32_t max_context_len, float scale,
-                   int32_t partition_size, void *workspace, size_t ws_bytes, pa::DecodeArgs *a) {
+                   int32_t partition_size, void *workspace, size_t ws_bytes, pa::DecodeArgs *a,
+                   bool split_k_workspace = true) {
   int st = check_cache(cache, true);
   if (st) return st;
   if ((st = check_heads(cache, num_heads))) return st;
@@ -136,7 +139,9 @@ int prepare_decode(const pa_kv_cache *cache, void *out, const void *q, int32_t n
     return fail(PA_ERR_NULL, "out=%p q=%p block_tables=%p context_lens=%p: all must be device pointers",
                 out, q, (const void *)block_tables, (const void *)context_lens);
   const int P = num_partitions(max_context_len, partition_size);
-  const size_t need = workspace_bytes(num_seqs, num_heads, cache->head_dim, max_context_len, partition_size);
+  const size_t need = split_k_workspace
+                          ? workspace_bytes(num_seqs, num_heads, cache->head_dim, max_context_len, partition_size)
+                          : 0;
   if (need > 0) {
     if (!workspace) return fail(PA_ERR_WORKSPACE, "workspace is NULL; %zu bytes needed", need);
     if (ws_bytes < need)
@@ -323,6 +328,110 @@ int pa_decode(const pa_kv_cache *cache, void *out, const void *q, int32_t num_se
   if (e != hipSuccess) return hip_fail(e, "decode partition launch");
   e = pa::launch_decode_reduce(a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "decode reduce launch");
+  return ok();
+}
+
+// cascade decode: tokens per chunk of the shared part (one work-group and
+// one partial slot each; two 64-key tiles, so that the chunks fill the GPU)
+constexpr int kCascadeChunk = 128;
+
+// slots per (row, head): chunks of the shared part, then partitions of the
+// row's own tokens
+int cascade_slots(int max_context_len, int partition_size) {
+  const int c = std::max(1, (max_context_len + kCascadeChunk - 1) / kCascadeChunk);
+  return c + std::max(1, num_partitions(max_context_len, partition_size));
+}
+
+size_t pa_decode_cascade_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                         int32_t max_context_len, int32_t partition_size) {
+  if (num_seqs <= 0 || num_heads <= 0 || head_dim <= 0 || max_context_len < 0 || partition_size <= 0) return 0;
+  const size_t P = (size_t)cascade_slots(max_context_len, partition_size);
+  const size_t n = (size_t)num_seqs * num_heads * P;
+  return 2 * align256(n * sizeof(float)) + align256(n * head_dim * sizeof(float));
+}
+
+int pa_decode_cascade(const pa_kv_cache *cache, void *out, const void *q, int32_t num_seqs, int32_t num_heads,
+                      const int32_t *block_tables, int32_t max_blocks_per_seq, const int32_t *context_lens,
+                      int32_t max_context_len, float scale, int32_t partition_size, int32_t num_groups,
+                      const int32_t *group_start, const int32_t *shared_len, int32_t max_group_size,
+                      int32_t max_shared_len, void *workspace, size_t workspace_bytes, void *stream) {
+  if (partition_size <= 0)
+    return fail(PA_ERR_PARTITION, "cascade decode needs partition_size > 0 (a multiple of block_size), got %d",
+                partition_size);
+  pa::DecodeArgs a;
+  // validation of the shared arguments (the plain-decode workspace check is
+  // replaced by the cascade one below)
+  int st = prepare_decode(cache, out, q, num_seqs, num_heads, block_tables, max_blocks_per_seq, context_lens,
+                          max_context_len, scale, partition_size, nullptr, 0, &a, false);
+  if (st) return st;
+  if (cache->dtype != PA_DTYPE_BF16)
+    return fail(PA_ERR_UNSUPPORTED, "cascade decode is bf16 only (dtype %d)", cache->dtype);
+  const int group = num_heads / cache->num_kv_heads;
+  if (group > 4) return fail(PA_ERR_UNSUPPORTED, "cascade decode takes num_heads / num_kv_heads in {1, 2, 4}, got %d",
+                             group);
+  if (num_groups < 0 || (num_seqs > 0 && num_groups == 0))
+    return fail(PA_ERR_SHAPE, "num_groups %d: every sequence belongs to one group", num_groups);
+  if (num_groups > kMaxGridYZ) return fail(PA_ERR_SHAPE, "num_groups %d above %d", num_groups, kMaxGridYZ);
+  if (num_seqs == 0) return ok();
+  if (!group_start || !shared_len)
+    return fail(PA_ERR_NULL, "group_start=%p shared_len=%p: both must be device pointers",
+                (const void *)group_start, (const void *)shared_len);
+  if (max_group_size <= 0 || max_group_size > num_seqs)
+    return fail(PA_ERR_SHAPE, "max_group_size %d not in [1, num_seqs %d]", max_group_size, num_seqs);
+  if (max_shared_len < 0) return fail(PA_ERR_SHAPE, "max_shared_len %d must be >= 0", max_shared_len);
+  const int P = cascade_slots(max_context_len, partition_size);
+  const size_t need = pa_decode_cascade_workspace_bytes(num_seqs, num_heads, cache->head_dim, max_context_len,
+                                                        partition_size);
+  if (!workspace) return fail(PA_ERR_WORKSPACE, "workspace is NULL; %zu bytes needed", need);
+  if (workspace_bytes < need) return fail(PA_ERR_WORKSPACE, "workspace_bytes %zu < %zu needed", workspace_bytes, need);
+  const size_t n = (size_t)num_seqs * num_heads * P;
+  char *w = static_cast<char *>(workspace);
+  a.ws_m = reinterpret_cast<float *>(w);
+  a.ws_l = reinterpret_cast<float *>(w + align256(n * sizeof(float)));
+  a.ws_o = reinterpret_cast<float *>(w + 2 * align256(n * sizeof(float)));
+  a.partition_size = partition_size;
+  a.max_partitions = P;
+  a.group_start = group_start;
+  a.shared_len = shared_len;
+  a.num_groups = num_groups;
+  const int chunk = kCascadeChunk;
+  a.shared_chunk = chunk;
+
+  // 1. the shared tokens of every group, once for all its rows (MFMA)
+  pa::PrefillArgs pf;
+  pf.cache = a.cache;
+  pf.out = out;
+  pf.q = q;
+  pf.query_start_loc = group_start;
+  pf.num_seqs = num_groups;
+  pf.num_heads = num_heads;
+  pf.num_query_tokens = num_seqs;
+  pf.max_query_len = max_group_size;
+  pf.block_tables = block_tables;
+  pf.max_blocks_per_seq = max_blocks_per_seq;
+  pf.context_lens = context_lens;
+  pf.max_context_len = max_context_len;
+  pf.scale = scale;
+  pf.group_start = group_start;
+  pf.shared_len = shared_len;
+  pf.ws_m = a.ws_m;
+  pf.ws_l = a.ws_l;
+  pf.ws_o = a.ws_o;
+  pf.ws_parts = P;
+  pf.shared_chunk = chunk;
+  // chunks launched per group: enough for max_shared_len.  Both passes clamp
+  // shared_len to the tokens those chunks cover (a multiple of 128, so of
+  // block_size); the members' partitions read anything past it.
+  pf.shared_chunks = std::max(1, (std::min(max_shared_len, max_context_len) + chunk - 1) / chunk);
+  a.shared_cap = pf.shared_chunks * chunk;
+  hipError_t e = pa::launch_prefill_chunk(pf, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "cascade shared-prefix launch");
+  // 2. every row's own tokens, split-K into slots 1..
+  e = pa::launch_decode_partition(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "cascade partition launch");
+  // 3. merge all slots
+  e = pa::launch_decode_reduce(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "cascade reduce launch");
   return ok();
 }
 

@@ -203,6 +203,15 @@ struct DecodeArgs {
   int partition_size;      // > 0: tokens per partition (split-K); 0: single pass
   int max_partitions;      // ceil(max_context_len / partition_size), >= 1
   float *ws_m, *ws_l, *ws_o;
+  // cascade decode (group_start non-NULL): rows group_start[g] ..
+  // group_start[g+1]-1 share their first shared_len[g] tokens, whose
+  // partial sits in slot 0; the partition launch covers each row's own
+  // tokens from there into slots 1.., and the reduce merges every slot
+  const int32_t *group_start = nullptr;
+  const int32_t *shared_len = nullptr;
+  int num_groups = 0;
+  int shared_chunk = 64;   // the shared part's partials: slot c = tokens [c*chunk, (c+1)*chunk)
+  int shared_cap = 0;      // shared tokens are clamped to this (shared_chunks * shared_chunk)
 };
 
 hipError_t launch_decode_partition(const DecodeArgs &a, hipStream_t stream);
@@ -219,6 +228,15 @@ struct PrefillArgs {
   const int32_t *context_lens;
   int max_context_len;
   float scale;
+  // cascade decode's shared-prefix pass (group_start non-NULL): num_seqs is
+  // the number of groups, max_query_len the largest group, num_query_tokens
+  // the number of decode rows; partials go to slot 0 of ws_*
+  const int32_t *group_start = nullptr;
+  const int32_t *shared_len = nullptr;
+  float *ws_m = nullptr, *ws_l = nullptr, *ws_o = nullptr;
+  int ws_parts = 0;
+  int shared_chunk = 64;   // tokens per chunk of the shared part (slot c = chunk c)
+  int shared_chunks = 1;   // chunks launched per group
 };
 
 hipError_t launch_prefill_chunk(const PrefillArgs &a, hipStream_t stream);

@@ -73,6 +73,13 @@ struct DecodeKernelArgs {
   int partition_size;    // tokens per partition; 0 = whole context
   int max_partitions;
   float scale_log2;      // scale * log2(e)
+  // cascade: rows group_start[g] .. group_start[g+1]-1 share their first
+  // shared_len[g] tokens (partial in slot 0); NULL for plain decode
+  const int32_t *group_start;
+  const int32_t *shared_len;
+  int num_groups;
+  int shared_chunk;      // the shared part's partials: slots 0 .. ceil(shared / shared_chunk) - 1
+  int shared_cap;        // shared tokens are clamped to this (the chunks launched)
 };
 
 __device__ __forceinline__ int decode_context(const DecodeKernelArgs &a, int seq) {
@@ -84,6 +91,19 @@ __device__ __forceinline__ int decode_context(const DecodeKernelArgs &a, int seq
 __device__ __forceinline__ int decode_num_partitions(const DecodeKernelArgs &a, int ctx) {
   if (a.partition_size <= 0 || ctx <= 0) return 1;
   return (ctx + a.partition_size - 1) / a.partition_size;
+}
+
+// cascade: the shared tokens of a row's group (0 outside cascade), at most
+// its context
+__device__ __forceinline__ int decode_shared(const DecodeKernelArgs &a, int seq, int ctx) {
+  if (!a.group_start) return 0;
+  int lo = 0, hi = a.num_groups - 1;  // the group g with group_start[g] <= seq
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (a.group_start[mid] <= seq) lo = mid;
+    else hi = mid - 1;
+  }
+  return max(0, min(min(a.shared_len[lo], a.shared_cap), ctx));
 }
 
 template <typename T>
@@ -637,11 +657,17 @@ decode_partition_bf16_kernel(const DecodeKernelArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
 
   const int ctx = decode_context(a, seq);
-  const int nparts = decode_num_partitions(a, ctx);
+  // cascade: this launch covers the row's own tokens after the shared ones,
+  // into the partition slots after those of the shared chunks
+  const bool cascade = a.group_start != nullptr;
+  const int sh = decode_shared(a, seq, ctx);
+  const int nparts = cascade ? (ctx - sh + a.partition_size - 1) / a.partition_size
+                             : decode_num_partitions(a, ctx);
   if (part >= nparts) return;
   const int ps = a.partition_size > 0 ? a.partition_size : ctx;
-  const int p0 = part * ps;
+  const int p0 = sh + part * ps;
   const int p1 = min(ctx, p0 + ps);
+  const int slot = cascade ? (sh + a.shared_chunk - 1) / a.shared_chunk + part : part;
 
   float m, l, acc[G][8];
   K::attend(a, seq, kvh, p0, p1, wave, lane, m, l, acc);
@@ -650,7 +676,7 @@ decode_partition_bf16_kernel(const DecodeKernelArgs a) {
   K::stage(sm, wave, lane, m, l, acc);
   __syncthreads();
 
-  const bool direct = (nparts == 1);
+  const bool direct = !cascade && nparts == 1;
   for (int i = threadIdx.x; i < G * D; i += 64 * W) {
     float M, o, lt;
     K::combine(sm, i, M, o, lt);
@@ -660,7 +686,7 @@ decode_partition_bf16_kernel(const DecodeKernelArgs a) {
       const float r = (lt > 0.f) ? o / lt : 0.f;
       store_one<bf16_t>(a.out, ((size_t)seq * a.num_heads + head) * D + d, r);
     } else {
-      const size_t idx = ((size_t)seq * a.num_heads + head) * a.max_partitions + part;
+      const size_t idx = ((size_t)seq * a.num_heads + head) * a.max_partitions + slot;
       a.ws_o[idx * D + d] = o;
       if (d == 0) {
         a.ws_m[idx] = M;
@@ -686,8 +712,17 @@ decode_reduce_kernel(const DecodeKernelArgs a) {
   const int head = blockIdx.x;
   const int seq = blockIdx.y;
   const int ctx = decode_context(a, seq);
-  const int nparts = decode_num_partitions(a, ctx);
-  if (nparts <= 1) return;
+  // cascade: a slot per chunk of the shared tokens and per partition of
+  // the rest; otherwise one slot per partition, and a single partition was
+  // written directly
+  const bool cascade = a.group_start != nullptr;
+  int nparts = decode_num_partitions(a, ctx);
+  if (cascade) {
+    const int sh = decode_shared(a, seq, ctx);
+    nparts = (sh + a.shared_chunk - 1) / a.shared_chunk + (ctx - sh + a.partition_size - 1) / a.partition_size;
+  }
+  if (!cascade && nparts <= 1) return;
+  // (a cascade row of context 0 has no slot: its output is zero)
 
   const size_t base = ((size_t)seq * a.num_heads + head) * a.max_partitions;
   __shared__ float sm_max;
@@ -780,6 +815,11 @@ static DecodeKernelArgs make_kernel_args(const DecodeArgs &a) {
   k.partition_size = a.partition_size;
   k.max_partitions = a.max_partitions;
   k.scale_log2 = a.scale * kLog2e;
+  k.group_start = a.group_start;
+  k.shared_len = a.shared_len;
+  k.num_groups = a.num_groups;
+  k.shared_chunk = a.shared_chunk;
+  k.shared_cap = a.shared_cap;
   return k;
 }
 

@@ -65,6 +65,18 @@ struct PrefillKernelArgs {
   int n_qtiles;           // query tiles per (sequence, head group)
   int n_work;             // work-groups with work
   float scale_log2;       // scale * log2(e)
+  // shared-prefix pass of cascade decode (group_start non-NULL): a "sequence"
+  // is a group of decode rows group_start[g] .. group_start[g+1]-1 whose
+  // first shared_len[g] tokens are the same blocks; their attention over
+  // those tokens is written as split-K partials into slot 0 of ws_*
+  const int32_t *group_start;
+  const int32_t *shared_len;
+  float *ws_m;
+  float *ws_l;
+  float *ws_o;
+  int ws_parts;           // partition slots per (row, head)
+  int n_chunks;           // key chunks per group (1 for prefill)
+  int chunk;              // tokens per key chunk, a multiple of 64 (cascade)
 };
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
@@ -97,6 +109,18 @@ __device__ __forceinline__ bf16x8_t pack8(const f32x16_t &s, int base) {
 constexpr int kPrefillThreads = 64 * PA_PREFILL_WAVES;
 #ifndef PA_PREFILL_VPAD
 #define PA_PREFILL_VPAD 4
+#endif
+// query heads per wave (1 or 2); with 2, each K and V^T fragment read from
+// LDS feeds two MFMAs
+#ifndef PA_PREFILL_HW
+#define PA_PREFILL_HW 1
+#endif
+// 1: a wave computes the scores of tile t+1 while it runs the softmax of
+// tile t (costs a second set of score registers); 0: the scores of tile t
+// at the start of step t (with two heads per wave, one head's products
+// overlap the other head's softmax)
+#ifndef PA_PREFILL_LOOKAHEAD
+#define PA_PREFILL_LOOKAHEAD (PA_PREFILL_HW == 1)
 #endif
 #ifndef PA_PREFILL_ORDER
 #define PA_PREFILL_ORDER 1
@@ -243,13 +267,25 @@ constexpr float kRescaleSlack = 8.f;
 constexpr uint32_t kBf16PairOnes = 0x3F803F80u;  // two bf16 1.0
 
 template <int D, int G>
-__global__ void __launch_bounds__(kPrefillThreads, 8 / PA_PREFILL_WAVES)
+struct PrefillShape {
+  static constexpr int NW = kPrefillThreads / 64;  // waves per work-group
+  static constexpr int HW = (G >= 2) ? PA_PREFILL_HW : 1;  // query heads per wave
+  static constexpr int HP = G / HW;                // head slots of a kv head
+  static constexpr int GWH = HP < NW ? HP : NW;    // head slots per work-group
+  static constexpr int HALVES = HP / GWH;          // work-groups per kv head along heads
+  static constexpr int TG = NW / GWH;              // 32-token query groups per work-group
+  static constexpr int QT = 32 * TG;               // query tokens per work-group
+  static_assert(HP % GWH == 0 && NW % GWH == 0, "heads and waves must divide");
+};
+
+template <int D, int G>
+__global__ void __launch_bounds__(kPrefillThreads, (8 / PA_PREFILL_WAVES) / PA_PREFILL_HW)
 prefill_chunk_kernel(const PrefillKernelArgs a) {
-  constexpr int NW = kPrefillThreads / 64;
-  constexpr int GW = G < NW ? G : NW;  // query heads per work-group
-  constexpr int HALVES = G / GW;       // work-groups per kv head along heads
-  constexpr int TG = NW / GW;          // 32-token query groups per work-group
-  constexpr int QT = 32 * TG;        // query tokens per work-group
+  using Sh = PrefillShape<D, G>;
+  constexpr int HW = Sh::HW;
+  constexpr int GWH = Sh::GWH;
+  constexpr int HALVES = Sh::HALVES;
+  constexpr int QT = Sh::QT;
   constexpr int KT = 64;             // keys per tile
   constexpr int KSTR = D + 8;        // LDS row stride of K, bf16 elements
   constexpr int VSTR = KT + PA_PREFILL_VPAD;  // LDS row stride of V^T, bf16 elements
@@ -263,16 +299,17 @@ prefill_chunk_kernel(const PrefillKernelArgs a) {
   __shared__ int sid[3][kMaxTileBlocks];
 
   // Work id.  Work-groups are dispatched round-robin over the 8 XCDs; the
-  // remap gives each XCD a contiguous range of work ids.  Ids are ordered
-  // (kv head, head half, query tile from the last, sequence), so an XCD
-  // serves whole kv heads of every sequence (equal work per XCD when the
-  // head groups are a multiple of 8), all query tiles of a (sequence, kv
-  // head) share one L2, and the tiles with the most keys start first.
+  // remap gives each XCD a contiguous range of work ids, ordered (kv head,
+  // head part, sequence, query tile from the last): the query tiles of one
+  // (sequence, kv head), which read the same K/V, run together on one XCD
+  // and share its L2, the tiles with more keys first.
   const int nwg = gridDim.x;  // a multiple of 8
   const int bid = blockIdx.x;
   const int wid = (bid & 7) * (nwg >> 3) + (bid >> 3);
   if (wid >= a.n_work) return;
   int rest = wid;
+  const int kchunk = rest % a.n_chunks;  // cascade: chunk of the shared tokens
+  rest /= a.n_chunks;
 #if PA_PREFILL_ORDER == 1
   const int qt_rev = rest % a.n_qtiles;
   rest /= a.n_qtiles;
@@ -288,74 +325,138 @@ prefill_chunk_kernel(const PrefillKernelArgs a) {
   const int kvh = rest / HALVES;
   const int qtile = a.n_qtiles - 1 - qt_rev;
 
-  int r1 = min(a.query_start_loc[seq + 1], a.num_query_tokens);
-  int r0 = a.query_start_loc[seq];
+  const bool cascade = a.group_start != nullptr;
+  const int32_t *rows = cascade ? a.group_start : a.query_start_loc;
+  int r1 = min(rows[seq + 1], a.num_query_tokens);
+  int r0 = rows[seq];
   r0 = max(0, min(r0, r1));
   const int q_len = r1 - r0;
-  int ctx = min(a.context_lens[seq], a.ctx_cap);
+  // prefill: the chunk ends the context; cascade: the shared tokens
+  int ctx = min(cascade ? min(a.shared_len[seq], a.n_chunks * a.chunk) : a.context_lens[seq], a.ctx_cap);
   ctx = max(ctx, 0);
   const int t_begin = qtile * QT;
   if (t_begin >= q_len) return;
+  if (cascade && kchunk * a.chunk >= ctx) return;  // a chunk past the group's shared tokens
   const int prefix = ctx - q_len;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int hl = wave % GW;
-  const int tg = wave / GW;
-  const int head = kvh * G + half * GW + hl;
-  const int tw0 = t_begin + tg * 32;  // first query of this wave
+  const int hs = wave % GWH;           // head slot of this wave
+  const int tg = wave / GWH;
+  const int head0 = kvh * G + (half * GWH + hs) * HW;  // first of the wave's HW heads
+  const int tw0 = t_begin + tg * 32;   // first query of this wave
   const int col = lane & 31;
   const int hh = lane >> 5;
-  const int t = tw0 + col;            // this lane's query (chunk row)
+  const int t = tw0 + col;             // this lane's query (chunk row)
   const bool qvalid = t < q_len;
-  const int qpos = prefix + t;
-
-  bf16x8_t qb[NDS];
-  {
-    const uint4 *qrow = reinterpret_cast<const uint4 *>(
-        static_cast<const uint16_t *>(a.q) + ((size_t)(r0 + (qvalid ? t : 0)) * a.num_heads + head) * D);
+  // last key this lane's query sees: its chunk position (prefill), or the
+  // end of the shared tokens within the row's own context (cascade)
+  int qpos = prefix + t;
+  if (cascade) {
+    const int own = qvalid ? max(0, min(a.context_lens[r0 + t], a.ctx_cap)) : ctx;
+    qpos = min(ctx, own) - 1;
+  }
+  // smallest of them in the wave: tiles past it need the mask
+  int qpos_lo = qpos;
 #pragma unroll
-    for (int ds = 0; ds < NDS; ++ds) qb[ds] = as_bf16x8(qvalid ? qrow[ds * 2 + hh] : make_uint4(0, 0, 0, 0));
+  for (int sft = 1; sft < 64; sft <<= 1) qpos_lo = min(qpos_lo, __shfl_xor(qpos_lo, sft));
+  qpos_lo = __builtin_amdgcn_readfirstlane(qpos_lo);
+
+  bf16x8_t qb[HW][NDS];
+#pragma unroll
+  for (int h = 0; h < HW; ++h) {
+    const uint4 *qrow = reinterpret_cast<const uint4 *>(
+        static_cast<const uint16_t *>(a.q) + ((size_t)(r0 + (qvalid ? t : 0)) * a.num_heads + head0 + h) * D);
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) qb[h][ds] = as_bf16x8(qvalid ? qrow[ds * 2 + hh] : make_uint4(0, 0, 0, 0));
   }
 
   // keys this work-group needs: 0 .. (largest query position of the tile)
   const int t_last = min(t_begin + QT, q_len) - 1;
-  const int kend = max(0, min(ctx, prefix + t_last + 1));
-  const int ntiles = (kend + KT - 1) / KT;
+  int kend = max(0, min(ctx, prefix + t_last + 1));
+  // cascade: the shared blocks are read through the table of the group's
+  // longest row, up to min(shared, its context), so every key read lies in
+  // a real context (a shorter row masks the keys it does not have)
+  int tab_row = seq;
+  if (cascade) {
+    __shared__ int s_best[2];
+    if (wave == 0) {
+      int best = -1, brow = r0;
+      for (int i = r0 + lane; i < r1; i += 64) {
+        const int c = max(0, min(a.context_lens[i], a.ctx_cap));
+        if (c > best) {
+          best = c;
+          brow = i;
+        }
+      }
+#pragma unroll
+      for (int sft = 1; sft < 64; sft <<= 1) {
+        const int ob = __shfl_xor(best, sft);
+        const int orow = __shfl_xor(brow, sft);
+        if (ob > best || (ob == best && orow < brow)) {
+          best = ob;
+          brow = orow;
+        }
+      }
+      if (lane == 0) {
+        s_best[0] = best;
+        s_best[1] = brow;
+      }
+    }
+    __syncthreads();
+    kend = max(0, min(ctx, s_best[0]));
+    tab_row = s_best[1];
+  }
+  // cascade: this work-group's chunk of the shared tokens
+  const int kbeg = cascade ? kchunk * a.chunk : 0;
+  if (cascade) {
+    kend = min(kend, kbeg + a.chunk);
+    if (kbeg >= kend) return;  // past every row's shared tokens: a slot no merge reads
+  }
 
   const uint32_t slot_stride = (uint32_t)a.num_kv_heads * D;
   const size_t block_stride = (size_t)slot_stride << a.block_shift;
   const uint16_t *kbase = static_cast<const uint16_t *>(a.k_cache) + (size_t)kvh * D;
   const uint16_t *vbase = static_cast<const uint16_t *>(a.v_cache) + (size_t)kvh * D;
-  const int32_t *bt = a.block_tables + (size_t)seq * a.max_blocks_per_seq;
+  const int32_t *bt = a.block_tables + (size_t)tab_row * a.max_blocks_per_seq;
   const int shift = a.block_shift;
   const int bs_mask = (1 << shift) - 1;
   const float sl = a.scale_log2;
   TileLanes<D> lanes;
   tile_lanes<D>(lanes, tid, shift, bs_mask, slot_stride);
 
-  float m = -INFINITY;  // reference max of this lane's query (base-2 units)
-  float l = 0.f;        // running sum over this lane's keys
-  f32x16_t o[NDT];
+  float m[HW], l[HW];  // reference max (base-2 units) and running sum of this lane's query, per head
+  f32x16_t o[HW][NDT];
 #pragma unroll
-  for (int dt = 0; dt < NDT; ++dt)
+  for (int h = 0; h < HW; ++h) {
+    m[h] = -INFINITY;
+    l[h] = 0.f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[h][dt][r] = 0.f;
+  }
 
-  // S^T tile of keys k0 .. k0+63 (s0: first 32 keys, s1: last 32)
-  auto qk = [&](const uint16_t *skb, f32x16_t &s0, f32x16_t &s1) {
+  // S^T tiles of keys k0 .. k0+63 for the wave's heads (s0: first 32 keys,
+  // s1: last 32); each K fragment read from LDS feeds HW products
+  auto qk = [&](const uint16_t *skb, f32x16_t (&s0)[HW], f32x16_t (&s1)[HW]) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      s0[r] = 0.f;
-      s1[r] = 0.f;
-    }
+    for (int h = 0; h < HW; ++h)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s0[h][r] = 0.f;
+        s1[h][r] = 0.f;
+      }
 #pragma unroll
     for (int ds = 0; ds < NDS; ++ds) {
       const bf16x8_t a0 = *reinterpret_cast<const bf16x8_t *>(skb + col * KSTR + ds * 16 + hh * 8);
       const bf16x8_t a1 = *reinterpret_cast<const bf16x8_t *>(skb + (32 + col) * KSTR + ds * 16 + hh * 8);
-      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qb[ds], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qb[ds], s1, 0, 0, 0);
+#pragma unroll
+      for (int h = 0; h < HW; ++h) {
+        s0[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qb[h][ds], s0[h], 0, 0, 0);
+        s1[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qb[h][ds], s1[h], 0, 0, 0);
+      }
     }
   };
 
@@ -365,99 +466,118 @@ prefill_chunk_kernel(const PrefillKernelArgs a) {
   // Block ids: sid[j % 3] holds the ids of tile j, filled three tiles ahead.
   if (tid < kMaxTileBlocks) {
 #pragma unroll
-    for (int j = 0; j < 3; ++j) sid[j][tid] = tile_block_id(bt, j * KT, tid, shift, a.max_blocks_per_seq);
+    for (int j = 0; j < 3; ++j) sid[j][tid] = tile_block_id(bt, kbeg + j * KT, tid, shift, a.max_blocks_per_seq);
   }
   __syncthreads();
   TileRegs<D> tr;
-  tile_load<D>(tr, lanes, sid[0], kbase, vbase, 0, kend, a.num_blocks, block_stride, slot_stride);
+  const int ntiles = (kend - kbeg + KT - 1) / KT;
+  tile_load<D>(tr, lanes, sid[0], kbase, vbase, kbeg, kend, a.num_blocks, block_stride, slot_stride);
   tile_store<D, KSTR, VSTR>(tr, sk[0], svt[0], tid);
-  tile_load<D>(tr, lanes, sid[1], kbase, vbase, KT, kend, a.num_blocks, block_stride, slot_stride);
+  tile_load<D>(tr, lanes, sid[1], kbase, vbase, kbeg + KT, kend, a.num_blocks, block_stride, slot_stride);
   tile_store<D, KSTR, VSTR>(tr, sk[1], svt[1], tid);
   __syncthreads();
 
-  f32x16_t c0, c1;  // S of the current tile
+  f32x16_t c0[HW], c1[HW];  // S of the current tile
+#if PA_PREFILL_LOOKAHEAD
   qk(sk[0], c0, c1);
+#endif
 
   for (int kt = 0; kt < ntiles; ++kt) {
-    const int k0 = kt * KT;
+    const int k0 = kbeg + kt * KT;
     const int b0 = kt % 3;
     const int b1 = (kt + 1) % 3;
     const int b2 = (kt + 2) % 3;
+#if !PA_PREFILL_LOOKAHEAD
+    qk(sk[b0], c0, c1);
+#endif
     // tile t+2 from the pool (past the last tile: in-pool rows, zeroed)
     tile_load<D>(tr, lanes, sid[b2], kbase, vbase, k0 + 2 * KT, kend, a.num_blocks, block_stride, slot_stride);
     int next_id = 0;
     if (tid < kMaxTileBlocks) next_id = tile_block_id(bt, k0 + 3 * KT, tid, shift, a.max_blocks_per_seq);
 
     // causal mask on tiles that cross this wave's diagonal (raw scores;
-    // register r of this lane holds key 8*(r/4) + 4*hh + r%4)
-    if (k0 + KT - 1 > prefix + tw0) {
+    // register r of this lane holds key 8*(r/4) + 4*hh + r%4); the same
+    // keys are masked for every head of the wave
+    if (k0 + KT - 1 > qpos_lo) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int kr = 8 * (r >> 2) + 4 * hh + (r & 3);
-        c0[r] = (k0 + kr <= qpos) ? c0[r] : -INFINITY;
-        c1[r] = (k0 + 32 + kr <= qpos) ? c1[r] : -INFINITY;
+        const bool keep0 = k0 + kr <= qpos;
+        const bool keep1 = k0 + 32 + kr <= qpos;
+#pragma unroll
+        for (int h = 0; h < HW; ++h) {
+          c0[h][r] = keep0 ? c0[h][r] : -INFINITY;
+          c1[h][r] = keep1 ? c1[h][r] : -INFINITY;
+        }
       }
     }
-    float rmax = -INFINITY;
+    bool any_grow = false;
+    float tmax[HW];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) rmax = fmaxf(fmaxf(rmax, c0[r]), c1[r]);
-    const float tmax = xor32_max(rmax) * sl;  // scale > 0 keeps the order
-    const bool grow = tmax > m + kRescaleSlack;
-    if (__builtin_amdgcn_ballot_w64(grow)) {
-      const float m_new = grow ? tmax : m;
-      const float alpha = (m == -INFINITY) ? 0.f : fast_exp2(m - m_new);
-      m = m_new;
-      l *= alpha;
+    for (int h = 0; h < HW; ++h) {
+      float rmax = -INFINITY;
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
+      for (int r = 0; r < 16; ++r) rmax = fmaxf(fmaxf(rmax, c0[h][r]), c1[h][r]);
+      tmax[h] = xor32_max(rmax) * sl;  // scale > 0 keeps the order
+      any_grow = any_grow || (tmax[h] > m[h] + kRescaleSlack);
+    }
+    if (__builtin_amdgcn_ballot_w64(any_grow)) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+      for (int h = 0; h < HW; ++h) {
+        const bool grow = tmax[h] > m[h] + kRescaleSlack;
+        const float m_new = grow ? tmax[h] : m[h];
+        const float alpha = (m[h] == -INFINITY) ? 0.f : fast_exp2(m[h] - m_new);
+        m[h] = m_new;
+        l[h] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[h][dt][r] *= alpha;
+      }
     }
     // From here to the P.V products the code is one basic block: the
     // scores of the next tile (independent of this tile's softmax; on the
     // last step the buffer holds the zero-filled tile past the end and the
     // result is not used) are interleaved with the exponentials below, so
     // the matrix and vector units work at the same time.
-    f32x16_t n0, n1;
+#if PA_PREFILL_LOOKAHEAD
+    f32x16_t n0[HW], n1[HW];
     qk(sk[b1], n0, n1);
-    const float nm = (m == -INFINITY) ? 0.f : -m;  // rows with no key yet: every score is -inf
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      c0[r] = fast_exp2(fmaf(c0[r], sl, nm));
-      c1[r] = fast_exp2(fmaf(c1[r], sl, nm));
-    }
-#if PA_PREFILL_INTERLEAVE
-#pragma unroll
-    for (int i = 0; i < 2 * NDS; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, PA_PREFILL_INTERLEAVE, 0);  // some VALU
-    }
+#else
+    (void)b1;
 #endif
-
-    // P^T in the B layout: k-step (sub-tile st, half u) = registers 8u..8u+7
-    // of c_st, i.e. keys st*32 + 16u + 8*(e/4) + 4*hh + e%4 for slot e
-    bf16x8_t pb[4];
-    pb[0] = pack8(c0, 0);
-    pb[1] = pack8(c0, 8);
-    pb[2] = pack8(c1, 0);
-    pb[3] = pack8(c1, 8);
-    // the running sum takes the same bf16 weights that multiply V, two at a
-    // time (v_dot2_f32_bf16 against ones), so numerator and denominator agree
-    {
+    bf16x8_t pb[HW][4];
+#pragma unroll
+    for (int h = 0; h < HW; ++h) {
+      const float nm = (m[h] == -INFINITY) ? 0.f : -m[h];  // rows with no key yet: every score is -inf
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        c0[h][r] = fast_exp2(fmaf(c0[h][r], sl, nm));
+        c1[h][r] = fast_exp2(fmaf(c1[h][r], sl, nm));
+      }
+      // P^T in the B layout: k-step (sub-tile st, half u) = registers
+      // 8u..8u+7 of c_st, i.e. keys st*32 + 16u + 8*(e/4) + 4*hh + e%4
+      pb[h][0] = pack8(c0[h], 0);
+      pb[h][1] = pack8(c0[h], 8);
+      pb[h][2] = pack8(c1[h], 0);
+      pb[h][3] = pack8(c1[h], 8);
+      // the running sum takes the same bf16 weights that multiply V, two
+      // at a time (v_dot2_f32_bf16 against ones), so numerator and
+      // denominator agree
       float ps = 0.f;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const uint4 w = __builtin_bit_cast(uint4, pb[u]);
+        const uint4 w = __builtin_bit_cast(uint4, pb[h][u]);
         ps = dot2_bf16(w.x, kBf16PairOnes, ps);
         ps = dot2_bf16(w.y, kBf16PairOnes, ps);
         ps = dot2_bf16(w.z, kBf16PairOnes, ps);
         ps = dot2_bf16(w.w, kBf16PairOnes, ps);
       }
-      l += ps;
+      l[h] += ps;
     }
 
-    // O^T += V^T P^T; the A operand takes the same keys from row d of V^T
+    // O^T += V^T P^T; the A operand takes the same keys from row d of V^T,
+    // and each V^T fragment read from LDS feeds HW products
     const uint16_t *svb = svt[b0];
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
@@ -468,39 +588,71 @@ prefill_chunk_kernel(const PrefillKernelArgs a) {
         const uint2 lo = *reinterpret_cast<const uint2 *>(vrow + kb0);
         const uint2 hi = *reinterpret_cast<const uint2 *>(vrow + kb0 + 8);
         const bf16x8_t av = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[ks], o[dt], 0, 0, 0);
+#pragma unroll
+        for (int h = 0; h < HW; ++h) o[h][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[h][ks], o[h][dt], 0, 0, 0);
       }
     }
 
     tile_store<D, KSTR, VSTR>(tr, sk[b2], svt[b2], tid);
     if (tid < kMaxTileBlocks) sid[b0][tid] = next_id;  // ids of tile t+3
     __syncthreads();
-    c0 = n0;
-    c1 = n1;
+#if PA_PREFILL_LOOKAHEAD
+#pragma unroll
+    for (int h = 0; h < HW; ++h) {
+      c0[h] = n0[h];
+      c1[h] = n1[h];
+    }
+#endif
   }
 
-  const float lt = xor32_sum(l);
-  if (qvalid) {
-    uint16_t *orow = static_cast<uint16_t *>(a.out) + ((size_t)(r0 + t) * a.num_heads + head) * D;
+  float lsum[HW];
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
+  for (int h = 0; h < HW; ++h) lsum[h] = xor32_sum(l[h]);  // cross-lane: before the divergent store
+  if (cascade) {
+    // partials (reference max in base-2 units, sum, unnormalised output)
+    if (qvalid) {
 #pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        const int d0 = dt * 32 + 8 * rq + 4 * hh;
-        float v[4];
+      for (int h = 0; h < HW; ++h) {
+        const size_t idx = ((size_t)(r0 + t) * a.num_heads + head0 + h) * a.ws_parts + kchunk;
+        float *orow = a.ws_o + idx * D;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = (lt > 0.f) ? o[dt][4 * rq + e] / lt : 0.f;
-        *reinterpret_cast<uint2 *>(orow + d0) = make_uint2(pack_bf16x2_rne(v[0], v[1]), pack_bf16x2_rne(v[2], v[3]));
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+          for (int rq = 0; rq < 4; ++rq) {
+            const int d0 = dt * 32 + 8 * rq + 4 * hh;
+            *reinterpret_cast<float4 *>(orow + d0) =
+                make_float4(o[h][dt][4 * rq], o[h][dt][4 * rq + 1], o[h][dt][4 * rq + 2], o[h][dt][4 * rq + 3]);
+          }
+        if (hh == 0) {
+          a.ws_m[idx] = m[h];
+          a.ws_l[idx] = lsum[h];
+        }
       }
+    }
+    return;
+  }
+  if (qvalid) {
+#pragma unroll
+    for (int h = 0; h < HW; ++h) {
+      const float lt = lsum[h];
+      uint16_t *orow = static_cast<uint16_t *>(a.out) + ((size_t)(r0 + t) * a.num_heads + head0 + h) * D;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          const int d0 = dt * 32 + 8 * rq + 4 * hh;
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = (lt > 0.f) ? o[h][dt][4 * rq + e] / lt : 0.f;
+          *reinterpret_cast<uint2 *>(orow + d0) = make_uint2(pack_bf16x2_rne(v[0], v[1]), pack_bf16x2_rne(v[2], v[3]));
+        }
+    }
   }
 }
 
 template <int D, int G>
 static hipError_t launch_t(const PrefillArgs &a, hipStream_t stream) {
-  constexpr int NW = kPrefillThreads / 64;
-  constexpr int GW = G < NW ? G : NW;
-  constexpr int HALVES = G / GW;
-  constexpr int QT = 32 * (NW / GW);
+  using Sh = PrefillShape<D, G>;
   PrefillKernelArgs k;
   k.out = a.out;
   k.q = a.q;
@@ -520,12 +672,20 @@ static hipError_t launch_t(const PrefillArgs &a, hipStream_t stream) {
   const int64_t table_cap = (int64_t)a.max_blocks_per_seq * a.cache.block_size;
   k.ctx_cap = (int)(table_cap < a.max_context_len ? table_cap : a.max_context_len);
   k.num_query_tokens = a.num_query_tokens;
-  k.n_qtiles = (a.max_query_len + QT - 1) / QT;
-  const int64_t n_work = (int64_t)a.num_seqs * a.cache.num_kv_heads * HALVES * k.n_qtiles;
+  k.n_qtiles = (a.max_query_len + Sh::QT - 1) / Sh::QT;
+  k.n_chunks = a.group_start ? a.shared_chunks : 1;
+  k.chunk = a.shared_chunk;
+  const int64_t n_work = (int64_t)a.num_seqs * a.cache.num_kv_heads * Sh::HALVES * k.n_qtiles * k.n_chunks;
   if (n_work <= 0) return hipSuccess;
   if (n_work > (int64_t)0x7fffffff - 8) return hipErrorInvalidConfiguration;
   k.n_work = (int)n_work;
   k.scale_log2 = a.scale * kLog2e;
+  k.group_start = a.group_start;
+  k.shared_len = a.shared_len;
+  k.ws_m = a.ws_m;
+  k.ws_l = a.ws_l;
+  k.ws_o = a.ws_o;
+  k.ws_parts = a.ws_parts;
   const unsigned grid = (unsigned)((n_work + 7) / 8 * 8);
   hipLaunchKernelGGL((prefill_chunk_kernel<D, G>), dim3(grid), dim3(kPrefillThreads), 0, stream, k);
   return hipGetLastError();

@@ -237,3 +237,26 @@ def test_copy_blocks_validation(lib):
     assert cp(a, b, n=11) == -3 and "identity copy of 11 blocks" in msg()
     assert cp(b, a, n=11) == -3
     assert cp(a, cache(k=0)) == -1
+
+
+def test_cascade_validation(lib):
+    c = cache()
+    def casc(c=c, S=4, H=32, ps=256, ng=2, gs=FAKE, sl=FAKE, mg=2, ws=FAKE, ws_bytes=10 ** 9, mcl=1000, msl=512):
+        return lib.pa_decode_cascade(ctypes.byref(c), FAKE, FAKE, S, H, FAKE, 8, FAKE, mcl, 0.1, ps, ng, gs, sl, mg,
+                                     msl, ws, ws_bytes, None)
+    assert casc(ps=0) == -10 and "partition_size > 0" in msg()
+    assert casc(ps=48) == -10
+    assert casc(c=cache(dtype=0)) == -8 and "bf16 only" in msg()
+    assert casc(H=64) == -8                                   # 8 query heads per kv head
+    assert casc(ng=0) == -3
+    assert casc(gs=None) == -1
+    assert casc(mg=0) == -3 and casc(mg=5) == -3
+    assert casc(msl=-1) == -3 and "max_shared_len" in msg()
+    need = P.pa_decode_cascade_workspace_bytes(4, 32, 128, 1000, 256)
+    assert casc(ws=None) == -7 and f"{need} bytes needed" in msg()
+    assert casc(ws_bytes=need - 1) == -7
+    # slots: 128-token chunks of the shared part, then the row's partitions
+    n = 4 * 32 * (-(-1000 // 128) + -(-1000 // 256))
+    a = lambda x: (x + 255) // 256 * 256
+    assert need == 2 * a(4 * n) + a(4 * n * 128)
+    assert casc(S=0, ng=0) == 0

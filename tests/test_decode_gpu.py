@@ -234,3 +234,84 @@ def test_many_partitions():
         log(f"{-(-case.max_context_len // ps)} partitions")
         _, got = _run(case, ps)
         assert_close(got, ref, W.BF16, f"ps{ps}")
+
+
+# ------------------------------------------------------------ cascade decode
+
+def _cascade(case, group_start, shared_len, partition_size=256, max_context_len=None, max_shared_len=None):
+    import paged_attention_kv_cache_amd as P
+    t = torch()
+    dev = DeviceCase(case)
+    dev.write()
+    gs = t.tensor(group_start, dtype=t.int32, device="cuda")
+    sl = t.tensor(shared_len, dtype=t.int32, device="cuda")
+    mg = max(b - a for a, b in zip(group_start[:-1], group_start[1:]))
+    mcl = case.max_context_len if max_context_len is None else max_context_len
+    msl = max(shared_len) if max_shared_len is None else max_shared_len
+    out = P.pa_decode_cascade(dev.q, dev.k_cache, dev.v_cache, dev.block_tables, dev.context_lens, case.scale, mcl,
+                              gs, sl, mg, partition_size, max_shared_len=msl)
+    t.cuda.synchronize()
+    return to_host_f32(out, case.dtype)
+
+
+@pytest.mark.parametrize("name", ["prefix_shared_decode_bs8", "prefix_shared_decode_bs16"])
+def test_cascade_prefix_shared_full(name):
+    case = W.make_config(name)
+    bs = case.block_size
+    ref = oracle_decode(case)
+    for ps in (256, 512):
+        log(f"cascade {name} partition={ps}")
+        got = _cascade(case, [0, 16, 32, 48, 64], [64 * bs] * 4, ps)
+        mx, mean = assert_close(got, ref, W.BF16, f"cascade {name} ps{ps}")
+        print(f"cascade {name} ps={ps}: max-abs {mx:.2e} mean-abs {mean:.2e}")
+
+
+@pytest.mark.parametrize("group", [1, 2, 4])
+def test_cascade_irregular_groups(group):
+    """Groups of 1, 3, 70 (two member tiles) and 6 rows; shared lengths below
+    the true sharing, 0, and rows whose context ends inside or exactly at
+    the shared part (no own tokens)."""
+    sizes = [1, 3, 70, 6]
+    starts = np.cumsum([0] + sizes).tolist()
+    group_of = [g for g, n in enumerate(sizes) for _ in range(n)]
+    bs, shared_blocks = 16, 12
+    rng = np.random.default_rng(group)
+    ctx = [int(x) for x in rng.integers(shared_blocks * bs + 1, 1500, size=sum(sizes))]
+    ctx[1], ctx[2] = 5 * bs, 8 * bs           # group 1: its first row ends inside the shared part, one exactly at it
+    ctx[4] = 2 * bs - 3                        # group 2: a row far shorter than the shared part
+    hkv = 2
+    case = W.random_decode(300 + group, ctx, num_heads=hkv * group, num_kv_heads=hkv, head_dim=128, block_size=bs,
+                           dtype=W.BF16, shared_blocks=shared_blocks, group_of=group_of)
+    ref = oracle_decode(case)
+    shared = [shared_blocks * bs, 8 * bs, shared_blocks * bs, 0]
+    for ps in (64, 256):
+        log(f"cascade irregular G={group} partition={ps}")
+        got = _cascade(case, starts, shared, ps)
+        assert_close(got, ref, W.BF16, f"cascade irregular G{group} ps{ps}")
+    # a max_shared_len below the largest shared_len: the 192 shared tokens
+    # are clamped to one 128-token chunk and the rest run in the partitions
+    for msl in (0, 100):
+        log(f"cascade irregular G={group} max_shared_len={msl}")
+        got = _cascade(case, starts, shared, 64, max_shared_len=msl)
+        assert_close(got, ref, W.BF16, f"cascade irregular G{group} clamp{msl}")
+
+
+@pytest.mark.parametrize("bs", [8, 16, 32])
+def test_cascade_index_probe(bs):
+    """Index probe through cascade decode: groups of one row that claim a
+    shared part, so the target is read by the MFMA pass or by the
+    partitions; the output is that row's V bit for bit."""
+    ctx = 3 * 64 + 5
+    targets = list(range(0, ctx, 3))
+    case = _probe_case(70 + bs, ctx, bs, len(targets), targets)
+    vflat = W.storage_to_f32(case.v_cache, W.BF16).reshape(-1, 8, 128)
+    vnew = W.storage_to_f32(case.new_value, W.BF16)
+    S = len(targets)
+    starts = list(range(S + 1))
+    shared = [((i % 5) * 2 * bs) for i in range(S)]    # 0 .. 8 blocks, some past the context
+    log(f"cascade index probe bs={bs}")
+    got = _cascade(case, starts, shared, 64)
+    for i, p in enumerate(targets):
+        s = int(case.block_tables[i, p // bs]) * bs + p % bs
+        v = vnew[i] if p == ctx - 1 else vflat[s]
+        assert np.array_equal(got[i], np.repeat(v, 4, axis=0)), f"bs{bs} target {p} shared {shared[i]}"

@@ -19,13 +19,14 @@ def _run(case, max_context_len=None):
     return dev, to_host_f32(out, case.dtype)
 
 
-def test_chunked_prefill_full():
-    case = W.make_config("chunked_prefill")
-    log(f"chunked prefill 8 x 512 over prefixes {(case.context_lens - 512).tolist()}")
+@pytest.mark.parametrize("block_size", [32, 16, 8])
+def test_chunked_prefill_full(block_size):
+    case = W.chunked_prefill(block_size=block_size)
+    log(f"chunked prefill 8 x 512 over prefixes {(case.context_lens - 512).tolist()}, block size {block_size}")
     _, got = _run(case)
     ref = oracle_prefill(case)
-    mx, mean = assert_close(got, ref, W.BF16, "chunked prefill")
-    print(f"chunked prefill: max-abs {mx:.2e} mean-abs {mean:.2e}")
+    mx, mean = assert_close(got, ref, W.BF16, f"chunked prefill bs{block_size}")
+    print(f"chunked prefill bs{block_size}: max-abs {mx:.2e} mean-abs {mean:.2e}")
 
 
 PREFIXES = [0, 0, 5, 31, 32, 64, 100, 257]

@@ -389,20 +389,22 @@ def long_context_decode(seed: int = 3000, poison: bool = True, num_seqs: int = 4
 
 
 def chunked_prefill(seed: int = 4000, poison: bool = True, num_seqs: int = 8, chunk: int = 512,
-                    prefix_high: int = 3584) -> PrefillCase:
+                    prefix_high: int = 3584, block_size: int = 32) -> PrefillCase:
     """8 sequences each appending a 512-token chunk (4096-token budget) onto
     a cached prefix uniform in [0, 3584]; 32 q / 8 kv heads, head_dim 128,
-    block_size 32, bf16.  The chunk's slot mapping follows the randomly
-    drawn block table, continuing the prefix's partial last block."""
+    block_size 32 (8 and 16 as variants), bf16.  The chunk's slot mapping
+    follows the randomly drawn block table, continuing the prefix's partial
+    last block."""
     rng = np.random.default_rng(seed)
     prefix = rng.integers(0, prefix_high, size=num_seqs, endpoint=True).tolist()
     qlen = [chunk] * num_seqs
     ctx = [p + chunk for p in prefix]
-    tables, nb, pad = _layout(rng, ctx, 32)
+    tables, nb, pad = _layout(rng, ctx, block_size)
     qsl = np.zeros(num_seqs + 1, dtype=np.int32)
     qsl[1:] = np.cumsum(qlen)
-    return _finish(rng, kind="prefill", name="chunked_prefill", dtype=BF16, Hq=32, Hkv=8, D=128,
-                   bs=32, ctx=ctx, tables=tables, nb=nb, pad=pad, q_rows=int(qsl[-1]),
+    name = "chunked_prefill" if block_size == 32 else f"chunked_prefill_bs{block_size}"
+    return _finish(rng, kind="prefill", name=name, dtype=BF16, Hq=32, Hkv=8, D=128,
+                   bs=block_size, ctx=ctx, tables=tables, nb=nb, pad=pad, q_rows=int(qsl[-1]),
                    new_positions=[np.arange(p, p + chunk) for p in prefix], poison=poison,
                    query_start_loc=qsl)
 
