@@ -46,7 +46,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--partition", type=int, default=256, help="split-K partition (tokens)")
+    ap.add_argument("--partition", type=int, default=512, help="split-K partition (tokens)")
     ap.add_argument("--rotate-gb", type=float, default=2.0, help="total size of rotated KV pools")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")

@@ -72,6 +72,7 @@ struct DecodeKernelArgs {
   int ctx_cap;           // min(max_context_len, max_blocks_per_seq * block_size)
   int partition_size;    // tokens per partition; 0 = whole context
   int max_partitions;
+  int num_seqs;
   float scale_log2;      // scale * log2(e)
   // cascade: rows group_start[g] .. group_start[g+1]-1 share their first
   // shared_len[g] tokens (partial in slot 0); NULL for plain decode
@@ -321,9 +322,13 @@ decode_partition_kernel(const DecodeKernelArgs a) {
 #endif
 // grid order of the partition kernel: 1 = kv head fastest, then sequence,
 // then partition, so that the partitions that exist for every sequence are
-// dispatched first and the empty ones (past short contexts) come last
+// dispatched first and the empty ones (past short contexts) come last;
+// 3 = kv head fastest, then the (sequence, partition) pairs by size: every
+// full partition first, then the partial last partitions, longest first, so
+// that the work-groups dispatched last are the short ones (batches of at
+// most 64 sequences; larger ones keep order 1)
 #ifndef PA_DECODE_ORDER
-#define PA_DECODE_ORDER 1
+#define PA_DECODE_ORDER 3
 #endif
 
 // Reduce-scatter of G per-lane partial sums over a row of L lanes: lane c
@@ -639,12 +644,79 @@ struct Bf16Decode {
   }
 };
 
+// Dispatch order by size.  The (sequence, partition) pairs of a batch of at
+// most 64 sequences are numbered so that every full partition comes first
+// (partition-major), then the partial last partitions, longest first (ties
+// by sequence); work-group item i takes pair i.  Computed by one wave, lane
+// s holding sequence s.  Returns false for an item past the last pair.
+__device__ __forceinline__ bool size_order_item(const DecodeKernelArgs &a, int item, int lane, int &seq_out,
+                                                int &part_out) {
+  const int S = a.num_seqs;
+  const int ps = a.partition_size;
+  const int ctx = lane < S ? decode_context(a, lane) : 0;
+  const int nfull = ctx / ps;
+  const int rem = ctx - nfull * ps;
+  // full pairs: cum(p) = sum_s min(nfull_s, p) pairs come before partition p
+  auto cum = [&](int p) {
+    int v = min(nfull, p);
+#pragma unroll
+    for (int sft = 1; sft < 64; sft <<= 1) v += __shfl_xor(v, sft);
+    return v;
+  };
+  const int total_full = cum(a.max_partitions);
+  if (item < total_full) {
+    int lo = 0, hi = a.max_partitions - 1;  // the p with cum(p) <= item < cum(p+1)
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (cum(mid) <= item) lo = mid;
+      else hi = mid - 1;
+    }
+    const int k = item - cum(lo);
+    const unsigned long long has = __builtin_amdgcn_ballot_w64(nfull > lo);
+    const int rank = __builtin_amdgcn_mbcnt_hi((unsigned)(has >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)has, 0));
+    const unsigned long long hit = __builtin_amdgcn_ballot_w64(nfull > lo && rank == k);
+    if (hit == 0) return false;
+    seq_out = __builtin_ctzll(hit);
+    part_out = lo;
+    return true;
+  }
+  const int j = item - total_full;
+  int rank = 0;  // among partial pairs: longer first, then lower sequence
+  for (int s = 0; s < S; ++s) {
+    const int r = __builtin_amdgcn_readlane(rem, s);
+    rank += (r > rem || (r == rem && s < lane)) ? 1 : 0;
+  }
+  const unsigned long long hit = __builtin_amdgcn_ballot_w64(lane < S && rem > 0 && rank == j);
+  if (hit == 0) return false;
+  seq_out = __builtin_ctzll(hit);
+  part_out = __builtin_amdgcn_readlane(nfull, seq_out);
+  return true;
+}
+
 template <int D, int G>
 __global__ void __launch_bounds__(64 * PA_DECODE_WAVES)
 decode_partition_bf16_kernel(const DecodeKernelArgs a) {
   using K = Bf16Decode<D, G>;
   constexpr int W = K::W;
-#if PA_DECODE_ORDER == 1
+#if PA_DECODE_ORDER == 3
+  const int kvh = blockIdx.x;
+  int seq = blockIdx.y;
+  int part = blockIdx.z;
+  if (a.group_start == nullptr && a.partition_size > 0 && a.num_seqs <= 64) {
+    __shared__ int s_map[2];
+    if (threadIdx.x < 64) {
+      int sq = 0, pt = 0;
+      const bool ok = size_order_item(a, blockIdx.z * gridDim.y + blockIdx.y, threadIdx.x, sq, pt);
+      if (threadIdx.x == 0) {
+        s_map[0] = ok ? sq : 0;
+        s_map[1] = ok ? pt : a.max_partitions;  // no pair: past every sequence's partitions
+      }
+    }
+    __syncthreads();
+    seq = s_map[0];
+    part = s_map[1];
+  }
+#elif PA_DECODE_ORDER == 1
   const int kvh = blockIdx.x;
   const int seq = blockIdx.y;
   const int part = blockIdx.z;
@@ -814,6 +886,7 @@ static DecodeKernelArgs make_kernel_args(const DecodeArgs &a) {
   k.ctx_cap = (int)(table_cap < a.max_context_len ? table_cap : a.max_context_len);
   k.partition_size = a.partition_size;
   k.max_partitions = a.max_partitions;
+  k.num_seqs = a.num_seqs;
   k.scale_log2 = a.scale * kLog2e;
   k.group_start = a.group_start;
   k.shared_len = a.shared_len;
@@ -828,7 +901,7 @@ static hipError_t launch_partition_t(const DecodeArgs &a, hipStream_t stream) {
   const DecodeKernelArgs k = make_kernel_args(a);
   dim3 grid(a.max_partitions, a.cache.num_kv_heads, a.num_seqs);
   if constexpr (std::is_same<T, bf16_t>::value && G <= 4) {
-#if PA_DECODE_ORDER == 1
+#if PA_DECODE_ORDER == 1 || PA_DECODE_ORDER == 3
     grid = dim3(a.cache.num_kv_heads, a.num_seqs, a.max_partitions);
 #endif
     hipLaunchKernelGGL((decode_partition_bf16_kernel<D, G>), grid, dim3(64 * PA_DECODE_WAVES), 0, stream, k);
