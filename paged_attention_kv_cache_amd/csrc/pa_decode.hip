@@ -647,7 +647,8 @@ struct Bf16Decode {
 // Dispatch order by size.  The (sequence, partition) pairs of a batch of at
 // most 64 sequences are numbered so that every full partition comes first
 // (partition-major), then the partial last partitions, longest first (ties
-// by sequence); work-group item i takes pair i.  Computed by one wave, lane
+// by sequence; the single empty partition of a sequence with no context
+// counts as a partial one of length 0); work-group item i takes pair i.  Computed by one wave, lane
 // s holding sequence s.  Returns false for an item past the last pair.
 __device__ __forceinline__ bool size_order_item(const DecodeKernelArgs &a, int item, int lane, int &seq_out,
                                                 int &part_out) {
@@ -680,13 +681,17 @@ __device__ __forceinline__ bool size_order_item(const DecodeKernelArgs &a, int i
     part_out = lo;
     return true;
   }
+  // partial pairs: a last partition shorter than ps, or the one empty
+  // partition of a sequence with no context (its output row is zero)
+  const bool partial = lane < S && (rem > 0 || ctx == 0);
+  const unsigned long long has = __builtin_amdgcn_ballot_w64(partial);
   const int j = item - total_full;
   int rank = 0;  // among partial pairs: longer first, then lower sequence
   for (int s = 0; s < S; ++s) {
     const int r = __builtin_amdgcn_readlane(rem, s);
-    rank += (r > rem || (r == rem && s < lane)) ? 1 : 0;
+    rank += ((has >> s) & 1) && (r > rem || (r == rem && s < lane)) ? 1 : 0;
   }
-  const unsigned long long hit = __builtin_amdgcn_ballot_w64(lane < S && rem > 0 && rank == j);
+  const unsigned long long hit = __builtin_amdgcn_ballot_w64(partial && rank == j);
   if (hit == 0) return false;
   seq_out = __builtin_ctzll(hit);
   part_out = __builtin_amdgcn_readlane(nfull, seq_out);

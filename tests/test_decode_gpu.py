@@ -12,7 +12,7 @@ from gpu_util import (DeviceCase, assert_close, log, oracle_decode, to_host_bits
 
 pytestmark = pytest.mark.gpu
 
-BENCH_PARTITION = 256     # the split-K partition the benchmark times for the bs32 batch
+BENCH_PARTITION = 512     # the split-K partition the benchmark times for the bs32 batch
 
 
 def _run(case, partition_size, max_context_len=None):
@@ -212,6 +212,26 @@ def test_context_zero_and_one():
         assert np.array_equal(got[0], np.zeros_like(got[0]))
         assert np.array_equal(got[1], np.repeat(W.storage_to_f32(case.new_value, W.F32)[0], 4, axis=0))
         assert_close(got, ref, W.F32, f"ps{ps}")
+
+
+@pytest.mark.parametrize("num_seqs", [63, 64, 65])
+def test_dispatch_order_edge_batches(num_seqs):
+    """The partition kernel hands out (sequence, partition) pairs by size for
+    batches of up to 64 sequences (65 takes the plain order): contexts of 0
+    and 1, exact multiples of the partition size, one token past them, and
+    long ones, so that full, partial and empty pairs all occur."""
+    rng = np.random.default_rng(num_seqs)
+    base = [0, 1, 32, 33, 64, 511, 512, 513, 1024, 1537, 2048]
+    ctx = (base * 6)[:num_seqs]
+    ctx = [int(c) for c in rng.permutation(ctx)]
+    case = W.random_decode(500 + num_seqs, ctx, num_heads=8, num_kv_heads=2, head_dim=128, block_size=32,
+                           dtype=W.BF16)
+    ref = oracle_decode(case)
+    for ps in (32, 512):
+        log(f"{num_seqs} sequences, partition {ps}")
+        _, got = _run(case, ps)
+        assert_close(got, ref, W.BF16, f"S{num_seqs} ps{ps}")
+        assert np.array_equal(got[ctx.index(0)], np.zeros_like(got[0]))
 
 
 def test_loose_max_context_len():
