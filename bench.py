@@ -548,7 +548,7 @@ def main():
         line["prefill_chunk"] = {
             "workload": "8 sequences x 512-token chunk over prefix U[0,3584], 32q/8kv, D128, BS32, bf16",
             "us": round(pre["us"], 2), "tokens_per_s": round(pre["tokens_per_s"], 1),
-            "roofline": {"kernel": "prefill_chunk_kernel<128, 4>", "bound": "mfma", "achieved": round(pre["tflops"], 1), "peak": BF16_DENSE_PEAK_TFLOPS,
+            "roofline": {"kernel": "prefill_chunk_kernel<128, 128, 4>", "bound": "mfma", "achieved": round(pre["tflops"], 1), "peak": BF16_DENSE_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(pre["frac"], 4),
                          "traffic": traffic_from_profiles("prefill_chunk", pre["src"]),
                          "algorithmic_flops_per_launch": pre["flops"]},

@@ -32,7 +32,11 @@
  *    Every call only enqueues work on it.  Results are visible after the
  *    caller synchronises with that stream.
  *  - Layouts are row-major and contiguous:
- *      k_cache, v_cache : [num_blocks, block_size, num_kv_heads, head_dim]
+ *      k_cache          : [num_blocks, block_size, num_kv_heads, head_dim]
+ *      v_cache          : [num_blocks, block_size, num_kv_heads, v_head_dim]
+ *    where v_head_dim (the value head dim) is head_dim unless the cache
+ *    descriptor sets it ([TS] section 4.1: separate key and value lengths,
+ *    each defaulting to the head dim).
  *      block_tables     : [num_seqs, max_blocks_per_seq] int32
  *      context_lens     : [num_seqs] int32 (tokens already in the cache,
  *                         including the tokens this step wrote)
@@ -45,8 +49,9 @@
  *  - Element types: q, k_cache, v_cache and out share one dtype (fp32 or
  *    bf16).  Arithmetic is fp32 in either case.  bf16 outputs are rounded
  *    to nearest even.
- *  - Supported shapes: block_size in {8, 16, 32}, head_dim in {64, 128},
- *    num_heads / num_kv_heads in {1, 2, 4, 8}.
+ *  - Supported shapes: block_size in {8, 16, 32}, head_dim and v_head_dim
+ *    each in {64, 128}, num_heads / num_kv_heads in {1, 2, 4, 8}.  Queries
+ *    have head_dim elements per head, outputs v_head_dim.
  *
  * Errors
  * ------
@@ -100,16 +105,18 @@ typedef enum pa_status {
 } pa_status;
 
 /* One layer's paged KV pool.  The pointers are device memory owned by the
- * caller, laid out [num_blocks, block_size, num_kv_heads, head_dim] and
- * contiguous.  [TS] section 11. */
+ * caller, contiguous, K laid out [num_blocks, block_size, num_kv_heads,
+ * head_dim] and V [num_blocks, block_size, num_kv_heads, v_head_dim].
+ * [TS] section 11 (layout), section 4.1 (separate key and value lengths). */
 typedef struct pa_kv_cache {
   void *k_cache;
   void *v_cache;
   int32_t num_blocks;
   int32_t block_size;
   int32_t num_kv_heads;
-  int32_t head_dim;
-  int32_t dtype; /* pa_dtype */
+  int32_t head_dim;   /* key (and query) head dim */
+  int32_t dtype;      /* pa_dtype */
+  int32_t v_head_dim; /* value (and output) head dim; 0 means head_dim */
 } pa_kv_cache;
 
 /* ---------------------------------------------------------------------
@@ -118,7 +125,8 @@ typedef struct pa_kv_cache {
  * appended before attention, so the tokens a step writes are attended by
  * that same step.
  *
- *   key, value   : device, [num_tokens, num_kv_heads, head_dim], cache dtype.
+ *   key, value   : device, [num_tokens, num_kv_heads, head_dim] and
+ *                  [num_tokens, num_kv_heads, v_head_dim], cache dtype.
  *   slot_mapping : device, [num_tokens] int64.  Token t is copied to slot
  *                  slot_mapping[t], i.e. to block slot/block_size at offset
  *                  slot%block_size, for every kv head.  A negative slot
@@ -128,8 +136,9 @@ typedef struct pa_kv_cache {
  *
  * The copy is bit-exact.  Slots must be distinct: if two tokens name the
  * same slot, which one lands there is unspecified.  Only num_kv_heads *
- * head_dim * element_size % 16 == 0 is required of the shape; block_size
- * and head_dim need not be in the attention-supported sets.
+ * head_dim * element_size % 16 == 0 (and the same of v_head_dim) is
+ * required of the shape; block_size and the head dims need not be in the
+ * attention-supported sets.
  * --------------------------------------------------------------------- */
 int pa_kv_cache_write(const pa_kv_cache *cache, const void *key, const void *value,
                       const int64_t *slot_mapping, int32_t num_tokens, void *stream);
@@ -140,9 +149,9 @@ int pa_kv_cache_write(const pa_kv_cache *cache, const void *key, const void *val
  * grown into a larger allocation keeps the K/V already written; with an id
  * map the same call copies a shared block into a sequence's own block.
  *
- *   src, dst         : pools with the same dtype, block_size, num_kv_heads
- *                      and head_dim (num_blocks may differ; they may be the
- *                      same pool).
+ *   src, dst         : pools with the same dtype, block_size, num_kv_heads,
+ *                      head_dim and v_head_dim (num_blocks may differ; they
+ *                      may be the same pool).
  *   src_ids, dst_ids : device, [num_copies] int32, copy i moves block
  *                      src_ids[i] of src to block dst_ids[i] of dst; or both
  *                      NULL to copy blocks 0 .. num_copies-1 to the same ids
@@ -160,7 +169,8 @@ int pa_kv_cache_copy_blocks(const pa_kv_cache *src, const pa_kv_cache *dst, cons
  * pa_decode_workspace_bytes - bytes of fp32 workspace that split-K decode
  * needs: the per-partition running max m, sum l and unnormalised output
  * o[head_dim] for every (sequence, query head, partition), where there are
- * ceil(max_context_len / partition_size) partitions.  Returns 0 when
+ * ceil(max_context_len / partition_size) partitions.  head_dim is the
+ * width of the output rows: the cache's v_head_dim.  Returns 0 when
  * partition_size <= 0 (single pass) or when there is at most one
  * partition.  Negative sizes also give 0.
  * --------------------------------------------------------------------- */
@@ -173,7 +183,7 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t he
  * cache, the new token included once written), section 11 (paged buffers
  * and the online-softmax loop over (sequence, head)).
  *
- *   out            : device, [num_seqs, num_heads, head_dim], cache dtype.
+ *   out            : device, [num_seqs, num_heads, v_head_dim], cache dtype.
  *   q              : device, [num_seqs, num_heads, head_dim], cache dtype.
  *   block_tables   : device, [num_seqs, max_blocks_per_seq] int32.  Entries
  *                    past a sequence's last block are never read.
@@ -222,7 +232,8 @@ int pa_decode_partition(const pa_kv_cache *cache, void *out, const void *q, int3
  * more than one partition, it merges the partitions' (m, l, o) into
  *   out = sum_p o_p * 2^(m_p - M) / sum_p l_p * 2^(m_p - M),  M = max_p m_p,
  * where m is kept in base-2 units of the scaled scores.  Sequences with
- * at most one partition are left untouched.  dtype, num_seqs, num_heads,
+ * at most one partition are left untouched.  head_dim is the output row
+ * width (the cache's v_head_dim).  dtype, num_seqs, num_heads,
  * head_dim, context_lens, max_context_len, partition_size and the
  * workspace must match the pa_decode_partition call that filled it.
  * --------------------------------------------------------------------- */
@@ -265,8 +276,8 @@ int pa_decode_reduce(void *out, int32_t dtype, int32_t num_seqs, int32_t num_hea
  *                    stays correct and only the sharing is lost.
  *   workspace      : device, >= pa_decode_cascade_workspace_bytes(...)
  *                    bytes; scratch.
- * bf16 only, num_heads / num_kv_heads in {1, 2, 4} (PA_ERR_UNSUPPORTED
- * otherwise).
+ * bf16 only, num_heads / num_kv_heads in {1, 2, 4}, v_head_dim equal to
+ * head_dim (PA_ERR_UNSUPPORTED otherwise).
  * --------------------------------------------------------------------- */
 size_t pa_decode_cascade_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
                                          int32_t max_context_len, int32_t partition_size);
@@ -283,7 +294,8 @@ int pa_decode_cascade(const pa_kv_cache *cache, void *out, const void *q, int32_
  * pa_kv_cache_write first.  [MR] scheduling section: prefill proceeds in
  * chunks of up to 512 tokens under a 4096-token step budget.
  *
- *   out, q          : device, [num_query_tokens, num_heads, head_dim], cache
+ *   out, q          : device, [num_query_tokens, num_heads, v_head_dim] and
+ *                     [num_query_tokens, num_heads, head_dim], cache
  *                     dtype.  Sequence i owns rows
  *                     query_start_loc[i] .. query_start_loc[i+1]-1.
  *   query_start_loc : device, [num_seqs + 1] int32, non-decreasing, with

@@ -34,6 +34,11 @@ Readings where the pages are silent (each also listed in the design notes):
 * a row with no visible key (``n = 0``) returns zeros;
 * arithmetic is float64 unless ``acc_dtype`` says otherwise.
 
+Key and value head dims may differ (section 4.1: separate key and value
+lengths, each defaulting to the head dim).  Below, ``D`` is the key (and
+query) head dim and ``Dv`` the value head dim, which is also the width of
+the outputs; every function works for ``Dv == D`` and ``Dv != D`` alike.
+
 Parity pins live in the CPU test suite; every function here is pinned.
 """
 
@@ -56,9 +61,10 @@ def kv_cache_write(k_cache, v_cache, key, value, slot_mapping):
     ``slot_mapping[t]`` (TensorSharp Mistral 3, section 11, slotMapping
     scatter).
 
-    ``k_cache``/``v_cache``: ``[num_blocks, block_size, num_kv_heads,
-    head_dim]`` (any element type: the write is a copy).  ``key``/``value``:
-    ``[T, num_kv_heads, head_dim]``.  A negative slot skips its token.
+    ``k_cache``/``v_cache``: ``[num_blocks, block_size, num_kv_heads, D]``
+    and ``[..., Dv]`` (any element type: the write is a copy).
+    ``key``/``value``: ``[T, num_kv_heads, D]`` and ``[T, num_kv_heads, Dv]``.
+    A negative slot skips its token.
     """
     k = np.array(k_cache, copy=True)
     v = np.array(v_cache, copy=True)
@@ -114,8 +120,8 @@ def attention_weights(q_h, k_g, scale, query_pos, acc_dtype=np.float64):
 
 def attention(q, k, v, scale, query_pos, acc_dtype=np.float64):
     """Grouped-query attention of ``q [Tq, Hq, D]`` over dense
-    ``k, v [n, Hkv, D]``; query head ``h`` uses kv head ``h // (Hq // Hkv)``.
-    Returns ``[Tq, Hq, D]`` in ``acc_dtype``."""
+    ``k [n, Hkv, D]``, ``v [n, Hkv, Dv]``; query head ``h`` uses kv head
+    ``h // (Hq // Hkv)``.  Returns ``[Tq, Hq, Dv]`` in ``acc_dtype``."""
     Tq, Hq, D = q.shape
     Hkv = k.shape[1]
     if Hq % Hkv:
@@ -133,10 +139,10 @@ def paged_decode(q, k_cache, v_cache, block_tables, context_lens, scale,
                  acc_dtype=np.float64, seqs=None):
     """One query token per sequence over its whole context.
 
-    ``q [S, Hq, D]``; caches ``[NB, BS, Hkv, D]`` already holding the new
-    tokens; ``block_tables [S, max_blocks]``; ``context_lens [S]``.
-    ``seqs`` restricts the work to some sequences (others stay zero).
-    Returns ``[S, Hq, D]`` in ``acc_dtype``.
+    ``q [S, Hq, D]``; caches ``[NB, BS, Hkv, D]`` and ``[NB, BS, Hkv, Dv]``
+    already holding the new tokens; ``block_tables [S, max_blocks]``;
+    ``context_lens [S]``.  ``seqs`` restricts the work to some sequences
+    (others stay zero).  Returns ``[S, Hq, Dv]`` in ``acc_dtype``.
     """
     S, Hq, D = q.shape
     out = np.zeros((S, Hq, v_cache.shape[3]), dtype=acc_dtype)
@@ -155,7 +161,7 @@ def paged_prefill(q, query_start_loc, k_cache, v_cache, block_tables, context_le
 
     Sequence ``i`` owns query rows ``query_start_loc[i] .. [i+1]-1`` of
     ``q [Tq, Hq, D]``; ``context_lens[i]`` counts prefix + chunk.  Returns
-    ``[Tq, Hq, D]`` in ``acc_dtype``.
+    ``[Tq, Hq, Dv]`` in ``acc_dtype``.
     """
     Tq, Hq, D = q.shape
     out = np.zeros((Tq, Hq, v_cache.shape[3]), dtype=acc_dtype)

@@ -53,6 +53,7 @@ class PaKvCache(ctypes.Structure):
         ("num_kv_heads", _i32),
         ("head_dim", _i32),
         ("dtype", _i32),
+        ("v_head_dim", _i32),
     ]
 
 
@@ -201,14 +202,17 @@ def _stream(stream) -> ctypes.c_void_p:
 
 
 def make_cache(k_cache, v_cache) -> PaKvCache:
-    """Descriptor for one layer's pool ``[num_blocks, block_size, num_kv_heads, head_dim]``."""
-    if k_cache.shape != v_cache.shape or k_cache.dim() != 4:
-        raise ValueError(f"k_cache {tuple(k_cache.shape)} and v_cache {tuple(v_cache.shape)} must be equal 4-d shapes")
+    """Descriptor for one layer's pool: K ``[num_blocks, block_size,
+    num_kv_heads, head_dim]`` and V ``[num_blocks, block_size, num_kv_heads,
+    v_head_dim]`` (the value head dim may differ from the key head dim)."""
+    if k_cache.dim() != 4 or v_cache.dim() != 4 or k_cache.shape[:3] != v_cache.shape[:3]:
+        raise ValueError(f"k_cache {tuple(k_cache.shape)} and v_cache {tuple(v_cache.shape)} must be 4-d "
+                         "shapes that agree in all but the last dim")
     if k_cache.dtype != v_cache.dtype:
         raise TypeError("k_cache and v_cache dtypes differ")
     nb, bs, hkv, d = (int(x) for x in k_cache.shape)
     return PaKvCache(_dev(k_cache, "k_cache").value, _dev(v_cache, "v_cache").value, nb, bs, hkv, d,
-                     _dtype_code(k_cache))
+                     _dtype_code(k_cache), int(v_cache.shape[3]))
 
 
 # ------------------------------------------------------------ entry points
@@ -232,12 +236,14 @@ def pa_decode_workspace_bytes(num_seqs: int, num_heads: int, head_dim: int, max_
 
 
 def pa_kv_cache_write(key, value, k_cache, v_cache, slot_mapping, stream=None) -> None:
-    """Scatter ``key``/``value`` ``[T, Hkv, D]`` into the pool at ``slot_mapping`` (int64 [T])."""
+    """Scatter ``key [T, Hkv, D]`` / ``value [T, Hkv, Dv]`` into the pool at
+    ``slot_mapping`` (int64 [T])."""
     torch = _torch()
     cache = make_cache(k_cache, v_cache)
-    if key.shape != value.shape or key.dim() != 3 or tuple(key.shape[1:]) != tuple(k_cache.shape[2:]):
+    if (key.dim() != 3 or value.dim() != 3 or tuple(key.shape[1:]) != tuple(k_cache.shape[2:])
+            or tuple(value.shape[1:]) != tuple(v_cache.shape[2:]) or key.shape[0] != value.shape[0]):
         raise ValueError(f"key/value {tuple(key.shape)}/{tuple(value.shape)} must be [T, "
-                         f"{k_cache.shape[2]}, {k_cache.shape[3]}]")
+                         f"{k_cache.shape[2]}, {k_cache.shape[3]}] / [T, {v_cache.shape[2]}, {v_cache.shape[3]}]")
     if slot_mapping.shape != (key.shape[0],):
         raise ValueError(f"slot_mapping {tuple(slot_mapping.shape)} must be [{key.shape[0]}]")
     code = load_library().pa_kv_cache_write(
@@ -279,13 +285,14 @@ def _decode_args(q, k_cache, v_cache, block_tables, context_lens, out):
         raise ValueError(f"block_tables {tuple(block_tables.shape)} must be [{S}, max_blocks_per_seq]")
     if tuple(context_lens.shape) != (S,):
         raise ValueError(f"context_lens {tuple(context_lens.shape)} must be [{S}]")
+    Dv = int(v_cache.shape[3])
     if out is None:
-        out = torch.empty_like(q)
-    elif tuple(out.shape) != tuple(q.shape) or out.dtype != q.dtype:
-        raise ValueError("out must match q in shape and dtype")
+        out = torch.empty((S, H, Dv), dtype=q.dtype, device=q.device)
+    elif tuple(out.shape) != (S, H, Dv) or out.dtype != q.dtype:
+        raise ValueError(f"out must be [{S}, {H}, {Dv}] of q's dtype")
     ptrs = (_dev(out, "out", k_cache.dtype, 3), _dev(q, "q", k_cache.dtype, 3),
             _dev(block_tables, "block_tables", torch.int32), _dev(context_lens, "context_lens", torch.int32))
-    return cache, S, H, D, out, ptrs
+    return cache, S, H, Dv, out, ptrs
 
 
 def _workspace(workspace, need: int, device):
@@ -302,16 +309,16 @@ def _workspace(workspace, need: int, device):
 
 def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, max_context_len: int,
               partition_size: int = 512, out=None, workspace=None, stream=None, _stage: str = "both"):
-    """Paged decode: ``q [S, H, D]`` -> ``out [S, H, D]``.
+    """Paged decode: ``q [S, H, D]`` -> ``out [S, H, Dv]``.
 
     ``partition_size`` 0 runs one pass per (sequence, kv head); otherwise
     split-K partitions of that many tokens plus the reduce kernel.
     ``workspace`` (uint8 GPU tensor) is allocated here when not given.
     """
-    cache, S, H, D, out, (p_out, p_q, p_bt, p_cl) = _decode_args(q, k_cache, v_cache, block_tables,
+    cache, S, H, Dv, out, (p_out, p_q, p_bt, p_cl) = _decode_args(q, k_cache, v_cache, block_tables,
                                                                  context_lens, out)
     lib = load_library()
-    need = int(lib.pa_decode_workspace_bytes(S, H, D, int(max_context_len), int(partition_size)))
+    need = int(lib.pa_decode_workspace_bytes(S, H, Dv, int(max_context_len), int(partition_size)))
     p_ws, ws_bytes = _workspace(workspace, need, q.device)
     st = _stream(stream)
     mbps = int(block_tables.shape[1])
@@ -321,7 +328,7 @@ def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, max
                   float(scale), int(partition_size), p_ws, ws_bytes, st)
         _check("pa_decode" if _stage == "both" else "pa_decode_partition", code)
     if _stage == "reduce":
-        code = lib.pa_decode_reduce(p_out, cache.dtype, S, H, D, p_cl, int(max_context_len),
+        code = lib.pa_decode_reduce(p_out, cache.dtype, S, H, Dv, p_cl, int(max_context_len),
                                     int(partition_size), p_ws, ws_bytes, st)
         _check("pa_decode_reduce", code)
     return out
@@ -356,13 +363,13 @@ def pa_decode_cascade(q, k_cache, v_cache, block_tables, context_lens, scale: fl
     [G]`` int32 GPU tensors; ``max_group_size`` and ``max_shared_len`` host
     ints, the latter defaulting to ``max_context_len``)."""
     torch = _torch()
-    cache, S, H, D, out, (p_out, p_q, p_bt, p_cl) = _decode_args(q, k_cache, v_cache, block_tables,
+    cache, S, H, Dv, out, (p_out, p_q, p_bt, p_cl) = _decode_args(q, k_cache, v_cache, block_tables,
                                                                  context_lens, out)
     G = int(shared_len.numel())
     if tuple(group_start.shape) != (G + 1,):
         raise ValueError(f"group_start {tuple(group_start.shape)} must be [{G + 1}]")
     lib = load_library()
-    need = int(lib.pa_decode_cascade_workspace_bytes(S, H, D, int(max_context_len), int(partition_size)))
+    need = int(lib.pa_decode_cascade_workspace_bytes(S, H, Dv, int(max_context_len), int(partition_size)))
     p_ws, ws_bytes = _workspace(workspace, need, q.device)
     code = lib.pa_decode_cascade(ctypes.byref(cache), p_out, p_q, S, H, p_bt, int(block_tables.shape[1]), p_cl,
                                  int(max_context_len), float(scale), int(partition_size), G,
@@ -376,7 +383,7 @@ def pa_decode_cascade(q, k_cache, v_cache, block_tables, context_lens, scale: fl
 
 def pa_prefill_chunk(q, query_start_loc, k_cache, v_cache, block_tables, context_lens, scale: float,
                      max_query_len: int, max_context_len: int, out=None, stream=None):
-    """Chunked prefill: packed ``q [Tq, H, D]`` -> ``out [Tq, H, D]``."""
+    """Chunked prefill: packed ``q [Tq, H, D]`` -> ``out [Tq, H, Dv]``."""
     torch = _torch()
     cache = make_cache(k_cache, v_cache)
     Tq, H, D = (int(x) for x in q.shape)
@@ -385,8 +392,13 @@ def pa_prefill_chunk(q, query_start_loc, k_cache, v_cache, block_tables, context
         raise ValueError(f"query_start_loc {tuple(query_start_loc.shape)} must be [{S + 1}]")
     if block_tables.dim() != 2 or int(block_tables.shape[0]) != S:
         raise ValueError(f"block_tables {tuple(block_tables.shape)} must be [{S}, max_blocks_per_seq]")
+    if D != int(k_cache.shape[3]):
+        raise ValueError(f"q head_dim {D} != cache head_dim {k_cache.shape[3]}")
+    Dv = int(v_cache.shape[3])
     if out is None:
-        out = torch.empty_like(q)
+        out = torch.empty((Tq, H, Dv), dtype=q.dtype, device=q.device)
+    elif tuple(out.shape) != (Tq, H, Dv) or out.dtype != q.dtype:
+        raise ValueError(f"out must be [{Tq}, {H}, {Dv}] of q's dtype")
     code = load_library().pa_prefill_chunk(
         ctypes.byref(cache), _dev(out, "out", k_cache.dtype, 3), _dev(q, "q", k_cache.dtype, 3),
         _dev(query_start_loc, "query_start_loc", torch.int32), S, H, Tq, int(max_query_len),

@@ -62,6 +62,22 @@ int elem_bytes(int dtype) { return dtype == PA_DTYPE_BF16 ? 2 : 4; }
 
 constexpr int kMaxGridYZ = 65535;
 
+// value head dim of a pool (0 in the descriptor: the key head dim)
+int v_dim(const pa_kv_cache *c) { return c->v_head_dim ? c->v_head_dim : c->head_dim; }
+
+pa::CacheView view(const pa_kv_cache *c) {
+  pa::CacheView v;
+  v.k = c->k_cache;
+  v.v = c->v_cache;
+  v.num_blocks = c->num_blocks;
+  v.block_size = c->block_size;
+  v.num_kv_heads = c->num_kv_heads;
+  v.head_dim = c->head_dim;
+  v.dtype = c->dtype;
+  v.head_dim_v = v_dim(c);
+  return v;
+}
+
 // Cache descriptor checks shared by all entry points.  `attention` adds
 // the shape limits of the attention kernels.
 int check_cache(const pa_kv_cache *c, bool attention) {
@@ -74,12 +90,16 @@ int check_cache(const pa_kv_cache *c, bool attention) {
   if (c->num_blocks <= 0) return fail(PA_ERR_SHAPE, "num_blocks %d must be > 0", c->num_blocks);
   if (c->num_kv_heads <= 0) return fail(PA_ERR_SHAPE, "num_kv_heads %d must be > 0", c->num_kv_heads);
   if (c->head_dim <= 0) return fail(PA_ERR_HEAD_DIM, "head_dim %d must be > 0", c->head_dim);
+  if (c->v_head_dim < 0)
+    return fail(PA_ERR_HEAD_DIM, "v_head_dim %d must be > 0 (or 0: same as head_dim)", c->v_head_dim);
   if (c->block_size <= 0) return fail(PA_ERR_BLOCK_SIZE, "block_size %d must be > 0", c->block_size);
   if (attention) {
     if (c->block_size != 8 && c->block_size != 16 && c->block_size != 32)
       return fail(PA_ERR_BLOCK_SIZE, "block_size %d not in {8, 16, 32}", c->block_size);
     if (c->head_dim != 64 && c->head_dim != 128)
       return fail(PA_ERR_HEAD_DIM, "head_dim %d not in {64, 128}", c->head_dim);
+    if (v_dim(c) != 64 && v_dim(c) != 128)
+      return fail(PA_ERR_HEAD_DIM, "v_head_dim %d not in {64, 128}", v_dim(c));
     if (c->num_kv_heads > kMaxGridYZ)
       return fail(PA_ERR_SHAPE, "num_kv_heads %d above %d", c->num_kv_heads, kMaxGridYZ);
   }
@@ -140,15 +160,14 @@ int prepare_decode(const pa_kv_cache *cache, void *out, const void *q, int32_t n
                 out, q, (const void *)block_tables, (const void *)context_lens);
   const int P = num_partitions(max_context_len, partition_size);
   const size_t need = split_k_workspace
-                          ? workspace_bytes(num_seqs, num_heads, cache->head_dim, max_context_len, partition_size)
+                          ? workspace_bytes(num_seqs, num_heads, v_dim(cache), max_context_len, partition_size)
                           : 0;
   if (need > 0) {
     if (!workspace) return fail(PA_ERR_WORKSPACE, "workspace is NULL; %zu bytes needed", need);
     if (ws_bytes < need)
       return fail(PA_ERR_WORKSPACE, "workspace_bytes %zu < %zu needed", ws_bytes, need);
   }
-  a->cache = {cache->k_cache, cache->v_cache, cache->num_blocks, cache->block_size,
-              cache->num_kv_heads, cache->head_dim, cache->dtype};
+  a->cache = view(cache);
   a->out = out;
   a->q = q;
   a->num_seqs = num_seqs;
@@ -175,7 +194,7 @@ int prepare_decode(const pa_kv_cache *cache, void *out, const void *q, int32_t n
 
 extern "C" {
 
-int pa_version(void) { return 10000; }  // 1.0.0
+int pa_version(void) { return 10100; }  // 1.1.0: v_head_dim in pa_kv_cache
 
 const char *pa_last_error_message(void) { return pa::last_error(); }
 
@@ -204,17 +223,24 @@ int pa_kv_cache_write(const pa_kv_cache *cache, const void *key, const void *val
   if (st) return st;
   if (num_tokens < 0) return fail(PA_ERR_SHAPE, "num_tokens %d must be >= 0", num_tokens);
   const int64_t row_bytes = (int64_t)cache->num_kv_heads * cache->head_dim * elem_bytes(cache->dtype);
+  const int64_t v_row_bytes = (int64_t)cache->num_kv_heads * v_dim(cache) * elem_bytes(cache->dtype);
   if (row_bytes % 16)
     return fail(PA_ERR_SHAPE, "num_kv_heads * head_dim * element size = %lld bytes is not a multiple of 16",
                 (long long)row_bytes);
-  if (row_bytes > (1 << 30)) return fail(PA_ERR_SHAPE, "row of %lld bytes too large", (long long)row_bytes);
+  if (v_row_bytes % 16)
+    return fail(PA_ERR_SHAPE, "num_kv_heads * v_head_dim * element size = %lld bytes is not a multiple of 16",
+                (long long)v_row_bytes);
+  if (row_bytes > (1 << 29) || v_row_bytes > (1 << 29))
+    return fail(PA_ERR_SHAPE, "rows of %lld and %lld bytes too large", (long long)row_bytes,
+                (long long)v_row_bytes);
   if (num_tokens == 0) return ok();
   if (!key || !value || !slot_mapping)
     return fail(PA_ERR_NULL, "key=%p value=%p slot_mapping=%p: all must be device pointers", key, value,
                 (const void *)slot_mapping);
   const int64_t num_slots = (int64_t)cache->num_blocks * cache->block_size;
-  hipError_t e = pa::launch_kv_cache_write(cache->k_cache, cache->v_cache, num_slots, (int)row_bytes, key,
-                                           value, slot_mapping, num_tokens, (hipStream_t)stream);
+  hipError_t e = pa::launch_kv_cache_write(cache->k_cache, cache->v_cache, num_slots, (int)row_bytes,
+                                           (int)v_row_bytes, key, value, slot_mapping, num_tokens,
+                                           (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "kv_cache_write launch");
   return ok();
 }
@@ -227,10 +253,10 @@ int pa_kv_cache_copy_blocks(const pa_kv_cache *src, const pa_kv_cache *dst, cons
   if (src->dtype != dst->dtype)
     return fail(PA_ERR_DTYPE, "source dtype %d differs from destination dtype %d", src->dtype, dst->dtype);
   if (src->block_size != dst->block_size || src->num_kv_heads != dst->num_kv_heads ||
-      src->head_dim != dst->head_dim)
-    return fail(PA_ERR_SHAPE, "block shapes differ: source (%d, %d, %d), destination (%d, %d, %d) as "
-                "(block_size, num_kv_heads, head_dim)", src->block_size, src->num_kv_heads, src->head_dim,
-                dst->block_size, dst->num_kv_heads, dst->head_dim);
+      src->head_dim != dst->head_dim || v_dim(src) != v_dim(dst))
+    return fail(PA_ERR_SHAPE, "block shapes differ: source (%d, %d, %d, %d), destination (%d, %d, %d, %d) as "
+                "(block_size, num_kv_heads, head_dim, v_head_dim)", src->block_size, src->num_kv_heads,
+                src->head_dim, v_dim(src), dst->block_size, dst->num_kv_heads, dst->head_dim, v_dim(dst));
   if (num_copies < 0) return fail(PA_ERR_SHAPE, "num_copies %d must be >= 0", num_copies);
   if ((src_ids == nullptr) != (dst_ids == nullptr))
     return fail(PA_ERR_NULL, "src_ids=%p dst_ids=%p: give both or neither", (const void *)src_ids,
@@ -240,12 +266,15 @@ int pa_kv_cache_copy_blocks(const pa_kv_cache *src, const pa_kv_cache *dst, cons
                 src->num_blocks, dst->num_blocks);
   const int64_t block_bytes =
       (int64_t)src->block_size * src->num_kv_heads * src->head_dim * elem_bytes(src->dtype);
-  if (block_bytes % 16)
-    return fail(PA_ERR_SHAPE, "a block is %lld bytes, not a multiple of 16", (long long)block_bytes);
+  const int64_t v_block_bytes =
+      (int64_t)src->block_size * src->num_kv_heads * v_dim(src) * elem_bytes(src->dtype);
+  if (block_bytes % 16 || v_block_bytes % 16)
+    return fail(PA_ERR_SHAPE, "a block is %lld bytes of K and %lld of V, not multiples of 16",
+                (long long)block_bytes, (long long)v_block_bytes);
   if (num_copies == 0) return ok();
   hipError_t e = pa::launch_kv_cache_copy_blocks(src->k_cache, src->v_cache, dst->k_cache, dst->v_cache,
-                                                 src->num_blocks, dst->num_blocks, block_bytes, src_ids,
-                                                 dst_ids, num_copies, (hipStream_t)stream);
+                                                 src->num_blocks, dst->num_blocks, block_bytes, v_block_bytes,
+                                                 src_ids, dst_ids, num_copies, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "kv_cache_copy_blocks launch");
   return ok();
 }
@@ -294,6 +323,7 @@ int pa_decode_reduce(void *out, int32_t dtype, int32_t num_seqs, int32_t num_hea
   pa::DecodeArgs a{};
   a.cache.dtype = dtype;
   a.cache.head_dim = head_dim;
+  a.cache.head_dim_v = head_dim;  // the output row width
   a.cache.block_size = 1;  // unused by the reduce
   a.cache.num_kv_heads = 1;
   a.out = out;
@@ -366,6 +396,9 @@ int pa_decode_cascade(const pa_kv_cache *cache, void *out, const void *q, int32_
   if (st) return st;
   if (cache->dtype != PA_DTYPE_BF16)
     return fail(PA_ERR_UNSUPPORTED, "cascade decode is bf16 only (dtype %d)", cache->dtype);
+  if (v_dim(cache) != cache->head_dim)
+    return fail(PA_ERR_UNSUPPORTED, "cascade decode needs v_head_dim equal to head_dim (%d vs %d)",
+                v_dim(cache), cache->head_dim);
   const int group = num_heads / cache->num_kv_heads;
   if (group > 4) return fail(PA_ERR_UNSUPPORTED, "cascade decode takes num_heads / num_kv_heads in {1, 2, 4}, got %d",
                              group);
@@ -458,8 +491,7 @@ int pa_prefill_chunk(const pa_kv_cache *cache, void *out, const void *q, const i
                 "out=%p q=%p query_start_loc=%p block_tables=%p context_lens=%p: all must be device pointers",
                 out, q, (const void *)query_start_loc, (const void *)block_tables, (const void *)context_lens);
   pa::PrefillArgs a;
-  a.cache = {cache->k_cache, cache->v_cache, cache->num_blocks, cache->block_size,
-             cache->num_kv_heads, cache->head_dim, cache->dtype};
+  a.cache = view(cache);
   a.out = out;
   a.q = q;
   a.query_start_loc = query_start_loc;
@@ -474,8 +506,9 @@ int pa_prefill_chunk(const pa_kv_cache *cache, void *out, const void *q, const i
   a.scale = scale;
   hipError_t e = pa::launch_prefill_chunk(a, (hipStream_t)stream);
   if (e == hipErrorNotSupported)
-    return fail(PA_ERR_UNSUPPORTED, "prefill_chunk: head_dim %d with num_heads/num_kv_heads %d not built",
-                cache->head_dim, num_heads / cache->num_kv_heads);
+    return fail(PA_ERR_UNSUPPORTED,
+                "prefill_chunk: head_dim %d, v_head_dim %d with num_heads/num_kv_heads %d not built",
+                cache->head_dim, v_dim(cache), num_heads / cache->num_kv_heads);
   if (e != hipSuccess) return hip_fail(e, "prefill_chunk launch");
   return ok();
 }

@@ -68,6 +68,42 @@ struct Chunk<bf16_t> {
   }
 };
 
+// N consecutive elements of T (N * sizeof(T) in {8, 16, 32} bytes, as
+// aligned) loaded with 64- or 128-bit loads, then widened into floats.
+template <typename T, int N>
+struct Vec {
+  static constexpr int kWords = N * ElemTraits<T>::kBytes / 4;
+  static_assert(kWords == 2 || kWords == 4 || kWords == 8, "8, 16 or 32 bytes");
+  uint32_t w[kWords];
+  __device__ __forceinline__ void load(const T *p) {
+    if constexpr (kWords == 2) {
+      const uint2 c = *reinterpret_cast<const uint2 *>(p);
+      w[0] = c.x, w[1] = c.y;
+    } else {
+#pragma unroll
+      for (int i = 0; i < kWords / 4; ++i) {
+        const uint4 c = reinterpret_cast<const uint4 *>(p)[i];
+        w[4 * i] = c.x, w[4 * i + 1] = c.y, w[4 * i + 2] = c.z, w[4 * i + 3] = c.w;
+      }
+    }
+  }
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int i = 0; i < kWords; ++i) w[i] = 0;
+  }
+  __device__ __forceinline__ void widen(float *f) const {
+#pragma unroll
+    for (int i = 0; i < kWords; ++i) {
+      if constexpr (ElemTraits<T>::kBytes == 2) {
+        f[2 * i] = bf16_lo(w[i]);
+        f[2 * i + 1] = bf16_hi(w[i]);
+      } else {
+        f[i] = __uint_as_float(w[i]);
+      }
+    }
+  }
+};
+
 // ------------------------------------------------------- lane exchanges
 // DPP controls (GCN/CDNA encoding).
 enum : int {
@@ -180,15 +216,16 @@ struct CacheView {
   const void *k;
   const void *v;
   int num_blocks, block_size, num_kv_heads, head_dim, dtype;
+  int head_dim_v;  // value (and output) head dim
 };
 
-hipError_t launch_kv_cache_write(void *k_cache, void *v_cache, int64_t num_slots, int row_bytes,
-                                 const void *key, const void *value, const int64_t *slots,
+hipError_t launch_kv_cache_write(void *k_cache, void *v_cache, int64_t num_slots, int k_row_bytes,
+                                 int v_row_bytes, const void *key, const void *value, const int64_t *slots,
                                  int num_tokens, hipStream_t stream);
 hipError_t launch_kv_cache_copy_blocks(const void *src_k, const void *src_v, void *dst_k, void *dst_v,
-                                       int src_blocks, int dst_blocks, int64_t block_bytes,
-                                       const int32_t *src_ids, const int32_t *dst_ids, int num_copies,
-                                       hipStream_t stream);
+                                       int src_blocks, int dst_blocks, int64_t k_block_bytes,
+                                       int64_t v_block_bytes, const int32_t *src_ids, const int32_t *dst_ids,
+                                       int num_copies, hipStream_t stream);
 
 struct DecodeArgs {
   CacheView cache;

@@ -35,6 +35,10 @@
 //  * The block id of each load is the same for the whole wave (a load
 //    covers 64 / L consecutive tokens inside one block), so block-table
 //    reads are scalar loads.
+//  * Key and value head dims may differ (section 4.1 of the same page):
+//    the L lanes of a token's K row also cover its V row, each lane
+//    loading DV / L elements of V (8, 16 or 32 bytes), so the softmax
+//    weights of a lane's token serve both.
 #include <type_traits>
 
 #include "pa_common.h"
@@ -118,11 +122,13 @@ __device__ __forceinline__ void store_one<bf16_t>(void *base, size_t idx, float 
   static_cast<uint16_t *>(base)[idx] = (uint16_t)f32_to_bf16_bits(v);
 }
 
-template <typename T, int D, int G>
+template <typename T, int D, int DV, int G>
 __global__ void __launch_bounds__(256)
 decode_partition_kernel(const DecodeKernelArgs a) {
   using S = DecodeShape<T, D>;
   constexpr int E = S::kElems;
+  constexpr int EV = DV / S::kLanesPerRow;  // V elements per lane
+  using VRow = Vec<T, EV>;
   constexpr int L = S::kLanesPerRow;
   constexpr int R = S::kRowsPerWave;
   constexpr int U = S::kUnroll;
@@ -159,26 +165,28 @@ decode_partition_kernel(const DecodeKernelArgs a) {
     }
   }
 
-  const size_t slot_stride = (size_t)a.num_kv_heads * D;  // elements between slots
+  const size_t slot_stride = (size_t)a.num_kv_heads * D;  // elements between K slots
+  const size_t vslot_stride = (size_t)a.num_kv_heads * DV;
   const T *kbase = static_cast<const T *>(a.k_cache) + (size_t)kvh * D + col * E;
-  const T *vbase = static_cast<const T *>(a.v_cache) + (size_t)kvh * D + col * E;
+  const T *vbase = static_cast<const T *>(a.v_cache) + (size_t)kvh * DV + col * EV;
   const int32_t *bt = a.block_tables + (size_t)seq * a.max_blocks_per_seq;
   const int bs_mask = (1 << a.block_shift) - 1;
 
-  float m_run[G], l_run[G], acc[G][E];
+  float m_run[G], l_run[G], acc[G][EV];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     m_run[h] = -INFINITY;
     l_run[h] = 0.f;
 #pragma unroll
-    for (int e = 0; e < E; ++e) acc[h][e] = 0.f;
+    for (int e = 0; e < EV; ++e) acc[h][e] = 0.f;
   }
 
   const int ntok = p1 - p0;
   const int nchunks = ntok > 0 ? (ntok + CH - 1) / CH : 0;
   for (int c = wave; c < nchunks; c += W) {
     const int cbase = p0 + c * CH;
-    uint4 kr[U], vr[U];
+    uint4 kr[U];
+    VRow vr[U];
     bool valid[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -188,11 +196,11 @@ decode_partition_kernel(const DecodeKernelArgs a) {
       if (tok0 < p1) blk = bt[tok0 >> a.block_shift];
       valid[u] = (tok < p1) && ((unsigned)blk < (unsigned)a.num_blocks);
       kr[u] = make_uint4(0, 0, 0, 0);
-      vr[u] = make_uint4(0, 0, 0, 0);
+      vr[u].zero();
       if (valid[u]) {
         const size_t slot = ((size_t)blk << a.block_shift) + (tok & bs_mask);
         kr[u] = *reinterpret_cast<const uint4 *>(kbase + slot * slot_stride);
-        vr[u] = *reinterpret_cast<const uint4 *>(vbase + slot * slot_stride);
+        vr[u].load(vbase + slot * vslot_stride);
       }
     }
 
@@ -224,18 +232,18 @@ decode_partition_kernel(const DecodeKernelArgs a) {
       m_run[h] = m_new;
       l_run[h] *= alpha;
 #pragma unroll
-      for (int e = 0; e < E; ++e) acc[h][e] *= alpha;
+      for (int e = 0; e < EV; ++e) acc[h][e] *= alpha;
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      float vf[E];
-      Chunk<T>::widen(vr[u], vf);
+      float vf[EV];
+      vr[u].widen(vf);
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         const float p = valid[u] ? fast_exp2(s[u][h] - m_run[h]) : 0.f;
         l_run[h] += p;
 #pragma unroll
-        for (int e = 0; e < E; ++e) acc[h][e] = fmaf(p, vf[e], acc[h][e]);
+        for (int e = 0; e < EV; ++e) acc[h][e] = fmaf(p, vf[e], acc[h][e]);
       }
     }
   }
@@ -245,17 +253,17 @@ decode_partition_kernel(const DecodeKernelArgs a) {
   for (int h = 0; h < G; ++h) {
     l_run[h] = across_groups_sum<L>(l_run[h]);
 #pragma unroll
-    for (int e = 0; e < E; ++e) acc[h][e] = across_groups_sum<L>(acc[h][e]);
+    for (int e = 0; e < EV; ++e) acc[h][e] = across_groups_sum<L>(acc[h][e]);
   }
 
   __shared__ float sm_m[W][G];
   __shared__ float sm_l[W][G];
-  __shared__ float sm_o[W][G][D];
+  __shared__ float sm_o[W][G][DV];
   if (lane < L) {
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int e = 0; e < E; ++e) sm_o[wave][h][col * E + e] = acc[h][e];
+      for (int e = 0; e < EV; ++e) sm_o[wave][h][col * EV + e] = acc[h][e];
   }
   if (lane == 0) {
 #pragma unroll
@@ -267,9 +275,9 @@ decode_partition_kernel(const DecodeKernelArgs a) {
   __syncthreads();
 
   const bool direct = (nparts == 1);
-  for (int i = threadIdx.x; i < G * D; i += S::kThreads) {
-    const int h = i / D;
-    const int d = i - h * D;
+  for (int i = threadIdx.x; i < G * DV; i += S::kThreads) {
+    const int h = i / DV;
+    const int d = i - h * DV;
     float M = sm_m[0][h];
 #pragma unroll
     for (int w = 1; w < W; ++w) M = fmaxf(M, sm_m[w][h]);
@@ -286,10 +294,10 @@ decode_partition_kernel(const DecodeKernelArgs a) {
     const int head = kvh * G + h;
     if (direct) {
       const float r = (l > 0.f) ? o / l : 0.f;
-      store_one<T>(a.out, ((size_t)seq * a.num_heads + head) * D + d, r);
+      store_one<T>(a.out, ((size_t)seq * a.num_heads + head) * DV + d, r);
     } else {
       const size_t idx = ((size_t)seq * a.num_heads + head) * a.max_partitions + part;
-      a.ws_o[idx * D + d] = o;
+      a.ws_o[idx * DV + d] = o;
       if (d == 0) {
         a.ws_m[idx] = M;
         a.ws_l[idx] = l;
@@ -901,39 +909,41 @@ static DecodeKernelArgs make_kernel_args(const DecodeArgs &a) {
   return k;
 }
 
-template <typename T, int D, int G>
+template <typename T, int D, int DV, int G>
 static hipError_t launch_partition_t(const DecodeArgs &a, hipStream_t stream) {
   const DecodeKernelArgs k = make_kernel_args(a);
   dim3 grid(a.max_partitions, a.cache.num_kv_heads, a.num_seqs);
-  if constexpr (std::is_same<T, bf16_t>::value && G <= 4) {
+  if constexpr (std::is_same<T, bf16_t>::value && G <= 4 && D == DV) {
 #if PA_DECODE_ORDER == 1 || PA_DECODE_ORDER == 3
     grid = dim3(a.cache.num_kv_heads, a.num_seqs, a.max_partitions);
 #endif
     hipLaunchKernelGGL((decode_partition_bf16_kernel<D, G>), grid, dim3(64 * PA_DECODE_WAVES), 0, stream, k);
   } else {
-    hipLaunchKernelGGL((decode_partition_kernel<T, D, G>), grid, dim3(DecodeShape<T, D>::kThreads), 0,
+    // (cascade launches are bf16 with G <= 4 and D == DV: never here)
+    hipLaunchKernelGGL((decode_partition_kernel<T, D, DV, G>), grid, dim3(DecodeShape<T, D>::kThreads), 0,
                        stream, k);
   }
   return hipGetLastError();
 }
 
-template <typename T, int D>
+template <typename T, int D, int DV>
 static hipError_t launch_partition_g(const DecodeArgs &a, hipStream_t stream) {
   switch (a.num_heads / a.cache.num_kv_heads) {
-    case 1: return launch_partition_t<T, D, 1>(a, stream);
-    case 2: return launch_partition_t<T, D, 2>(a, stream);
-    case 4: return launch_partition_t<T, D, 4>(a, stream);
-    case 8: return launch_partition_t<T, D, 8>(a, stream);
+    case 1: return launch_partition_t<T, D, DV, 1>(a, stream);
+    case 2: return launch_partition_t<T, D, DV, 2>(a, stream);
+    case 4: return launch_partition_t<T, D, DV, 4>(a, stream);
+    case 8: return launch_partition_t<T, D, DV, 8>(a, stream);
   }
   return hipErrorInvalidValue;
 }
 
 template <typename T>
 static hipError_t launch_partition_d(const DecodeArgs &a, hipStream_t stream) {
-  switch (a.cache.head_dim) {
-    case 64: return launch_partition_g<T, 64>(a, stream);
-    case 128: return launch_partition_g<T, 128>(a, stream);
-  }
+  const int dk = a.cache.head_dim, dv = a.cache.head_dim_v;
+  if (dk == 64 && dv == 64) return launch_partition_g<T, 64, 64>(a, stream);
+  if (dk == 128 && dv == 128) return launch_partition_g<T, 128, 128>(a, stream);
+  if (dk == 128 && dv == 64) return launch_partition_g<T, 128, 64>(a, stream);
+  if (dk == 64 && dv == 128) return launch_partition_g<T, 64, 128>(a, stream);
   return hipErrorInvalidValue;
 }
 
@@ -954,7 +964,7 @@ static hipError_t launch_reduce_t(const DecodeArgs &a, hipStream_t stream) {
 hipError_t launch_decode_reduce(const DecodeArgs &a, hipStream_t stream) {
   if (a.num_seqs == 0 || a.partition_size <= 0 || a.max_partitions <= 1) return hipSuccess;
   const bool bf = (a.cache.dtype == 1);
-  switch (a.cache.head_dim) {
+  switch (a.cache.head_dim_v) {  // the width of the partials and output rows
     case 64: return bf ? launch_reduce_t<bf16_t, 64>(a, stream) : launch_reduce_t<float, 64>(a, stream);
     case 128: return bf ? launch_reduce_t<bf16_t, 128>(a, stream) : launch_reduce_t<float, 128>(a, stream);
   }

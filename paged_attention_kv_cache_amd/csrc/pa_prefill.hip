@@ -39,6 +39,9 @@
 //    sequence: the XCDs get equal work, and the query tiles of one
 //    (sequence, kv head), which read the same K/V, share that XCD's L2.
 //    Tiles with more keys (later in the chunk) are dispatched first.
+//  * Key and value head dims may differ (section 4.1 of the same page):
+//    the K tile, Q and the score products take the key dim D, the V^T tile
+//    and the output tiles the value dim DV.
 #include "pa_common.h"
 
 namespace pa {
@@ -126,11 +129,12 @@ constexpr int kPrefillThreads = 64 * PA_PREFILL_WAVES;
 #define PA_PREFILL_ORDER 1
 #endif
 
-template <int D>
+template <int D, int DV>
 struct TileRegs {
-  static constexpr int C16 = D / 8;
-  static constexpr int NK = (64 * C16 + kPrefillThreads - 1) / kPrefillThreads;  // K chunks per thread
-  static constexpr int NV = (32 * C16 + kPrefillThreads - 1) / kPrefillThreads;  // V key pairs per thread
+  static constexpr int C16K = D / 8;   // 16-byte chunks of a K row
+  static constexpr int C16V = DV / 8;  // of a V row
+  static constexpr int NK = (64 * C16K + kPrefillThreads - 1) / kPrefillThreads;  // K chunks per thread
+  static constexpr int NV = (32 * C16V + kPrefillThreads - 1) / kPrefillThreads;  // V key pairs per thread
   uint4 k[NK];
   uint4 va[NV], vb[NV];
   bool kok[NK], vaok[NV], vbok[NV];
@@ -140,37 +144,38 @@ struct TileRegs {
 // 64 keys and the block size divides 64, so a thread's key, its block's
 // index inside the tile, its row inside that block and its 16-byte column
 // are the same for every tile; only the block ids change.
-template <int D>
+template <int D, int DV>
 struct TileLanes {
-  static constexpr int C16 = D / 8;
-  int kkey[TileRegs<D>::NK];   // key of K chunk j (or 64: no chunk)
-  int kblk[TileRegs<D>::NK];   // its block's index inside the tile
-  uint32_t koff[TileRegs<D>::NK];  // element offset inside the block
-  int vkey[TileRegs<D>::NV];   // first key of V pair j (or 64)
-  int vblk[TileRegs<D>::NV];
-  uint32_t voff[TileRegs<D>::NV];
+  using R = TileRegs<D, DV>;
+  int kkey[R::NK];   // key of K chunk j (or 64: no chunk)
+  int kblk[R::NK];   // its block's index inside the tile
+  uint32_t koff[R::NK];  // element offset inside the block
+  int vkey[R::NV];   // first key of V pair j (or 64)
+  int vblk[R::NV];
+  uint32_t voff[R::NV];
 };
 
 constexpr int kMaxTileBlocks = 8;  // 64 keys / smallest block size
 
-template <int D>
-__device__ __forceinline__ void tile_lanes(TileLanes<D> &t, int tid, int shift, int bs_mask, uint32_t slot_stride) {
-  constexpr int C16 = D / 8;
+template <int D, int DV>
+__device__ __forceinline__ void tile_lanes(TileLanes<D, DV> &t, int tid, int shift, int bs_mask,
+                                           uint32_t k_slot_stride, uint32_t v_slot_stride) {
+  using R = TileRegs<D, DV>;
 #pragma unroll
-  for (int j = 0; j < TileRegs<D>::NK; ++j) {
+  for (int j = 0; j < R::NK; ++j) {
     const int i = tid + kPrefillThreads * j;
-    const int key = (i < 64 * C16) ? (i / C16) : 64;
+    const int key = (i < 64 * R::C16K) ? (i / R::C16K) : 64;
     t.kkey[j] = key;
     t.kblk[j] = (key & 63) >> shift;
-    t.koff[j] = (uint32_t)(key & bs_mask) * slot_stride + (uint32_t)(i % C16) * 8;
+    t.koff[j] = (uint32_t)(key & bs_mask) * k_slot_stride + (uint32_t)(i % R::C16K) * 8;
   }
 #pragma unroll
-  for (int j = 0; j < TileRegs<D>::NV; ++j) {
+  for (int j = 0; j < R::NV; ++j) {
     const int i = tid + kPrefillThreads * j;
-    const int key = (i < 32 * C16) ? 2 * (i % 32) : 64;
+    const int key = (i < 32 * R::C16V) ? 2 * (i % 32) : 64;
     t.vkey[j] = key;
     t.vblk[j] = (key & 63) >> shift;
-    t.voff[j] = (uint32_t)(key & bs_mask) * slot_stride + (uint32_t)((i / 32) % C16) * 8;
+    t.voff[j] = (uint32_t)(key & bs_mask) * v_slot_stride + (uint32_t)((i / 32) % R::C16V) * 8;
   }
 }
 
@@ -183,25 +188,27 @@ __device__ __forceinline__ int tile_block_id(const int32_t *bt, int k0, int j, i
 // Gather of one K/V tile (keys k0 .. k0+63) into registers.  Loads are
 // unconditional: a key at or past kend, or in an invalid block, reads a row
 // of block 0 instead (inside the pool) and is fixed when stored.
-template <int D>
-__device__ __forceinline__ void tile_load(TileRegs<D> &r, const TileLanes<D> &t, const int *ids,
+template <int D, int DV>
+__device__ __forceinline__ void tile_load(TileRegs<D, DV> &r, const TileLanes<D, DV> &t, const int *ids,
                                           const uint16_t *kbase, const uint16_t *vbase, int k0, int kend,
-                                          int num_blocks, size_t block_stride, uint32_t slot_stride) {
+                                          int num_blocks, size_t k_block_stride, size_t v_block_stride,
+                                          uint32_t v_slot_stride) {
+  using R = TileRegs<D, DV>;
 #pragma unroll
-  for (int j = 0; j < TileRegs<D>::NK; ++j) {
+  for (int j = 0; j < R::NK; ++j) {
     const int blk = ids[t.kblk[j]];
     const bool ok = (t.kkey[j] < 64) && ((unsigned)blk < (unsigned)num_blocks);
-    const size_t base = (size_t)(ok ? blk : 0) * block_stride + t.koff[j];
+    const size_t base = (size_t)(ok ? blk : 0) * k_block_stride + t.koff[j];
     r.k[j] = *reinterpret_cast<const uint4 *>(kbase + base);
     r.kok[j] = ok || t.kkey[j] >= 64;  // K of a masked key needs no fix: its score is replaced
   }
 #pragma unroll
-  for (int j = 0; j < TileRegs<D>::NV; ++j) {
+  for (int j = 0; j < R::NV; ++j) {
     const int blk = ids[t.vblk[j]];  // keys 2p and 2p+1 share a block
     const bool inb = (t.vkey[j] < 64) && ((unsigned)blk < (unsigned)num_blocks);
-    const size_t base = (size_t)(inb ? blk : 0) * block_stride + t.voff[j];
+    const size_t base = (size_t)(inb ? blk : 0) * v_block_stride + t.voff[j];
     r.va[j] = *reinterpret_cast<const uint4 *>(vbase + base);
-    r.vb[j] = *reinterpret_cast<const uint4 *>(vbase + base + slot_stride);
+    r.vb[j] = *reinterpret_cast<const uint4 *>(vbase + base + v_slot_stride);
     r.vaok[j] = inb && (k0 + t.vkey[j] < kend);
     r.vbok[j] = inb && (k0 + t.vkey[j] + 1 < kend);
   }
@@ -213,34 +220,34 @@ __device__ __forceinline__ uint4 keep_if(bool ok, const uint4 &v) {
   return make_uint4(ok ? v.x : 0u, ok ? v.y : 0u, ok ? v.z : 0u, ok ? v.w : 0u);
 }
 
-template <int D, int KSTR, int VSTR>
-__device__ __forceinline__ void tile_store(TileRegs<D> &r, uint16_t *sk, uint16_t *svt, int tid) {
-  constexpr int C16 = D / 8;
+template <int D, int DV, int KSTR, int VSTR>
+__device__ __forceinline__ void tile_store(TileRegs<D, DV> &r, uint16_t *sk, uint16_t *svt, int tid) {
+  using R = TileRegs<D, DV>;
   // zero what must not enter the products (rare: the last tile, or a block
   // id outside the pool); the common full tile skips the selects
   bool all_ok = true;
 #pragma unroll
-  for (int j = 0; j < TileRegs<D>::NK; ++j) all_ok = all_ok && r.kok[j];
+  for (int j = 0; j < R::NK; ++j) all_ok = all_ok && r.kok[j];
 #pragma unroll
-  for (int j = 0; j < TileRegs<D>::NV; ++j) all_ok = all_ok && r.vaok[j] && r.vbok[j];
+  for (int j = 0; j < R::NV; ++j) all_ok = all_ok && r.vaok[j] && r.vbok[j];
   if (!all_ok) {
 #pragma unroll
-    for (int j = 0; j < TileRegs<D>::NK; ++j) r.k[j] = keep_if(r.kok[j], r.k[j]);
+    for (int j = 0; j < R::NK; ++j) r.k[j] = keep_if(r.kok[j], r.k[j]);
 #pragma unroll
-    for (int j = 0; j < TileRegs<D>::NV; ++j) {
+    for (int j = 0; j < R::NV; ++j) {
       r.va[j] = keep_if(r.vaok[j], r.va[j]);
       r.vb[j] = keep_if(r.vbok[j], r.vb[j]);
     }
   }
 #pragma unroll
-  for (int j = 0; j < TileRegs<D>::NK; ++j) {
+  for (int j = 0; j < R::NK; ++j) {
     const int i = tid + kPrefillThreads * j;
-    if (i < 64 * C16) *reinterpret_cast<uint4 *>(sk + (i / C16) * KSTR + (i % C16) * 8) = r.k[j];
+    if (i < 64 * R::C16K) *reinterpret_cast<uint4 *>(sk + (i / R::C16K) * KSTR + (i % R::C16K) * 8) = r.k[j];
   }
 #pragma unroll
-  for (int j = 0; j < TileRegs<D>::NV; ++j) {
+  for (int j = 0; j < R::NV; ++j) {
     const int i = tid + kPrefillThreads * j;
-    if (i < 32 * C16) {
+    if (i < 32 * R::C16V) {
       const int p = i % 32;
       const int c = i / 32;
       uint32_t *dst = reinterpret_cast<uint32_t *>(svt + (c * 8) * VSTR + 2 * p);
@@ -266,7 +273,7 @@ constexpr float kRescaleSlack = 8.f;
 
 constexpr uint32_t kBf16PairOnes = 0x3F803F80u;  // two bf16 1.0
 
-template <int D, int G>
+template <int G>
 struct PrefillShape {
   static constexpr int NW = kPrefillThreads / 64;  // waves per work-group
   static constexpr int HW = (G >= 2) ? PA_PREFILL_HW : 1;  // query heads per wave
@@ -278,10 +285,10 @@ struct PrefillShape {
   static_assert(HP % GWH == 0 && NW % GWH == 0, "heads and waves must divide");
 };
 
-template <int D, int G>
+template <int D, int DV, int G>
 __global__ void __launch_bounds__(kPrefillThreads, (8 / PA_PREFILL_WAVES) / PA_PREFILL_HW)
 prefill_chunk_kernel(const PrefillKernelArgs a) {
-  using Sh = PrefillShape<D, G>;
+  using Sh = PrefillShape<G>;
   constexpr int HW = Sh::HW;
   constexpr int GWH = Sh::GWH;
   constexpr int HALVES = Sh::HALVES;
@@ -290,12 +297,12 @@ prefill_chunk_kernel(const PrefillKernelArgs a) {
   constexpr int KSTR = D + 8;        // LDS row stride of K, bf16 elements
   constexpr int VSTR = KT + PA_PREFILL_VPAD;  // LDS row stride of V^T, bf16 elements
   constexpr int NDS = D / 16;        // k-steps of Q K^T
-  constexpr int NDT = D / 32;        // 32-row tiles of O^T
+  constexpr int NDT = DV / 32;       // 32-row tiles of O^T
 
   // three buffers each for K and V: at step t the waves read K of tile t+1
   // and V of tile t while tile t+2 is stored
   __shared__ __attribute__((aligned(16))) uint16_t sk[3][KT * KSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t svt[3][D * VSTR];
+  __shared__ __attribute__((aligned(16))) uint16_t svt[3][DV * VSTR];
   __shared__ int sid[3][kMaxTileBlocks];
 
   // Work id.  Work-groups are dispatched round-robin over the 8 XCDs; the
@@ -415,16 +422,18 @@ prefill_chunk_kernel(const PrefillKernelArgs a) {
     if (kbeg >= kend) return;  // past every row's shared tokens: a slot no merge reads
   }
 
-  const uint32_t slot_stride = (uint32_t)a.num_kv_heads * D;
+  const uint32_t slot_stride = (uint32_t)a.num_kv_heads * D;  // elements between K slots
+  const uint32_t vslot_stride = (uint32_t)a.num_kv_heads * DV;
   const size_t block_stride = (size_t)slot_stride << a.block_shift;
+  const size_t vblock_stride = (size_t)vslot_stride << a.block_shift;
   const uint16_t *kbase = static_cast<const uint16_t *>(a.k_cache) + (size_t)kvh * D;
-  const uint16_t *vbase = static_cast<const uint16_t *>(a.v_cache) + (size_t)kvh * D;
+  const uint16_t *vbase = static_cast<const uint16_t *>(a.v_cache) + (size_t)kvh * DV;
   const int32_t *bt = a.block_tables + (size_t)tab_row * a.max_blocks_per_seq;
   const int shift = a.block_shift;
   const int bs_mask = (1 << shift) - 1;
   const float sl = a.scale_log2;
-  TileLanes<D> lanes;
-  tile_lanes<D>(lanes, tid, shift, bs_mask, slot_stride);
+  TileLanes<D, DV> lanes;
+  tile_lanes<D, DV>(lanes, tid, shift, bs_mask, slot_stride, vslot_stride);
 
   float m[HW], l[HW];  // reference max (base-2 units) and running sum of this lane's query, per head
   f32x16_t o[HW][NDT];
@@ -469,12 +478,14 @@ prefill_chunk_kernel(const PrefillKernelArgs a) {
     for (int j = 0; j < 3; ++j) sid[j][tid] = tile_block_id(bt, kbeg + j * KT, tid, shift, a.max_blocks_per_seq);
   }
   __syncthreads();
-  TileRegs<D> tr;
+  TileRegs<D, DV> tr;
   const int ntiles = (kend - kbeg + KT - 1) / KT;
-  tile_load<D>(tr, lanes, sid[0], kbase, vbase, kbeg, kend, a.num_blocks, block_stride, slot_stride);
-  tile_store<D, KSTR, VSTR>(tr, sk[0], svt[0], tid);
-  tile_load<D>(tr, lanes, sid[1], kbase, vbase, kbeg + KT, kend, a.num_blocks, block_stride, slot_stride);
-  tile_store<D, KSTR, VSTR>(tr, sk[1], svt[1], tid);
+  tile_load<D, DV>(tr, lanes, sid[0], kbase, vbase, kbeg, kend, a.num_blocks, block_stride, vblock_stride,
+                   vslot_stride);
+  tile_store<D, DV, KSTR, VSTR>(tr, sk[0], svt[0], tid);
+  tile_load<D, DV>(tr, lanes, sid[1], kbase, vbase, kbeg + KT, kend, a.num_blocks, block_stride, vblock_stride,
+                   vslot_stride);
+  tile_store<D, DV, KSTR, VSTR>(tr, sk[1], svt[1], tid);
   __syncthreads();
 
   f32x16_t c0[HW], c1[HW];  // S of the current tile
@@ -491,7 +502,8 @@ prefill_chunk_kernel(const PrefillKernelArgs a) {
     qk(sk[b0], c0, c1);
 #endif
     // tile t+2 from the pool (past the last tile: in-pool rows, zeroed)
-    tile_load<D>(tr, lanes, sid[b2], kbase, vbase, k0 + 2 * KT, kend, a.num_blocks, block_stride, slot_stride);
+    tile_load<D, DV>(tr, lanes, sid[b2], kbase, vbase, k0 + 2 * KT, kend, a.num_blocks, block_stride,
+                     vblock_stride, vslot_stride);
     int next_id = 0;
     if (tid < kMaxTileBlocks) next_id = tile_block_id(bt, k0 + 3 * KT, tid, shift, a.max_blocks_per_seq);
 
@@ -593,7 +605,7 @@ prefill_chunk_kernel(const PrefillKernelArgs a) {
       }
     }
 
-    tile_store<D, KSTR, VSTR>(tr, sk[b2], svt[b2], tid);
+    tile_store<D, DV, KSTR, VSTR>(tr, sk[b2], svt[b2], tid);
     if (tid < kMaxTileBlocks) sid[b0][tid] = next_id;  // ids of tile t+3
     __syncthreads();
 #if PA_PREFILL_LOOKAHEAD
@@ -614,7 +626,7 @@ prefill_chunk_kernel(const PrefillKernelArgs a) {
 #pragma unroll
       for (int h = 0; h < HW; ++h) {
         const size_t idx = ((size_t)(r0 + t) * a.num_heads + head0 + h) * a.ws_parts + kchunk;
-        float *orow = a.ws_o + idx * D;
+        float *orow = a.ws_o + idx * DV;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
@@ -635,7 +647,7 @@ prefill_chunk_kernel(const PrefillKernelArgs a) {
 #pragma unroll
     for (int h = 0; h < HW; ++h) {
       const float lt = lsum[h];
-      uint16_t *orow = static_cast<uint16_t *>(a.out) + ((size_t)(r0 + t) * a.num_heads + head0 + h) * D;
+      uint16_t *orow = static_cast<uint16_t *>(a.out) + ((size_t)(r0 + t) * a.num_heads + head0 + h) * DV;
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
@@ -650,9 +662,9 @@ prefill_chunk_kernel(const PrefillKernelArgs a) {
   }
 }
 
-template <int D, int G>
+template <int D, int DV, int G>
 static hipError_t launch_t(const PrefillArgs &a, hipStream_t stream) {
-  using Sh = PrefillShape<D, G>;
+  using Sh = PrefillShape<G>;
   PrefillKernelArgs k;
   k.out = a.out;
   k.q = a.q;
@@ -687,27 +699,28 @@ static hipError_t launch_t(const PrefillArgs &a, hipStream_t stream) {
   k.ws_o = a.ws_o;
   k.ws_parts = a.ws_parts;
   const unsigned grid = (unsigned)((n_work + 7) / 8 * 8);
-  hipLaunchKernelGGL((prefill_chunk_kernel<D, G>), dim3(grid), dim3(kPrefillThreads), 0, stream, k);
+  hipLaunchKernelGGL((prefill_chunk_kernel<D, DV, G>), dim3(grid), dim3(kPrefillThreads), 0, stream, k);
   return hipGetLastError();
 }
 
-template <int D>
+template <int D, int DV>
 static hipError_t launch_g(const PrefillArgs &a, hipStream_t stream) {
   switch (a.num_heads / a.cache.num_kv_heads) {
-    case 1: return launch_t<D, 1>(a, stream);
-    case 2: return launch_t<D, 2>(a, stream);
-    case 4: return launch_t<D, 4>(a, stream);
-    case 8: return launch_t<D, 8>(a, stream);
+    case 1: return launch_t<D, DV, 1>(a, stream);
+    case 2: return launch_t<D, DV, 2>(a, stream);
+    case 4: return launch_t<D, DV, 4>(a, stream);
+    case 8: return launch_t<D, DV, 8>(a, stream);
   }
   return hipErrorNotSupported;
 }
 
 hipError_t launch_prefill_chunk(const PrefillArgs &a, hipStream_t stream) {
   if (a.cache.dtype != 1) return hipErrorNotSupported;
-  switch (a.cache.head_dim) {
-    case 64: return launch_g<64>(a, stream);
-    case 128: return launch_g<128>(a, stream);
-  }
+  const int dk = a.cache.head_dim, dv = a.cache.head_dim_v;
+  if (dk == 64 && dv == 64) return launch_g<64, 64>(a, stream);
+  if (dk == 128 && dv == 128) return launch_g<128, 128>(a, stream);
+  if (dk == 128 && dv == 64) return launch_g<128, 64>(a, stream);
+  if (dk == 64 && dv == 128) return launch_g<64, 128>(a, stream);
   return hipErrorNotSupported;
 }
 

@@ -22,6 +22,7 @@ What pins what:
 * ``pin_fp32_close_to_fp64``        - the float32 mode stays within 1e-5 of float64
 * ``pin_decode_is_prefill_of_one``  - a chunk of one token is the decode step
 * ``pin_empty_context``             - a context of 0 tokens gives zeros
+* ``pin_separate_value_dim``        - value head dim != key head dim: SDPA with a narrower/wider V (write, decode, prefill)
 """
 
 from __future__ import annotations
@@ -61,8 +62,9 @@ def _sequences_into_pool(denses_k, denses_v, block_size, rng, extra=3):
     nblks = [-(-d.shape[0] // block_size) for d in denses_k]
     total = sum(nblks) + extra
     H, D = denses_k[0].shape[1:]
+    Dv = denses_v[0].shape[2]
     kpool = np.full((total, block_size, H, D), np.nan)
-    vpool = np.full((total, block_size, H, D), np.nan)
+    vpool = np.full((total, block_size, H, Dv), np.nan)
     perm = rng.permutation(total)
     tables = np.full((len(denses_k), max(nblks)), perm[-1], dtype=np.int32)
     c = 0
@@ -70,10 +72,11 @@ def _sequences_into_pool(denses_k, denses_v, block_size, rng, extra=3):
         n = dk.shape[0]
         ids = perm[c:c + nblks[i]]
         c += nblks[i]
-        for name, dense, pool in (("k", dk, kpool), ("v", dv, vpool)):
-            padded = np.full((nblks[i] * block_size, H, D), np.nan)
+        for dense, pool in ((dk, kpool), (dv, vpool)):
+            width = dense.shape[2]
+            padded = np.full((nblks[i] * block_size, H, width), np.nan)
             padded[:n] = dense
-            pool[ids] = padded.reshape(nblks[i], block_size, H, D)
+            pool[ids] = padded.reshape(nblks[i], block_size, H, width)
         tables[i, :nblks[i]] = ids
     return kpool, vpool, tables
 
@@ -84,8 +87,9 @@ def _torch():
 
 
 def _sdpa(q, k, v, scale, causal):
-    """torch SDPA on the CPU in float64; q [Tq, Hq, D], k/v [n, Hkv, D];
-    GQA by repeating each kv head over its group of query heads."""
+    """torch SDPA on the CPU in float64; q [Tq, Hq, D], k [n, Hkv, D],
+    v [n, Hkv, Dv]; GQA by repeating each kv head over its group of query
+    heads."""
     torch = _torch()
     Hq, Hkv = q.shape[1], k.shape[1]
     tq = torch.from_numpy(np.ascontiguousarray(q, dtype=np.float64)).permute(1, 0, 2)[None]
@@ -440,6 +444,42 @@ def pin_empty_context(orc):
     assert np.array_equal(out[0], np.zeros((Hq, D)))
     alone = orc.paged_decode(q[1:], kpool, vpool, tables[1:], np.array(lens[1:]), 0.3)
     assert np.array_equal(out[1], alone[0])
+
+
+def pin_separate_value_dim(orc):
+    """Key and value head dims differ (TensorSharp, section 4.1: separate
+    key and value lengths): the write stores each row at its own width and
+    decode / prefill agree with SDPA, which takes a V of any width."""
+    rng = np.random.default_rng(23)
+    Hq, Hkv = 4, 2
+    for D, Dv in ((8, 3), (4, 12)):
+        # write: rows of both widths land in their slots, nothing else moves
+        kpool = np.full((5, 2, Hkv, D), np.nan)
+        vpool = np.full((5, 2, Hkv, Dv), np.nan)
+        key = rng.standard_normal((3, Hkv, D))
+        val = rng.standard_normal((3, Hkv, Dv))
+        k2, v2 = orc.kv_cache_write(kpool, vpool, key, val, np.array([7, -1, 2]))
+        assert np.array_equal(k2[3, 1], key[0]) and np.array_equal(v2[3, 1], val[0])
+        assert np.array_equal(k2[1, 0], key[2]) and np.array_equal(v2[1, 0], val[2])
+        assert np.isnan(k2).sum() == k2.size - 2 * Hkv * D and np.isnan(v2).sum() == v2.size - 2 * Hkv * Dv
+        # decode and prefill against SDPA
+        lens = [1, 6, 19]
+        ks = [rng.standard_normal((n, Hkv, D)) for n in lens]
+        vs = [rng.standard_normal((n, Hkv, Dv)) for n in lens]
+        kpool, vpool, tables = _sequences_into_pool(ks, vs, 4, rng)
+        q = rng.standard_normal((len(lens), Hq, D))
+        out = orc.paged_decode(q, kpool, vpool, tables, np.array(lens), 0.4)
+        assert out.shape == (len(lens), Hq, Dv)
+        for i in range(len(lens)):
+            ref = _sdpa(q[i:i + 1], ks[i], vs[i], 0.4, causal=False)
+            assert np.allclose(out[i:i + 1], ref, rtol=0, atol=1e-12), f"decode seq {i}"
+        qs = [rng.standard_normal((n, Hq, D)) for n in lens]
+        qsl = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+        out = orc.paged_prefill(np.concatenate(qs), qsl, kpool, vpool, tables, np.array(lens), 0.4)
+        assert out.shape == (sum(lens), Hq, Dv)
+        for i in range(len(lens)):
+            ref = _sdpa(qs[i], ks[i], vs[i], 0.4, causal=True)
+            assert np.allclose(out[qsl[i]:qsl[i + 1]], ref, rtol=0, atol=1e-12), f"prefill seq {i}"
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

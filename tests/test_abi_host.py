@@ -57,7 +57,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert P.pa_version() == 10000
+    assert P.pa_version() == 10100
     for code, name in _binding.STATUS.items():
         assert P.pa_status_string(code) == name
     assert P.pa_status_string(-99) == "PA_UNKNOWN_STATUS"
@@ -66,8 +66,8 @@ def test_version_and_status_strings(lib):
 FAKE = 0x1000  # never dereferenced: every call below fails validation first
 
 
-def cache(nb=10, bs=32, hkv=8, d=128, dtype=1, k=FAKE, v=FAKE):
-    return _binding.PaKvCache(k, v, nb, bs, hkv, d, dtype)
+def cache(nb=10, bs=32, hkv=8, d=128, dtype=1, k=FAKE, v=FAKE, dv=0):
+    return _binding.PaKvCache(k, v, nb, bs, hkv, d, dtype, dv)
 
 
 def decode(lib, c, S=4, H=32, mbps=8, mcl=100, scale=0.1, ps=0, ws=None, ws_bytes=0, out=FAKE, q=FAKE,
@@ -237,6 +237,39 @@ def test_copy_blocks_validation(lib):
     assert cp(a, b, n=11) == -3 and "identity copy of 11 blocks" in msg()
     assert cp(b, a, n=11) == -3
     assert cp(a, cache(k=0)) == -1
+
+
+def test_value_head_dim_validation(lib):
+    """A value head dim of its own (0 = the key head dim): attention takes
+    64 or 128, the workspace is sized by it, the copy checks it, and
+    cascade decode needs it equal to the key head dim."""
+    assert ctypes.sizeof(_binding.PaKvCache) == 2 * 8 + 6 * 4
+    for dv in (32, 96, 256):
+        assert decode(lib, cache(dv=dv)) == -5
+        assert f"v_head_dim {dv} not in {{64, 128}}" in msg()
+    assert decode(lib, cache(dv=-1)) == -5 and "v_head_dim -1" in msg()
+    need = P.pa_decode_workspace_bytes(4, 32, 64, 1000, 256)
+    assert need < P.pa_decode_workspace_bytes(4, 32, 128, 1000, 256)
+    assert decode(lib, cache(dv=64), mcl=1000, ps=256) == -7 and f"{need} bytes needed" in msg()
+    assert decode(lib, cache(d=64, dv=128), mcl=1000, ps=256, ws=FAKE, ws_bytes=need) == -7
+    # write: each row width must be a multiple of 16 bytes
+    odd_v = cache(hkv=1, d=8, dv=6)                                 # 16-byte K rows, 12-byte V rows
+    assert lib.pa_kv_cache_write(ctypes.byref(odd_v), FAKE, FAKE, FAKE, 5, None) == -3
+    assert "v_head_dim" in msg()
+    assert lib.pa_kv_cache_write(ctypes.byref(cache(dv=24)), FAKE, FAKE, FAKE, 0, None) == 0
+    # copy: both pools must agree on the value head dim (0 and the key dim are the same)
+    cp = lambda s, d: lib.pa_kv_cache_copy_blocks(ctypes.byref(s), ctypes.byref(d), None, None, 0, None)
+    assert cp(cache(dv=64), cache(dv=128)) == -3 and "v_head_dim" in msg()
+    assert cp(cache(dv=0), cache(dv=128)) == 0
+    # cascade decode: equal dims only
+    assert lib.pa_decode_cascade(ctypes.byref(cache(dv=64)), FAKE, FAKE, 4, 32, FAKE, 8, FAKE, 1000, 0.1, 256, 2,
+                                 FAKE, FAKE, 2, 512, FAKE, 10 ** 9, None) == -8
+    assert "v_head_dim" in msg()
+    # prefill takes unequal dims
+    assert lib.pa_prefill_chunk(ctypes.byref(cache(dv=64)), FAKE, FAKE, FAKE, 2, 32, 0, 32, FAKE, 8, FAKE, 100,
+                                0.1, None) == 0
+    assert lib.pa_prefill_chunk(ctypes.byref(cache(dv=96)), FAKE, FAKE, FAKE, 2, 32, 0, 32, FAKE, 8, FAKE, 100,
+                                0.1, None) == -5
 
 
 def test_cascade_validation(lib):

@@ -50,6 +50,24 @@ def test_decode_shapes(dtype, head_dim, group):
             assert_close(got, ref, dtype, f"{dtype} D{head_dim} G{group} bs{bs} ps{ps}")
 
 
+@pytest.mark.parametrize("dtype", [W.BF16, W.F32])
+@pytest.mark.parametrize("dims", [(128, 64), (64, 128)])
+@pytest.mark.parametrize("group", [1, 2, 4, 8])
+def test_decode_separate_value_dim(dtype, dims, group):
+    """Key head dim D, value head dim Dv != D: outputs are [S, H, Dv]."""
+    D, Dv = dims
+    hkv = 2
+    for bs in (8, 16, 32):
+        case = W.random_decode(7000 + 100 * group + bs + D, CTX_MIX, num_heads=hkv * group, num_kv_heads=hkv,
+                               head_dim=D, v_head_dim=Dv, block_size=bs, dtype=dtype, extra_table_cols=2)
+        ref = oracle_decode(case)
+        assert ref.shape == (len(CTX_MIX), hkv * group, Dv)
+        for ps in (0, bs, 256):
+            log(f"decode {dtype} D={D} Dv={Dv} G={group} bs={bs} partition={ps}")
+            _, got = _run(case, ps)
+            assert_close(got, ref, dtype, f"{dtype} D{D} Dv{Dv} G{group} bs{bs} ps{ps}")
+
+
 @pytest.mark.parametrize("ps", [0, 512, BENCH_PARTITION])
 def test_decode_batch_bs32_full(ps):
     case = W.make_config("decode_batch_bs32")

@@ -92,3 +92,28 @@ def test_copy_blocks_grow_and_remap():
         for a, b in zip(src[:3], dst[:3]):
             ek[b], ev[b] = k[a], v[a]
         assert np.array_equal(to_host_bits(dk), ek) and np.array_equal(to_host_bits(dv), ev)
+
+
+@pytest.mark.parametrize("dims", [(128, 64), (64, 128)])
+@pytest.mark.parametrize("dtype", [W.BF16, W.F32])
+def test_write_and_copy_separate_value_dim(dims, dtype):
+    """K and V rows of different widths: the write stores each at its own
+    width, bit-exact, and a grow copy moves both pools whole."""
+    import paged_attention_kv_cache_amd as P
+    t = torch()
+    D, Dv = dims
+    case = W.random_prefill(900 + D, [0, 7, 33, 100], [5, 64, 31, 1], num_heads=8, num_kv_heads=2,
+                            head_dim=D, v_head_dim=Dv, block_size=16, dtype=dtype)
+    assert case.v_cache.shape[3] == Dv and case.new_value.shape[2] == Dv
+    _check_write(case, f"separate value dim D={D} Dv={Dv}")
+    dev = DeviceCase(case)
+    n = case.num_blocks
+    log(f"copy blocks grow with D={D} Dv={Dv} {dtype}")
+    big_k = t.zeros((n + 3,) + tuple(dev.k_cache.shape[1:]), dtype=dev.k_cache.dtype, device="cuda")
+    big_v = t.zeros((n + 3,) + tuple(dev.v_cache.shape[1:]), dtype=dev.v_cache.dtype, device="cuda")
+    P.pa_kv_cache_copy_blocks(dev.k_cache, dev.v_cache, big_k, big_v)
+    t.cuda.synchronize()
+    bits = np.uint16 if dtype == W.BF16 else np.uint32
+    assert np.array_equal(to_host_bits(big_k)[:n].view(bits), case.k_cache.view(bits))
+    assert np.array_equal(to_host_bits(big_v)[:n].view(bits), case.v_cache.view(bits))
+    assert not to_host_bits(big_v)[n:].any()

@@ -68,6 +68,9 @@ MUTANTS = {
     "write_in_place": (
         "k = np.array(k_cache, copy=True)",
         "k = k_cache"),
+    "decode_output_width_from_key": (
+        "out = np.zeros((S, Hq, v_cache.shape[3]), dtype=acc_dtype)",
+        "out = np.zeros((S, Hq, D), dtype=acc_dtype)"),
     "no_guard_for_rows_without_keys": (
         "if not visible[t].any():",
         "if False:"),

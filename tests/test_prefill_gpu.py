@@ -47,6 +47,23 @@ def test_prefill_shapes(head_dim, group):
         assert_close(got, ref, W.BF16, f"D{head_dim} G{group} bs{bs}")
 
 
+@pytest.mark.parametrize("dims", [(128, 64), (64, 128)])
+@pytest.mark.parametrize("group", [1, 2, 4, 8])
+def test_prefill_separate_value_dim(dims, group):
+    """Key head dim D, value head dim Dv != D: outputs are [Tq, H, Dv]."""
+    D, Dv = dims
+    hkv = 2
+    for bs in (8, 16, 32):
+        case = W.random_prefill(800 + 10 * group + bs + D, PREFIXES, QLENS, num_heads=hkv * group,
+                                num_kv_heads=hkv, head_dim=D, v_head_dim=Dv, block_size=bs, dtype=W.BF16,
+                                extra_table_cols=2)
+        log(f"prefill D={D} Dv={Dv} G={group} bs={bs}")
+        _, got = _run(case)
+        ref = oracle_prefill(case)
+        assert ref.shape == (sum(QLENS), hkv * group, Dv)
+        assert_close(got, ref, W.BF16, f"D{D} Dv{Dv} G{group} bs{bs}")
+
+
 def test_prefill_empty_and_single_token_chunks():
     case = W.random_prefill(7, [10, 0, 40, 3], [0, 1, 0, 5], num_heads=8, num_kv_heads=2, head_dim=128,
                             block_size=16, dtype=W.BF16)

@@ -129,3 +129,22 @@ def test_serving_trace_kv_depends_only_on_the_token_prefix():
     assert tr.prompts[0][:64] == tr.prompts[2][:64]
     assert not np.array_equal(tr.q(0, 0, 1), tr.q(2, 0, 1))
     assert ka.dtype == np.uint16 and tr.q(1, 5, 3).shape == (3, tr.num_heads, tr.head_dim)
+
+
+def test_separate_value_dim_case():
+    """A value head dim of its own changes only the V side of a case: Q, K,
+    the layout and the slots are those of the equal-dim case of the seed."""
+    a = W.random_decode(41, [5, 40, 17], head_dim=128, block_size=8, dtype=W.BF16)
+    b = W.random_decode(41, [5, 40, 17], head_dim=128, v_head_dim=64, block_size=8, dtype=W.BF16)
+    assert b.v_head_dim == 64 and a.v_head_dim == 128
+    assert b.v_cache.shape == b.k_cache.shape[:3] + (64,) and b.new_value.shape == (3, 2, 64)
+    for f in ("q", "k_cache", "new_key", "slot_mapping", "block_tables", "context_lens"):
+        x, y = getattr(a, f), getattr(b, f)
+        assert np.array_equal(x.view(np.uint8), y.view(np.uint8)), f
+    assert b.scale == a.scale == 1.0 / np.sqrt(128)
+    assert b.kv_bytes_logical() == 62 * 2 * (128 + 64) * 2
+    # the new tokens' V rows are the pool rows at their slots, NaN until written
+    vflat = b.v_cache.reshape(-1, 2, 64)
+    assert np.isnan(W.storage_to_f32(vflat[b.slot_mapping], W.BF16)).all()
+    c = W.random_prefill(42, [3, 0], [4, 9], head_dim=64, v_head_dim=128, block_size=16)
+    assert c.v_cache.shape[3] == 128 and c.q.shape == (13, 8, 64)

@@ -13,7 +13,9 @@ Recipe (shared by every workload):
   bf16 (ties to even) and both sides consume those rounded values;
 * the cache layout is ``[num_blocks, block_size, num_kv_heads, head_dim]``,
   the flat product order of the per-layer paged buffers in the TensorSharp
-  Mistral 3 page, section 11 ("Batched / paged forward");
+  Mistral 3 page, section 11 ("Batched / paged forward"); the V pool's last
+  dim is the value head dim, which a case may draw apart from the key head
+  dim (section 4.1: separate key and value lengths);
 * a slot is ``block_id * block_size + offset`` (same section, the
   slotMapping scatter);
 * in "poison" mode every slot that no sequence references, including the
@@ -131,6 +133,12 @@ class _PagedBase:
         return int(self.k_cache.shape[0])
 
     @property
+    def v_head_dim(self) -> int:
+        """Value head dim (the output width); equals head_dim unless the
+        case was drawn with a value head dim of its own."""
+        return int(self.v_cache.shape[3])
+
+    @property
     def max_context_len(self) -> int:
         return int(self.context_lens.max()) if self.context_lens.size else 0
 
@@ -159,7 +167,8 @@ class _PagedBase:
     def kv_bytes_logical(self) -> int:
         """K+V bytes a kernel must read: every context token, all kv heads."""
         el = 2 if self.dtype == BF16 else 4
-        return int(self.context_lens.astype(np.int64).sum()) * self.num_kv_heads * self.head_dim * el * 2
+        return (int(self.context_lens.astype(np.int64).sum()) * self.num_kv_heads
+                * (self.head_dim + self.v_head_dim) * el)
 
     def unique_blocks(self) -> int:
         used = set()
@@ -253,14 +262,16 @@ def _slots_of(table_row, positions, bs):
 
 def _finish(rng, *, kind, name, dtype, Hq, Hkv, D, bs, ctx, tables, nb, pad, q_rows,
             new_positions, boost_frac=0.0, boost=8.0, poison=True, chunk_rows=256,
-            query_start_loc=None):
+            query_start_loc=None, Dv=None):
     """Draw Q, K, V (in that order), apply the boost mask, split off the new
-    tokens and poison what no sequence may read."""
+    tokens and poison what no sequence may read.  ``Dv`` is the value head
+    dim (default ``D``)."""
+    Dv = D if Dv is None else int(Dv)
     q = _draw_normal(rng, (q_rows, Hq, D), dtype)
     k = _draw_normal(rng, (nb, bs, Hkv, D), dtype, chunk_rows=chunk_rows)
-    v = _draw_normal(rng, (nb, bs, Hkv, D), dtype, chunk_rows=chunk_rows)
+    v = _draw_normal(rng, (nb, bs, Hkv, Dv), dtype, chunk_rows=chunk_rows)
     kflat = k.reshape(nb * bs, Hkv, D)
-    vflat = v.reshape(nb * bs, Hkv, D)
+    vflat = v.reshape(nb * bs, Hkv, Dv)
 
     if boost_frac > 0.0:
         # iid Bernoulli(boost_frac) per (sequence, position, kv head); the
@@ -310,8 +321,9 @@ def _finish(rng, *, kind, name, dtype, Hq, Hkv, D, bs, ctx, tables, nb, pad, q_r
 def random_decode(seed: int, context_lens: Sequence[int], *, num_heads=8, num_kv_heads=2,
                   head_dim=64, block_size=16, dtype=F32, num_blocks=None, pool_factor=1.25,
                   shared_blocks=0, group_of=None, boost_frac=0.0, poison=True,
-                  extra_table_cols=0, name="decode") -> DecodeCase:
-    """One decode token per sequence; ``context_lens`` include that token."""
+                  extra_table_cols=0, name="decode", v_head_dim=None) -> DecodeCase:
+    """One decode token per sequence; ``context_lens`` include that token.
+    ``v_head_dim`` (default ``head_dim``) is the value head dim."""
     rng = np.random.default_rng(seed)
     ctx = [int(n) for n in context_lens]
     tables, nb, pad = _layout(rng, ctx, block_size, num_blocks=num_blocks, pool_factor=pool_factor,
@@ -321,15 +333,16 @@ def random_decode(seed: int, context_lens: Sequence[int], *, num_heads=8, num_kv
     return _finish(rng, kind="decode", name=name, dtype=dtype, Hq=num_heads, Hkv=num_kv_heads,
                    D=head_dim, bs=block_size, ctx=ctx, tables=tables, nb=nb, pad=pad,
                    q_rows=len(ctx), new_positions=new_positions, boost_frac=boost_frac,
-                   poison=poison)
+                   poison=poison, Dv=v_head_dim)
 
 
 def random_prefill(seed: int, prefix_lens: Sequence[int], query_lens: Sequence[int], *,
                    num_heads=8, num_kv_heads=2, head_dim=64, block_size=16, dtype=BF16,
                    num_blocks=None, pool_factor=1.25, poison=True, extra_table_cols=0,
-                   name="prefill") -> PrefillCase:
+                   name="prefill", v_head_dim=None) -> PrefillCase:
     """A packed chunk of ``query_lens[i]`` new tokens per sequence appended
-    after ``prefix_lens[i]`` cached tokens."""
+    after ``prefix_lens[i]`` cached tokens.  ``v_head_dim`` (default
+    ``head_dim``) is the value head dim."""
     rng = np.random.default_rng(seed)
     prefix = [int(n) for n in prefix_lens]
     qlen = [int(n) for n in query_lens]
@@ -342,7 +355,7 @@ def random_prefill(seed: int, prefix_lens: Sequence[int], query_lens: Sequence[i
     return _finish(rng, kind="prefill", name=name, dtype=dtype, Hq=num_heads, Hkv=num_kv_heads,
                    D=head_dim, bs=block_size, ctx=ctx, tables=tables, nb=nb, pad=pad,
                    q_rows=int(qsl[-1]), new_positions=new_positions, poison=poison,
-                   query_start_loc=qsl)
+                   query_start_loc=qsl, Dv=v_head_dim)
 
 
 # --------------------------------------------------------------------------
