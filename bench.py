@@ -200,7 +200,7 @@ def bench_decode(args):
     return res
 
 
-def bench_decode_secondary(name, ps, steps=30, groups=None):
+def bench_decode_secondary(name, ps, steps=30, groups=None, case=None):
     """Decode partition + reduce on another workload: time per launch pair
     (back to back over rotated pools), logical KV GB/s (every context token
     of every sequence) and unique KV GB/s (each shared physical block once)."""
@@ -209,7 +209,8 @@ def bench_decode_secondary(name, ps, steps=30, groups=None):
     import workloads as W
 
     log(f"building {name}")
-    case = W.make_config(name, poison=False)
+    if case is None:
+        case = W.make_config(name, poison=False)
     S, H, D = case.q.shape
     pool_bytes = 2 * case.k_cache.nbytes
     R = max(2, int(math.ceil(2.0e9 / pool_bytes)))
@@ -491,6 +492,7 @@ def main():
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     import paged_attention_kv_cache_amd as P
+    import workloads as W
     P.load_library()
 
     if args.copy_calibration:
@@ -563,6 +565,9 @@ def main():
     if not args.quick:
         line["decode_other_workloads"] = [
             bench_decode_secondary("long_context_decode", 512),
+            # the metric's literal shape: 32 sequences of exactly 4096 tokens
+            bench_decode_secondary("decode_batch_bs32_ctx4096", 1024,
+                                   case=W.decode_batch(2000, poison=False, fixed_ctx=4096)),
             bench_decode_secondary("prefix_shared_decode_bs16", 512, groups=([0, 16, 32, 48, 64], [64 * 16] * 4)),
             bench_decode_secondary("prefix_shared_decode_bs8", 512, groups=([0, 16, 32, 48, 64], [64 * 8] * 4)),
         ]

@@ -425,7 +425,11 @@ __device__ __forceinline__ void chunk_rows(size_t (&off)[U], bool (&ok)[U], cons
   for (int u = 0; u < U; ++u) {
     const int tok0 = cbase + u * R;
     ok[u] = (tok0 < p1) && ((unsigned)blk[u] < (unsigned)num_blocks);
-    off[u] = ok[u] ? (((size_t)blk[u] << shift) + (size_t)(tok0 & bs_mask)) * slot_stride : 0;  // 0: pool start
+    // selects on the inputs, not on the product, keep this branch-free so
+    // that the table reads are not serialised by waits before branches
+    const uint32_t b = ok[u] ? (uint32_t)blk[u] : 0u;
+    const uint32_t t = ok[u] ? (uint32_t)(tok0 & bs_mask) : 0u;
+    off[u] = (((size_t)b << shift) + t) * slot_stride;  // 0: pool start
   }
 }
 
