@@ -311,9 +311,11 @@ int pa_decode_cascade(const pa_kv_cache *cache, void *out, const void *q, int32_
  *   block_tables, max_blocks_per_seq, max_context_len, scale : as for
  *                     pa_decode.
  *
- * This build implements bf16 only, on bf16 MFMA tiles with fp32
- * accumulation.  The softmax weights are rounded to bf16 before they
- * multiply V.  fp32 caches return PA_ERR_UNSUPPORTED.
+ * bf16 runs on bf16 MFMA tiles with fp32 accumulation; the softmax
+ * weights are rounded to bf16 before they multiply V.  fp32 runs every
+ * packed row as a single-pass decode of its own (fp32 arithmetic
+ * throughout, no tiling across rows), at most 65535 query rows
+ * (PA_ERR_UNSUPPORTED above that).
  * --------------------------------------------------------------------- */
 int pa_prefill_chunk(const pa_kv_cache *cache, void *out, const void *q,
                      const int32_t *query_start_loc, int32_t num_seqs, int32_t num_heads,

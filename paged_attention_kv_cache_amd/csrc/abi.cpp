@@ -475,8 +475,6 @@ int pa_prefill_chunk(const pa_kv_cache *cache, void *out, const void *q, const i
   int st = check_cache(cache, true);
   if (st) return st;
   if ((st = check_heads(cache, num_heads))) return st;
-  if (cache->dtype != PA_DTYPE_BF16)
-    return fail(PA_ERR_UNSUPPORTED, "prefill_chunk supports dtype 1 (bf16) only; got %d", cache->dtype);
   if (num_seqs < 0 || num_seqs > kMaxGridYZ)
     return fail(PA_ERR_SHAPE, "num_seqs %d not in [0, %d]", num_seqs, kMaxGridYZ);
   if (num_query_tokens < 0) return fail(PA_ERR_SHAPE, "num_query_tokens %d must be >= 0", num_query_tokens);
@@ -490,6 +488,32 @@ int pa_prefill_chunk(const pa_kv_cache *cache, void *out, const void *q, const i
     return fail(PA_ERR_NULL,
                 "out=%p q=%p query_start_loc=%p block_tables=%p context_lens=%p: all must be device pointers",
                 out, q, (const void *)query_start_loc, (const void *)block_tables, (const void *)context_lens);
+  if (cache->dtype == PA_DTYPE_F32) {
+    // fp32: one single-pass row of the generic decode kernel per packed
+    // query row, over its sequence's keys up to the row's own position
+    if (num_query_tokens > kMaxGridYZ)
+      return fail(PA_ERR_UNSUPPORTED, "fp32 prefill_chunk takes at most %d query rows, got %d", kMaxGridYZ,
+                  num_query_tokens);
+    pa::DecodeArgs d;
+    d.cache = view(cache);
+    d.out = out;
+    d.q = q;
+    d.num_seqs = num_query_tokens;
+    d.num_heads = num_heads;
+    d.block_tables = block_tables;
+    d.max_blocks_per_seq = max_blocks_per_seq;
+    d.context_lens = context_lens;
+    d.max_context_len = max_context_len;
+    d.scale = scale;
+    d.partition_size = 0;
+    d.max_partitions = 1;
+    d.ws_m = d.ws_l = d.ws_o = nullptr;
+    d.query_start_loc = query_start_loc;
+    d.num_prefill_seqs = num_seqs;
+    hipError_t e = pa::launch_decode_partition(d, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "fp32 prefill_chunk launch");
+    return ok();
+  }
   pa::PrefillArgs a;
   a.cache = view(cache);
   a.out = out;

@@ -249,6 +249,12 @@ struct DecodeArgs {
   int num_groups = 0;
   int shared_chunk = 64;   // the shared part's partials: slot c = tokens [c*chunk, (c+1)*chunk)
   int shared_cap = 0;      // shared tokens are clamped to this (shared_chunks * shared_chunk)
+  // prefill rows (query_start_loc non-NULL; generic kernel, single pass):
+  // "sequence" r is packed query row r of a chunked prefill over
+  // num_prefill_seqs sequences; it reads the block table of the sequence
+  // that owns it and sees that sequence's keys up to its own position
+  const int32_t *query_start_loc = nullptr;
+  int num_prefill_seqs = 0;
 };
 
 hipError_t launch_decode_partition(const DecodeArgs &a, hipStream_t stream);

@@ -85,6 +85,10 @@ struct DecodeKernelArgs {
   int num_groups;
   int shared_chunk;      // the shared part's partials: slots 0 .. ceil(shared / shared_chunk) - 1
   int shared_cap;        // shared tokens are clamped to this (the chunks launched)
+  // prefill rows (non-NULL): index r of the generic kernel is packed query
+  // row r of sequences 0 .. num_prefill_seqs-1 (see decode_row)
+  const int32_t *query_start_loc;
+  int num_prefill_seqs;
 };
 
 __device__ __forceinline__ int decode_context(const DecodeKernelArgs &a, int seq) {
@@ -96,6 +100,36 @@ __device__ __forceinline__ int decode_context(const DecodeKernelArgs &a, int seq
 __device__ __forceinline__ int decode_num_partitions(const DecodeKernelArgs &a, int ctx) {
   if (a.partition_size <= 0 || ctx <= 0) return 1;
   return (ctx + a.partition_size - 1) / a.partition_size;
+}
+
+// Row r of the generic kernel: the block-table row it reads and the keys
+// it sees.  Decode: sequence r, its whole context.  Prefill rows: the
+// sequence i that owns packed query row r, and the keys up to that row's
+// own position context_lens[i] - q_len_i + (r - query_start_loc[i]) (the
+// chunk ends its context).  Returns false for a row that no sequence owns
+// (it is left untouched).
+__device__ __forceinline__ bool decode_row(const DecodeKernelArgs &a, int r, int &tab_row, int &ctx) {
+  if (!a.query_start_loc) {
+    tab_row = r;
+    ctx = decode_context(a, r);
+    return true;
+  }
+  const int32_t *qsl = a.query_start_loc;
+  tab_row = 0;
+  ctx = 0;
+  if (a.num_prefill_seqs <= 0 || r < max(qsl[0], 0) || r >= qsl[a.num_prefill_seqs]) return false;
+  int lo = 0, hi = a.num_prefill_seqs - 1;  // the i with qsl[i] <= r < qsl[i+1]
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (qsl[mid] <= r) lo = mid;
+    else hi = mid - 1;
+  }
+  const int q_len = qsl[lo + 1] - qsl[lo];
+  const int full = decode_context(a, lo);
+  const int n = full - q_len + (r - qsl[lo]) + 1;  // at most `full` for an ascending query_start_loc
+  tab_row = lo;
+  ctx = max(0, min(n, full));
+  return true;
 }
 
 // cascade: the shared tokens of a row's group (0 outside cascade), at most
@@ -143,7 +177,8 @@ decode_partition_kernel(const DecodeKernelArgs a) {
   const int row = lane / L;
   const int col = lane % L;
 
-  const int ctx = decode_context(a, seq);
+  int tab_row, ctx;
+  if (!decode_row(a, seq, tab_row, ctx)) return;
   const int nparts = decode_num_partitions(a, ctx);
   if (part >= nparts) return;
   const int ps = a.partition_size > 0 ? a.partition_size : ctx;
@@ -169,7 +204,7 @@ decode_partition_kernel(const DecodeKernelArgs a) {
   const size_t vslot_stride = (size_t)a.num_kv_heads * DV;
   const T *kbase = static_cast<const T *>(a.k_cache) + (size_t)kvh * D + col * E;
   const T *vbase = static_cast<const T *>(a.v_cache) + (size_t)kvh * DV + col * EV;
-  const int32_t *bt = a.block_tables + (size_t)seq * a.max_blocks_per_seq;
+  const int32_t *bt = a.block_tables + (size_t)tab_row * a.max_blocks_per_seq;
   const int bs_mask = (1 << a.block_shift) - 1;
 
   float m_run[G], l_run[G], acc[G][EV];
@@ -910,6 +945,8 @@ static DecodeKernelArgs make_kernel_args(const DecodeArgs &a) {
   k.num_groups = a.num_groups;
   k.shared_chunk = a.shared_chunk;
   k.shared_cap = a.shared_cap;
+  k.query_start_loc = a.query_start_loc;
+  k.num_prefill_seqs = a.num_prefill_seqs;
   return k;
 }
 
@@ -918,6 +955,7 @@ static hipError_t launch_partition_t(const DecodeArgs &a, hipStream_t stream) {
   const DecodeKernelArgs k = make_kernel_args(a);
   dim3 grid(a.max_partitions, a.cache.num_kv_heads, a.num_seqs);
   if constexpr (std::is_same<T, bf16_t>::value && G <= 4 && D == DV) {
+    if (a.query_start_loc) return hipErrorNotSupported;  // prefill rows run on the generic kernel only
 #if PA_DECODE_ORDER == 1 || PA_DECODE_ORDER == 3
     grid = dim3(a.cache.num_kv_heads, a.num_seqs, a.max_partitions);
 #endif

@@ -167,8 +167,9 @@ def test_prefill_validation(lib):
     c = cache()
     args = lambda cc, **kw: (ctypes.byref(cc), kw.get("out", FAKE), FAKE, FAKE, kw.get("S", 2), kw.get("H", 32),
                              kw.get("T", 64), kw.get("mql", 32), FAKE, 8, FAKE, 100, kw.get("scale", 0.1), None)
-    assert lib.pa_prefill_chunk(*args(cache(dtype=0))) == -8
-    assert "bf16" in msg()
+    # fp32 runs a row per query token: at most 65535 rows (checked before any launch)
+    assert lib.pa_prefill_chunk(*args(cache(dtype=0), T=70000)) == -8
+    assert "at most 65535 query rows" in msg()
     assert lib.pa_prefill_chunk(*args(cache(bs=24))) == -4
     assert lib.pa_prefill_chunk(*args(c, H=33)) == -6
     assert lib.pa_prefill_chunk(*args(c, T=-1)) == -3

@@ -160,3 +160,41 @@ def test_prefill_causal_boundary_probe(bs):
         for t in range(q_len):
             exp = np.repeat(v_target if t <= ti else v_big, 4, axis=0)
             assert np.array_equal(got[int(qsl[i]) + t], exp), f"bs{bs} seq {i} (t_i={ti}) row {t}"
+
+
+@pytest.mark.parametrize("dims", [(64, 64), (128, 128), (128, 64), (64, 128)])
+@pytest.mark.parametrize("group", [1, 4, 8])
+def test_prefill_fp32(dims, group):
+    """fp32 chunked prefill: each packed row as a single-pass decode over
+    its own causal prefix, within the fp32 tolerance of the oracle."""
+    D, Dv = dims
+    hkv = 2
+    for bs in (8, 16, 32):
+        case = W.random_prefill(1300 + 10 * group + bs + D + Dv, PREFIXES, QLENS, num_heads=hkv * group,
+                                num_kv_heads=hkv, head_dim=D, v_head_dim=Dv, block_size=bs, dtype=W.F32,
+                                extra_table_cols=2)
+        log(f"fp32 prefill D={D} Dv={Dv} G={group} bs={bs}")
+        _, got = _run(case)
+        ref = oracle_prefill(case)
+        assert_close(got, ref, W.F32, f"fp32 D{D} Dv{Dv} G{group} bs{bs}")
+
+
+def test_prefill_fp32_rows_outside_sequences_untouched():
+    """Rows past the last sequence's chunk keep their contents; an empty
+    chunk writes nothing; the rows of the other sequences match the oracle."""
+    import paged_attention_kv_cache_amd as P
+    t = torch()
+    case = W.random_prefill(77, [10, 0, 40, 3], [0, 1, 0, 5], num_heads=8, num_kv_heads=2, head_dim=64,
+                            block_size=16, dtype=W.F32)
+    dev = DeviceCase(case)
+    dev.write()
+    Tq = int(case.query_start_loc[-1])
+    q = t.cat([dev.q, t.zeros((3,) + tuple(dev.q.shape[1:]), dtype=dev.q.dtype, device="cuda")])
+    out = t.full((Tq + 3,) + tuple(dev.q.shape[1:]), 7.0, dtype=dev.q.dtype, device="cuda")
+    log("fp32 prefill with trailing unowned rows")
+    P.pa_prefill_chunk(q, dev.query_start_loc, dev.k_cache, dev.v_cache, dev.block_tables, dev.context_lens,
+                       case.scale, case.max_query_len, case.max_context_len, out=out)
+    t.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert (got[Tq:] == 7.0).all(), "rows outside every sequence were written"
+    assert_close(got[:Tq], oracle_prefill(case), W.F32, "owned rows")
