@@ -38,7 +38,8 @@
 //  * Work ids are remapped so that each XCD serves whole kv heads of every
 //    sequence: the XCDs get equal work, and the query tiles of one
 //    (sequence, kv head), which read the same K/V, share that XCD's L2.
-//    Tiles with more keys (later in the chunk) are dispatched first.
+//    Within a kv head the (sequence, query tile) items are dispatched
+//    longest first (most keys to read).
 //  * Key and value head dims may differ (section 4.1 of the same page):
 //    the K tile, Q and the score products take the key dim D, the V^T tile
 //    and the output tiles the value dim DV.
@@ -127,6 +128,13 @@ constexpr int kPrefillThreads = 64 * PA_PREFILL_WAVES;
 #endif
 #ifndef PA_PREFILL_ORDER
 #define PA_PREFILL_ORDER 1
+#endif
+// 1: within each (kv head, head part), the (sequence, query tile) items of
+// a batch with at most 64 of them are dispatched longest first (keys to
+// read, largest first), the classic longest-processing-time order; larger
+// batches and cascade launches keep the plain order
+#ifndef PA_PREFILL_LPT
+#define PA_PREFILL_LPT 1
 #endif
 
 template <int D, int DV>
@@ -320,19 +328,62 @@ prefill_chunk_kernel(const PrefillKernelArgs a) {
 #if PA_PREFILL_ORDER == 1
   const int qt_rev = rest % a.n_qtiles;
   rest /= a.n_qtiles;
-  const int seq = rest % a.num_seqs;
+  const int seq0 = rest % a.num_seqs;
   rest /= a.num_seqs;
 #else
-  const int seq = rest % a.num_seqs;
+  const int seq0 = rest % a.num_seqs;
   rest /= a.num_seqs;
   const int qt_rev = rest % a.n_qtiles;
   rest /= a.n_qtiles;
 #endif
   const int half = rest % HALVES;
   const int kvh = rest / HALVES;
-  const int qtile = a.n_qtiles - 1 - qt_rev;
-
+  int qtile = a.n_qtiles - 1 - qt_rev;
   const bool cascade = a.group_start != nullptr;
+#if PA_PREFILL_LPT && PA_PREFILL_ORDER == 1
+  int seq = seq0;
+  if (!cascade && a.num_seqs * a.n_qtiles <= 64) {
+    // item j of this (kv head, head part) takes the j-th largest item: lane
+    // i of wave 0 holds item i = (sequence i / n_qtiles, query tile
+    // i % n_qtiles) and its key-tile count, ranked by (count descending,
+    // index ascending)
+    __shared__ int s_item;
+    if (threadIdx.x < 64) {
+      const int i = threadIdx.x;
+      const int n_items = a.num_seqs * a.n_qtiles;
+      int work = -1;  // past the items: ranked after every item
+      if (i < n_items) {
+        const int sq = i / a.n_qtiles;
+        const int qt = i - sq * a.n_qtiles;
+        const int e1 = min(a.query_start_loc[sq + 1], a.num_query_tokens);
+        const int e0 = max(0, min(a.query_start_loc[sq], e1));
+        const int ql = e1 - e0;
+        const int c = max(0, min(a.context_lens[sq], a.ctx_cap));
+        work = 0;
+        if (qt * QT < ql) {
+          const int tl = min(qt * QT + QT, ql) - 1;
+          const int ke = max(0, min(c, c - ql + tl + 1));
+          work = (ke + KT - 1) / KT + 1;  // key tiles, plus about one tile of fixed cost
+        }
+      }
+      int rank = 0;
+      for (int k = 0; k < 64; ++k) {
+        const int wk = __builtin_amdgcn_readlane(work, k);
+        rank += (wk > work || (wk == work && k < i)) ? 1 : 0;
+      }
+      const int j = seq0 * a.n_qtiles + qt_rev;
+      const unsigned long long hit = __builtin_amdgcn_ballot_w64(i < n_items && rank == j);
+      if (i == 0) s_item = hit ? (int)__builtin_ctzll(hit) : 0;
+    }
+    __syncthreads();
+    const int item = __builtin_amdgcn_readfirstlane(s_item);
+    seq = item / a.n_qtiles;
+    qtile = item - seq * a.n_qtiles;
+  }
+#else
+  const int seq = seq0;
+#endif
+
   const int32_t *rows = cascade ? a.group_start : a.query_start_loc;
   int r1 = min(rows[seq + 1], a.num_query_tokens);
   int r0 = rows[seq];
