@@ -215,6 +215,33 @@ int pa_decode(const pa_kv_cache *cache, void *out, const void *q, int32_t num_se
               int32_t partition_size, void *workspace, size_t workspace_bytes, void *stream);
 
 /* ---------------------------------------------------------------------
+ * pa_decode_append - one whole decode step: writes each sequence's newest
+ * K and V rows into the cache and attends over the context, as
+ * pa_kv_cache_write (with slot = the slot of position context_lens[i] - 1
+ * through the block table) followed by pa_decode.  [TS] section 3 appends
+ * the new token's K/V to the cache and then attends with it; section 11
+ * writes them through the slot mapping.  On bf16 pools with num_heads /
+ * num_kv_heads <= 4 and equal head dims the write happens inside the
+ * partition kernel: the partition that holds the newest token takes its
+ * rows from key / value and stores them into the slot, saving a launch;
+ * other shapes run a separate write first.  Results equal pa_decode's up
+ * to rounding (the newest token's weight is merged last).
+ *
+ *   cache ... workspace_bytes : as pa_decode.
+ *   key, value : device, [num_seqs, num_kv_heads, head_dim] and
+ *                [num_seqs, num_kv_heads, v_head_dim], cache dtype: the
+ *                rows of position context_lens[i] - 1 of sequence i.  A
+ *                sequence with context 0 has no new token (its rows are
+ *                not read).  A slot whose block id is outside the pool is
+ *                not written and its token is left out, as pa_decode
+ *                leaves out a token in an invalid block.
+ * --------------------------------------------------------------------- */
+int pa_decode_append(const pa_kv_cache *cache, void *out, const void *q, const void *key, const void *value,
+                     int32_t num_seqs, int32_t num_heads, const int32_t *block_tables, int32_t max_blocks_per_seq,
+                     const int32_t *context_lens, int32_t max_context_len, float scale, int32_t partition_size,
+                     void *workspace, size_t workspace_bytes, void *stream);
+
+/* ---------------------------------------------------------------------
  * pa_decode_partition - first stage of pa_decode, same arguments.  It
  * writes the final output of every sequence with at most one partition.
  * For every other sequence it writes (m, l, o) per partition into the

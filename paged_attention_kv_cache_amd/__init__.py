@@ -31,6 +31,7 @@ from ._binding import (  # noqa: F401
     load_library,
     make_cache,
     pa_decode,
+    pa_decode_append,
     pa_decode_cascade,
     pa_decode_cascade_workspace_bytes,
     pa_decode_partition,

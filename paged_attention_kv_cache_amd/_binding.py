@@ -95,6 +95,8 @@ SIGNATURES = {
                                         _i32, _f32, _vp]),
     "pa_kv_cache_copy_blocks": (ctypes.c_int, [_PCACHE, _PCACHE, _vp, _vp, _i32, _vp]),
     "pa_decode_cascade_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
+    "pa_decode_append": (ctypes.c_int, [_PCACHE, _vp, _vp, _vp, _vp, _i32, _i32, _vp, _i32, _vp, _i32, _f32, _i32,
+                                        _vp, _sz, _vp]),
     "pa_decode_cascade": (ctypes.c_int, [_PCACHE, _vp, _vp, _i32, _i32, _vp, _i32, _vp, _i32, _f32, _i32, _i32,
                                          _vp, _vp, _i32, _i32, _vp, _sz, _vp]),
     "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -331,6 +333,28 @@ def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, max
         code = lib.pa_decode_reduce(p_out, cache.dtype, S, H, Dv, p_cl, int(max_context_len),
                                     int(partition_size), p_ws, ws_bytes, st)
         _check("pa_decode_reduce", code)
+    return out
+
+
+def pa_decode_append(q, key, value, k_cache, v_cache, block_tables, context_lens, scale: float,
+                     max_context_len: int, partition_size: int = 512, out=None, workspace=None, stream=None):
+    """One decode step: writes ``key [S, Hkv, D]`` / ``value [S, Hkv, Dv]``
+    (the newest token of each sequence, position ``context_lens[i] - 1``)
+    into the cache and attends: ``q [S, H, D]`` -> ``out [S, H, Dv]``."""
+    cache, S, H, Dv, out, (p_out, p_q, p_bt, p_cl) = _decode_args(q, k_cache, v_cache, block_tables,
+                                                                  context_lens, out)
+    if (key.dim() != 3 or value.dim() != 3 or tuple(key.shape) != (S,) + tuple(k_cache.shape[2:])
+            or tuple(value.shape) != (S,) + tuple(v_cache.shape[2:])):
+        raise ValueError(f"key/value {tuple(key.shape)}/{tuple(value.shape)} must be [{S}, {k_cache.shape[2]}, "
+                         f"{k_cache.shape[3]}] / [{S}, {v_cache.shape[2]}, {v_cache.shape[3]}]")
+    lib = load_library()
+    need = int(lib.pa_decode_workspace_bytes(S, H, Dv, int(max_context_len), int(partition_size)))
+    p_ws, ws_bytes = _workspace(workspace, need, q.device)
+    code = lib.pa_decode_append(ctypes.byref(cache), p_out, p_q, _dev(key, "key", k_cache.dtype),
+                                _dev(value, "value", k_cache.dtype), S, H, p_bt, int(block_tables.shape[1]), p_cl,
+                                int(max_context_len), float(scale), int(partition_size), p_ws, ws_bytes,
+                                _stream(stream))
+    _check("pa_decode_append", code)
     return out
 
 

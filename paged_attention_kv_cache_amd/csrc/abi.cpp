@@ -361,6 +361,39 @@ int pa_decode(const pa_kv_cache *cache, void *out, const void *q, int32_t num_se
   return ok();
 }
 
+int pa_decode_append(const pa_kv_cache *cache, void *out, const void *q, const void *key, const void *value,
+                     int32_t num_seqs, int32_t num_heads, const int32_t *block_tables, int32_t max_blocks_per_seq,
+                     const int32_t *context_lens, int32_t max_context_len, float scale, int32_t partition_size,
+                     void *workspace, size_t workspace_bytes, void *stream) {
+  pa::DecodeArgs a;
+  int st = prepare_decode(cache, out, q, num_seqs, num_heads, block_tables, max_blocks_per_seq, context_lens,
+                          max_context_len, scale, partition_size, workspace, workspace_bytes, &a);
+  if (st) return st;
+  const int64_t k_row = (int64_t)cache->num_kv_heads * cache->head_dim * elem_bytes(cache->dtype);
+  const int64_t v_row = (int64_t)cache->num_kv_heads * v_dim(cache) * elem_bytes(cache->dtype);
+  if (k_row % 16 || v_row % 16)
+    return fail(PA_ERR_SHAPE, "K and V rows of %lld and %lld bytes are not multiples of 16", (long long)k_row,
+                (long long)v_row);
+  if (num_seqs == 0) return ok();
+  if (!key || !value)
+    return fail(PA_ERR_NULL, "key=%p value=%p: both must be device pointers", key, value);
+  a.new_k = key;
+  a.new_v = value;
+  hipError_t e;
+  if (!pa::decode_fast_path(a)) {
+    // shapes the fast kernel does not take: the cache write first, then the
+    // plain decode, which reads the new rows from the cache
+    e = pa::launch_kv_cache_append(a, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "decode append write launch");
+    a.new_k = a.new_v = nullptr;
+  }
+  e = pa::launch_decode_partition(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "decode partition launch");
+  e = pa::launch_decode_reduce(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "decode reduce launch");
+  return ok();
+}
+
 // cascade decode: tokens per chunk of the shared part (one work-group and
 // one partial slot each; two 64-key tiles, so that the chunks fill the GPU)
 constexpr int kCascadeChunk = 128;

@@ -99,4 +99,55 @@ hipError_t launch_kv_cache_copy_blocks(const void *src_k, const void *src_v, voi
   return hipGetLastError();
 }
 
+// Cache write of a fused append on the shapes the fast decode kernel does
+// not take: sequence i's new K and V rows go to the slot of its position
+// context_len - 1, found through its block table (the slot mapping a decode
+// step would pass to the scatter above).  One thread per 16-byte chunk, K
+// chunks then V chunks of each sequence.
+__global__ void __launch_bounds__(256)
+kv_cache_append_kernel(uint4 *__restrict__ k_cache, uint4 *__restrict__ v_cache, int num_blocks, int block_shift,
+                       int k_chunks, int v_chunks, const uint4 *__restrict__ key, const uint4 *__restrict__ value,
+                       const int32_t *__restrict__ block_tables, int max_blocks_per_seq,
+                       const int32_t *__restrict__ context_lens, int ctx_cap, int num_seqs) {
+  const int per_seq = k_chunks + v_chunks;
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t seq = gid / per_seq;
+  int chunk = (int)(gid - seq * per_seq);
+  if (seq >= num_seqs) return;
+  int ctx = context_lens[seq];
+  ctx = ctx < ctx_cap ? ctx : ctx_cap;
+  if (ctx <= 0) return;
+  const int pos = ctx - 1;
+  const int blk = block_tables[seq * (int64_t)max_blocks_per_seq + (pos >> block_shift)];
+  if ((unsigned)blk >= (unsigned)num_blocks) return;
+  const int64_t slot = ((int64_t)blk << block_shift) + (pos & ((1 << block_shift) - 1));
+  if (chunk < k_chunks) {
+    k_cache[slot * k_chunks + chunk] = key[seq * k_chunks + chunk];
+  } else {
+    chunk -= k_chunks;
+    v_cache[slot * v_chunks + chunk] = value[seq * v_chunks + chunk];
+  }
+}
+
+hipError_t launch_kv_cache_append(const DecodeArgs &a, hipStream_t stream) {
+  const int eb = a.cache.dtype == 1 ? 2 : 4;
+  const int k_chunks = a.cache.num_kv_heads * a.cache.head_dim * eb / 16;
+  const int v_chunks = a.cache.num_kv_heads * a.cache.head_dim_v * eb / 16;
+  const int64_t total = (int64_t)a.num_seqs * (k_chunks + v_chunks);
+  if (total == 0) return hipSuccess;
+  int shift = 0;
+  while ((1 << shift) < a.cache.block_size) ++shift;
+  const int64_t table_cap = (int64_t)a.max_blocks_per_seq * a.cache.block_size;
+  const int ctx_cap = (int)(table_cap < a.max_context_len ? table_cap : a.max_context_len);
+  const int threads = 256;
+  const int64_t blocks = (total + threads - 1) / threads;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(kv_cache_append_kernel, dim3((unsigned)blocks), dim3(threads), 0, stream,
+                     static_cast<uint4 *>(const_cast<void *>(a.cache.k)),
+                     static_cast<uint4 *>(const_cast<void *>(a.cache.v)), a.cache.num_blocks, shift, k_chunks,
+                     v_chunks, static_cast<const uint4 *>(a.new_k), static_cast<const uint4 *>(a.new_v),
+                     a.block_tables, a.max_blocks_per_seq, a.context_lens, ctx_cap, a.num_seqs);
+  return hipGetLastError();
+}
+
 }  // namespace pa

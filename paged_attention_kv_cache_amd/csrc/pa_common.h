@@ -255,9 +255,23 @@ struct DecodeArgs {
   // that owns it and sees that sequence's keys up to its own position
   const int32_t *query_start_loc = nullptr;
   int num_prefill_seqs = 0;
+  // fused append (new_k non-NULL, bf16 fast kernel only): the newest
+  // token of each sequence (position context_len - 1) has its K and V rows
+  // in new_k / new_v ([S, Hkv, D]) instead of the cache; the partition that
+  // holds it attends to those rows and writes them into the token's slot
+  const void *new_k = nullptr;
+  const void *new_v = nullptr;
 };
 
 hipError_t launch_decode_partition(const DecodeArgs &a, hipStream_t stream);
+// whether launch_decode_partition runs these shapes on the bf16 fast
+// kernel (the one that can take the fused append)
+bool decode_fast_path(const DecodeArgs &a);
+// the cache write of a fused append, for the shapes the fast kernel does
+// not take: each sequence's new rows into the slot of its position
+// context_len - 1 (through its block table); skipped for a context of 0 or
+// a block id outside the pool
+hipError_t launch_kv_cache_append(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_decode_reduce(const DecodeArgs &a, hipStream_t stream);
 
 struct PrefillArgs {

@@ -89,6 +89,9 @@ struct DecodeKernelArgs {
   // row r of sequences 0 .. num_prefill_seqs-1 (see decode_row)
   const int32_t *query_start_loc;
   int num_prefill_seqs;
+  // fused append (non-NULL): newest tokens' K and V rows, [S, Hkv, D]
+  const void *new_k;
+  const void *new_v;
 };
 
 __device__ __forceinline__ int decode_context(const DecodeKernelArgs &a, int seq) {
@@ -647,6 +650,62 @@ struct Bf16Decode {
     l = rows_sum<L>(l);
   }
 
+  // Adds the newest token of sequence `seq` (position pos), whose K and V
+  // rows come from the fused-append input instead of the cache, to a wave's
+  // totals (m, l, acc) as attend returns them, and writes the rows into the
+  // token's cache slot.  Every row of lanes takes the same token, so the
+  // totals stay the same in every row.  The weight is rounded to bf16 before
+  // it multiplies V and the sum takes it unrounded, as in attend.  A token
+  // whose block id is outside the pool is left out and not written, as the
+  // separate cache write and the partition loop would leave it.
+  __device__ static __forceinline__ void attend_new(const DecodeKernelArgs &a, int seq, int kvh, int pos,
+                                                    int lane, float &m, float &l, float (&acc)[G][8]) {
+    const int col = lane % L;
+    const int blk = read_only(a.block_tables + (size_t)seq * a.max_blocks_per_seq)[pos >> a.block_shift];
+    if ((unsigned)blk >= (unsigned)a.num_blocks) return;
+    const size_t in_row = ((size_t)seq * a.num_kv_heads + kvh) * D + (size_t)col * 8;
+    const uint4 kc = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.new_k) + in_row);
+    const uint4 vc = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.new_v) + in_row);
+    const uint4 *qv = reinterpret_cast<const uint4 *>(
+        static_cast<const uint16_t *>(a.q) + ((size_t)seq * a.num_heads + (size_t)kvh * G) * D);
+    float d[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const uint4 qc = qv[h * L + col];
+      float t = dot2_bf16(qc.x, kc.x, 0.f);
+      t = dot2_bf16(qc.y, kc.y, t);
+      t = dot2_bf16(qc.z, kc.z, t);
+      d[h] = dot2_bf16(qc.w, kc.w, t);
+    }
+    const float s = row_scatter_sum<L, G>(d, col) * a.scale_log2;  // head col % G
+    const float m_new = fmaxf(m, s);
+    const float alpha = fast_exp2(m - m_new);  // 0 while m is still -inf
+    const float p = fast_exp2(s - m_new);
+    m = m_new;
+    l = l * alpha + p;
+    float vf[8];
+    Chunk<bf16_t>::widen(vc, vf);
+    float ah[G], pb[G];
+    if constexpr (G >= 1) ah[0] = from_head<G, 0>(alpha), pb[0] = from_head<G, 0>(p);
+    if constexpr (G >= 2) ah[1] = from_head<G, 1>(alpha), pb[1] = from_head<G, 1>(p);
+    if constexpr (G >= 4) {
+      ah[2] = from_head<G, 2>(alpha), pb[2] = from_head<G, 2>(p);
+      ah[3] = from_head<G, 3>(alpha), pb[3] = from_head<G, 3>(p);
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float pr = bf16_lo(pack_bf16x2_rne(pb[h], 0.f));  // the weight rounded to bf16
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(pr, vf[e], acc[h][e] * ah[h]);
+    }
+    if (lane < L) {
+      const size_t slot = ((size_t)blk << a.block_shift) + (size_t)(pos & ((1 << a.block_shift) - 1));
+      const size_t at = slot * a.num_kv_heads * D + (size_t)kvh * D + (size_t)col * 8;
+      *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(const_cast<void *>(a.k_cache)) + at) = kc;
+      *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(const_cast<void *>(a.v_cache)) + at) = vc;
+    }
+  }
+
   // LDS staging of the W waves' (m, l, acc) for the combine
   struct Stage {
     float m[W][G];
@@ -793,8 +852,12 @@ decode_partition_bf16_kernel(const DecodeKernelArgs a) {
   const int p1 = min(ctx, p0 + ps);
   const int slot = cascade ? (sh + a.shared_chunk - 1) / a.shared_chunk + part : part;
 
+  // fused append: the newest token comes from the input rows, in wave 0,
+  // after the cached tokens
+  const bool append = a.new_k != nullptr && !cascade && part == nparts - 1 && ctx > 0;
   float m, l, acc[G][8];
-  K::attend(a, seq, kvh, p0, p1, wave, lane, m, l, acc);
+  K::attend(a, seq, kvh, p0, append ? p1 - 1 : p1, wave, lane, m, l, acc);
+  if (append && wave == 0) K::attend_new(a, seq, kvh, ctx - 1, lane, m, l, acc);
 
   __shared__ typename K::Stage sm;
   K::stage(sm, wave, lane, m, l, acc);
@@ -947,6 +1010,8 @@ static DecodeKernelArgs make_kernel_args(const DecodeArgs &a) {
   k.shared_cap = a.shared_cap;
   k.query_start_loc = a.query_start_loc;
   k.num_prefill_seqs = a.num_prefill_seqs;
+  k.new_k = a.new_k;
+  k.new_v = a.new_v;
   return k;
 }
 
@@ -989,7 +1054,14 @@ static hipError_t launch_partition_d(const DecodeArgs &a, hipStream_t stream) {
   return hipErrorInvalidValue;
 }
 
+bool decode_fast_path(const DecodeArgs &a) {
+  const int g = a.cache.num_kv_heads > 0 ? a.num_heads / a.cache.num_kv_heads : 0;
+  return a.cache.dtype == 1 && g >= 1 && g <= 4 && a.cache.head_dim == a.cache.head_dim_v &&
+         !a.query_start_loc;
+}
+
 hipError_t launch_decode_partition(const DecodeArgs &a, hipStream_t stream) {
+  if (a.new_k && !decode_fast_path(a)) return hipErrorInvalidValue;  // the ABI routes these to the plain write
   if (a.num_seqs == 0) return hipSuccess;
   if (a.cache.dtype == 1) return launch_partition_d<bf16_t>(a, stream);
   return launch_partition_d<float>(a, stream);

@@ -294,3 +294,18 @@ def test_cascade_validation(lib):
     a = lambda x: (x + 255) // 256 * 256
     assert need == 2 * a(4 * n) + a(4 * n * 128)
     assert casc(S=0, ng=0) == 0
+
+
+def test_decode_append_validation(lib):
+    """pa_decode_append checks what pa_decode checks, then the new rows."""
+    def app(c=None, key=FAKE, value=FAKE, S=4, H=32, ps=0, ws=None, ws_bytes=0):
+        c = c or cache()
+        return lib.pa_decode_append(ctypes.byref(c), FAKE, FAKE, key, value, S, H, FAKE, 8, FAKE, 100, 0.1, ps, ws,
+                                    ws_bytes, None)
+    assert app(c=cache(bs=24)) == -4
+    assert app(H=30) == -6
+    assert app(key=None) == -1 and "key=" in msg()
+    assert app(value=None) == -1
+    assert app(ps=48) == -10
+    assert app(c=cache(hkv=1, d=8, dv=6), H=1) == -5          # v_head_dim 6 not an attention shape
+    assert app(S=0, key=None, value=None) == 0                  # nothing to do

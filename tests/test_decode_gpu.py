@@ -7,7 +7,7 @@ import pytest
 
 import oracle
 import workloads as W
-from gpu_util import (DeviceCase, assert_close, log, oracle_decode, to_host_bits, to_host_f32,
+from gpu_util import (DeviceCase, assert_close, log, oracle_decode, to_dev, to_host_bits, to_host_f32,
                       torch)
 
 pytestmark = pytest.mark.gpu
@@ -353,3 +353,66 @@ def test_cascade_index_probe(bs):
         s = int(case.block_tables[i, p // bs]) * bs + p % bs
         v = vnew[i] if p == ctx - 1 else vflat[s]
         assert np.array_equal(got[i], np.repeat(v, 4, axis=0)), f"bs{bs} target {p} shared {shared[i]}"
+
+
+def _append_rows(case):
+    """The newest token's K and V rows of every sequence, [S, Hkv, D] / [S,
+    Hkv, Dv] in storage dtype (zeros for a sequence with no context): the
+    case's new rows are in sequence order, one per sequence with a context."""
+    S = case.num_seqs
+    key = np.zeros((S,) + case.new_key.shape[1:], dtype=case.new_key.dtype)
+    val = np.zeros((S,) + case.new_value.shape[1:], dtype=case.new_value.dtype)
+    j = 0
+    for i, n in enumerate(case.context_lens.tolist()):
+        if n > 0:
+            key[i], val[i] = case.new_key[j], case.new_value[j]
+            j += 1
+    assert j == case.new_key.shape[0]
+    return key, val
+
+
+@pytest.mark.parametrize("dtype,group,dims", [(W.BF16, 1, (128, 128)), (W.BF16, 2, (64, 64)), (W.BF16, 4, (128, 128)),
+                                              (W.BF16, 8, (128, 128)), (W.F32, 4, (64, 64)),
+                                              (W.BF16, 4, (128, 64))])
+def test_decode_append(dtype, group, dims):
+    """pa_decode_append = the cache write of each sequence's newest token
+    plus pa_decode: outputs within tolerance of the oracle and the pools
+    bit-exact with the oracle's write (bf16 with G <= 4 and equal head dims
+    take the fused kernel, the others a separate write)."""
+    import paged_attention_kv_cache_amd as P
+    t = torch()
+    D, Dv = dims
+    hkv = 2
+    for bs in (8, 16, 32):
+        case = W.random_decode(9100 + 10 * group + bs + D + Dv, CTX_MIX + [0], num_heads=hkv * group,
+                               num_kv_heads=hkv, head_dim=D, v_head_dim=Dv, block_size=bs, dtype=dtype,
+                               extra_table_cols=2)
+        ref = oracle_decode(case)
+        k_ref, v_ref = oracle.kv_cache_write(case.k_cache, case.v_cache, case.new_key, case.new_value,
+                                             case.slot_mapping)
+        key, val = _append_rows(case)
+        for ps in (0, bs, 256):
+            log(f"decode append {dtype} G={group} D={D} Dv={Dv} bs={bs} partition={ps}")
+            dev = DeviceCase(case)   # fresh pools: the new tokens' slots still hold NaN
+            out = P.pa_decode_append(dev.q, to_dev(key, dtype), to_dev(val, dtype), dev.k_cache, dev.v_cache,
+                                     dev.block_tables, dev.context_lens, case.scale, case.max_context_len, ps)
+            t.cuda.synchronize()
+            assert_close(to_host_f32(out, dtype), ref, dtype, f"append {dtype} G{group} bs{bs} ps{ps}")
+            bits = np.uint16 if dtype == W.BF16 else np.uint32
+            assert np.array_equal(to_host_bits(dev.k_cache).view(bits), k_ref.view(bits)), "K pool"
+            assert np.array_equal(to_host_bits(dev.v_cache).view(bits), v_ref.view(bits)), "V pool"
+
+
+def test_decode_append_bs32_full():
+    """The bs32 batch through the fused step at the benchmark's partition."""
+    import paged_attention_kv_cache_amd as P
+    case = W.make_config("decode_batch_bs32")
+    ref = oracle_decode(case)
+    key, val = _append_rows(case)
+    dev = DeviceCase(case)
+    log("decode append bs32 batch")
+    out = P.pa_decode_append(dev.q, to_dev(key, W.BF16), to_dev(val, W.BF16), dev.k_cache, dev.v_cache,
+                             dev.block_tables, dev.context_lens, case.scale, case.max_context_len, BENCH_PARTITION)
+    torch().cuda.synchronize()
+    mx, mean = assert_close(to_host_f32(out, W.BF16), ref, W.BF16, "append bs32")
+    print(f"append bs32: max-abs {mx:.2e} mean-abs {mean:.2e}")
