@@ -14,25 +14,27 @@
 //    G = 4).
 //    Every K/V tile is gathered once per work-group and shared by all of
 //    its query heads through LDS.
-//  * K/V tiles of 64 keys are gathered through the block table (one 16-byte
-//    load per lane, whole rows coalesced) into LDS.  K is stored row-major
-//    [key][d]; V is stored transposed [d][key].  Keys past the last
-//    position the work-group needs, and keys in an invalid block, are
-//    zero-filled, so a masked key never brings a NaN into the products.
+//  * K/V tiles of 64 keys are gathered through the block table straight
+//    into LDS with 16-byte global-to-LDS loads (no registers, no LDS store
+//    instructions), both row-major [key][d] in swizzled 64-byte chunk
+//    groups (see TileGather).  Keys past the last position the work-group
+//    needs, and keys in an invalid block, read a zero chunk instead, so a
+//    masked key never brings a NaN into the products.
 //  * Scores are computed transposed, S^T = K Q^T, on
 //    v_mfma_f32_32x32x16_bf16 (A = K from LDS, B = Q^T held in registers).
 //    In the accumulator layout every lane then holds 16 keys of one query,
 //    so the online-softmax max and sum need one cross-half exchange only,
 //    and the rescale factor is a per-lane scalar.
 //  * The weights, rounded to bf16, are already in the B-operand layout of
-//    O^T += V^T P^T (A = V^T from LDS), so P never goes through LDS.
+//    O^T += V^T P^T, so P never goes through LDS; the A operand (V^T) comes
+//    from the row-major V tile through gfx950's transposing LDS reads.
 //  * The causal mask (bottom-right aligned) is applied only on tiles that
 //    cross the diagonal of the wave's 32 queries, by selecting -inf.
 //  * LDS holds three K and three V tiles.  In step t a wave computes the
 //    scores of tile t+1 while it runs the softmax of tile t (independent
 //    work for the matrix and vector units), then multiplies V of tile t;
-//    the global loads of tile t+2 are in flight meanwhile and are stored
-//    before the step's single barrier.
+//    the loads of tile t+2 into LDS are in flight meanwhile and are waited
+//    for before the step's single barrier.
 //  * The output is rescaled only when a query's max grows by more than 2^8
 //    (the final division by the running sum makes any reference max exact).
 //  * Work ids are remapped so that each XCD serves whole kv heads of every
@@ -92,28 +94,12 @@ __device__ __forceinline__ bf16x8_t pack8(const f32x16_t &s, int base) {
   return r;
 }
 
-// Gather of one K/V tile (keys k0 .. k0+63) from the pool into registers.
-// The tile's block ids come from a small LDS array filled ahead of time, so
-// no load waits on a block-table read.  Each lane's loads have fixed
-// (key, column) slots:
-//   K: chunk i = tid + 512 j is key i / C16, 16-byte column i % C16 (whole
-//      rows coalesced);
-//   V: a lane takes keys 2p, 2p+1 (same block) of one column chunk so that
-//      it can write (V[2p][d], V[2p+1][d]) dword pairs of the transposed tile.
-// Loads are unconditional: a key at or past kend, or in an invalid block,
-// reads the first row of the pool instead and is zeroed when stored.
 // waves per work-group (8: one work-group per CU shares each tile among
 // 8 waves; 4: two work-groups per CU, whose phases drift apart)
-#ifndef PA_PREFILL_INTERLEAVE
-#define PA_PREFILL_INTERLEAVE 0
-#endif
 #ifndef PA_PREFILL_WAVES
 #define PA_PREFILL_WAVES 8
 #endif
 constexpr int kPrefillThreads = 64 * PA_PREFILL_WAVES;
-#ifndef PA_PREFILL_VPAD
-#define PA_PREFILL_VPAD 4
-#endif
 // query heads per wave (1 or 2); with 2, each K and V^T fragment read from
 // LDS feeds two MFMAs
 #ifndef PA_PREFILL_HW
@@ -137,55 +123,7 @@ constexpr int kPrefillThreads = 64 * PA_PREFILL_WAVES;
 #define PA_PREFILL_LPT 1
 #endif
 
-template <int D, int DV>
-struct TileRegs {
-  static constexpr int C16K = D / 8;   // 16-byte chunks of a K row
-  static constexpr int C16V = DV / 8;  // of a V row
-  static constexpr int NK = (64 * C16K + kPrefillThreads - 1) / kPrefillThreads;  // K chunks per thread
-  static constexpr int NV = (32 * C16V + kPrefillThreads - 1) / kPrefillThreads;  // V key pairs per thread
-  uint4 k[NK];
-  uint4 va[NV], vb[NV];
-  bool kok[NK], vaok[NV], vbok[NV];
-};
-
-// Per-thread constants of the tile gather.  A tile starts at a multiple of
-// 64 keys and the block size divides 64, so a thread's key, its block's
-// index inside the tile, its row inside that block and its 16-byte column
-// are the same for every tile; only the block ids change.
-template <int D, int DV>
-struct TileLanes {
-  using R = TileRegs<D, DV>;
-  int kkey[R::NK];   // key of K chunk j (or 64: no chunk)
-  int kblk[R::NK];   // its block's index inside the tile
-  uint32_t koff[R::NK];  // element offset inside the block
-  int vkey[R::NV];   // first key of V pair j (or 64)
-  int vblk[R::NV];
-  uint32_t voff[R::NV];
-};
-
 constexpr int kMaxTileBlocks = 8;  // 64 keys / smallest block size
-
-template <int D, int DV>
-__device__ __forceinline__ void tile_lanes(TileLanes<D, DV> &t, int tid, int shift, int bs_mask,
-                                           uint32_t k_slot_stride, uint32_t v_slot_stride) {
-  using R = TileRegs<D, DV>;
-#pragma unroll
-  for (int j = 0; j < R::NK; ++j) {
-    const int i = tid + kPrefillThreads * j;
-    const int key = (i < 64 * R::C16K) ? (i / R::C16K) : 64;
-    t.kkey[j] = key;
-    t.kblk[j] = (key & 63) >> shift;
-    t.koff[j] = (uint32_t)(key & bs_mask) * k_slot_stride + (uint32_t)(i % R::C16K) * 8;
-  }
-#pragma unroll
-  for (int j = 0; j < R::NV; ++j) {
-    const int i = tid + kPrefillThreads * j;
-    const int key = (i < 32 * R::C16V) ? 2 * (i % 32) : 64;
-    t.vkey[j] = key;
-    t.vblk[j] = (key & 63) >> shift;
-    t.voff[j] = (uint32_t)(key & bs_mask) * v_slot_stride + (uint32_t)((i / 32) % R::C16V) * 8;
-  }
-}
 
 // block ids of the tile starting at key k0 (64 / block_size entries); the
 // work-group keeps them in a tiny LDS array, filled ahead of time
@@ -193,86 +131,59 @@ __device__ __forceinline__ int tile_block_id(const int32_t *bt, int k0, int j, i
   return bt[min((k0 >> shift) + j, max_blocks - 1)];
 }
 
-// Gather of one K/V tile (keys k0 .. k0+63) into registers.  Loads are
-// unconditional: a key at or past kend, or in an invalid block, reads a row
-// of block 0 instead (inside the pool) and is fixed when stored.
-template <int D, int DV>
-__device__ __forceinline__ void tile_load(TileRegs<D, DV> &r, const TileLanes<D, DV> &t, const int *ids,
-                                          const uint16_t *kbase, const uint16_t *vbase, int k0, int kend,
-                                          int num_blocks, size_t k_block_stride, size_t v_block_stride,
-                                          uint32_t v_slot_stride) {
-  using R = TileRegs<D, DV>;
-#pragma unroll
-  for (int j = 0; j < R::NK; ++j) {
-    const int blk = ids[t.kblk[j]];
-    const bool ok = (t.kkey[j] < 64) && ((unsigned)blk < (unsigned)num_blocks);
-    const size_t base = (size_t)(ok ? blk : 0) * k_block_stride + t.koff[j];
-    r.k[j] = *reinterpret_cast<const uint4 *>(kbase + base);
-    r.kok[j] = ok || t.kkey[j] >= 64;  // K of a masked key needs no fix: its score is replaced
-  }
-#pragma unroll
-  for (int j = 0; j < R::NV; ++j) {
-    const int blk = ids[t.vblk[j]];  // keys 2p and 2p+1 share a block
-    const bool inb = (t.vkey[j] < 64) && ((unsigned)blk < (unsigned)num_blocks);
-    const size_t base = (size_t)(inb ? blk : 0) * v_block_stride + t.voff[j];
-    r.va[j] = *reinterpret_cast<const uint4 *>(vbase + base);
-    r.vb[j] = *reinterpret_cast<const uint4 *>(vbase + base + v_slot_stride);
-    r.vaok[j] = inb && (k0 + t.vkey[j] < kend);
-    r.vbok[j] = inb && (k0 + t.vkey[j] + 1 < kend);
-  }
-}
+typedef __attribute__((address_space(3))) void *lds_ptr_t;
 
-// component-wise (a ?: 0); a select on the vector objects themselves would
-// pick between their addresses and force both into scratch memory
-__device__ __forceinline__ uint4 keep_if(bool ok, const uint4 &v) {
-  return make_uint4(ok ? v.x : 0u, ok ? v.y : 0u, ok ? v.z : 0u, ok ? v.w : 0u);
-}
+// source of the 16-byte chunks of keys that must read as zero
+__device__ const uint4 kZeroChunk = {0u, 0u, 0u, 0u};
 
-template <int D, int DV, int KSTR, int VSTR>
-__device__ __forceinline__ void tile_store(TileRegs<D, DV> &r, uint16_t *sk, uint16_t *svt, int tid) {
-  using R = TileRegs<D, DV>;
-  // zero what must not enter the products (rare: the last tile, or a block
-  // id outside the pool); the common full tile skips the selects
-  bool all_ok = true;
+// Gather of one K (or V) tile, keys k0 .. k0+63 of row width DIM, straight
+// from the pool into LDS with 16-byte global-to-LDS loads: no registers, no
+// LDS store instructions.  LDS layout: the row's 16-byte chunks in groups of
+// four (64 bytes, 32 elements): group g of every key forms a 4 KB block
+// [key][4 chunks], and inside a key's 64 bytes chunk c sits in slot
+// (c % 4) ^ ((k / 4) % 4).  Sixteen consecutive keys then cover all LDS
+// banks for any fixed chunk, and the slot pattern depends on a lane's key
+// only through (k / 4) % 4, so every fragment read is a per-lane base plus
+// a compile-time offset.  A wave's load writes 1 KB of consecutive LDS
+// (lane i at 16 i): 16 keys x one chunk group, each lane fetching the global
+// chunk that belongs in its slot.  A tile starts at a multiple of 64 keys
+// and the block size divides 64, so a lane's key, its block's index in the
+// tile and its offset inside the block are the same for every tile; only
+// the block ids change.  A key at or past kend, or in a block outside the
+// pool, reads a 16-byte zero chunk instead, so its K and V rows are zero.
+template <int DIM>
+struct TileGather {
+  static constexpr int CG = DIM / 32;                              // chunk groups per row
+  static constexpr int CPR = DIM / 8;                              // 16-byte chunks per row
+  static constexpr int PER_WAVE = (CG * 4) / (kPrefillThreads / 64);  // wave loads per tile
+  static_assert(PER_WAVE >= 1 && (CG * 4) % (kPrefillThreads / 64) == 0, "tile split over the waves");
+  int key[PER_WAVE];        // this lane's key inside the tile, per load
+  uint32_t off[PER_WAVE];   // element offset inside the block (row, head, chunk)
+  uint32_t lds[PER_WAVE];   // byte offset of the wave's load inside the tile (wave-uniform)
+
+  __device__ __forceinline__ void init(int wave, int lane, int shift, int bs_mask, uint32_t slot_stride) {
 #pragma unroll
-  for (int j = 0; j < R::NK; ++j) all_ok = all_ok && r.kok[j];
-#pragma unroll
-  for (int j = 0; j < R::NV; ++j) all_ok = all_ok && r.vaok[j] && r.vbok[j];
-  if (!all_ok) {
-#pragma unroll
-    for (int j = 0; j < R::NK; ++j) r.k[j] = keep_if(r.kok[j], r.k[j]);
-#pragma unroll
-    for (int j = 0; j < R::NV; ++j) {
-      r.va[j] = keep_if(r.vaok[j], r.va[j]);
-      r.vb[j] = keep_if(r.vbok[j], r.vb[j]);
+    for (int j = 0; j < PER_WAVE; ++j) {
+      const int load = wave * PER_WAVE + j;  // chunk group load / 4, key group load % 4
+      const int key = (load % 4) * 16 + lane / 4;
+      const int chunk = (load / 4) * 4 + ((lane % 4) ^ ((key >> 2) & 3));
+      this->key[j] = key;
+      off[j] = (uint32_t)(key & bs_mask) * slot_stride + (uint32_t)chunk * 8;
+      lds[j] = (uint32_t)load * 1024;
     }
   }
+  __device__ __forceinline__ void issue(uint16_t *tile, const int *ids, const uint16_t *base, int num_blocks,
+                                        size_t block_stride, int k0, int kend, int shift) const {
 #pragma unroll
-  for (int j = 0; j < R::NK; ++j) {
-    const int i = tid + kPrefillThreads * j;
-    if (i < 64 * R::C16K) *reinterpret_cast<uint4 *>(sk + (i / R::C16K) * KSTR + (i % R::C16K) * 8) = r.k[j];
-  }
-#pragma unroll
-  for (int j = 0; j < R::NV; ++j) {
-    const int i = tid + kPrefillThreads * j;
-    if (i < 32 * R::C16V) {
-      const int p = i % 32;
-      const int c = i / 32;
-      uint32_t *dst = reinterpret_cast<uint32_t *>(svt + (c * 8) * VSTR + 2 * p);
-      constexpr int W = VSTR / 2;  // dwords per V^T row
-      const uint4 a = r.va[j];
-      const uint4 b = r.vb[j];
-      dst[0 * W] = interleave_lo(a.x, b.x);
-      dst[1 * W] = interleave_hi(a.x, b.x);
-      dst[2 * W] = interleave_lo(a.y, b.y);
-      dst[3 * W] = interleave_hi(a.y, b.y);
-      dst[4 * W] = interleave_lo(a.z, b.z);
-      dst[5 * W] = interleave_hi(a.z, b.z);
-      dst[6 * W] = interleave_lo(a.w, b.w);
-      dst[7 * W] = interleave_hi(a.w, b.w);
+    for (int j = 0; j < PER_WAVE; ++j) {
+      const int b = ids[key[j] >> shift];
+      const bool ok = (unsigned)b < (unsigned)num_blocks && k0 + key[j] < kend;
+      const void *src = ok ? static_cast<const void *>(base + (size_t)b * block_stride + off[j])
+                           : static_cast<const void *>(&kZeroChunk);
+      __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)(reinterpret_cast<char *>(tile) + lds[j]), 16, 0, 0);
     }
   }
-}
+};
 
 // a rescale of O is done only when a query's running max grows by more than
 // this many base-2 units; until then the weights may exceed 1 by up to 2^8,
@@ -302,15 +213,15 @@ prefill_chunk_kernel(const PrefillKernelArgs a) {
   constexpr int HALVES = Sh::HALVES;
   constexpr int QT = Sh::QT;
   constexpr int KT = 64;             // keys per tile
-  constexpr int KSTR = D + 8;        // LDS row stride of K, bf16 elements
-  constexpr int VSTR = KT + PA_PREFILL_VPAD;  // LDS row stride of V^T, bf16 elements
+  using GK = TileGather<D>;
+  using GV = TileGather<DV>;
   constexpr int NDS = D / 16;        // k-steps of Q K^T
   constexpr int NDT = DV / 32;       // 32-row tiles of O^T
 
   // three buffers each for K and V: at step t the waves read K of tile t+1
-  // and V of tile t while tile t+2 is stored
-  __shared__ __attribute__((aligned(16))) uint16_t sk[3][KT * KSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t svt[3][DV * VSTR];
+  // and V of tile t while tile t+2 is loaded
+  __shared__ __attribute__((aligned(1024))) uint16_t sk[3][KT * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t sv[3][KT * DV];
   __shared__ int sid[3][kMaxTileBlocks];
 
   // Work id.  Work-groups are dispatched round-robin over the 8 XCDs; the
@@ -483,8 +394,18 @@ prefill_chunk_kernel(const PrefillKernelArgs a) {
   const int shift = a.block_shift;
   const int bs_mask = (1 << shift) - 1;
   const float sl = a.scale_log2;
-  TileLanes<D, DV> lanes;
-  tile_lanes<D, DV>(lanes, tid, shift, bs_mask, slot_stride, vslot_stride);
+  GK gk;
+  GV gv;
+  gk.init(wave, lane, shift, bs_mask, slot_stride);
+  gv.init(wave, lane, shift, bs_mask, vslot_stride);
+  // per-lane parts of the fragment addresses (see TileGather)
+  const int k_even = ((hh ^ ((col >> 2) & 3)) << 4);
+  const int k_odd = (((2 + hh) ^ ((col >> 2) & 3)) << 4);
+  const int vg = lane >> 4, vs = lane & 15;
+  const int v_lane = (4 * (vg >> 1) + (vs >> 2)) * 64 + (vs & 1) * 8;
+  const int v_slot = 2 * (vg & 1) + ((vs >> 1) & 1);
+  const int v_off0 = v_lane + ((v_slot ^ ((vg >> 1) & 3)) << 4);        // keys of the first read
+  const int v_off1 = v_lane + 8 * 64 + ((v_slot ^ (((vg >> 1) + 2) & 3)) << 4);  // 8 keys further
 
   float m[HW], l[HW];  // reference max (base-2 units) and running sum of this lane's query, per head
   f32x16_t o[HW][NDT];
@@ -508,10 +429,18 @@ prefill_chunk_kernel(const PrefillKernelArgs a) {
         s0[h][r] = 0.f;
         s1[h][r] = 0.f;
       }
+    // chunk 2 ds + hh of keys col and 32 + col: group ds / 2, slot
+    // (2 (ds % 2) + hh) ^ ((col / 4) % 4)
+    typedef __attribute__((address_space(3))) const char *lds_cptr;
+    typedef __attribute__((address_space(3))) const bf16x8_t *lds_frag_ptr;
+    uint32_t ke = (uint32_t)(size_t)((lds_cptr)(const char *)skb + col * 64 + k_even);
+    uint32_t ko = (uint32_t)(size_t)((lds_cptr)(const char *)skb + col * 64 + k_odd);
+    asm volatile("" : "+v"(ke), "+v"(ko));
 #pragma unroll
     for (int ds = 0; ds < NDS; ++ds) {
-      const bf16x8_t a0 = *reinterpret_cast<const bf16x8_t *>(skb + col * KSTR + ds * 16 + hh * 8);
-      const bf16x8_t a1 = *reinterpret_cast<const bf16x8_t *>(skb + (32 + col) * KSTR + ds * 16 + hh * 8);
+      const uint32_t p = ((ds & 1) ? ko : ke) + (ds / 2) * 4096;
+      const bf16x8_t a0 = *(lds_frag_ptr)(size_t)(p);
+      const bf16x8_t a1 = *(lds_frag_ptr)(size_t)(p + 2048);
 #pragma unroll
       for (int h = 0; h < HW; ++h) {
         s0[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qb[h][ds], s0[h], 0, 0, 0);
@@ -521,22 +450,20 @@ prefill_chunk_kernel(const PrefillKernelArgs a) {
   };
 
   // Pipeline, one barrier per step t:
-  //   loads of tile t+2 -> registers;  S(t+1) = K(t+1) Q^T;  softmax of S(t);
-  //   O += V(t) P(t);  registers -> LDS buffers of tile t+2.
+  //   global-to-LDS loads of tile t+2 issued;  S(t+1) = K(t+1) Q^T;
+  //   softmax of S(t);  O += V(t) P(t);  wait for this wave's loads.
   // Block ids: sid[j % 3] holds the ids of tile j, filled three tiles ahead.
   if (tid < kMaxTileBlocks) {
 #pragma unroll
     for (int j = 0; j < 3; ++j) sid[j][tid] = tile_block_id(bt, kbeg + j * KT, tid, shift, a.max_blocks_per_seq);
   }
   __syncthreads();
-  TileRegs<D, DV> tr;
   const int ntiles = (kend - kbeg + KT - 1) / KT;
-  tile_load<D, DV>(tr, lanes, sid[0], kbase, vbase, kbeg, kend, a.num_blocks, block_stride, vblock_stride,
-                   vslot_stride);
-  tile_store<D, DV, KSTR, VSTR>(tr, sk[0], svt[0], tid);
-  tile_load<D, DV>(tr, lanes, sid[1], kbase, vbase, kbeg + KT, kend, a.num_blocks, block_stride, vblock_stride,
-                   vslot_stride);
-  tile_store<D, DV, KSTR, VSTR>(tr, sk[1], svt[1], tid);
+  gk.issue(sk[0], sid[0], kbase, a.num_blocks, block_stride, kbeg, kend, shift);
+  gv.issue(sv[0], sid[0], vbase, a.num_blocks, vblock_stride, kbeg, kend, shift);
+  gk.issue(sk[1], sid[1], kbase, a.num_blocks, block_stride, kbeg + KT, kend, shift);
+  gv.issue(sv[1], sid[1], vbase, a.num_blocks, vblock_stride, kbeg + KT, kend, shift);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   f32x16_t c0[HW], c1[HW];  // S of the current tile
@@ -553,8 +480,9 @@ prefill_chunk_kernel(const PrefillKernelArgs a) {
     qk(sk[b0], c0, c1);
 #endif
     // tile t+2 from the pool (past the last tile: in-pool rows, zeroed)
-    tile_load<D, DV>(tr, lanes, sid[b2], kbase, vbase, k0 + 2 * KT, kend, a.num_blocks, block_stride,
-                     vblock_stride, vslot_stride);
+    // tile t+2 from the pool (past the last tile: zero rows, never used)
+    gk.issue(sk[b2], sid[b2], kbase, a.num_blocks, block_stride, k0 + 2 * KT, kend, shift);
+    gv.issue(sv[b2], sid[b2], vbase, a.num_blocks, vblock_stride, k0 + 2 * KT, kend, shift);
     int next_id = 0;
     if (tid < kMaxTileBlocks) next_id = tile_block_id(bt, k0 + 3 * KT, tid, shift, a.max_blocks_per_seq);
 
@@ -641,23 +569,41 @@ prefill_chunk_kernel(const PrefillKernelArgs a) {
 
     // O^T += V^T P^T; the A operand takes the same keys from row d of V^T,
     // and each V^T fragment read from LDS feeds HW products
-    const uint16_t *svb = svt[b0];
+    // A operand (V^T) by transposed LDS reads of the row-major V tile: in
+    // each 16-lane group, source lane s reads 4 d-values of one key (key
+    // K0 + s/4, d = D0 + 4 (s%4)) and lane o receives d = D0 + o of keys
+    // K0 .. K0+3; two reads give the 8 keys of the B operand's k-step
+    // source lane s of a 16-lane group reads key K0 + s/4, d = D0 + 4 (s%4):
+    // group dt, key (ks / 2) 32 + (ks % 2) 16 + 4 (g / 2) + s / 4 (+8), slot
+    // (2 (g % 2) + (s / 2) % 2) ^ ((key / 4) % 4), half s % 2
+    // (address arithmetic in the LDS address space, constants last, so that
+    // they fold into the instructions' offset fields)
+    typedef __attribute__((address_space(3))) const char *lds_cptr;
+    typedef short v4s __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) v4s *lds_v4s_ptr;
+    // the two per-lane bases pass through an empty asm statement: opaque
+    // vector values, so that base + constant selects the instructions'
+    // offset field instead of a separate address per read
+    uint32_t va0 = (uint32_t)(size_t)((lds_cptr)(const char *)sv[b0] + v_off0);
+    uint32_t va1 = (uint32_t)(size_t)((lds_cptr)(const char *)sv[b0] + v_off1);
+    asm volatile("" : "+v"(va0), "+v"(va1));
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
-      const uint16_t *vrow = svb + (dt * 32 + col) * VSTR;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const int kb0 = (ks >> 1) * 32 + (ks & 1) * 16 + 4 * hh;
-        const uint2 lo = *reinterpret_cast<const uint2 *>(vrow + kb0);
-        const uint2 hi = *reinterpret_cast<const uint2 *>(vrow + kb0 + 8);
-        const bf16x8_t av = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+        const uint32_t c = dt * 4096 + ((ks >> 1) * 32 + (ks & 1) * 16) * 64;
+        const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(size_t)(va0 + c));
+        const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(size_t)(va1 + c));
+        const uint2 l2 = __builtin_bit_cast(uint2, lo);
+        const uint2 h2 = __builtin_bit_cast(uint2, hi);
+        const bf16x8_t av = as_bf16x8(make_uint4(l2.x, l2.y, h2.x, h2.y));
 #pragma unroll
         for (int h = 0; h < HW; ++h) o[h][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[h][ks], o[h][dt], 0, 0, 0);
       }
     }
 
-    tile_store<D, DV, KSTR, VSTR>(tr, sk[b2], svt[b2], tid);
     if (tid < kMaxTileBlocks) sid[b0][tid] = next_id;  // ids of tile t+3
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of tile t+2 are in LDS
     __syncthreads();
 #if PA_PREFILL_LOOKAHEAD
 #pragma unroll
