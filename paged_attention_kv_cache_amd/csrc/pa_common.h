@@ -115,9 +115,17 @@ enum : int {
   kDppRowMirror = 0x140,
 };
 
+// Every control above reads a lane of the same row, so every lane gets a
+// source value: no "old" value is needed (none is materialised), and the
+// bound control (zero for a lane without a source) never applies; it lets
+// the compiler fold the move into the instruction that uses it.
+template <int kCtrl>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, kCtrl, 0xF, 0xF, true);
+}
 template <int kCtrl>
 __device__ __forceinline__ float dpp_f32(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl, 0xF, 0xF, false));
+  return __uint_as_float(dpp_u32<kCtrl>(__float_as_uint(x)));
 }
 
 // Sum over aligned groups of kLanes consecutive lanes (kLanes in
@@ -178,8 +186,12 @@ __device__ __forceinline__ float swizzle_xor4(float x) {
 }
 // every lane of a quad reads quad lane H
 template <int H>
+__device__ __forceinline__ uint32_t quad_bcast(uint32_t x) {
+  return dpp_u32<H * 0x55>(x);
+}
+template <int H>
 __device__ __forceinline__ float quad_bcast(float x) {
-  return dpp_f32<H * 0x55>(x);
+  return __uint_as_float(quad_bcast<H>(__float_as_uint(x)));
 }
 
 // bf16 pair helpers: fp32 dot product of two bf16 pairs plus an fp32

@@ -345,23 +345,31 @@ decode_partition_kernel(const DecodeKernelArgs a) {
 }
 
 // ------------------------------------------------------------------------
-// bf16 fast path (G in {1, 2, 4}).  Same decomposition and numerics as the
-// generic kernel above, with the per-token work cut down for the VALU:
+// bf16 fast path (G in {1, 2, 4, 8}, equal key and value head dims).  Same
+// decomposition as the generic kernel above, with the per-token work cut
+// down for the VALU:
 //  * q.k in bf16 pairs with v_dot2_f32_bf16 (products exact, fp32 sums), no
 //    widening of K;
 //  * a reduce-scatter across the row instead of an all-reduce: after it,
 //    lane c of a row holds the full score of head c % G only, so each lane
 //    computes one exponential per token;
-//  * P.V in bf16 pairs over two tokens: the weights of tokens t and t+1 are
-//    rounded to bf16 (nearest even) and paired, V elements of the two
-//    tokens are interleaved with v_perm_b32, and v_dot2_f32_bf16 adds both
-//    products to the fp32 accumulator.  The running sum l uses the fp32
-//    weights;
+//  * P.V in bf16 pairs over two tokens: a lane rounds its head's weights of
+//    tokens t and t+1 to bf16 (nearest even) and packs them, every lane of
+//    the row takes each head's packed pair from its owner with DPP moves, V
+//    elements of the two tokens are interleaved with v_perm_b32, and
+//    v_dot2_f32_bf16 adds both products to the fp32 accumulator.  The
+//    running sum l uses the fp32 weights;
+//  * the running max is a reference, moved only when a chunk exceeds it by
+//    more than 2^8 (the rescale of l and the accumulators is then rare);
+//    exact in real arithmetic, like the eager rescale;
 //  * the K and V loads of a wave's next chunk are issued as soon as the
 //    registers of the current chunk are consumed, so they overlap the
 //    softmax and P.V work of the current chunk.
 #ifndef PA_DECODE_UNROLL
 #define PA_DECODE_UNROLL 8
+#endif
+#ifndef PA_DECODE_UNROLL_G8
+#define PA_DECODE_UNROLL_G8 4  // groups of eight heads: fewer loads in flight, fewer registers
 #endif
 #ifndef PA_DECODE_WAVES
 #define PA_DECODE_WAVES 4
@@ -377,41 +385,45 @@ decode_partition_kernel(const DecodeKernelArgs a) {
 #define PA_DECODE_ORDER 3
 #endif
 
-// Reduce-scatter of G per-lane partial sums over a row of L lanes: lane c
-// returns the row total of head c % G (all lanes of the row with the same
-// c % G get the same value).
+// Reduce-scatter of G per-lane partial sums over a row of L lanes.  Slot j
+// of lane c holds the partial sum of head j ^ (c % G) (the query heads are
+// loaded in that lane-dependent order), so at every exchange the partner
+// lane holds the head a lane keeps in a fixed slot and no selects are
+// needed.  Lane c returns the row total of head c % G (all lanes of the row
+// with the same c % G get the same value).
 template <int L, int G>
-__device__ __forceinline__ float row_scatter_sum(const float (&v)[G], int col) {
+__device__ __forceinline__ float row_scatter_sum(const float (&v)[G]) {
   float r;
-  if constexpr (G == 4) {
-    const bool b0 = col & 1;
-    const bool b1 = (col >> 1) & 1;
-    float a = b0 ? v[1] : v[0];
-    float b = b0 ? v[3] : v[2];
-    const float sa = b0 ? v[0] : v[1];
-    const float sb = b0 ? v[2] : v[3];
-    a += dpp_f32<kDppQuadXor1>(sa);
-    b += dpp_f32<kDppQuadXor1>(sb);
-    const float keep = b1 ? b : a;
-    const float send = b1 ? a : b;
-    r = keep + dpp_f32<kDppQuadXor2>(send);
+  if constexpr (G == 8) {
+    // the half-row mirror pairs lane c with lane c ^ 7, whose slot 7 - j
+    // holds the head of slot j here; then xor 2 and xor 1.  The three
+    // partners generate all eight lanes of the group.
+    float x[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) x[j] = v[j] + dpp_f32<kDppRowHalfMirror>(v[7 - j]);
+    const float y0 = x[0] + dpp_f32<kDppQuadXor2>(x[2]);
+    const float y1 = x[1] + dpp_f32<kDppQuadXor2>(x[3]);
+    r = y0 + dpp_f32<kDppQuadXor1>(y1);
+  } else if constexpr (G == 4) {
+    const float x0 = v[0] + dpp_f32<kDppQuadXor1>(v[1]);
+    const float x2 = v[2] + dpp_f32<kDppQuadXor1>(v[3]);
+    r = x0 + dpp_f32<kDppQuadXor2>(x2);
   } else if constexpr (G == 2) {
-    const bool b0 = col & 1;
-    const float keep = b0 ? v[1] : v[0];
-    const float send = b0 ? v[0] : v[1];
-    r = keep + dpp_f32<kDppQuadXor1>(send);
+    r = v[0] + dpp_f32<kDppQuadXor1>(v[1]);
     r += dpp_f32<kDppQuadXor2>(r);
   } else {
     r = v[0];
     r += dpp_f32<kDppQuadXor1>(r);
     r += dpp_f32<kDppQuadXor2>(r);
   }
+  // the rest of the row: the other quads (G <= 4) or the other 8-lane
+  // group of a 16-lane row (G = 8)
   if constexpr (L == 16) {
-    r += dpp_f32<kDppRowRor4>(r);
+    if constexpr (G < 8) r += dpp_f32<kDppRowRor4>(r);
     r += dpp_f32<kDppRowRor8>(r);
   } else {
     static_assert(L == 8, "rows of 8 or 16 lanes");
-    r += swizzle_xor4(r);
+    if constexpr (G < 8) r += swizzle_xor4(r);
   }
   return r;
 }
@@ -430,12 +442,43 @@ __device__ __forceinline__ float rows_sum(float x) {
   return xor32_sum(x);
 }
 
-// value of head H from the quad lane that owns it
+// value of head H for this lane's row, from the lane of the row that owns
+// it (lane c owns head c % G; col = lane % L)
 template <int G, int H>
-__device__ __forceinline__ float from_head(float x) {
-  if constexpr (G == 1) return x;
-  else return quad_bcast<H>(x);
+__device__ __forceinline__ uint32_t from_head(uint32_t x, int col) {
+  if constexpr (G == 1) {
+    return x;
+  } else if constexpr (G <= 4) {
+    return quad_bcast<H>(x);
+  } else {
+    // quads of parity j hold heads 4j .. 4j+3: quad lane H % 4 has head H
+    // in the quads of parity H / 4, and the half-row mirror brings it to
+    // the quads of the other parity
+    const uint32_t q = quad_bcast<H % 4>(x);
+    const uint32_t o = dpp_u32<kDppRowHalfMirror>(q);
+    return (((col >> 2) & 1) == (H >> 2)) ? q : o;
+  }
 }
+// out[h] = the value of head h, for every head of the group
+template <int G, int H = 0>
+__device__ __forceinline__ void every_head(uint32_t x, int col, uint32_t (&out)[G]) {
+  if constexpr (H < G) {
+    out[H] = from_head<G, H>(x, col);
+    every_head<G, H + 1>(x, col, out);
+  }
+}
+template <int G>
+__device__ __forceinline__ void every_head(float x, int col, float (&out)[G]) {
+  uint32_t u[G];
+  every_head<G>(__float_as_uint(x), col, u);
+#pragma unroll
+  for (int h = 0; h < G; ++h) out[h] = __uint_as_float(u[h]);
+}
+
+// A wave rescales its running sums only when a head's max grows by more
+// than this many base-2 units; until then the weights exp2(s - m) may reach
+// 2^8, which the fp32 sums and the bf16 weights hold exactly as well.
+constexpr float kDecodeRescaleSlack = 8.f;
 
 // Addressing of one wave step.  Load u of chunk c covers the R tokens
 // tok0 .. tok0+R-1 (tok0 = chunk start + u*R), all in one block, so the
@@ -506,7 +549,7 @@ template <int D, int G>
 struct Bf16Decode {
   static constexpr int L = D / 8;   // lanes per token row (8 bf16 per lane)
   static constexpr int R = 64 / L;  // token rows per load instruction
-  static constexpr int U = PA_DECODE_UNROLL;
+  static constexpr int U = (G == 8) ? PA_DECODE_UNROLL_G8 : PA_DECODE_UNROLL;
   static constexpr int CH = R * U;  // tokens per wave step
   static constexpr int W = PA_DECODE_WAVES;
   static_assert(U % 2 == 0, "tokens are paired for the P.V dot products");
@@ -521,7 +564,7 @@ struct Bf16Decode {
           static_cast<const uint16_t *>(a.q) + ((size_t)seq * a.num_heads + (size_t)kvh * G) * D);
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        const uint4 c = qv[h * L + col];
+        const uint4 c = qv[(h ^ (col & (G - 1))) * L + col];  // slot h: head h ^ (col % G)
         qp[h][0] = c.x;
         qp[h][1] = c.y;
         qp[h][2] = c.z;
@@ -576,16 +619,28 @@ struct Bf16Decode {
           t = dot2_bf16(qp[h][2], kr[u].z, t);
           d[h] = dot2_bf16(qp[h][3], kr[u].w, t);
         }
-        const float r = row_scatter_sum<L, G>(d, col);
+        const float r = row_scatter_sum<L, G>(d);
         s[u] = valid[u] ? r * sl : -INFINITY;
       }
       float cm = s[0];
 #pragma unroll
       for (int u = 1; u < U; ++u) cm = fmaxf(cm, s[u]);
       cm = rows_max<L>(cm);
-      const float m_new = fmaxf(m, cm);
-      const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m - m_new);
-      m = m_new;
+      // lazy rescale: a head's reference max moves only when the chunk
+      // exceeds it by more than the slack (always on its first valid chunk,
+      // when m is still -inf)
+      const bool grow = cm > m + kDecodeRescaleSlack;
+      if (__builtin_amdgcn_ballot_w64(grow)) {
+        const float alpha = grow ? fast_exp2(m - cm) : 1.f;  // 0 when m is -inf
+        m = grow ? cm : m;
+        l *= alpha;
+        float ah[G];
+        every_head<G>(alpha, col, ah);
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[h][e] *= ah[h];
+      }
       float p[U];
       float psum = 0.f;
 #pragma unroll
@@ -593,19 +648,7 @@ struct Bf16Decode {
         p[u] = valid[u] ? fast_exp2(s[u] - m) : 0.f;
         psum += p[u];
       }
-      l = l * alpha + psum;
-
-      float ah[G];
-      if constexpr (G >= 1) ah[0] = from_head<G, 0>(alpha);
-      if constexpr (G >= 2) ah[1] = from_head<G, 1>(alpha);
-      if constexpr (G >= 4) {
-        ah[2] = from_head<G, 2>(alpha);
-        ah[3] = from_head<G, 3>(alpha);
-      }
-#pragma unroll
-      for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[h][e] *= ah[h];
+      l += psum;
 
       // rows outside the context (or in an invalid block) may hold anything,
       // NaN included: select them to zero so that weight 0 gives exactly 0
@@ -628,13 +671,10 @@ struct Bf16Decode {
         vp[5] = interleave_hi(vr[u].z, vr[u + 1].z);
         vp[6] = interleave_lo(vr[u].w, vr[u + 1].w);
         vp[7] = interleave_hi(vr[u].w, vr[u + 1].w);
+        // this lane's head's two weights, rounded to bf16 and packed, then
+        // the packed pair of every head from the lane that owns it
         uint32_t pk[G];
-        if constexpr (G >= 1) pk[0] = pack_bf16x2_rne(from_head<G, 0>(p[u]), from_head<G, 0>(p[u + 1]));
-        if constexpr (G >= 2) pk[1] = pack_bf16x2_rne(from_head<G, 1>(p[u]), from_head<G, 1>(p[u + 1]));
-        if constexpr (G >= 4) {
-          pk[2] = pack_bf16x2_rne(from_head<G, 2>(p[u]), from_head<G, 2>(p[u + 1]));
-          pk[3] = pack_bf16x2_rne(from_head<G, 3>(p[u]), from_head<G, 3>(p[u + 1]));
-        }
+        every_head<G>(pack_bf16x2_rne(p[u], p[u + 1]), col, pk);
 #pragma unroll
         for (int h = 0; h < G; ++h)
 #pragma unroll
@@ -671,13 +711,13 @@ struct Bf16Decode {
     float d[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      const uint4 qc = qv[h * L + col];
+      const uint4 qc = qv[(h ^ (col & (G - 1))) * L + col];  // slot h: head h ^ (col % G)
       float t = dot2_bf16(qc.x, kc.x, 0.f);
       t = dot2_bf16(qc.y, kc.y, t);
       t = dot2_bf16(qc.z, kc.z, t);
       d[h] = dot2_bf16(qc.w, kc.w, t);
     }
-    const float s = row_scatter_sum<L, G>(d, col) * a.scale_log2;  // head col % G
+    const float s = row_scatter_sum<L, G>(d) * a.scale_log2;  // head col % G
     const float m_new = fmaxf(m, s);
     const float alpha = fast_exp2(m - m_new);  // 0 while m is still -inf
     const float p = fast_exp2(s - m_new);
@@ -686,12 +726,8 @@ struct Bf16Decode {
     float vf[8];
     Chunk<bf16_t>::widen(vc, vf);
     float ah[G], pb[G];
-    if constexpr (G >= 1) ah[0] = from_head<G, 0>(alpha), pb[0] = from_head<G, 0>(p);
-    if constexpr (G >= 2) ah[1] = from_head<G, 1>(alpha), pb[1] = from_head<G, 1>(p);
-    if constexpr (G >= 4) {
-      ah[2] = from_head<G, 2>(alpha), pb[2] = from_head<G, 2>(p);
-      ah[3] = from_head<G, 3>(alpha), pb[3] = from_head<G, 3>(p);
-    }
+    every_head<G>(alpha, col, ah);
+    every_head<G>(p, col, pb);
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       const float pr = bf16_lo(pack_bf16x2_rne(pb[h], 0.f));  // the weight rounded to bf16
@@ -806,6 +842,7 @@ __device__ __forceinline__ bool size_order_item(const DecodeKernelArgs &a, int i
 
 template <int D, int G>
 __global__ void __launch_bounds__(64 * PA_DECODE_WAVES)
+__attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 : 1)))  // four work-groups per CU up to G = 4
 decode_partition_bf16_kernel(const DecodeKernelArgs a) {
   using K = Bf16Decode<D, G>;
   constexpr int W = K::W;
@@ -1019,14 +1056,14 @@ template <typename T, int D, int DV, int G>
 static hipError_t launch_partition_t(const DecodeArgs &a, hipStream_t stream) {
   const DecodeKernelArgs k = make_kernel_args(a);
   dim3 grid(a.max_partitions, a.cache.num_kv_heads, a.num_seqs);
-  if constexpr (std::is_same<T, bf16_t>::value && G <= 4 && D == DV) {
+  if constexpr (std::is_same<T, bf16_t>::value && D == DV) {
     if (a.query_start_loc) return hipErrorNotSupported;  // prefill rows run on the generic kernel only
 #if PA_DECODE_ORDER == 1 || PA_DECODE_ORDER == 3
     grid = dim3(a.cache.num_kv_heads, a.num_seqs, a.max_partitions);
 #endif
     hipLaunchKernelGGL((decode_partition_bf16_kernel<D, G>), grid, dim3(64 * PA_DECODE_WAVES), 0, stream, k);
   } else {
-    // (cascade launches are bf16 with G <= 4 and D == DV: never here)
+    // (cascade launches are bf16 with D == DV: never here)
     hipLaunchKernelGGL((decode_partition_kernel<T, D, DV, G>), grid, dim3(DecodeShape<T, D>::kThreads), 0,
                        stream, k);
   }
@@ -1056,7 +1093,7 @@ static hipError_t launch_partition_d(const DecodeArgs &a, hipStream_t stream) {
 
 bool decode_fast_path(const DecodeArgs &a) {
   const int g = a.cache.num_kv_heads > 0 ? a.num_heads / a.cache.num_kv_heads : 0;
-  return a.cache.dtype == 1 && g >= 1 && g <= 4 && a.cache.head_dim == a.cache.head_dim_v &&
+  return a.cache.dtype == 1 && g >= 1 && g <= 8 && a.cache.head_dim == a.cache.head_dim_v &&
          !a.query_start_loc;
 }
 

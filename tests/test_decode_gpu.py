@@ -372,7 +372,7 @@ def _append_rows(case):
 
 
 @pytest.mark.parametrize("dtype,group,dims", [(W.BF16, 1, (128, 128)), (W.BF16, 2, (64, 64)), (W.BF16, 4, (128, 128)),
-                                              (W.BF16, 8, (128, 128)), (W.F32, 4, (64, 64)),
+                                              (W.BF16, 8, (128, 128)), (W.BF16, 8, (64, 64)), (W.F32, 4, (64, 64)),
                                               (W.BF16, 4, (128, 64))])
 def test_decode_append(dtype, group, dims):
     """pa_decode_append = the cache write of each sequence's newest token
