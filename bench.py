@@ -595,6 +595,9 @@ def main():
             # the metric's literal shape: 32 sequences of exactly 4096 tokens
             bench_decode_secondary("decode_batch_bs32_ctx4096", 1024,
                                    case=W.decode_batch(2000, poison=False, fixed_ctx=4096)),
+            # eight query heads per kv head: 64 q over the same 8 kv heads and K/V bytes
+            bench_decode_secondary("decode_batch_bs32_64q_8kv", 512,
+                                   case=W.decode_batch(2000, poison=False, num_heads=64)),
             bench_decode_secondary("prefix_shared_decode_bs16", 512, groups=([0, 16, 32, 48, 64], [64 * 16] * 4)),
             bench_decode_secondary("prefix_shared_decode_bs8", 512, groups=([0, 16, 32, 48, 64], [64 * 8] * 4)),
         ]

@@ -432,9 +432,6 @@ int pa_decode_cascade(const pa_kv_cache *cache, void *out, const void *q, int32_
   if (v_dim(cache) != cache->head_dim)
     return fail(PA_ERR_UNSUPPORTED, "cascade decode needs v_head_dim equal to head_dim (%d vs %d)",
                 v_dim(cache), cache->head_dim);
-  const int group = num_heads / cache->num_kv_heads;
-  if (group > 4) return fail(PA_ERR_UNSUPPORTED, "cascade decode takes num_heads / num_kv_heads in {1, 2, 4}, got %d",
-                             group);
   if (num_groups < 0 || (num_seqs > 0 && num_groups == 0))
     return fail(PA_ERR_SHAPE, "num_groups %d: every sequence belongs to one group", num_groups);
   if (num_groups > kMaxGridYZ) return fail(PA_ERR_SHAPE, "num_groups %d above %d", num_groups, kMaxGridYZ);

@@ -281,7 +281,7 @@ def test_cascade_validation(lib):
     assert casc(ps=0) == -10 and "partition_size > 0" in msg()
     assert casc(ps=48) == -10
     assert casc(c=cache(dtype=0)) == -8 and "bf16 only" in msg()
-    assert casc(H=64) == -8                                   # 8 query heads per kv head
+    assert casc(H=48) == -6                                   # 6 query heads per kv head
     assert casc(ng=0) == -3
     assert casc(gs=None) == -1
     assert casc(mg=0) == -3 and casc(mg=5) == -3

@@ -78,6 +78,16 @@ def test_decode_batch_bs32_full(ps):
     print(f"bs32 batch ps={ps}: max-abs {mx:.2e} mean-abs {mean:.2e}")
 
 
+def test_decode_batch_bs32_eight_heads_per_kv_head_full():
+    """The bs32 batch with 64 query heads over its 8 kv heads (G = 8)."""
+    case = W.decode_batch(2000, num_heads=64)
+    ref = oracle_decode(case)
+    log("decode batch 32 x U[512,4096], 64 q / 8 kv heads, partition=512")
+    _, got = _run(case, 512)
+    mx, mean = assert_close(got, ref, W.BF16, "bs32 batch G8 ps512")
+    print(f"bs32 batch G=8: max-abs {mx:.2e} mean-abs {mean:.2e}")
+
+
 @pytest.mark.timeout(900)
 def test_long_context_split_k_full():
     case = W.make_config("long_context_decode")
@@ -304,7 +314,7 @@ def test_cascade_prefix_shared_full(name):
         print(f"cascade {name} ps={ps}: max-abs {mx:.2e} mean-abs {mean:.2e}")
 
 
-@pytest.mark.parametrize("group", [1, 2, 4])
+@pytest.mark.parametrize("group", [1, 2, 4, 8])
 def test_cascade_irregular_groups(group):
     """Groups of 1, 3, 70 (two member tiles) and 6 rows; shared lengths below
     the true sharing, 0, and rows whose context ends inside or exactly at

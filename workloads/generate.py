@@ -375,16 +375,18 @@ def tiny_fp32_decode(seed: int = 1000, poison: bool = True) -> DecodeCase:
 
 
 def decode_batch(seed: int = 2000, poison: bool = True, num_seqs: int = 32,
-                 ctx_low: int = 512, ctx_high: int = 4096, fixed_ctx: Optional[int] = None) -> DecodeCase:
+                 ctx_low: int = 512, ctx_high: int = 4096, fixed_ctx: Optional[int] = None,
+                 num_heads: int = 32) -> DecodeCase:
     """32 sequences, 32 q / 8 kv heads, head_dim 128, block_size 32, context
-    uniform in [512, 4096], pool 1.25x the blocks in use, bf16."""
+    uniform in [512, 4096], pool 1.25x the blocks in use, bf16.  ``num_heads``
+    = 64 gives eight query heads per kv head over the same K/V."""
     rng = np.random.default_rng(seed)
     if fixed_ctx is not None:
         ctx = [int(fixed_ctx)] * num_seqs
     else:
         ctx = rng.integers(ctx_low, ctx_high, size=num_seqs, endpoint=True).tolist()
     tables, nb, pad = _layout(rng, ctx, 32)
-    return _finish(rng, kind="decode", name="decode_batch_bs32", dtype=BF16, Hq=32, Hkv=8, D=128,
+    return _finish(rng, kind="decode", name="decode_batch_bs32", dtype=BF16, Hq=num_heads, Hkv=8, D=128,
                    bs=32, ctx=ctx, tables=tables, nb=nb, pad=pad, q_rows=num_seqs,
                    new_positions=[np.array([n - 1]) for n in ctx], poison=poison)
 
