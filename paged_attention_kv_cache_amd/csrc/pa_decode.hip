@@ -923,9 +923,14 @@ decode_partition_bf16_kernel(const DecodeKernelArgs a) {
 // Merge the partitions of every multi-partition sequence:
 //   M = max_p m_p,  out = sum_p o_p 2^(m_p - M) / sum_p l_p 2^(m_p - M).
 // One work-group of 256 threads per (query head, sequence).  Thread t owns
-// four consecutive dimensions (one 16-byte load) of every partition
-// p = t / (D/4) (mod 256 / (D/4)); each thread keeps four partitions' loads
-// in flight.
+// four consecutive dimensions (one 16-byte load) of partitions
+// p = t / (D/4) (mod 256 / (D/4)), four of them per batch.  The first batch
+// is loaded before the context length is known (every slot below
+// max_partitions lies inside the workspace; slots past the row's partition
+// count are selected out, whatever they hold), so the kernel waits for
+// one round trip to memory instead of three.  Each thread merges its
+// partitions with a running max (the online-softmax rule); the 256 / (D/4)
+// thread groups are then merged through LDS with the same rule.
 template <typename T, int D>
 __global__ void __launch_bounds__(256)
 decode_reduce_kernel(const DecodeKernelArgs a) {
@@ -933,8 +938,28 @@ decode_reduce_kernel(const DecodeKernelArgs a) {
   constexpr int kLanesPerPart = D / 4;               // float4 per lane
   constexpr int kGroups = kThreads / kLanesPerPart;  // partitions per pass
   constexpr int kUnroll = 4;
+  constexpr int kBatch = kGroups * kUnroll;          // partitions per batch
   const int head = blockIdx.x;
   const int seq = blockIdx.y;
+  const size_t base = ((size_t)seq * a.num_heads + head) * a.max_partitions;
+  const int d4 = threadIdx.x % kLanesPerPart;
+  const int g = threadIdx.x / kLanesPerPart;
+  const float4 *o4 = reinterpret_cast<const float4 *>(a.ws_o);
+
+  float mp[kUnroll], lp[kUnroll];
+  float4 op[kUnroll];
+  auto load = [&](int p0) {
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int p = p0 + g + u * kGroups;
+      const size_t idx = base + (p < a.max_partitions ? p : 0);
+      mp[u] = a.ws_m[idx];
+      lp[u] = a.ws_l[idx];
+      op[u] = o4[idx * (D / 4) + d4];
+    }
+  };
+  load(0);
+
   const int ctx = decode_context(a, seq);
   // cascade: a slot per chunk of the shared tokens and per partition of
   // the rest; otherwise one slot per partition, and a single partition was
@@ -948,64 +973,67 @@ decode_reduce_kernel(const DecodeKernelArgs a) {
   if (!cascade && nparts <= 1) return;
   // (a cascade row of context 0 has no slot: its output is zero)
 
-  const size_t base = ((size_t)seq * a.num_heads + head) * a.max_partitions;
-  __shared__ float sm_max;
-  __shared__ float4 sm_o[kGroups][kLanesPerPart];
-  __shared__ float sm_l[kGroups];
-
-  if (threadIdx.x < 64) {  // one wave finds M
-    float mx = -INFINITY;
-    for (int p = threadIdx.x; p < nparts; p += 64) mx = fmaxf(mx, a.ws_m[base + p]);
-#pragma unroll
-    for (int k = 1; k < 64; k <<= 1) mx = fmaxf(mx, __shfl_xor(mx, k));
-    if (threadIdx.x == 0) sm_max = mx;
-  }
-  __syncthreads();
-  const float M = sm_max;
-
-  const int d4 = threadIdx.x % kLanesPerPart;
-  const int g = threadIdx.x / kLanesPerPart;
-  const float4 *o4 = reinterpret_cast<const float4 *>(a.ws_o);
+  // this thread's running (m, l, o) over its partitions; a partition with
+  // no token has m = -inf and weight 0
+  float m = -INFINITY, l = 0.f;
   float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-  float l = 0.f;
-  if (M != -INFINITY) {
-    for (int p0 = g; p0 < nparts; p0 += kGroups * kUnroll) {
-      float mp[kUnroll], lp[kUnroll];
-      float4 op[kUnroll];
+  for (int p0 = 0; p0 < nparts; p0 += kBatch) {
+    if (p0 > 0) load(p0);
+    float bm = -INFINITY;
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const int p = p0 + u * kGroups;
-        const bool in = p < nparts;
-        const size_t idx = base + (in ? p : 0);
-        mp[u] = in ? a.ws_m[idx] : -INFINITY;
-        lp[u] = in ? a.ws_l[idx] : 0.f;
-        op[u] = in ? o4[idx * (D / 4) + d4] : make_float4(0.f, 0.f, 0.f, 0.f);
-      }
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const float f = (mp[u] == -INFINITY) ? 0.f : fast_exp2(mp[u] - M);
-        o.x = fmaf(op[u].x, f, o.x);
-        o.y = fmaf(op[u].y, f, o.y);
-        o.z = fmaf(op[u].z, f, o.z);
-        o.w = fmaf(op[u].w, f, o.w);
-        l = fmaf(lp[u], f, l);
-      }
+    for (int u = 0; u < kUnroll; ++u) {
+      const bool in = p0 + g + u * kGroups < nparts;
+      mp[u] = in ? mp[u] : -INFINITY;
+      lp[u] = in ? lp[u] : 0.f;
+      op[u] = in ? op[u] : make_float4(0.f, 0.f, 0.f, 0.f);
+      bm = fmaxf(bm, mp[u]);
     }
+    if (bm == -INFINITY) continue;
+    const float mn = fmaxf(m, bm);
+    const float alpha = fast_exp2(m - mn);  // 0 while m is still -inf
+    o.x *= alpha;
+    o.y *= alpha;
+    o.z *= alpha;
+    o.w *= alpha;
+    l *= alpha;
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const float f = (mp[u] == -INFINITY) ? 0.f : fast_exp2(mp[u] - mn);
+      o.x = fmaf(op[u].x, f, o.x);
+      o.y = fmaf(op[u].y, f, o.y);
+      o.z = fmaf(op[u].z, f, o.z);
+      o.w = fmaf(op[u].w, f, o.w);
+      l = fmaf(lp[u], f, l);
+    }
+    m = mn;
   }
+
+  __shared__ float4 sm_o[kGroups][kLanesPerPart];
+  __shared__ float sm_m[kGroups], sm_l[kGroups];
   sm_o[g][d4] = o;
-  if (d4 == 0) sm_l[g] = l;
+  if (d4 == 0) {
+    sm_m[g] = m;
+    sm_l[g] = l;
+  }
   __syncthreads();
   if (g == 0) {
+    float M = sm_m[0];
+#pragma unroll
+    for (int i = 1; i < kGroups; ++i) M = fmaxf(M, sm_m[i]);
     float4 ot = make_float4(0.f, 0.f, 0.f, 0.f);
     float lt = 0.f;
+    if (M != -INFINITY) {
 #pragma unroll
-    for (int i = 0; i < kGroups; ++i) {
-      const float4 v = sm_o[i][d4];
-      ot.x += v.x;
-      ot.y += v.y;
-      ot.z += v.z;
-      ot.w += v.w;
-      lt += sm_l[i];
+      for (int i = 0; i < kGroups; ++i) {
+        const float mi = sm_m[i];
+        const float f = (mi == -INFINITY) ? 0.f : fast_exp2(mi - M);
+        const float4 v = sm_o[i][d4];
+        ot.x = fmaf(v.x, f, ot.x);
+        ot.y = fmaf(v.y, f, ot.y);
+        ot.z = fmaf(v.z, f, ot.z);
+        ot.w = fmaf(v.w, f, ot.w);
+        lt = fmaf(sm_l[i], f, lt);
+      }
     }
     const size_t ob = ((size_t)seq * a.num_heads + head) * D + d4 * 4;
     store_one<T>(a.out, ob + 0, lt > 0.f ? ot.x / lt : 0.f);

@@ -479,7 +479,6 @@ prefill_chunk_kernel(const PrefillKernelArgs a) {
 #if !PA_PREFILL_LOOKAHEAD
     qk(sk[b0], c0, c1);
 #endif
-    // tile t+2 from the pool (past the last tile: in-pool rows, zeroed)
     // tile t+2 from the pool (past the last tile: zero rows, never used)
     gk.issue(sk[b2], sid[b2], kbase, a.num_blocks, block_stride, k0 + 2 * KT, kend, shift);
     gv.issue(sv[b2], sid[b2], vbase, a.num_blocks, vblock_stride, k0 + 2 * KT, kend, shift);
@@ -568,16 +567,16 @@ prefill_chunk_kernel(const PrefillKernelArgs a) {
     }
 
     // O^T += V^T P^T; the A operand takes the same keys from row d of V^T,
-    // and each V^T fragment read from LDS feeds HW products
-    // A operand (V^T) by transposed LDS reads of the row-major V tile: in
-    // each 16-lane group, source lane s reads 4 d-values of one key (key
-    // K0 + s/4, d = D0 + 4 (s%4)) and lane o receives d = D0 + o of keys
-    // K0 .. K0+3; two reads give the 8 keys of the B operand's k-step
-    // source lane s of a 16-lane group reads key K0 + s/4, d = D0 + 4 (s%4):
-    // group dt, key (ks / 2) 32 + (ks % 2) 16 + 4 (g / 2) + s / 4 (+8), slot
-    // (2 (g % 2) + (s / 2) % 2) ^ ((key / 4) % 4), half s % 2
-    // (address arithmetic in the LDS address space, constants last, so that
-    // they fold into the instructions' offset fields)
+    // and each V^T fragment read from LDS feeds HW products.  The A operand
+    // comes from transposing LDS reads of the row-major V tile: in each
+    // 16-lane group, source lane s reads 4 d-values of one key (key K0 +
+    // s/4, d = D0 + 4 (s%4)) and lane o receives d = D0 + o of keys K0 ..
+    // K0+3; two reads give the 8 keys of the B operand's k-step.  Lane s of
+    // 16-lane group g reads, for tile dt and k-step ks, key (ks / 2) 32 +
+    // (ks % 2) 16 + 4 (g / 2) + s / 4 (+8 for the second read), slot
+    // (2 (g % 2) + (s / 2) % 2) ^ ((key / 4) % 4), half s % 2 (address
+    // arithmetic in the LDS address space, constants last, so that they
+    // fold into the instructions' offset fields)
     typedef __attribute__((address_space(3))) const char *lds_cptr;
     typedef short v4s __attribute__((ext_vector_type(4)));
     typedef __attribute__((address_space(3))) v4s *lds_v4s_ptr;
