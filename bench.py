@@ -327,13 +327,15 @@ def bench_decode_secondary(name, ps, steps=30, groups=None, case=None):
     return res
 
 
-def bench_serving(seed=7000, num_requests=96, num_blocks=12000):
+def bench_serving(seed=7000, num_requests=96, num_blocks=12000, mixed=False):
     """The scheduler driving the kernels over a request trace: every step the
     host plans (pa_sched_next_step), copies the step's tables through pinned
     buffers, and launches kv_cache_write plus prefill or decode; the step is
     then committed with 'sampled' tokens.  K/V/Q values are random device
     data (they do not change the work).  Reports prompt + generated tokens
-    per second of wall time, and the share of it the GPU was busy."""
+    per second of wall time, and the share of it the GPU was busy.  With
+    ``mixed`` each step is one batch (decode rows, then prompt chunks) and a
+    step holding both runs as one prefill launch."""
     import torch
     import paged_attention_kv_cache_amd as P
     import workloads as W
@@ -349,7 +351,7 @@ def bench_serving(seed=7000, num_requests=96, num_blocks=12000):
     kvm = P.KvManager(num_blocks, bs)
     cap_seqs, cap_tokens, cap_blocks = 64, 4096, 128
     sched = P.StepScheduler(kvm, max_batched_tokens=cap_tokens, max_chunk_tokens=512, max_decode_steps=8,
-                            min_decode_steps=1, max_seqs=cap_seqs, max_blocks_per_seq=cap_blocks)
+                            min_decode_steps=1, max_seqs=cap_seqs, max_blocks_per_seq=cap_blocks, mixed=mixed)
     for r in range(num_requests):
         sched.add_request(r, prompts[r], max_new[r])
     kc = torch.randn((num_blocks, bs, Hkv, D), device="cuda").to(torch.bfloat16)
@@ -385,10 +387,17 @@ def bench_serving(seed=7000, num_requests=96, num_blocks=12000):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         P.pa_kv_cache_write(src_k[:T], src_v[:T], kc, vc, dev["slots"][:T])
-        if st.kind == P.KIND_PROMPT:
+        if st.kind in (P.KIND_PROMPT, P.KIND_MIXED):
             P.pa_prefill_chunk(src_q[:T], dev["qsl"][: n + 1], kc, vc, dev["tab"][:n], dev["ctx"][:n], scale,
                                st.max_query_len, st.max_context_len, out=out[:T])
-            prompt_tokens += T
+            # a mixed step's decode rows come first, one token each
+            nd = 0
+            if st.kind == P.KIND_MIXED:
+                qlen = np.diff(st.query_start_loc)
+                while nd < n and qlen[nd] == 1:
+                    nd += 1
+            prompt_tokens += T - nd
+            decode_tokens += nd
         else:
             P.pa_decode(src_q[:n], kc, vc, dev["tab"][:n], dev["ctx"][:n], scale, st.max_context_len, 256,
                         out=out[:n], workspace=ws)
@@ -404,13 +413,15 @@ def bench_serving(seed=7000, num_requests=96, num_blocks=12000):
     res = {
         "workload": f"{num_requests} requests, prompts U[128,2048] (+512-token shared system prompt on a third), "
                     f"generation U[32,256]; 32q/8kv, D128, BS32, bf16; budget 4096 tokens, 512-token chunks, "
-                    f"<= 8 decode steps in a row, pool {num_blocks} blocks",
+                    + ("one mixed batch per step" if mixed else "<= 8 decode steps in a row")
+                    + f", pool {num_blocks} blocks",
+        "policy": "mixed" if mixed else "alternating",
         "steps": steps, "prompt_tokens": prompt_tokens, "generated_tokens": decode_tokens,
         "wall_s": round(wall, 3), "tokens_per_s": round((prompt_tokens + decode_tokens) / wall, 1),
         "gpu_busy_frac": round(gpu_ms * 1e-3 / wall, 3),
         "prefix_hit_tokens": st["prefix_hit_tokens"],
     }
-    log(f"serving: {steps} steps, {prompt_tokens} prompt + {decode_tokens} generated tokens in {wall:.2f} s "
+    log(f"serving ({res['policy']}): {steps} steps, {prompt_tokens} prompt + {decode_tokens} generated tokens in {wall:.2f} s "
         f"({res['tokens_per_s']:.0f} tokens/s, GPU busy {res['gpu_busy_frac']:.0%})")
     sched.close()
     kvm.close()
@@ -602,6 +613,7 @@ def main():
             bench_decode_secondary("prefix_shared_decode_bs8", 512, groups=([0, 16, 32, 48, 64], [64 * 8] * 4)),
         ]
         line["serving_loop"] = bench_serving()
+        line["serving_loop_mixed"] = bench_serving(mixed=True)
     if not args.no_cpu_baseline:
         log(f"timing the CPU oracle for ~{args.cpu_seconds:.0f} s")
         line["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)

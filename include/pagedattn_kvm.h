@@ -137,6 +137,14 @@ int pa_kvm_grow(pa_kvm *m, int32_t new_num_blocks);
  *  - A request's block table must fit a step row (cap_blocks), and the
  *    oldest request must fit the pool; otherwise next_step fails with
  *    PA_ERR_SHAPE or PA_ERR_NO_BLOCKS.
+ *
+ * Mixed policy (config.mixed != 0; the one-batch variant of the same
+ * limits): every step first gives each decoding sequence one token, in
+ * admission order, then fills the rest of max_batched_tokens with prompt
+ * chunks as a prompt step does.  Decode tokens count against the budget.
+ * A step holding both kinds is kind 3 and runs as one pa_prefill_chunk
+ * over all its rows (a decode row is a chunk of one token); a step with
+ * one kind only is kind 1 or 2 as above.
  * ------------------------------------------------------------------------ */
 typedef struct pa_sched pa_sched; /* opaque */
 
@@ -146,11 +154,13 @@ typedef struct pa_sched_config {
   int32_t max_decode_steps;     /* 8    */
   int32_t min_decode_steps;     /* 1    */
   int32_t max_seqs;             /* sequences per step */
+  int32_t mixed;                /* 0: alternate; else one mixed batch per step */
 } pa_sched_config;
 
 /* One step's inputs for the attention kernels, written into caller-owned
  * host arrays of the given capacities.  kind: 0 = none (idle), 1 = prompt
- * (use pa_prefill_chunk), 2 = decode (use pa_decode). */
+ * (use pa_prefill_chunk), 2 = decode (use pa_decode), 3 = mixed (decode rows
+ * first, then prompt chunks; use pa_prefill_chunk over all rows). */
 typedef struct pa_step {
   int32_t kind;
   int32_t num_seqs;

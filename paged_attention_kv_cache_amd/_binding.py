@@ -71,7 +71,7 @@ class PaKvmStats(ctypes.Structure):
 
 class PaSchedConfig(ctypes.Structure):
     _fields_ = [(n, _i32) for n in (
-        "max_batched_tokens", "max_chunk_tokens", "max_decode_steps", "min_decode_steps", "max_seqs")]
+        "max_batched_tokens", "max_chunk_tokens", "max_decode_steps", "min_decode_steps", "max_seqs", "mixed")]
 
 
 class PaStep(ctypes.Structure):

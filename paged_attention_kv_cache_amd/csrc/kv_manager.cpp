@@ -455,6 +455,81 @@ int grow_admitted(pa_sched *s, const pa_step *st, int64_t id, int32_t n) {
 
 }  // namespace
 
+namespace {
+
+// Prompt work of a step under `budget` tokens: partly computed prompts in
+// admission order, then waiting requests first come, first served.
+int fill_prompts(pa_sched *s, pa_step *st, int32_t &budget, int32_t seq_cap) {
+  pa_kvm *kvm = s->kvm;
+  const int32_t bs = kvm->block_size;
+  const std::vector<int64_t> order = s->admitted;
+  for (int64_t id : order) {
+    if (budget <= 0 || st->num_seqs >= seq_cap) break;
+    if (s->reqs[id].phase != pa_sched::kPrefill) continue;
+    if (std::find(s->admitted.begin(), s->admitted.end(), id) == s->admitted.end()) continue;  // preempted
+    const Request *r = find(kvm, id);
+    const int32_t ntok = (int32_t)r->tokens.size(), done = r->num_computed;
+    if (blocks_for(ntok, bs) > st->cap_blocks)
+      return pa::set_error(PA_ERR_SHAPE, "request %lld needs %d blocks, step rows hold %d", (long long)id,
+                           blocks_for(ntok, bs), st->cap_blocks);
+    const int32_t chunk = std::min({ntok - done, s->cfg.max_chunk_tokens, budget});
+    const int rc = grow_admitted(s, st, id, chunk);
+    if (rc == kWait) break;
+    if (rc) return rc;
+    step_add(st, kvm, id, done, chunk);
+    budget -= chunk;
+  }
+  while (!s->waiting.empty() && budget > 0 && st->num_seqs < seq_cap) {
+    const int64_t id = s->waiting.front();
+    const Request *r = find(kvm, id);
+    const int32_t ntok = (int32_t)r->tokens.size();
+    if (blocks_for(ntok, bs) > st->cap_blocks)
+      return pa::set_error(PA_ERR_SHAPE, "request %lld needs %d blocks, step rows hold %d", (long long)id,
+                           blocks_for(ntok, bs), st->cap_blocks);
+    int32_t done = 0;
+    pa_kvm_get_computed_blocks(kvm, id, &done);
+    const int32_t chunk = std::min({ntok - done, s->cfg.max_chunk_tokens, budget});
+    if (pa_kvm_allocate_slots(kvm, id, chunk) != PA_OK) {
+      reset_request(kvm, id);  // give back the prefix blocks it attached
+      if (s->admitted.empty() && st->num_seqs == 0)
+        return pa::set_error(PA_ERR_NO_BLOCKS, "request %lld does not fit in a pool of %d blocks", (long long)id,
+                             kvm->num_blocks);
+      break;
+    }
+    s->waiting.pop_front();
+    s->reqs[id].phase = pa_sched::kPrefill;
+    s->admitted.push_back(id);
+    step_add(st, kvm, id, done, chunk);
+    budget -= chunk;
+  }
+  return PA_OK;
+}
+
+// One new token for every decoding sequence, in admission order, while the
+// budget and the step's rows last.
+int fill_decodes(pa_sched *s, pa_step *st, int32_t &budget, int32_t seq_cap) {
+  pa_kvm *kvm = s->kvm;
+  const int32_t bs = kvm->block_size;
+  const std::vector<int64_t> order = s->admitted;
+  for (int64_t id : order) {
+    if (st->num_seqs >= seq_cap || budget <= 0) break;
+    if (s->reqs[id].phase != pa_sched::kRunning) continue;
+    if (std::find(s->admitted.begin(), s->admitted.end(), id) == s->admitted.end()) continue;  // preempted
+    const int32_t done = find(kvm, id)->num_computed;
+    if (blocks_for(done + 1, bs) > st->cap_blocks)
+      return pa::set_error(PA_ERR_SHAPE, "request %lld needs %d blocks, step rows hold %d", (long long)id,
+                           blocks_for(done + 1, bs), st->cap_blocks);
+    const int rc = grow_admitted(s, st, id, 1);
+    if (rc == kWait) continue;
+    if (rc) return rc;
+    step_add(st, kvm, id, done, 1);
+    budget -= 1;
+  }
+  return PA_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 int pa_sched_next_step(pa_sched *s, pa_step *st) {
@@ -466,9 +541,21 @@ int pa_sched_next_step(pa_sched *s, pa_step *st) {
   st->num_seqs = st->num_tokens = st->max_query_len = st->max_context_len = 0;
   st->max_blocks_per_seq = st->cap_blocks;
   st->query_start_loc[0] = 0;
-  pa_kvm *kvm = s->kvm;
-  const int32_t bs = kvm->block_size;
   const int32_t seq_cap = std::min(s->cfg.max_seqs, st->cap_seqs);
+
+  if (s->cfg.mixed) {
+    // one batch: every decoding sequence's token first, then prompt chunks
+    // in the rest of the budget
+    int32_t budget = std::min(s->cfg.max_batched_tokens, st->cap_tokens);
+    int rc = fill_decodes(s, st, budget, seq_cap);
+    if (rc) return rc;
+    const int32_t decode_rows = st->num_seqs;
+    rc = fill_prompts(s, st, budget, seq_cap);
+    if (rc) return rc;
+    if (st->num_seqs > 0) st->kind = st->num_seqs == decode_rows ? 2 : (decode_rows == 0 ? 1 : 3);
+    pa::clear_error();
+    return PA_OK;
+  }
 
   bool has_prefill = false, has_running = false;
   for (int64_t id : s->admitted) (s->reqs[id].phase == pa_sched::kPrefill ? has_prefill : has_running) = true;
@@ -478,48 +565,8 @@ int pa_sched_next_step(pa_sched *s, pa_step *st) {
 
   if (want_prompt) {
     int32_t budget = std::min(s->cfg.max_batched_tokens, st->cap_tokens);
-    // partly computed prompts first, in admission order
-    const std::vector<int64_t> order = s->admitted;
-    for (int64_t id : order) {
-      if (budget <= 0 || st->num_seqs >= seq_cap) break;
-      if (s->reqs[id].phase != pa_sched::kPrefill) continue;
-      if (std::find(s->admitted.begin(), s->admitted.end(), id) == s->admitted.end()) continue;  // preempted
-      const Request *r = find(kvm, id);
-      const int32_t ntok = (int32_t)r->tokens.size(), done = r->num_computed;
-      if (blocks_for(ntok, bs) > st->cap_blocks)
-        return pa::set_error(PA_ERR_SHAPE, "request %lld needs %d blocks, step rows hold %d", (long long)id,
-                             blocks_for(ntok, bs), st->cap_blocks);
-      const int32_t chunk = std::min({ntok - done, s->cfg.max_chunk_tokens, budget});
-      const int rc = grow_admitted(s, st, id, chunk);
-      if (rc == kWait) break;
-      if (rc) return rc;
-      step_add(st, kvm, id, done, chunk);
-      budget -= chunk;
-    }
-    // then admit waiting requests first come, first served
-    while (!s->waiting.empty() && budget > 0 && st->num_seqs < seq_cap) {
-      const int64_t id = s->waiting.front();
-      const Request *r = find(kvm, id);
-      const int32_t ntok = (int32_t)r->tokens.size();
-      if (blocks_for(ntok, bs) > st->cap_blocks)
-        return pa::set_error(PA_ERR_SHAPE, "request %lld needs %d blocks, step rows hold %d", (long long)id,
-                             blocks_for(ntok, bs), st->cap_blocks);
-      int32_t done = 0;
-      pa_kvm_get_computed_blocks(kvm, id, &done);
-      const int32_t chunk = std::min({ntok - done, s->cfg.max_chunk_tokens, budget});
-      if (pa_kvm_allocate_slots(kvm, id, chunk) != PA_OK) {
-        reset_request(kvm, id);  // give back the prefix blocks it attached
-        if (s->admitted.empty() && st->num_seqs == 0)
-          return pa::set_error(PA_ERR_NO_BLOCKS, "request %lld does not fit in a pool of %d blocks",
-                               (long long)id, kvm->num_blocks);
-        break;
-      }
-      s->waiting.pop_front();
-      s->reqs[id].phase = pa_sched::kPrefill;
-      s->admitted.push_back(id);
-      step_add(st, kvm, id, done, chunk);
-      budget -= chunk;
-    }
+    const int rc = fill_prompts(s, st, budget, seq_cap);
+    if (rc) return rc;
     if (st->num_seqs > 0) {
       st->kind = 1;
       s->decode_streak = 0;
@@ -529,20 +576,9 @@ int pa_sched_next_step(pa_sched *s, pa_step *st) {
   }
 
   // decode step: one new token for every running sequence
-  const std::vector<int64_t> order = s->admitted;
-  for (int64_t id : order) {
-    if (st->num_seqs >= seq_cap || st->num_tokens >= st->cap_tokens) break;
-    if (s->reqs[id].phase != pa_sched::kRunning) continue;
-    if (std::find(s->admitted.begin(), s->admitted.end(), id) == s->admitted.end()) continue;  // preempted
-    const int32_t done = find(kvm, id)->num_computed;
-    if (blocks_for(done + 1, bs) > st->cap_blocks)
-      return pa::set_error(PA_ERR_SHAPE, "request %lld needs %d blocks, step rows hold %d", (long long)id,
-                           blocks_for(done + 1, bs), st->cap_blocks);
-    const int rc = grow_admitted(s, st, id, 1);
-    if (rc == kWait) continue;
-    if (rc) return rc;
-    step_add(st, kvm, id, done, 1);
-  }
+  int32_t budget = st->cap_tokens;
+  const int rc = fill_decodes(s, st, budget, seq_cap);
+  if (rc) return rc;
   if (st->num_seqs > 0) {
     st->kind = 2;
     ++s->decode_streak;

@@ -117,7 +117,7 @@ class KvManager:
 class Step:
     """One planned step (views into the scheduler's host arrays)."""
 
-    kind: int                      # 0 idle, 1 prompt, 2 decode
+    kind: int                      # 0 idle, 1 prompt, 2 decode, 3 mixed (decode rows, then prompt chunks)
     request_ids: np.ndarray        # [num_seqs] int64
     query_start_loc: np.ndarray    # [num_seqs + 1] int32
     context_lens: np.ndarray       # [num_seqs] int32
@@ -135,18 +135,21 @@ class Step:
         return int(self.slot_mapping.size)
 
 
-KIND_IDLE, KIND_PROMPT, KIND_DECODE = 0, 1, 2
+KIND_IDLE, KIND_PROMPT, KIND_DECODE, KIND_MIXED = 0, 1, 2, 3
 
 
 class StepScheduler:
-    """Alternating all-prompt / all-decode step planner over a KvManager."""
+    """Step planner over a KvManager: alternating all-prompt / all-decode
+    steps, or with ``mixed`` one batch per step (every decoding sequence's
+    token, then prompt chunks in the rest of the token budget)."""
 
     def __init__(self, kvm: KvManager, max_batched_tokens: int = 4096, max_chunk_tokens: int = 512,
                  max_decode_steps: int = 8, min_decode_steps: int = 1, max_seqs: int = 256,
-                 max_blocks_per_seq: int = 512):
+                 max_blocks_per_seq: int = 512, mixed: bool = False):
         self._lib = load_library()
         self.kvm = kvm
-        cfg = PaSchedConfig(max_batched_tokens, max_chunk_tokens, max_decode_steps, min_decode_steps, max_seqs)
+        cfg = PaSchedConfig(max_batched_tokens, max_chunk_tokens, max_decode_steps, min_decode_steps, max_seqs,
+                            1 if mixed else 0)
         h = self._lib.pa_sched_create(kvm.handle, ctypes.byref(cfg))
         if not h:
             _check("pa_sched_create", -3)

@@ -46,7 +46,7 @@ class OracleBackend:
     def step(self, st, keys, vals, qs, scale, partition_size):
         f = lambda x: W.storage_to_f32(x, W.BF16).astype(np.float64)
         self.kc, self.vc = oracle.kv_cache_write(self.kc, self.vc, f(keys), f(vals), st.slot_mapping)
-        if st.kind == 1:
+        if st.kind in (1, 3):  # prompt or mixed: decode rows are chunks of one token
             return oracle.paged_prefill(f(qs), st.query_start_loc, self.kc, self.vc, st.block_tables,
                                         st.context_lens, scale)
         return oracle.paged_decode(f(qs), self.kc, self.vc, st.block_tables, st.context_lens, scale)
@@ -76,7 +76,7 @@ class LibraryBackend:
         tables = t.from_numpy(st.block_tables.copy()).cuda()
         lens = t.from_numpy(st.context_lens.copy()).cuda()
         P.pa_kv_cache_write(dev_k, dev_v, self.kc, self.vc, slots)
-        if st.kind == P.KIND_PROMPT:
+        if st.kind in (P.KIND_PROMPT, P.KIND_MIXED):  # mixed: decode rows are chunks of one token
             qstart = t.from_numpy(st.query_start_loc.copy()).cuda()
             out = P.pa_prefill_chunk(dev_q, qstart, self.kc, self.vc, tables, lens, scale, st.max_query_len,
                                      st.max_context_len)
@@ -87,7 +87,7 @@ class LibraryBackend:
 
 
 def serve_and_check(trace, backend, partition_size=0, max_batched_tokens=256, max_chunk_tokens=128,
-                    max_seqs=8, max_blocks_per_seq=32, tag="", grow_at=None):
+                    max_seqs=8, max_blocks_per_seq=32, tag="", grow_at=None, mixed=False):
     """Runs the trace to completion; returns a summary dict.  ``grow_at``
     maps a step index to a larger pool size: before that step the backend's
     pool is moved into the larger allocation and the manager extended."""
@@ -95,7 +95,7 @@ def serve_and_check(trace, backend, partition_size=0, max_batched_tokens=256, ma
 
     m = P.KvManager(trace.num_blocks, trace.block_size)
     s = P.StepScheduler(m, max_batched_tokens=max_batched_tokens, max_chunk_tokens=max_chunk_tokens,
-                        max_seqs=max_seqs, max_blocks_per_seq=max_blocks_per_seq)
+                        max_seqs=max_seqs, max_blocks_per_seq=max_blocks_per_seq, mixed=mixed)
     for rid, prompt in trace.prompts.items():
         s.add_request(rid, prompt, trace.max_new[rid])
     H, Hkv, D = trace.num_heads, trace.num_kv_heads, trace.head_dim
@@ -112,7 +112,7 @@ def serve_and_check(trace, backend, partition_size=0, max_batched_tokens=256, ma
             log(f"serving{tag}: pool grows to {grow_at[step]} blocks before step {step}")
             backend.grow(m, grow_at[step])
         st = s.next_step()
-        assert st.kind in (P.KIND_PROMPT, P.KIND_DECODE)
+        assert st.kind in ((P.KIND_PROMPT, P.KIND_DECODE, P.KIND_MIXED) if mixed else (P.KIND_PROMPT, P.KIND_DECODE))
         kinds.append(st.kind)
         ids = st.request_ids.tolist()
         qsl = st.query_start_loc.astype(np.int64)

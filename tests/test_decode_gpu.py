@@ -129,6 +129,32 @@ def test_stages_equal_fused_call():
     assert np.array_equal(to_host_bits(out), to_host_bits(fused))
 
 
+@pytest.mark.parametrize("dtype,group", [(W.BF16, 4), (W.BF16, 8), (W.F32, 4)])
+def test_reduce_ignores_stale_workspace(dtype, group):
+    """Workspace slots past a row's partitions are never written; the reduce
+    loads some of them before it knows the row's partition count and must
+    select them out.  A workspace full of NaN bit patterns gives the same
+    bits as a zeroed one."""
+    import paged_attention_kv_cache_amd as P
+    t = torch()
+    case = W.random_decode(91 + group, [1, 40, 513, 700, 2049, 64], num_heads=8 * group, num_kv_heads=8,
+                           head_dim=128, block_size=16, dtype=dtype)
+    dev = DeviceCase(case)
+    dev.write()
+    ref = oracle_decode(case)
+    ps, mcl = 64, 4096  # 64 slots per row, most of them unused
+    need = P.pa_decode_workspace_bytes(6, 8 * group, 128, mcl, ps)
+    bits = []
+    for fill in (0x00, 0xFF):
+        log(f"decode {dtype} G={group} partition={ps} workspace filled with {fill:#x}")
+        ws = t.full((need,), fill, dtype=t.uint8, device="cuda")
+        out = dev.decode(ps, max_context_len=mcl, workspace=ws)
+        t.cuda.synchronize()
+        assert_close(to_host_f32(out, dtype), ref, dtype, f"{dtype} G{group} fill {fill:#x}")
+        bits.append(to_host_bits(out).copy())
+    assert np.array_equal(bits[0], bits[1])
+
+
 def test_no_cross_sequence_leakage():
     """Each sequence's output in a batch equals the same sequence run alone,
     bit for bit (same kernel configuration)."""

@@ -230,7 +230,7 @@ def sampled_token(rid, pos):
     return (rid * 7919 + pos * 31) % 30000 + 1
 
 
-def run_serving(requests, num_blocks, block_size, max_steps=20000, **cfg):
+def run_serving(requests, num_blocks, block_size, max_steps=20000, check_all_decoders=False, **cfg):
     """Drives the scheduler to completion over a simulated pool and checks
     every step.  Returns (kinds per step, final sequences, manager stats,
     number of recomputed sequences, i.e. preemptions)."""
@@ -248,17 +248,34 @@ def run_serving(requests, num_blocks, block_size, max_steps=20000, **cfg):
     recomputed = set()
     max_chunk = cfg.get("max_chunk_tokens", 512)
     max_batched = cfg.get("max_batched_tokens", 4096)
+    mixed = cfg.get("mixed", False)
+    decoding = set()  # requests whose next token is a decode token
     for _ in range(max_steps):
         w, a, f = s.counts()
         if w == 0 and a == 0:
             break
         st = s.next_step()
-        assert st.kind in (1, 2), f"idle step with {w} waiting and {a} admitted"
+        assert st.kind in ((1, 2, 3) if mixed else (1, 2)), f"idle step with {w} waiting and {a} admitted"
         kinds.append(st.kind)
         qlen = np.diff(st.query_start_loc)
         assert st.query_start_loc[0] == 0 and qlen.sum() == st.num_tokens
         assert len(set(st.request_ids.tolist())) == st.num_seqs
-        if st.kind == 2:
+        ids = st.request_ids.tolist()
+        if mixed:
+            # all rows under the one token budget, prompt chunks within the
+            # chunk limit
+            assert st.num_tokens <= max_batched and qlen.max() <= max_chunk and (qlen >= 1).all()
+            recomputed |= {rid for j, rid in enumerate(ids) if qlen[j] > 1 and gen[rid] > 0}
+            if check_all_decoders:
+                # no preemption possible: decode rows (one token each, requests
+                # that finished their prompt) come first and none is left out
+                is_dec = [rid in decoding for rid in ids]
+                nd = sum(is_dec)
+                assert all(is_dec[:nd]) and not any(is_dec[nd:]), "decode rows must come first"
+                assert (qlen[:nd] == 1).all()
+                assert st.kind == (2 if nd == len(ids) else (1 if nd == 0 else 3))
+                assert decoding <= set(ids), f"decoders left out: {decoding - set(ids)}"
+        elif st.kind == 2:
             assert (qlen == 1).all()
         else:
             assert (qlen >= 1).all() and qlen.max() <= max_chunk and st.num_tokens <= max_batched
@@ -297,13 +314,16 @@ def run_serving(requests, num_blocks, block_size, max_steps=20000, **cfg):
         nfin = 0
         for i, rid in enumerate(ids):
             if ctxs[i] < len(expected[rid]):
+                decoding.discard(rid)  # a prompt (or its recomputation) still running
                 continue
             if gen[rid] >= requests[rid][1]:
                 done_seqs[rid] = expected[rid]
+                decoding.discard(rid)
                 nfin += 1
             else:
                 expected[rid].append(samp[i])
                 gen[rid] += 1
+                decoding.add(rid)
         assert fin == nfin
     else:
         raise AssertionError("serving did not finish")
@@ -323,6 +343,28 @@ def test_serving_alternates_and_finishes():
     for rid, (p, n) in reqs.items():
         assert len(seqs[rid]) == len(p) + n
     assert 1 in kinds and 2 in kinds
+
+
+def test_mixed_steps_carry_every_decoder():
+    """Mixed policy: each step holds every decoding sequence's token first,
+    then prompt chunks in the rest of the budget; with a pool large enough
+    that nobody is preempted, no decoder is ever left out."""
+    rng = np.random.default_rng(5)
+    reqs = {i: (toks(int(rng.integers(5, 300)), base=i * 17), int(rng.integers(1, 12))) for i in range(24)}
+    kinds, seqs, _, _ = run_serving(reqs, 1000, 16, max_chunk_tokens=64, max_batched_tokens=256, max_seqs=32,
+                                    mixed=True, check_all_decoders=True)
+    assert sorted(seqs) == sorted(reqs)
+    for rid, (p, n) in reqs.items():
+        assert len(seqs[rid]) == len(p) + n
+    assert 3 in kinds and 2 in kinds
+
+
+def test_mixed_steps_under_pool_pressure():
+    reqs = {i: (toks(60, base=i * 3), 120) for i in range(12)}
+    kinds, seqs, stats, npre = run_serving(reqs, 40, 16, max_chunk_tokens=64, max_batched_tokens=512,
+                                           max_seqs=12, mixed=True)
+    assert all(len(seqs[i]) == 180 for i in range(12))
+    assert npre > 0 and stats["prefix_hit_tokens"] > 0
 
 
 def test_decode_runs_bounded_by_max_decode_steps():

@@ -29,3 +29,15 @@ def test_serving_with_pool_growth_oracle_backend():
                         max_blocks_per_seq=16, tag="-cpu-grow", grow_at={4: 24, 9: 64})
     assert r["stats"]["num_blocks"] == 64
     assert r["worst"] < 1e-5
+
+
+def test_mixed_batch_serving_with_oracle_backend():
+    """One batch per step (decode rows, then prompt chunks) through the
+    prefill path: every row still equals the dense attention."""
+    tr = W.serving_trace(seed=6004, num_requests=8, num_blocks=16, prompt_range=(10, 150), new_range=(2, 10),
+                         shared_prefix=32, num_heads=4, num_kv_heads=2, head_dim=64)
+    r = serve_and_check(tr, OracleBackend(tr), max_batched_tokens=128, max_chunk_tokens=64, max_seqs=6,
+                        max_blocks_per_seq=16, tag="-cpu-mixed", mixed=True)
+    assert 3 in r["kinds"]
+    assert r["recomputed"] > 0
+    assert r["worst"] < 1e-5

@@ -34,3 +34,13 @@ def test_serving_with_pool_growth():
     r = serve_and_check(tr, LibraryBackend(tr), partition_size=64, grow_at={6: 56, 14: 160}, tag="-grow")
     assert r["stats"]["num_blocks"] == 160
     assert r["worst"] <= BF16_MAX_ABS
+
+
+def test_mixed_batch_serving_matches_dense_oracle():
+    """Mixed steps (every decode row, then prompt chunks, one prefill launch)
+    through the library's kernels match the oracle's dense attention."""
+    tr = W.serving_trace(seed=6005, num_requests=12, num_blocks=64)
+    r = serve_and_check(tr, LibraryBackend(tr), partition_size=64, tag="-mixed", mixed=True)
+    assert 3 in r["kinds"]
+    assert r["worst"] <= BF16_MAX_ABS
+    log(f"serving mixed: {r['steps']} steps ({r['kinds'].count(3)} mixed), worst max-abs {r['worst']:.2e}")
