@@ -303,7 +303,9 @@ int pa_decode_reduce(void *out, int32_t dtype, int32_t num_seqs, int32_t num_hea
  *                    stays correct and only the sharing is lost.
  *   workspace      : device, >= pa_decode_cascade_workspace_bytes(...)
  *                    bytes; scratch.
- * bf16 only, v_head_dim equal to head_dim (PA_ERR_UNSUPPORTED otherwise).
+ * bf16 only (PA_ERR_UNSUPPORTED otherwise).  The workspace size takes the
+ * width of the output rows (the cache's v_head_dim) as head_dim, as
+ * pa_decode_workspace_bytes does.
  * --------------------------------------------------------------------- */
 size_t pa_decode_cascade_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
                                          int32_t max_context_len, int32_t partition_size);

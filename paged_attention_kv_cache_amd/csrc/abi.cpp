@@ -429,9 +429,6 @@ int pa_decode_cascade(const pa_kv_cache *cache, void *out, const void *q, int32_
   if (st) return st;
   if (cache->dtype != PA_DTYPE_BF16)
     return fail(PA_ERR_UNSUPPORTED, "cascade decode is bf16 only (dtype %d)", cache->dtype);
-  if (v_dim(cache) != cache->head_dim)
-    return fail(PA_ERR_UNSUPPORTED, "cascade decode needs v_head_dim equal to head_dim (%d vs %d)",
-                v_dim(cache), cache->head_dim);
   if (num_groups < 0 || (num_seqs > 0 && num_groups == 0))
     return fail(PA_ERR_SHAPE, "num_groups %d: every sequence belongs to one group", num_groups);
   if (num_groups > kMaxGridYZ) return fail(PA_ERR_SHAPE, "num_groups %d above %d", num_groups, kMaxGridYZ);
@@ -443,7 +440,7 @@ int pa_decode_cascade(const pa_kv_cache *cache, void *out, const void *q, int32_
     return fail(PA_ERR_SHAPE, "max_group_size %d not in [1, num_seqs %d]", max_group_size, num_seqs);
   if (max_shared_len < 0) return fail(PA_ERR_SHAPE, "max_shared_len %d must be >= 0", max_shared_len);
   const int P = cascade_slots(max_context_len, partition_size);
-  const size_t need = pa_decode_cascade_workspace_bytes(num_seqs, num_heads, cache->head_dim, max_context_len,
+  const size_t need = pa_decode_cascade_workspace_bytes(num_seqs, num_heads, v_dim(cache), max_context_len,
                                                         partition_size);
   if (!workspace) return fail(PA_ERR_WORKSPACE, "workspace is NULL; %zu bytes needed", need);
   if (workspace_bytes < need) return fail(PA_ERR_WORKSPACE, "workspace_bytes %zu < %zu needed", workspace_bytes, need);

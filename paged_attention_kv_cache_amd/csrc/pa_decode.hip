@@ -368,8 +368,8 @@ decode_partition_kernel(const DecodeKernelArgs a) {
 #ifndef PA_DECODE_UNROLL
 #define PA_DECODE_UNROLL 8
 #endif
-#ifndef PA_DECODE_UNROLL_G8
-#define PA_DECODE_UNROLL_G8 4  // groups of eight heads: fewer loads in flight, fewer registers
+#ifndef PA_DECODE_UNROLL_WIDE
+#define PA_DECODE_UNROLL_WIDE 4  // more than 32 accumulators per lane: fewer loads in flight, fewer registers
 #endif
 #ifndef PA_DECODE_WAVES
 #define PA_DECODE_WAVES 4
@@ -540,22 +540,48 @@ __device__ __forceinline__ void chunk_load(uint4 (&buf)[U], const size_t (&off)[
   }
 }
 
+// The same for a V slice of VW words (8, 16 or 32 bytes) per lane.
+template <int U, int VW>
+__device__ __forceinline__ void chunk_load_words(uint32_t (&buf)[U][VW], const size_t (&off)[U],
+                                                 const uint16_t *base, uint32_t lane_bytes) {
+  typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const char *ptr = reinterpret_cast<const char *>(base + off[u]) + lane_bytes;
+    if constexpr (VW == 2) {
+      const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t *>(ptr));
+      buf[u][0] = v.x, buf[u][1] = v.y;
+    } else {
+#pragma unroll
+      for (int i = 0; i < VW / 4; ++i) {
+        const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(ptr) + i);
+        buf[u][4 * i] = v.x, buf[u][4 * i + 1] = v.y, buf[u][4 * i + 2] = v.z, buf[u][4 * i + 3] = v.w;
+      }
+    }
+  }
+}
+
 // Per-wave online softmax of the G query heads of kv head `kvh` over the
 // tokens p0 .. p1-1 of sequence `seq`.  The wave takes chunks of CH tokens
 // c = wave, wave + W, ...; on return m (base-2 units) and l hold the wave's
 // running max and sum of head col % G, acc the wave's P.V sums (rows already
-// summed, valid in every lane).
-template <int D, int G>
+// summed, valid in every lane).  D is the key head dim, DV the value head
+// dim: the L lanes that read a token's K row (16 bytes each) also read its
+// V row, EV = DV / L elements each (8, 16 or 32 bytes).
+template <int D, int DV, int G>
 struct Bf16Decode {
-  static constexpr int L = D / 8;   // lanes per token row (8 bf16 per lane)
+  static constexpr int L = D / 8;   // lanes per token row (8 bf16 of K per lane)
   static constexpr int R = 64 / L;  // token rows per load instruction
-  static constexpr int U = (G == 8) ? PA_DECODE_UNROLL_G8 : PA_DECODE_UNROLL;
+  static constexpr int EV = DV / L; // V elements per lane
+  static constexpr int VW = EV / 2; // V words (bf16 pairs) per lane
+  static constexpr int U = (G * EV > 32) ? PA_DECODE_UNROLL_WIDE : PA_DECODE_UNROLL;
   static constexpr int CH = R * U;  // tokens per wave step
   static constexpr int W = PA_DECODE_WAVES;
   static_assert(U % 2 == 0, "tokens are paired for the P.V dot products");
+  static_assert(VW == 2 || VW == 4 || VW == 8, "8, 16 or 32 bytes of V per lane");
 
   __device__ static __forceinline__ void attend(const DecodeKernelArgs &a, int seq, int kvh, int p0, int p1,
-                                                int wave, int lane, float &m, float &l, float (&acc)[G][8]) {
+                                                int wave, int lane, float &m, float &l, float (&acc)[G][EV]) {
     const int row = lane / L;
     const int col = lane % L;
     uint32_t qp[G][4];
@@ -574,8 +600,9 @@ struct Bf16Decode {
     const float sl = a.scale_log2;
     const size_t slot_stride = (size_t)a.num_kv_heads * D;
     const uint16_t *kbase = static_cast<const uint16_t *>(a.k_cache) + (size_t)kvh * D;
-    const uint16_t *vbase = static_cast<const uint16_t *>(a.v_cache) + (size_t)kvh * D;
+    const uint16_t *vbase = static_cast<const uint16_t *>(a.v_cache) + (size_t)kvh * DV;
     const uint32_t lane_bytes = (uint32_t)(((size_t)row * slot_stride + (size_t)col * 8) * 2);
+    const uint32_t vlane_bytes = (uint32_t)(((size_t)row * a.num_kv_heads * DV + (size_t)col * EV) * 2);
     const int32_t *bt = a.block_tables + (size_t)seq * a.max_blocks_per_seq;
     const int shift = a.block_shift;
     const int bs_mask = (1 << shift) - 1;
@@ -585,7 +612,7 @@ struct Bf16Decode {
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+      for (int e = 0; e < EV; ++e) acc[h][e] = 0.f;
 
     const int ntok = p1 - p0;
     const int nchunks = ntok > 0 ? (ntok + CH - 1) / CH : 0;
@@ -595,12 +622,24 @@ struct Bf16Decode {
       bool ok[U];
       chunk_rows<U, R>(off, ok, bt, cbase, p1, shift, bs_mask, a.num_blocks, slot_stride,
                        a.max_blocks_per_seq);
-      uint4 kr[U], vr[U];
+      uint4 kr[U];
+      uint32_t vr[U][VW];
 #if PA_DECODE_PRIO
       __builtin_amdgcn_s_setprio(3);
 #endif
       chunk_load<U>(kr, off, kbase, lane_bytes);
-      chunk_load<U>(vr, off, vbase, lane_bytes);
+      if constexpr (DV == D) {
+        uint4 v4[U];
+        chunk_load<U>(v4, off, vbase, lane_bytes);
+#pragma unroll
+        for (int u = 0; u < U; ++u) vr[u][0] = v4[u].x, vr[u][1] = v4[u].y, vr[u][2] = v4[u].z, vr[u][3] = v4[u].w;
+      } else {
+        // V's slot stride is DV / D times K's: the same slot, scaled offset
+        size_t voff[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) voff[u] = (DV > D) ? off[u] << 1 : off[u] >> 1;
+        chunk_load_words<U, VW>(vr, voff, vbase, vlane_bytes);
+      }
 #if PA_DECODE_PRIO
       __builtin_amdgcn_s_setprio(0);
 #endif
@@ -639,7 +678,7 @@ struct Bf16Decode {
 #pragma unroll
         for (int h = 0; h < G; ++h)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) acc[h][e] *= ah[h];
+          for (int e = 0; e < EV; ++e) acc[h][e] *= ah[h];
       }
       float p[U];
       float psum = 0.f;
@@ -658,19 +697,20 @@ struct Bf16Decode {
       if (!full) {
 #pragma unroll
         for (int u = 0; u < U; ++u)
-          if (!valid[u]) vr[u] = make_uint4(0, 0, 0, 0);
+          if (!valid[u]) {
+#pragma unroll
+            for (int j = 0; j < VW; ++j) vr[u][j] = 0;
+          }
       }
 #pragma unroll
       for (int u = 0; u < U; u += 2) {
-        uint32_t vp[8];
-        vp[0] = interleave_lo(vr[u].x, vr[u + 1].x);
-        vp[1] = interleave_hi(vr[u].x, vr[u + 1].x);
-        vp[2] = interleave_lo(vr[u].y, vr[u + 1].y);
-        vp[3] = interleave_hi(vr[u].y, vr[u + 1].y);
-        vp[4] = interleave_lo(vr[u].z, vr[u + 1].z);
-        vp[5] = interleave_hi(vr[u].z, vr[u + 1].z);
-        vp[6] = interleave_lo(vr[u].w, vr[u + 1].w);
-        vp[7] = interleave_hi(vr[u].w, vr[u + 1].w);
+        // element 2j (2j+1) of the two tokens in one bf16 pair
+        uint32_t vp[EV];
+#pragma unroll
+        for (int j = 0; j < VW; ++j) {
+          vp[2 * j] = interleave_lo(vr[u][j], vr[u + 1][j]);
+          vp[2 * j + 1] = interleave_hi(vr[u][j], vr[u + 1][j]);
+        }
         // this lane's head's two weights, rounded to bf16 and packed, then
         // the packed pair of every head from the lane that owns it
         uint32_t pk[G];
@@ -678,7 +718,7 @@ struct Bf16Decode {
 #pragma unroll
         for (int h = 0; h < G; ++h)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) acc[h][e] = dot2_bf16(pk[h], vp[e], acc[h][e]);
+          for (int e = 0; e < EV; ++e) acc[h][e] = dot2_bf16(pk[h], vp[e], acc[h][e]);
       }
     }
 
@@ -686,7 +726,7 @@ struct Bf16Decode {
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[h][e] = rows_sum<L>(acc[h][e]);
+      for (int e = 0; e < EV; ++e) acc[h][e] = rows_sum<L>(acc[h][e]);
     l = rows_sum<L>(l);
   }
 
@@ -699,13 +739,15 @@ struct Bf16Decode {
   // whose block id is outside the pool is left out and not written, as the
   // separate cache write and the partition loop would leave it.
   __device__ static __forceinline__ void attend_new(const DecodeKernelArgs &a, int seq, int kvh, int pos,
-                                                    int lane, float &m, float &l, float (&acc)[G][8]) {
+                                                    int lane, float &m, float &l, float (&acc)[G][EV]) {
     const int col = lane % L;
     const int blk = read_only(a.block_tables + (size_t)seq * a.max_blocks_per_seq)[pos >> a.block_shift];
     if ((unsigned)blk >= (unsigned)a.num_blocks) return;
     const size_t in_row = ((size_t)seq * a.num_kv_heads + kvh) * D + (size_t)col * 8;
+    const size_t in_vrow = ((size_t)seq * a.num_kv_heads + kvh) * DV + (size_t)col * EV;
     const uint4 kc = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.new_k) + in_row);
-    const uint4 vc = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.new_v) + in_row);
+    Vec<bf16_t, EV> vc;
+    vc.load(static_cast<const bf16_t *>(a.new_v) + in_vrow);
     const uint4 *qv = reinterpret_cast<const uint4 *>(
         static_cast<const uint16_t *>(a.q) + ((size_t)seq * a.num_heads + (size_t)kvh * G) * D);
     float d[G];
@@ -723,8 +765,8 @@ struct Bf16Decode {
     const float p = fast_exp2(s - m_new);
     m = m_new;
     l = l * alpha + p;
-    float vf[8];
-    Chunk<bf16_t>::widen(vc, vf);
+    float vf[EV];
+    vc.widen(vf);
     float ah[G], pb[G];
     every_head<G>(alpha, col, ah);
     every_head<G>(p, col, pb);
@@ -732,13 +774,21 @@ struct Bf16Decode {
     for (int h = 0; h < G; ++h) {
       const float pr = bf16_lo(pack_bf16x2_rne(pb[h], 0.f));  // the weight rounded to bf16
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(pr, vf[e], acc[h][e] * ah[h]);
+      for (int e = 0; e < EV; ++e) acc[h][e] = fmaf(pr, vf[e], acc[h][e] * ah[h]);
     }
     if (lane < L) {
       const size_t slot = ((size_t)blk << a.block_shift) + (size_t)(pos & ((1 << a.block_shift) - 1));
       const size_t at = slot * a.num_kv_heads * D + (size_t)kvh * D + (size_t)col * 8;
+      const size_t vat = slot * a.num_kv_heads * DV + (size_t)kvh * DV + (size_t)col * EV;
       *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(const_cast<void *>(a.k_cache)) + at) = kc;
-      *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(const_cast<void *>(a.v_cache)) + at) = vc;
+      uint32_t *vdst = reinterpret_cast<uint32_t *>(static_cast<uint16_t *>(const_cast<void *>(a.v_cache)) + vat);
+      if constexpr (VW == 2) {
+        *reinterpret_cast<uint2 *>(vdst) = make_uint2(vc.w[0], vc.w[1]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < VW / 4; ++i)
+          reinterpret_cast<uint4 *>(vdst)[i] = make_uint4(vc.w[4 * i], vc.w[4 * i + 1], vc.w[4 * i + 2], vc.w[4 * i + 3]);
+      }
     }
   }
 
@@ -746,17 +796,17 @@ struct Bf16Decode {
   struct Stage {
     float m[W][G];
     float l[W][G];
-    float o[W][G][D];
+    float o[W][G][DV];
   };
 
   __device__ static __forceinline__ void stage(Stage &sm, int wave, int lane, float m, float l,
-                                               const float (&acc)[G][8]) {
+                                               const float (&acc)[G][EV]) {
     const int col = lane % L;
     if (lane < L) {
 #pragma unroll
       for (int h = 0; h < G; ++h)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) sm.o[wave][h][col * 8 + e] = acc[h][e];
+        for (int e = 0; e < EV; ++e) sm.o[wave][h][col * EV + e] = acc[h][e];
     }
     if (lane < G) {  // lane c of row 0 owns head c
       sm.m[wave][lane] = m;
@@ -764,11 +814,11 @@ struct Bf16Decode {
     }
   }
 
-  // combine of output i = h * D + d over the staged waves: M = max, o and
+  // combine of output i = h * DV + d over the staged waves: M = max, o and
   // the sum scaled to M (both 0 when every wave is empty)
   __device__ static __forceinline__ void combine(const Stage &sm, int i, float &M, float &o, float &lt) {
-    const int h = i / D;
-    const int d = i - h * D;
+    const int h = i / DV;
+    const int d = i - h * DV;
     M = sm.m[0][h];
 #pragma unroll
     for (int w = 1; w < W; ++w) M = fmaxf(M, sm.m[w][h]);
@@ -840,11 +890,12 @@ __device__ __forceinline__ bool size_order_item(const DecodeKernelArgs &a, int i
   return true;
 }
 
-template <int D, int G>
+template <int D, int DV, int G>
 __global__ void __launch_bounds__(64 * PA_DECODE_WAVES)
-__attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 : 1)))  // four work-groups per CU up to G = 4
+// four work-groups per CU while the accumulators fit (up to G = 4 at DV <= D)
+__attribute__((amdgpu_waves_per_eu((G <= 4 && G * (DV / (D / 8)) <= 32) ? 4 : 1)))
 decode_partition_bf16_kernel(const DecodeKernelArgs a) {
-  using K = Bf16Decode<D, G>;
+  using K = Bf16Decode<D, DV, G>;
   constexpr int W = K::W;
 #if PA_DECODE_ORDER == 3
   const int kvh = blockIdx.x;
@@ -892,7 +943,7 @@ decode_partition_bf16_kernel(const DecodeKernelArgs a) {
   // fused append: the newest token comes from the input rows, in wave 0,
   // after the cached tokens
   const bool append = a.new_k != nullptr && !cascade && part == nparts - 1 && ctx > 0;
-  float m, l, acc[G][8];
+  float m, l, acc[G][K::EV];
   K::attend(a, seq, kvh, p0, append ? p1 - 1 : p1, wave, lane, m, l, acc);
   if (append && wave == 0) K::attend_new(a, seq, kvh, ctx - 1, lane, m, l, acc);
 
@@ -901,17 +952,17 @@ decode_partition_bf16_kernel(const DecodeKernelArgs a) {
   __syncthreads();
 
   const bool direct = !cascade && nparts == 1;
-  for (int i = threadIdx.x; i < G * D; i += 64 * W) {
+  for (int i = threadIdx.x; i < G * DV; i += 64 * W) {
     float M, o, lt;
     K::combine(sm, i, M, o, lt);
-    const int head = kvh * G + i / D;
-    const int d = i % D;
+    const int head = kvh * G + i / DV;
+    const int d = i % DV;
     if (direct) {
       const float r = (lt > 0.f) ? o / lt : 0.f;
-      store_one<bf16_t>(a.out, ((size_t)seq * a.num_heads + head) * D + d, r);
+      store_one<bf16_t>(a.out, ((size_t)seq * a.num_heads + head) * DV + d, r);
     } else {
       const size_t idx = ((size_t)seq * a.num_heads + head) * a.max_partitions + slot;
-      a.ws_o[idx * D + d] = o;
+      a.ws_o[idx * DV + d] = o;
       if (d == 0) {
         a.ws_m[idx] = M;
         a.ws_l[idx] = lt;
@@ -1084,14 +1135,14 @@ template <typename T, int D, int DV, int G>
 static hipError_t launch_partition_t(const DecodeArgs &a, hipStream_t stream) {
   const DecodeKernelArgs k = make_kernel_args(a);
   dim3 grid(a.max_partitions, a.cache.num_kv_heads, a.num_seqs);
-  if constexpr (std::is_same<T, bf16_t>::value && D == DV) {
+  if constexpr (std::is_same<T, bf16_t>::value) {
     if (a.query_start_loc) return hipErrorNotSupported;  // prefill rows run on the generic kernel only
 #if PA_DECODE_ORDER == 1 || PA_DECODE_ORDER == 3
     grid = dim3(a.cache.num_kv_heads, a.num_seqs, a.max_partitions);
 #endif
-    hipLaunchKernelGGL((decode_partition_bf16_kernel<D, G>), grid, dim3(64 * PA_DECODE_WAVES), 0, stream, k);
+    hipLaunchKernelGGL((decode_partition_bf16_kernel<D, DV, G>), grid, dim3(64 * PA_DECODE_WAVES), 0, stream, k);
   } else {
-    // (cascade launches are bf16 with D == DV: never here)
+    // (cascade launches are bf16: never here)
     hipLaunchKernelGGL((decode_partition_kernel<T, D, DV, G>), grid, dim3(DecodeShape<T, D>::kThreads), 0,
                        stream, k);
   }
@@ -1121,7 +1172,7 @@ static hipError_t launch_partition_d(const DecodeArgs &a, hipStream_t stream) {
 
 bool decode_fast_path(const DecodeArgs &a) {
   const int g = a.cache.num_kv_heads > 0 ? a.num_heads / a.cache.num_kv_heads : 0;
-  return a.cache.dtype == 1 && g >= 1 && g <= 8 && a.cache.head_dim == a.cache.head_dim_v &&
+  return a.cache.dtype == 1 && g >= 1 && g <= 8 &&
          !a.query_start_loc;
 }
 

@@ -242,8 +242,8 @@ def test_copy_blocks_validation(lib):
 
 def test_value_head_dim_validation(lib):
     """A value head dim of its own (0 = the key head dim): attention takes
-    64 or 128, the workspace is sized by it, the copy checks it, and
-    cascade decode needs it equal to the key head dim."""
+    64 or 128, the workspace is sized by it (cascade decode's too), and the
+    copy checks it."""
     assert ctypes.sizeof(_binding.PaKvCache) == 2 * 8 + 6 * 4
     for dv in (32, 96, 256):
         assert decode(lib, cache(dv=dv)) == -5
@@ -262,10 +262,11 @@ def test_value_head_dim_validation(lib):
     cp = lambda s, d: lib.pa_kv_cache_copy_blocks(ctypes.byref(s), ctypes.byref(d), None, None, 0, None)
     assert cp(cache(dv=64), cache(dv=128)) == -3 and "v_head_dim" in msg()
     assert cp(cache(dv=0), cache(dv=128)) == 0
-    # cascade decode: equal dims only
+    # cascade decode: the partials take the value head dim
+    need_v = P.pa_decode_cascade_workspace_bytes(4, 32, 64, 1000, 256)
+    assert need_v < P.pa_decode_cascade_workspace_bytes(4, 32, 128, 1000, 256)
     assert lib.pa_decode_cascade(ctypes.byref(cache(dv=64)), FAKE, FAKE, 4, 32, FAKE, 8, FAKE, 1000, 0.1, 256, 2,
-                                 FAKE, FAKE, 2, 512, FAKE, 10 ** 9, None) == -8
-    assert "v_head_dim" in msg()
+                                 FAKE, FAKE, 2, 512, FAKE, need_v - 1, None) == -7 and f"{need_v} needed" in msg()
     # prefill takes unequal dims
     assert lib.pa_prefill_chunk(ctypes.byref(cache(dv=64)), FAKE, FAKE, FAKE, 2, 32, 0, 32, FAKE, 8, FAKE, 100,
                                 0.1, None) == 0

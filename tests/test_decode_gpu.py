@@ -340,6 +340,31 @@ def test_cascade_prefix_shared_full(name):
         print(f"cascade {name} ps={ps}: max-abs {mx:.2e} mean-abs {mean:.2e}")
 
 
+@pytest.mark.parametrize("dims", [(128, 64), (64, 128)])
+@pytest.mark.parametrize("group", [2, 8])
+def test_cascade_separate_value_dim(dims, group):
+    """Cascade decode with a value head dim of its own: the shared pass and
+    the partitions write partials of the value width."""
+    D, Dv = dims
+    sizes = [3, 40, 5]
+    starts = np.cumsum([0] + sizes).tolist()
+    group_of = [g for g, n in enumerate(sizes) for _ in range(n)]
+    bs, shared_blocks = 16, 10
+    rng = np.random.default_rng(77 + group + D)
+    ctx = [int(x) for x in rng.integers(shared_blocks * bs + 1, 900, size=sum(sizes))]
+    ctx[0] = 3 * bs                            # a row that ends inside the shared part
+    hkv = 2
+    case = W.random_decode(900 + group + D, ctx, num_heads=hkv * group, num_kv_heads=hkv, head_dim=D, block_size=bs,
+                           dtype=W.BF16, shared_blocks=shared_blocks, group_of=group_of, v_head_dim=Dv)
+    ref = oracle_decode(case)
+    assert ref.shape[-1] == Dv
+    shared = [shared_blocks * bs, shared_blocks * bs, 4 * bs]
+    for ps in (64, 256):
+        log(f"cascade D={D} Dv={Dv} G={group} partition={ps}")
+        got = _cascade(case, starts, shared, ps)
+        assert_close(got, ref, W.BF16, f"cascade D{D} Dv{Dv} G{group} ps{ps}")
+
+
 @pytest.mark.parametrize("group", [1, 2, 4, 8])
 def test_cascade_irregular_groups(group):
     """Groups of 1, 3, 70 (two member tiles) and 6 rows; shared lengths below
@@ -409,7 +434,8 @@ def _append_rows(case):
 
 @pytest.mark.parametrize("dtype,group,dims", [(W.BF16, 1, (128, 128)), (W.BF16, 2, (64, 64)), (W.BF16, 4, (128, 128)),
                                               (W.BF16, 8, (128, 128)), (W.BF16, 8, (64, 64)), (W.F32, 4, (64, 64)),
-                                              (W.BF16, 4, (128, 64))])
+                                              (W.BF16, 4, (128, 64)), (W.BF16, 2, (64, 128)),
+                                              (W.BF16, 8, (64, 128))])
 def test_decode_append(dtype, group, dims):
     """pa_decode_append = the cache write of each sequence's newest token
     plus pa_decode: outputs within tolerance of the oracle and the pools
