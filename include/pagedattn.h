@@ -220,11 +220,10 @@ int pa_decode(const pa_kv_cache *cache, void *out, const void *q, int32_t num_se
  * pa_kv_cache_write (with slot = the slot of position context_lens[i] - 1
  * through the block table) followed by pa_decode.  [TS] section 3 appends
  * the new token's K/V to the cache and then attends with it; section 11
- * writes them through the slot mapping.  On bf16 pools with equal key and
- * value head dims the write happens inside the partition kernel: the
- * partition that holds the newest token takes its rows from key / value
- * and stores them into the slot, saving a launch; other shapes run a
- * separate write first.  Results equal pa_decode's up
+ * writes them through the slot mapping.  On bf16 pools the write happens
+ * inside the partition kernel: the partition that holds the newest token
+ * takes its rows from key / value and stores them into the slot, saving a
+ * launch; fp32 pools run a separate write first.  Results equal pa_decode's up
  * to rounding (the newest token's weight is merged last).
  *
  *   cache ... workspace_bytes : as pa_decode.
