@@ -565,7 +565,7 @@ def main():
         "kv_gbps": round(dec["achieved"], 1),
         "kv_hbm_frac": round(dec["achieved"] / HBM_PEAK_GBPS, 4),
         "roofline": {
-            "kernel": "decode_partition_bf16_kernel<128, 4>",
+            "kernel": "decode_partition_bf16_kernel<128, 128, 4>",
             "bound": "hbm",
             "achieved": round(dec["achieved"], 1),
             "peak": HBM_PEAK_GBPS,
