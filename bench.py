@@ -234,7 +234,8 @@ def bench_decode_secondary(name, ps, steps=30, groups=None, case=None):
     if case is None:
         case = W.make_config(name, poison=False)
     S, H, D = case.q.shape
-    pool_bytes = 2 * case.k_cache.nbytes
+    Dv = case.v_cache.shape[-1]  # width of the output rows and partials
+    pool_bytes = case.k_cache.nbytes + case.v_cache.nbytes
     R = max(2, int(math.ceil(2.0e9 / pool_bytes)))
     k0 = to_dev(case.k_cache, case.dtype)
     v0 = to_dev(case.v_cache, case.dtype)
@@ -242,9 +243,9 @@ def bench_decode_secondary(name, ps, steps=30, groups=None, case=None):
     q = to_dev(case.q, case.dtype)
     bt = torch.from_numpy(case.block_tables).cuda()
     cl = torch.from_numpy(case.context_lens).cuda()
-    out = torch.empty_like(q)
+    out = torch.empty((S, H, Dv), dtype=q.dtype, device="cuda")
     mcl = case.max_context_len
-    ws = torch.empty(max(P.pa_decode_workspace_bytes(S, H, D, mcl, ps), 1), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(max(P.pa_decode_workspace_bytes(S, H, Dv, mcl, ps), 1), dtype=torch.uint8, device="cuda")
 
     def part(i):
         k, v = pools[i % R]
@@ -273,7 +274,7 @@ def bench_decode_secondary(name, ps, steps=30, groups=None, case=None):
     torch.cuda.synchronize()
     t_both = e0.elapsed_time(e1) / steps
     logical = case.kv_bytes_logical()
-    row_bytes = case.num_kv_heads * case.head_dim * 2 * 2          # K+V of one token, all kv heads
+    row_bytes = case.num_kv_heads * (case.head_dim + case.v_head_dim) * 2  # K+V of one token, all kv heads
     unique_tokens = 0
     seen = set()
     for i, n in enumerate(case.context_lens.tolist()):
@@ -609,6 +610,9 @@ def main():
             # eight query heads per kv head: 64 q over the same 8 kv heads and K/V bytes
             bench_decode_secondary("decode_batch_bs32_64q_8kv", 512,
                                    case=W.decode_batch(2000, poison=False, num_heads=64)),
+            # a value head dim of its own: 128-wide keys, 64-wide values
+            bench_decode_secondary("decode_batch_bs32_k128_v64", 512,
+                                   case=W.decode_batch(2000, poison=False, v_head_dim=64)),
             bench_decode_secondary("prefix_shared_decode_bs16", 512, groups=([0, 16, 32, 48, 64], [64 * 16] * 4)),
             bench_decode_secondary("prefix_shared_decode_bs8", 512, groups=([0, 16, 32, 48, 64], [64 * 8] * 4)),
         ]

@@ -376,10 +376,11 @@ def tiny_fp32_decode(seed: int = 1000, poison: bool = True) -> DecodeCase:
 
 def decode_batch(seed: int = 2000, poison: bool = True, num_seqs: int = 32,
                  ctx_low: int = 512, ctx_high: int = 4096, fixed_ctx: Optional[int] = None,
-                 num_heads: int = 32) -> DecodeCase:
+                 num_heads: int = 32, v_head_dim: Optional[int] = None) -> DecodeCase:
     """32 sequences, 32 q / 8 kv heads, head_dim 128, block_size 32, context
     uniform in [512, 4096], pool 1.25x the blocks in use, bf16.  ``num_heads``
-    = 64 gives eight query heads per kv head over the same K/V."""
+    = 64 gives eight query heads per kv head over the same K/V;
+    ``v_head_dim`` a value head dim of its own."""
     rng = np.random.default_rng(seed)
     if fixed_ctx is not None:
         ctx = [int(fixed_ctx)] * num_seqs
@@ -388,7 +389,7 @@ def decode_batch(seed: int = 2000, poison: bool = True, num_seqs: int = 32,
     tables, nb, pad = _layout(rng, ctx, 32)
     return _finish(rng, kind="decode", name="decode_batch_bs32", dtype=BF16, Hq=num_heads, Hkv=8, D=128,
                    bs=32, ctx=ctx, tables=tables, nb=nb, pad=pad, q_rows=num_seqs,
-                   new_positions=[np.array([n - 1]) for n in ctx], poison=poison)
+                   new_positions=[np.array([n - 1]) for n in ctx], poison=poison, Dv=v_head_dim)
 
 
 def long_context_decode(seed: int = 3000, poison: bool = True, num_seqs: int = 4,
