@@ -146,6 +146,14 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
         if _lib is not None and path is None:
             return _lib
         p = path or LIB_PATH
+        # torch first: the library needs libamdhip64.so.7, which torch's own
+        # HIP runtime provides once torch is imported.  Loaded before torch,
+        # the library would bring up a second HIP runtime in the process,
+        # and whichever initialises the GPU second finds no device.
+        try:
+            import torch  # noqa: F401
+        except ImportError:
+            pass
         if not os.path.exists(p):
             raise RuntimeError(
                 f"{p} is not built; build it with `python -c \"import __graft_entry__ as g; g.build()\"` "
@@ -297,12 +305,26 @@ def _decode_args(q, k_cache, v_cache, block_tables, context_lens, out):
     return cache, S, H, Dv, out, ptrs
 
 
-def _workspace(workspace, need: int, device):
+def _on_stream(tensor, stream) -> None:
+    """A tensor allocated here and handed to kernels enqueued on ``stream``
+    (not torch's current stream) is recorded on that stream, so the caching
+    allocator does not reuse its memory before those kernels finish."""
+    if stream is None:
+        return
+    torch = _torch()
+    s = stream if isinstance(stream, torch.cuda.Stream) else torch.cuda.ExternalStream(
+        stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+    if s != torch.cuda.current_stream():
+        tensor.record_stream(s)
+
+
+def _workspace(workspace, need: int, device, stream=None):
     torch = _torch()
     if need == 0:
         return ctypes.c_void_p(0), 0
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=device)
+        _on_stream(workspace, stream)
     if not workspace.is_cuda or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous GPU tensor")
     nbytes = workspace.numel() * workspace.element_size()
@@ -321,7 +343,7 @@ def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, max
                                                                  context_lens, out)
     lib = load_library()
     need = int(lib.pa_decode_workspace_bytes(S, H, Dv, int(max_context_len), int(partition_size)))
-    p_ws, ws_bytes = _workspace(workspace, need, q.device)
+    p_ws, ws_bytes = _workspace(workspace, need, q.device, stream)
     st = _stream(stream)
     mbps = int(block_tables.shape[1])
     if _stage in ("both", "partition"):
@@ -349,7 +371,7 @@ def pa_decode_append(q, key, value, k_cache, v_cache, block_tables, context_lens
                          f"{k_cache.shape[3]}] / [{S}, {v_cache.shape[2]}, {v_cache.shape[3]}]")
     lib = load_library()
     need = int(lib.pa_decode_workspace_bytes(S, H, Dv, int(max_context_len), int(partition_size)))
-    p_ws, ws_bytes = _workspace(workspace, need, q.device)
+    p_ws, ws_bytes = _workspace(workspace, need, q.device, stream)
     code = lib.pa_decode_append(ctypes.byref(cache), p_out, p_q, _dev(key, "key", k_cache.dtype),
                                 _dev(value, "value", k_cache.dtype), S, H, p_bt, int(block_tables.shape[1]), p_cl,
                                 int(max_context_len), float(scale), int(partition_size), p_ws, ws_bytes,
@@ -394,7 +416,7 @@ def pa_decode_cascade(q, k_cache, v_cache, block_tables, context_lens, scale: fl
         raise ValueError(f"group_start {tuple(group_start.shape)} must be [{G + 1}]")
     lib = load_library()
     need = int(lib.pa_decode_cascade_workspace_bytes(S, H, Dv, int(max_context_len), int(partition_size)))
-    p_ws, ws_bytes = _workspace(workspace, need, q.device)
+    p_ws, ws_bytes = _workspace(workspace, need, q.device, stream)
     code = lib.pa_decode_cascade(ctypes.byref(cache), p_out, p_q, S, H, p_bt, int(block_tables.shape[1]), p_cl,
                                  int(max_context_len), float(scale), int(partition_size), G,
                                  _dev(group_start, "group_start", torch.int32),

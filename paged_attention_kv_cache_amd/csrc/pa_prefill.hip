@@ -11,15 +11,20 @@
 // How it maps to gfx950:
 //  * A work-group (8 waves) serves one kv head: its G query heads (8 at
 //    most) x 32-token query groups of one sequence's chunk (64 tokens for
-//    G = 4).
-//    Every K/V tile is gathered once per work-group and shared by all of
-//    its query heads through LDS.
+//    G = 4).  Every K/V tile is gathered once per work-group and shared by
+//    all of its query heads through LDS.
 //  * K/V tiles of 64 keys are gathered through the block table straight
 //    into LDS with 16-byte global-to-LDS loads (no registers, no LDS store
 //    instructions), both row-major [key][d] in swizzled 64-byte chunk
-//    groups (see TileGather).  Keys past the last position the work-group
-//    needs, and keys in an invalid block, read a zero chunk instead, so a
-//    masked key never brings a NaN into the products.
+//    groups (see TileGather).  A wave's load covers 16 keys, which lie in
+//    one block for block sizes 16 and 32, so the block id is a scalar load
+//    and the block's address a scalar sum.  Keys past the last position
+//    the work-group needs, and keys in an invalid block, read a zero chunk
+//    instead, so a masked key never brings a NaN into the products.
+//  * The scale (times log2(e), so that the softmax uses exp2) multiplies
+//    the fp32 scores: each weight is one FMA (score * scale - max) and one
+//    exp2.  A negative scale is applied as |scale| to -Q (exact in bf16),
+//    which keeps the order of the scaled scores that of the raw ones.
 //  * Scores are computed transposed, S^T = K Q^T, on
 //    v_mfma_f32_32x32x16_bf16 (A = K from LDS, B = Q^T held in registers).
 //    In the accumulator layout every lane then holds 16 keys of one query,
@@ -28,15 +33,20 @@
 //  * The weights, rounded to bf16, are already in the B-operand layout of
 //    O^T += V^T P^T, so P never goes through LDS; the A operand (V^T) comes
 //    from the row-major V tile through gfx950's transposing LDS reads.
-//  * The causal mask (bottom-right aligned) is applied only on tiles that
-//    cross the diagonal of the wave's 32 queries, by selecting -inf.
-//  * LDS holds three K and three V tiles.  In step t a wave computes the
-//    scores of tile t+1 while it runs the softmax of tile t (independent
-//    work for the matrix and vector units), then multiplies V of tile t;
-//    the loads of tile t+2 into LDS are in flight meanwhile and are waited
-//    for before the step's single barrier.
-//  * The output is rescaled only when a query's max grows by more than 2^8
-//    (the final division by the running sum makes any reference max exact).
+//  * Online softmax with a lazy reference max: the first tile of a
+//    work-group and the tiles that cross the causal diagonal take the max
+//    of their scores (and move the reference when it grows by more than
+//    2^8).  The tiles in between take no max at all: their weights are
+//    exponentials relative to the reference, and only if a lane's sum of
+//    them exceeds 2^32 (a score far above the reference) is the tile
+//    recomputed with a new reference.  The final division by the running
+//    sum makes any reference exact up to rounding.
+//  * LDS holds four K and four V tiles.  In step t a wave computes the
+//    scores of tile t+1 while it runs the exponentials of tile t
+//    (independent work for the matrix and vector units), then multiplies V
+//    of tile t; the loads of tiles t+2 and t+3 into LDS are in flight
+//    meanwhile, and those of tile t+2 are waited for before the step's
+//    single barrier.
 //  * Work ids are remapped so that each XCD serves whole kv heads of every
 //    sequence: the XCDs get equal work, and the query tiles of one
 //    (sequence, kv head), which read the same K/V, share that XCD's L2.
@@ -94,47 +104,71 @@ __device__ __forceinline__ bf16x8_t pack8(const f32x16_t &s, int base) {
   return r;
 }
 
-// waves per work-group (8: one work-group per CU shares each tile among
-// 8 waves; 4: two work-groups per CU, whose phases drift apart)
-#ifndef PA_PREFILL_WAVES
-#define PA_PREFILL_WAVES 8
-#endif
-constexpr int kPrefillThreads = 64 * PA_PREFILL_WAVES;
-// query heads per wave (1 or 2); with 2, each K and V^T fragment read from
-// LDS feeds two MFMAs
-#ifndef PA_PREFILL_HW
-#define PA_PREFILL_HW 1
-#endif
-// 1: a wave computes the scores of tile t+1 while it runs the softmax of
-// tile t (costs a second set of score registers); 0: the scores of tile t
-// at the start of step t (with two heads per wave, one head's products
-// overlap the other head's softmax)
-#ifndef PA_PREFILL_LOOKAHEAD
-#define PA_PREFILL_LOOKAHEAD (PA_PREFILL_HW == 1)
-#endif
-#ifndef PA_PREFILL_ORDER
-#define PA_PREFILL_ORDER 1
-#endif
-// 1: within each (kv head, head part), the (sequence, query tile) items of
-// a batch with at most 64 of them are dispatched longest first (keys to
-// read, largest first), the classic longest-processing-time order; larger
-// batches and cascade launches keep the plain order
-#ifndef PA_PREFILL_LPT
-#define PA_PREFILL_LPT 1
-#endif
+constexpr int kPrefillWaves = 8;  // one work-group per CU shares each tile among 8 waves
+constexpr int kPrefillThreads = 64 * kPrefillWaves;
+constexpr int KT = 64;            // keys per tile
+constexpr int kBufs = 4;          // LDS tile buffers: loads run three tiles ahead
 
-constexpr int kMaxTileBlocks = 8;  // 64 keys / smallest block size
-
-// block ids of the tile starting at key k0 (64 / block_size entries); the
-// work-group keeps them in a tiny LDS array, filled ahead of time
-__device__ __forceinline__ int tile_block_id(const int32_t *bt, int k0, int j, int shift, int max_blocks) {
-  return bt[min((k0 >> shift) + j, max_blocks - 1)];
-}
-
+typedef const __attribute__((address_space(4))) int32_t *tab_ptr_t;  // scalar loads of table entries
 typedef __attribute__((address_space(3))) void *lds_ptr_t;
 
-// source of the 16-byte chunks of keys that must read as zero
+// source of the 16-byte chunks of keys that must read as zero (blocks of 8)
 __device__ const uint4 kZeroChunk = {0u, 0u, 0u, 0u};
+// last word of a raw buffer descriptor (32-bit data format, no swizzle)
+constexpr int kRsrcWord3 = 0x00020000;
+
+// The tile loads are issued as inline assembly.  The compiler then does
+// not know that they write LDS, so it does not wait for them before the
+// step's own LDS reads (of other tiles); the kernel waits for them itself,
+// one step later, before the barrier that precedes their first reader.
+//
+// 16 bytes per lane from a raw buffer of `bytes` bytes at `base` (uniform)
+// into LDS at lds_addr + 16 * lane; a lane whose offset is out of range gets
+// zeros.  M0 holds the LDS address of the load (one wait state after its
+// write).
+__device__ __forceinline__ void dma_buffer16(uint32_t lds_addr, uint32_t voffset, const char *base, int bytes) {
+  typedef int v4i __attribute__((ext_vector_type(4)));
+  const uint64_t b = (uint64_t)base;
+  const v4i r = {(int)(uint32_t)b, (int)((uint32_t)(b >> 32) & 0xffffu), bytes, kRsrcWord3};
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds_addr), "v"(voffset), "s"(r)
+               : "memory", "m0");
+}
+// 16 bytes per lane from src into LDS at lds_addr + 16 * lane
+__device__ __forceinline__ void dma_global16(uint32_t lds_addr, const void *src) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(lds_addr), "v"(src)
+               : "memory", "m0");
+}
+// entries i[0..1] (or i[0..3]) of a table row, read through the scalar
+// cache and waited for at once (a few cycles from the scalar cache; issued
+// where the wave has no LDS reads in flight, so the wait holds up nothing
+// else).  The outputs are early-clobber: a load may land before the next
+// one has read its inputs.
+__device__ __forceinline__ void table_entries2(const int32_t *row, const int (&i)[4], int (&v)[4]) {
+  asm volatile("s_load_dword %0, %2, %3\n\ts_load_dword %1, %2, %4\n\ts_waitcnt lgkmcnt(0)"
+               : "=&s"(v[0]), "=&s"(v[1])
+               : "s"(row), "s"(i[0] * 4), "s"(i[1] * 4)
+               : "memory");
+  v[2] = v[0];
+  v[3] = v[1];
+}
+__device__ __forceinline__ void table_entries4(const int32_t *row, const int (&i)[4], int (&v)[4]) {
+  asm volatile(
+      "s_load_dword %0, %4, %5\n\ts_load_dword %1, %4, %6\n\t"
+      "s_load_dword %2, %4, %7\n\ts_load_dword %3, %4, %8\n\ts_waitcnt lgkmcnt(0)"
+      : "=&s"(v[0]), "=&s"(v[1]), "=&s"(v[2]), "=&s"(v[3])
+      : "s"(row), "s"(i[0] * 4), "s"(i[1] * 4), "s"(i[2] * 4), "s"(i[3] * 4)
+      : "memory");
+}
+// s_waitcnt with only vmcnt = n (n < 64) counted
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
 
 // Gather of one K (or V) tile, keys k0 .. k0+63 of row width DIM, straight
 // from the pool into LDS with 16-byte global-to-LDS loads: no registers, no
@@ -145,113 +179,146 @@ __device__ const uint4 kZeroChunk = {0u, 0u, 0u, 0u};
 // banks for any fixed chunk, and the slot pattern depends on a lane's key
 // only through (k / 4) % 4, so every fragment read is a per-lane base plus
 // a compile-time offset.  A wave's load writes 1 KB of consecutive LDS
-// (lane i at 16 i): 16 keys x one chunk group, each lane fetching the global
-// chunk that belongs in its slot.  A tile starts at a multiple of 64 keys
-// and the block size divides 64, so a lane's key, its block's index in the
-// tile and its offset inside the block are the same for every tile; only
-// the block ids change.  A key at or past kend, or in a block outside the
-// pool, reads a 16-byte zero chunk instead, so its K and V rows are zero.
+// (lane i at 16 i): the 16 keys kg .. kg+15 x one chunk group, each lane
+// fetching the global chunk that belongs in its slot.  A tile starts at a
+// multiple of 64 keys and the block size divides 64, so a lane's offset
+// inside its block is the same for every tile; only the block ids change.
+// With blocks of 16 or 32 keys a load's 16 keys share one block, whose id
+// and address are wave-uniform; with blocks of 8 the two half-waves have a
+// block each.
 template <int DIM>
 struct TileGather {
-  static constexpr int CG = DIM / 32;                              // chunk groups per row
-  static constexpr int CPR = DIM / 8;                              // 16-byte chunks per row
-  static constexpr int PER_WAVE = (CG * 4) / (kPrefillThreads / 64);  // wave loads per tile
-  static_assert(PER_WAVE >= 1 && (CG * 4) % (kPrefillThreads / 64) == 0, "tile split over the waves");
-  int key[PER_WAVE];        // this lane's key inside the tile, per load
-  uint32_t off[PER_WAVE];   // element offset inside the block (row, head, chunk)
+  static constexpr int CG = DIM / 32;                        // chunk groups per row
+  static constexpr int PER_WAVE = (CG * 4) / kPrefillWaves;  // wave loads per tile
+  static_assert(PER_WAVE >= 1 && (CG * 4) % kPrefillWaves == 0, "tile split over the waves");
+  int kg[PER_WAVE];         // first key of the load's 16 keys (wave-uniform)
+  uint32_t off[PER_WAVE];   // byte offset of this lane's chunk inside its block
   uint32_t lds[PER_WAVE];   // byte offset of the wave's load inside the tile (wave-uniform)
+  int lkey;                 // this lane's key within the load's 16: lane / 4
 
-  __device__ __forceinline__ void init(int wave, int lane, int shift, int bs_mask, uint32_t slot_stride) {
+  __device__ __forceinline__ void init(int wave, int lane, int bs_mask, uint32_t slot_stride) {
+    lkey = lane >> 2;
 #pragma unroll
     for (int j = 0; j < PER_WAVE; ++j) {
       const int load = wave * PER_WAVE + j;  // chunk group load / 4, key group load % 4
-      const int key = (load % 4) * 16 + lane / 4;
+      kg[j] = (load % 4) * 16;
+      const int key = kg[j] + lkey;
       const int chunk = (load / 4) * 4 + ((lane % 4) ^ ((key >> 2) & 3));
-      this->key[j] = key;
-      off[j] = (uint32_t)(key & bs_mask) * slot_stride + (uint32_t)chunk * 8;
+      off[j] = ((uint32_t)(key & bs_mask) * slot_stride + (uint32_t)chunk * 8) * 2u;
       lds[j] = (uint32_t)load * 1024;
     }
   }
-  __device__ __forceinline__ void issue(uint16_t *tile, const int *ids, const uint16_t *base, int num_blocks,
-                                        size_t block_stride, int k0, int kend, int shift) const {
+  // block ids (wave-uniform) the loads of the tile at k0 need, read from the
+  // table row (indices clamped into it): load j takes block id[j][0], with
+  // blocks of 8 keys its upper half-wave id[j][1]
+  struct Ids {
+    int id[PER_WAVE][2];
+  };
+  __device__ __forceinline__ Ids ids(bool kBs8, const int32_t *row, int k0, int shift, int max_blocks) const {
+    static_assert(PER_WAVE <= 2, "at most four table entries per read");
+    // entry e: load e / 2 (blocks of 8: half e % 2), or load e (larger blocks)
+    int idx[4], v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int j = (kBs8 ? e / 2 : e) % PER_WAVE, h = kBs8 ? e % 2 : 0;
+      idx[e] = min(__builtin_amdgcn_readfirstlane(((k0 + kg[j]) >> shift) + h), max_blocks - 1);
+    }
+    if (kBs8)
+      table_entries4(row, idx, v);
+    else
+      table_entries2(row, idx, v);
+    Ids r;
 #pragma unroll
     for (int j = 0; j < PER_WAVE; ++j) {
-      const int b = ids[key[j] >> shift];
-      const bool ok = (unsigned)b < (unsigned)num_blocks && k0 + key[j] < kend;
-      const void *src = ok ? static_cast<const void *>(base + (size_t)b * block_stride + off[j])
-                           : static_cast<const void *>(&kZeroChunk);
-      __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)(reinterpret_cast<char *>(tile) + lds[j]), 16, 0, 0);
+      r.id[j][0] = kBs8 ? v[2 * j] : v[j];
+      r.id[j][1] = kBs8 ? v[2 * j + 1] : v[j];
+    }
+    return r;
+  }
+  // kBs8: blocks of 8 keys; kPartial: keys at or past kend read zeros (the
+  // last tile of a range).  Both are constants at every call.
+  // loads of one tile into the LDS tile at lds_tile (PER_WAVE per wave)
+  __device__ __forceinline__ void issue(bool kBs8, bool kPartial, uint32_t lds_tile, const Ids &ids, const char *base,
+                                        const char *zero, int num_blocks, uint32_t block_bytes, int k0, int kend,
+                                        int lane) const {
+#pragma unroll
+    for (int j = 0; j < PER_WAVE; ++j) {
+      const bool kok = !kPartial || (k0 + kg[j] + lkey < kend);
+      if (!kBs8) {
+        // one block for the wave: a buffer over it, empty for an id outside
+        // the pool; out-of-range reads (an empty buffer, or a key past kend
+        // sent past the end) return zeros
+        const int b = ids.id[j][0];
+        const bool bok = (unsigned)b < (unsigned)num_blocks;
+        const char *blk = base + (size_t)(unsigned)(bok ? b : 0) * block_bytes;
+        dma_buffer16(lds_tile + lds[j], kok ? off[j] : 0x80000000u, blk, bok ? (int)block_bytes : 0);
+      } else {
+        const int b = (lane < 32) ? ids.id[j][0] : ids.id[j][1];
+        const bool ok = kok && (unsigned)b < (unsigned)num_blocks;
+        const char *src = ok ? base + (size_t)(unsigned)b * block_bytes + off[j] : zero;
+        dma_global16(lds_tile + lds[j], src);
+      }
     }
   }
 };
 
-// a rescale of O is done only when a query's running max grows by more than
-// this many base-2 units; until then the weights may exceed 1 by up to 2^8,
-// which the fp32 accumulators and the bf16 weights carry exactly as well
+// the reference max moves on a max-taking tile only when a score exceeds it
+// by more than this many base-2 units
 constexpr float kRescaleSlack = 8.f;
+// a tile without a max is redone when one of a lane's sums of weights
+// relative to the reference exceeds this (weights below 2^32 keep the fp32
+// sums and bf16 weights far from overflow)
+constexpr float kSumLimit = 4294967296.f;
 
 constexpr uint32_t kBf16PairOnes = 0x3F803F80u;  // two bf16 1.0
 
 template <int G>
 struct PrefillShape {
-  static constexpr int NW = kPrefillThreads / 64;  // waves per work-group
-  static constexpr int HW = (G >= 2) ? PA_PREFILL_HW : 1;  // query heads per wave
-  static constexpr int HP = G / HW;                // head slots of a kv head
-  static constexpr int GWH = HP < NW ? HP : NW;    // head slots per work-group
-  static constexpr int HALVES = HP / GWH;          // work-groups per kv head along heads
+  static constexpr int NW = kPrefillWaves;         // waves per work-group
+  static constexpr int GWH = G < NW ? G : NW;      // head slots per work-group
+  static constexpr int HALVES = G / GWH;           // work-groups per kv head along heads
   static constexpr int TG = NW / GWH;              // 32-token query groups per work-group
   static constexpr int QT = 32 * TG;               // query tokens per work-group
-  static_assert(HP % GWH == 0 && NW % GWH == 0, "heads and waves must divide");
+  static_assert(G % GWH == 0 && NW % GWH == 0, "heads and waves must divide");
 };
 
-template <int D, int DV, int G>
-__global__ void __launch_bounds__(kPrefillThreads, (8 / PA_PREFILL_WAVES) / PA_PREFILL_HW)
-prefill_chunk_kernel(const PrefillKernelArgs a) {
+template <int D, int DV, int G, bool kBs8>
+__global__ void __launch_bounds__(kPrefillThreads, 1) prefill_chunk_kernel(const PrefillKernelArgs a) {
   using Sh = PrefillShape<G>;
-  constexpr int HW = Sh::HW;
   constexpr int GWH = Sh::GWH;
   constexpr int HALVES = Sh::HALVES;
   constexpr int QT = Sh::QT;
-  constexpr int KT = 64;             // keys per tile
   using GK = TileGather<D>;
   using GV = TileGather<DV>;
   constexpr int NDS = D / 16;        // k-steps of Q K^T
   constexpr int NDT = DV / 32;       // 32-row tiles of O^T
 
-  // three buffers each for K and V: at step t the waves read K of tile t+1
-  // and V of tile t while tile t+2 is loaded
-  __shared__ __attribute__((aligned(1024))) uint16_t sk[3][KT * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t sv[3][KT * DV];
-  __shared__ int sid[3][kMaxTileBlocks];
+  // four buffers each for K and V: at step t the waves read K of tile t+1
+  // and V of tile t while tiles t+2 (issued in step t-1) and t+3 (issued in
+  // step t) are loaded
+  __shared__ __attribute__((aligned(1024))) uint16_t sk[kBufs][KT * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t sv[kBufs][KT * DV];
 
   // Work id.  Work-groups are dispatched round-robin over the 8 XCDs; the
   // remap gives each XCD a contiguous range of work ids, ordered (kv head,
-  // head part, sequence, query tile from the last): the query tiles of one
-  // (sequence, kv head), which read the same K/V, run together on one XCD
-  // and share its L2, the tiles with more keys first.
-  const int nwg = gridDim.x;  // a multiple of 8
-  const int bid = blockIdx.x;
+  // head part, query tile from the last, sequence): each XCD serves whole
+  // kv heads, and the query tiles of one (sequence, kv head), which read
+  // the same K/V, share its L2.
+  const int nwg = (a.n_work + 7) & ~7;  // the grid: a multiple of 8
+  const int bid = (int)__builtin_amdgcn_workgroup_id_x();
   const int wid = (bid & 7) * (nwg >> 3) + (bid >> 3);
   if (wid >= a.n_work) return;
   int rest = wid;
   const int kchunk = rest % a.n_chunks;  // cascade: chunk of the shared tokens
   rest /= a.n_chunks;
-#if PA_PREFILL_ORDER == 1
   const int qt_rev = rest % a.n_qtiles;
   rest /= a.n_qtiles;
   const int seq0 = rest % a.num_seqs;
   rest /= a.num_seqs;
-#else
-  const int seq0 = rest % a.num_seqs;
-  rest /= a.num_seqs;
-  const int qt_rev = rest % a.n_qtiles;
-  rest /= a.n_qtiles;
-#endif
   const int half = rest % HALVES;
   const int kvh = rest / HALVES;
   int qtile = a.n_qtiles - 1 - qt_rev;
   const bool cascade = a.group_start != nullptr;
-#if PA_PREFILL_LPT && PA_PREFILL_ORDER == 1
   int seq = seq0;
   if (!cascade && a.num_seqs * a.n_qtiles <= 64) {
     // item j of this (kv head, head part) takes the j-th largest item: lane
@@ -291,10 +358,8 @@ prefill_chunk_kernel(const PrefillKernelArgs a) {
     seq = item / a.n_qtiles;
     qtile = item - seq * a.n_qtiles;
   }
-#else
-  const int seq = seq0;
-#endif
 
+  seq = __builtin_amdgcn_readfirstlane(seq);
   const int32_t *rows = cascade ? a.group_start : a.query_start_loc;
   int r1 = min(rows[seq + 1], a.num_query_tokens);
   int r0 = rows[seq];
@@ -313,7 +378,7 @@ prefill_chunk_kernel(const PrefillKernelArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hs = wave % GWH;           // head slot of this wave
   const int tg = wave / GWH;
-  const int head0 = kvh * G + (half * GWH + hs) * HW;  // first of the wave's HW heads
+  const int head = kvh * G + half * GWH + hs;  // the wave's query head
   const int tw0 = t_begin + tg * 32;   // first query of this wave
   const int col = lane & 31;
   const int hh = lane >> 5;
@@ -332,13 +397,19 @@ prefill_chunk_kernel(const PrefillKernelArgs a) {
   for (int sft = 1; sft < 64; sft <<= 1) qpos_lo = min(qpos_lo, __shfl_xor(qpos_lo, sft));
   qpos_lo = __builtin_amdgcn_readfirstlane(qpos_lo);
 
-  bf16x8_t qb[HW][NDS];
+  // Q of this lane's query (negated, exactly, under a negative scale; the
+  // scores are then multiplied by |scale| * log2(e))
+  const float sl = fabsf(a.scale_log2);
+  const uint32_t qsign = a.scale_log2 < 0.f ? 0x80008000u : 0u;
+  bf16x8_t qb[NDS];
+  {
+    const uint4 *qrow = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.q) +
+                                                        ((size_t)(r0 + (qvalid ? t : 0)) * a.num_heads + head) * D);
 #pragma unroll
-  for (int h = 0; h < HW; ++h) {
-    const uint4 *qrow = reinterpret_cast<const uint4 *>(
-        static_cast<const uint16_t *>(a.q) + ((size_t)(r0 + (qvalid ? t : 0)) * a.num_heads + head0 + h) * D);
-#pragma unroll
-    for (int ds = 0; ds < NDS; ++ds) qb[h][ds] = as_bf16x8(qvalid ? qrow[ds * 2 + hh] : make_uint4(0, 0, 0, 0));
+    for (int ds = 0; ds < NDS; ++ds) {
+      const uint4 w = qvalid ? qrow[ds * 2 + hh] : make_uint4(0, 0, 0, 0);
+      qb[ds] = as_bf16x8(make_uint4(w.x ^ qsign, w.y ^ qsign, w.z ^ qsign, w.w ^ qsign));
+    }
   }
 
   // keys this work-group needs: 0 .. (largest query position of the tile)
@@ -375,29 +446,33 @@ prefill_chunk_kernel(const PrefillKernelArgs a) {
     }
     __syncthreads();
     kend = max(0, min(ctx, s_best[0]));
-    tab_row = s_best[1];
+    tab_row = __builtin_amdgcn_readfirstlane(s_best[1]);
   }
   // cascade: this work-group's chunk of the shared tokens
-  const int kbeg = cascade ? kchunk * a.chunk : 0;
+  const int kbeg = __builtin_amdgcn_readfirstlane(cascade ? kchunk * a.chunk : 0);
   if (cascade) {
     kend = min(kend, kbeg + a.chunk);
     if (kbeg >= kend) return;  // past every row's shared tokens: a slot no merge reads
   }
+  kend = __builtin_amdgcn_readfirstlane(kend);
 
-  const uint32_t slot_stride = (uint32_t)a.num_kv_heads * D;  // elements between K slots
-  const uint32_t vslot_stride = (uint32_t)a.num_kv_heads * DV;
-  const size_t block_stride = (size_t)slot_stride << a.block_shift;
-  const size_t vblock_stride = (size_t)vslot_stride << a.block_shift;
-  const uint16_t *kbase = static_cast<const uint16_t *>(a.k_cache) + (size_t)kvh * D;
-  const uint16_t *vbase = static_cast<const uint16_t *>(a.v_cache) + (size_t)kvh * DV;
-  const int32_t *bt = a.block_tables + (size_t)tab_row * a.max_blocks_per_seq;
   const int shift = a.block_shift;
   const int bs_mask = (1 << shift) - 1;
-  const float sl = a.scale_log2;
+  const uint32_t slot_stride = (uint32_t)a.num_kv_heads * D;  // elements between K slots
+  const uint32_t vslot_stride = (uint32_t)a.num_kv_heads * DV;
+  const uint32_t block_bytes = (slot_stride << shift) * 2u;
+  const uint32_t vblock_bytes = (vslot_stride << shift) * 2u;
+  const char *kbase = reinterpret_cast<const char *>(static_cast<const uint16_t *>(a.k_cache) + (size_t)kvh * D);
+  const char *vbase = reinterpret_cast<const char *>(static_cast<const uint16_t *>(a.v_cache) + (size_t)kvh * DV);
+  const char *zero = reinterpret_cast<const char *>(&kZeroChunk);
+  tab_row = __builtin_amdgcn_readfirstlane(tab_row);
+  const int32_t *bt = a.block_tables + (size_t)tab_row * a.max_blocks_per_seq;
+  const int max_blocks = a.max_blocks_per_seq;
+  const int num_blocks = a.num_blocks;
   GK gk;
   GV gv;
-  gk.init(wave, lane, shift, bs_mask, slot_stride);
-  gv.init(wave, lane, shift, bs_mask, vslot_stride);
+  gk.init(wave, lane, bs_mask, slot_stride);
+  gv.init(wave, lane, bs_mask, vslot_stride);
   // per-lane parts of the fragment addresses (see TileGather)
   const int k_even = ((hh ^ ((col >> 2) & 3)) << 4);
   const int k_odd = (((2 + hh) ^ ((col >> 2) & 3)) << 4);
@@ -407,28 +482,18 @@ prefill_chunk_kernel(const PrefillKernelArgs a) {
   const int v_off0 = v_lane + ((v_slot ^ ((vg >> 1) & 3)) << 4);        // keys of the first read
   const int v_off1 = v_lane + 8 * 64 + ((v_slot ^ (((vg >> 1) + 2) & 3)) << 4);  // 8 keys further
 
-  float m[HW], l[HW];  // reference max (base-2 units) and running sum of this lane's query, per head
-  f32x16_t o[HW][NDT];
+  // running state of this lane's query: reference max m (base-2 units of
+  // the scaled scores), nm = -m (0 while no key has been seen, m = -inf),
+  // and the running sum l
+  float m = -INFINITY, nm = 0.f, l = 0.f;
+  f32x16_t o[NDT];
 #pragma unroll
-  for (int h = 0; h < HW; ++h) {
-    m[h] = -INFINITY;
-    l[h] = 0.f;
+  for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[h][dt][r] = 0.f;
-  }
+    for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
 
-  // S^T tiles of keys k0 .. k0+63 for the wave's heads (s0: first 32 keys,
-  // s1: last 32); each K fragment read from LDS feeds HW products
-  auto qk = [&](const uint16_t *skb, f32x16_t (&s0)[HW], f32x16_t (&s1)[HW]) {
-#pragma unroll
-    for (int h = 0; h < HW; ++h)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s0[h][r] = 0.f;
-        s1[h][r] = 0.f;
-      }
+  // raw scores S^T for keys k0 .. k0+63 (s[0]: first 32 keys, s[1]: last 32)
+  auto qk = [&](const uint16_t *skb, f32x16_t (&s)[2]) {
     // chunk 2 ds + hh of keys col and 32 + col: group ds / 2, slot
     // (2 (ds % 2) + hh) ^ ((col / 4) % 4)
     typedef __attribute__((address_space(3))) const char *lds_cptr;
@@ -441,150 +506,30 @@ prefill_chunk_kernel(const PrefillKernelArgs a) {
       const uint32_t p = ((ds & 1) ? ko : ke) + (ds / 2) * 4096;
       const bf16x8_t a0 = *(lds_frag_ptr)(size_t)(p);
       const bf16x8_t a1 = *(lds_frag_ptr)(size_t)(p + 2048);
-#pragma unroll
-      for (int h = 0; h < HW; ++h) {
-        s0[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qb[h][ds], s0[h], 0, 0, 0);
-        s1[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qb[h][ds], s1[h], 0, 0, 0);
-      }
+      s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qb[ds], ds == 0 ? f32x16_t{} : s[0], 0, 0, 0);
+      s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qb[ds], ds == 0 ? f32x16_t{} : s[1], 0, 0, 0);
     }
   };
 
-  // Pipeline, one barrier per step t:
-  //   global-to-LDS loads of tile t+2 issued;  S(t+1) = K(t+1) Q^T;
-  //   softmax of S(t);  O += V(t) P(t);  wait for this wave's loads.
-  // Block ids: sid[j % 3] holds the ids of tile j, filled three tiles ahead.
-  if (tid < kMaxTileBlocks) {
-#pragma unroll
-    for (int j = 0; j < 3; ++j) sid[j][tid] = tile_block_id(bt, kbeg + j * KT, tid, shift, a.max_blocks_per_seq);
-  }
-  __syncthreads();
-  const int ntiles = (kend - kbeg + KT - 1) / KT;
-  gk.issue(sk[0], sid[0], kbase, a.num_blocks, block_stride, kbeg, kend, shift);
-  gv.issue(sv[0], sid[0], vbase, a.num_blocks, vblock_stride, kbeg, kend, shift);
-  gk.issue(sk[1], sid[1], kbase, a.num_blocks, block_stride, kbeg + KT, kend, shift);
-  gv.issue(sv[1], sid[1], vbase, a.num_blocks, vblock_stride, kbeg + KT, kend, shift);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-
-  f32x16_t c0[HW], c1[HW];  // S of the current tile
-#if PA_PREFILL_LOOKAHEAD
-  qk(sk[0], c0, c1);
-#endif
-
-  for (int kt = 0; kt < ntiles; ++kt) {
-    const int k0 = kbeg + kt * KT;
-    const int b0 = kt % 3;
-    const int b1 = (kt + 1) % 3;
-    const int b2 = (kt + 2) % 3;
-#if !PA_PREFILL_LOOKAHEAD
-    qk(sk[b0], c0, c1);
-#endif
-    // tile t+2 from the pool (past the last tile: zero rows, never used)
-    gk.issue(sk[b2], sid[b2], kbase, a.num_blocks, block_stride, k0 + 2 * KT, kend, shift);
-    gv.issue(sv[b2], sid[b2], vbase, a.num_blocks, vblock_stride, k0 + 2 * KT, kend, shift);
-    int next_id = 0;
-    if (tid < kMaxTileBlocks) next_id = tile_block_id(bt, k0 + 3 * KT, tid, shift, a.max_blocks_per_seq);
-
-    // causal mask on tiles that cross this wave's diagonal (raw scores;
-    // register r of this lane holds key 8*(r/4) + 4*hh + r%4); the same
-    // keys are masked for every head of the wave
-    if (k0 + KT - 1 > qpos_lo) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int kr = 8 * (r >> 2) + 4 * hh + (r & 3);
-        const bool keep0 = k0 + kr <= qpos;
-        const bool keep1 = k0 + 32 + kr <= qpos;
-#pragma unroll
-        for (int h = 0; h < HW; ++h) {
-          c0[h][r] = keep0 ? c0[h][r] : -INFINITY;
-          c1[h][r] = keep1 ? c1[h][r] : -INFINITY;
-        }
-      }
-    }
-    bool any_grow = false;
-    float tmax[HW];
-#pragma unroll
-    for (int h = 0; h < HW; ++h) {
-      float rmax = -INFINITY;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) rmax = fmaxf(fmaxf(rmax, c0[h][r]), c1[h][r]);
-      tmax[h] = xor32_max(rmax) * sl;  // scale > 0 keeps the order
-      any_grow = any_grow || (tmax[h] > m[h] + kRescaleSlack);
-    }
-    if (__builtin_amdgcn_ballot_w64(any_grow)) {
-#pragma unroll
-      for (int h = 0; h < HW; ++h) {
-        const bool grow = tmax[h] > m[h] + kRescaleSlack;
-        const float m_new = grow ? tmax[h] : m[h];
-        const float alpha = (m[h] == -INFINITY) ? 0.f : fast_exp2(m[h] - m_new);
-        m[h] = m_new;
-        l[h] *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) o[h][dt][r] *= alpha;
-      }
-    }
-    // From here to the P.V products the code is one basic block: the
-    // scores of the next tile (independent of this tile's softmax; on the
-    // last step the buffer holds the zero-filled tile past the end and the
-    // result is not used) are interleaved with the exponentials below, so
-    // the matrix and vector units work at the same time.
-#if PA_PREFILL_LOOKAHEAD
-    f32x16_t n0[HW], n1[HW];
-    qk(sk[b1], n0, n1);
-#else
-    (void)b1;
-#endif
-    bf16x8_t pb[HW][4];
-#pragma unroll
-    for (int h = 0; h < HW; ++h) {
-      const float nm = (m[h] == -INFINITY) ? 0.f : -m[h];  // rows with no key yet: every score is -inf
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        c0[h][r] = fast_exp2(fmaf(c0[h][r], sl, nm));
-        c1[h][r] = fast_exp2(fmaf(c1[h][r], sl, nm));
-      }
-      // P^T in the B layout: k-step (sub-tile st, half u) = registers
-      // 8u..8u+7 of c_st, i.e. keys st*32 + 16u + 8*(e/4) + 4*hh + e%4
-      pb[h][0] = pack8(c0[h], 0);
-      pb[h][1] = pack8(c0[h], 8);
-      pb[h][2] = pack8(c1[h], 0);
-      pb[h][3] = pack8(c1[h], 8);
-      // the running sum takes the same bf16 weights that multiply V, two
-      // at a time (v_dot2_f32_bf16 against ones), so numerator and
-      // denominator agree
-      float ps = 0.f;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const uint4 w = __builtin_bit_cast(uint4, pb[h][u]);
-        ps = dot2_bf16(w.x, kBf16PairOnes, ps);
-        ps = dot2_bf16(w.y, kBf16PairOnes, ps);
-        ps = dot2_bf16(w.z, kBf16PairOnes, ps);
-        ps = dot2_bf16(w.w, kBf16PairOnes, ps);
-      }
-      l[h] += ps;
-    }
-
-    // O^T += V^T P^T; the A operand takes the same keys from row d of V^T,
-    // and each V^T fragment read from LDS feeds HW products.  The A operand
-    // comes from transposing LDS reads of the row-major V tile: in each
-    // 16-lane group, source lane s reads 4 d-values of one key (key K0 +
-    // s/4, d = D0 + 4 (s%4)) and lane o receives d = D0 + o of keys K0 ..
-    // K0+3; two reads give the 8 keys of the B operand's k-step.  Lane s of
-    // 16-lane group g reads, for tile dt and k-step ks, key (ks / 2) 32 +
-    // (ks % 2) 16 + 4 (g / 2) + s / 4 (+8 for the second read), slot
-    // (2 (g % 2) + (s / 2) % 2) ^ ((key / 4) % 4), half s % 2 (address
-    // arithmetic in the LDS address space, constants last, so that they
-    // fold into the instructions' offset fields)
+  // O^T += V^T P^T; the A operand takes the same keys from row d of V^T.
+  // It comes from transposing LDS reads of the row-major V tile: in each
+  // 16-lane group, source lane s reads 4 d-values of one key (key K0 + s/4,
+  // d = D0 + 4 (s%4)) and lane o receives d = D0 + o of keys K0 .. K0+3;
+  // two reads give the 8 keys of the B operand's k-step.  Lane s of 16-lane
+  // group g reads, for tile dt and k-step ks, key (ks / 2) 32 + (ks % 2) 16
+  // + 4 (g / 2) + s / 4 (+8 for the second read), slot (2 (g % 2) + (s / 2)
+  // % 2) ^ ((key / 4) % 4), half s % 2 (address arithmetic in the LDS
+  // address space, constants last, so that they fold into the
+  // instructions' offset fields)
+  auto pv = [&](const uint16_t *svb, const bf16x8_t (&pb)[4]) {
     typedef __attribute__((address_space(3))) const char *lds_cptr;
     typedef short v4s __attribute__((ext_vector_type(4)));
     typedef __attribute__((address_space(3))) v4s *lds_v4s_ptr;
     // the two per-lane bases pass through an empty asm statement: opaque
     // vector values, so that base + constant selects the instructions'
     // offset field instead of a separate address per read
-    uint32_t va0 = (uint32_t)(size_t)((lds_cptr)(const char *)sv[b0] + v_off0);
-    uint32_t va1 = (uint32_t)(size_t)((lds_cptr)(const char *)sv[b0] + v_off1);
+    uint32_t va0 = (uint32_t)(size_t)((lds_cptr)(const char *)svb + v_off0);
+    uint32_t va1 = (uint32_t)(size_t)((lds_cptr)(const char *)svb + v_off1);
     asm volatile("" : "+v"(va0), "+v"(va1));
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
@@ -596,70 +541,246 @@ prefill_chunk_kernel(const PrefillKernelArgs a) {
         const uint2 l2 = __builtin_bit_cast(uint2, lo);
         const uint2 h2 = __builtin_bit_cast(uint2, hi);
         const bf16x8_t av = as_bf16x8(make_uint4(l2.x, l2.y, h2.x, h2.y));
-#pragma unroll
-        for (int h = 0; h < HW; ++h) o[h][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[h][ks], o[h][dt], 0, 0, 0);
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[ks], o[dt], 0, 0, 0);
       }
     }
+  };
 
-    if (tid < kMaxTileBlocks) sid[b0][tid] = next_id;  // ids of tile t+3
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of tile t+2 are in LDS
-    __syncthreads();
-#if PA_PREFILL_LOOKAHEAD
+  // weights of one tile, 2^(s * scale - m) from raw scores s (raw) or 2^s
+  // from exponents already relative to the reference, bf16 in the B layout
+  // of the P.V products, and their sum over this lane's keys; the running
+  // sum takes the same bf16 weights that multiply V, two at a time
+  // (v_dot2_f32_bf16 against ones), so numerator and denominator agree
+  auto weights = [&](f32x16_t (&s)[2], bf16x8_t (&pb)[4], bool raw) -> float {
 #pragma unroll
-    for (int h = 0; h < HW; ++h) {
-      c0[h] = n0[h];
-      c1[h] = n1[h];
+    for (int r = 0; r < 16; ++r) {
+      s[0][r] = fast_exp2(raw ? fmaf(s[0][r], sl, nm) : s[0][r]);
+      s[1][r] = fast_exp2(raw ? fmaf(s[1][r], sl, nm) : s[1][r]);
     }
-#endif
+    // P^T in the B layout: k-step (sub-tile st, half u) = registers
+    // 8u..8u+7 of s[st], i.e. keys st*32 + 16u + 8*(e/4) + 4*hh + e%4
+    pb[0] = pack8(s[0], 0);
+    pb[1] = pack8(s[0], 8);
+    pb[2] = pack8(s[1], 0);
+    pb[3] = pack8(s[1], 8);
+    float ps = 0.f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint4 w = __builtin_bit_cast(uint4, pb[u]);
+      ps = dot2_bf16(w.x, kBf16PairOnes, ps);
+      ps = dot2_bf16(w.y, kBf16PairOnes, ps);
+      ps = dot2_bf16(w.z, kBf16PairOnes, ps);
+      ps = dot2_bf16(w.w, kBf16PairOnes, ps);
+    }
+    return ps;
+  };
+
+  // New reference from the exponents of one tile (s = scaled scores + nm):
+  // the lane's max over both halves of the wave; when it exceeds m by more
+  // than the slack (always on the first tile with a key), O and l are
+  // rescaled and nm changes by d, which is returned (0 when it stays).
+  auto new_reference = [&](const f32x16_t (&s)[2]) -> float {
+    float rmax = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) rmax = fmaxf(fmaxf(rmax, s[0][r]), s[1][r]);
+    const float tmax = xor32_max(rmax) - nm;  // -inf when no key of the tile is seen
+    const bool grow = tmax > m + kRescaleSlack;
+    float d = 0.f;
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+      const float m_new = grow ? tmax : m;
+      const float alpha = (m == -INFINITY) ? 0.f : fast_exp2(m - m_new);
+      const float nm_new = (m_new == -INFINITY) ? 0.f : -m_new;
+      d = nm_new - nm;
+      m = m_new;
+      nm = nm_new;
+      l *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+    }
+    return d;
+  };
+
+  const int ntiles = (kend - kbeg + KT - 1) / KT;
+  // leading tiles every query of this wave sees whole: no mask, no max
+  const int n_plain = min(ntiles, max(0, (qpos_lo + 1 - kbeg) / KT));
+
+  // loads of tile j (its ids read beforehand) into buffer j % kBufs
+  typedef __attribute__((address_space(3))) const char *lds_cptr;
+  const uint32_t sk_lds = (uint32_t)(size_t)((lds_cptr)(const char *)&sk[0][0]);
+  const uint32_t sv_lds = (uint32_t)(size_t)((lds_cptr)(const char *)&sv[0][0]);
+  auto gather = [&](int j, const typename GK::Ids &ik, const typename GV::Ids &iv) {
+    const int k0 = kbeg + j * KT;
+    const uint32_t b = (uint32_t)(j % kBufs);
+    const uint32_t dk = sk_lds + b * (KT * D * 2), dv = sv_lds + b * (KT * DV * 2);
+    if (k0 + KT <= kend) {
+      gk.issue(kBs8, false, dk, ik, kbase, zero, num_blocks, block_bytes, k0, kend, lane);
+      gv.issue(kBs8, false, dv, iv, vbase, zero, num_blocks, vblock_bytes, k0, kend, lane);
+    } else {
+      gk.issue(kBs8, true, dk, ik, kbase, zero, num_blocks, block_bytes, k0, kend, lane);
+      gv.issue(kBs8, true, dv, iv, vbase, zero, num_blocks, vblock_bytes, k0, kend, lane);
+    }
+  };
+  // block ids of the V loads: with equal head dims a wave's V loads cover
+  // the keys of its K loads, so the ids are the same
+  auto same_ids = [&](const typename GK::Ids &k_ids, const GV &g, bool bs8, const int32_t *row, int k0, int sh,
+                      int mb) {
+    if constexpr (D == DV) {
+      (void)g, (void)bs8, (void)row, (void)k0, (void)sh, (void)mb;
+      return k_ids;
+    } else {
+      return g.ids(bs8, row, k0, sh, mb);
+    }
+  };
+  // tile loads a wave issues per step (the only vector memory operations
+  // inside the loop)
+  constexpr int kStepLoads = GK::PER_WAVE + GV::PER_WAVE;
+
+  // Pipeline, one barrier per step t:
+  //   loads of tile t+3 issued;  S(t+1) = K(t+1) Q^T;  weights of S(t);
+  //   O += V(t) P(t);  block ids of tile t+4 read;  wait for this wave's
+  //   loads of tile t+2 (issued in step t-1; those of tile t+3 stay in
+  //   flight);  barrier.
+  typename GK::Ids ik = gk.ids(kBs8, bt, kbeg, shift, max_blocks);
+  typename GV::Ids iv = same_ids(ik, gv, kBs8, bt, kbeg, shift, max_blocks);
+  gather(0, ik, iv);
+  ik = gk.ids(kBs8, bt, kbeg + KT, shift, max_blocks);
+  iv = same_ids(ik, gv, kBs8, bt, kbeg + KT, shift, max_blocks);
+  gather(1, ik, iv);
+  ik = gk.ids(kBs8, bt, kbeg + 2 * KT, shift, max_blocks);
+  iv = same_ids(ik, gv, kBs8, bt, kbeg + 2 * KT, shift, max_blocks);
+  gather(2, ik, iv);
+  ik = gk.ids(kBs8, bt, kbeg + 3 * KT, shift, max_blocks);
+  iv = same_ids(ik, gv, kBs8, bt, kbeg + 3 * KT, shift, max_blocks);
+  wait_vmcnt<0>();
+  __syncthreads();
+
+  f32x16_t sa[2], sb[2];  // scores of two consecutive tiles (ping-pong)
+  qk(sk[0], sa);
+
+  // one step on tile j whose scores are in cur; the next tile's go to nxt.
+  // kFull: causal mask where the tile crosses the diagonal, and the tile's
+  // max (first tile, diagonal tiles); otherwise no mask and no max, with
+  // the sum check.
+  auto step = [&](bool kFull, int j, f32x16_t (&cur)[2], f32x16_t (&nxt)[2]) __attribute__((always_inline)) {
+    const int k0 = kbeg + j * KT;
+    gather(j + 3, ik, iv);
+    if (kFull) {
+      // exponents relative to the reference; causal mask on tiles that
+      // cross this wave's diagonal (register r of this lane holds key
+      // 8*(r/4) + 4*hh + r%4)
+      const bool diag = k0 + KT - 1 > qpos_lo;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kr = 8 * (r >> 2) + 4 * hh + (r & 3);
+        cur[0][r] = (!diag || k0 + kr <= qpos) ? fmaf(cur[0][r], sl, nm) : -INFINITY;
+        cur[1][r] = (!diag || k0 + 32 + kr <= qpos) ? fmaf(cur[1][r], sl, nm) : -INFINITY;
+      }
+      const float d = new_reference(cur);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        cur[0][r] += d;
+        cur[1][r] += d;
+      }
+    }
+    // From here to the P.V products the code is one basic block: the
+    // scores of the next tile (independent of this tile's weights; past the
+    // last tile the buffer holds zero rows and the result is not used) are
+    // interleaved with the exponentials, so the matrix and vector units
+    // work at the same time.
+    qk(sk[(j + 1) % kBufs], nxt);
+    bf16x8_t pb[4];
+    float ps = weights(cur, pb, !kFull);
+    if (!kFull) {
+      if (__builtin_amdgcn_ballot_w64(ps > kSumLimit)) {
+        // a score far above the reference: redo this tile's scores and
+        // move the reference (the tile is still in LDS)
+        qk(sk[j % kBufs], cur);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          cur[0][r] = fmaf(cur[0][r], sl, nm);
+          cur[1][r] = fmaf(cur[1][r], sl, nm);
+        }
+        const float d = new_reference(cur);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          cur[0][r] += d;
+          cur[1][r] += d;
+        }
+        ps = weights(cur, pb, false);
+      }
+    }
+    l += ps;
+    pv(sv[j % kBufs], pb);
+    ik = gk.ids(kBs8, bt, k0 + 4 * KT, shift, max_blocks);
+    iv = same_ids(ik, gv, kBs8, bt, k0 + 4 * KT, shift, max_blocks);
+    wait_vmcnt<kStepLoads>();  // this wave's loads of tile j+2 are in LDS
+    __syncthreads();
+  };
+
+  constexpr bool full = true, plain = false;
+  int j = 0;
+  if (ntiles > 0) {
+    step(full, 0, sa, sb);
+    j = 1;
+    // plain tiles, two per iteration so that the score registers alternate
+    for (; j + 1 < n_plain; j += 2) {
+      step(plain, j, sb, sa);
+      step(plain, j + 1, sa, sb);
+    }
+    if (j < n_plain) {
+      step(plain, j, sb, sa);
+      ++j;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) sb[s] = sa[s];
+    }
+    for (; j < ntiles; ++j) {
+      step(full, j, sb, sa);
+#pragma unroll
+      for (int s = 0; s < 2; ++s) sb[s] = sa[s];
+    }
   }
 
-  float lsum[HW];
-#pragma unroll
-  for (int h = 0; h < HW; ++h) lsum[h] = xor32_sum(l[h]);  // cross-lane: before the divergent store
+  const float lsum = xor32_sum(l);  // cross-lane: before the divergent store
   if (cascade) {
     // partials (reference max in base-2 units, sum, unnormalised output)
     if (qvalid) {
-#pragma unroll
-      for (int h = 0; h < HW; ++h) {
-        const size_t idx = ((size_t)(r0 + t) * a.num_heads + head0 + h) * a.ws_parts + kchunk;
-        float *orow = a.ws_o + idx * DV;
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-          for (int rq = 0; rq < 4; ++rq) {
-            const int d0 = dt * 32 + 8 * rq + 4 * hh;
-            *reinterpret_cast<float4 *>(orow + d0) =
-                make_float4(o[h][dt][4 * rq], o[h][dt][4 * rq + 1], o[h][dt][4 * rq + 2], o[h][dt][4 * rq + 3]);
-          }
-        if (hh == 0) {
-          a.ws_m[idx] = m[h];
-          a.ws_l[idx] = lsum[h];
-        }
-      }
-    }
-    return;
-  }
-  if (qvalid) {
-#pragma unroll
-    for (int h = 0; h < HW; ++h) {
-      const float lt = lsum[h];
-      uint16_t *orow = static_cast<uint16_t *>(a.out) + ((size_t)(r0 + t) * a.num_heads + head0 + h) * DV;
+      const size_t idx = ((size_t)(r0 + t) * a.num_heads + head) * a.ws_parts + kchunk;
+      float *orow = a.ws_o + idx * DV;
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
         for (int rq = 0; rq < 4; ++rq) {
           const int d0 = dt * 32 + 8 * rq + 4 * hh;
-          float v[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = (lt > 0.f) ? o[h][dt][4 * rq + e] / lt : 0.f;
-          *reinterpret_cast<uint2 *>(orow + d0) = make_uint2(pack_bf16x2_rne(v[0], v[1]), pack_bf16x2_rne(v[2], v[3]));
+          *reinterpret_cast<float4 *>(orow + d0) =
+              make_float4(o[dt][4 * rq], o[dt][4 * rq + 1], o[dt][4 * rq + 2], o[dt][4 * rq + 3]);
         }
+      if (hh == 0) {
+        a.ws_m[idx] = m;
+        a.ws_l[idx] = lsum;
+      }
     }
+    return;
+  }
+  if (qvalid) {
+    uint16_t *orow = static_cast<uint16_t *>(a.out) + ((size_t)(r0 + t) * a.num_heads + head) * DV;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        const int d0 = dt * 32 + 8 * rq + 4 * hh;
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (lsum > 0.f) ? o[dt][4 * rq + e] / lsum : 0.f;
+        *reinterpret_cast<uint2 *>(orow + d0) = make_uint2(pack_bf16x2_rne(v[0], v[1]), pack_bf16x2_rne(v[2], v[3]));
+      }
   }
 }
 
 template <int D, int DV, int G>
 static hipError_t launch_t(const PrefillArgs &a, hipStream_t stream) {
+  const bool bs8 = a.cache.block_size == 8;
   using Sh = PrefillShape<G>;
   PrefillKernelArgs k;
   k.out = a.out;
@@ -695,7 +816,10 @@ static hipError_t launch_t(const PrefillArgs &a, hipStream_t stream) {
   k.ws_o = a.ws_o;
   k.ws_parts = a.ws_parts;
   const unsigned grid = (unsigned)((n_work + 7) / 8 * 8);
-  hipLaunchKernelGGL((prefill_chunk_kernel<D, DV, G>), dim3(grid), dim3(kPrefillThreads), 0, stream, k);
+  if (bs8)
+    hipLaunchKernelGGL((prefill_chunk_kernel<D, DV, G, true>), dim3(grid), dim3(kPrefillThreads), 0, stream, k);
+  else
+    hipLaunchKernelGGL((prefill_chunk_kernel<D, DV, G, false>), dim3(grid), dim3(kPrefillThreads), 0, stream, k);
   return hipGetLastError();
 }
 

@@ -340,6 +340,28 @@ def test_cascade_prefix_shared_full(name):
         print(f"cascade {name} ps={ps}: max-abs {mx:.2e} mean-abs {mean:.2e}")
 
 
+@pytest.mark.parametrize("scale", [0.37, 0.0, -0.05])
+def test_cascade_other_scales(scale):
+    """Cascade decode and plain decode under scales other than
+    1/sqrt(head_dim) (zero and negative included) against the oracle."""
+    sizes = [5, 12]
+    starts = np.cumsum([0] + sizes).tolist()
+    group_of = [g for g, n in enumerate(sizes) for _ in range(n)]
+    bs, shared_blocks = 16, 20
+    rng = np.random.default_rng(99)
+    ctx = [int(x) for x in rng.integers(shared_blocks * bs + 1, 1200, size=sum(sizes))]
+    case = W.random_decode(990, ctx, num_heads=32, num_kv_heads=8, head_dim=128, block_size=bs, dtype=W.BF16,
+                           shared_blocks=shared_blocks, group_of=group_of)
+    case.scale = float(scale)
+    ref = oracle_decode(case)
+    log(f"cascade scale {scale}")
+    got = _cascade(case, starts, [shared_blocks * bs] * 2, 256)
+    assert_close(got, ref, W.BF16, f"cascade scale {scale}")
+    log(f"decode scale {scale}")
+    _, got = _run(case, 256)
+    assert_close(got, ref, W.BF16, f"decode scale {scale}")
+
+
 @pytest.mark.parametrize("dims", [(128, 64), (64, 128)])
 @pytest.mark.parametrize("group", [2, 8])
 def test_cascade_separate_value_dim(dims, group):
@@ -439,8 +461,10 @@ def _append_rows(case):
 def test_decode_append(dtype, group, dims):
     """pa_decode_append = the cache write of each sequence's newest token
     plus pa_decode: outputs within tolerance of the oracle and the pools
-    bit-exact with the oracle's write (bf16 with G <= 4 and equal head dims
-    take the fused kernel, the others a separate write)."""
+    bit-exact with the oracle's write.  Every bf16 case (all G, equal or
+    separate head dims) takes the fused kernel, which writes the rows inside
+    the partition kernel; the fp32 case is the only one that runs the
+    separate slot-deriving write kernel first."""
     import paged_attention_kv_cache_amd as P
     t = torch()
     D, Dv = dims

@@ -29,6 +29,32 @@ def test_chunked_prefill_full(block_size):
     print(f"chunked prefill bs{block_size}: max-abs {mx:.2e} mean-abs {mean:.2e}")
 
 
+def test_chunked_prefill_eight_heads_per_kv_head_full():
+    """The 8 x 512 chunk workload at 64 query over 8 kv heads: 16 query tiles
+    of 32 per sequence, 128 (sequence, query tile) items per kv head, more
+    than the longest-first ranking takes (the plain dispatch order)."""
+    case = W.chunked_prefill(num_heads=64)
+    log("chunked prefill 8 x 512, 64 q / 8 kv heads")
+    _, got = _run(case)
+    ref = oracle_prefill(case)
+    mx, mean = assert_close(got, ref, W.BF16, "chunked prefill 64q")
+    print(f"chunked prefill 64q: max-abs {mx:.2e} mean-abs {mean:.2e}")
+
+
+@pytest.mark.parametrize("scale", [0.37, 0.0, -0.05, 1.0 / 64])
+def test_prefill_other_scales(scale):
+    """Scales other than 1/sqrt(head_dim), zero and negative included: the
+    scale multiplies every q.k, so a negative one reverses the order of the
+    scores and zero gives uniform weights."""
+    case = W.random_prefill(91, [0, 70, 300, 5], [100, 64, 130, 1], num_heads=32, num_kv_heads=8, head_dim=128,
+                            block_size=16, dtype=W.BF16)
+    case.scale = float(scale)
+    log(f"prefill scale {scale}")
+    _, got = _run(case)
+    ref = oracle_prefill(case)
+    assert_close(got, ref, W.BF16, f"scale {scale}")
+
+
 PREFIXES = [0, 0, 5, 31, 32, 64, 100, 257]
 QLENS = [1, 64, 33, 1, 32, 95, 128, 200]
 

@@ -146,24 +146,6 @@ class _PagedBase:
     def max_blocks_per_seq(self) -> int:
         return int(self.block_tables.shape[1])
 
-    def written_caches(self):
-        """Caches with the new tokens stored at their slots (storage dtype).
-
-        This is the input-side bookkeeping of the case (a copy of values to
-        their given slots), used to hand both sides identical caches when a
-        test wants to bypass the write step.
-        """
-        k = self.k_cache.copy()
-        v = self.v_cache.copy()
-        nb, bs = k.shape[0], k.shape[1]
-        kf = k.reshape(nb * bs, *k.shape[2:])
-        vf = v.reshape(nb * bs, *v.shape[2:])
-        for t, s in enumerate(self.slot_mapping.tolist()):
-            if s >= 0:
-                kf[s] = self.new_key[t]
-                vf[s] = self.new_value[t]
-        return k, v
-
     def kv_bytes_logical(self) -> int:
         """K+V bytes a kernel must read: every context token, all kv heads."""
         el = 2 if self.dtype == BF16 else 4
@@ -405,12 +387,12 @@ def long_context_decode(seed: int = 3000, poison: bool = True, num_seqs: int = 4
 
 
 def chunked_prefill(seed: int = 4000, poison: bool = True, num_seqs: int = 8, chunk: int = 512,
-                    prefix_high: int = 3584, block_size: int = 32) -> PrefillCase:
+                    prefix_high: int = 3584, block_size: int = 32, num_heads: int = 32) -> PrefillCase:
     """8 sequences each appending a 512-token chunk (4096-token budget) onto
     a cached prefix uniform in [0, 3584]; 32 q / 8 kv heads, head_dim 128,
     block_size 32 (8 and 16 as variants), bf16.  The chunk's slot mapping
     follows the randomly drawn block table, continuing the prefix's partial
-    last block."""
+    last block.  ``num_heads`` = 64 gives eight query heads per kv head."""
     rng = np.random.default_rng(seed)
     prefix = rng.integers(0, prefix_high, size=num_seqs, endpoint=True).tolist()
     qlen = [chunk] * num_seqs
@@ -419,7 +401,9 @@ def chunked_prefill(seed: int = 4000, poison: bool = True, num_seqs: int = 8, ch
     qsl = np.zeros(num_seqs + 1, dtype=np.int32)
     qsl[1:] = np.cumsum(qlen)
     name = "chunked_prefill" if block_size == 32 else f"chunked_prefill_bs{block_size}"
-    return _finish(rng, kind="prefill", name=name, dtype=BF16, Hq=32, Hkv=8, D=128,
+    if num_heads != 32:
+        name += f"_{num_heads}q"
+    return _finish(rng, kind="prefill", name=name, dtype=BF16, Hq=num_heads, Hkv=8, D=128,
                    bs=block_size, ctx=ctx, tables=tables, nb=nb, pad=pad, q_rows=int(qsl[-1]),
                    new_positions=[np.arange(p, p + chunk) for p in prefix], poison=poison,
                    query_start_loc=qsl)
