@@ -215,6 +215,31 @@ int pa_decode(const pa_kv_cache *cache, void *out, const void *q, int32_t num_se
               int32_t partition_size, void *workspace, size_t workspace_bytes, void *stream);
 
 /* ---------------------------------------------------------------------
+ * pa_decode_static - pa_decode for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same kernels and arguments, without the
+ * workspace.  The split-K partials go to a static scratch array that the
+ * library holds on every GPU it runs on, PA_STATIC_WORKSPACE_BYTES bytes,
+ * until the process ends.  The call allocates nothing and frees nothing.
+ *
+ *   cache ... partition_size, stream : as pa_decode.
+ *
+ * A request whose partials need more than PA_STATIC_WORKSPACE_BYTES
+ * (pa_decode_workspace_bytes of the same sizes) returns PA_ERR_WORKSPACE
+ * before anything is enqueued; a larger partition_size or pa_decode with
+ * a caller workspace serves it.  The current device must be the device of
+ * `stream` (PA_ERR_SHAPE otherwise).  Every call on one GPU shares that
+ * GPU's scratch: two calls whose kernels overlap on one GPU (different
+ * streams, or graph replays in flight together) race and their results
+ * are unspecified; calls ordered on one stream are safe.  The scratch
+ * needs no clearing: each call writes every partial it reads.
+ * --------------------------------------------------------------------- */
+#define PA_STATIC_WORKSPACE_BYTES ((size_t)32 << 20)
+int pa_decode_static(const pa_kv_cache *cache, void *out, const void *q, int32_t num_seqs, int32_t num_heads,
+                     const int32_t *block_tables, int32_t max_blocks_per_seq, const int32_t *context_lens,
+                     int32_t max_context_len, float scale, int32_t partition_size, void *stream);
+
+/* ---------------------------------------------------------------------
  * pa_decode_append - one whole decode step: writes each sequence's newest
  * K and V rows into the cache and attends over the context, as
  * pa_kv_cache_write (with slot = the slot of position context_lens[i] - 1

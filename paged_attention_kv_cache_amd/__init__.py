@@ -10,6 +10,8 @@ The work is done by hand-written HIP kernels behind the C ABI in
 * ``pa_decode``          - one query per sequence over its context; split-K
   partitions plus reduce (``pa_decode_partition`` / ``pa_decode_reduce``
   run the two stages separately)
+* ``pa_decode_static``   - ``pa_decode`` with its split-K partials in a
+  static device scratch of the library, for callers that cannot allocate
 * ``pa_decode_cascade``  - decode of groups sharing a prefix of whole blocks,
   the shared tokens read once per group (an MFMA pass) and merged with each
   sequence's own split-K partitions
@@ -36,6 +38,7 @@ from ._binding import (  # noqa: F401
     pa_decode_cascade_workspace_bytes,
     pa_decode_partition,
     pa_decode_reduce,
+    pa_decode_static,
     pa_decode_workspace_bytes,
     pa_kv_cache_copy_blocks,
     pa_kv_cache_write,

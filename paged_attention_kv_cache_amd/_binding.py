@@ -88,6 +88,7 @@ SIGNATURES = {
     "pa_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
     "pa_decode": (ctypes.c_int, [_PCACHE, _vp, _vp, _i32, _i32, _vp, _i32, _vp, _i32, _f32, _i32,
                                  _vp, _sz, _vp]),
+    "pa_decode_static": (ctypes.c_int, [_PCACHE, _vp, _vp, _i32, _i32, _vp, _i32, _vp, _i32, _f32, _i32, _vp]),
     "pa_decode_partition": (ctypes.c_int, [_PCACHE, _vp, _vp, _i32, _i32, _vp, _i32, _vp, _i32, _f32,
                                            _i32, _vp, _sz, _vp]),
     "pa_decode_reduce": (ctypes.c_int, [_vp, _i32, _i32, _i32, _i32, _vp, _i32, _i32, _vp, _sz, _vp]),
@@ -355,6 +356,20 @@ def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, max
         code = lib.pa_decode_reduce(p_out, cache.dtype, S, H, Dv, p_cl, int(max_context_len),
                                     int(partition_size), p_ws, ws_bytes, st)
         _check("pa_decode_reduce", code)
+    return out
+
+
+def pa_decode_static(q, k_cache, v_cache, block_tables, context_lens, scale: float, max_context_len: int,
+                     partition_size: int = 512, out=None, stream=None):
+    """:func:`pa_decode` whose split-K partials live in the library's static
+    device scratch: nothing is allocated for them (``out`` is still
+    allocated here when not given)."""
+    cache, S, H, Dv, out, (p_out, p_q, p_bt, p_cl) = _decode_args(q, k_cache, v_cache, block_tables,
+                                                                 context_lens, out)
+    code = load_library().pa_decode_static(ctypes.byref(cache), p_out, p_q, S, H, p_bt, int(block_tables.shape[1]),
+                                           p_cl, int(max_context_len), float(scale), int(partition_size),
+                                           _stream(stream))
+    _check("pa_decode_static", code)
     return out
 
 

@@ -11,6 +11,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <mutex>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -190,6 +191,55 @@ int prepare_decode(const pa_kv_cache *cache, void *out, const void *q, int32_t n
   return PA_OK;
 }
 
+// Split-K scratch of pa_decode_static: a file-scope device array of
+// PA_STATIC_WORKSPACE_BYTES, one copy per GPU, held until the process ends.
+// In host code `scratch` is only a stand-in for the symbol; its device
+// address (different on every GPU) comes from hipGetSymbolAddress, once per
+// device, and only that address is ever passed to a kernel.
+static __device__ __align__(256) char scratch[PA_STATIC_WORKSPACE_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// device address of `scratch` on the current device (looked up on the first
+// call on that device); nullptr with the error recorded on failure
+void *static_scratch(hipStream_t stream, int *status) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    *status = hip_fail(e, "hipGetDevice");
+    return nullptr;
+  }
+  if (stream) {
+    int sdev = -1;
+    e = hipStreamGetDevice(stream, &sdev);
+    if (e != hipSuccess) {
+      *status = hip_fail(e, "hipStreamGetDevice");
+      return nullptr;
+    }
+    if (sdev != dev) {
+      *status = fail(PA_ERR_SHAPE, "stream belongs to device %d but device %d is current", sdev, dev);
+      return nullptr;
+    }
+  }
+  if (dev < 0 || dev >= kMaxDevices) {
+    *status = fail(PA_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      *status = hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol, "hipGetSymbolAddress(scratch)");
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -359,6 +409,34 @@ int pa_decode(const pa_kv_cache *cache, void *out, const void *q, int32_t num_se
   e = pa::launch_decode_reduce(a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "decode reduce launch");
   return ok();
+}
+
+int pa_decode_static(const pa_kv_cache *cache, void *out, const void *q, int32_t num_seqs, int32_t num_heads,
+                     const int32_t *block_tables, int32_t max_blocks_per_seq, const int32_t *context_lens,
+                     int32_t max_context_len, float scale, int32_t partition_size, void *stream) {
+  // the split-K size check comes before any HIP call, so an oversized
+  // request is refused without touching the device
+  int st = check_cache(cache, true);
+  if (st) return st;
+  const size_t need = workspace_bytes(num_seqs, num_heads, v_dim(cache), max_context_len, partition_size);
+  if (need > (size_t)PA_STATIC_WORKSPACE_BYTES)
+    return fail(PA_ERR_WORKSPACE,
+                "split-K partials need %zu bytes, above the static scratch of %zu bytes; use a larger "
+                "partition_size or pa_decode with a caller workspace",
+                need, (size_t)PA_STATIC_WORKSPACE_BYTES);
+  void *ws = nullptr;
+  if (need > 0) {
+    // validate the rest before the first device query
+    pa::DecodeArgs probe;
+    st = prepare_decode(cache, out, q, num_seqs, num_heads, block_tables, max_blocks_per_seq, context_lens,
+                        max_context_len, scale, partition_size, nullptr, 0, &probe, false);
+    if (st) return st;
+    if (num_seqs == 0) return ok();
+    ws = static_scratch((hipStream_t)stream, &st);
+    if (!ws) return st;
+  }
+  return pa_decode(cache, out, q, num_seqs, num_heads, block_tables, max_blocks_per_seq, context_lens,
+                   max_context_len, scale, partition_size, ws, need, stream);
 }
 
 int pa_decode_append(const pa_kv_cache *cache, void *out, const void *q, const void *key, const void *value,

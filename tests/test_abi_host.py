@@ -118,6 +118,19 @@ def test_decode_rejects_partition_and_workspace(lib):
     assert f"< {need} needed" in msg()
 
 
+def test_static_decode_rejects_partials_above_the_scratch(lib):
+    """pa_decode_static refuses, on the host and before any HIP call, a
+    request whose split-K partials exceed its static scratch."""
+    need = P.pa_decode_workspace_bytes(64, 64, 128, 1 << 20, 32)
+    assert need > 32 << 20
+    c = cache(hkv=8)
+    code = lib.pa_decode_static(ctypes.byref(c), FAKE, FAKE, 64, 64, FAKE, 1 << 15, FAKE, 1 << 20, 0.1, 32, None)
+    assert code == -7
+    assert f"need {need} bytes" in msg() and str(32 << 20) in msg()
+    assert lib.pa_decode_static(ctypes.byref(cache(bs=24)), FAKE, FAKE, 4, 32, FAKE, 8, FAKE, 100, 0.1, 0,
+                                None) == -4
+
+
 def test_decode_rejects_shapes(lib):
     assert decode(lib, cache(), S=-1) == -3
     assert decode(lib, cache(), S=70000) == -3
