@@ -10,10 +10,14 @@ timing starts.  Each step uses the next of R copies of the KV pool (about
 2 GB in total), so the 256 MB Infinity Cache cannot serve the KV from an
 earlier step.
 
-Prints one JSON line: throughput in tokens/s, the roofline of the decode
-partition kernel (its algorithmic bytes over its event-timed duration,
-against 8 TB/s), a secondary prefill-chunk measurement (MFMA fraction),
-and the CPU oracle timed on the host as a baseline.
+Prints one JSON line: throughput in tokens/s, the KV bytes per second of
+the step and of the decode partition kernel alone (against 8 TB/s and
+against the read rate a plain sequential read reaches on the same device
+in the same run), the roofline of the partition kernel, timing statistics
+(median, p10, p90 over the timed steps; a warm number beside the cold
+headline), a secondary prefill-chunk measurement (MFMA fraction), other
+decode workloads, the scheduler-driven serving loop, and the CPU oracle
+timed on the host as a baseline.
 
     python bench.py [--steps K] [--warmup W] [--partition P] [--no-cpu-baseline]
 """
@@ -48,15 +52,24 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--partition", type=int, default=512, help="split-K partition (tokens)")
+    ap.add_argument("--partition", type=int, default=192, help="split-K partition of the bs32 step (tokens)")
     ap.add_argument("--rotate-gb", type=float, default=2.0, help="total size of rotated KV pools")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--quick", action="store_true", help="skip the long-context and prefix-shared decode lines")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-seconds", type=float, default=3.0, help="per run of the CPU oracle's decode leg")
+    ap.add_argument("--only", default=None, choices=sorted(ONLY),
+                    help="time one workload alone (for per-workload counter runs); prints its own JSON line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first copy 1 GiB device-to-device (a kernel of known traffic for counter runs)")
     return ap.parse_args()
+
+
+# workloads --only can time alone, each in its own process
+ONLY = ("decode_bs32", "tiny_fp32_decode", "long_context_decode", "decode_batch_bs32_ctx4096",
+        "decode_batch_bs32_64q_8kv", "decode_batch_bs32_k128_v64", "prefix_shared_decode_bs16",
+        "prefix_shared_decode_bs8", "chunked_prefill", "chunked_prefill_bs16", "chunked_prefill_bs8",
+        "stream_read")
 
 
 def source_hash(*names) -> str:
@@ -81,6 +94,52 @@ def traffic_from_profiles(kernel_key: str, src_hash: str):
     except (OSError, ValueError):
         return None
     return None
+
+
+def stats_ms(samples_ms):
+    """median, p10, p90 (microseconds) of per-iteration times in ms"""
+    a = np.asarray(samples_ms, dtype=np.float64) * 1e3
+    return {"median_us": round(float(np.median(a)), 2), "p10_us": round(float(np.percentile(a, 10)), 2),
+            "p90_us": round(float(np.percentile(a, 90)), 2), "n": int(a.size)}
+
+
+def timed_each(fn, n):
+    """run fn(i) n times with an event pair around each call; per-call ms"""
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    torch.cuda.synchronize()
+    for i in range(n):
+        evs[i][0].record()
+        fn(i)
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in evs]
+
+
+def bench_stream_ceiling(gib=1.0, launches=20):
+    """The library's plain sequential read kernel over two 1 GiB buffers in
+    turn (2 GiB: no buffer stays in the 256 MB Infinity Cache): GB/s."""
+    import torch
+    import paged_attention_kv_cache_amd as P
+    n = int(gib * (1 << 30))
+    bufs = [torch.ones(n // 2, dtype=torch.int16, device="cuda") for _ in range(2)]
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for i in range(4):
+        P.pa_stream_read(bufs[i % 2], sink)
+    ms = timed_each(lambda i: P.pa_stream_read(bufs[i % 2], sink), launches)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(launches):
+        P.pa_stream_read(bufs[i % 2], sink)
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / launches
+    del bufs
+    torch.cuda.empty_cache()
+    return {"bytes_per_launch": n, "gbps": round(n / (t * 1e-3) / 1e9, 1),
+            "gbps_median_launch": round(n / (float(np.median(ms)) * 1e-3) / 1e9, 1),
+            "frac_of_nominal": round(n / (t * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
 
 
 def to_dev(arr, dtype):
@@ -161,6 +220,20 @@ def bench_decode(args):
     wall = time.perf_counter() - t0
     ms_step_plain = start.elapsed_time(end) / args.steps
 
+    # per-step statistics: the same steps, an event pair around each
+    step_each = timed_each(lambda i: step(i % R), args.steps)
+    # warm: every step on the same pool, which the Infinity Cache then
+    # partly holds (the cold headline rotates R pools)
+    for i in range(args.warmup):
+        step(0)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        step(0)
+    end.record()
+    torch.cuda.synchronize()
+    ms_step_warm = start.elapsed_time(end) / args.steps
+
     # the same step through pa_decode_append, K steps after a warmup of its own
     for i in range(args.warmup):
         step_fused(i % R)
@@ -197,6 +270,8 @@ def bench_decode(args):
     end.record()
     torch.cuda.synchronize()
     t_part_b2b = start.elapsed_time(end) / args.steps
+    part_each = timed_each(lambda i: P.pa_decode_partition(q, *pools[i % R], bt, cl, case.scale, mcl, ps, out=out,
+                                                           workspace=ws), args.steps)
 
     # algorithmic bytes of one decode partition launch: every context
     # token's K and V row for all kv heads, q read once, the output (for
@@ -208,7 +283,8 @@ def bench_decode(args):
     src = source_hash("pa_decode.hip", "pa_common.h")
     res = dict(
         case=case, S=S, R=R, ms_step=ms_step_plain, ms_step_fused=ms_step_fused,
-        ms_step_with_events=ms_step, wall=wall,
+        ms_step_with_events=ms_step, wall=wall, ms_step_warm=ms_step_warm,
+        step_stats=stats_ms(step_each), part_stats=stats_ms(part_each),
         t_write=t_write, t_part=t_part, t_red=t_red, t_part_b2b=t_part_b2b, kv_bytes=kv_bytes,
         part_bytes=part_bytes,
         achieved=achieved, src=src, ps=ps,
@@ -469,7 +545,8 @@ def bench_prefill(args, block_size=32):
         run()
         evs[i][1].record()
     torch.cuda.synchronize()
-    t_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    each = [a.elapsed_time(b) for a, b in evs]
+    t_ms = float(np.mean(each))
     # algorithmic FLOPs: 4 * D per visible (query, key) pair per query head
     H, D = case.num_heads, case.head_dim
     pairs = 0
@@ -479,41 +556,181 @@ def bench_prefill(args, block_size=32):
         pairs += ql * prefix + ql * (ql + 1) // 2
     flops = 4.0 * D * pairs * H
     tflops = flops / (t_ms * 1e-3) / 1e12
-    return dict(us=t_ms * 1e3, tflops=tflops, frac=tflops / BF16_DENSE_PEAK_TFLOPS, flops=flops,
+    return dict(us=t_ms * 1e3, tflops=tflops, frac=tflops / BF16_DENSE_PEAK_TFLOPS, flops=flops, stats=stats_ms(each),
                 tokens_per_s=int(case.query_start_loc[-1]) / (t_ms * 1e-3),
                 src=source_hash("pa_prefill.hip", "pa_common.h"))
 
 
-def cpu_baseline(case, seconds):
-    """The oracle as it stands, on the host cores: write + decode steps of the
-    whole bs32 batch, repeated for about ``seconds``."""
+def host_info():
+    """What the CPU baseline ran on: cores available to this process, the
+    CPU model, numpy and its BLAS."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    blas = []
+    try:
+        from threadpoolctl import threadpool_info
+        for d in threadpool_info():
+            blas.append({k: d.get(k) for k in ("internal_api", "version", "num_threads", "threading_layer")})
+    except ImportError:  # pragma: no cover
+        pass
+    return {"cores": len(os.sched_getaffinity(0)), "cpu_model": model, "numpy": np.__version__, "blas": blas}
+
+
+def bench_tiny(steps=200):
+    """The tiny fp32 workload: kv_cache_write of its one new token, then
+    decode (partition 16 tokens, so that split-K and the reduce run):
+    launch-bound, a correctness workload rather than a roofline claim."""
+    import torch
+    import paged_attention_kv_cache_amd as P
+    import workloads as W
+    case = W.make_config("tiny_fp32_decode", poison=False)
+    k, v = to_dev(case.k_cache, case.dtype), to_dev(case.v_cache, case.dtype)
+    nk, nv = to_dev(case.new_key, case.dtype), to_dev(case.new_value, case.dtype)
+    sm = torch.from_numpy(case.slot_mapping).cuda()
+    q = to_dev(case.q, case.dtype)
+    bt = torch.from_numpy(case.block_tables).cuda()
+    cl = torch.from_numpy(case.context_lens).cuda()
+    out = torch.empty((1, q.shape[1], case.v_cache.shape[-1]), dtype=q.dtype, device="cuda")
+    ws = torch.empty(max(P.pa_decode_workspace_bytes(1, q.shape[1], case.v_cache.shape[-1], case.max_context_len, 16), 1),
+                     dtype=torch.uint8, device="cuda")
+
+    def step(i):
+        P.pa_kv_cache_write(nk, nv, k, v, sm)
+        P.pa_decode(q, k, v, bt, cl, case.scale, case.max_context_len, 16, out=out, workspace=ws)
+
+    for i in range(10):
+        step(i)
+    each = timed_each(step, steps)
+    return {"workload": "tiny fp32 decode: 1 sequence, 8 q / 2 kv heads, head_dim 64, context 100, block_size 16; "
+                        "write of 1 token + decode (partition 16) + reduce",
+            "step": stats_ms(each), "kv_bytes": case.kv_bytes_logical()}
+
+
+def run_only(args):
+    """One workload alone, for counter runs: its timing dict as a JSON line."""
+    import workloads as W
+    name = args.only
+    if name == "decode_bs32":
+        r = bench_decode(args)
+        r = {k: v for k, v in r.items() if k != "case"}
+    elif name == "tiny_fp32_decode":
+        r = bench_tiny()
+    elif name == "stream_read":
+        r = bench_stream_ceiling()
+    elif name.startswith("chunked_prefill"):
+        bs = int(name[len("chunked_prefill_bs"):]) if name != "chunked_prefill" else 32
+        r = bench_prefill(args, block_size=bs)
+    elif name == "long_context_decode":
+        r = bench_decode_secondary(name, 512)
+    elif name == "decode_batch_bs32_ctx4096":
+        r = bench_decode_secondary(name, 1024, case=W.decode_batch(2000, poison=False, fixed_ctx=4096))
+    elif name == "decode_batch_bs32_64q_8kv":
+        r = bench_decode_secondary(name, 512, case=W.decode_batch(2000, poison=False, num_heads=64))
+    elif name == "decode_batch_bs32_k128_v64":
+        r = bench_decode_secondary(name, 192, case=W.decode_batch(2000, poison=False, v_head_dim=64))
+    else:
+        bs = 16 if name.endswith("16") else 8
+        r = bench_decode_secondary(name, 512, groups=([0, 16, 32, 48, 64], [64 * bs] * 4))
+    print(json.dumps({"only": name, **{k: v for k, v in r.items() if isinstance(v, (int, float, str, dict, list))}}),
+          flush=True)
+
+
+def cpu_baseline(dec_case, pre_case, long_case, seconds):
+    """The oracle as it stands (not tuned), in its fp32 mode, with BLAS on
+    every host core this process may use, on the same inputs as the GPU
+    lines: three legs, each the median of three runs.
+      decode:  whole write + decode steps of the bs32 batch, repeated for
+               about ``seconds`` per run;
+      prefill: the 8 x 512-token chunk workload (the chunk's write, then
+               every query row), once per run;
+      long:    one sequence of the long-context batch (its blocks only).
+    Reported in the GPU lines' units (tokens/s, and KV GB/s under the
+    same byte formula)."""
     import oracle
     import workloads as W
-    try:
-        from threadpoolctl import threadpool_limits
-    except ImportError:  # pragma: no cover
-        threadpool_limits = None
-    q = W.storage_to_f32(case.q, case.dtype)
-    kf = W.storage_to_f32(case.k_cache, case.dtype)
-    vf = W.storage_to_f32(case.v_cache, case.dtype)
-    nk = W.storage_to_f32(case.new_key, case.dtype)
-    nv = W.storage_to_f32(case.new_value, case.dtype)
-    ctx_mgr = threadpool_limits(1) if threadpool_limits else None
-    steps, t0 = 0, time.perf_counter()
-    try:
-        while True:
-            k2, v2 = oracle.kv_cache_write(kf, vf, nk, nv, case.slot_mapping)
-            oracle.paged_decode(q, k2, v2, case.block_tables, case.context_lens, case.scale)
-            steps += 1
-            if time.perf_counter() - t0 >= seconds:
-                break
-    finally:
-        if ctx_mgr is not None:
-            ctx_mgr.__exit__(None, None, None)
-    dt = time.perf_counter() - t0
-    return dict(value=case.num_seqs * steps / dt, unit="tokens/s", cores=1, kind="oracle",
-                sample=f"{steps} whole write+decode steps of the bs32 batch ({case.num_seqs} sequences, "
-                       f"float64 oracle, 1 BLAS thread) in {dt:.1f} s")
+    from threadpoolctl import threadpool_limits
+    info = host_info()
+    threads = info["cores"]
+    f32 = np.float32
+
+    def runs3(fn):
+        fn()  # first touch of the fresh host arrays, not timed
+        vals = [fn() for _ in range(3)]
+        return float(np.median(vals)), [round(v, 3) for v in vals]
+
+    with threadpool_limits(threads):
+        # decode leg
+        q = W.storage_to_f32(dec_case.q, dec_case.dtype)
+        kf = W.storage_to_f32(dec_case.k_cache, dec_case.dtype)
+        vf = W.storage_to_f32(dec_case.v_cache, dec_case.dtype)
+        nk = W.storage_to_f32(dec_case.new_key, dec_case.dtype)
+        nv = W.storage_to_f32(dec_case.new_value, dec_case.dtype)
+
+        def dec_run():
+            steps, t0 = 0, time.perf_counter()
+            while True:
+                k2, v2 = oracle.kv_cache_write(kf, vf, nk, nv, dec_case.slot_mapping)
+                oracle.paged_decode(q, k2, v2, dec_case.block_tables, dec_case.context_lens, dec_case.scale, f32)
+                steps += 1
+                if time.perf_counter() - t0 >= seconds:
+                    break
+            return dec_case.num_seqs * steps / (time.perf_counter() - t0)
+
+        dec_tps, dec_runs = runs3(dec_run)
+        del kf, vf
+        legs = [{"leg": "decode", "tokens_per_s": round(dec_tps, 1), "runs_tokens_per_s": dec_runs,
+                 "kv_gbps": round(dec_tps / dec_case.num_seqs * dec_case.kv_bytes_logical() / 1e9, 3),
+                 "sample": f"whole write + decode steps of the bs32 batch for ~{seconds:.0f} s per run"}]
+        # prefill leg
+        if pre_case is not None:
+            pq = W.storage_to_f32(pre_case.q, pre_case.dtype)
+            pk = W.storage_to_f32(pre_case.k_cache, pre_case.dtype)
+            pv = W.storage_to_f32(pre_case.v_cache, pre_case.dtype)
+            pnk = W.storage_to_f32(pre_case.new_key, pre_case.dtype)
+            pnv = W.storage_to_f32(pre_case.new_value, pre_case.dtype)
+            tq = int(pre_case.query_start_loc[-1])
+
+            def pre_run():
+                t0 = time.perf_counter()
+                k2, v2 = oracle.kv_cache_write(pk, pv, pnk, pnv, pre_case.slot_mapping)
+                oracle.paged_prefill(pq, pre_case.query_start_loc, k2, v2, pre_case.block_tables,
+                                     pre_case.context_lens, pre_case.scale, f32)
+                return tq / (time.perf_counter() - t0)
+
+            pre_tps, pre_runs = runs3(pre_run)
+            del pk, pv
+            legs.append({"leg": "prefill", "tokens_per_s": round(pre_tps, 1), "runs_tokens_per_s": pre_runs,
+                         "sample": "the whole 8 x 512-token chunk workload per run"})
+        # long-context leg: sequence 0's blocks only
+        if long_case is not None:
+            n = int(long_case.context_lens[0])
+            nb = -(-n // long_case.block_size)
+            ids = long_case.block_tables[0, :nb]
+            lk = W.storage_to_f32(long_case.k_cache[ids], long_case.dtype)
+            lv = W.storage_to_f32(long_case.v_cache[ids], long_case.dtype)
+            lq = W.storage_to_f32(long_case.q[:1], long_case.dtype)
+            table = np.arange(nb, dtype=np.int32)[None, :]
+
+            def long_run():
+                t0 = time.perf_counter()
+                oracle.paged_decode(lq, lk, lv, table, np.array([n], dtype=np.int32), long_case.scale, f32)
+                return 1.0 / (time.perf_counter() - t0)
+
+            long_tps, long_runs = runs3(long_run)
+            row = long_case.num_kv_heads * (long_case.head_dim + long_case.v_head_dim) * 2
+            legs.append({"leg": "long_context", "tokens_per_s": round(long_tps, 3), "runs_tokens_per_s": long_runs,
+                         "kv_gbps": round(long_tps * n * row / 1e9, 3),
+                         "sample": f"one decode token of sequence 0 ({n} context tokens, its {nb} blocks)"})
+    return dict(value=round(dec_tps, 1), unit="tokens/s", cores=threads, kind="oracle",
+                sample=f"decode leg: whole write + decode steps of the bs32 batch ({dec_case.num_seqs} sequences), "
+                       f"fp32 oracle, {threads} BLAS threads, median of 3 runs of ~{seconds:.0f} s",
+                threads=threads, host=info, legs=legs)
 
 
 def main():
@@ -529,6 +746,14 @@ def main():
     import workloads as W
     P.load_library()
 
+    if args.only:
+        if args.copy_calibration:
+            src = torch.ones(1 << 29, dtype=torch.bfloat16, device="cuda")
+            torch.empty_like(src).copy_(src)
+            torch.cuda.synchronize()
+            del src
+        run_only(args)
+        return
     if args.copy_calibration:
         src = torch.ones(1 << 29, dtype=torch.bfloat16, device="cuda")
         dst = torch.empty_like(src)
@@ -536,10 +761,13 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     dec = bench_decode(args)
+    ceiling = bench_stream_ceiling()
+    log(f"plain sequential read: {ceiling['gbps']:.0f} GB/s")
     pre = None if args.no_prefill else bench_prefill(args)
     case = dec["case"]
     tokens_per_s = dec["S"] / (dec["ms_step"] * 1e-3)
     traffic = traffic_from_profiles("decode_partition", dec["src"])
+    step_gbps = dec["kv_bytes"] / (dec["ms_step"] * 1e-3) / 1e9
     line = {
         "metric": METRIC,
         "value": round(tokens_per_s, 1),
@@ -563,10 +791,22 @@ def main():
             "partition_size": dec["ps"],
             "kv_pool_rotations": dec["R"],
         },
-        "kv_gbps": round(dec["achieved"], 1),
-        "kv_hbm_frac": round(dec["achieved"] / HBM_PEAK_GBPS, 4),
+        # KV bytes of the step over the step time (what tokens/s describes)
+        "kv_gbps": round(step_gbps, 1),
+        "kv_hbm_frac": round(step_gbps / HBM_PEAK_GBPS, 4),
+        # the same bytes over the partition kernel's own launch time
+        "kv_gbps_partition_kernel": round(dec["achieved"], 1),
+        "kv_hbm_frac_partition_kernel": round(dec["achieved"] / HBM_PEAK_GBPS, 4),
+        "stream_read_ceiling": ceiling,
+        "partition_kernel_frac_of_stream_ceiling": round(dec["achieved"] / ceiling["gbps"], 4),
+        "timing": {
+            "step_cold": dec["step_stats"],
+            "step_warm_ms": round(dec["ms_step_warm"], 5),
+            "step_warm_tokens_per_s": round(dec["S"] / (dec["ms_step_warm"] * 1e-3), 1),
+            "partition_kernel": dec["part_stats"],
+        },
         "roofline": {
-            "kernel": "decode_partition_bf16_kernel<128, 128, 4>",
+            "kernel": "decode_partition_rows_kernel<128, 128, 4>",
             "bound": "hbm",
             "achieved": round(dec["achieved"], 1),
             "peak": HBM_PEAK_GBPS,
@@ -588,7 +828,7 @@ def main():
     if pre is not None:
         line["prefill_chunk"] = {
             "workload": "8 sequences x 512-token chunk over prefix U[0,3584], 32q/8kv, D128, BS32, bf16",
-            "us": round(pre["us"], 2), "tokens_per_s": round(pre["tokens_per_s"], 1),
+            "us": round(pre["us"], 2), "tokens_per_s": round(pre["tokens_per_s"], 1), "timing": pre["stats"],
             "roofline": {"kernel": "prefill_chunk_kernel<128, 128, 4>", "bound": "mfma", "achieved": round(pre["tflops"], 1), "peak": BF16_DENSE_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(pre["frac"], 4),
                          "traffic": traffic_from_profiles("prefill_chunk", pre["src"]),
@@ -601,9 +841,11 @@ def main():
             line["prefill_other_block_sizes"].append({
                 "block_size": bs, "us": round(p2["us"], 2), "tokens_per_s": round(p2["tokens_per_s"], 1),
                 "tflops": round(p2["tflops"], 1), "mfma_frac": round(p2["frac"], 4)})
+    line["tiny_fp32_decode"] = bench_tiny()
+    long_case = None if args.quick else W.make_config("long_context_decode", poison=False)
     if not args.quick:
         line["decode_other_workloads"] = [
-            bench_decode_secondary("long_context_decode", 512),
+            bench_decode_secondary("long_context_decode", 512, case=long_case),
             # the metric's literal shape: 32 sequences of exactly 4096 tokens
             bench_decode_secondary("decode_batch_bs32_ctx4096", 1024,
                                    case=W.decode_batch(2000, poison=False, fixed_ctx=4096)),
@@ -611,7 +853,7 @@ def main():
             bench_decode_secondary("decode_batch_bs32_64q_8kv", 512,
                                    case=W.decode_batch(2000, poison=False, num_heads=64)),
             # a value head dim of its own: 128-wide keys, 64-wide values
-            bench_decode_secondary("decode_batch_bs32_k128_v64", 512,
+            bench_decode_secondary("decode_batch_bs32_k128_v64", 192,
                                    case=W.decode_batch(2000, poison=False, v_head_dim=64)),
             bench_decode_secondary("prefix_shared_decode_bs16", 512, groups=([0, 16, 32, 48, 64], [64 * 16] * 4)),
             bench_decode_secondary("prefix_shared_decode_bs8", 512, groups=([0, 16, 32, 48, 64], [64 * 8] * 4)),
@@ -619,8 +861,9 @@ def main():
         line["serving_loop"] = bench_serving()
         line["serving_loop_mixed"] = bench_serving(mixed=True)
     if not args.no_cpu_baseline:
-        log(f"timing the CPU oracle for ~{args.cpu_seconds:.0f} s")
-        line["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
+        log("timing the CPU oracle (decode, prefill and long-context legs, median of 3 each)")
+        pre_case = None if args.no_prefill else W.chunked_prefill(poison=False)
+        line["cpu_baseline"] = cpu_baseline(case, pre_case, long_case, args.cpu_seconds)
     print(json.dumps(line), flush=True)
 
 

@@ -45,6 +45,7 @@ from ._binding import (  # noqa: F401
     pa_last_error_message,
     pa_prefill_chunk,
     pa_status_string,
+    pa_stream_read,
     pa_version,
 )
 from .kv_manager import (KIND_DECODE, KIND_IDLE, KIND_MIXED, KIND_PROMPT, KvManager, Step, StepScheduler,  # noqa: F401

@@ -103,6 +103,7 @@ SIGNATURES = {
     "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "pa_last_error_message": (ctypes.c_char_p, []),
     "pa_version": (ctypes.c_int, []),
+    "pa_stream_read": (ctypes.c_int, [_vp, _sz, _vp, _vp]),
     # host KV manager and step scheduler
     "pa_kvm_create": (_vp, [_i32, _i32, _i32]),
     "pa_kvm_destroy": (None, [_vp]),
@@ -244,6 +245,17 @@ def pa_decode_workspace_bytes(num_seqs: int, num_heads: int, head_dim: int, max_
                               partition_size: int) -> int:
     return int(load_library().pa_decode_workspace_bytes(num_seqs, num_heads, head_dim, max_context_len,
                                                         partition_size))
+
+
+def pa_stream_read(buf, sink, stream=None) -> None:
+    """Read the whole GPU tensor ``buf`` once (the HBM read-rate probe of
+    ``include/pagedattn_bench.h``); ``sink`` is a GPU tensor of at least 4
+    bytes."""
+    nbytes = buf.numel() * buf.element_size()
+    if sink.numel() * sink.element_size() < 4:
+        raise ValueError("sink must hold at least 4 bytes")
+    code = load_library().pa_stream_read(_dev(buf, "buf"), nbytes, _dev(sink, "sink"), _stream(stream))
+    _check("pa_stream_read", code)
 
 
 def pa_kv_cache_write(key, value, k_cache, v_cache, slot_mapping, stream=None) -> None:

@@ -12,7 +12,7 @@ from gpu_util import (DeviceCase, assert_close, log, oracle_decode, to_dev, to_h
 
 pytestmark = pytest.mark.gpu
 
-BENCH_PARTITION = 512     # the split-K partition the benchmark times for the bs32 batch
+BENCH_PARTITION = 192     # the split-K partition the benchmark times for the bs32 batch
 
 
 def _run(case, partition_size, max_context_len=None):
@@ -68,7 +68,7 @@ def test_decode_separate_value_dim(dtype, dims, group):
             assert_close(got, ref, dtype, f"{dtype} D{D} Dv{Dv} G{group} bs{bs} ps{ps}")
 
 
-@pytest.mark.parametrize("ps", [0, 512, BENCH_PARTITION])
+@pytest.mark.parametrize("ps", [0, 256, 512, BENCH_PARTITION])
 def test_decode_batch_bs32_full(ps):
     case = W.make_config("decode_batch_bs32")
     ref = oracle_decode(case)
@@ -86,6 +86,33 @@ def test_decode_batch_bs32_eight_heads_per_kv_head_full():
     _, got = _run(case, 512)
     mx, mean = assert_close(got, ref, W.BF16, "bs32 batch G8 ps512")
     print(f"bs32 batch G=8: max-abs {mx:.2e} mean-abs {mean:.2e}")
+
+
+def test_decode_batch_bs32_ctx4096_full_sampled():
+    """The metric's literal shape, 32 sequences of exactly 4096 tokens, at
+    the partition the benchmark times it with (1024) and at 512; every
+    output row computed by the kernel, 8 of the 32 sequences (every fourth)
+    compared with the oracle, so that the fp64 oracle stays within seconds."""
+    case = W.decode_batch(2000, fixed_ctx=4096)
+    sample = list(range(0, 32, 4))
+    ref = oracle_decode(case, seqs=sample)[sample]
+    for ps in (1024, 512):
+        log(f"decode batch 32 x 4096 partition={ps}")
+        _, got = _run(case, ps)
+        mx, mean = assert_close(got[sample], ref, W.BF16, f"bs32 ctx4096 ps{ps}")
+        print(f"bs32 ctx4096 ps={ps}: max-abs {mx:.2e} mean-abs {mean:.2e} (8 sampled sequences)")
+
+
+def test_decode_batch_bs32_k128_v64_full():
+    """The bs32 batch with 64-wide values under its 128-wide keys, at the
+    benchmark's partition."""
+    case = W.decode_batch(2000, v_head_dim=64)
+    ref = oracle_decode(case)
+    for ps in (BENCH_PARTITION, 512):
+        log(f"decode batch 32 x U[512,4096], key dim 128, value dim 64, partition={ps}")
+        _, got = _run(case, ps)
+        mx, mean = assert_close(got, ref, W.BF16, f"bs32 k128 v64 ps{ps}")
+        print(f"bs32 k128 v64 ps={ps}: max-abs {mx:.2e} mean-abs {mean:.2e}")
 
 
 @pytest.mark.timeout(900)

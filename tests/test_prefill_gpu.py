@@ -41,6 +41,27 @@ def test_chunked_prefill_eight_heads_per_kv_head_full():
     print(f"chunked prefill 64q: max-abs {mx:.2e} mean-abs {mean:.2e}")
 
 
+def test_mixed_step_full_size():
+    """One full-size mixed step as the mixed scheduler policy issues it: 64
+    decode rows (one token each, contexts U[128, 4096]) and prompt chunks
+    (seven of 512 tokens and one of 448 over prefixes U[0, 2048]) in a single
+    4096-token prefill launch: 72 sequences, 576 (sequence, query tile)
+    items per kv head, the plain dispatch order."""
+    rng = np.random.default_rng(4242)
+    dec_ctx = rng.integers(128, 4097, size=64)
+    pro_prefix = rng.integers(0, 2049, size=8)
+    prefixes = [int(c) - 1 for c in dec_ctx] + [int(p) for p in pro_prefix]
+    qlens = [1] * 64 + [512] * 7 + [448]
+    assert sum(qlens) == 4096
+    case = W.random_prefill(4243, prefixes, qlens, num_heads=32, num_kv_heads=8, head_dim=128, block_size=32,
+                            dtype=W.BF16)
+    log("mixed step: 64 decode rows + 8 prompt chunks, 4096 tokens")
+    _, got = _run(case)
+    ref = oracle_prefill(case)
+    mx, mean = assert_close(got, ref, W.BF16, "mixed step")
+    print(f"mixed step: max-abs {mx:.2e} mean-abs {mean:.2e}")
+
+
 @pytest.mark.parametrize("scale", [0.37, 0.0, -0.05, 1.0 / 64])
 def test_prefill_other_scales(scale):
     """Scales other than 1/sqrt(head_dim), zero and negative included: the
