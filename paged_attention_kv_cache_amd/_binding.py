@@ -147,7 +147,9 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     with _lock:
         if _lib is not None and path is None:
             return _lib
-        p = path or LIB_PATH
+        # PA_LIBRARY names another build of the same library (the host
+        # sanitizer build runs the host test suites on it)
+        p = path or os.environ.get("PA_LIBRARY") or LIB_PATH
         # torch first: the library needs libamdhip64.so.7, which torch's own
         # HIP runtime provides once torch is imported.  Loaded before torch,
         # the library would bring up a second HIP runtime in the process,

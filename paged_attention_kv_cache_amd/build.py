@@ -48,10 +48,12 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (set HIPCC or install ROCm)")
 
 
-def _compile(src: str, extra: list[str], build_dir: str = BUILD) -> str:
+def _compile(src: str, extra: list[str], build_dir: str = BUILD, host_cxx: str | None = None,
+             host_extra: list[str] | None = None) -> str:
     obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
     if src in HOST_SOURCES:
-        cmd = [os.environ.get("CXX", "g++"), *HOST_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [host_cxx or os.environ.get("CXX", "g++"), *HOST_FLAGS, *(host_extra or []),
+               "-c", os.path.join(CSRC, src), "-o", obj]
     else:
         cmd = [hipcc(), *COMMON_FLAGS, *SOURCE_FLAGS.get(src, []), *extra, "-c", os.path.join(CSRC, src), "-o", obj]
         if src.endswith(".cpp"):
@@ -63,17 +65,21 @@ def _compile(src: str, extra: list[str], build_dir: str = BUILD) -> str:
 
 
 def build(verbose: bool = False, extra_flags: list[str] | None = None, out_path: str | None = None,
-          build_dir: str | None = None) -> str:
+          build_dir: str | None = None, host_cxx: str | None = None, host_extra: list[str] | None = None,
+          link_extra: list[str] | None = None) -> str:
     """Compile every source and link the library (default: in-tree next to
-    this file).  ``extra_flags`` go to every compile, e.g. ``-DNAME=value``."""
+    this file).  ``extra_flags`` go to every hipcc compile, e.g.
+    ``-DNAME=value``; ``host_cxx`` / ``host_extra`` replace the compiler of
+    the plain C++ sources and add flags to it; ``link_extra`` goes to the
+    link step."""
     bdir = build_dir or BUILD
     out = out_path or LIB_PATH
     os.makedirs(bdir, exist_ok=True)
     extra = list(extra_flags or [])
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, extra, bdir), SOURCES))
+        objs = list(ex.map(lambda s: _compile(s, extra, bdir, host_cxx, host_extra), SOURCES))
     tmp = out + ".tmp"
-    cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
+    cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, *(link_extra or []), "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"linking failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

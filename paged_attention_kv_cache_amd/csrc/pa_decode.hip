@@ -370,25 +370,16 @@ decode_partition_kernel(const DecodeKernelArgs a) {
 //  * the K and V loads of a wave's next chunk are issued as soon as the
 //    registers of the current chunk are consumed, so they overlap the
 //    softmax and P.V work of the current chunk.
-#ifndef PA_DECODE_UNROLL
-#define PA_DECODE_UNROLL 8
-#endif
-#ifndef PA_DECODE_UNROLL_WIDE
-#define PA_DECODE_UNROLL_WIDE 4  // more than 32 accumulators per lane: fewer loads in flight, fewer registers
-#endif
-#ifndef PA_DECODE_WAVES
-#define PA_DECODE_WAVES 4
-#endif
-// grid order of the partition kernel: 1 = kv head fastest, then sequence,
-// then partition, so that the partitions that exist for every sequence are
-// dispatched first and the empty ones (past short contexts) come last;
-// 3 = kv head fastest, then the (sequence, partition) pairs by size: every
-// full partition first, then the partial last partitions, longest first, so
-// that the work-groups dispatched last are the short ones (batches of at
-// most 64 sequences; larger ones keep order 1)
-#ifndef PA_DECODE_ORDER
-#define PA_DECODE_ORDER 3
-#endif
+constexpr int kDecodeUnroll = 8;      // tokens per wave step
+constexpr int kDecodeUnrollWide = 4;  // more than 32 accumulators per lane: fewer loads in flight, fewer registers
+constexpr int kDecodeWaves = 4;       // waves per work-group
+// Grid order of the partition kernels: kv head fastest, then the
+// (sequence, partition) pairs by size: every full partition first, then the
+// partial last partitions, longest first, so that the work-groups
+// dispatched last are the short ones (batches of at most 64 sequences;
+// larger ones, and cascade launches, take sequence then partition, so that
+// the partitions that exist for every sequence are dispatched first and
+// the empty ones past short contexts come last).
 
 // Reduce-scatter of G per-lane partial sums over a row of L lanes.  Slot j
 // of lane c holds the partial sum of head j ^ (c % G) (the query heads are
@@ -522,12 +513,6 @@ __device__ __forceinline__ void chunk_rows(size_t (&off)[U], bool (&ok)[U], cons
 // Unconditional loads: a lane past the context still reads inside the
 // pool (its own row of the same block, or the first row of the pool when
 // the block id is invalid), and its values are discarded by selects.
-#ifndef PA_DECODE_PRIO
-#define PA_DECODE_PRIO 0
-#endif
-#ifndef PA_DECODE_NT
-#define PA_DECODE_NT 1
-#endif
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 
 template <int U>
@@ -536,12 +521,8 @@ __device__ __forceinline__ void chunk_load(uint4 (&buf)[U], const size_t (&off)[
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const char *ptr = reinterpret_cast<const char *>(base + off[u]) + lane_bytes;
-#if PA_DECODE_NT
     const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(ptr));
     buf[u] = make_uint4(v.x, v.y, v.z, v.w);
-#else
-    buf[u] = *reinterpret_cast<const uint4 *>(ptr);
-#endif
   }
 }
 
@@ -579,9 +560,9 @@ struct Bf16Decode {
   static constexpr int R = 64 / L;  // token rows per load instruction
   static constexpr int EV = DV / L; // V elements per lane
   static constexpr int VW = EV / 2; // V words (bf16 pairs) per lane
-  static constexpr int U = (G * EV > 32) ? PA_DECODE_UNROLL_WIDE : PA_DECODE_UNROLL;
+  static constexpr int U = (G * EV > 32) ? kDecodeUnrollWide : kDecodeUnroll;
   static constexpr int CH = R * U;  // tokens per wave step
-  static constexpr int W = PA_DECODE_WAVES;
+  static constexpr int W = kDecodeWaves;
   static_assert(U % 2 == 0, "tokens are paired for the P.V dot products");
   static_assert(VW == 2 || VW == 4 || VW == 8, "8, 16 or 32 bytes of V per lane");
 
@@ -629,9 +610,6 @@ struct Bf16Decode {
                        a.max_blocks_per_seq);
       uint4 kr[U];
       uint32_t vr[U][VW];
-#if PA_DECODE_PRIO
-      __builtin_amdgcn_s_setprio(3);
-#endif
       chunk_load<U>(kr, off, kbase, lane_bytes);
       if constexpr (DV == D) {
         uint4 v4[U];
@@ -645,9 +623,6 @@ struct Bf16Decode {
         for (int u = 0; u < U; ++u) voff[u] = (DV > D) ? off[u] << 1 : off[u] >> 1;
         chunk_load_words<U, VW>(vr, voff, vbase, vlane_bytes);
       }
-#if PA_DECODE_PRIO
-      __builtin_amdgcn_s_setprio(0);
-#endif
       bool valid[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) valid[u] = ok[u] && (cbase + u * R + row < p1);
@@ -856,8 +831,8 @@ struct Bf16DecodeRows {
   static constexpr int R = 64 / L;  // kv heads per load instruction
   static constexpr int EV = DV / L; // V elements per lane
   static constexpr int VW = EV / 2; // V words (bf16 pairs) per lane
-  static constexpr int U = (G * EV > 32) ? PA_DECODE_UNROLL_WIDE : PA_DECODE_UNROLL;  // tokens per wave step
-  static constexpr int W = PA_DECODE_WAVES;
+  static constexpr int U = (G * EV > 32) ? kDecodeUnrollWide : kDecodeUnroll;  // tokens per wave step
+  static constexpr int W = kDecodeWaves;
   static_assert(U % 2 == 0, "tokens are paired for the P.V dot products");
   static_assert(VW == 2 || VW == 4 || VW == 8, "8, 16 or 32 bytes of V per lane");
 
@@ -1150,13 +1125,12 @@ __device__ __forceinline__ bool size_order_item(const DecodeKernelArgs &a, int i
 }
 
 template <int D, int DV, int G>
-__global__ void __launch_bounds__(64 * PA_DECODE_WAVES)
+__global__ void __launch_bounds__(64 * kDecodeWaves)
 // four work-groups per CU while the accumulators fit (up to G = 4 at DV <= D)
 __attribute__((amdgpu_waves_per_eu((G <= 4 && G * (DV / (D / 8)) <= 32) ? 4 : 1)))
 decode_partition_bf16_kernel(const DecodeKernelArgs a) {
   using K = Bf16Decode<D, DV, G>;
   constexpr int W = K::W;
-#if PA_DECODE_ORDER == 3
   const int kvh = blockIdx.x;
   int seq = blockIdx.y;
   int part = blockIdx.z;
@@ -1174,15 +1148,6 @@ decode_partition_bf16_kernel(const DecodeKernelArgs a) {
     seq = s_map[0];
     part = s_map[1];
   }
-#elif PA_DECODE_ORDER == 1
-  const int kvh = blockIdx.x;
-  const int seq = blockIdx.y;
-  const int part = blockIdx.z;
-#else
-  const int part = blockIdx.x;
-  const int kvh = blockIdx.y;
-  const int seq = blockIdx.z;
-#endif
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
 
@@ -1233,7 +1198,7 @@ decode_partition_bf16_kernel(const DecodeKernelArgs a) {
 // The partition kernel on Bf16DecodeRows: work-group (kv head group,
 // sequence, partition), the kv head group being R consecutive kv heads.
 template <int D, int DV, int G>
-__global__ void __launch_bounds__(64 * PA_DECODE_WAVES)
+__global__ void __launch_bounds__(64 * kDecodeWaves)
 __attribute__((amdgpu_waves_per_eu((G <= 4 && G * (DV / (D / 8)) <= 32) ? 4 : 1)))
 decode_partition_rows_kernel(const DecodeKernelArgs a) {
   using K = Bf16DecodeRows<D, DV, G>;
@@ -1471,12 +1436,10 @@ static hipError_t launch_partition_t(const DecodeArgs &a, hipStream_t stream) {
       // rows across kv heads: R = 4 kv heads per work-group
       constexpr int R = Bf16DecodeRows<D, DV, G>::R;
       grid = dim3((a.cache.num_kv_heads + R - 1) / R, a.num_seqs, a.max_partitions);
-      hipLaunchKernelGGL((decode_partition_rows_kernel<D, DV, G>), grid, dim3(64 * PA_DECODE_WAVES), 0, stream, k);
+      hipLaunchKernelGGL((decode_partition_rows_kernel<D, DV, G>), grid, dim3(64 * kDecodeWaves), 0, stream, k);
     } else {
-#if PA_DECODE_ORDER == 1 || PA_DECODE_ORDER == 3
       grid = dim3(a.cache.num_kv_heads, a.num_seqs, a.max_partitions);
-#endif
-      hipLaunchKernelGGL((decode_partition_bf16_kernel<D, DV, G>), grid, dim3(64 * PA_DECODE_WAVES), 0, stream, k);
+      hipLaunchKernelGGL((decode_partition_bf16_kernel<D, DV, G>), grid, dim3(64 * kDecodeWaves), 0, stream, k);
     }
   } else {
     // (cascade launches are bf16: never here)

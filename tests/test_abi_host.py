@@ -47,7 +47,7 @@ def test_header_declares_the_expected_entry_points():
 
 
 def test_library_exports_every_declared_symbol(lib):
-    out = subprocess.run(["nm", "-D", "--defined-only", P.LIB_PATH], capture_output=True, text=True).stdout
+    out = subprocess.run(["nm", "-D", "--defined-only", lib._name], capture_output=True, text=True).stdout
     exported = set(re.findall(r"\bT\s+(pa_[a-z0-9_]+)\b", out))
     for name in declared_functions():
         assert name in exported, f"{name} declared in include/ but not exported"

@@ -1,0 +1,18 @@
+"""The host suites (block manager, scheduler, C ABI argument checks) again,
+on a build of the library whose host code carries AddressSanitizer and
+UndefinedBehaviorSanitizer: any out-of-bounds access, use after free or
+undefined arithmetic in the host code aborts the inner run.  CPU only."""
+
+import os
+import shutil
+
+import pytest
+
+from paged_attention_kv_cache_amd import sanitize
+
+
+@pytest.mark.skipif(not os.path.isdir(sanitize.LLVM) or shutil.which("nm") is None,
+                    reason="needs the ROCm clang and its sanitizer runtime")
+def test_host_suites_clean_under_asan_and_ubsan():
+    sanitize.build_sanitized(verbose=False)
+    assert sanitize.run_suites() == 0
