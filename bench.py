@@ -631,7 +631,7 @@ def run_only(args):
     elif name == "decode_batch_bs32_ctx4096":
         r = bench_decode_secondary(name, 1024, case=W.decode_batch(2000, poison=False, fixed_ctx=4096))
     elif name == "decode_batch_bs32_64q_8kv":
-        r = bench_decode_secondary(name, 512, case=W.decode_batch(2000, poison=False, num_heads=64))
+        r = bench_decode_secondary(name, 192, case=W.decode_batch(2000, poison=False, num_heads=64))
     elif name == "decode_batch_bs32_k128_v64":
         r = bench_decode_secondary(name, 192, case=W.decode_batch(2000, poison=False, v_head_dim=64))
     else:
@@ -850,7 +850,7 @@ def main():
             bench_decode_secondary("decode_batch_bs32_ctx4096", 1024,
                                    case=W.decode_batch(2000, poison=False, fixed_ctx=4096)),
             # eight query heads per kv head: 64 q over the same 8 kv heads and K/V bytes
-            bench_decode_secondary("decode_batch_bs32_64q_8kv", 512,
+            bench_decode_secondary("decode_batch_bs32_64q_8kv", 192,
                                    case=W.decode_batch(2000, poison=False, num_heads=64)),
             # a value head dim of its own: 128-wide keys, 64-wide values
             bench_decode_secondary("decode_batch_bs32_k128_v64", 192,

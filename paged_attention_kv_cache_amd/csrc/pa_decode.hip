@@ -43,7 +43,11 @@
 //    heads instead of tokens (Bf16DecodeRows): a work-group covers 4 kv
 //    heads, and each load instruction reads one token's rows of those 4
 //    heads, 1 KB contiguous, instead of 256-byte slices at the 2 KB token
-//    stride.  Long and uniform contexts read 3-6% faster this way.
+//    stride.  Long and uniform contexts read 3-6% faster this way.  Each
+//    wave keeps its next step's K and V loads in flight while it computes
+//    the current step (two register sets), and the four waves' totals are
+//    merged in a tree through two LDS slots, which keeps the staging of
+//    eight query heads per kv head at 33 KB (three work-groups per CU).
 #include <type_traits>
 
 #include "pa_common.h"
@@ -373,6 +377,8 @@ decode_partition_kernel(const DecodeKernelArgs a) {
 constexpr int kDecodeUnroll = 8;      // tokens per wave step
 constexpr int kDecodeUnrollWide = 4;  // more than 32 accumulators per lane: fewer loads in flight, fewer registers
 constexpr int kDecodeWaves = 4;       // waves per work-group
+constexpr int kRowsUnroll = 4;        // the same for the row-layout kernel, which pipelines two steps
+constexpr int kRowsUnrollWide = 2;
 // Grid order of the partition kernels: kv head fastest, then the
 // (sequence, partition) pairs by size: every full partition first, then the
 // partial last partitions, longest first, so that the work-groups
@@ -831,7 +837,8 @@ struct Bf16DecodeRows {
   static constexpr int R = 64 / L;  // kv heads per load instruction
   static constexpr int EV = DV / L; // V elements per lane
   static constexpr int VW = EV / 2; // V words (bf16 pairs) per lane
-  static constexpr int U = (G * EV > 32) ? kDecodeUnrollWide : kDecodeUnroll;  // tokens per wave step
+  // tokens per wave step (two steps' rows are held at once)
+  static constexpr int U = (G * EV > 32) ? kRowsUnrollWide : kRowsUnroll;
   static constexpr int W = kDecodeWaves;
   static_assert(U % 2 == 0, "tokens are paired for the P.V dot products");
   static_assert(VW == 2 || VW == 4 || VW == 8, "8, 16 or 32 bytes of V per lane");
@@ -861,15 +868,11 @@ struct Bf16DecodeRows {
       }
     }
     const float sl = a.scale_log2;
-    const size_t slot_stride = (size_t)a.num_kv_heads * D;    // K elements per token slot
-    const size_t vslot_stride = (size_t)a.num_kv_heads * DV;  // V elements per token slot
     const uint16_t *kbase = static_cast<const uint16_t *>(a.k_cache);
     const uint16_t *vbase = static_cast<const uint16_t *>(a.v_cache);
     const uint32_t lane_bytes = (uint32_t)(((size_t)kvh * D + (size_t)col * 8) * 2);
     const uint32_t vlane_bytes = (uint32_t)(((size_t)kvh * DV + (size_t)col * EV) * 2);
     const ro_i32_ptr tab = read_only(a.block_tables + (size_t)seq * a.max_blocks_per_seq);
-    const int shift = a.block_shift;
-    const int bs_mask = (1 << shift) - 1;
 
     m = -INFINITY;
     l = 0.f;
@@ -880,91 +883,125 @@ struct Bf16DecodeRows {
 
     const int ntok = p1 - p0;
     const int nchunks = ntok > 0 ? (ntok + U - 1) / U : 0;
-    for (int c = wave; c < nchunks; c += W) {
-      const int cbase = p0 + c * U;
-      // token u of the step: its slot (0, the pool start, when it lies
-      // past the range or in a block outside the pool); the same for the
-      // whole wave
-      size_t off[U], voff[U];
-      bool ok[U];
-      int blk[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) blk[u] = tab[min((cbase + u) >> shift, a.max_blocks_per_seq - 1)];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int tok = cbase + u;
-        ok[u] = (tok < p1) && ((unsigned)blk[u] < (unsigned)a.num_blocks);
-        const size_t slot = ok[u] ? (((size_t)(uint32_t)blk[u] << shift) + (size_t)(tok & bs_mask)) : 0;
-        off[u] = slot * slot_stride;
-        voff[u] = slot * vslot_stride;
-      }
-      uint4 kr[U];
-      uint32_t vr[U][VW];
-      chunk_load<U>(kr, off, kbase, lane_bytes);
-      chunk_load_words<U, VW>(vr, voff, vbase, vlane_bytes);
+    // Software pipeline: a wave's next step (c + W) has its K and V loads
+    // in flight while the current step is computed, two register sets
+    // taking turns.
+    Step sa, sb;
+    int c = wave;
+    if (c >= nchunks) return;
+    issue(a, tab, p0, p1, c, kbase, vbase, lane_bytes, vlane_bytes, sa);
+    while (true) {
+      if (c + W < nchunks) issue(a, tab, p0, p1, c + W, kbase, vbase, lane_bytes, vlane_bytes, sb);
+      consume(sa, qp, sl, col, m, l, acc);
+      c += W;
+      if (c >= nchunks) break;
+      if (c + W < nchunks) issue(a, tab, p0, p1, c + W, kbase, vbase, lane_bytes, vlane_bytes, sa);
+      consume(sb, qp, sl, col, m, l, acc);
+      c += W;
+      if (c >= nchunks) break;
+    }
+  }
 
-      float s[U];
+  // One wave step's loaded rows: U tokens' K (16 bytes per lane) and V
+  // slices, and whether each token is inside the range and its block id
+  // inside the pool.
+  struct Step {
+    uint4 kr[U];
+    uint32_t vr[U][VW];
+    bool ok[U];
+  };
+
+  // Issue the loads of step c (tokens p0 + c*U ..): token u's slot (0,
+  // the pool start, when it lies past the range or in a block outside the
+  // pool), the same for the whole wave.
+  __device__ static __forceinline__ void issue(const DecodeKernelArgs &a, ro_i32_ptr tab, int p0, int p1, int c,
+                                               const uint16_t *kbase, const uint16_t *vbase, uint32_t lane_bytes,
+                                               uint32_t vlane_bytes, Step &st) {
+    const int shift = a.block_shift;
+    const int bs_mask = (1 << shift) - 1;
+    const size_t slot_stride = (size_t)a.num_kv_heads * D;    // K elements per token slot
+    const size_t vslot_stride = (size_t)a.num_kv_heads * DV;  // V elements per token slot
+    const int cbase = p0 + c * U;
+    size_t off[U], voff[U];
+    int blk[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        float d[G];
+    for (int u = 0; u < U; ++u) blk[u] = tab[min((cbase + u) >> shift, a.max_blocks_per_seq - 1)];
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-          float t = dot2_bf16(qp[h][0], kr[u].x, 0.f);
-          t = dot2_bf16(qp[h][1], kr[u].y, t);
-          t = dot2_bf16(qp[h][2], kr[u].z, t);
-          d[h] = dot2_bf16(qp[h][3], kr[u].w, t);
-        }
-        const float r = row_scatter_sum<L, G>(d);
-        s[u] = ok[u] ? r * sl : -INFINITY;
+    for (int u = 0; u < U; ++u) {
+      const int tok = cbase + u;
+      st.ok[u] = (tok < p1) && ((unsigned)blk[u] < (unsigned)a.num_blocks);
+      const size_t slot = st.ok[u] ? (((size_t)(uint32_t)blk[u] << shift) + (size_t)(tok & bs_mask)) : 0;
+      off[u] = slot * slot_stride;
+      voff[u] = slot * vslot_stride;
+    }
+    chunk_load<U>(st.kr, off, kbase, lane_bytes);
+    chunk_load_words<U, VW>(st.vr, voff, vbase, vlane_bytes);
+  }
+
+  // Scores, online softmax and P.V of one loaded step.
+  __device__ static __forceinline__ void consume(Step &st, const uint32_t (&qp)[G][4], float sl, int col, float &m,
+                                                 float &l, float (&acc)[G][EV]) {
+    float s[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float d[G];
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float t = dot2_bf16(qp[h][0], st.kr[u].x, 0.f);
+        t = dot2_bf16(qp[h][1], st.kr[u].y, t);
+        t = dot2_bf16(qp[h][2], st.kr[u].z, t);
+        d[h] = dot2_bf16(qp[h][3], st.kr[u].w, t);
       }
-      float cm = s[0];
+      const float r = row_scatter_sum<L, G>(d);
+      s[u] = st.ok[u] ? r * sl : -INFINITY;
+    }
+    float cm = s[0];
 #pragma unroll
-      for (int u = 1; u < U; ++u) cm = fmaxf(cm, s[u]);
-      // lazy rescale, per lane (each lane's row is one kv head; the lanes
-      // of a row with the same head index hold the same values)
-      const bool grow = cm > m + kDecodeRescaleSlack;
-      if (__builtin_amdgcn_ballot_w64(grow)) {
-        const float alpha = grow ? fast_exp2(m - cm) : 1.f;  // 0 when m is -inf
-        m = grow ? cm : m;
-        l *= alpha;
-        float ah[G];
-        every_head<G>(alpha, col, ah);
+    for (int u = 1; u < U; ++u) cm = fmaxf(cm, s[u]);
+    // lazy rescale, per lane (each lane's row is one kv head; the lanes
+    // of a row with the same head index hold the same values)
+    const bool grow = cm > m + kDecodeRescaleSlack;
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+      const float alpha = grow ? fast_exp2(m - cm) : 1.f;  // 0 when m is -inf
+      m = grow ? cm : m;
+      l *= alpha;
+      float ah[G];
+      every_head<G>(alpha, col, ah);
 #pragma unroll
-        for (int h = 0; h < G; ++h)
+      for (int h = 0; h < G; ++h)
 #pragma unroll
-          for (int e = 0; e < EV; ++e) acc[h][e] *= ah[h];
+        for (int e = 0; e < EV; ++e) acc[h][e] *= ah[h];
+    }
+    float p[U];
+    float psum = 0.f;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      p[u] = st.ok[u] ? fast_exp2(s[u] - m) : 0.f;
+      psum += p[u];
+    }
+    l += psum;
+    // a token outside the range (or in an invalid block) may hold
+    // anything, NaN included: zero its V so that weight 0 gives exactly 0
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (!st.ok[u]) {
+#pragma unroll
+        for (int j = 0; j < VW; ++j) st.vr[u][j] = 0;
       }
-      float p[U];
-      float psum = 0.f;
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        p[u] = ok[u] ? fast_exp2(s[u] - m) : 0.f;
-        psum += p[u];
+    for (int u = 0; u < U; u += 2) {
+      uint32_t vp[EV];
+#pragma unroll
+      for (int j = 0; j < VW; ++j) {
+        vp[2 * j] = interleave_lo(st.vr[u][j], st.vr[u + 1][j]);
+        vp[2 * j + 1] = interleave_hi(st.vr[u][j], st.vr[u + 1][j]);
       }
-      l += psum;
-      // a token outside the range (or in an invalid block) may hold
-      // anything, NaN included: zero its V so that weight 0 gives exactly 0
+      uint32_t pk[G];
+      every_head<G>(pack_bf16x2_rne(p[u], p[u + 1]), col, pk);
 #pragma unroll
-      for (int u = 0; u < U; ++u)
-        if (!ok[u]) {
+      for (int h = 0; h < G; ++h)
 #pragma unroll
-          for (int j = 0; j < VW; ++j) vr[u][j] = 0;
-        }
-#pragma unroll
-      for (int u = 0; u < U; u += 2) {
-        uint32_t vp[EV];
-#pragma unroll
-        for (int j = 0; j < VW; ++j) {
-          vp[2 * j] = interleave_lo(vr[u][j], vr[u + 1][j]);
-          vp[2 * j + 1] = interleave_hi(vr[u][j], vr[u + 1][j]);
-        }
-        uint32_t pk[G];
-        every_head<G>(pack_bf16x2_rne(p[u], p[u + 1]), col, pk);
-#pragma unroll
-        for (int h = 0; h < G; ++h)
-#pragma unroll
-          for (int e = 0; e < EV; ++e) acc[h][e] = dot2_bf16(pk[h], vp[e], acc[h][e]);
-      }
+        for (int e = 0; e < EV; ++e) acc[h][e] = dot2_bf16(pk[h], vp[e], acc[h][e]);
     }
   }
 
@@ -1027,44 +1064,99 @@ struct Bf16DecodeRows {
     }
   }
 
-  // LDS staging of the W waves' (m, l, acc) for every row's kv head
+  // The W = 4 waves' (m, l, acc) are merged in a tree through two wave
+  // slots of LDS: waves 2 and 3 park theirs, waves 0 and 1 fold them in,
+  // wave 1 parks the result, wave 0 folds it in and writes.  Two slots
+  // instead of four keep the staging of eight heads per kv head small
+  // enough for three work-groups per CU.
+  static_assert(W == 4, "the merge tree takes four waves");
   struct Stage {
-    float m[W][R][G];
-    float l[W][R][G];
-    float o[W][R][G][DV];
+    float m[2][R][G];
+    float l[2][R][G];
+    float o[2][R][G][DV];
   };
 
-  __device__ static __forceinline__ void stage(Stage &sm, int wave, int lane, float m, float l,
-                                               const float (&acc)[G][EV]) {
+  __device__ static __forceinline__ void put(Stage &sm, int slot, int lane, float m, float l,
+                                             const float (&acc)[G][EV]) {
     const int row = lane / L;
     const int col = lane % L;
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int e = 0; e < EV; ++e) sm.o[wave][row][h][col * EV + e] = acc[h][e];
+      for (int e = 0; e < EV; ++e) sm.o[slot][row][h][col * EV + e] = acc[h][e];
     if (col < G) {  // lane c of each row owns head c
-      sm.m[wave][row][col] = m;
-      sm.l[wave][row][col] = l;
+      sm.m[slot][row][col] = m;
+      sm.l[slot][row][col] = l;
     }
   }
 
-  // combine of output i = (row * G + h) * DV + d over the staged waves
-  __device__ static __forceinline__ void combine(const Stage &sm, int i, float &M, float &o, float &lt) {
-    const int row = i / (G * DV);
-    const int h = (i / DV) % G;
-    const int d = i % DV;
-    M = sm.m[0][row][h];
+  // this wave's totals merged with a parked slot's: M = max(m, m'),
+  // o = o 2^(m - M) + o' 2^(m' - M), l likewise (a side with no token has
+  // m = -inf and weight 0)
+  __device__ static __forceinline__ void merge(const Stage &sm, int slot, int lane, float &m, float &l,
+                                               float (&acc)[G][EV]) {
+    const int row = lane / L;
+    const int col = lane % L;
+    float mh[G];
+    every_head<G>(m, col, mh);
 #pragma unroll
-    for (int w = 1; w < W; ++w) M = fmaxf(M, sm.m[w][row][h]);
-    o = 0.f;
-    lt = 0.f;
-    if (M != -INFINITY) {
+    for (int h = 0; h < G; ++h) {
+      const float ms = sm.m[slot][row][h];
+      const float M = fmaxf(mh[h], ms);
+      const float fa = mh[h] == -INFINITY ? 0.f : fast_exp2(mh[h] - M);
+      const float fb = ms == -INFINITY ? 0.f : fast_exp2(ms - M);
 #pragma unroll
-      for (int w = 0; w < W; ++w) {
-        const float mw = sm.m[w][row][h];
-        const float f = (mw == -INFINITY) ? 0.f : fast_exp2(mw - M);
-        o = fmaf(sm.o[w][row][h][d], f, o);
-        lt = fmaf(sm.l[w][row][h], f, lt);
+      for (int e = 0; e < EV; ++e) acc[h][e] = fmaf(sm.o[slot][row][h][col * EV + e], fb, acc[h][e] * fa);
+    }
+    const int hh = col % G;  // this lane's own head
+    const float ms = sm.m[slot][row][hh];
+    const float M = fmaxf(m, ms);
+    const float fa = m == -INFINITY ? 0.f : fast_exp2(m - M);
+    const float fb = ms == -INFINITY ? 0.f : fast_exp2(ms - M);
+    l = fmaf(sm.l[slot][row][hh], fb, l * fa);
+    m = M;
+  }
+
+  // The merged totals of one wave: the output rows o / l (`direct`) or the
+  // partial (o, m, l) of partition slot `slot`, for every row's kv head
+  // below num_kv_heads.  Lane (row, col) holds dims col*EV .. col*EV+EV-1
+  // of every head of its row.
+  __device__ static __forceinline__ void write(const DecodeKernelArgs &a, int seq, int kvh0, int lane, float m,
+                                               float l, const float (&acc)[G][EV], bool direct, int slot) {
+    const int row = lane / L;
+    const int col = lane % L;
+    float lh[G];
+    every_head<G>(l, col, lh);
+    const int kvh = kvh0 + row;
+    if (kvh >= a.num_kv_heads) return;  // rows past the last kv head
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const size_t head = (size_t)seq * a.num_heads + (size_t)kvh * G + h;
+      if (direct) {
+        uint32_t w[EV / 2];
+#pragma unroll
+        for (int j = 0; j < EV / 2; ++j) {
+          const float r0 = lh[h] > 0.f ? acc[h][2 * j] / lh[h] : 0.f;
+          const float r1 = lh[h] > 0.f ? acc[h][2 * j + 1] / lh[h] : 0.f;
+          w[j] = pack_bf16x2(r0, r1);
+        }
+        uint16_t *dst = static_cast<uint16_t *>(a.out) + head * DV + (size_t)col * EV;
+        if constexpr (EV == 8) {
+          *reinterpret_cast<uint4 *>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+        } else {
+#pragma unroll
+          for (int j = 0; j < EV / 4; ++j) reinterpret_cast<uint2 *>(dst)[j] = make_uint2(w[2 * j], w[2 * j + 1]);
+        }
+      } else {
+        const size_t idx = head * a.max_partitions + slot;
+        float4 *dst = reinterpret_cast<float4 *>(a.ws_o + idx * DV + (size_t)col * EV);
+#pragma unroll
+        for (int j = 0; j < EV / 4; ++j)
+          dst[j] = make_float4(acc[h][4 * j], acc[h][4 * j + 1], acc[h][4 * j + 2], acc[h][4 * j + 3]);
+        if (col == h) {  // the lane whose own head is h
+          a.ws_m[idx] = m;
+          a.ws_l[idx] = l;
+        }
       }
     }
   }
@@ -1145,8 +1237,10 @@ decode_partition_bf16_kernel(const DecodeKernelArgs a) {
       }
     }
     __syncthreads();
-    seq = s_map[0];
-    part = s_map[1];
+    // uniform over the work-group: kept in scalar registers, so that every
+    // address derived from them is a scalar base plus the lane's offset
+    seq = __builtin_amdgcn_readfirstlane(s_map[0]);
+    part = __builtin_amdgcn_readfirstlane(s_map[1]);
   }
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
@@ -1199,10 +1293,11 @@ decode_partition_bf16_kernel(const DecodeKernelArgs a) {
 // sequence, partition), the kv head group being R consecutive kv heads.
 template <int D, int DV, int G>
 __global__ void __launch_bounds__(64 * kDecodeWaves)
-__attribute__((amdgpu_waves_per_eu((G <= 4 && G * (DV / (D / 8)) <= 32) ? 4 : 1)))
+// three work-groups per CU while the two steps' rows and the accumulators
+// fit (up to G = 4 at DV <= D)
+__attribute__((amdgpu_waves_per_eu((G <= 4 && G * (DV / (D / 8)) <= 32) ? 3 : 1)))
 decode_partition_rows_kernel(const DecodeKernelArgs a) {
   using K = Bf16DecodeRows<D, DV, G>;
-  constexpr int W = K::W;
   constexpr int R = K::R;
   const int kvh0 = blockIdx.x * R;
   int seq = blockIdx.y;
@@ -1218,8 +1313,10 @@ decode_partition_rows_kernel(const DecodeKernelArgs a) {
       }
     }
     __syncthreads();
-    seq = s_map[0];
-    part = s_map[1];
+    // uniform over the work-group: kept in scalar registers, so that every
+    // address derived from them is a scalar base plus the lane's offset
+    seq = __builtin_amdgcn_readfirstlane(s_map[0]);
+    part = __builtin_amdgcn_readfirstlane(s_map[1]);
   }
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
@@ -1241,28 +1338,15 @@ decode_partition_rows_kernel(const DecodeKernelArgs a) {
   if (append && wave == 0) K::attend_new(a, seq, kvh0, ctx - 1, lane, m, l, acc);
 
   __shared__ typename K::Stage sm;
-  K::stage(sm, wave, lane, m, l, acc);
+  if (wave >= 2) K::put(sm, wave - 2, lane, m, l, acc);
   __syncthreads();
-
-  const bool direct = !cascade && nparts == 1;
-  for (int i = threadIdx.x; i < R * G * DV; i += 64 * W) {
-    const int kvh = kvh0 + i / (G * DV);
-    if (kvh >= a.num_kv_heads) break;  // rows past the last kv head (i only grows)
-    float M, o, lt;
-    K::combine(sm, i, M, o, lt);
-    const int head = kvh * G + (i / DV) % G;
-    const int d = i % DV;
-    if (direct) {
-      const float r = (lt > 0.f) ? o / lt : 0.f;
-      store_one<bf16_t>(a.out, ((size_t)seq * a.num_heads + head) * DV + d, r);
-    } else {
-      const size_t idx = ((size_t)seq * a.num_heads + head) * a.max_partitions + slot;
-      a.ws_o[idx * DV + d] = o;
-      if (d == 0) {
-        a.ws_m[idx] = M;
-        a.ws_l[idx] = lt;
-      }
-    }
+  if (wave < 2) K::merge(sm, wave, lane, m, l, acc);
+  __syncthreads();
+  if (wave == 1) K::put(sm, 0, lane, m, l, acc);
+  __syncthreads();
+  if (wave == 0) {
+    K::merge(sm, 0, lane, m, l, acc);
+    K::write(a, seq, kvh0, lane, m, l, acc, !cascade && nparts == 1, slot);
   }
 }
 

@@ -82,10 +82,11 @@ def test_decode_batch_bs32_eight_heads_per_kv_head_full():
     """The bs32 batch with 64 query heads over its 8 kv heads (G = 8)."""
     case = W.decode_batch(2000, num_heads=64)
     ref = oracle_decode(case)
-    log("decode batch 32 x U[512,4096], 64 q / 8 kv heads, partition=512")
-    _, got = _run(case, 512)
-    mx, mean = assert_close(got, ref, W.BF16, "bs32 batch G8 ps512")
-    print(f"bs32 batch G=8: max-abs {mx:.2e} mean-abs {mean:.2e}")
+    for ps in (192, 512):
+        log(f"decode batch 32 x U[512,4096], 64 q / 8 kv heads, partition={ps}")
+        _, got = _run(case, ps)
+        mx, mean = assert_close(got, ref, W.BF16, f"bs32 batch G8 ps{ps}")
+        print(f"bs32 batch G=8 ps {ps}: max-abs {mx:.2e} mean-abs {mean:.2e}")
 
 
 def test_decode_batch_bs32_ctx4096_full_sampled():
@@ -182,25 +183,42 @@ def test_reduce_ignores_stale_workspace(dtype, group):
     assert np.array_equal(bits[0], bits[1])
 
 
-def test_no_cross_sequence_leakage():
-    """Each sequence's output in a batch equals the same sequence run alone,
-    bit for bit (same kernel configuration)."""
+@pytest.mark.parametrize("num_seqs", [5, 65])
+def test_no_cross_sequence_leakage(num_seqs):
+    """Each sequence reads only its own blocks: with every pool block that
+    sequence i does not own overwritten by NaN, row i of the batch keeps
+    its bits; and the sequence run alone gives the same bits as in the
+    batch.  Five sequences take the size-ordered dispatch, 65 the plain
+    order."""
+    import paged_attention_kv_cache_amd as P
     t = torch()
-    case = W.random_decode(31, [40, 1, 513, 2000, 77], num_heads=32, num_kv_heads=8, head_dim=128,
-                           block_size=16, dtype=W.BF16)
+    base = [40, 1, 513, 2000, 77]
+    ctx = (base * 13)[:num_seqs]
+    case = W.random_decode(31, ctx, num_heads=32, num_kv_heads=8, head_dim=128, block_size=16, dtype=W.BF16)
     dev = DeviceCase(case)
     dev.write()
     ps = 256
-    log("decode batch for leakage check")
+    log(f"decode batch of {num_seqs} for leakage check")
     full = to_host_bits(dev.decode(ps))
-    import paged_attention_kv_cache_amd as P
-    for i in range(case.num_seqs):
+    k0, v0 = dev.k_cache.clone(), dev.v_cache.clone()
+    nan = t.tensor(0x7FC0, dtype=t.int16).view(t.bfloat16).item()
+    for i in range(min(num_seqs, 5)):
+        nb = -(-ctx[i] // case.block_size)
+        own = set(int(b) for b in case.block_tables[i, :nb])
+        others = t.tensor([b for b in range(case.num_blocks) if b not in own], dtype=t.long, device="cuda")
+        dev.k_cache.copy_(k0)
+        dev.v_cache.copy_(v0)
+        dev.k_cache.index_fill_(0, others, nan)
+        dev.v_cache.index_fill_(0, others, nan)
+        log(f"decode with every block but sequence {i}'s set to NaN")
+        got = to_host_bits(dev.decode(ps))
+        assert np.array_equal(got[i], full[i]), f"sequence {i}"
         log(f"decode sequence {i} alone")
         one = P.pa_decode(dev.q[i:i + 1].contiguous(), dev.k_cache, dev.v_cache,
                           dev.block_tables[i:i + 1].contiguous(), dev.context_lens[i:i + 1].contiguous(),
                           case.scale, case.max_context_len, ps)
         t.cuda.synchronize()
-        assert np.array_equal(to_host_bits(one)[0], full[i]), f"sequence {i}"
+        assert np.array_equal(to_host_bits(one)[0], full[i]), f"sequence {i} alone"
 
 
 def _bf16(x):
@@ -335,6 +353,56 @@ def test_many_partitions():
         log(f"{-(-case.max_context_len // ps)} partitions")
         _, got = _run(case, ps)
         assert_close(got, ref, W.BF16, f"ps{ps}")
+
+
+
+BOUNDARY_CTX = [64, 64, 0, 128, 1, 63, 65, 200, 0, 3, 5, 7, 700, 64, 1, 130]
+
+
+@pytest.mark.parametrize("group,dims", [(1, (128, 128)), (4, (128, 128)), (8, (128, 128)), (4, (128, 64))])
+def test_partition_boundary_contexts(group, dims):
+    """Contexts of exactly one or two partitions, one token either side of
+    a partition boundary, 0 and 1 tokens, beside long ones (bf16, head dim
+    128, partitions of 64 and 128 tokens): pa_decode, its two stages over a
+    workspace of NaN bit patterns, and the fused append all agree with the
+    oracle, and the stages give the fused call's bits."""
+    import paged_attention_kv_cache_amd as P
+    t = torch()
+    D, Dv = dims
+    case = W.random_decode(8800 + group + Dv, BOUNDARY_CTX, num_heads=4 * group, num_kv_heads=4, head_dim=D,
+                           v_head_dim=Dv, block_size=16, dtype=W.BF16, extra_table_cols=1)
+    ref = oracle_decode(case)
+    dev = DeviceCase(case)
+    dev.write()
+    for ps in (64, 128):
+        log(f"boundary contexts G={group} D={D} Dv={Dv} partition={ps}")
+        need = P.pa_decode_workspace_bytes(len(BOUNDARY_CTX), 4 * group, Dv, case.max_context_len, ps)
+        ws = t.full((need,), 0xFF, dtype=t.uint8, device="cuda")
+        fused = dev.decode(ps, workspace=ws).clone()
+        t.cuda.synchronize()
+        got = to_host_f32(fused, W.BF16)
+        assert_close(got, ref, W.BF16, f"boundary G{group} ps{ps}")
+        for i, n in enumerate(BOUNDARY_CTX):
+            if n == 0:
+                assert np.array_equal(got[i], np.zeros_like(got[i]))
+        out = t.empty((len(BOUNDARY_CTX), 4 * group, Dv), dtype=fused.dtype, device="cuda")
+        args = (dev.q, dev.k_cache, dev.v_cache, dev.block_tables, dev.context_lens, case.scale,
+                case.max_context_len, ps)
+        P.pa_decode_partition(*args, out=out, workspace=ws)
+        P.pa_decode_reduce(*args, out=out, workspace=ws)
+        t.cuda.synchronize()
+        assert np.array_equal(to_host_bits(out), to_host_bits(fused))
+    k_ref, v_ref = oracle.kv_cache_write(case.k_cache, case.v_cache, case.new_key, case.new_value,
+                                         case.slot_mapping)
+    key, val = _append_rows(case)
+    log(f"boundary contexts, fused append G={group}")
+    dev2 = DeviceCase(case)
+    out = P.pa_decode_append(dev2.q, to_dev(key, W.BF16), to_dev(val, W.BF16), dev2.k_cache, dev2.v_cache,
+                             dev2.block_tables, dev2.context_lens, case.scale, case.max_context_len, 64)
+    t.cuda.synchronize()
+    assert_close(to_host_f32(out, W.BF16), ref, W.BF16, f"boundary append G{group}")
+    assert np.array_equal(to_host_bits(dev2.k_cache).view(np.uint16), k_ref.view(np.uint16)), "K pool"
+    assert np.array_equal(to_host_bits(dev2.v_cache).view(np.uint16), v_ref.view(np.uint16)), "V pool"
 
 
 # ------------------------------------------------------------ cascade decode
