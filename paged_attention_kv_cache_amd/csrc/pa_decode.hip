@@ -1182,15 +1182,35 @@ __device__ __forceinline__ bool size_order_item(const DecodeKernelArgs &a, int i
     for (int sft = 1; sft < 64; sft <<= 1) v += __shfl_xor(v, sft);
     return v;
   };
-  const int total_full = cum(a.max_partitions);
-  if (item < total_full) {
-    int lo = 0, hi = a.max_partitions - 1;  // the p with cum(p) <= item < cum(p+1)
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (cum(mid) <= item) lo = mid;
-      else hi = mid - 1;
+  // lane p holds cum(p) (up to 64 partitions): one pass over the
+  // sequences' counts in scalar registers instead of a cross-lane sum per
+  // step of a search
+  int cum_l = 0, total_full = 0;
+  if (a.max_partitions <= 64) {
+    for (int s = 0; s < S; ++s) {
+      const int nf = __builtin_amdgcn_readlane(nfull, s);
+      cum_l += min(nf, lane);
+      total_full += nf;
     }
-    const int k = item - cum(lo);
+  } else {
+    total_full = cum(a.max_partitions);
+  }
+  if (item < total_full) {
+    int lo;  // the p with cum(p) <= item < cum(p+1)
+    int k;
+    if (a.max_partitions <= 64) {
+      lo = __builtin_popcountll(__builtin_amdgcn_ballot_w64(lane < a.max_partitions && cum_l <= item)) - 1;
+      k = item - __builtin_amdgcn_readlane(cum_l, lo);
+    } else {
+      lo = 0;
+      int hi = a.max_partitions - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (cum(mid) <= item) lo = mid;
+        else hi = mid - 1;
+      }
+      k = item - cum(lo);
+    }
     const unsigned long long has = __builtin_amdgcn_ballot_w64(nfull > lo);
     const int rank = __builtin_amdgcn_mbcnt_hi((unsigned)(has >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)has, 0));
     const unsigned long long hit = __builtin_amdgcn_ballot_w64(nfull > lo && rank == k);
