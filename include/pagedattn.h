@@ -45,7 +45,10 @@
  *    block_id * block_size + offset.
  *  - Query head h reads kv head h / (num_heads / num_kv_heads).
  *  - `scale` multiplies every q.k dot product.  It is normally
- *    1/sqrt(head_dim).
+ *    1/sqrt(head_dim); any finite value is accepted, zero and negative
+ *    included, and every entry point applies it to the fp32 dot product
+ *    before the softmax takes its max (a non-finite scale returns
+ *    PA_ERR_SHAPE).
  *  - Element types: q, k_cache, v_cache and out share one dtype (fp32 or
  *    bf16).  Arithmetic is fp32 in either case.  bf16 outputs are rounded
  *    to nearest even.
