@@ -50,6 +50,39 @@ def test_decode_shapes(dtype, head_dim, group):
             assert_close(got, ref, dtype, f"{dtype} D{head_dim} G{group} bs{bs} ps{ps}")
 
 
+
+@pytest.mark.parametrize("hkv,group", [(1, 8), (3, 4), (5, 2), (6, 1), (12, 4)])
+def test_decode_kv_head_counts(hkv, group):
+    """Key head dim 128 reads the rows of 4 kv heads per load: kv-head
+    counts that are not a multiple of 4 leave rows past the last kv head in
+    the last work-group (they read a real head and are dropped), and 12 kv
+    heads make three groups.  bf16, both value widths, with and without
+    split-K and through the fused append."""
+    import paged_attention_kv_cache_amd as P
+    t = torch()
+    for dv in (128, 64):
+        case = W.random_decode(7100 + 10 * hkv + group + dv, [1, 33, 200, 513, 1100], num_heads=hkv * group,
+                               num_kv_heads=hkv, head_dim=128, v_head_dim=dv, block_size=16, dtype=W.BF16,
+                               extra_table_cols=1)
+        ref = oracle_decode(case)
+        dev = DeviceCase(case)
+        dev.write()
+        for ps in (0, 64, 256):
+            log(f"decode Hkv={hkv} G={group} Dv={dv} partition={ps}")
+            got = to_host_f32(dev.decode(ps), W.BF16)
+            assert_close(got, ref, W.BF16, f"Hkv{hkv} G{group} Dv{dv} ps{ps}")
+        key, val = _append_rows(case)
+        dev2 = DeviceCase(case)
+        log(f"decode append Hkv={hkv} G={group} Dv={dv}")
+        out = P.pa_decode_append(dev2.q, to_dev(key, W.BF16), to_dev(val, W.BF16), dev2.k_cache, dev2.v_cache,
+                                 dev2.block_tables, dev2.context_lens, case.scale, case.max_context_len, 64)
+        t.cuda.synchronize()
+        assert_close(to_host_f32(out, W.BF16), ref, W.BF16, f"append Hkv{hkv} G{group} Dv{dv}")
+        k_ref, v_ref = oracle.kv_cache_write(case.k_cache, case.v_cache, case.new_key, case.new_value,
+                                             case.slot_mapping)
+        assert np.array_equal(to_host_bits(dev2.k_cache).view(np.uint16), k_ref.view(np.uint16)), "K pool"
+        assert np.array_equal(to_host_bits(dev2.v_cache).view(np.uint16), v_ref.view(np.uint16)), "V pool"
+
 @pytest.mark.parametrize("dtype", [W.BF16, W.F32])
 @pytest.mark.parametrize("dims", [(128, 64), (64, 128)])
 @pytest.mark.parametrize("group", [1, 2, 4, 8])
