@@ -48,6 +48,13 @@
 //    the current step (two register sets), and the four waves' totals are
 //    merged in a tree through two LDS slots, which keeps the staging of
 //    eight query heads per kv head at 33 KB (three work-groups per CU).
+//    It serves separate value head dims and the own-token pass of cascade
+//    decode.
+//  * Plain bf16 decode with key and value head dims 128 runs on the matrix
+//    cores instead (Bf16DecodeMfma, below): per kv head, the scores of 16
+//    tokens and their weighted V rows are two small MFMA products, so the
+//    vector work per token no longer grows with the query heads per kv
+//    head.
 #include <type_traits>
 
 #include "pa_common.h"
@@ -1370,6 +1377,343 @@ decode_partition_rows_kernel(const DecodeKernelArgs a) {
   }
 }
 
+// ------------------------------------------------------------------------
+// Matrix-core decode (bf16, key and value head dim 128).  Per kv head, the
+// scores of a tile of 16 tokens and the tile's share of the weighted sum
+// are two small matrix products:
+//   S^T = K Q^T    on v_mfma_f32_16x16x32_bf16 (16 tokens x 16 columns, the
+//                  G query heads of the kv head as columns, the rest zero),
+//   O^T += V^T P^T on v_mfma_f32_16x16x16_bf16 (value dims x columns).
+// In the accumulator layout lane l holds column l % 16 and tokens
+// 4 (l / 16) .. 4 (l / 16) + 3 of S^T, which is also the B operand layout
+// of the second product, so the weights go from the exponentials straight
+// into the products.  The vector work per token (a scale, an exponential,
+// the max and the sum, shared by up to 16 heads) no longer grows with G.
+//  * One wave per kv head: a work-group (4 waves) covers 4 consecutive kv
+//    heads of one (sequence, partition), every wave all of the partition's
+//    tokens; no cross-wave merge.
+//  * A tile is loaded row-major, 4 tokens x the kv head's 256-byte row per
+//    load instruction (a scalar block id per instruction: a load's 4 tokens
+//    start at a multiple of 4 and share one block), into registers, and
+//    from there into the wave's own LDS slice; the registers then take the
+//    next tile's loads, which are in flight while the staged tile is
+//    computed.  One register set per wave leaves room for four work-groups
+//    per CU.  The score product reads K from LDS with one 16-byte read per
+//    lane and k-step, the value product V^T with gfx950's transposing 8-byte
+//    reads.  Rows are padded (K 272 bytes, V 288 bytes) so that both kinds
+//    of reads hit distinct banks.
+//  * Tokens outside the range, or in a block outside the pool, are
+//    selected out: score -inf, weight 0, and their V rows zeroed before
+//    they enter the product, whatever the slot holds.
+//  * The running max is a reference moved only when a tile exceeds it by
+//    more than 2^8, as in the row-layout kernel; the running sum takes the
+//    fp32 weights, the products their bf16 roundings (nearest even).
+//  * Fused append: the newest token's rows come from the input rows (they
+//    replace the loaded slot contents in registers) and are written into
+//    its slot after the last tile.
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) u32x4_t *lds_u4_ptr;
+typedef __attribute__((address_space(3))) const bf16x8_t *lds_b8_ptr;
+typedef __attribute__((address_space(3))) v4i16_t *lds_v4_ptr;
+
+template <int G, int TT = 16>
+struct Bf16DecodeMfma {
+  static constexpr int D = 128;
+  static constexpr int DV = 128;
+  static constexpr int MT = TT / 16;   // 16-token sub-tiles per tile
+  static constexpr int NL = TT / 4;    // K (and V) load instructions per tile: 4 tokens x 256 B each
+  static constexpr int NKS = D / 32;   // k-steps of the score product
+  static constexpr int NDT = DV / 16;  // 16-row tiles of O^T
+  static constexpr int KROW = 272;     // LDS bytes per K row: 16 rows at one chunk cover every bank
+  static constexpr int VROW = 288;     // LDS bytes per V row: the transposing reads of 8 rows cover every bank
+  static constexpr int KBYTES = TT * KROW;
+  static constexpr int LDS_BYTES = KBYTES + TT * VROW;  // one wave's slice
+  static_assert(TT % 16 == 0, "tiles of whole 16-token sub-tiles");
+  static_assert(G >= 1 && G <= 16, "the query heads of a kv head are columns of a 16-wide tile");
+
+  // One tile's rows: load j holds tokens t0 + 4j .. t0 + 4j + 3 (lane l:
+  // token t0 + 4j + l / 16, 16-byte chunk l % 16 of its row); bit j of ok:
+  // load j's first token is in range and its block inside the pool.
+  struct Tile {
+    uint4 k[NL];
+    uint4 v[NL];
+    int ok;
+  };
+
+  __device__ static __forceinline__ void issue(const DecodeKernelArgs &a, ro_i32_ptr tab, int t0, int p1,
+                                               const char *kbase, const char *vbase, uint32_t lane_off,
+                                               size_t slot_bytes, Tile &t) {
+    const int shift = a.block_shift;
+    const int bs_mask = (1 << shift) - 1;
+    int blk[NL];
+#pragma unroll
+    for (int j = 0; j < NL; ++j) blk[j] = tab[min((t0 + 4 * j) >> shift, a.max_blocks_per_seq - 1)];
+    int ok = 0;
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+      const int tok = t0 + 4 * j;
+      const bool good = (tok < p1) && ((unsigned)blk[j] < (unsigned)a.num_blocks);
+      ok |= good ? (1 << j) : 0;
+      // a load that is not attended reads the pool's first slots
+      const size_t off = good ? (((size_t)(uint32_t)blk[j] << shift) + (size_t)(tok & bs_mask)) * slot_bytes : 0;
+      const u32x4_t kv = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(kbase + off + lane_off));
+      const u32x4_t vv = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(vbase + off + lane_off));
+      t.k[j] = make_uint4(kv.x, kv.y, kv.z, kv.w);
+      t.v[j] = make_uint4(vv.x, vv.y, vv.z, vv.w);
+    }
+    t.ok = ok;
+  }
+
+  // Per-wave state.
+  struct State {
+    bf16x8_t qf[NKS];  // Q^T fragments: column l % 16, chunk 4 ks + l / 16 of that head's row
+    f32x4_t o[NDT];    // O^T: column l % 16, value dims 16 dt + 4 (l / 16) + r
+    float m, l;        // reference max (base-2 units) and this lane's part of the running sum
+  };
+
+  // The loaded tile at tokens t0 .. into the wave's LDS slice (row-major,
+  // padded rows).  Rows that are not attended get a zero V row; the
+  // appended token's rows come from the input.
+  __device__ static __forceinline__ void stage(Tile &t, int t0, int p1, int pnew, uint4 kn, uint4 vn, int lane,
+                                               uint32_t lds) {
+    const int g = lane >> 4;
+    const int c = lane & 15;
+    if (t.ok != (1 << NL) - 1 || t0 + TT > p1) {
+#pragma unroll
+      for (int j = 0; j < NL; ++j)
+        if (!(((t.ok >> j) & 1) && t0 + 4 * j + g < p1)) t.v[j] = make_uint4(0u, 0u, 0u, 0u);
+    }
+    if (pnew >= t0 && pnew < t0 + TT) {
+      const int tl = pnew - t0;
+#pragma unroll
+      for (int j = 0; j < NL; ++j)
+        if (j == (tl >> 2) && g == (tl & 3) && ((t.ok >> j) & 1)) {
+          t.k[j] = kn;
+          t.v[j] = vn;
+        }
+    }
+    const uint32_t kw = lds + (uint32_t)(g * KROW + c * 16);
+    const uint32_t vw = lds + (uint32_t)(KBYTES + g * VROW + c * 16);
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+      *(lds_u4_ptr)(size_t)(kw + j * 4 * KROW) = u32x4_t{t.k[j].x, t.k[j].y, t.k[j].z, t.k[j].w};
+      *(lds_u4_ptr)(size_t)(vw + j * 4 * VROW) = u32x4_t{t.v[j].x, t.v[j].y, t.v[j].z, t.v[j].w};
+    }
+  }
+
+  // Scores, online softmax and P.V of the tile at tokens t0 .. staged in
+  // LDS (ok: its loads' bits).
+  __device__ static __forceinline__ void compute(int ok, int t0, int p1, float sl, int lane, uint32_t lds,
+                                                 State &st) {
+    const int g = lane >> 4;
+    const int c = lane & 15;
+    // S^T = K Q^T per sub-tile: A = K rows (lane: token 16 mt + c, chunk
+    // 4 ks + g)
+    const uint32_t kr = lds + (uint32_t)(c * KROW + g * 16);
+    f32x4_t s[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      s[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const bf16x8_t kf = *(lds_b8_ptr)(size_t)(kr + mt * 16 * KROW + ks * 64);
+        s[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, st.qf[ks], s[mt], 0, 0, 0);
+      }
+    }
+    // weights of column c for tokens 16 mt + 4g .. 16 mt + 4g + 3 (loaded
+    // by load 4 mt + g)
+    float sv[MT][4];
+    bool vok[MT][4];
+    float cm = -INFINITY;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const bool row_ok = (ok >> (4 * mt + g)) & 1;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        vok[mt][r] = row_ok && (t0 + 16 * mt + 4 * g + r < p1);
+        sv[mt][r] = vok[mt][r] ? s[mt][r] * sl : -INFINITY;
+        cm = fmaxf(cm, sv[mt][r]);
+      }
+    }
+    cm = xor32_max(xor16_max(cm));  // the column's max over the tile
+    const bool grow = cm > st.m + kDecodeRescaleSlack;
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+      const float alpha = grow ? fast_exp2(st.m - cm) : 1.f;  // 0 when m is -inf
+      st.m = grow ? cm : st.m;
+      st.l *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) st.o[dt] *= alpha;
+    }
+    // O^T += V^T P^T per sub-tile: A = V^T from transposing reads.  In
+    // 16-lane group g, lane c sends the address of 4 value dims of one
+    // token (token 16 mt + 4g + c / 4, dims 16 dt + 4 (c % 4)) and receives
+    // dim 16 dt + c of tokens 16 mt + 4g .. 16 mt + 4g + 3.
+    const uint32_t vr = lds + (uint32_t)(KBYTES + (4 * g + (c >> 2)) * VROW + (c & 3) * 8);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      float p[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) p[r] = vok[mt][r] ? fast_exp2(sv[mt][r] - st.m) : 0.f;
+      st.l += (p[0] + p[1]) + (p[2] + p[3]);
+      const uint32_t p01 = pack_bf16x2_rne(p[0], p[1]);
+      const uint32_t p23 = pack_bf16x2_rne(p[2], p[3]);
+      const v4i16_t pb = __builtin_bit_cast(v4i16_t, make_uint2(p01, p23));
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const v4i16_t vf =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4_ptr)(size_t)(vr + mt * 16 * VROW + dt * 32));
+        st.o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf, pb, st.o[dt], 0, 0, 0);
+      }
+    }
+  }
+
+  // Online softmax of kv head kvh's query heads over tokens p0 .. p1-1 of
+  // sequence seq; pnew (or -1): the appended token, whose rows are kn, vn.
+  __device__ static __forceinline__ void attend(const DecodeKernelArgs &a, int seq, int kvh, int p0, int p1,
+                                                int pnew, uint4 kn, uint4 vn, int lane, uint32_t lds, State &st) {
+    const int g = lane >> 4;
+    const int c = lane & 15;
+    {
+      const uint4 *qrow = reinterpret_cast<const uint4 *>(
+          static_cast<const uint16_t *>(a.q) + ((size_t)seq * a.num_heads + (size_t)kvh * G + (c < G ? c : 0)) * D);
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const uint4 w = c < G ? qrow[4 * ks + g] : make_uint4(0u, 0u, 0u, 0u);
+        st.qf[ks] = __builtin_bit_cast(bf16x8_t, w);
+      }
+    }
+    st.m = -INFINITY;
+    st.l = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) st.o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const int ntiles = p1 > p0 ? (p1 - p0 + TT - 1) / TT : 0;
+    if (ntiles == 0) return;
+
+    const float sl = a.scale_log2;
+    const size_t slot_bytes = (size_t)a.num_kv_heads * D * 2;
+    const uint32_t lane_off = (uint32_t)((size_t)g * slot_bytes + (size_t)kvh * D * 2 + (size_t)c * 16);
+    const char *kbase = static_cast<const char *>(a.k_cache);
+    const char *vbase = static_cast<const char *>(a.v_cache);
+    const ro_i32_ptr tab = read_only(a.block_tables + (size_t)seq * a.max_blocks_per_seq);
+    // One register set: once a tile is in LDS its registers take the next
+    // tile's loads, which are in flight while the staged tile is computed.
+    Tile t;
+    issue(a, tab, p0, p1, kbase, vbase, lane_off, slot_bytes, t);
+    for (int i = 0; i < ntiles; ++i) {
+      const int t0 = p0 + i * TT;
+      stage(t, t0, p1, pnew, kn, vn, lane, lds);
+      const int ok = t.ok;
+      if (i + 1 < ntiles) issue(a, tab, t0 + TT, p1, kbase, vbase, lane_off, slot_bytes, t);
+      compute(ok, t0, p1, sl, lane, lds, st);
+    }
+  }
+
+  // The wave's totals: the output rows o / l (direct) or the partial
+  // (o, m, l) of partition slot `slot`, for the G heads of kv head kvh.
+  __device__ static __forceinline__ void write(const DecodeKernelArgs &a, int seq, int kvh, int lane, State &st,
+                                               bool direct, int slot) {
+    const int g = lane >> 4;
+    const int c = lane & 15;
+    const float lt = xor32_sum(xor16_sum(st.l));  // the column's sum over the four rows of lanes
+    if (c >= G) return;
+    const size_t head = (size_t)seq * a.num_heads + (size_t)kvh * G + c;
+    if (direct) {
+      uint16_t *dst = static_cast<uint16_t *>(a.out) + head * DV + 4 * g;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const f32x4_t v = st.o[dt];
+        const float r0 = lt > 0.f ? v[0] / lt : 0.f;
+        const float r1 = lt > 0.f ? v[1] / lt : 0.f;
+        const float r2 = lt > 0.f ? v[2] / lt : 0.f;
+        const float r3 = lt > 0.f ? v[3] / lt : 0.f;
+        *reinterpret_cast<uint2 *>(dst + 16 * dt) = make_uint2(pack_bf16x2(r0, r1), pack_bf16x2(r2, r3));
+      }
+    } else {
+      const size_t idx = head * a.max_partitions + slot;
+      float *dst = a.ws_o + idx * DV + 4 * g;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const f32x4_t v = st.o[dt];
+        *reinterpret_cast<float4 *>(dst + 16 * dt) = make_float4(v[0], v[1], v[2], v[3]);
+      }
+      if (g == 0) {
+        a.ws_m[idx] = st.m;
+        a.ws_l[idx] = lt;
+      }
+    }
+  }
+};
+
+// The partition kernel on Bf16DecodeMfma: work-group (group of 4 kv heads,
+// sequence, partition) in the size order of the row-layout kernel, one
+// wave per kv head.  Plain decode only (no cascade).
+template <int G>
+__global__ void __launch_bounds__(64 * kDecodeWaves)
+// four work-groups per CU (one tile's rows in registers per wave, 35 KB of
+// LDS per work-group)
+__attribute__((amdgpu_waves_per_eu(4)))
+decode_partition_mfma_kernel(const DecodeKernelArgs a) {
+  using K = Bf16DecodeMfma<G>;
+  int seq = blockIdx.y;
+  int part = blockIdx.z;
+  if (a.partition_size > 0 && a.num_seqs <= 64) {
+    __shared__ int s_map[2];
+    if (threadIdx.x < 64) {
+      int sq = 0, pt = 0;
+      const bool ok = size_order_item(a, blockIdx.z * gridDim.y + blockIdx.y, threadIdx.x, sq, pt);
+      if (threadIdx.x == 0) {
+        s_map[0] = ok ? sq : 0;
+        s_map[1] = ok ? pt : a.max_partitions;  // no pair: past every sequence's partitions
+      }
+    }
+    __syncthreads();
+    seq = __builtin_amdgcn_readfirstlane(s_map[0]);
+    part = __builtin_amdgcn_readfirstlane(s_map[1]);
+  }
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int kvh = blockIdx.x * kDecodeWaves + wave;
+  if (kvh >= a.num_kv_heads) return;
+
+  const int ctx = decode_context(a, seq);
+  const int nparts = decode_num_partitions(a, ctx);
+  if (part >= nparts) return;
+  const int ps = a.partition_size > 0 ? a.partition_size : ctx;
+  const int p0 = part * ps;
+  const int p1 = min(ctx, p0 + ps);
+
+  // fused append: the newest token's rows from the input rows
+  const bool append = a.new_k != nullptr && part == nparts - 1 && ctx > 0;
+  const int pnew = append ? ctx - 1 : -1;
+  uint4 kn = make_uint4(0u, 0u, 0u, 0u), vn = kn;
+  if (append) {
+    const size_t in_row = ((size_t)seq * a.num_kv_heads + kvh) * K::D + (size_t)(lane & 15) * 8;
+    kn = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.new_k) + in_row);
+    vn = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.new_v) + in_row);
+  }
+
+  __shared__ __attribute__((aligned(16))) char lds[kDecodeWaves][K::LDS_BYTES];
+  typedef __attribute__((address_space(3))) char *lds_char_ptr;
+  const uint32_t my_lds = (uint32_t)(size_t)(lds_char_ptr)(&lds[wave][0]);
+  typename K::State st;
+  K::attend(a, seq, kvh, p0, p1, pnew, kn, vn, lane, my_lds, st);
+
+  if (append && lane < 16) {
+    // the appended rows into the token's slot (after every load of this
+    // wave has been consumed); a block outside the pool is skipped
+    const int blk = read_only(a.block_tables + (size_t)seq * a.max_blocks_per_seq)[pnew >> a.block_shift];
+    if ((unsigned)blk < (unsigned)a.num_blocks) {
+      const size_t slot = ((size_t)blk << a.block_shift) + (size_t)(pnew & ((1 << a.block_shift) - 1));
+      const size_t at = (slot * a.num_kv_heads + kvh) * K::D + (size_t)lane * 8;
+      *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(const_cast<void *>(a.k_cache)) + at) = kn;
+      *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(const_cast<void *>(a.v_cache)) + at) = vn;
+    }
+  }
+  K::write(a, seq, kvh, lane, st, nparts == 1, part);
+}
+
 // Merge the partitions of every multi-partition sequence:
 //   M = max_p m_p,  out = sum_p o_p 2^(m_p - M) / sum_p l_p 2^(m_p - M).
 // One work-group of 256 threads per (query head, sequence).  Thread t owns
@@ -1536,6 +1880,15 @@ static hipError_t launch_partition_t(const DecodeArgs &a, hipStream_t stream) {
   dim3 grid(a.max_partitions, a.cache.num_kv_heads, a.num_seqs);
   if constexpr (std::is_same<T, bf16_t>::value) {
     if (a.query_start_loc) return hipErrorNotSupported;  // prefill rows run on the generic kernel only
+    if constexpr (D == 128 && DV == 128) {
+      // plain decode at head dims 128 on the matrix cores; the own-token
+      // pass of cascade decode below, on the row-layout kernel
+      if (!a.group_start) {
+        grid = dim3((a.cache.num_kv_heads + kDecodeWaves - 1) / kDecodeWaves, a.num_seqs, a.max_partitions);
+        hipLaunchKernelGGL((decode_partition_mfma_kernel<G>), grid, dim3(64 * kDecodeWaves), 0, stream, k);
+        return hipGetLastError();
+      }
+    }
     if constexpr (D == 128) {
       // rows across kv heads: R = 4 kv heads per work-group
       constexpr int R = Bf16DecodeRows<D, DV, G>::R;
