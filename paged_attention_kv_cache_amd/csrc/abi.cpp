@@ -459,8 +459,9 @@ int pa_decode_append(const pa_kv_cache *cache, void *out, const void *q, const v
   a.new_v = value;
   hipError_t e;
   if (!pa::decode_fast_path(a)) {
-    // shapes the fast kernel does not take: the cache write first, then the
-    // plain decode, which reads the new rows from the cache
+    // shapes the matrix-core kernel does not take (fp32 pools): the cache
+    // write first, then the plain decode, which reads the new rows from the
+    // cache
     e = pa::launch_kv_cache_append(a, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "decode append write launch");
     a.new_k = a.new_v = nullptr;

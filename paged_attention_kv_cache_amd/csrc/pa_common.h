@@ -112,7 +112,6 @@ enum : int {
   kDppRowRor4 = 0x124,     // row_ror:4  (lane i reads lane (i+4) mod 16 of its row)
   kDppRowRor8 = 0x128,     // row_ror:8
   kDppRowHalfMirror = 0x141,
-  kDppRowMirror = 0x140,
 };
 
 // Every control above reads a lane of the same row, so every lane gets a
@@ -180,19 +179,6 @@ __device__ __forceinline__ float xor32_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
-// lane l reads lane l^4 (within 32-lane halves), through the LDS crossbar
-__device__ __forceinline__ float swizzle_xor4(float x) {
-  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x101F));
-}
-// every lane of a quad reads quad lane H
-template <int H>
-__device__ __forceinline__ uint32_t quad_bcast(uint32_t x) {
-  return dpp_u32<H * 0x55>(x);
-}
-template <int H>
-__device__ __forceinline__ float quad_bcast(float x) {
-  return __uint_as_float(quad_bcast<H>(__float_as_uint(x)));
-}
 
 // bf16 pair helpers: fp32 dot product of two bf16 pairs plus an fp32
 // addend (v_dot2_f32_bf16), and round-to-nearest-even packing of two floats
@@ -204,13 +190,6 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 __device__ __forceinline__ uint32_t pack_bf16x2_rne(float lo, float hi) {
   const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
   return __builtin_bit_cast(uint32_t, v);
-}
-// (lo half of a, lo half of b) and (hi half of a, hi half of b)
-__device__ __forceinline__ uint32_t interleave_lo(uint32_t a, uint32_t b) {
-  return __builtin_amdgcn_perm(b, a, 0x05040100u);
-}
-__device__ __forceinline__ uint32_t interleave_hi(uint32_t a, uint32_t b) {
-  return __builtin_amdgcn_perm(b, a, 0x07060302u);
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -267,7 +246,7 @@ struct DecodeArgs {
   // that owns it and sees that sequence's keys up to its own position
   const int32_t *query_start_loc = nullptr;
   int num_prefill_seqs = 0;
-  // fused append (new_k non-NULL, bf16 fast kernel only): the newest
+  // fused append (new_k non-NULL, bf16 matrix-core kernel only): the newest
   // token of each sequence (position context_len - 1) has its K and V rows
   // in new_k / new_v ([S, Hkv, D]) instead of the cache; the partition that
   // holds it attends to those rows and writes them into the token's slot
@@ -276,11 +255,11 @@ struct DecodeArgs {
 };
 
 hipError_t launch_decode_partition(const DecodeArgs &a, hipStream_t stream);
-// whether launch_decode_partition runs these shapes on the bf16 fast
-// kernel (the one that can take the fused append)
+// whether launch_decode_partition runs these shapes on the bf16
+// matrix-core kernel (the one that can take the fused append)
 bool decode_fast_path(const DecodeArgs &a);
-// the cache write of a fused append, for the shapes the fast kernel does
-// not take: each sequence's new rows into the slot of its position
+// the cache write of a fused append, for the shapes the matrix-core kernel
+// does not take: each sequence's new rows into the slot of its position
 // context_len - 1 (through its block table); skipped for a context of 0 or
 // a block id outside the pool
 hipError_t launch_kv_cache_append(const DecodeArgs &a, hipStream_t stream);
