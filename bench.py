@@ -818,7 +818,7 @@ def main():
             "partition_kernel": dec["part_stats"],
         },
         "roofline": {
-            "kernel": "decode_partition_mfma_kernel<4>",
+            "kernel": "decode_partition_mfma_kernel<128, 128, 4>",
             "bound": "hbm",
             "achieved": round(dec["achieved"], 1),
             "peak": HBM_PEAK_GBPS,

@@ -315,10 +315,10 @@ int pa_decode_reduce(void *out, int32_t dtype, int32_t num_seqs, int32_t num_hea
  *                    num_seqs: group g is rows group_start[g] ..
  *                    group_start[g+1]-1 (a sequence sharing nothing is a
  *                    group of one with shared_len 0).
- *   shared_len     : device, [num_groups] int32, tokens the group shares (a
- *                    multiple of block_size): every row of the group that
- *                    has a token at position p < shared_len keeps it in the
- *                    same block.  The shared blocks are read through the
+ *   shared_len     : device, [num_groups] int32, tokens the group shares
+ *                    (any count, usually a multiple of block_size): every
+ *                    row of the group that has a token at position
+ *                    p < shared_len keeps it in the same block.  The shared blocks are read through the
  *                    table of the group's longest row; a row whose context
  *                    ends inside the shared part sees only its own tokens.
  *   max_group_size : host int, >= every group's size (sizes the grid).

@@ -545,6 +545,31 @@ def test_cascade_irregular_groups(group):
         assert_close(got, ref, W.BF16, f"cascade irregular G{group} clamp{msl}")
 
 
+@pytest.mark.parametrize("group,dims", [(4, (128, 128)), (8, (128, 128)), (2, (64, 128)), (4, (128, 64))])
+def test_cascade_unaligned_shared_lengths(group, dims):
+    """Shared lengths that are not multiples of 8 (100, 37, 3 tokens over 7
+    truly shared blocks of 16): every member's own tokens then start inside
+    a block and inside a tile of the partition kernel, whose first tile
+    masks the tokens before them."""
+    D, Dv = dims
+    sizes = [4, 7, 2]
+    starts = np.cumsum([0] + sizes).tolist()
+    group_of = [g for g, n in enumerate(sizes) for _ in range(n)]
+    bs, shared_blocks = 16, 7
+    rng = np.random.default_rng(40 + group + D + Dv)
+    ctx = [int(x) for x in rng.integers(shared_blocks * bs + 1, 700, size=sum(sizes))]
+    ctx[5] = 40                                # a row ending just past its group's 37 shared tokens
+    hkv = 2
+    case = W.random_decode(4000 + group + D + Dv, ctx, num_heads=hkv * group, num_kv_heads=hkv, head_dim=D,
+                           v_head_dim=Dv, block_size=bs, dtype=W.BF16, shared_blocks=shared_blocks,
+                           group_of=group_of)
+    ref = oracle_decode(case)
+    for ps in (64, 256):
+        log(f"cascade unaligned shared G={group} D={D} Dv={Dv} partition={ps}")
+        got = _cascade(case, starts, [100, 37, 3], ps)
+        assert_close(got, ref, W.BF16, f"cascade unaligned G{group} D{D} Dv{Dv} ps{ps}")
+
+
 @pytest.mark.parametrize("bs", [8, 16, 32])
 def test_cascade_index_probe(bs):
     """Index probe through cascade decode: groups of one row that claim a
