@@ -303,7 +303,7 @@ def bench_decode(args):
     return res
 
 
-def bench_decode_secondary(name, ps, steps=30, groups=None, case=None):
+def bench_decode_secondary(name, ps, steps=30, groups=None, case=None, cascade_ps=None):
     """Decode partition + reduce on another workload: time per launch pair
     (back to back over rotated pools), logical KV GB/s (every context token
     of every sequence) and unique KV GB/s (each shared physical block once)."""
@@ -380,12 +380,13 @@ def bench_decode_secondary(name, ps, steps=30, groups=None, case=None):
         gs = torch.tensor(groups[0], dtype=torch.int32, device="cuda")
         sl = torch.tensor(groups[1], dtype=torch.int32, device="cuda")
         mg = max(b - a for a, b in zip(groups[0][:-1], groups[0][1:]))
-        wsc = torch.empty(max(P.pa_decode_cascade_workspace_bytes(S, H, D, mcl, ps), 1), dtype=torch.uint8,
+        cps = cascade_ps or ps  # the own tokens after the shared ones are shorter than whole contexts
+        wsc = torch.empty(max(P.pa_decode_cascade_workspace_bytes(S, H, Dv, mcl, cps), 1), dtype=torch.uint8,
                           device="cuda")
 
         def casc(i):
             k, v = pools[i % R]
-            P.pa_decode_cascade(q, k, v, bt, cl, case.scale, mcl, gs, sl, mg, ps, out=out, workspace=wsc,
+            P.pa_decode_cascade(q, k, v, bt, cl, case.scale, mcl, gs, sl, mg, cps, out=out, workspace=wsc,
                                 max_shared_len=max(groups[1]))
 
         for i in range(4):
@@ -397,6 +398,7 @@ def bench_decode_secondary(name, ps, steps=30, groups=None, case=None):
         e1.record()
         torch.cuda.synchronize()
         t_c = e0.elapsed_time(e1) / steps
+        res["cascade_partition_size"] = cps
         res["cascade_us"] = round(t_c * 1e3, 2)
         res["cascade_tokens_per_s"] = round(S / (t_c * 1e-3), 1)
         res["cascade_unique_kv_gbps"] = round(unique / (t_c * 1e-3) / 1e9, 1)
@@ -641,7 +643,7 @@ def run_only(args):
         r = bench_decode_secondary(name, 192, case=W.decode_batch(2000, poison=False, v_head_dim=64))
     else:
         bs = 16 if name.endswith("16") else 8
-        r = bench_decode_secondary(name, 512, groups=([0, 16, 32, 48, 64], [64 * bs] * 4))
+        r = bench_decode_secondary(name, 512, groups=([0, 16, 32, 48, 64], [64 * bs] * 4), cascade_ps=256)
     print(json.dumps({"only": name, **{k: v for k, v in r.items() if isinstance(v, (int, float, str, dict, list))}}),
           flush=True)
 
@@ -868,8 +870,10 @@ def main():
             # a value head dim of its own: 128-wide keys, 64-wide values
             bench_decode_secondary("decode_batch_bs32_k128_v64", 192,
                                    case=W.decode_batch(2000, poison=False, v_head_dim=64)),
-            bench_decode_secondary("prefix_shared_decode_bs16", 512, groups=([0, 16, 32, 48, 64], [64 * 16] * 4)),
-            bench_decode_secondary("prefix_shared_decode_bs8", 512, groups=([0, 16, 32, 48, 64], [64 * 8] * 4)),
+            bench_decode_secondary("prefix_shared_decode_bs16", 512, groups=([0, 16, 32, 48, 64], [64 * 16] * 4),
+                                   cascade_ps=256),
+            bench_decode_secondary("prefix_shared_decode_bs8", 512, groups=([0, 16, 32, 48, 64], [64 * 8] * 4),
+                                   cascade_ps=256),
         ]
         line["serving_loop"] = bench_serving()
         line["serving_loop_mixed"] = bench_serving(mixed=True)

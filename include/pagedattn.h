@@ -301,10 +301,11 @@ int pa_decode_reduce(void *out, int32_t dtype, int32_t num_seqs, int32_t num_hea
  * that share a prefix of whole blocks (the same physical blocks lead their
  * block tables, as the block-hash prefix cache of [MR] produces; [TS]
  * section 11 reuses blocks across sequences the same way).  The shared
- * tokens are read once per group: an MFMA pass computes every member's
- * attention over them (one split-K partial per 128-token chunk), the
- * members' own tokens run as split-K partitions after those, and the
- * reduce merges all of them.  The workspace holds
+ * tokens are read once per group: in the same launch as the members' own
+ * tokens (split-K partitions after the shared ones), work-groups compute
+ * every member's attention over the shared tokens on MFMA tiles whose
+ * columns are the members' query heads (one split-K partial per 128-token
+ * chunk), and the reduce merges all of them.  The workspace holds
  * ceil(max_context_len / 128) + ceil(max_context_len / partition_size)
  * partials per (row, head).  The result
  * is pa_decode's up to rounding.

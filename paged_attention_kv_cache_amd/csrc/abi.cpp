@@ -536,37 +536,22 @@ int pa_decode_cascade(const pa_kv_cache *cache, void *out, const void *q, int32_
   const int chunk = kCascadeChunk;
   a.shared_chunk = chunk;
 
-  // 1. the shared tokens of every group, once for all its rows (MFMA)
-  pa::PrefillArgs pf;
-  pf.cache = a.cache;
-  pf.out = out;
-  pf.q = q;
-  pf.query_start_loc = group_start;
-  pf.num_seqs = num_groups;
-  pf.num_heads = num_heads;
-  pf.num_query_tokens = num_seqs;
-  pf.max_query_len = max_group_size;
-  pf.block_tables = block_tables;
-  pf.max_blocks_per_seq = max_blocks_per_seq;
-  pf.context_lens = context_lens;
-  pf.max_context_len = max_context_len;
-  pf.scale = scale;
-  pf.group_start = group_start;
-  pf.shared_len = shared_len;
-  pf.ws_m = a.ws_m;
-  pf.ws_l = a.ws_l;
-  pf.ws_o = a.ws_o;
-  pf.ws_parts = P;
-  pf.shared_chunk = chunk;
-  // chunks launched per group: enough for max_shared_len.  Both passes clamp
-  // shared_len to the tokens those chunks cover (a multiple of 128, so of
-  // block_size); the members' partitions read anything past it.
-  pf.shared_chunks = std::max(1, (std::min(max_shared_len, max_context_len) + chunk - 1) / chunk);
-  a.shared_cap = pf.shared_chunks * chunk;
-  hipError_t e = pa::launch_prefill_chunk(pf, (hipStream_t)stream);
-  if (e != hipSuccess) return hip_fail(e, "cascade shared-prefix launch");
-  // 2. every row's own tokens, split-K into slots 1..
-  e = pa::launch_decode_partition(a, (hipStream_t)stream);
+  // chunks per group: enough for max_shared_len.  shared_len is clamped to
+  // the tokens those chunks cover (a multiple of 128, so of block_size);
+  // the members' partitions read anything past it.
+  a.shared_chunks = std::max(1, (std::min(max_shared_len, max_context_len) + chunk - 1) / chunk);
+  a.shared_cap = a.shared_chunks * chunk;
+  a.max_group_size = max_group_size;
+  const int col_tiles = (max_group_size * (num_heads / cache->num_kv_heads) + 15) / 16;
+  const int grid_z = pa::cascade_grid_z(a, col_tiles);
+  if (grid_z > kMaxGridYZ || (int64_t)grid_z * num_seqs > INT32_MAX)
+    return fail(PA_ERR_SHAPE,
+                "cascade launch needs %d grid rows of %d items (shared chunks x column tiles per group, then own "
+                "partitions), above %d; lower max_shared_len or max_group_size, or raise partition_size",
+                grid_z, num_seqs, kMaxGridYZ);
+  // 1-2. every group's shared chunks, once for all its rows, and every
+  // row's own tokens after them, in one launch
+  hipError_t e = pa::launch_decode_partition(a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "cascade partition launch");
   // 3. merge all slots
   e = pa::launch_decode_reduce(a, (hipStream_t)stream);

@@ -233,13 +233,17 @@ struct DecodeArgs {
   float *ws_m, *ws_l, *ws_o;
   // cascade decode (group_start non-NULL): rows group_start[g] ..
   // group_start[g+1]-1 share their first shared_len[g] tokens, whose
-  // partial sits in slot 0; the partition launch covers each row's own
-  // tokens from there into slots 1.., and the reduce merges every slot
+  // partials sit in slots 0 .. ceil(shared / shared_chunk) - 1 (one per
+  // chunk); the partition launch computes those chunks once per group and
+  // each row's own tokens into the following slots, and the reduce merges
+  // every slot
   const int32_t *group_start = nullptr;
   const int32_t *shared_len = nullptr;
   int num_groups = 0;
   int shared_chunk = 64;   // the shared part's partials: slot c = tokens [c*chunk, (c+1)*chunk)
   int shared_cap = 0;      // shared tokens are clamped to this (shared_chunks * shared_chunk)
+  int shared_chunks = 0;   // chunks per group the partition launch runs (cascade)
+  int max_group_size = 0;  // rows of the largest group (cascade)
   // prefill rows (query_start_loc non-NULL; generic kernel, single pass):
   // "sequence" r is packed query row r of a chunked prefill over
   // num_prefill_seqs sequences; it reads the block table of the sequence
@@ -255,6 +259,11 @@ struct DecodeArgs {
 };
 
 hipError_t launch_decode_partition(const DecodeArgs &a, hipStream_t stream);
+// own-token partitions a cascade row may have, and the grid z extent of a
+// cascade launch (its shared chunks and own partitions laid out over
+// num_seqs x z)
+int cascade_own_partitions(const DecodeArgs &a);
+int cascade_grid_z(const DecodeArgs &a, int col_tiles);
 // whether launch_decode_partition runs these shapes on the bf16
 // matrix-core kernel (the one that can take the fused append)
 bool decode_fast_path(const DecodeArgs &a);
@@ -276,15 +285,6 @@ struct PrefillArgs {
   const int32_t *context_lens;
   int max_context_len;
   float scale;
-  // cascade decode's shared-prefix pass (group_start non-NULL): num_seqs is
-  // the number of groups, max_query_len the largest group, num_query_tokens
-  // the number of decode rows; partials go to slot 0 of ws_*
-  const int32_t *group_start = nullptr;
-  const int32_t *shared_len = nullptr;
-  float *ws_m = nullptr, *ws_l = nullptr, *ws_o = nullptr;
-  int ws_parts = 0;
-  int shared_chunk = 64;   // tokens per chunk of the shared part (slot c = chunk c)
-  int shared_chunks = 1;   // chunks launched per group
 };
 
 hipError_t launch_prefill_chunk(const PrefillArgs &a, hipStream_t stream);

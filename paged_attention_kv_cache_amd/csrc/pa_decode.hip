@@ -85,6 +85,8 @@ struct DecodeKernelArgs {
   int num_groups;
   int shared_chunk;      // the shared part's partials: slots 0 .. ceil(shared / shared_chunk) - 1
   int shared_cap;        // shared tokens are clamped to this (the chunks launched)
+  int shared_z;          // grid z slots of the shared chunks (chunks x col_tiles; 0: none in this launch)
+  int col_tiles;         // 16-column tiles per group: ceil(max_group_size * G / 16)
   // prefill rows (non-NULL): index r of the generic kernel is packed query
   // row r of sequences 0 .. num_prefill_seqs-1 (see decode_row)
   const int32_t *query_start_loc;
@@ -379,7 +381,10 @@ __device__ __forceinline__ bool size_order_item(const DecodeKernelArgs &a, int i
                                                 int &part_out) {
   const int S = a.num_seqs;
   const int ps = a.partition_size;
-  const int ctx = lane < S ? decode_context(a, lane) : 0;
+  // the tokens a row's partitions cover: its context, or (cascade) the
+  // part of it after its shared tokens
+  int ctx = lane < S ? decode_context(a, lane) : 0;
+  if (a.group_start && lane < S) ctx -= decode_shared(a, lane, ctx);
   const int nfull = ctx / ps;
   const int rem = ctx - nfull * ps;
   // full pairs: cum(p) = sum_s min(nfull_s, p) pairs come before partition p
@@ -600,8 +605,11 @@ struct Bf16DecodeMfma {
 
   // Scores, online softmax and P.V of the tile at tokens t0 .. staged in
   // LDS (ok: its 4-token groups' block bits).
-  __device__ static __forceinline__ void compute(int ok, int t0, int p0, int p1, float sl, int lane, uint32_t lds,
-                                                 State &st) {
+  // kCols: column c also stops at its own key limit lim (the shared
+  // chunks of cascade decode, whose columns belong to different rows).
+  template <bool kCols>
+  __device__ static __forceinline__ void compute(int ok, int t0, int p0, int p1, int lim, float sl, int lane,
+                                                 uint32_t lds, State &st) {
     const int g = lane >> 4;
     const int c = lane & 15;
     // S^T = K Q^T: A = K rows (lane: token c, chunk 4 ks + g)
@@ -620,7 +628,7 @@ struct Bf16DecodeMfma {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int tok = t0 + 4 * g + r;
-      vok[r] = grp_ok && tok >= p0 && tok < p1;
+      vok[r] = grp_ok && tok >= p0 && tok < p1 && (!kCols || tok < lim);
       sv[r] = vok[r] ? s[r] * sl : -INFINITY;
       cm = fmaxf(cm, sv[r]);
     }
@@ -652,33 +660,37 @@ struct Bf16DecodeMfma {
     }
   }
 
-  // Online softmax of kv head kvh's query heads over tokens p0 .. p1-1 of
-  // sequence seq; pnew (or -1): the appended token, whose rows are kn, vn
-  // (this lane's chunks).
-  __device__ static __forceinline__ void attend(const DecodeKernelArgs &a, int seq, int kvh, int p0, int p1,
-                                                int pnew, uint4 kn, uint4 vn, int lane, uint32_t lds, State &st) {
+  // Q^T fragments of this lane's column from its query row (zero without
+  // one), and the empty running state.
+  __device__ static __forceinline__ void begin(const uint16_t *qrow, int lane, State &st) {
     const int g = lane >> 4;
-    const int c = lane & 15;
-    {
-      const uint4 *qrow = reinterpret_cast<const uint4 *>(
-          static_cast<const uint16_t *>(a.q) + ((size_t)seq * a.num_heads + (size_t)kvh * G + (c < G ? c : 0)) * D);
+    const uint4 *q4 = reinterpret_cast<const uint4 *>(qrow);
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        const uint4 x = c < G ? qrow[4 * ks + g] : make_uint4(0u, 0u, 0u, 0u);
-        st.qf[ks] = __builtin_bit_cast(bf16x8_t, x);
-      }
+    for (int ks = 0; ks < NKS; ++ks) {
+      const uint4 x = qrow ? q4[4 * ks + g] : make_uint4(0u, 0u, 0u, 0u);
+      st.qf[ks] = __builtin_bit_cast(bf16x8_t, x);
     }
     st.m = -INFINITY;
     st.l = 0.f;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) st.o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // Online softmax of kv head kvh's columns over tokens p0 .. p1-1, read
+  // through block-table row tab_row; pnew (or -1): the appended token,
+  // whose rows are kn, vn (this lane's chunks); with kCols each column
+  // stops at its own limit lim.
+  template <bool kCols>
+  __device__ static __forceinline__ void attend(const DecodeKernelArgs &a, int tab_row, int kvh, int p0, int p1,
+                                                int lim, int pnew, uint4 kn, uint4 vn, int lane, uint32_t lds,
+                                                State &st) {
     const int tbeg = p0 & ~7;  // tiles start at a multiple of 8
     const int ntiles = p1 > p0 ? (p1 - tbeg + TT - 1) / TT : 0;
     if (ntiles == 0) return;
 
     const float sl = a.scale_log2;
     Rows w;
-    w.tab = read_only(a.block_tables + (size_t)seq * a.max_blocks_per_seq);
+    w.tab = read_only(a.block_tables + (size_t)tab_row * a.max_blocks_per_seq);
     w.kbase = static_cast<const char *>(a.k_cache);
     w.vbase = static_cast<const char *>(a.v_cache);
     w.kslot = (size_t)a.num_kv_heads * D * 2;
@@ -694,7 +706,7 @@ struct Bf16DecodeMfma {
       stage(t, t0, p0, p1, pnew, kn, vn, lane, lds);
       const int ok = t.ok;
       if (i + 1 < ntiles) issue(a, w, t0 + TT, p1, t);
-      compute(ok, t0, p0, p1, sl, lane, lds, st);
+      compute<kCols>(ok, t0, p0, p1, lim, sl, lane, lds, st);
     }
   }
 
@@ -734,10 +746,80 @@ struct Bf16DecodeMfma {
   }
 };
 
+// One shared chunk of cascade decode for kv head kvh: keys c*chunk ..
+// of group g's shared tokens against the columns of column tile ct, column
+// j being head j % G of member ct*16/G + j / G of the group.  The keys are
+// read through the table of the group's longest row; each column stops at
+// its row's own shared tokens (its context may end inside the shared
+// part).  Writes partition slot c of every column whose row reads it.
+template <int D, int DV, int G>
+__device__ __forceinline__ void decode_shared_chunk(const DecodeKernelArgs &a, int grp, int c, int ct, int kvh,
+                                                    int lane, uint32_t lds) {
+  using K = Bf16DecodeMfma<D, DV, G>;
+  static_assert(16 % G == 0, "whole members per column tile");
+  const int r0 = a.group_start[grp], r1 = min(a.group_start[grp + 1], a.num_seqs);
+  const int mcol = 16 / G;  // members per column tile
+  if (ct * mcol >= r1 - r0) return;
+  // the group's longest row (lowest index among equals): its table holds
+  // every shared block any member reads
+  int best = -1, brow = r0;
+  for (int i = r0 + lane; i < r1; i += 64) {
+    const int cx = decode_context(a, i);
+    if (cx > best) {
+      best = cx;
+      brow = i;
+    }
+  }
+#pragma unroll
+  for (int sft = 1; sft < 64; sft <<= 1) {
+    const int ob = __shfl_xor(best, sft);
+    const int orow = __shfl_xor(brow, sft);
+    if (ob > best || (ob == best && orow < brow)) {
+      best = ob;
+      brow = orow;
+    }
+  }
+  const int ctx_max = __builtin_amdgcn_readfirstlane(best);
+  const int tab_row = __builtin_amdgcn_readfirstlane(brow);
+  const int sh_g = min(a.shared_len[grp], a.shared_cap);
+  const int p0 = c * a.shared_chunk;
+  const int p1 = min(min(p0 + a.shared_chunk, sh_g), ctx_max);
+  if (p1 <= p0) return;  // no row of the group reads this slot
+
+  // this lane's column: member row and head, and the keys it sees
+  const int col = lane & 15;
+  const int row = r0 + ct * mcol + col / G;
+  const bool has_row = row < r1;
+  const int lim = has_row ? decode_shared(a, row, decode_context(a, row)) : 0;
+  const uint16_t *qrow = has_row ? static_cast<const uint16_t *>(a.q) +
+                                       ((size_t)row * a.num_heads + (size_t)kvh * G + col % G) * D
+                                 : nullptr;
+  typename K::State st;
+  K::begin(qrow, lane, st);
+  K::template attend<true>(a, tab_row, kvh, p0, p1, lim, -1, make_uint4(0u, 0u, 0u, 0u),
+                           make_uint4(0u, 0u, 0u, 0u), lane, lds, st);
+  const float lt = xor32_sum(xor16_sum(st.l));
+  if (!has_row || p0 >= lim) return;  // the row's reduce does not read slot c
+  const int g = lane >> 4;
+  const size_t idx = ((size_t)row * a.num_heads + (size_t)kvh * G + col % G) * a.max_partitions + c;
+  float *dst = a.ws_o + idx * DV + 4 * g;
+#pragma unroll
+  for (int dt = 0; dt < K::NDT; ++dt) {
+    const f32x4_t v = st.o[dt];
+    *reinterpret_cast<float4 *>(dst + 16 * dt) = make_float4(v[0], v[1], v[2], v[3]);
+  }
+  if (g == 0) {
+    a.ws_m[idx] = st.m;
+    a.ws_l[idx] = lt;
+  }
+}
+
 // The partition kernel on Bf16DecodeMfma: work-group (group of 4 kv heads,
 // sequence, partition), one wave per kv head; plain decode in size order
-// (size_order_item), cascade (a row's own tokens after the shared ones,
-// into the slots after the shared chunks') in grid order.
+// (size_order_item).  Cascade launches number their items z * S + y: the
+// groups' shared chunks first (shared_z = chunks x column tiles per
+// group), then each row's own tokens after its shared ones, partition by
+// partition (into the slots after the row's shared chunks').
 template <int D, int DV, int G>
 __global__ void __launch_bounds__(64 * kDecodeWaves)
 // four work-groups per CU (one tile's rows in registers per wave, up to
@@ -747,11 +829,30 @@ decode_partition_mfma_kernel(const DecodeKernelArgs a) {
   using K = Bf16DecodeMfma<D, DV, G>;
   int seq = blockIdx.y;
   int part = blockIdx.z;
-  if (a.group_start == nullptr && a.partition_size > 0 && a.num_seqs <= 64) {
+  const bool cascade = a.group_start != nullptr;
+  // Cascade launches number their items L = z * S + y: the groups' shared
+  // chunks first, then the rows' own partitions.  The branch is uniform
+  // over the work-group, so every wave meets the barrier below.
+  int shared_item = -1, own_item = -1;
+  if (cascade) {
+    const int L = blockIdx.z * gridDim.y + blockIdx.y;
+    const int nsh = a.num_groups * a.shared_z;
+    if (L < nsh) {
+      shared_item = L;
+    } else {
+      own_item = L - nsh;
+      seq = own_item % a.num_seqs;
+      part = own_item / a.num_seqs;
+    }
+  }
+  if (shared_item < 0 && a.partition_size > 0 && a.num_seqs <= 64) {
+    // (sequence, partition) in size order (for cascade: of the tokens after
+    // each row's shared ones)
     __shared__ int s_map[2];
     if (threadIdx.x < 64) {
       int sq = 0, pt = 0;
-      const bool ok = size_order_item(a, blockIdx.z * gridDim.y + blockIdx.y, threadIdx.x, sq, pt);
+      const bool ok = size_order_item(a, cascade ? own_item : (int)(blockIdx.z * gridDim.y + blockIdx.y),
+                                      threadIdx.x, sq, pt);
       if (threadIdx.x == 0) {
         s_map[0] = ok ? sq : 0;
         s_map[1] = ok ? pt : a.max_partitions;  // no pair: past every sequence's partitions
@@ -766,8 +867,15 @@ decode_partition_mfma_kernel(const DecodeKernelArgs a) {
   const int kvh = blockIdx.x * kDecodeWaves + wave;
   if (kvh >= a.num_kv_heads) return;
 
+  __shared__ __attribute__((aligned(16))) char lds[kDecodeWaves][K::LDS_BYTES];
+  typedef __attribute__((address_space(3))) char *lds_char_ptr;
+  const uint32_t my_lds = (uint32_t)(size_t)(lds_char_ptr)(&lds[wave][0]);
+  if (shared_item >= 0) {
+    const int grp = shared_item / a.shared_z, r = shared_item % a.shared_z;
+    decode_shared_chunk<D, DV, G>(a, grp, r / a.col_tiles, r % a.col_tiles, kvh, lane, my_lds);
+    return;
+  }
   const int ctx = decode_context(a, seq);
-  const bool cascade = a.group_start != nullptr;
   const int sh = decode_shared(a, seq, ctx);
   const int nparts = cascade ? (ctx - sh + a.partition_size - 1) / a.partition_size
                              : decode_num_partitions(a, ctx);
@@ -788,11 +896,12 @@ decode_partition_mfma_kernel(const DecodeKernelArgs a) {
                                           ((size_t)seq * a.num_kv_heads + kvh) * DV + (size_t)(lane % K::LV) * 8);
   }
 
-  __shared__ __attribute__((aligned(16))) char lds[kDecodeWaves][K::LDS_BYTES];
-  typedef __attribute__((address_space(3))) char *lds_char_ptr;
-  const uint32_t my_lds = (uint32_t)(size_t)(lds_char_ptr)(&lds[wave][0]);
   typename K::State st;
-  K::attend(a, seq, kvh, p0, p1, pnew, kn, vn, lane, my_lds, st);
+  const int col = lane & 15;
+  K::begin(col < G ? static_cast<const uint16_t *>(a.q) + ((size_t)seq * a.num_heads + (size_t)kvh * G + col) * D
+                   : nullptr,
+           lane, st);
+  K::template attend<false>(a, seq, kvh, p0, p1, p1, pnew, kn, vn, lane, my_lds, st);
 
   if (append) {
     // the appended rows into the token's slot (after every load of this
@@ -964,6 +1073,8 @@ static DecodeKernelArgs make_kernel_args(const DecodeArgs &a) {
   k.num_groups = a.num_groups;
   k.shared_chunk = a.shared_chunk;
   k.shared_cap = a.shared_cap;
+  k.shared_z = 0;
+  k.col_tiles = 1;
   k.query_start_loc = a.query_start_loc;
   k.num_prefill_seqs = a.num_prefill_seqs;
   k.new_k = a.new_k;
@@ -971,15 +1082,38 @@ static DecodeKernelArgs make_kernel_args(const DecodeArgs &a) {
   return k;
 }
 
+// own-token partitions a cascade row may have: its tokens after the
+// shared ones, at most the (clamped) context
+int cascade_own_partitions(const DecodeArgs &a) {
+  const int64_t table_cap = (int64_t)a.max_blocks_per_seq * a.cache.block_size;
+  const int64_t cap = table_cap < a.max_context_len ? table_cap : a.max_context_len;
+  const int64_t n = (cap + a.partition_size - 1) / a.partition_size;
+  return (int)(n > 1 ? n : 1);
+}
+
+int cascade_grid_z(const DecodeArgs &a, int col_tiles) {
+  const int64_t items =
+      (int64_t)a.num_groups * a.shared_chunks * col_tiles + (int64_t)a.num_seqs * cascade_own_partitions(a);
+  const int64_t z = (items + a.num_seqs - 1) / a.num_seqs;
+  return (int)(z < 0x7fffffff ? z : 0x7fffffff);
+}
+
 template <typename T, int D, int DV, int G>
 static hipError_t launch_partition_t(const DecodeArgs &a, hipStream_t stream) {
-  const DecodeKernelArgs k = make_kernel_args(a);
+  DecodeKernelArgs k = make_kernel_args(a);
   dim3 grid(a.max_partitions, a.cache.num_kv_heads, a.num_seqs);
   if constexpr (std::is_same<T, bf16_t>::value) {
     if (a.query_start_loc) return hipErrorNotSupported;  // prefill rows run on the generic kernel only
     // every bf16 decode (plain and cascade, any head dim pair) on the
-    // matrix-core kernel
-    grid = dim3((a.cache.num_kv_heads + kDecodeWaves - 1) / kDecodeWaves, a.num_seqs, a.max_partitions);
+    // matrix-core kernel; a cascade launch also runs the groups' shared
+    // chunks, ahead of the rows' own tokens in the grid
+    int zs = a.max_partitions;
+    if (a.group_start) {
+      k.col_tiles = (a.max_group_size * G + 15) / 16;
+      k.shared_z = a.shared_chunks * k.col_tiles;
+      zs = cascade_grid_z(a, k.col_tiles);
+    }
+    grid = dim3((a.cache.num_kv_heads + kDecodeWaves - 1) / kDecodeWaves, a.num_seqs, zs);
     hipLaunchKernelGGL((decode_partition_mfma_kernel<D, DV, G>), grid, dim3(64 * kDecodeWaves), 0, stream, k);
   } else {
     // (cascade launches are bf16: never here)

@@ -81,18 +81,6 @@ struct PrefillKernelArgs {
   int n_qtiles;           // query tiles per (sequence, head group)
   int n_work;             // work-groups with work
   float scale_log2;       // scale * log2(e)
-  // shared-prefix pass of cascade decode (group_start non-NULL): a "sequence"
-  // is a group of decode rows group_start[g] .. group_start[g+1]-1 whose
-  // first shared_len[g] tokens are the same blocks; their attention over
-  // those tokens is written as split-K partials into slot 0 of ws_*
-  const int32_t *group_start;
-  const int32_t *shared_len;
-  float *ws_m;
-  float *ws_l;
-  float *ws_o;
-  int ws_parts;           // partition slots per (row, head)
-  int n_chunks;           // key chunks per group (1 for prefill)
-  int chunk;              // tokens per key chunk, a multiple of 64 (cascade)
 };
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
@@ -309,8 +297,6 @@ __global__ void __launch_bounds__(kPrefillThreads, 1) prefill_chunk_kernel(const
   const int wid = (bid & 7) * (nwg >> 3) + (bid >> 3);
   if (wid >= a.n_work) return;
   int rest = wid;
-  const int kchunk = rest % a.n_chunks;  // cascade: chunk of the shared tokens
-  rest /= a.n_chunks;
   const int qt_rev = rest % a.n_qtiles;
   rest /= a.n_qtiles;
   const int seq0 = rest % a.num_seqs;
@@ -318,9 +304,8 @@ __global__ void __launch_bounds__(kPrefillThreads, 1) prefill_chunk_kernel(const
   const int half = rest % HALVES;
   const int kvh = rest / HALVES;
   int qtile = a.n_qtiles - 1 - qt_rev;
-  const bool cascade = a.group_start != nullptr;
   int seq = seq0;
-  if (!cascade && a.num_seqs * a.n_qtiles <= 64) {
+  if (a.num_seqs * a.n_qtiles <= 64) {
     // item j of this (kv head, head part) takes the j-th largest item: lane
     // i of wave 0 holds item i = (sequence i / n_qtiles, query tile
     // i % n_qtiles) and its key-tile count, ranked by (count descending,
@@ -360,17 +345,15 @@ __global__ void __launch_bounds__(kPrefillThreads, 1) prefill_chunk_kernel(const
   }
 
   seq = __builtin_amdgcn_readfirstlane(seq);
-  const int32_t *rows = cascade ? a.group_start : a.query_start_loc;
-  int r1 = min(rows[seq + 1], a.num_query_tokens);
-  int r0 = rows[seq];
+  int r1 = min(a.query_start_loc[seq + 1], a.num_query_tokens);
+  int r0 = a.query_start_loc[seq];
   r0 = max(0, min(r0, r1));
   const int q_len = r1 - r0;
-  // prefill: the chunk ends the context; cascade: the shared tokens
-  int ctx = min(cascade ? min(a.shared_len[seq], a.n_chunks * a.chunk) : a.context_lens[seq], a.ctx_cap);
+  // the chunk ends the context
+  int ctx = min(a.context_lens[seq], a.ctx_cap);
   ctx = max(ctx, 0);
   const int t_begin = qtile * QT;
   if (t_begin >= q_len) return;
-  if (cascade && kchunk * a.chunk >= ctx) return;  // a chunk past the group's shared tokens
   const int prefix = ctx - q_len;
 
   const int tid = threadIdx.x;
@@ -384,13 +367,8 @@ __global__ void __launch_bounds__(kPrefillThreads, 1) prefill_chunk_kernel(const
   const int hh = lane >> 5;
   const int t = tw0 + col;             // this lane's query (chunk row)
   const bool qvalid = t < q_len;
-  // last key this lane's query sees: its chunk position (prefill), or the
-  // end of the shared tokens within the row's own context (cascade)
-  int qpos = prefix + t;
-  if (cascade) {
-    const int own = qvalid ? max(0, min(a.context_lens[r0 + t], a.ctx_cap)) : ctx;
-    qpos = min(ctx, own) - 1;
-  }
+  // last key this lane's query sees: its position in the context
+  const int qpos = prefix + t;
   // smallest of them in the wave: tiles past it need the mask
   int qpos_lo = qpos;
 #pragma unroll
@@ -415,45 +393,6 @@ __global__ void __launch_bounds__(kPrefillThreads, 1) prefill_chunk_kernel(const
   // keys this work-group needs: 0 .. (largest query position of the tile)
   const int t_last = min(t_begin + QT, q_len) - 1;
   int kend = max(0, min(ctx, prefix + t_last + 1));
-  // cascade: the shared blocks are read through the table of the group's
-  // longest row, up to min(shared, its context), so every key read lies in
-  // a real context (a shorter row masks the keys it does not have)
-  int tab_row = seq;
-  if (cascade) {
-    __shared__ int s_best[2];
-    if (wave == 0) {
-      int best = -1, brow = r0;
-      for (int i = r0 + lane; i < r1; i += 64) {
-        const int c = max(0, min(a.context_lens[i], a.ctx_cap));
-        if (c > best) {
-          best = c;
-          brow = i;
-        }
-      }
-#pragma unroll
-      for (int sft = 1; sft < 64; sft <<= 1) {
-        const int ob = __shfl_xor(best, sft);
-        const int orow = __shfl_xor(brow, sft);
-        if (ob > best || (ob == best && orow < brow)) {
-          best = ob;
-          brow = orow;
-        }
-      }
-      if (lane == 0) {
-        s_best[0] = best;
-        s_best[1] = brow;
-      }
-    }
-    __syncthreads();
-    kend = max(0, min(ctx, s_best[0]));
-    tab_row = __builtin_amdgcn_readfirstlane(s_best[1]);
-  }
-  // cascade: this work-group's chunk of the shared tokens
-  const int kbeg = __builtin_amdgcn_readfirstlane(cascade ? kchunk * a.chunk : 0);
-  if (cascade) {
-    kend = min(kend, kbeg + a.chunk);
-    if (kbeg >= kend) return;  // past every row's shared tokens: a slot no merge reads
-  }
   kend = __builtin_amdgcn_readfirstlane(kend);
 
   const int shift = a.block_shift;
@@ -465,8 +404,7 @@ __global__ void __launch_bounds__(kPrefillThreads, 1) prefill_chunk_kernel(const
   const char *kbase = reinterpret_cast<const char *>(static_cast<const uint16_t *>(a.k_cache) + (size_t)kvh * D);
   const char *vbase = reinterpret_cast<const char *>(static_cast<const uint16_t *>(a.v_cache) + (size_t)kvh * DV);
   const char *zero = reinterpret_cast<const char *>(&kZeroChunk);
-  tab_row = __builtin_amdgcn_readfirstlane(tab_row);
-  const int32_t *bt = a.block_tables + (size_t)tab_row * a.max_blocks_per_seq;
+  const int32_t *bt = a.block_tables + (size_t)seq * a.max_blocks_per_seq;
   const int max_blocks = a.max_blocks_per_seq;
   const int num_blocks = a.num_blocks;
   GK gk;
@@ -602,16 +540,16 @@ __global__ void __launch_bounds__(kPrefillThreads, 1) prefill_chunk_kernel(const
     return d;
   };
 
-  const int ntiles = (kend - kbeg + KT - 1) / KT;
+  const int ntiles = (kend + KT - 1) / KT;
   // leading tiles every query of this wave sees whole: no mask, no max
-  const int n_plain = min(ntiles, max(0, (qpos_lo + 1 - kbeg) / KT));
+  const int n_plain = min(ntiles, max(0, (qpos_lo + 1) / KT));
 
   // loads of tile j (its ids read beforehand) into buffer j % kBufs
   typedef __attribute__((address_space(3))) const char *lds_cptr;
   const uint32_t sk_lds = (uint32_t)(size_t)((lds_cptr)(const char *)&sk[0][0]);
   const uint32_t sv_lds = (uint32_t)(size_t)((lds_cptr)(const char *)&sv[0][0]);
   auto gather = [&](int j, const typename GK::Ids &ik, const typename GV::Ids &iv) {
-    const int k0 = kbeg + j * KT;
+    const int k0 = j * KT;
     const uint32_t b = (uint32_t)(j % kBufs);
     const uint32_t dk = sk_lds + b * (KT * D * 2), dv = sv_lds + b * (KT * DV * 2);
     if (k0 + KT <= kend) {
@@ -642,17 +580,17 @@ __global__ void __launch_bounds__(kPrefillThreads, 1) prefill_chunk_kernel(const
   //   O += V(t) P(t);  block ids of tile t+4 read;  wait for this wave's
   //   loads of tile t+2 (issued in step t-1; those of tile t+3 stay in
   //   flight);  barrier.
-  typename GK::Ids ik = gk.ids(kBs8, bt, kbeg, shift, max_blocks);
-  typename GV::Ids iv = same_ids(ik, gv, kBs8, bt, kbeg, shift, max_blocks);
+  typename GK::Ids ik = gk.ids(kBs8, bt, 0, shift, max_blocks);
+  typename GV::Ids iv = same_ids(ik, gv, kBs8, bt, 0, shift, max_blocks);
   gather(0, ik, iv);
-  ik = gk.ids(kBs8, bt, kbeg + KT, shift, max_blocks);
-  iv = same_ids(ik, gv, kBs8, bt, kbeg + KT, shift, max_blocks);
+  ik = gk.ids(kBs8, bt, KT, shift, max_blocks);
+  iv = same_ids(ik, gv, kBs8, bt, KT, shift, max_blocks);
   gather(1, ik, iv);
-  ik = gk.ids(kBs8, bt, kbeg + 2 * KT, shift, max_blocks);
-  iv = same_ids(ik, gv, kBs8, bt, kbeg + 2 * KT, shift, max_blocks);
+  ik = gk.ids(kBs8, bt, 2 * KT, shift, max_blocks);
+  iv = same_ids(ik, gv, kBs8, bt, 2 * KT, shift, max_blocks);
   gather(2, ik, iv);
-  ik = gk.ids(kBs8, bt, kbeg + 3 * KT, shift, max_blocks);
-  iv = same_ids(ik, gv, kBs8, bt, kbeg + 3 * KT, shift, max_blocks);
+  ik = gk.ids(kBs8, bt, 3 * KT, shift, max_blocks);
+  iv = same_ids(ik, gv, kBs8, bt, 3 * KT, shift, max_blocks);
   wait_vmcnt<0>();
   __syncthreads();
 
@@ -664,7 +602,7 @@ __global__ void __launch_bounds__(kPrefillThreads, 1) prefill_chunk_kernel(const
   // max (first tile, diagonal tiles); otherwise no mask and no max, with
   // the sum check.
   auto step = [&](bool kFull, int j, f32x16_t (&cur)[2], f32x16_t (&nxt)[2]) __attribute__((always_inline)) {
-    const int k0 = kbeg + j * KT;
+    const int k0 = j * KT;
     gather(j + 3, ik, iv);
     if (kFull) {
       // exponents relative to the reference; causal mask on tiles that
@@ -743,26 +681,6 @@ __global__ void __launch_bounds__(kPrefillThreads, 1) prefill_chunk_kernel(const
   }
 
   const float lsum = xor32_sum(l);  // cross-lane: before the divergent store
-  if (cascade) {
-    // partials (reference max in base-2 units, sum, unnormalised output)
-    if (qvalid) {
-      const size_t idx = ((size_t)(r0 + t) * a.num_heads + head) * a.ws_parts + kchunk;
-      float *orow = a.ws_o + idx * DV;
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-        for (int rq = 0; rq < 4; ++rq) {
-          const int d0 = dt * 32 + 8 * rq + 4 * hh;
-          *reinterpret_cast<float4 *>(orow + d0) =
-              make_float4(o[dt][4 * rq], o[dt][4 * rq + 1], o[dt][4 * rq + 2], o[dt][4 * rq + 3]);
-        }
-      if (hh == 0) {
-        a.ws_m[idx] = m;
-        a.ws_l[idx] = lsum;
-      }
-    }
-    return;
-  }
   if (qvalid) {
     uint16_t *orow = static_cast<uint16_t *>(a.out) + ((size_t)(r0 + t) * a.num_heads + head) * DV;
 #pragma unroll
@@ -802,19 +720,11 @@ static hipError_t launch_t(const PrefillArgs &a, hipStream_t stream) {
   k.ctx_cap = (int)(table_cap < a.max_context_len ? table_cap : a.max_context_len);
   k.num_query_tokens = a.num_query_tokens;
   k.n_qtiles = (a.max_query_len + Sh::QT - 1) / Sh::QT;
-  k.n_chunks = a.group_start ? a.shared_chunks : 1;
-  k.chunk = a.shared_chunk;
-  const int64_t n_work = (int64_t)a.num_seqs * a.cache.num_kv_heads * Sh::HALVES * k.n_qtiles * k.n_chunks;
+  const int64_t n_work = (int64_t)a.num_seqs * a.cache.num_kv_heads * Sh::HALVES * k.n_qtiles;
   if (n_work <= 0) return hipSuccess;
   if (n_work > (int64_t)0x7fffffff - 8) return hipErrorInvalidConfiguration;
   k.n_work = (int)n_work;
   k.scale_log2 = a.scale * kLog2e;
-  k.group_start = a.group_start;
-  k.shared_len = a.shared_len;
-  k.ws_m = a.ws_m;
-  k.ws_l = a.ws_l;
-  k.ws_o = a.ws_o;
-  k.ws_parts = a.ws_parts;
   const unsigned grid = (unsigned)((n_work + 7) / 8 * 8);
   if (bs8)
     hipLaunchKernelGGL((prefill_chunk_kernel<D, DV, G, true>), dim3(grid), dim3(kPrefillThreads), 0, stream, k);

@@ -493,8 +493,8 @@ def test_cascade_other_scales(scale):
 @pytest.mark.parametrize("dims", [(128, 64), (64, 128)])
 @pytest.mark.parametrize("group", [2, 8])
 def test_cascade_separate_value_dim(dims, group):
-    """Cascade decode with a value head dim of its own: the shared pass and
-    the partitions write partials of the value width."""
+    """Cascade decode with a value head dim of its own: the shared chunks
+    and the own-token partitions write partials of the value width."""
     D, Dv = dims
     sizes = [3, 40, 5]
     starts = np.cumsum([0] + sizes).tolist()
