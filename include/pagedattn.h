@@ -304,9 +304,9 @@ int pa_decode_reduce(void *out, int32_t dtype, int32_t num_seqs, int32_t num_hea
  * tokens are read once per group: in the same launch as the members' own
  * tokens (split-K partitions after the shared ones), work-groups compute
  * every member's attention over the shared tokens on MFMA tiles whose
- * columns are the members' query heads (one split-K partial per 128-token
+ * columns are the members' query heads (one split-K partial per 512-token
  * chunk), and the reduce merges all of them.  The workspace holds
- * ceil(max_context_len / 128) + ceil(max_context_len / partition_size)
+ * ceil(max_context_len / 512) + ceil(max_context_len / partition_size)
  * partials per (row, head).  The result
  * is pa_decode's up to rounding.
  *
@@ -324,9 +324,9 @@ int pa_decode_reduce(void *out, int32_t dtype, int32_t num_seqs, int32_t num_hea
  *                    ends inside the shared part sees only its own tokens.
  *   max_group_size : host int, >= every group's size (sizes the grid).
  *   max_shared_len : host int, >= 0, an upper bound of shared_len that sizes
- *                    the shared pass's grid (ceil(max_shared_len / 128)
- *                    chunks per group).  A shared_len above it is clamped
- *                    to 128 * that many chunks; the tokens past the clamp
+ *                    the launch's shared chunks (ceil(max_shared_len / 512)
+ *                    per group).  A shared_len above it is clamped to
+ *                    512 * that many chunks; the tokens past the clamp
  *                    run in the members' own partitions, so the result
  *                    stays correct and only the sharing is lost.
  *   workspace      : device, >= pa_decode_cascade_workspace_bytes(...)

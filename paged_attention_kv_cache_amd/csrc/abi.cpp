@@ -473,9 +473,11 @@ int pa_decode_append(const pa_kv_cache *cache, void *out, const void *q, const v
   return ok();
 }
 
-// cascade decode: tokens per chunk of the shared part (one work-group and
-// one partial slot each; two 64-key tiles, so that the chunks fill the GPU)
-constexpr int kCascadeChunk = 128;
+// cascade decode: tokens per chunk of the shared part (one partial slot
+// each, and one work-group per 16 of its columns).  Longer chunks mean
+// fewer slots for the reduce to merge; 512 was the fastest of 128, 256 and
+// 512 on the prefix-shared batches.
+constexpr int kCascadeChunk = 512;
 
 // slots per (row, head): chunks of the shared part, then partitions of the
 // row's own tokens
@@ -537,7 +539,7 @@ int pa_decode_cascade(const pa_kv_cache *cache, void *out, const void *q, int32_
   a.shared_chunk = chunk;
 
   // chunks per group: enough for max_shared_len.  shared_len is clamped to
-  // the tokens those chunks cover (a multiple of 128, so of block_size);
+  // the tokens those chunks cover (a multiple of 512, so of block_size);
   // the members' partitions read anything past it.
   a.shared_chunks = std::max(1, (std::min(max_shared_len, max_context_len) + chunk - 1) / chunk);
   a.shared_cap = a.shared_chunks * chunk;

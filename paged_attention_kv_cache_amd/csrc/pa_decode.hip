@@ -84,9 +84,11 @@ struct DecodeKernelArgs {
   const int32_t *shared_len;
   int num_groups;
   int shared_chunk;      // the shared part's partials: slots 0 .. ceil(shared / shared_chunk) - 1
+  int shared_chunks;     // cascade: chunks per group this launch computes
   int shared_cap;        // shared tokens are clamped to this (the chunks launched)
-  int shared_z;          // grid z slots of the shared chunks (chunks x col_tiles; 0: none in this launch)
-  int col_tiles;         // 16-column tiles per group: ceil(max_group_size * G / 16)
+  int shared_items;      // cascade: launch items of the shared chunks (0: none in this launch)
+  int shared_stride;     // cascade: items between the column tiles of one shared chunk
+  int col_tiles;         // cascade: 16-column tiles per group, ceil(max_group_size * G / 16)
   // prefill rows (non-NULL): index r of the generic kernel is packed query
   // row r of sequences 0 .. num_prefill_seqs-1 (see decode_row)
   const int32_t *query_start_loc;
@@ -817,9 +819,12 @@ __device__ __forceinline__ void decode_shared_chunk(const DecodeKernelArgs &a, i
 // The partition kernel on Bf16DecodeMfma: work-group (group of 4 kv heads,
 // sequence, partition), one wave per kv head; plain decode in size order
 // (size_order_item).  Cascade launches number their items z * S + y: the
-// groups' shared chunks first (shared_z = chunks x column tiles per
-// group), then each row's own tokens after its shared ones, partition by
-// partition (into the slots after the row's shared chunks').
+// groups' shared chunks first (every column tile of every chunk), then each
+// row's own tokens after its shared ones in size order (into the slots
+// after the row's shared chunks').  The column tiles of one chunk are
+// shared_stride items apart, so that (with work-groups dealt round-robin
+// to the 8 XCDs by their linear id) they run on one XCD and the chunk's
+// K/V rows are fetched into its L2 once.
 template <int D, int DV, int G>
 __global__ void __launch_bounds__(64 * kDecodeWaves)
 // four work-groups per CU (one tile's rows in registers per wave, up to
@@ -836,11 +841,10 @@ decode_partition_mfma_kernel(const DecodeKernelArgs a) {
   int shared_item = -1, own_item = -1;
   if (cascade) {
     const int L = blockIdx.z * gridDim.y + blockIdx.y;
-    const int nsh = a.num_groups * a.shared_z;
-    if (L < nsh) {
+    if (L < a.shared_items) {
       shared_item = L;
     } else {
-      own_item = L - nsh;
+      own_item = L - a.shared_items;
       seq = own_item % a.num_seqs;
       part = own_item / a.num_seqs;
     }
@@ -871,8 +875,11 @@ decode_partition_mfma_kernel(const DecodeKernelArgs a) {
   typedef __attribute__((address_space(3))) char *lds_char_ptr;
   const uint32_t my_lds = (uint32_t)(size_t)(lds_char_ptr)(&lds[wave][0]);
   if (shared_item >= 0) {
-    const int grp = shared_item / a.shared_z, r = shared_item % a.shared_z;
-    decode_shared_chunk<D, DV, G>(a, grp, r / a.col_tiles, r % a.col_tiles, kvh, lane, my_lds);
+    const int st = a.shared_stride;
+    const int ct = (shared_item / st) % a.col_tiles;                    // column tile
+    const int pc = (shared_item / (st * a.col_tiles)) * st + shared_item % st;  // (group, chunk)
+    if (pc < a.num_groups * a.shared_chunks)
+      decode_shared_chunk<D, DV, G>(a, pc / a.shared_chunks, pc % a.shared_chunks, ct, kvh, lane, my_lds);
     return;
   }
   const int ctx = decode_context(a, seq);
@@ -1073,7 +1080,9 @@ static DecodeKernelArgs make_kernel_args(const DecodeArgs &a) {
   k.num_groups = a.num_groups;
   k.shared_chunk = a.shared_chunk;
   k.shared_cap = a.shared_cap;
-  k.shared_z = 0;
+  k.shared_chunks = a.shared_chunks;
+  k.shared_items = 0;
+  k.shared_stride = 1;
   k.col_tiles = 1;
   k.query_start_loc = a.query_start_loc;
   k.num_prefill_seqs = a.num_prefill_seqs;
@@ -1091,9 +1100,21 @@ int cascade_own_partitions(const DecodeArgs &a) {
   return (int)(n > 1 ? n : 1);
 }
 
+// Launch items of a cascade's shared chunks: (group, chunk) pairs in runs
+// of `stride`, each run repeated for every column tile, so that the column
+// tiles of one chunk are `stride` items apart.  With gridDim.x work-groups
+// per item and linear work-group ids dealt round-robin over 8 XCDs, items
+// 8 / gcd(gridDim.x, 8) apart run on the same XCD.
+int64_t cascade_shared_items(const DecodeArgs &a, int col_tiles, int &stride) {
+  const int x = (a.cache.num_kv_heads + kDecodeWaves - 1) / kDecodeWaves;
+  stride = (x % 8 == 0) ? 1 : (x % 4 == 0) ? 2 : (x % 2 == 0) ? 4 : 8;
+  const int64_t pairs = (int64_t)a.num_groups * a.shared_chunks;
+  return (pairs + stride - 1) / stride * stride * col_tiles;
+}
+
 int cascade_grid_z(const DecodeArgs &a, int col_tiles) {
-  const int64_t items =
-      (int64_t)a.num_groups * a.shared_chunks * col_tiles + (int64_t)a.num_seqs * cascade_own_partitions(a);
+  int stride;
+  const int64_t items = cascade_shared_items(a, col_tiles, stride) + (int64_t)a.num_seqs * cascade_own_partitions(a);
   const int64_t z = (items + a.num_seqs - 1) / a.num_seqs;
   return (int)(z < 0x7fffffff ? z : 0x7fffffff);
 }
@@ -1110,7 +1131,7 @@ static hipError_t launch_partition_t(const DecodeArgs &a, hipStream_t stream) {
     int zs = a.max_partitions;
     if (a.group_start) {
       k.col_tiles = (a.max_group_size * G + 15) / 16;
-      k.shared_z = a.shared_chunks * k.col_tiles;
+      k.shared_items = (int)cascade_shared_items(a, k.col_tiles, k.shared_stride);
       zs = cascade_grid_z(a, k.col_tiles);
     }
     grid = dim3((a.cache.num_kv_heads + kDecodeWaves - 1) / kDecodeWaves, a.num_seqs, zs);

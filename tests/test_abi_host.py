@@ -303,8 +303,8 @@ def test_cascade_validation(lib):
     need = P.pa_decode_cascade_workspace_bytes(4, 32, 128, 1000, 256)
     assert casc(ws=None) == -7 and f"{need} bytes needed" in msg()
     assert casc(ws_bytes=need - 1) == -7
-    # slots: 128-token chunks of the shared part, then the row's partitions
-    n = 4 * 32 * (-(-1000 // 128) + -(-1000 // 256))
+    # slots: 512-token chunks of the shared part, then the row's partitions
+    n = 4 * 32 * (-(-1000 // 512) + -(-1000 // 256))
     a = lambda x: (x + 255) // 256 * 256
     assert need == 2 * a(4 * n) + a(4 * n * 128)
     assert casc(S=0, ng=0) == 0

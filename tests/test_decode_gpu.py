@@ -537,12 +537,35 @@ def test_cascade_irregular_groups(group):
         log(f"cascade irregular G={group} partition={ps}")
         got = _cascade(case, starts, shared, ps)
         assert_close(got, ref, W.BF16, f"cascade irregular G{group} ps{ps}")
-    # a max_shared_len below the largest shared_len: the 192 shared tokens
-    # are clamped to one 128-token chunk and the rest run in the partitions
+    # max_shared_len below the largest shared_len (one 512-token chunk
+    # still covers the 192 shared tokens)
     for msl in (0, 100):
         log(f"cascade irregular G={group} max_shared_len={msl}")
         got = _cascade(case, starts, shared, 64, max_shared_len=msl)
         assert_close(got, ref, W.BF16, f"cascade irregular G{group} clamp{msl}")
+
+
+@pytest.mark.parametrize("group", [4, 8])
+def test_cascade_shared_clamp(group):
+    """Shared parts longer than one 512-token chunk (640 and 900 tokens)
+    under max_shared_len 0, 100 and 600: one chunk each (the tokens past 512
+    then run in the members' own partitions) or two (no clamp)."""
+    sizes = [3, 5, 2]
+    starts = np.cumsum([0] + sizes).tolist()
+    group_of = [g for g, n in enumerate(sizes) for _ in range(n)]
+    bs, shared_blocks = 16, 57
+    rng = np.random.default_rng(60 + group)
+    ctx = [int(x) for x in rng.integers(shared_blocks * bs + 1, 1600, size=sum(sizes))]
+    ctx[3] = 700                               # a row ending inside its group's shared part
+    hkv = 2
+    case = W.random_decode(6000 + group, ctx, num_heads=hkv * group, num_kv_heads=hkv, head_dim=128, block_size=bs,
+                           dtype=W.BF16, shared_blocks=shared_blocks, group_of=group_of)
+    ref = oracle_decode(case)
+    shared = [640, 900, 0]
+    for msl in (0, 100, 600, None):
+        log(f"cascade clamp G={group} max_shared_len={msl}")
+        got = _cascade(case, starts, shared, 384, max_shared_len=msl)
+        assert_close(got, ref, W.BF16, f"cascade clamp G{group} msl{msl}")
 
 
 @pytest.mark.parametrize("group,dims", [(4, (128, 128)), (8, (128, 128)), (2, (64, 128)), (4, (128, 64))])
