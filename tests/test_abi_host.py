@@ -308,6 +308,11 @@ def test_cascade_validation(lib):
     a = lambda x: (x + 255) // 256 * 256
     assert need == 2 * a(4 * n) + a(4 * n * 128)
     assert casc(S=0, ng=0) == 0
+    # one launch runs every group's shared chunks (x their column tiles)
+    # ahead of the rows' own partitions: more than 65,535 grid rows of
+    # num_seqs items are rejected before any launch
+    huge = 1 << 26
+    assert casc(S=256, ng=256, mg=1, mcl=huge, msl=huge, ws_bytes=1 << 60) == -3 and "grid rows" in msg()
 
 
 def test_decode_append_validation(lib):
