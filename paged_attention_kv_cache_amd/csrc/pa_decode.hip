@@ -488,6 +488,10 @@ __device__ __forceinline__ bool size_order_item(const DecodeKernelArgs &a, int i
 //  * Fused append: the newest token's rows come from the input rows (they
 //    replace the loaded slot contents in registers) and are written into
 //    its slot after the last tile.
+//  * Cascade decode's shared chunks run on the same products with other
+//    columns: column j is query head j % G of member j / G of a group's
+//    16/G-member column tile, each column with a key limit of its own
+//    (decode_shared_chunk).
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
