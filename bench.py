@@ -444,11 +444,15 @@ def bench_serving(seed=7000, num_requests=96, num_blocks=12000, mixed=False):
     src_v = torch.randn_like(src_k)
     src_q = torch.randn((cap_tokens, Hq, D), device="cuda").to(torch.bfloat16)
     out = torch.empty_like(src_q)
-    pin = dict(qsl=torch.zeros(cap_seqs + 1, dtype=torch.int32).pin_memory(),
-               ctx=torch.zeros(cap_seqs, dtype=torch.int32).pin_memory(),
-               tab=torch.zeros((cap_seqs, cap_blocks), dtype=torch.int32).pin_memory(),
-               slots=torch.zeros(cap_tokens, dtype=torch.int64).pin_memory())
-    dev = {k: torch.empty_like(v, device="cuda") for k, v in pin.items()}
+    # two sets of pinned staging buffers: the host fills one while the
+    # other's copies may still wait in the stream behind earlier kernels;
+    # a set is refilled only after the event recorded behind its copies
+    pins = [dict(qsl=torch.zeros(cap_seqs + 1, dtype=torch.int32).pin_memory(),
+                 ctx=torch.zeros(cap_seqs, dtype=torch.int32).pin_memory(),
+                 tab=torch.zeros((cap_seqs, cap_blocks), dtype=torch.int32).pin_memory(),
+                 slots=torch.zeros(cap_tokens, dtype=torch.int64).pin_memory()) for _ in range(2)]
+    copied = [None, None]
+    dev = {k: torch.empty_like(v, device="cuda") for k, v in pins[0].items()}
     ws = torch.zeros(P.pa_decode_workspace_bytes(cap_seqs, Hq, D, cap_blocks * bs, 256), dtype=torch.uint8,
                      device="cuda")
     scale = 1.0 / math.sqrt(D)
@@ -462,12 +466,18 @@ def bench_serving(seed=7000, num_requests=96, num_blocks=12000, mixed=False):
             break
         st = sched.next_step()
         n, T = st.num_seqs, st.num_tokens
+        b = steps % 2
+        if copied[b] is not None:
+            copied[b].synchronize()  # this set's previous copies have run
+        pin = pins[b]
         pin["qsl"][: n + 1].numpy()[:] = st.query_start_loc
         pin["ctx"][:n].numpy()[:] = st.context_lens
         pin["tab"][:n].numpy()[:] = st.block_tables
         pin["slots"][:T].numpy()[:] = st.slot_mapping
         for k in pin:
             dev[k].copy_(pin[k], non_blocking=True)
+        copied[b] = torch.cuda.Event()
+        copied[b].record()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         P.pa_kv_cache_write(src_k[:T], src_v[:T], kc, vc, dev["slots"][:T])
