@@ -683,6 +683,9 @@ __global__ void __launch_bounds__(kPrefillThreads, 1) prefill_chunk_kernel(const
   const float lsum = xor32_sum(l);  // cross-lane: before the divergent store
   if (qvalid) {
     uint16_t *orow = static_cast<uint16_t *>(a.out) + ((size_t)(r0 + t) * a.num_heads + head) * DV;
+    // one division per row, then a multiply per element (an IEEE division
+    // per element is ~10 vector instructions)
+    const float inv = (lsum > 0.f) ? 1.f / lsum : 0.f;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
@@ -690,7 +693,7 @@ __global__ void __launch_bounds__(kPrefillThreads, 1) prefill_chunk_kernel(const
         const int d0 = dt * 32 + 8 * rq + 4 * hh;
         float v[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = (lsum > 0.f) ? o[dt][4 * rq + e] / lsum : 0.f;
+        for (int e = 0; e < 4; ++e) v[e] = o[dt][4 * rq + e] * inv;
         *reinterpret_cast<uint2 *>(orow + d0) = make_uint2(pack_bf16x2_rne(v[0], v[1]), pack_bf16x2_rne(v[2], v[3]));
       }
   }
