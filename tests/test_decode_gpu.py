@@ -678,3 +678,58 @@ def test_decode_append_bs32_full():
     torch().cuda.synchronize()
     mx, mean = assert_close(to_host_f32(out, W.BF16), ref, W.BF16, "append bs32")
     print(f"append bs32: max-abs {mx:.2e} mean-abs {mean:.2e}")
+
+
+@pytest.mark.parametrize("seed", range(36))
+def test_decode_random_shapes(seed):
+    """Seeded random shapes through the bf16 decode kernel against the
+    oracle: query heads per kv head, kv heads (not always a multiple of
+    four), key and value head dims, block size, partition size (0 = single
+    pass), contexts from 0 to ~2,500 tokens, and the mode: plain decode,
+    fused append (pools bit-exact with the oracle's write) or cascade over
+    random groups with random shared lengths up to their true sharing."""
+    import paged_attention_kv_cache_amd as P
+    t = torch()
+    rng = np.random.default_rng(8800 + seed)
+    G = int(rng.choice([1, 2, 4, 8]))
+    hkv = int(rng.choice([1, 2, 3, 5, 8]))
+    D, Dv = int(rng.choice([64, 128])), int(rng.choice([64, 128]))
+    bs = int(rng.choice([8, 16, 32]))
+    S = int(rng.integers(1, 41))
+    mode = ["plain", "append", "cascade"][seed % 3]
+    ps = int(rng.choice([0, bs, 64, 192, 512])) if mode != "cascade" else int(rng.choice([bs, 64, 192, 384]))
+    ctx = rng.integers(0, 2500, size=S).tolist()
+    for i in rng.choice(S, size=min(S, 3), replace=False):
+        ctx[int(i)] = int(rng.choice([0, 1, bs - 1, bs, bs + 1, 63, 64, 65]))
+    group_of, shared_blocks = None, 0
+    if mode == "cascade":
+        shared_blocks = int(rng.integers(1, 24))
+        sizes, left = [], S
+        while left > 0:
+            sizes.append(int(min(left, rng.integers(1, 12))))
+            left -= sizes[-1]
+        group_of = [g for g, n in enumerate(sizes) for _ in range(n)]
+    case = W.random_decode(9900 + seed, ctx, num_heads=hkv * G, num_kv_heads=hkv, head_dim=D, v_head_dim=Dv,
+                           block_size=bs, dtype=W.BF16, shared_blocks=shared_blocks, group_of=group_of,
+                           extra_table_cols=1)
+    ref = oracle_decode(case)
+    what = f"seed {seed} {mode} G{G} hkv{hkv} D{D} Dv{Dv} bs{bs} S{S} ps{ps}"
+    log(what)
+    if mode == "plain":
+        _, got = _run(case, ps)
+    elif mode == "append":
+        key, val = _append_rows(case)
+        k_ref, v_ref = oracle.kv_cache_write(case.k_cache, case.v_cache, case.new_key, case.new_value,
+                                             case.slot_mapping)
+        dev = DeviceCase(case)
+        out = P.pa_decode_append(dev.q, to_dev(key, W.BF16), to_dev(val, W.BF16), dev.k_cache, dev.v_cache,
+                                 dev.block_tables, dev.context_lens, case.scale, case.max_context_len, ps)
+        t.cuda.synchronize()
+        got = to_host_f32(out, W.BF16)
+        assert np.array_equal(to_host_bits(dev.k_cache).view(np.uint16), k_ref.view(np.uint16)), what + " K pool"
+        assert np.array_equal(to_host_bits(dev.v_cache).view(np.uint16), v_ref.view(np.uint16)), what + " V pool"
+    else:
+        starts = np.cumsum([0] + sizes).tolist()
+        shared = [int(rng.integers(0, shared_blocks * bs + 1)) for _ in sizes]
+        got = _cascade(case, starts, shared, ps, max_shared_len=int(rng.choice([0, 256, 4096])))
+    assert_close(got, ref, W.BF16, what)
