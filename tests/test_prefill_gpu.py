@@ -245,3 +245,32 @@ def test_prefill_fp32_rows_outside_sequences_untouched():
     got = out.cpu().numpy()
     assert (got[Tq:] == 7.0).all(), "rows outside every sequence were written"
     assert_close(got[:Tq], oracle_prefill(case), W.F32, "owned rows")
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_prefill_random_shapes(seed):
+    """Seeded random chunked-prefill shapes against the oracle: query heads
+    per kv head, kv heads, key and value head dims, block size, 1 to 10
+    sequences with cached prefixes of 0 to ~1,500 tokens and chunks of 0 to
+    ~300 new tokens (some of one token, some empty), and the storage type
+    (one seed in four in fp32)."""
+    rng = np.random.default_rng(7700 + seed)
+    G = int(rng.choice([1, 2, 4, 8]))
+    hkv = int(rng.choice([1, 2, 3, 5, 8]))
+    D, Dv = int(rng.choice([64, 128])), int(rng.choice([64, 128]))
+    bs = int(rng.choice([8, 16, 32]))
+    dtype = W.F32 if seed % 4 == 3 else W.BF16
+    S = int(rng.integers(1, 11))
+    prefixes = rng.integers(0, 1500, size=S).tolist()
+    qlens = rng.integers(0, 300, size=S).tolist()
+    for i in rng.choice(S, size=min(S, 2), replace=False):
+        qlens[int(i)] = int(rng.choice([0, 1, 31, 32, 33]))
+        prefixes[int(i)] = int(rng.choice([0, bs - 1, bs, prefixes[int(i)]]))
+    case = W.random_prefill(7800 + seed, prefixes, qlens, num_heads=hkv * G, num_kv_heads=hkv, head_dim=D,
+                            v_head_dim=Dv, block_size=bs, dtype=dtype, extra_table_cols=1)
+    what = f"seed {seed} {dtype} G{G} hkv{hkv} D{D} Dv{Dv} bs{bs} prefixes {prefixes} chunks {qlens}"
+    log(what)
+    _, got = _run(case)
+    ref = oracle_prefill(case)
+    assert ref.shape == (sum(qlens), hkv * G, Dv)
+    assert_close(got, ref, dtype, what)
