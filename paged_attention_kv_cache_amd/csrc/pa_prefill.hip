@@ -9,16 +9,19 @@
 // shapes of the scheduling section of the mistral.rs comparison page.
 //
 // How it maps to gfx950:
-//  * A work-group (8 waves) serves one kv head: its G query heads (8 at
-//    most) x 32-token query groups of one sequence's chunk (64 tokens for
-//    G = 4).  Every K/V tile is gathered once per work-group and shared by
-//    all of its query heads through LDS.
+//  * A work-group (4 waves, two per CU) serves one kv head: 4 of its
+//    query heads x 32 tokens of one sequence's chunk (fewer heads and more
+//    32-token groups for G < 4; G = 8 takes two work-groups).  Every K/V
+//    tile is gathered once per work-group and shared by its waves through
+//    LDS.  Small work items (32 queries at G = 4) let the CUs share a
+//    launch evenly, and the two work-groups of a CU, which do not wait for
+//    each other, fill each other's stalls.
 //  * K/V tiles of 64 keys are gathered through the block table straight
 //    into LDS with 16-byte global-to-LDS loads (no registers, no LDS store
 //    instructions), both row-major [key][d] in swizzled 64-byte chunk
-//    groups (see TileGather).  A wave's load covers 16 keys, which lie in
-//    one block for block sizes 16 and 32, so the block id is a scalar load
-//    and the block's address a scalar sum.  Keys past the last position
+//    groups (see TileGather).  A wave's loads of a tile cover 16 keys,
+//    which lie in one block for block sizes 16 and 32, so the block id is
+//    one scalar load and the block's address a scalar sum.  Keys past the last position
 //    the work-group needs, and keys in an invalid block, read a zero chunk
 //    instead, so a masked key never brings a NaN into the products.
 //  * The scale (times log2(e), so that the softmax uses exp2) multiplies
@@ -41,17 +44,17 @@
 //    them exceeds 2^32 (a score far above the reference) is the tile
 //    recomputed with a new reference.  The final division by the running
 //    sum makes any reference exact up to rounding.
-//  * LDS holds four K and four V tiles.  In step t a wave computes the
+//  * LDS holds three K and two V tiles.  In step t a wave computes the
 //    scores of tile t+1 while it runs the exponentials of tile t
 //    (independent work for the matrix and vector units), then multiplies V
-//    of tile t; the loads of tiles t+2 and t+3 into LDS are in flight
-//    meanwhile, and those of tile t+2 are waited for before the step's
-//    single barrier.
+//    of tile t; K of tile t+2 and V of tile t+1 are loaded into LDS
+//    meanwhile and waited for before the step's single barrier.
 //  * Work ids are remapped so that each XCD serves whole kv heads of every
 //    sequence: the XCDs get equal work, and the query tiles of one
 //    (sequence, kv head), which read the same K/V, share that XCD's L2.
 //    Within a kv head the (sequence, query tile) items are dispatched
-//    longest first (most keys to read).
+//    longest first (most key tiles to read), each work-group finding its
+//    item from the context lengths (pick_item).
 //  * Key and value head dims may differ (section 4.1 of the same page):
 //    the K tile, Q and the score products take the key dim D, the V^T tile
 //    and the output tiles the value dim DV.
@@ -92,23 +95,26 @@ __device__ __forceinline__ bf16x8_t pack8(const f32x16_t &s, int base) {
   return r;
 }
 
-constexpr int kPrefillWaves = 8;  // one work-group per CU shares each tile among 8 waves
+constexpr int kPrefillWaves = 4;  // waves per work-group, two work-groups per CU (2 waves per SIMD)
 constexpr int kPrefillThreads = 64 * kPrefillWaves;
 constexpr int KT = 64;            // keys per tile
-constexpr int kBufs = 4;          // LDS tile buffers: loads run three tiles ahead
+constexpr int kKBufs = 3;         // K tiles in LDS: scores of t+1 read, t+2 loading, t kept
+constexpr int kVBufs = 2;         // V tiles in LDS: P.V of t read, t+1 loading
 
 typedef const __attribute__((address_space(4))) int32_t *tab_ptr_t;  // scalar loads of table entries
 typedef __attribute__((address_space(3))) void *lds_ptr_t;
 
-// source of the 16-byte chunks of keys that must read as zero (blocks of 8)
-__device__ const uint4 kZeroChunk = {0u, 0u, 0u, 0u};
+// source of the 16-byte chunks of keys that must read as zero (blocks of 8;
+// a wave's loads of one tile read it at offsets of up to 192 bytes)
+__device__ const uint4 kZeroChunk[16] = {};
 // last word of a raw buffer descriptor (32-bit data format, no swizzle)
 constexpr int kRsrcWord3 = 0x00020000;
 
 // The tile loads are issued as inline assembly.  The compiler then does
 // not know that they write LDS, so it does not wait for them before the
 // step's own LDS reads (of other tiles); the kernel waits for them itself,
-// one step later, before the barrier that precedes their first reader.
+// at the end of the step that issues them, before the barrier that precedes
+// their first reader.
 //
 // 16 bytes per lane from a raw buffer of `bytes` bytes at `base` (uniform)
 // into LDS at lds_addr + 16 * lane; a lane whose offset is out of range gets
@@ -130,7 +136,7 @@ __device__ __forceinline__ void dma_global16(uint32_t lds_addr, const void *src)
                : "s"(lds_addr), "v"(src)
                : "memory", "m0");
 }
-// entries i[0..1] (or i[0..3]) of a table row, read through the scalar
+// entries i[0..1] of a table row, read through the scalar
 // cache and waited for at once (a few cycles from the scalar cache; issued
 // where the wave has no LDS reads in flight, so the wait holds up nothing
 // else).  The outputs are early-clobber: a load may land before the next
@@ -142,14 +148,6 @@ __device__ __forceinline__ void table_entries2(const int32_t *row, const int (&i
                : "memory");
   v[2] = v[0];
   v[3] = v[1];
-}
-__device__ __forceinline__ void table_entries4(const int32_t *row, const int (&i)[4], int (&v)[4]) {
-  asm volatile(
-      "s_load_dword %0, %4, %5\n\ts_load_dword %1, %4, %6\n\t"
-      "s_load_dword %2, %4, %7\n\ts_load_dword %3, %4, %8\n\ts_waitcnt lgkmcnt(0)"
-      : "=&s"(v[0]), "=&s"(v[1]), "=&s"(v[2]), "=&s"(v[3])
-      : "s"(row), "s"(i[0] * 4), "s"(i[1] * 4), "s"(i[2] * 4), "s"(i[3] * 4)
-      : "memory");
 }
 // s_waitcnt with only vmcnt = n (n < 64) counted
 template <int N>
@@ -166,86 +164,80 @@ __device__ __forceinline__ void wait_vmcnt() {
 // (c % 4) ^ ((k / 4) % 4).  Sixteen consecutive keys then cover all LDS
 // banks for any fixed chunk, and the slot pattern depends on a lane's key
 // only through (k / 4) % 4, so every fragment read is a per-lane base plus
-// a compile-time offset.  A wave's load writes 1 KB of consecutive LDS
-// (lane i at 16 i): the 16 keys kg .. kg+15 x one chunk group, each lane
-// fetching the global chunk that belongs in its slot.  A tile starts at a
-// multiple of 64 keys and the block size divides 64, so a lane's offset
-// inside its block is the same for every tile; only the block ids change.
-// With blocks of 16 or 32 keys a load's 16 keys share one block, whose id
-// and address are wave-uniform; with blocks of 8 the two half-waves have a
-// block each.
-template <int DIM>
-struct TileGather {
-  static constexpr int CG = DIM / 32;                        // chunk groups per row
-  static constexpr int PER_WAVE = (CG * 4) / kPrefillWaves;  // wave loads per tile
-  static_assert(PER_WAVE >= 1 && (CG * 4) % kPrefillWaves == 0, "tile split over the waves");
-  int kg[PER_WAVE];         // first key of the load's 16 keys (wave-uniform)
-  uint32_t off[PER_WAVE];   // byte offset of this lane's chunk inside its block
-  uint32_t lds[PER_WAVE];   // byte offset of the wave's load inside the tile (wave-uniform)
-  int lkey;                 // this lane's key within the load's 16: lane / 4
+// a compile-time offset.  One load writes 1 KB of consecutive LDS (lane i
+// at 16 i): 16 keys x one chunk group, each lane fetching the global chunk
+// that belongs in its slot.  The NWL waves that share a tile split its
+// loads so that all loads of one wave cover the same 16 keys (key group
+// wave % 4) and differ only in the chunk group: one block id per wave and
+// tile (two with blocks of 8 keys, one per half-wave), and a lane's byte
+// offset inside its block that changes by 64 bytes per chunk group.  A tile
+// starts at a multiple of 64 keys and the block size divides 64, so that
+// offset is the same for every tile; only the block ids change.
+struct TileIds {
+  int id[2];
+};
 
-  __device__ __forceinline__ void init(int wave, int lane, int bs_mask, uint32_t slot_stride) {
+template <int DIM, int NWL>
+struct TileGather {
+  static constexpr int CG = DIM / 32;            // chunk groups per row
+  static constexpr int PER_WAVE = (CG * 4) / NWL;  // loads per wave and tile
+  static constexpr uint32_t kChunkStep = (NWL / 4) * 64;  // bytes between a wave's loads in the block
+  static_assert(NWL % 4 == 0 && PER_WAVE >= 1 && (CG * 4) % NWL == 0, "tile split over the waves");
+  int kg;          // first key of the wave's 16 keys (wave-uniform)
+  uint32_t off0;   // byte offset of this lane's first chunk inside its block
+  uint32_t lds0;   // byte offset of the wave's first load inside the tile (wave-uniform)
+  int lkey;        // this lane's key within the 16: lane / 4
+
+  __device__ __forceinline__ void init(int wl, int lane, int bs_mask, uint32_t slot_stride) {
     lkey = lane >> 2;
-#pragma unroll
-    for (int j = 0; j < PER_WAVE; ++j) {
-      const int load = wave * PER_WAVE + j;  // chunk group load / 4, key group load % 4
-      kg[j] = (load % 4) * 16;
-      const int key = kg[j] + lkey;
-      const int chunk = (load / 4) * 4 + ((lane % 4) ^ ((key >> 2) & 3));
-      off[j] = ((uint32_t)(key & bs_mask) * slot_stride + (uint32_t)chunk * 8) * 2u;
-      lds[j] = (uint32_t)load * 1024;
-    }
+    kg = (wl % 4) * 16;
+    const int key = kg + lkey;
+    // load j of this wave is tile load j * NWL + wl: key group wl % 4, chunk
+    // group j * NWL / 4 + wl / 4
+    const int chunk = (wl / 4) * 4 + ((lane % 4) ^ ((key >> 2) & 3));
+    off0 = ((uint32_t)(key & bs_mask) * slot_stride + (uint32_t)chunk * 8) * 2u;
+    lds0 = (uint32_t)wl * 1024;
   }
-  // block ids (wave-uniform) the loads of the tile at k0 need, read from the
-  // table row (indices clamped into it): load j takes block id[j][0], with
-  // blocks of 8 keys its upper half-wave id[j][1]
-  struct Ids {
-    int id[PER_WAVE][2];
-  };
+  // block ids (wave-uniform) of the wave's 16 keys in the tile at k0, read
+  // from the table row (indices clamped into it): id[0], and with blocks of
+  // 8 keys id[1] for the upper half-wave
+  using Ids = TileIds;
   __device__ __forceinline__ Ids ids(bool kBs8, const int32_t *row, int k0, int shift, int max_blocks) const {
-    static_assert(PER_WAVE <= 2, "at most four table entries per read");
-    // entry e: load e / 2 (blocks of 8: half e % 2), or load e (larger blocks)
     int idx[4], v[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int j = (kBs8 ? e / 2 : e) % PER_WAVE, h = kBs8 ? e % 2 : 0;
-      idx[e] = min(__builtin_amdgcn_readfirstlane(((k0 + kg[j]) >> shift) + h), max_blocks - 1);
-    }
-    if (kBs8)
-      table_entries4(row, idx, v);
-    else
-      table_entries2(row, idx, v);
+    const int e = (k0 + kg) >> shift;
+    idx[0] = __builtin_amdgcn_readfirstlane(min(e, max_blocks - 1));
+    idx[1] = __builtin_amdgcn_readfirstlane(min(e + (kBs8 ? 1 : 0), max_blocks - 1));
+    table_entries2(row, idx, v);
     Ids r;
-#pragma unroll
-    for (int j = 0; j < PER_WAVE; ++j) {
-      r.id[j][0] = kBs8 ? v[2 * j] : v[j];
-      r.id[j][1] = kBs8 ? v[2 * j + 1] : v[j];
-    }
+    r.id[0] = v[0];
+    r.id[1] = v[1];
     return r;
   }
-  // kBs8: blocks of 8 keys; kPartial: keys at or past kend read zeros (the
-  // last tile of a range).  Both are constants at every call.
-  // loads of one tile into the LDS tile at lds_tile (PER_WAVE per wave)
+  // the wave's loads of one tile into the LDS tile at lds_tile.  kBs8:
+  // blocks of 8 keys; kPartial: keys at or past kend read zeros (the last
+  // tiles of a range).  Both are constants at every call.
   __device__ __forceinline__ void issue(bool kBs8, bool kPartial, uint32_t lds_tile, const Ids &ids, const char *base,
                                         const char *zero, int num_blocks, uint32_t block_bytes, int k0, int kend,
                                         int lane) const {
+    const bool kok = !kPartial || (k0 + kg + lkey < kend);
+    if (!kBs8) {
+      // one block for the wave: a buffer over it, empty for an id outside
+      // the pool; out-of-range reads (an empty buffer, or a key past kend
+      // sent past the end) return zeros
+      const int b = ids.id[0];
+      const bool bok = (unsigned)b < (unsigned)num_blocks;
+      const char *blk = base + (size_t)(unsigned)(bok ? b : 0) * block_bytes;
+      const uint32_t vo = kok ? off0 : 0x80000000u;
+      const int nbytes = bok ? (int)block_bytes : 0;
 #pragma unroll
-    for (int j = 0; j < PER_WAVE; ++j) {
-      const bool kok = !kPartial || (k0 + kg[j] + lkey < kend);
-      if (!kBs8) {
-        // one block for the wave: a buffer over it, empty for an id outside
-        // the pool; out-of-range reads (an empty buffer, or a key past kend
-        // sent past the end) return zeros
-        const int b = ids.id[j][0];
-        const bool bok = (unsigned)b < (unsigned)num_blocks;
-        const char *blk = base + (size_t)(unsigned)(bok ? b : 0) * block_bytes;
-        dma_buffer16(lds_tile + lds[j], kok ? off[j] : 0x80000000u, blk, bok ? (int)block_bytes : 0);
-      } else {
-        const int b = (lane < 32) ? ids.id[j][0] : ids.id[j][1];
-        const bool ok = kok && (unsigned)b < (unsigned)num_blocks;
-        const char *src = ok ? base + (size_t)(unsigned)b * block_bytes + off[j] : zero;
-        dma_global16(lds_tile + lds[j], src);
-      }
+      for (int j = 0; j < PER_WAVE; ++j)
+        dma_buffer16(lds_tile + lds0 + (uint32_t)j * NWL * 1024, vo + (uint32_t)j * kChunkStep, blk, nbytes);
+    } else {
+      const int b = (lane < 32) ? ids.id[0] : ids.id[1];
+      const bool ok = kok && (unsigned)b < (unsigned)num_blocks;
+      const char *src = ok ? base + (size_t)(unsigned)b * block_bytes + off0 : zero;
+#pragma unroll
+      for (int j = 0; j < PER_WAVE; ++j) dma_global16(lds_tile + lds0 + (uint32_t)j * NWL * 1024, src + j * kChunkStep);
     }
   }
 };
@@ -260,6 +252,9 @@ constexpr float kSumLimit = 4294967296.f;
 
 constexpr uint32_t kBf16PairOnes = 0x3F803F80u;  // two bf16 1.0
 
+// Work-group shape for G query heads per kv head: 4 waves, each one query
+// head x 32 queries; with G < 4 the waves take more query groups of the
+// same heads, with G = 8 a kv head's heads take two work-groups.
 template <int G>
 struct PrefillShape {
   static constexpr int NW = kPrefillWaves;         // waves per work-group
@@ -270,81 +265,153 @@ struct PrefillShape {
   static_assert(G % GWH == 0 && NW % GWH == 0, "heads and waves must divide");
 };
 
+// sum over the wave of x (0 <= x < 2^bits, bits wave-uniform): one ballot
+// and one popcount per bit, all scalar after the compare
+__device__ __forceinline__ int wave_sum_bits(int x, int bits) {
+  int s = 0;
+  for (int b = 0; b < bits; ++b) s += (int)__builtin_popcountll(__builtin_amdgcn_ballot_w64((x >> b) & 1)) << b;
+  return s;
+}
+// the same sum over the lanes below this one
+__device__ __forceinline__ int wave_prefix_bits(int x, int bits) {
+  int s = 0;
+  for (int b = 0; b < bits; ++b) {
+    const unsigned long long m = __builtin_amdgcn_ballot_w64((x >> b) & 1);
+    s += (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u)) << b;
+  }
+  return s;
+}
+
+// sequences up to which a work-group picks its item by size
+constexpr int kRankSeqChunks = 4;
+
+// Dispatch order by size.  The items of one (kv head, head part) are the
+// pairs (sequence s, query tile qt) with qt * QT < q_len(s); an item reads
+// tiles = ceil(keys / 64) key tiles, keys = min(context, prefix + QT (qt +
+// 1)), and costs about tiles + 1 (its fixed work).  The cost does not
+// decrease with qt, so the number of items of s that cost more than W has a
+// closed form: every qt from (64 (W - 1) - prefix) / QT on, if the context
+// has more than 64 (W - 1) keys.  The work-group at dispatch
+// position pos takes the pos-th costliest item (ties in (s, qt) order): a
+// binary search over W for the cost of that item, each probe summing the
+// per-sequence counts over the wave (lane = sequence, up to 4 per lane),
+// then the rank among the items of that cost.  Returns false for a position
+// past the last item.  Every wave computes the same result from the same
+// values.
+template <int QT>
+__device__ __forceinline__ bool pick_item(const PrefillKernelArgs &a, int pos, int lane, int &seq_out,
+                                          int &qt_out) {
+  constexpr int U = KT;  // keys per step of an item
+  const int nchunks = (a.num_seqs + 63) / 64;
+  int nq[kRankSeqChunks], cx[kRankSeqChunks], pf[kRankSeqChunks];
+#pragma unroll
+  for (int c = 0; c < kRankSeqChunks; ++c) {
+    nq[c] = 0;
+    cx[c] = 0;
+    pf[c] = 0;
+    const int s = c * 64 + lane;
+    if (c < nchunks && s < a.num_seqs) {
+      const int e1 = min(a.query_start_loc[s + 1], a.num_query_tokens);
+      const int e0 = max(0, min(a.query_start_loc[s], e1));
+      const int ql = e1 - e0;
+      cx[c] = max(0, min(a.context_lens[s], a.ctx_cap));
+      pf[c] = cx[c] - ql;
+      nq[c] = min((ql + QT - 1) / QT, a.n_qtiles);
+    }
+  }
+  // items of lane's sequences that cost more than W
+  auto above = [&](int W, int c) -> int {
+    if (W <= 0) return nq[c];
+    const int kth = U * (W - 1);
+    if (cx[c] <= kth) return 0;
+    const int d = kth - pf[c];
+    return max(0, nq[c] - (d > 0 ? d / QT : 0));
+  };
+  const int bits = 34 - __builtin_clz((unsigned)a.n_qtiles);  // 4 chunks of counts < 2 n_qtiles + 1
+  auto count_above = [&](int W) -> int {
+    int x = 0;
+#pragma unroll
+    for (int c = 0; c < kRankSeqChunks; ++c) x += above(W, c);
+    return wave_sum_bits(x, bits);
+  };
+  if (pos >= count_above(0)) return false;
+  // smallest W with count_above(W) <= pos: the cost of the pos-th item
+  int lo = 1, hi = (a.ctx_cap + U - 1) / U + 1;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (count_above(mid) <= pos)
+      hi = mid;
+    else
+      lo = mid + 1;
+  }
+  int r = pos - count_above(lo);  // rank among the items that cost exactly lo
+  const int nbits = 33 - __builtin_clz((unsigned)a.n_qtiles);
+#pragma unroll
+  for (int c = 0; c < kRankSeqChunks; ++c) {
+    if (c < nchunks) {
+      const int hi_c = above(lo - 1, c);
+      const int e = hi_c - above(lo, c);  // this lane's items of cost lo: qt in [nq - hi_c, nq - hi_c + e)
+      const int pre = wave_prefix_bits(e, nbits);
+      const int tot = wave_sum_bits(e, nbits);
+      if (r < tot) {
+        const unsigned long long hit = __builtin_amdgcn_ballot_w64(e > 0 && pre <= r && r < pre + e);
+        const int l = (int)__builtin_ctzll(hit);
+        const int qt = nq[c] - hi_c + (r - pre);
+        seq_out = c * 64 + l;
+        qt_out = __builtin_amdgcn_readlane(qt, l);
+        return true;
+      }
+      r -= tot;
+    }
+  }
+  return false;
+}
+
 template <int D, int DV, int G, bool kBs8>
-__global__ void __launch_bounds__(kPrefillThreads, 1) prefill_chunk_kernel(const PrefillKernelArgs a) {
+__global__ void __launch_bounds__(kPrefillThreads, 2) prefill_chunk_kernel(const PrefillKernelArgs a) {
   using Sh = PrefillShape<G>;
   constexpr int GWH = Sh::GWH;
   constexpr int HALVES = Sh::HALVES;
   constexpr int QT = Sh::QT;
-  using GK = TileGather<D>;
-  using GV = TileGather<DV>;
+  using GK = TileGather<D, kPrefillWaves>;
+  using GV = TileGather<DV, kPrefillWaves>;
   constexpr int NDS = D / 16;        // k-steps of Q K^T
   constexpr int NDT = DV / 32;       // 32-row tiles of O^T
 
-  // four buffers each for K and V: at step t the waves read K of tile t+1
-  // and V of tile t while tiles t+2 (issued in step t-1) and t+3 (issued in
-  // step t) are loaded
-  __shared__ __attribute__((aligned(1024))) uint16_t sk[kBufs][KT * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t sv[kBufs][KT * DV];
+  // kKBufs K tiles and kVBufs V tiles (80 KB at head dims 128: two
+  // work-groups fill a CU's LDS).  At step t the waves read K of tile t+1
+  // (scores) and V of tile t (P.V) while K of tile t+2 and V of tile t+1
+  // are loaded; K of tile t stays for a redo.
+  constexpr int kKTile = KT * D * 2, kVTile = KT * DV * 2;  // bytes
+  constexpr int kVBase = kKBufs * kKTile;
+  constexpr int kLdsBytes = kVBase + kVBufs * kVTile;
+  __shared__ __attribute__((aligned(1024))) char lds[kLdsBytes];
 
   // Work id.  Work-groups are dispatched round-robin over the 8 XCDs; the
   // remap gives each XCD a contiguous range of work ids, ordered (kv head,
-  // head part, query tile from the last, sequence): each XCD serves whole
-  // kv heads, and the query tiles of one (sequence, kv head), which read
-  // the same K/V, share its L2.
+  // head part, dispatch position): each XCD serves whole kv heads, whose
+  // items read the same K/V in its L2.
   const int nwg = (a.n_work + 7) & ~7;  // the grid: a multiple of 8
   const int bid = (int)__builtin_amdgcn_workgroup_id_x();
   const int wid = (bid & 7) * (nwg >> 3) + (bid >> 3);
   if (wid >= a.n_work) return;
-  int rest = wid;
-  const int qt_rev = rest % a.n_qtiles;
-  rest /= a.n_qtiles;
-  const int seq0 = rest % a.num_seqs;
-  rest /= a.num_seqs;
-  const int half = rest % HALVES;
-  const int kvh = rest / HALVES;
-  int qtile = a.n_qtiles - 1 - qt_rev;
-  int seq = seq0;
-  if (a.num_seqs * a.n_qtiles <= 64) {
-    // item j of this (kv head, head part) takes the j-th largest item: lane
-    // i of wave 0 holds item i = (sequence i / n_qtiles, query tile
-    // i % n_qtiles) and its key-tile count, ranked by (count descending,
-    // index ascending)
-    __shared__ int s_item;
-    if (threadIdx.x < 64) {
-      const int i = threadIdx.x;
-      const int n_items = a.num_seqs * a.n_qtiles;
-      int work = -1;  // past the items: ranked after every item
-      if (i < n_items) {
-        const int sq = i / a.n_qtiles;
-        const int qt = i - sq * a.n_qtiles;
-        const int e1 = min(a.query_start_loc[sq + 1], a.num_query_tokens);
-        const int e0 = max(0, min(a.query_start_loc[sq], e1));
-        const int ql = e1 - e0;
-        const int c = max(0, min(a.context_lens[sq], a.ctx_cap));
-        work = 0;
-        if (qt * QT < ql) {
-          const int tl = min(qt * QT + QT, ql) - 1;
-          const int ke = max(0, min(c, c - ql + tl + 1));
-          work = (ke + KT - 1) / KT + 1;  // key tiles, plus about one tile of fixed cost
-        }
-      }
-      int rank = 0;
-      for (int k = 0; k < 64; ++k) {
-        const int wk = __builtin_amdgcn_readlane(work, k);
-        rank += (wk > work || (wk == work && k < i)) ? 1 : 0;
-      }
-      const int j = seq0 * a.n_qtiles + qt_rev;
-      const unsigned long long hit = __builtin_amdgcn_ballot_w64(i < n_items && rank == j);
-      if (i == 0) s_item = hit ? (int)__builtin_ctzll(hit) : 0;
-    }
-    __syncthreads();
-    const int item = __builtin_amdgcn_readfirstlane(s_item);
-    seq = item / a.n_qtiles;
-    qtile = item - seq * a.n_qtiles;
+  const int n_items = a.num_seqs * a.n_qtiles;
+  const int pos = wid % n_items;
+  const int half = (wid / n_items) % HALVES;
+  const int kvh = wid / n_items / HALVES;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  int seq, qtile;
+  if (a.num_seqs <= 64 * kRankSeqChunks) {
+    if (!pick_item<QT>(a, pos, lane, seq, qtile)) return;
+  } else {
+    // plain order: each sequence's query tiles from the last
+    seq = pos / a.n_qtiles;
+    qtile = a.n_qtiles - 1 - pos % a.n_qtiles;
   }
 
   seq = __builtin_amdgcn_readfirstlane(seq);
+  qtile = __builtin_amdgcn_readfirstlane(qtile);
   int r1 = min(a.query_start_loc[seq + 1], a.num_query_tokens);
   int r0 = a.query_start_loc[seq];
   r0 = max(0, min(r0, r1));
@@ -356,8 +423,6 @@ __global__ void __launch_bounds__(kPrefillThreads, 1) prefill_chunk_kernel(const
   if (t_begin >= q_len) return;
   const int prefix = ctx - q_len;
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hs = wave % GWH;           // head slot of this wave
   const int tg = wave / GWH;
@@ -394,6 +459,7 @@ __global__ void __launch_bounds__(kPrefillThreads, 1) prefill_chunk_kernel(const
   const int t_last = min(t_begin + QT, q_len) - 1;
   int kend = max(0, min(ctx, prefix + t_last + 1));
   kend = __builtin_amdgcn_readfirstlane(kend);
+  const int ntiles = (kend + KT - 1) / KT;
 
   const int shift = a.block_shift;
   const int bs_mask = (1 << shift) - 1;
@@ -403,7 +469,7 @@ __global__ void __launch_bounds__(kPrefillThreads, 1) prefill_chunk_kernel(const
   const uint32_t vblock_bytes = (vslot_stride << shift) * 2u;
   const char *kbase = reinterpret_cast<const char *>(static_cast<const uint16_t *>(a.k_cache) + (size_t)kvh * D);
   const char *vbase = reinterpret_cast<const char *>(static_cast<const uint16_t *>(a.v_cache) + (size_t)kvh * DV);
-  const char *zero = reinterpret_cast<const char *>(&kZeroChunk);
+  const char *zero = reinterpret_cast<const char *>(&kZeroChunk[0]);
   const int32_t *bt = a.block_tables + (size_t)seq * a.max_blocks_per_seq;
   const int max_blocks = a.max_blocks_per_seq;
   const int num_blocks = a.num_blocks;
@@ -430,11 +496,16 @@ __global__ void __launch_bounds__(kPrefillThreads, 1) prefill_chunk_kernel(const
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
 
+  typedef __attribute__((address_space(3))) const char *lds_cptr;
+  const uint32_t sk_lds = (uint32_t)(size_t)((lds_cptr)(const char *)&lds[0]);
+  const uint32_t sv_lds = sk_lds + (uint32_t)kVBase;
+  auto ktile = [&](int j) { return reinterpret_cast<const uint16_t *>(&lds[(j % kKBufs) * kKTile]); };
+  auto vtile = [&](int j) { return reinterpret_cast<const uint16_t *>(&lds[kVBase + (j % kVBufs) * kVTile]); };
+
   // raw scores S^T for keys k0 .. k0+63 (s[0]: first 32 keys, s[1]: last 32)
   auto qk = [&](const uint16_t *skb, f32x16_t (&s)[2]) {
     // chunk 2 ds + hh of keys col and 32 + col: group ds / 2, slot
     // (2 (ds % 2) + hh) ^ ((col / 4) % 4)
-    typedef __attribute__((address_space(3))) const char *lds_cptr;
     typedef __attribute__((address_space(3))) const bf16x8_t *lds_frag_ptr;
     uint32_t ke = (uint32_t)(size_t)((lds_cptr)(const char *)skb + col * 64 + k_even);
     uint32_t ko = (uint32_t)(size_t)((lds_cptr)(const char *)skb + col * 64 + k_odd);
@@ -460,7 +531,6 @@ __global__ void __launch_bounds__(kPrefillThreads, 1) prefill_chunk_kernel(const
   // address space, constants last, so that they fold into the
   // instructions' offset fields)
   auto pv = [&](const uint16_t *svb, const bf16x8_t (&pb)[4]) {
-    typedef __attribute__((address_space(3))) const char *lds_cptr;
     typedef short v4s __attribute__((ext_vector_type(4)));
     typedef __attribute__((address_space(3))) v4s *lds_v4s_ptr;
     // the two per-lane bases pass through an empty asm statement: opaque
@@ -540,70 +610,54 @@ __global__ void __launch_bounds__(kPrefillThreads, 1) prefill_chunk_kernel(const
     return d;
   };
 
-  const int ntiles = (kend + KT - 1) / KT;
   // leading tiles every query of this wave sees whole: no mask, no max
   const int n_plain = min(ntiles, max(0, (qpos_lo + 1) / KT));
 
-  // loads of tile j (its ids read beforehand) into buffer j % kBufs
-  typedef __attribute__((address_space(3))) const char *lds_cptr;
-  const uint32_t sk_lds = (uint32_t)(size_t)((lds_cptr)(const char *)&sk[0][0]);
-  const uint32_t sv_lds = (uint32_t)(size_t)((lds_cptr)(const char *)&sv[0][0]);
-  auto gather = [&](int j, const typename GK::Ids &ik, const typename GV::Ids &iv) {
+  // loads of tile j, K into buffer j % kKBufs and V into buffer j % kVBufs
+  auto gather_k = [&](int j, const TileIds &ids) {
     const int k0 = j * KT;
-    const uint32_t b = (uint32_t)(j % kBufs);
-    const uint32_t dk = sk_lds + b * (KT * D * 2), dv = sv_lds + b * (KT * DV * 2);
-    if (k0 + KT <= kend) {
-      gk.issue(kBs8, false, dk, ik, kbase, zero, num_blocks, block_bytes, k0, kend, lane);
-      gv.issue(kBs8, false, dv, iv, vbase, zero, num_blocks, vblock_bytes, k0, kend, lane);
-    } else {
-      gk.issue(kBs8, true, dk, ik, kbase, zero, num_blocks, block_bytes, k0, kend, lane);
-      gv.issue(kBs8, true, dv, iv, vbase, zero, num_blocks, vblock_bytes, k0, kend, lane);
-    }
+    const uint32_t dk = sk_lds + (uint32_t)((j % kKBufs) * kKTile);
+    if (k0 + KT <= kend)
+      gk.issue(kBs8, false, dk, ids, kbase, zero, num_blocks, block_bytes, k0, kend, lane);
+    else
+      gk.issue(kBs8, true, dk, ids, kbase, zero, num_blocks, block_bytes, k0, kend, lane);
   };
-  // block ids of the V loads: with equal head dims a wave's V loads cover
-  // the keys of its K loads, so the ids are the same
-  auto same_ids = [&](const typename GK::Ids &k_ids, const GV &g, bool bs8, const int32_t *row, int k0, int sh,
-                      int mb) {
-    if constexpr (D == DV) {
-      (void)g, (void)bs8, (void)row, (void)k0, (void)sh, (void)mb;
-      return k_ids;
-    } else {
-      return g.ids(bs8, row, k0, sh, mb);
-    }
+  auto gather_v = [&](int j, const TileIds &ids) {
+    const int k0 = j * KT;
+    const uint32_t dv = sv_lds + (uint32_t)((j % kVBufs) * kVTile);
+    if (k0 + KT <= kend)
+      gv.issue(kBs8, false, dv, ids, vbase, zero, num_blocks, vblock_bytes, k0, kend, lane);
+    else
+      gv.issue(kBs8, true, dv, ids, vbase, zero, num_blocks, vblock_bytes, k0, kend, lane);
   };
-  // tile loads a wave issues per step (the only vector memory operations
-  // inside the loop)
-  constexpr int kStepLoads = GK::PER_WAVE + GV::PER_WAVE;
+  // K and V rows of one key share the block, and a wave's K and V loads
+  // cover the same 16 keys, so one read of block ids serves both
+  auto tile_ids = [&](int j) { return gk.ids(kBs8, bt, j * KT, shift, max_blocks); };
 
   // Pipeline, one barrier per step t:
-  //   loads of tile t+3 issued;  S(t+1) = K(t+1) Q^T;  weights of S(t);
-  //   O += V(t) P(t);  block ids of tile t+4 read;  wait for this wave's
-  //   loads of tile t+2 (issued in step t-1; those of tile t+3 stay in
-  //   flight);  barrier.
-  typename GK::Ids ik = gk.ids(kBs8, bt, 0, shift, max_blocks);
-  typename GV::Ids iv = same_ids(ik, gv, kBs8, bt, 0, shift, max_blocks);
-  gather(0, ik, iv);
-  ik = gk.ids(kBs8, bt, KT, shift, max_blocks);
-  iv = same_ids(ik, gv, kBs8, bt, KT, shift, max_blocks);
-  gather(1, ik, iv);
-  ik = gk.ids(kBs8, bt, 2 * KT, shift, max_blocks);
-  iv = same_ids(ik, gv, kBs8, bt, 2 * KT, shift, max_blocks);
-  gather(2, ik, iv);
-  ik = gk.ids(kBs8, bt, 3 * KT, shift, max_blocks);
-  iv = same_ids(ik, gv, kBs8, bt, 3 * KT, shift, max_blocks);
+  //   loads of K(t+2) and V(t+1) issued;  S(t+1) = K(t+1) Q^T;  weights of
+  //   S(t);  O += V(t) P(t);  block ids of tile t+3 read;  wait for this
+  //   wave's loads;  barrier.
+  // ids1 holds the block ids of tile t+1, ids2 those of tile t+2.
+  TileIds ids1 = tile_ids(0);
+  gather_k(0, ids1);
+  gather_v(0, ids1);
+  ids1 = tile_ids(1);
+  gather_k(1, ids1);
+  TileIds ids2 = tile_ids(2);
   wait_vmcnt<0>();
   __syncthreads();
 
   f32x16_t sa[2], sb[2];  // scores of two consecutive tiles (ping-pong)
-  qk(sk[0], sa);
+  qk(ktile(0), sa);
 
-  // one step on tile j whose scores are in cur; the next tile's go to nxt.
-  // kFull: causal mask where the tile crosses the diagonal, and the tile's
-  // max (first tile, diagonal tiles); otherwise no mask and no max, with
-  // the sum check.
+  // one step on tile j whose scores are in cur; the next tile's go to nxt.  kFull: causal mask where the tile crosses the diagonal, and
+  // the tile's max (first tile, diagonal tiles); otherwise no mask and no
+  // max, with the sum check.
   auto step = [&](bool kFull, int j, f32x16_t (&cur)[2], f32x16_t (&nxt)[2]) __attribute__((always_inline)) {
     const int k0 = j * KT;
-    gather(j + 3, ik, iv);
+    gather_k(j + 2, ids2);
+    gather_v(j + 1, ids1);
     if (kFull) {
       // exponents relative to the reference; causal mask on tiles that
       // cross this wave's diagonal (register r of this lane holds key
@@ -627,14 +681,14 @@ __global__ void __launch_bounds__(kPrefillThreads, 1) prefill_chunk_kernel(const
     // last tile the buffer holds zero rows and the result is not used) are
     // interleaved with the exponentials, so the matrix and vector units
     // work at the same time.
-    qk(sk[(j + 1) % kBufs], nxt);
+    qk(ktile(j + 1), nxt);
     bf16x8_t pb[4];
     float ps = weights(cur, pb, !kFull);
     if (!kFull) {
       if (__builtin_amdgcn_ballot_w64(ps > kSumLimit)) {
         // a score far above the reference: redo this tile's scores and
         // move the reference (the tile is still in LDS)
-        qk(sk[j % kBufs], cur);
+        qk(ktile(j), cur);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           cur[0][r] = fmaf(cur[0][r], sl, nm);
@@ -650,10 +704,10 @@ __global__ void __launch_bounds__(kPrefillThreads, 1) prefill_chunk_kernel(const
       }
     }
     l += ps;
-    pv(sv[j % kBufs], pb);
-    ik = gk.ids(kBs8, bt, k0 + 4 * KT, shift, max_blocks);
-    iv = same_ids(ik, gv, kBs8, bt, k0 + 4 * KT, shift, max_blocks);
-    wait_vmcnt<kStepLoads>();  // this wave's loads of tile j+2 are in LDS
+    pv(vtile(j), pb);
+    ids1 = ids2;
+    ids2 = tile_ids(j + 3);
+    wait_vmcnt<0>();  // this wave's loads of K(j+2) and V(j+1) are in LDS
     __syncthreads();
   };
 
