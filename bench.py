@@ -42,6 +42,7 @@ sys.path.insert(0, ROOT)
 METRIC = "paged decode tokens/s + achieved KV GB/s (% HBM peak), bs32 ctx4K GQA 32/8 bf16"
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
 BF16_DENSE_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+PEAK_CLOCK_GHZ = 2.4  # the engine clock the published MFMA peak is quoted at
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 
 
@@ -524,6 +525,35 @@ def bench_serving(seed=7000, num_requests=96, num_blocks=12000, mixed=False):
     return res
 
 
+def measure_clock(fn=None, launches=30, ticks=200_000):
+    """Shader clock in GHz over `ticks` ticks of the GPU's 100 MHz reference
+    counter, from the library's clock probe (one wave).  With `fn`, the probe
+    runs on a second stream (default priority) while `launches` back-to-back
+    calls of fn run on the current one, starting after the second call has
+    finished, so it sees the clock those kernels run at; without, the clock
+    of an otherwise idle device.  None if the counters disagree with any
+    plausible clock."""
+    import torch
+    import paged_attention_kv_cache_amd as P
+    out = torch.zeros(3, dtype=torch.int64, device="cuda")
+    torch.cuda.synchronize()
+    if fn is None:
+        P.pa_clock_probe(out, ticks)
+    else:
+        side = torch.cuda.Stream()
+        ev = torch.cuda.Event()
+        for i in range(launches):
+            fn()
+            if i == 1:
+                ev.record()
+                side.wait_event(ev)
+                P.pa_clock_probe(out, ticks, stream=side)
+    torch.cuda.synchronize()
+    cycles, tk, steps = (int(x) for x in out.cpu().tolist())
+    ghz = cycles / tk * 0.1 if tk > 0 else 0.0
+    return {"ghz": round(ghz, 4) if 0.1 < ghz < 4.0 else None, "cycles": cycles, "ref_ticks": tk, "sleep_steps": steps}
+
+
 def bench_prefill(args, block_size=32):
     import torch
     import paged_attention_kv_cache_amd as P
@@ -573,9 +603,12 @@ def bench_prefill(args, block_size=32):
         pairs += ql * prefix + ql * (ql + 1) // 2
     flops = 4.0 * D * pairs * H
     tflops = flops / (t_ms * 1e-3) / 1e12
+    # the matrix unit's peak scales with the clock, which drops under this load
+    clk = measure_clock(run)
+    at_clock = (tflops / (BF16_DENSE_PEAK_TFLOPS * clk["ghz"] / PEAK_CLOCK_GHZ)) if clk["ghz"] else None
     return dict(us=t_ms * 1e3, tflops=tflops, frac=tflops / BF16_DENSE_PEAK_TFLOPS, flops=flops, stats=stats_ms(each),
-                tokens_per_s=int(case.query_start_loc[-1]) / (t_ms * 1e-3),
-                src=source_hash("pa_prefill.hip", "pa_common.h"))
+                tokens_per_s=int(case.query_start_loc[-1]) / (t_ms * 1e-3), clock=clk,
+                frac_at_measured_clock=at_clock, src=source_hash("pa_prefill.hip", "pa_common.h"))
 
 
 def host_info():
@@ -777,6 +810,7 @@ def main():
         dst.copy_(src)          # 1 GiB read + 1 GiB written
         torch.cuda.synchronize()
         del src, dst
+    clock_idle_before = measure_clock()
     dec = bench_decode(args)
     ceiling = bench_stream_ceiling()
     # the same read at the partition kernel's own byte count (launch ramp
@@ -858,6 +892,8 @@ def main():
                          "unit": "TFLOP/s", "frac": round(pre["frac"], 4),
                          "traffic": traffic_from_profiles("prefill_chunk", pre["src"]),
                          "algorithmic_flops_per_launch": pre["flops"]},
+            "clock_during_launches": pre["clock"],
+            "mfma_frac_at_measured_clock": round(pre["frac_at_measured_clock"], 4) if pre["frac_at_measured_clock"] else None,
         }
     if not args.quick and pre is not None:
         line["prefill_other_block_sizes"] = []
@@ -891,6 +927,7 @@ def main():
         log("timing the CPU oracle (decode, prefill and long-context legs, median of 3 each)")
         pre_case = None if args.no_prefill else W.chunked_prefill(poison=False)
         line["cpu_baseline"] = cpu_baseline(case, pre_case, long_case, args.cpu_seconds)
+    line["clock_idle_ghz"] = {"before": clock_idle_before["ghz"], "after": measure_clock()["ghz"]}
     print(json.dumps(line), flush=True)
 
 

@@ -46,6 +46,7 @@ from ._binding import (  # noqa: F401
     pa_prefill_chunk,
     pa_status_string,
     pa_stream_read,
+    pa_clock_probe,
     pa_version,
 )
 from .kv_manager import (KIND_DECODE, KIND_IDLE, KIND_MIXED, KIND_PROMPT, KvManager, Step, StepScheduler,  # noqa: F401

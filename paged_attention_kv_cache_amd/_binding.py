@@ -104,6 +104,7 @@ SIGNATURES = {
     "pa_last_error_message": (ctypes.c_char_p, []),
     "pa_version": (ctypes.c_int, []),
     "pa_stream_read": (ctypes.c_int, [_vp, _sz, _vp, _vp]),
+    "pa_clock_probe": (ctypes.c_int, [_vp, _i64, _vp]),
     # host KV manager and step scheduler
     "pa_kvm_create": (_vp, [_i32, _i32, _i32]),
     "pa_kvm_destroy": (None, [_vp]),
@@ -258,6 +259,17 @@ def pa_stream_read(buf, sink, stream=None) -> None:
         raise ValueError("sink must hold at least 4 bytes")
     code = load_library().pa_stream_read(_dev(buf, "buf"), nbytes, _dev(sink, "sink"), _stream(stream))
     _check("pa_stream_read", code)
+
+
+def pa_clock_probe(out, ticks: int, stream=None) -> None:
+    """Enqueue the shader-clock probe of ``include/pagedattn_bench.h``:
+    ``out`` is a GPU int64 tensor of at least 3 elements that receives
+    (shader cycles, 100 MHz reference ticks, sleep steps) over ``ticks``
+    reference ticks."""
+    if out.numel() * out.element_size() < 24:
+        raise ValueError("out must hold at least 3 x 8 bytes")
+    code = load_library().pa_clock_probe(_dev(out, "out"), int(ticks), _stream(stream))
+    _check("pa_clock_probe", code)
 
 
 def pa_kv_cache_write(key, value, k_cache, v_cache, slot_mapping, stream=None) -> None:

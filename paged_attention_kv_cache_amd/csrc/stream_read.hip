@@ -1,3 +1,5 @@
+// Measurement helpers: the HBM read ceiling, and the shader clock.
+//
 // HBM read ceiling: a kernel that only streams a buffer in.
 //
 // Decode is bound by how fast HBM delivers the K/V bytes.  The nominal
@@ -33,6 +35,32 @@ __global__ void __launch_bounds__(256) stream_read_kernel(const u32x4_sr *__rest
   if (acc == 0x9e3779b9u) sink[0] = acc;
 }
 
+// Shader clock: one wave reads the shader-cycle counter (s_memtime) and the
+// constant 100 MHz reference counter (s_memrealtime) at its start, sleeps
+// in short steps until `ticks` reference ticks have passed (or max_iter
+// steps, whichever comes first, so the loop ends even if a counter stood
+// still), reads both again and stores the two differences and the step
+// count.  Cycles over ticks times 100 MHz is the clock the CU ran at over
+// that interval; run beside other kernels, it is their clock.
+__global__ void __launch_bounds__(64) clock_probe_kernel(unsigned long long *__restrict__ out, long long ticks,
+                                                        int max_iter) {
+  const unsigned long long c0 = __builtin_amdgcn_s_memtime();
+  const unsigned long long r0 = __builtin_amdgcn_s_memrealtime();
+  unsigned long long r1 = r0;
+  int i = 0;
+  for (; i < max_iter; ++i) {
+    r1 = __builtin_amdgcn_s_memrealtime();
+    if ((long long)(r1 - r0) >= ticks) break;
+    __builtin_amdgcn_s_sleep(2);
+  }
+  const unsigned long long c1 = __builtin_amdgcn_s_memtime();
+  if (threadIdx.x == 0) {
+    out[0] = c1 - c0;
+    out[1] = r1 - r0;
+    out[2] = (unsigned long long)i;
+  }
+}
+
 }  // namespace pa
 
 extern "C" int pa_stream_read(const void *buf, size_t bytes, void *sink, void *stream) {
@@ -48,5 +76,21 @@ extern "C" int pa_stream_read(const void *buf, size_t bytes, void *sink, void *s
                      static_cast<const pa::u32x4_sr *>(buf), bytes / 16, static_cast<uint32_t *>(sink));
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return pa::set_error(PA_ERR_HIP, "stream_read launch: HIP error %d (%s)", (int)e, hipGetErrorString(e));
+  return pa::clear_error();
+}
+
+extern "C" int pa_clock_probe(void *out, int64_t ticks, void *stream) {
+  if (!out) return pa::set_error(PA_ERR_NULL, "out=%p: must be a device pointer to 3 x 8 bytes", out);
+  if (ticks < 1 || ticks > PA_CLOCK_PROBE_MAX_TICKS)
+    return pa::set_error(PA_ERR_SHAPE, "ticks %lld outside [1, %lld]", (long long)ticks,
+                         (long long)PA_CLOCK_PROBE_MAX_TICKS);
+  // a sleep step takes at least 128 shader cycles, more than one reference
+  // tick at any clock below 12.8 GHz, so while the counters advance the
+  // step limit is never what ends the loop
+  const int max_iter = (int)(ticks * 16 + 1024);
+  hipLaunchKernelGGL(pa::clock_probe_kernel, dim3(1), dim3(64), 0, (hipStream_t)stream,
+                     static_cast<unsigned long long *>(out), (long long)ticks, max_iter);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return pa::set_error(PA_ERR_HIP, "clock_probe launch: HIP error %d (%s)", (int)e, hipGetErrorString(e));
   return pa::clear_error();
 }

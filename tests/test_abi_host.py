@@ -253,6 +253,18 @@ def test_copy_blocks_validation(lib):
     assert cp(a, cache(k=0)) == -1
 
 
+def test_measurement_helpers_validation(lib):
+    """The stream-read and clock probes reject their arguments before any
+    launch."""
+    assert lib.pa_stream_read(None, 16, FAKE, None) == -1
+    assert lib.pa_stream_read(FAKE, 16, None, None) == -1
+    assert lib.pa_stream_read(FAKE, 20, FAKE, None) == -3 and "multiple of 16" in msg()
+    assert lib.pa_stream_read(FAKE, 0, FAKE, None) == 0  # nothing to read
+    assert lib.pa_clock_probe(None, 1000, None) == -1
+    assert lib.pa_clock_probe(FAKE, 0, None) == -3 and "ticks 0 outside" in msg()
+    assert lib.pa_clock_probe(FAKE, 1000001, None) == -3
+
+
 def test_value_head_dim_validation(lib):
     """A value head dim of its own (0 = the key head dim): attention takes
     64 or 128, the workspace is sized by it (cascade decode's too), and the

@@ -45,8 +45,9 @@ def test_mixed_step_full_size():
     """One full-size mixed step as the mixed scheduler policy issues it: 64
     decode rows (one token each, contexts U[128, 4096]) and prompt chunks
     (seven of 512 tokens and one of 448 over prefixes U[0, 2048]) in a single
-    4096-token prefill launch: 72 sequences, 576 (sequence, query tile)
-    items per kv head, the plain dispatch order."""
+    4096-token prefill launch: 72 sequences (two lanes' worth of sequences
+    in the work-groups' cost ranking), 1,152 (sequence, 32-query tile) items
+    per kv head."""
     rng = np.random.default_rng(4242)
     dec_ctx = rng.integers(128, 4097, size=64)
     pro_prefix = rng.integers(0, 2049, size=8)
@@ -274,3 +275,23 @@ def test_prefill_random_shapes(seed):
     ref = oracle_prefill(case)
     assert ref.shape == (sum(qlens), hkv * G, Dv)
     assert_close(got, ref, dtype, what)
+
+
+@pytest.mark.parametrize("num_seqs", [130, 256, 257, 300])
+def test_prefill_many_sequences(num_seqs):
+    """Batches of more sequences than a wave has lanes: up to 256 sequences
+    the work-groups rank the items by cost over several sequences per lane
+    (130: three, 256: four), past 256 they take the plain order.  Short
+    chunks (0 to 40 tokens, some of one) over prefixes of 0 to 300 tokens,
+    every sequence's output against the oracle."""
+    rng = np.random.default_rng(9100 + num_seqs)
+    prefixes = rng.integers(0, 301, size=num_seqs).tolist()
+    qlens = rng.integers(0, 41, size=num_seqs).tolist()
+    for i in rng.choice(num_seqs, size=8, replace=False):
+        qlens[int(i)] = int(rng.choice([0, 1, 32, 33]))
+    case = W.random_prefill(9200 + num_seqs, prefixes, qlens, num_heads=8, num_kv_heads=2, head_dim=64,
+                            block_size=16, dtype=W.BF16)
+    what = f"{num_seqs} sequences, {sum(qlens)} query rows"
+    log(what)
+    _, got = _run(case)
+    assert_close(got, oracle_prefill(case), W.BF16, what)
