@@ -287,21 +287,24 @@ constexpr int kRankSeqChunks = 4;
 
 // Dispatch order by size.  The items of one (kv head, head part) are the
 // pairs (sequence s, query tile qt) with qt * QT < q_len(s); an item reads
-// tiles = ceil(keys / 64) key tiles, keys = min(context, prefix + QT (qt +
-// 1)), and costs about tiles + 1 (its fixed work).  The cost does not
-// decrease with qt, so the number of items of s that cost more than W has a
-// closed form: every qt from (64 (W - 1) - prefix) / QT on, if the context
-// has more than 64 (W - 1) keys.  The work-group at dispatch
-// position pos takes the pos-th costliest item (ties in (s, qt) order): a
-// binary search over W for the cost of that item, each probe summing the
-// per-sequence counts over the wave (lane = sequence, up to 4 per lane),
-// then the rank among the items of that cost.  Returns false for a position
-// past the last item.  Every wave computes the same result from the same
-// values.
+// keys = min(context, prefix + QT (qt + 1)) keys.  Its cost class is
+// ceil(keys / U) with U = 512 keys (8 key tiles): coarse enough that the
+// items of one sequence, which read the same K/V, mostly share a class and
+// are dispatched together (their tiles then come into the XCD's L2 about
+// once), fine enough to keep the longest first.  The class does not
+// decrease with qt, so the number of items of s whose class is at least W
+// has a closed form: every qt from (U (W - 1) - prefix) / QT on, if the
+// context has more than U (W - 1) keys.  The work-group at dispatch
+// position pos takes the pos-th item in (class descending, s ascending, qt
+// descending) order: a binary search over W for the class of that item,
+// each probe summing the per-sequence counts over the wave (lane =
+// sequence, up to 4 per lane), then its rank among the items of that
+// class.  Returns false for a position past the last item.  Every wave
+// computes the same result from the same values.
 template <int QT>
 __device__ __forceinline__ bool pick_item(const PrefillKernelArgs &a, int pos, int lane, int &seq_out,
                                           int &qt_out) {
-  constexpr int U = KT;  // keys per step of an item
+  constexpr int U = 8 * KT;  // keys per cost class
   const int nchunks = (a.num_seqs + 63) / 64;
   int nq[kRankSeqChunks], cx[kRankSeqChunks], pf[kRankSeqChunks];
 #pragma unroll
@@ -319,7 +322,7 @@ __device__ __forceinline__ bool pick_item(const PrefillKernelArgs &a, int pos, i
       nq[c] = min((ql + QT - 1) / QT, a.n_qtiles);
     }
   }
-  // items of lane's sequences that cost more than W
+  // items of lane's sequences whose class is at least W (all for W <= 0)
   auto above = [&](int W, int c) -> int {
     if (W <= 0) return nq[c];
     const int kth = U * (W - 1);
@@ -335,7 +338,7 @@ __device__ __forceinline__ bool pick_item(const PrefillKernelArgs &a, int pos, i
     return wave_sum_bits(x, bits);
   };
   if (pos >= count_above(0)) return false;
-  // smallest W with count_above(W) <= pos: the cost of the pos-th item
+  // smallest W with count_above(W) <= pos: the pos-th item is of class W - 1
   int lo = 1, hi = (a.ctx_cap + U - 1) / U + 1;
   while (lo < hi) {
     const int mid = (lo + hi) >> 1;
@@ -344,19 +347,19 @@ __device__ __forceinline__ bool pick_item(const PrefillKernelArgs &a, int pos, i
     else
       lo = mid + 1;
   }
-  int r = pos - count_above(lo);  // rank among the items that cost exactly lo
+  int r = pos - count_above(lo);  // rank among the items of class lo - 1
   const int nbits = 33 - __builtin_clz((unsigned)a.n_qtiles);
 #pragma unroll
   for (int c = 0; c < kRankSeqChunks; ++c) {
     if (c < nchunks) {
-      const int hi_c = above(lo - 1, c);
-      const int e = hi_c - above(lo, c);  // this lane's items of cost lo: qt in [nq - hi_c, nq - hi_c + e)
+      const int lo_c = above(lo, c);
+      const int e = above(lo - 1, c) - lo_c;  // this lane's items of class lo - 1: qt in [nq - lo_c - e, nq - lo_c)
       const int pre = wave_prefix_bits(e, nbits);
       const int tot = wave_sum_bits(e, nbits);
       if (r < tot) {
         const unsigned long long hit = __builtin_amdgcn_ballot_w64(e > 0 && pre <= r && r < pre + e);
         const int l = (int)__builtin_ctzll(hit);
-        const int qt = nq[c] - hi_c + (r - pre);
+        const int qt = nq[c] - lo_c - 1 - (r - pre);  // the longest first
         seq_out = c * 64 + l;
         qt_out = __builtin_amdgcn_readlane(qt, l);
         return true;
