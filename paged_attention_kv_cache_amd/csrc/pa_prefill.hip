@@ -323,12 +323,13 @@ __device__ __forceinline__ bool pick_item(const PrefillKernelArgs &a, int pos, i
     }
   }
   // items of lane's sequences whose class is at least W (all for W <= 0)
+  // (64-bit key counts: a context bound near 2^31 keys must not wrap)
   auto above = [&](int W, int c) -> int {
     if (W <= 0) return nq[c];
-    const int kth = U * (W - 1);
+    const long long kth = (long long)U * (W - 1);
     if (cx[c] <= kth) return 0;
-    const int d = kth - pf[c];
-    return max(0, nq[c] - (d > 0 ? d / QT : 0));
+    const long long d = kth - pf[c];
+    return max(0, nq[c] - (d > 0 ? (int)(d / QT) : 0));
   };
   const int bits = 34 - __builtin_clz((unsigned)a.n_qtiles);  // 4 chunks of counts < 2 n_qtiles + 1
   auto count_above = [&](int W) -> int {
@@ -339,7 +340,7 @@ __device__ __forceinline__ bool pick_item(const PrefillKernelArgs &a, int pos, i
   };
   if (pos >= count_above(0)) return false;
   // smallest W with count_above(W) <= pos: the pos-th item is of class W - 1
-  int lo = 1, hi = (a.ctx_cap + U - 1) / U + 1;
+  int lo = 1, hi = a.ctx_cap / U + 2;  // every item's class is at most ctx_cap / U + 1
   while (lo < hi) {
     const int mid = (lo + hi) >> 1;
     if (count_above(mid) <= pos)
