@@ -414,8 +414,9 @@ def bench_decode_secondary(name, ps, steps=30, groups=None, case=None, cascade_p
 
 def bench_serving(seed=7000, num_requests=96, num_blocks=12000, mixed=False):
     """The scheduler driving the kernels over a request trace: every step the
-    host plans (pa_sched_next_step), copies the step's tables through pinned
-    buffers, and launches kv_cache_write plus prefill or decode; the step is
+    host plans (pa_sched_next_step), copies the step's tables through a
+    pinned buffer (one copy), and launches kv_cache_write plus prefill or
+    decode; the step is
     then committed with 'sampled' tokens.  K/V/Q values are random device
     data (they do not change the work).  Reports prompt + generated tokens
     per second of wall time, and the share of it the GPU was busy.  With
@@ -445,15 +446,26 @@ def bench_serving(seed=7000, num_requests=96, num_blocks=12000, mixed=False):
     src_v = torch.randn_like(src_k)
     src_q = torch.randn((cap_tokens, Hq, D), device="cuda").to(torch.bfloat16)
     out = torch.empty_like(src_q)
-    # two sets of pinned staging buffers: the host fills one while the
-    # other's copies may still wait in the stream behind earlier kernels;
-    # a set is refilled only after the event recorded behind its copies
-    pins = [dict(qsl=torch.zeros(cap_seqs + 1, dtype=torch.int32).pin_memory(),
-                 ctx=torch.zeros(cap_seqs, dtype=torch.int32).pin_memory(),
-                 tab=torch.zeros((cap_seqs, cap_blocks), dtype=torch.int32).pin_memory(),
-                 slots=torch.zeros(cap_tokens, dtype=torch.int64).pin_memory()) for _ in range(2)]
+    # the step's host arrays travel in one pinned buffer and one copy:
+    # int32 words [query_start_loc | context_lens | block tables | slot
+    # mapping (int64, 8-byte aligned)]; two such buffers, the host filling
+    # one while the other's copy may still wait in the stream behind earlier
+    # kernels, a buffer refilled only after the event recorded behind its copy
+    o_ctx = cap_seqs + 1
+    o_tab = o_ctx + cap_seqs
+    o_slots = (o_tab + cap_seqs * cap_blocks + 1) // 2 * 2
+    words = o_slots + 2 * cap_tokens
+
+    def views(buf):
+        return dict(qsl=buf[:o_ctx], ctx=buf[o_ctx:o_tab],
+                    tab=buf[o_tab:o_tab + cap_seqs * cap_blocks].view(cap_seqs, cap_blocks),
+                    slots=buf[o_slots:words].view(torch.int64))
+
+    pin_bufs = [torch.zeros(words, dtype=torch.int32).pin_memory() for _ in range(2)]
+    pins = [views(b) for b in pin_bufs]
     copied = [None, None]
-    dev = {k: torch.empty_like(v, device="cuda") for k, v in pins[0].items()}
+    dev_buf = torch.empty(words, dtype=torch.int32, device="cuda")
+    dev = views(dev_buf)
     ws = torch.zeros(P.pa_decode_workspace_bytes(cap_seqs, Hq, D, cap_blocks * bs, 256), dtype=torch.uint8,
                      device="cuda")
     scale = 1.0 / math.sqrt(D)
@@ -475,8 +487,7 @@ def bench_serving(seed=7000, num_requests=96, num_blocks=12000, mixed=False):
         pin["ctx"][:n].numpy()[:] = st.context_lens
         pin["tab"][:n].numpy()[:] = st.block_tables
         pin["slots"][:T].numpy()[:] = st.slot_mapping
-        for k in pin:
-            dev[k].copy_(pin[k], non_blocking=True)
+        dev_buf.copy_(pin_bufs[b], non_blocking=True)
         copied[b] = torch.cuda.Event()
         copied[b].record()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -488,9 +499,8 @@ def bench_serving(seed=7000, num_requests=96, num_blocks=12000, mixed=False):
             # a mixed step's decode rows come first, one token each
             nd = 0
             if st.kind == P.KIND_MIXED:
-                qlen = np.diff(st.query_start_loc)
-                while nd < n and qlen[nd] == 1:
-                    nd += 1
+                longer = np.flatnonzero(np.diff(st.query_start_loc) != 1)
+                nd = int(longer[0]) if longer.size else n
             prompt_tokens += T - nd
             decode_tokens += nd
         else:
@@ -499,7 +509,7 @@ def bench_serving(seed=7000, num_requests=96, num_blocks=12000, mixed=False):
             decode_tokens += T
         e1.record()
         busy.append((e0, e1))
-        sched.complete_step(rng.integers(1, 32000, n).tolist())
+        sched.complete_step(rng.integers(1, 32000, n, dtype=np.int32))
         steps += 1
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
