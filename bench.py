@@ -55,7 +55,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--partition", type=int, default=192, help="split-K partition of the bs32 step (tokens)")
+    ap.add_argument("--partition", type=int, default=320, help="split-K partition of the bs32 step (tokens)")
     ap.add_argument("--rotate-gb", type=float, default=2.0, help="total size of rotated KV pools")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
@@ -83,16 +83,17 @@ def source_hash(*names) -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_from_profiles(kernel_key: str, src_hash: str):
+def traffic_from_profiles(kernel_key: str, src_hash: str, partition_size=None):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they were
-    taken on the current kernel source; else None."""
+    taken on the current kernel source (and, for decode, at the same split-K
+    partition, which sets the bytes of partials written); else None."""
     path = os.path.join(PROFILE_DIR, "traffic.json")
     if not os.path.exists(path):
         return None
     try:
         data = json.load(open(path))
         rec = data.get(kernel_key)
-        if rec and rec.get("source_hash") == src_hash:
+        if rec and rec.get("source_hash") == src_hash and rec.get("partition_size") == partition_size:
             return rec.get("hbm_bytes_per_launch")
     except (OSError, ValueError):
         return None
@@ -691,7 +692,7 @@ def run_only(args):
     elif name == "decode_batch_bs32_ctx4096":
         r = bench_decode_secondary(name, 1024, case=W.decode_batch(2000, poison=False, fixed_ctx=4096))
     elif name == "decode_batch_bs32_64q_8kv":
-        r = bench_decode_secondary(name, 192, case=W.decode_batch(2000, poison=False, num_heads=64))
+        r = bench_decode_secondary(name, 320, case=W.decode_batch(2000, poison=False, num_heads=64))
     elif name == "decode_batch_bs32_k128_v64":
         r = bench_decode_secondary(name, 192, case=W.decode_batch(2000, poison=False, v_head_dim=64))
     else:
@@ -831,7 +832,7 @@ def main():
     pre = None if args.no_prefill else bench_prefill(args)
     case = dec["case"]
     tokens_per_s = dec["S"] / (dec["ms_step"] * 1e-3)
-    traffic = traffic_from_profiles("decode_partition", dec["src"])
+    traffic = traffic_from_profiles("decode_partition", dec["src"], dec["ps"])
     step_gbps = dec["kv_bytes"] / (dec["ms_step"] * 1e-3) / 1e9
     line = {
         "metric": METRIC,
@@ -921,7 +922,7 @@ def main():
             bench_decode_secondary("decode_batch_bs32_ctx4096", 1024,
                                    case=W.decode_batch(2000, poison=False, fixed_ctx=4096)),
             # eight query heads per kv head: 64 q over the same 8 kv heads and K/V bytes
-            bench_decode_secondary("decode_batch_bs32_64q_8kv", 192,
+            bench_decode_secondary("decode_batch_bs32_64q_8kv", 320,
                                    case=W.decode_batch(2000, poison=False, num_heads=64)),
             # a value head dim of its own: 128-wide keys, 64-wide values
             bench_decode_secondary("decode_batch_bs32_k128_v64", 192,

@@ -12,7 +12,8 @@ from gpu_util import (DeviceCase, assert_close, log, oracle_decode, to_dev, to_h
 
 pytestmark = pytest.mark.gpu
 
-BENCH_PARTITION = 192     # the split-K partition the benchmark times for the bs32 batch
+BENCH_PARTITION = 320     # the split-K partition the benchmark times for the bs32 batch (and its G = 8 form)
+BENCH_PARTITION_V64 = 192  # ... and for its 64-wide-value form
 
 
 def _run(case, partition_size, max_context_len=None):
@@ -101,7 +102,7 @@ def test_decode_separate_value_dim(dtype, dims, group):
             assert_close(got, ref, dtype, f"{dtype} D{D} Dv{Dv} G{group} bs{bs} ps{ps}")
 
 
-@pytest.mark.parametrize("ps", [0, 256, 512, BENCH_PARTITION])
+@pytest.mark.parametrize("ps", [0, 192, 256, 512, BENCH_PARTITION])
 def test_decode_batch_bs32_full(ps):
     case = W.make_config("decode_batch_bs32")
     ref = oracle_decode(case)
@@ -115,7 +116,7 @@ def test_decode_batch_bs32_eight_heads_per_kv_head_full():
     """The bs32 batch with 64 query heads over its 8 kv heads (G = 8)."""
     case = W.decode_batch(2000, num_heads=64)
     ref = oracle_decode(case)
-    for ps in (192, 512):
+    for ps in (BENCH_PARTITION, 512):
         log(f"decode batch 32 x U[512,4096], 64 q / 8 kv heads, partition={ps}")
         _, got = _run(case, ps)
         mx, mean = assert_close(got, ref, W.BF16, f"bs32 batch G8 ps{ps}")
@@ -142,7 +143,7 @@ def test_decode_batch_bs32_k128_v64_full():
     benchmark's partition."""
     case = W.decode_batch(2000, v_head_dim=64)
     ref = oracle_decode(case)
-    for ps in (BENCH_PARTITION, 512):
+    for ps in (BENCH_PARTITION_V64, 512):
         log(f"decode batch 32 x U[512,4096], key dim 128, value dim 64, partition={ps}")
         _, got = _run(case, ps)
         mx, mean = assert_close(got, ref, W.BF16, f"bs32 k128 v64 ps{ps}")
