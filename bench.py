@@ -697,7 +697,7 @@ def run_only(args):
         r = bench_decode_secondary(name, 192, case=W.decode_batch(2000, poison=False, v_head_dim=64))
     else:
         bs = 16 if name.endswith("16") else 8
-        r = bench_decode_secondary(name, 512, groups=([0, 16, 32, 48, 64], [64 * bs] * 4), cascade_ps=384)
+        r = bench_decode_secondary(name, 512, groups=([0, 16, 32, 48, 64], [64 * bs] * 4), cascade_ps=640)
     print(json.dumps({"only": name, **{k: v for k, v in r.items() if isinstance(v, (int, float, str, dict, list))}}),
           flush=True)
 
@@ -928,9 +928,9 @@ def main():
             bench_decode_secondary("decode_batch_bs32_k128_v64", 192,
                                    case=W.decode_batch(2000, poison=False, v_head_dim=64)),
             bench_decode_secondary("prefix_shared_decode_bs16", 512, groups=([0, 16, 32, 48, 64], [64 * 16] * 4),
-                                   cascade_ps=384),
+                                   cascade_ps=640),
             bench_decode_secondary("prefix_shared_decode_bs8", 512, groups=([0, 16, 32, 48, 64], [64 * 8] * 4),
-                                   cascade_ps=384),
+                                   cascade_ps=640),
         ]
         line["serving_loop"] = bench_serving()
         line["serving_loop_mixed"] = bench_serving(mixed=True)

@@ -14,6 +14,7 @@ pytestmark = pytest.mark.gpu
 
 BENCH_PARTITION = 320     # the split-K partition the benchmark times for the bs32 batch (and its G = 8 form)
 BENCH_PARTITION_V64 = 192  # ... and for its 64-wide-value form
+CASCADE_BENCH_PARTITION = 640  # own-token partition of the benchmark's cascade decode (prefix-shared batches)
 
 
 def _run(case, partition_size, max_context_len=None):
@@ -462,7 +463,7 @@ def test_cascade_prefix_shared_full(name):
     case = W.make_config(name)
     bs = case.block_size
     ref = oracle_decode(case)
-    for ps in (256, 512):
+    for ps in (256, 512, CASCADE_BENCH_PARTITION):
         log(f"cascade {name} partition={ps}")
         got = _cascade(case, [0, 16, 32, 48, 64], [64 * bs] * 4, ps)
         mx, mean = assert_close(got, ref, W.BF16, f"cascade {name} ps{ps}")
