@@ -72,7 +72,7 @@ def parse():
 ONLY = ("decode_bs32", "tiny_fp32_decode", "long_context_decode", "decode_batch_bs32_ctx4096",
         "decode_batch_bs32_64q_8kv", "decode_batch_bs32_k128_v64", "prefix_shared_decode_bs16",
         "prefix_shared_decode_bs8", "chunked_prefill", "chunked_prefill_bs16", "chunked_prefill_bs8",
-        "stream_read")
+        "stream_read", "mfma_ceiling")
 
 
 def source_hash(*names) -> str:
@@ -536,6 +536,35 @@ def bench_serving(seed=7000, num_requests=96, num_blocks=12000, mixed=False):
     return res
 
 
+def bench_mfma_ceiling(iters=2048, launches=20):
+    """The library's matrix-unit ceiling kernel (pa_mfma_peak: 4 waves per
+    SIMD, each 4 independent bf16 MFMA chains, no memory traffic), launched
+    back to back: dense bf16 TFLOP/s the device sustains, and the clock
+    beside it."""
+    import torch
+    import paged_attention_kv_cache_amd as P
+    sink = torch.zeros(1, dtype=torch.float32, device="cuda")
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    flops = cus * 4 * 4 * iters * 4 * 32768.0
+    for _ in range(3):
+        P.pa_mfma_peak(sink, iters)
+    ms = timed_each(lambda i: P.pa_mfma_peak(sink, iters), launches)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(launches):
+        P.pa_mfma_peak(sink, iters)
+    e1.record()
+    torch.cuda.synchronize()
+    t_ms = e0.elapsed_time(e1) / launches
+    clk = measure_clock(lambda: P.pa_mfma_peak(sink, iters), launches=12)
+    tflops = flops / (t_ms * 1e-3) / 1e12
+    log(f"matrix-unit ceiling: {tflops:.0f} TFLOP/s dense bf16 at {clk['ghz']} GHz")
+    return {"tflops": round(tflops, 1), "frac_of_nominal": round(tflops / BF16_DENSE_PEAK_TFLOPS, 4),
+            "launch_us": round(t_ms * 1e3, 2), "stats": stats_ms(ms), "flops_per_launch": flops,
+            "clock_ghz": clk["ghz"]}
+
+
 def measure_clock(fn=None, launches=30, ticks=200_000):
     """Shader clock in GHz over `ticks` ticks of the GPU's 100 MHz reference
     counter, from the library's clock probe (one wave).  With `fn`, the probe
@@ -684,6 +713,8 @@ def run_only(args):
         r = bench_tiny()
     elif name == "stream_read":
         r = bench_stream_ceiling()
+    elif name == "mfma_ceiling":
+        r = bench_mfma_ceiling()
     elif name.startswith("chunked_prefill"):
         bs = int(name[len("chunked_prefill_bs"):]) if name != "chunked_prefill" else 32
         r = bench_prefill(args, block_size=bs)
@@ -830,6 +861,7 @@ def main():
     log(f"plain sequential read: {ceiling['gbps']:.0f} GB/s at 1 GiB, {ceiling_same['gbps']:.0f} GB/s at "
         f"{dec['part_bytes'] / 1e6:.0f} MB")
     pre = None if args.no_prefill else bench_prefill(args)
+    mceil = None if args.no_prefill else bench_mfma_ceiling()
     case = dec["case"]
     tokens_per_s = dec["S"] / (dec["ms_step"] * 1e-3)
     traffic = traffic_from_profiles("decode_partition", dec["src"], dec["ps"])
@@ -903,6 +935,8 @@ def main():
                          "unit": "TFLOP/s", "frac": round(pre["frac"], 4),
                          "traffic": traffic_from_profiles("prefill_chunk", pre["src"]),
                          "algorithmic_flops_per_launch": pre["flops"]},
+            "mfma_ceiling": mceil,
+            "frac_of_mfma_ceiling": round(pre["tflops"] / mceil["tflops"], 4),
             "clock_during_launches": pre["clock"],
             "mfma_frac_at_measured_clock": round(pre["frac_at_measured_clock"], 4) if pre["frac_at_measured_clock"] else None,
         }

@@ -3,8 +3,9 @@
  * (MI355X, gfx950).  Not attention operations: they exist so that a
  * benchmark can measure, on the same device and in the same run as the
  * kernels, the HBM read rate that a plain sequential read reaches (the
- * practical ceiling of the bandwidth-bound decode) and the shader clock
- * the matrix-bound prefill runs at (the matrix unit's peak scales with it).
+ * practical ceiling of the bandwidth-bound decode), the dense bf16 rate
+ * the matrix units sustain (that of the matrix-bound prefill) and the
+ * shader clock (the matrix unit's peak scales with it).
  */
 #ifndef PAGEDATTN_BENCH_H
 #define PAGEDATTN_BENCH_H
@@ -25,6 +26,21 @@ extern "C" {
  * Returns PA_OK, or PA_ERR_NULL / PA_ERR_SHAPE / PA_ERR_HIP with the
  * message set (pa_last_error_message). */
 int pa_stream_read(const void *buf, size_t bytes, void *sink, void *stream);
+
+/* Most rounds pa_mfma_peak runs per wave. */
+#define PA_MFMA_PEAK_MAX_ITERS 65536
+
+/* Enqueues the matrix-unit ceiling kernel on `stream`: 4 work-groups of 4
+ * waves per compute unit, every wave running `iters` rounds (1 ..
+ * PA_MFMA_PEAK_MAX_ITERS) of four independent chains of
+ * v_mfma_f32_32x32x16_bf16 on register operands, with no memory traffic.
+ * One launch performs (compute units x 4) x 4 x iters x 4 x 32768 FLOP; its
+ * time gives the dense bf16 rate the device sustains (at the clock that
+ * load runs it at).  `sink` is a device pointer to 4 writable bytes that
+ * the kernel writes only if the folded accumulators equal one fixed value.
+ * Returns PA_OK, or PA_ERR_NULL / PA_ERR_SHAPE / PA_ERR_HIP with the
+ * message set. */
+int pa_mfma_peak(void *sink, int32_t iters, void *stream);
 
 /* Longest interval pa_clock_probe measures: 10 ms of the 100 MHz reference. */
 #define PA_CLOCK_PROBE_MAX_TICKS 1000000

@@ -47,6 +47,7 @@ from ._binding import (  # noqa: F401
     pa_status_string,
     pa_stream_read,
     pa_clock_probe,
+    pa_mfma_peak,
     pa_version,
 )
 from .kv_manager import (KIND_DECODE, KIND_IDLE, KIND_MIXED, KIND_PROMPT, KvManager, Step, StepScheduler,  # noqa: F401

@@ -105,6 +105,7 @@ SIGNATURES = {
     "pa_version": (ctypes.c_int, []),
     "pa_stream_read": (ctypes.c_int, [_vp, _sz, _vp, _vp]),
     "pa_clock_probe": (ctypes.c_int, [_vp, _i64, _vp]),
+    "pa_mfma_peak": (ctypes.c_int, [_vp, _i32, _vp]),
     # host KV manager and step scheduler
     "pa_kvm_create": (_vp, [_i32, _i32, _i32]),
     "pa_kvm_destroy": (None, [_vp]),
@@ -259,6 +260,16 @@ def pa_stream_read(buf, sink, stream=None) -> None:
         raise ValueError("sink must hold at least 4 bytes")
     code = load_library().pa_stream_read(_dev(buf, "buf"), nbytes, _dev(sink, "sink"), _stream(stream))
     _check("pa_stream_read", code)
+
+
+def pa_mfma_peak(sink, iters: int, stream=None) -> None:
+    """Enqueue the matrix-unit ceiling kernel of ``include/pagedattn_bench.h``
+    (``iters`` rounds of four bf16 MFMA chains per wave); ``sink`` is a GPU
+    tensor of at least 4 bytes."""
+    if sink.numel() * sink.element_size() < 4:
+        raise ValueError("sink must hold at least 4 bytes")
+    code = load_library().pa_mfma_peak(_dev(sink, "sink"), int(iters), _stream(stream))
+    _check("pa_mfma_peak", code)
 
 
 def pa_clock_probe(out, ticks: int, stream=None) -> None:

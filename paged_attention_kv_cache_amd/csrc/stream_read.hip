@@ -1,4 +1,5 @@
-// Measurement helpers: the HBM read ceiling, and the shader clock.
+// Measurement helpers: the HBM read ceiling, the matrix-unit ceiling and
+// the shader clock.
 //
 // HBM read ceiling: a kernel that only streams a buffer in.
 //
@@ -61,6 +62,35 @@ __global__ void __launch_bounds__(64) clock_probe_kernel(unsigned long long *__r
   }
 }
 
+// Matrix-unit ceiling: every wave runs `iters` rounds of four independent
+// chains of v_mfma_f32_32x32x16_bf16 (the prefill's product) on operands
+// made from its lane ids, with no memory traffic; four chains keep the
+// matrix pipeline full (each product waits only on the one four back).
+// The accumulators are folded into one word that is stored only if it
+// equals a constant no run produces in practice, so no product can be
+// dropped.  FLOPs per launch = work-groups x 4 waves x iters x 4 x 32768.
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_mp;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_mp;
+__global__ void __launch_bounds__(256) mfma_peak_kernel(float *__restrict__ sink, int iters) {
+  bf16x8_mp a, b;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    a[e] = (__bf16)((float)((threadIdx.x * 7 + e * 13) & 63) * 0.015625f - 0.5f);
+    b[e] = (__bf16)((float)((threadIdx.x * 5 + e * 11 + blockIdx.x) & 63) * 0.015625f - 0.5f);
+  }
+  f32x16_mp c0 = {}, c1 = {}, c2 = {}, c3 = {};
+  for (int i = 0; i < iters; ++i) {
+    c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c0, 0, 0, 0);
+    c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, a, c1, 0, 0, 0);
+    c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, a, c2, 0, 0, 0);
+    c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, b, c3, 0, 0, 0);
+  }
+  float acc = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc += c0[r] + c1[r] + c2[r] + c3[r];
+  if (acc == 1234567.75f) sink[0] = acc;
+}
+
 }  // namespace pa
 
 extern "C" int pa_stream_read(const void *buf, size_t bytes, void *sink, void *stream) {
@@ -92,5 +122,21 @@ extern "C" int pa_clock_probe(void *out, int64_t ticks, void *stream) {
                      static_cast<unsigned long long *>(out), (long long)ticks, max_iter);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return pa::set_error(PA_ERR_HIP, "clock_probe launch: HIP error %d (%s)", (int)e, hipGetErrorString(e));
+  return pa::clear_error();
+}
+
+extern "C" int pa_mfma_peak(void *sink, int32_t iters, void *stream) {
+  if (!sink) return pa::set_error(PA_ERR_NULL, "sink=%p: must be a device pointer to 4 writable bytes", sink);
+  if (iters < 1 || iters > PA_MFMA_PEAK_MAX_ITERS)
+    return pa::set_error(PA_ERR_SHAPE, "iters %d outside [1, %d]", (int)iters, (int)PA_MFMA_PEAK_MAX_ITERS);
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  const unsigned grid = (unsigned)(cus * 4);  // 4 work-groups of 4 waves per CU: 4 waves per SIMD
+  hipLaunchKernelGGL(pa::mfma_peak_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream,
+                     static_cast<float *>(sink), (int)iters);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return pa::set_error(PA_ERR_HIP, "mfma_peak launch: HIP error %d (%s)", (int)e, hipGetErrorString(e));
   return pa::clear_error();
 }

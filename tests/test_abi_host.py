@@ -254,8 +254,8 @@ def test_copy_blocks_validation(lib):
 
 
 def test_measurement_helpers_validation(lib):
-    """The stream-read and clock probes reject their arguments before any
-    launch."""
+    """The stream-read, matrix-ceiling and clock probes reject their
+    arguments before any launch."""
     assert lib.pa_stream_read(None, 16, FAKE, None) == -1
     assert lib.pa_stream_read(FAKE, 16, None, None) == -1
     assert lib.pa_stream_read(FAKE, 20, FAKE, None) == -3 and "multiple of 16" in msg()
@@ -263,6 +263,9 @@ def test_measurement_helpers_validation(lib):
     assert lib.pa_clock_probe(None, 1000, None) == -1
     assert lib.pa_clock_probe(FAKE, 0, None) == -3 and "ticks 0 outside" in msg()
     assert lib.pa_clock_probe(FAKE, 1000001, None) == -3
+    assert lib.pa_mfma_peak(None, 16, None) == -1
+    assert lib.pa_mfma_peak(FAKE, 0, None) == -3 and "iters 0 outside" in msg()
+    assert lib.pa_mfma_peak(FAKE, 65537, None) == -3
 
 
 def test_value_head_dim_validation(lib):
