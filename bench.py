@@ -413,16 +413,20 @@ def bench_decode_secondary(name, ps, steps=30, groups=None, case=None, cascade_p
     return res
 
 
-def bench_serving(seed=7000, num_requests=96, num_blocks=12000, mixed=False):
+def bench_serving(seed=7000, num_requests=96, num_blocks=12000, mixed=False, native=True):
     """The scheduler driving the kernels over a request trace: every step the
-    host plans (pa_sched_next_step), copies the step's tables through a
-    pinned buffer (one copy), and launches kv_cache_write plus prefill or
-    decode; the step is
-    then committed with 'sampled' tokens.  K/V/Q values are random device
+    host plans, copies the step's tables to the device through pinned memory
+    (one copy), and launches kv_cache_write plus prefill or decode; the step
+    is then committed with 'sampled' tokens.  K/V/Q values are random device
     data (they do not change the work).  Reports prompt + generated tokens
     per second of wall time, and the share of it the GPU was busy.  With
     ``mixed`` each step is one batch (decode rows, then prompt chunks) and a
-    step holding both runs as one prefill launch."""
+    step holding both runs as one prefill launch.  With ``native`` (the
+    default) each step is the library's native serving step
+    (``include/pagedattn_serve.h``: plan into pinned memory and copy, then
+    write and attend, then complete, one library call each); otherwise the
+    loop here stages the arrays and launches the kernels through the
+    Python binding."""
     import torch
     import paged_attention_kv_cache_amd as P
     import workloads as W
@@ -470,6 +474,7 @@ def bench_serving(seed=7000, num_requests=96, num_blocks=12000, mixed=False):
     ws = torch.zeros(P.pa_decode_workspace_bytes(cap_seqs, Hq, D, cap_blocks * bs, 256), dtype=torch.uint8,
                      device="cuda")
     scale = 1.0 / math.sqrt(D)
+    srv = P.Server(sched, Hq, scale, 256, cap_seqs, cap_blocks, cap_tokens) if native else None
     busy = []
     prompt_tokens = decode_tokens = steps = 0
     torch.cuda.synchronize()
@@ -478,6 +483,23 @@ def bench_serving(seed=7000, num_requests=96, num_blocks=12000, mixed=False):
         w, a, _ = sched.counts()
         if w == 0 and a == 0:
             break
+        if native:
+            st = srv.plan()
+            n, T = st.num_seqs, st.num_tokens
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            srv.attend(kc, vc, src_k[:T], src_v[:T], src_q[:T], out[:T], workspace=ws)
+            e1.record()
+            busy.append((e0, e1))
+            nd = T if st.kind == P.KIND_DECODE else 0
+            if st.kind == P.KIND_MIXED:
+                longer = np.flatnonzero(np.diff(st.query_start_loc) != 1)
+                nd = int(longer[0]) if longer.size else n
+            prompt_tokens += T - nd
+            decode_tokens += nd
+            srv.complete(rng.integers(1, 32000, n, dtype=np.int32))
+            steps += 1
+            continue
         st = sched.next_step()
         n, T = st.num_seqs, st.num_tokens
         b = steps % 2
@@ -522,6 +544,7 @@ def bench_serving(seed=7000, num_requests=96, num_blocks=12000, mixed=False):
                     + ("one mixed batch per step" if mixed else "<= 8 decode steps in a row")
                     + f", pool {num_blocks} blocks",
         "policy": "mixed" if mixed else "alternating",
+        "driver": "native step (pa_serve_plan / attend / complete)" if native else "python loop over the binding",
         "steps": steps, "prompt_tokens": prompt_tokens, "generated_tokens": decode_tokens,
         "wall_s": round(wall, 3), "tokens_per_s": round((prompt_tokens + decode_tokens) / wall, 1),
         "gpu_busy_frac": round(gpu_ms * 1e-3 / wall, 3),
@@ -529,6 +552,8 @@ def bench_serving(seed=7000, num_requests=96, num_blocks=12000, mixed=False):
     }
     log(f"serving ({res['policy']}): {steps} steps, {prompt_tokens} prompt + {decode_tokens} generated tokens in {wall:.2f} s "
         f"({res['tokens_per_s']:.0f} tokens/s, GPU busy {res['gpu_busy_frac']:.0%})")
+    if srv is not None:
+        srv.close()
     sched.close()
     kvm.close()
     del kc, vc
@@ -968,6 +993,7 @@ def main():
         ]
         line["serving_loop"] = bench_serving()
         line["serving_loop_mixed"] = bench_serving(mixed=True)
+        line["serving_loop_python_driver"] = bench_serving(native=False)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle (decode, prefill and long-context legs, median of 3 each)")
         pre_case = None if args.no_prefill else W.chunked_prefill(poison=False)

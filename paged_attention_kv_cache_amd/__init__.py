@@ -50,6 +50,6 @@ from ._binding import (  # noqa: F401
     pa_mfma_peak,
     pa_version,
 )
-from .kv_manager import (KIND_DECODE, KIND_IDLE, KIND_MIXED, KIND_PROMPT, KvManager, Step, StepScheduler,  # noqa: F401
-                         grow_pool)
+from .kv_manager import (KIND_DECODE, KIND_IDLE, KIND_MIXED, KIND_PROMPT, KvManager, Server, Step,  # noqa: F401
+                         StepScheduler, grow_pool)
 from .contracts import check_decode_contracts, check_prefill_contracts, check_slot_mapping  # noqa: F401

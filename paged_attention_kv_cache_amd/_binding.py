@@ -125,6 +125,13 @@ SIGNATURES = {
     "pa_sched_add_request": (ctypes.c_int, [_vp, _i64, _pi32, _i32, _i32]),
     "pa_sched_next_step": (ctypes.c_int, [_vp, ctypes.POINTER(PaStep)]),
     "pa_sched_complete_step": (ctypes.c_int, [_vp, ctypes.POINTER(PaStep), _pi32, _pi32]),
+    # native serving step (include/pagedattn_serve.h)
+    "pa_serve_meta_bytes": (_sz, [_i32, _i32, _i32]),
+    "pa_serve_create": (_vp, [_vp, _i32, _f32, _i32, _i32, _i32, _i32, _vp, _sz]),
+    "pa_serve_destroy": (None, [_vp]),
+    "pa_serve_plan": (ctypes.c_int, [_vp, ctypes.POINTER(PaStep), _vp]),
+    "pa_serve_attend": (ctypes.c_int, [_vp, _PCACHE, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "pa_serve_complete": (ctypes.c_int, [_vp, _pi32, _pi32]),
     "pa_sched_counts": (ctypes.c_int, [_vp, _pi32, _pi32, _pi32]),
 }
 

@@ -22,7 +22,8 @@ LIB_NAME = "libpagedattn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 ARCH = "gfx950"
 
-SOURCES = ["abi.cpp", "kv_cache_write.hip", "pa_decode.hip", "pa_prefill.hip", "kv_manager.cpp", "stream_read.hip"]
+SOURCES = ["abi.cpp", "kv_cache_write.hip", "pa_decode.hip", "pa_prefill.hip", "kv_manager.cpp", "stream_read.hip",
+           "serve.cpp"]
 # plain host C++ (no device code): built by the host compiler
 HOST_SOURCES = {"kv_manager.cpp"}
 # per-source device flags.  The prefill kernel never relies on NaN semantics

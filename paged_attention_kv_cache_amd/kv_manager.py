@@ -5,7 +5,8 @@
 device; ``StepScheduler`` plans alternating prompt / decode steps whose
 ``block_tables``, ``context_lens``, ``query_start_loc`` and
 ``slot_mapping`` feed ``pa_prefill_chunk`` / ``pa_decode`` /
-``pa_kv_cache_write`` directly.
+``pa_kv_cache_write`` directly; ``Server`` (``include/pagedattn_serve.h``)
+runs a step's planning, copy and launches inside the library.
 """
 
 from __future__ import annotations
@@ -199,6 +200,92 @@ class StepScheduler:
         _check("pa_sched_counts", self._lib.pa_sched_counts(self._h, ctypes.byref(a), ctypes.byref(b),
                                                              ctypes.byref(c)))
         return a.value, b.value, c.value
+
+
+class Server:
+    """The native serving step of ``include/pagedattn_serve.h`` over a
+    StepScheduler: ``plan`` (the scheduler plans into pinned host memory and
+    the step's arrays are copied to the device), ``attend`` (the step's K/V
+    write and attention launches) and ``complete`` (commit with sampled
+    tokens), each one library call.  The device buffer for the step's arrays
+    is allocated here; ``plan`` and ``attend`` of one step take the same
+    stream."""
+
+    def __init__(self, sched: StepScheduler, num_heads: int, scale: float, partition_size: int, max_seqs: int,
+                 max_blocks_per_seq: int, max_tokens: int, device="cuda"):
+        import torch
+        self._lib = load_library()
+        self.sched = sched
+        nbytes = int(self._lib.pa_serve_meta_bytes(max_seqs, max_blocks_per_seq, max_tokens))
+        if nbytes == 0:
+            raise ValueError(f"capacities must be positive: {max_seqs} seqs, {max_blocks_per_seq} blocks, "
+                             f"{max_tokens} tokens")
+        self._meta = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        h = self._lib.pa_serve_create(sched._h, num_heads, float(scale), partition_size, max_seqs,
+                                      max_blocks_per_seq, max_tokens, self._meta.data_ptr(), nbytes)
+        if not h:
+            _check("pa_serve_create", -3)
+        self._h = ctypes.c_void_p(h)
+        self._step = PaStep()
+        self._caps = (max_seqs, max_blocks_per_seq, max_tokens)
+        self._views = {}  # staging buffer (by address of its request ids) -> numpy views over it
+
+    def close(self) -> None:
+        if getattr(self, "_h", None):
+            self._lib.pa_serve_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        self.close()
+
+    def _arrays(self, st):
+        key = ctypes.cast(st.request_ids, ctypes.c_void_p).value
+        v = self._views.get(key)
+        if v is None:
+            S, B, T = self._caps
+            v = (np.ctypeslib.as_array(st.request_ids, shape=(S,)),
+                 np.ctypeslib.as_array(st.query_start_loc, shape=(S + 1,)),
+                 np.ctypeslib.as_array(st.context_lens, shape=(S,)),
+                 np.ctypeslib.as_array(st.block_tables, shape=(S * B,)).reshape(S, B),
+                 np.ctypeslib.as_array(st.slot_mapping, shape=(T,)))
+            self._views[key] = v
+        return v
+
+    def plan(self, stream=None) -> Step:
+        """Plan the next step; its arrays are views into pinned staging memory,
+        valid until the plan after the next."""
+        from ._binding import _stream
+        _check("pa_serve_plan", self._lib.pa_serve_plan(self._h, ctypes.byref(self._step), _stream(stream)))
+        st = self._step
+        n, t = st.num_seqs, st.num_tokens
+        if st.kind == KIND_IDLE:
+            e = np.zeros(0, np.int64)
+            return Step(KIND_IDLE, e, np.zeros(1, np.int32), np.zeros(0, np.int32),
+                        np.zeros((0, self._caps[1]), np.int32), e, 0, 0)
+        ids, qsl, ctx, tab, slots = self._arrays(st)
+        return Step(st.kind, ids[:n], qsl[:n + 1], ctx[:n], tab[:n], slots[:t], st.max_query_len,
+                    st.max_context_len)
+
+    def attend(self, k_cache, v_cache, new_key, new_value, q, out, workspace=None, stream=None) -> None:
+        """The planned step's K/V write and attention (GPU tensors: the pool,
+        the step's new K/V rows, its q rows and the output rows)."""
+        from ._binding import _stream, make_cache
+        cache = make_cache(k_cache, v_cache)
+        ws = 0 if workspace is None else workspace.data_ptr()
+        wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        _check("pa_serve_attend", self._lib.pa_serve_attend(
+            self._h, ctypes.byref(cache), new_key.data_ptr(), new_value.data_ptr(), q.data_ptr(), out.data_ptr(),
+            ws, wsb, _stream(stream)))
+
+    def complete(self, sampled: Optional[Sequence[int]] = None) -> int:
+        """Commit the planned step; returns how many requests finished."""
+        fin = ctypes.c_int32(0)
+        s = None if sampled is None else _tokens(sampled)
+        if s is not None and s.size < self._step.num_seqs:
+            raise ValueError(f"{s.size} sampled tokens for {self._step.num_seqs} sequences")
+        _check("pa_serve_complete", self._lib.pa_serve_complete(self._h, None if s is None else _p32(s),
+                                                                ctypes.byref(fin)))
+        return fin.value
 
 
 def grow_pool(kvm: KvManager, k_cache, v_cache, new_num_blocks: int):

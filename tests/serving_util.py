@@ -86,6 +86,43 @@ class LibraryBackend:
         return to_host_f32(out, W.BF16)
 
 
+class NativeBackend(LibraryBackend):
+    """The library's native serving step (pa_serve_plan / pa_serve_attend /
+    pa_serve_complete of include/pagedattn_serve.h): the scheduler plans into
+    pinned memory, one copy moves the step's arrays to the device, and the
+    library launches the write and the attention."""
+
+    def attach(self, sched, trace, max_seqs, max_blocks_per_seq, max_tokens, partition_size):
+        import paged_attention_kv_cache_amd as P
+        t = self.t
+        self.server = P.Server(sched, trace.num_heads, trace.scale, partition_size, max_seqs, max_blocks_per_seq,
+                               max_tokens)
+        self.shape = (trace.num_heads, trace.head_dim)
+        self.ws = None
+        if partition_size:
+            need = P.pa_decode_workspace_bytes(max_seqs, trace.num_heads, trace.head_dim,
+                                               max_blocks_per_seq * trace.block_size, partition_size)
+            self.ws = t.empty(max(need, 1), dtype=t.uint8, device="cuda")
+
+    def plan(self):
+        return self.server.plan()
+
+    def step(self, st, keys, vals, qs, scale, partition_size):
+        from gpu_util import to_dev, to_host_f32
+        t = self.t
+        dev_k, dev_v, dev_q = to_dev(keys, W.BF16), to_dev(vals, W.BF16), to_dev(qs, W.BF16)
+        out = t.empty((st.num_tokens,) + self.shape, dtype=t.bfloat16, device="cuda")
+        self.server.attend(self.kc, self.vc, dev_k, dev_v, dev_q, out, workspace=self.ws)
+        t.cuda.synchronize()
+        return to_host_f32(out, W.BF16)
+
+    def complete(self, sampled):
+        self.server.complete(sampled)
+
+    def close(self):
+        self.server.close()
+
+
 def serve_and_check(trace, backend, partition_size=0, max_batched_tokens=256, max_chunk_tokens=128,
                     max_seqs=8, max_blocks_per_seq=32, tag="", grow_at=None, mixed=False):
     """Runs the trace to completion; returns a summary dict.  ``grow_at``
@@ -98,6 +135,9 @@ def serve_and_check(trace, backend, partition_size=0, max_batched_tokens=256, ma
                         max_seqs=max_seqs, max_blocks_per_seq=max_blocks_per_seq, mixed=mixed)
     for rid, prompt in trace.prompts.items():
         s.add_request(rid, prompt, trace.max_new[rid])
+    native = hasattr(backend, "plan")
+    if native:
+        backend.attach(s, trace, max_seqs, max_blocks_per_seq, max(max_batched_tokens, max_seqs), partition_size)
     H, Hkv, D = trace.num_heads, trace.num_kv_heads, trace.head_dim
     expected = {rid: list(p) for rid, p in trace.prompts.items()}
     gen = {rid: 0 for rid in trace.prompts}
@@ -111,7 +151,7 @@ def serve_and_check(trace, backend, partition_size=0, max_batched_tokens=256, ma
         if grow_at and step in grow_at:
             log(f"serving{tag}: pool grows to {grow_at[step]} blocks before step {step}")
             backend.grow(m, grow_at[step])
-        st = s.next_step()
+        st = backend.plan() if native else s.next_step()
         assert st.kind in ((P.KIND_PROMPT, P.KIND_DECODE, P.KIND_MIXED) if mixed else (P.KIND_PROMPT, P.KIND_DECODE))
         kinds.append(st.kind)
         ids = st.request_ids.tolist()
@@ -146,7 +186,10 @@ def serve_and_check(trace, backend, partition_size=0, max_batched_tokens=256, ma
                                   f"step {step} request {rid} ctx {c} kind {st.kind}")
             worst = max(worst, err)
         sampled = [trace.sampled_token(rid, int(ctx[i])) for i, rid in enumerate(ids)]
-        s.complete_step(sampled)
+        if native:
+            backend.complete(sampled)
+        else:
+            s.complete_step(sampled)
         for i, rid in enumerate(ids):
             if int(ctx[i]) < len(expected[rid]):
                 continue
@@ -158,6 +201,8 @@ def serve_and_check(trace, backend, partition_size=0, max_batched_tokens=256, ma
     stats = m.stats()
     assert s.counts() == (0, 0, len(trace.prompts))
     assert all(gen[r] == trace.max_new[r] for r in gen)
+    if native:
+        backend.close()
     s.close()
     m.close()
     return {"steps": len(kinds), "kinds": kinds, "worst": worst, "recomputed": len(recomputed), "stats": stats}

@@ -268,6 +268,26 @@ def test_measurement_helpers_validation(lib):
     assert lib.pa_mfma_peak(FAKE, 65537, None) == -3
 
 
+def test_serve_validation(lib):
+    """The native serving step rejects bad arguments before touching the
+    device (no pinned allocation, no copy, no launch)."""
+    assert lib.pa_serve_meta_bytes(0, 8, 16) == 0
+    assert lib.pa_serve_meta_bytes(4, 8, 16) >= 16 * 8 + 5 * 4 + 4 * 4 + 4 * 8 * 4
+    assert lib.pa_serve_meta_bytes(4, 8, 16) % 256 == 0
+    assert not lib.pa_serve_create(None, 32, 0.1, 0, 4, 8, 16, FAKE, 1 << 20) and "required" in msg()
+    sched = FAKE  # never dereferenced: creation fails on the sizes first
+    assert not lib.pa_serve_create(sched, 32, 0.1, 0, 4, 8, 16, None, 1 << 20)
+    assert not lib.pa_serve_create(sched, 32, 0.1, 0, 0, 8, 16, FAKE, 1 << 20) and "positive" in msg()
+    assert not lib.pa_serve_create(sched, 32, 0.1, 0, 4, 8, 16, FAKE, 64) and "need" in msg()
+    assert not lib.pa_serve_create(sched, 32, 0.1, -1, 4, 8, 16, FAKE, 1 << 20)
+    step = _binding.PaStep()
+    fin = ctypes.c_int32(0)
+    assert lib.pa_serve_plan(None, ctypes.byref(step), None) == -1
+    assert lib.pa_serve_attend(None, None, FAKE, FAKE, FAKE, FAKE, None, 0, None) == -1
+    assert lib.pa_serve_complete(None, None, ctypes.byref(fin)) == -1
+    lib.pa_serve_destroy(None)
+
+
 def test_value_head_dim_validation(lib):
     """A value head dim of its own (0 = the key head dim): attention takes
     64 or 128, the workspace is sized by it (cascade decode's too), and the

@@ -10,7 +10,7 @@ import pytest
 import workloads as W
 
 from gpu_util import BF16_MAX_ABS, log
-from serving_util import LibraryBackend, serve_and_check
+from serving_util import LibraryBackend, NativeBackend, serve_and_check
 
 pytestmark = pytest.mark.gpu
 
@@ -44,3 +44,26 @@ def test_mixed_batch_serving_matches_dense_oracle():
     assert 3 in r["kinds"]
     assert r["worst"] <= BF16_MAX_ABS
     log(f"serving mixed: {r['steps']} steps ({r['kinds'].count(3)} mixed), worst max-abs {r['worst']:.2e}")
+
+
+@pytest.mark.parametrize("partition_size", [0, 64])
+def test_native_serving_matches_dense_oracle(partition_size):
+    """The same trace through the library's native serving step (plan into
+    pinned memory, one copy, write and attention launched by the library):
+    every output row matches the oracle's dense attention."""
+    tr = W.serving_trace(seed=6000, num_requests=12, num_blocks=64)
+    r = serve_and_check(tr, NativeBackend(tr), partition_size=partition_size, tag="-native")
+    assert r["recomputed"] > 0 and 1 in r["kinds"] and 2 in r["kinds"]
+    assert r["worst"] <= BF16_MAX_ABS
+    log(f"native serving ps={partition_size}: {r['steps']} steps, worst max-abs {r['worst']:.2e}")
+
+
+def test_native_serving_mixed_and_growth():
+    """Mixed batches through the native step, and a pool that grows mid-trace
+    (the pool is passed to every attend call)."""
+    tr = W.serving_trace(seed=6005, num_requests=12, num_blocks=64)
+    r = serve_and_check(tr, NativeBackend(tr), partition_size=64, tag="-native-mixed", mixed=True)
+    assert 3 in r["kinds"] and r["worst"] <= BF16_MAX_ABS
+    tr = W.serving_trace(seed=6003, num_requests=12, num_blocks=40)
+    r = serve_and_check(tr, NativeBackend(tr), partition_size=64, grow_at={6: 56, 14: 160}, tag="-native-grow")
+    assert r["stats"]["num_blocks"] == 160 and r["worst"] <= BF16_MAX_ABS
