@@ -991,6 +991,7 @@ def main():
             bench_decode_secondary("prefix_shared_decode_bs8", 512, groups=([0, 16, 32, 48, 64], [64 * 8] * 4),
                                    cascade_ps=640),
         ]
+        bench_serving(num_requests=8)  # untimed: the first pass on a device pays one-time costs
         line["serving_loop"] = bench_serving()
         line["serving_loop_mixed"] = bench_serving(mixed=True)
         line["serving_loop_python_driver"] = bench_serving(native=False)
