@@ -127,7 +127,7 @@ SIGNATURES = {
     "pa_sched_complete_step": (ctypes.c_int, [_vp, ctypes.POINTER(PaStep), _pi32, _pi32]),
     # native serving step (include/pagedattn_serve.h)
     "pa_serve_meta_bytes": (_sz, [_i32, _i32, _i32]),
-    "pa_serve_create": (_vp, [_vp, _i32, _f32, _i32, _i32, _i32, _i32, _vp, _sz]),
+    "pa_serve_create": (_vp, [_vp, _i32, _f32, _i32, _i32, _i32, _i32, _i32, _vp, _sz]),
     "pa_serve_destroy": (None, [_vp]),
     "pa_serve_plan": (ctypes.c_int, [_vp, ctypes.POINTER(PaStep), _vp]),
     "pa_serve_attend": (ctypes.c_int, [_vp, _PCACHE, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),

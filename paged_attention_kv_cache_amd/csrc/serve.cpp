@@ -43,7 +43,7 @@ bool layout(int32_t cap_seqs, int32_t cap_blocks, int32_t cap_tokens, Layout &L)
 
 struct pa_serve {
   pa_sched *sched = nullptr;
-  int32_t num_heads = 0, partition_size = 0;
+  int32_t num_heads = 0, partition_size = 0, mixed_split_context = 0;
   float scale = 0.f;
   int32_t cap_seqs = 0, cap_blocks = 0, cap_tokens = 0;
   Layout L{};
@@ -74,8 +74,8 @@ extern "C" void pa_serve_destroy(pa_serve *s) {
 }
 
 extern "C" pa_serve *pa_serve_create(pa_sched *sched, int32_t num_heads, float scale, int32_t partition_size,
-                                     int32_t max_seqs, int32_t max_blocks_per_seq, int32_t max_tokens,
-                                     void *dev_meta, size_t dev_meta_bytes) {
+                                     int32_t mixed_split_context, int32_t max_seqs, int32_t max_blocks_per_seq,
+                                     int32_t max_tokens, void *dev_meta, size_t dev_meta_bytes) {
   Layout L;
   if (!sched || !dev_meta) {
     pa::set_error(PA_ERR_NULL, "sched=%p dev_meta=%p: both are required", (void *)sched, dev_meta);
@@ -94,6 +94,10 @@ extern "C" pa_serve *pa_serve_create(pa_sched *sched, int32_t num_heads, float s
     pa::set_error(PA_ERR_PARTITION, "partition_size %d must be >= 0", partition_size);
     return nullptr;
   }
+  if (mixed_split_context < 0) {
+    pa::set_error(PA_ERR_SHAPE, "mixed_split_context %d must be >= 0", mixed_split_context);
+    return nullptr;
+  }
   pa_serve *s = new (std::nothrow) pa_serve();
   if (!s) {
     pa::set_error(PA_ERR_SHAPE, "out of host memory");
@@ -103,6 +107,7 @@ extern "C" pa_serve *pa_serve_create(pa_sched *sched, int32_t num_heads, float s
   s->num_heads = num_heads;
   s->scale = scale;
   s->partition_size = partition_size;
+  s->mixed_split_context = mixed_split_context;
   s->cap_seqs = max_seqs;
   s->cap_blocks = max_blocks_per_seq;
   s->cap_tokens = max_tokens;
@@ -168,6 +173,24 @@ extern "C" int pa_serve_attend(pa_serve *s, const pa_kv_cache *cache, const void
   const int32_t *d_tab = reinterpret_cast<const int32_t *>(s->dev_meta + s->L.tab);
   int rc = pa_kv_cache_write(cache, new_key, new_value, d_slots, st.num_tokens, stream);
   if (rc) return rc;
+  int nd = 0;  // leading one-token rows (a mixed step's decode rows)
+  int32_t longest = 0;
+  if (st.kind == 3 && s->partition_size > 0 && s->mixed_split_context > 0)
+    for (; nd < st.num_seqs && st.query_start_loc[nd + 1] - st.query_start_loc[nd] == 1; ++nd)
+      longest = st.context_lens[nd] > longest ? st.context_lens[nd] : longest;
+  if (nd > 0 && longest >= s->mixed_split_context) {
+    // A mixed step's decode rows through split-K decode (a long context
+    // spread over many work-groups instead of one per kv head), the prompt
+    // chunks after them through the prefill kernel.  A one-token row is a
+    // decode step under the causal alignment; packed row i is decode row i,
+    // and the chunks' query offsets are absolute rows of the same q and out.
+    rc = pa_decode(cache, out, q, nd, s->num_heads, d_tab, st.cap_blocks, d_ctx, st.max_context_len, s->scale,
+                   s->partition_size, workspace, workspace_bytes, stream);
+    if (rc || nd == st.num_seqs) return rc;
+    return pa_prefill_chunk(cache, out, q, d_qsl + nd, st.num_seqs - nd, s->num_heads, st.num_tokens,
+                            st.max_query_len, d_tab + (size_t)nd * st.cap_blocks, st.cap_blocks, d_ctx + nd,
+                            st.max_context_len, s->scale, stream);
+  }
   if (st.kind == 1 || st.kind == 3)
     return pa_prefill_chunk(cache, out, q, d_qsl, st.num_seqs, s->num_heads, st.num_tokens, st.max_query_len, d_tab,
                             st.cap_blocks, d_ctx, st.max_context_len, s->scale, stream);

@@ -209,10 +209,11 @@ class Server:
     write and attention launches) and ``complete`` (commit with sampled
     tokens), each one library call.  The device buffer for the step's arrays
     is allocated here; ``plan`` and ``attend`` of one step take the same
-    stream."""
+    stream.  A mixed step whose decode rows reach ``mixed_split_context``
+    tokens of context runs them through split-K decode (0: never)."""
 
     def __init__(self, sched: StepScheduler, num_heads: int, scale: float, partition_size: int, max_seqs: int,
-                 max_blocks_per_seq: int, max_tokens: int, device="cuda"):
+                 max_blocks_per_seq: int, max_tokens: int, mixed_split_context: int = 8192, device="cuda"):
         import torch
         self._lib = load_library()
         self.sched = sched
@@ -221,8 +222,8 @@ class Server:
             raise ValueError(f"capacities must be positive: {max_seqs} seqs, {max_blocks_per_seq} blocks, "
                              f"{max_tokens} tokens")
         self._meta = torch.empty(nbytes, dtype=torch.uint8, device=device)
-        h = self._lib.pa_serve_create(sched._h, num_heads, float(scale), partition_size, max_seqs,
-                                      max_blocks_per_seq, max_tokens, self._meta.data_ptr(), nbytes)
+        h = self._lib.pa_serve_create(sched._h, num_heads, float(scale), partition_size, mixed_split_context,
+                                      max_seqs, max_blocks_per_seq, max_tokens, self._meta.data_ptr(), nbytes)
         if not h:
             _check("pa_serve_create", -3)
         self._h = ctypes.c_void_p(h)

@@ -87,6 +87,11 @@ class LibraryBackend:
 
 
 class NativeBackend(LibraryBackend):
+    # decode-row context from which a mixed step splits its decode rows off
+    # to split-K decode (small here, so that the short test contexts take
+    # that path too; 0 keeps every mixed step in one prefill launch)
+    mixed_split_context = 1
+
     """The library's native serving step (pa_serve_plan / pa_serve_attend /
     pa_serve_complete of include/pagedattn_serve.h): the scheduler plans into
     pinned memory, one copy moves the step's arrays to the device, and the
@@ -96,7 +101,7 @@ class NativeBackend(LibraryBackend):
         import paged_attention_kv_cache_amd as P
         t = self.t
         self.server = P.Server(sched, trace.num_heads, trace.scale, partition_size, max_seqs, max_blocks_per_seq,
-                               max_tokens)
+                               max_tokens, mixed_split_context=self.mixed_split_context)
         self.shape = (trace.num_heads, trace.head_dim)
         self.ws = None
         if partition_size:

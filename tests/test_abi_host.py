@@ -274,12 +274,13 @@ def test_serve_validation(lib):
     assert lib.pa_serve_meta_bytes(0, 8, 16) == 0
     assert lib.pa_serve_meta_bytes(4, 8, 16) >= 16 * 8 + 5 * 4 + 4 * 4 + 4 * 8 * 4
     assert lib.pa_serve_meta_bytes(4, 8, 16) % 256 == 0
-    assert not lib.pa_serve_create(None, 32, 0.1, 0, 4, 8, 16, FAKE, 1 << 20) and "required" in msg()
+    assert not lib.pa_serve_create(None, 32, 0.1, 0, 0, 4, 8, 16, FAKE, 1 << 20) and "required" in msg()
     sched = FAKE  # never dereferenced: creation fails on the sizes first
-    assert not lib.pa_serve_create(sched, 32, 0.1, 0, 4, 8, 16, None, 1 << 20)
-    assert not lib.pa_serve_create(sched, 32, 0.1, 0, 0, 8, 16, FAKE, 1 << 20) and "positive" in msg()
-    assert not lib.pa_serve_create(sched, 32, 0.1, 0, 4, 8, 16, FAKE, 64) and "need" in msg()
-    assert not lib.pa_serve_create(sched, 32, 0.1, -1, 4, 8, 16, FAKE, 1 << 20)
+    assert not lib.pa_serve_create(sched, 32, 0.1, 0, 0, 4, 8, 16, None, 1 << 20)
+    assert not lib.pa_serve_create(sched, 32, 0.1, 0, 0, 0, 8, 16, FAKE, 1 << 20) and "positive" in msg()
+    assert not lib.pa_serve_create(sched, 32, 0.1, 0, 0, 4, 8, 16, FAKE, 64) and "need" in msg()
+    assert not lib.pa_serve_create(sched, 32, 0.1, -1, 0, 4, 8, 16, FAKE, 1 << 20)
+    assert not lib.pa_serve_create(sched, 32, 0.1, 0, -1, 4, 8, 16, FAKE, 1 << 20) and "mixed_split_context" in msg()
     step = _binding.PaStep()
     fin = ctypes.c_int32(0)
     assert lib.pa_serve_plan(None, ctypes.byref(step), None) == -1

@@ -58,11 +58,16 @@ def test_native_serving_matches_dense_oracle(partition_size):
     log(f"native serving ps={partition_size}: {r['steps']} steps, worst max-abs {r['worst']:.2e}")
 
 
-def test_native_serving_mixed_and_growth():
-    """Mixed batches through the native step, and a pool that grows mid-trace
-    (the pool is passed to every attend call)."""
+@pytest.mark.parametrize("split", [1, 0])
+def test_native_serving_mixed_and_growth(split):
+    """Mixed batches through the native step, their decode rows through
+    split-K decode (split 1: from any context) or with the chunks in one
+    prefill launch (0), and a pool that grows mid-trace (the pool is passed
+    to every attend call)."""
     tr = W.serving_trace(seed=6005, num_requests=12, num_blocks=64)
-    r = serve_and_check(tr, NativeBackend(tr), partition_size=64, tag="-native-mixed", mixed=True)
+    be = NativeBackend(tr)
+    be.mixed_split_context = split
+    r = serve_and_check(tr, be, partition_size=64, tag=f"-native-mixed-split{split}", mixed=True)
     assert 3 in r["kinds"] and r["worst"] <= BF16_MAX_ABS
     tr = W.serving_trace(seed=6003, num_requests=12, num_blocks=40)
     r = serve_and_check(tr, NativeBackend(tr), partition_size=64, grow_at={6: 56, 14: 160}, tag="-native-grow")
