@@ -213,7 +213,7 @@ class Server:
     tokens of context runs them through split-K decode (0: never)."""
 
     def __init__(self, sched: StepScheduler, num_heads: int, scale: float, partition_size: int, max_seqs: int,
-                 max_blocks_per_seq: int, max_tokens: int, mixed_split_context: int = 8192, device="cuda"):
+                 max_blocks_per_seq: int, max_tokens: int, mixed_split_context: int = 4096, device="cuda"):
         import torch
         self._lib = load_library()
         self.sched = sched
