@@ -19,9 +19,10 @@
  *                     steps) on `stream`; a mixed step runs all its rows
  *                     through pa_prefill_chunk (a decode row is a chunk of
  *                     one token), or, when one of its decode rows has a
- *                     context of mixed_split_context tokens or more, its
- *                     leading one-token rows through split-K pa_decode and
- *                     the prompt chunks after them through pa_prefill_chunk;
+ *                     context of mixed_split_context tokens or more and
+ *                     longer than every chunk's context, its leading
+ *                     one-token rows through split-K pa_decode and the
+ *                     prompt chunks after them through pa_prefill_chunk;
  *   pa_serve_complete commits the step with the tokens sampled from it.
  *
  * Two pinned staging buffers alternate: a plan waits (on the host) for the
@@ -59,7 +60,8 @@ size_t pa_serve_meta_bytes(int32_t max_seqs, int32_t max_blocks_per_seq, int32_t
  * sequence).  mixed_split_context (0: never) is the decode-row context at
  * which a mixed step's decode rows go through split-K decode instead of the
  * prefill kernel, which gives each of them one work-group per kv head: a
- * long context then spreads over many work-groups.  `dev_meta` is a device
+ * long context then spreads over many work-groups (only when that row is
+ * also longer than every chunk's context in the step).  `dev_meta` is a device
  * buffer of at least
  * pa_serve_meta_bytes(...) bytes, owned by the caller and used by every
  * step.  The object allocates its two pinned staging buffers and two HIP

@@ -174,11 +174,17 @@ extern "C" int pa_serve_attend(pa_serve *s, const pa_kv_cache *cache, const void
   int rc = pa_kv_cache_write(cache, new_key, new_value, d_slots, st.num_tokens, stream);
   if (rc) return rc;
   int nd = 0;  // leading one-token rows (a mixed step's decode rows)
-  int32_t longest = 0;
-  if (st.kind == 3 && s->partition_size > 0 && s->mixed_split_context > 0)
+  int32_t longest = 0, longest_chunk = 0;
+  if (st.kind == 3 && s->partition_size > 0 && s->mixed_split_context > 0) {
     for (; nd < st.num_seqs && st.query_start_loc[nd + 1] - st.query_start_loc[nd] == 1; ++nd)
       longest = st.context_lens[nd] > longest ? st.context_lens[nd] : longest;
-  if (nd > 0 && longest >= s->mixed_split_context) {
+    for (int i = nd; i < st.num_seqs; ++i)
+      longest_chunk = st.context_lens[i] > longest_chunk ? st.context_lens[i] : longest_chunk;
+  }
+  // the decode rows are worth a launch of their own when one of them is long
+  // and longer than every chunk's context (else a chunk's items, which read
+  // as many keys, set the prefill launch's time anyway)
+  if (nd > 0 && longest >= s->mixed_split_context && longest > longest_chunk) {
     // A mixed step's decode rows through split-K decode (a long context
     // spread over many work-groups instead of one per kv head), the prompt
     // chunks after them through the prefill kernel.  A one-token row is a

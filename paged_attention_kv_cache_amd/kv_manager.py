@@ -209,11 +209,13 @@ class Server:
     write and attention launches) and ``complete`` (commit with sampled
     tokens), each one library call.  The device buffer for the step's arrays
     is allocated here; ``plan`` and ``attend`` of one step take the same
-    stream.  A mixed step whose decode rows reach ``mixed_split_context``
-    tokens of context runs them through split-K decode (0: never)."""
+    stream.  With ``mixed_split_context`` > 0 a mixed step whose longest
+    decode row reaches that many tokens of context, and is longer than every
+    chunk's context, runs its decode rows through split-K decode (0, the
+    default: every mixed step in one prefill launch)."""
 
     def __init__(self, sched: StepScheduler, num_heads: int, scale: float, partition_size: int, max_seqs: int,
-                 max_blocks_per_seq: int, max_tokens: int, mixed_split_context: int = 4096, device="cuda"):
+                 max_blocks_per_seq: int, max_tokens: int, mixed_split_context: int = 0, device="cuda"):
         import torch
         self._lib = load_library()
         self.sched = sched
